@@ -1,0 +1,24 @@
+"""CPU oracle for the BitLinear forward pass (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The product path (the HIP library and its Python
+binding) never imports it, and it imports nothing from the product path.
+
+Parity pins: every function here is pinned by `tests/test_oracle_pins.py`
+against closed forms, brute force, the pages' printed code mapping and
+invariants; no function is "parity unpinned".
+"""
+from .oracle import (  # noqa: F401
+    absmean,
+    ternarize,
+    nm_keep,
+    apply_mask,
+    packed_bytes,
+    pack_dense,
+    pack_nm,
+    quantize_weights,
+    quant_act,
+    forward,
+    build,
+    LIB_PATH,
+)

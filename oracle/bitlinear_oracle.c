@@ -1,0 +1,285 @@
+/*
+ * bitlinear_oracle.c -- plain, slow, obviously-correct CPU oracle for the
+ * BitNet b1.58 BitLinear forward pass and its Sparse-BitNet N:M variant.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only
+ * the test suite, the smoke check and the CPU-baseline leg of the benchmark
+ * load it.  It shares no code, header, table or constant generator with the
+ * HIP library; the packed byte layout is re-implemented here from its written
+ * specification.
+ *
+ * Build: gcc -O2 -std=c99 -fno-fast-math -ffp-contract=off -fPIC -shared
+ * (no FMA contraction, IEEE binary32/binary64 arithmetic, round-to-nearest-even
+ * mode, which is the C default).
+ *
+ * Sources, cited by page and section:
+ *  [2B4T]  "BitNet b1.58 2B4T Technical Report 요약 설명" (greeksharifa), sec. 2
+ *          Architecture: absmean ternary weights, per-token absmax 8-bit
+ *          activations; sec. 5.1 GPU Inference: four ternary weights per int8.
+ *  [SURV]  "BitNet 논문 분석: 1-Bit LLM의 시대" (youngju.dev), section
+ *          "Absmean 양자화 함수" (weight_quant_ternary, BitLinear_b158 with
+ *          activation_quant and the integer linear + rescale), and section
+ *          "bitnet.cpp 추론 프레임워크" (I2_S 2-bit code: 00 = -1, 01 = 0,
+ *          10 = +1, sixteen weights per 32-bit word).
+ *  [SPARSE] "Sparse-BitNet: 1.58-bit LLMs are Naturally Friendly to
+ *          Semi-Structured Sparsity" (manon006 review), sec. 3.2: the N:M mask
+ *          keeps the N largest |master weight| per block of M, applied after
+ *          ternarisation (quant-then-mask).
+ *
+ * Readings where the pages are silent or disagree (each one is listed in the
+ * design notes of the repository):
+ *  - activation scale 127/max|x| with no epsilon, s computed once per row and
+ *    multiplied in (the [SURV] listing uses 128/(max|x|+1e-5));
+ *  - round half to even everywhere (torch.round semantics);
+ *  - beta accumulated in binary64 as per-row sums over k ascending, then those
+ *    row sums over n ascending, then divided by N*K and rounded to binary32;
+ *  - d = fl32(beta + 1e-5f); the weight dequant scale is beta itself;
+ *  - N:M groups run along K (the input dimension); ties keep the lower k;
+ *  - a row with max|x| = 0 quantises to zeros with x_scale = 0.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <string.h>
+
+#define OR_OK 0
+#define OR_EINVAL (-1)
+#define OR_ENONFINITE (-5)
+
+/* ------------------------------------------------------------------------ */
+/* Step 1: beta = mean |W| over the whole N x K tensor ([SURV] absmean;      */
+/* [2B4T] sec. 2).  Binary64 accumulation: sum_n ( sum_k |W[n,k]| ).          */
+/* ------------------------------------------------------------------------ */
+int oracle_absmean(const float *W, int64_t N, int64_t K, float *beta_out)
+{
+    if (!W || !beta_out || N < 1 || K < 1) return OR_EINVAL;
+    double total = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double row = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            float w = W[n * K + k];
+            if (!isfinite(w)) return OR_ENONFINITE;
+            row += fabs((double)w);
+        }
+        total += row;
+    }
+    double mean = total / (double)(N * K);
+    *beta_out = (float)mean;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Steps 2-3: d = fl32(beta + 1e-5); t = clamp(round(W / d), -1, 1)          */
+/* ([SURV] weight_quant_ternary).  Division and rounding in binary32.         */
+/* ------------------------------------------------------------------------ */
+int oracle_ternarize(const float *W, int64_t count, float beta, int8_t *t)
+{
+    if (!W || !t || count < 0) return OR_EINVAL;
+    float d = beta + 1e-5f;
+    for (int64_t i = 0; i < count; ++i) {
+        float r = rintf(W[i] / d);
+        if (r > 1.0f) r = 1.0f;
+        if (r < -1.0f) r = -1.0f;
+        t[i] = (int8_t)r;
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 4: N:M keep mask ([SPARSE] sec. 3.2).  Within each group of M        */
+/* consecutive inputs of one output row, keep the N entries of largest       */
+/* |W| (latent weight, not the ternary value).  Equal magnitudes: the lower  */
+/* index wins.  Selection is done the plain way: N rounds, each picking the  */
+/* largest not-yet-kept entry, scanning k upwards with a strict '>'.         */
+/* n == m means dense (everything kept).                                     */
+/* ------------------------------------------------------------------------ */
+int oracle_nm_keep(const float *W, int64_t N, int64_t K, int n, int m, uint8_t *keep)
+{
+    if (!W || !keep || N < 0 || K < 0 || m < 1 || n < 0 || n > m || K % m) return OR_EINVAL;
+    for (int64_t r = 0; r < N; ++r) {
+        for (int64_t g = 0; g < K / m; ++g) {
+            const float *w = W + r * K + g * m;
+            uint8_t *kp = keep + r * K + g * m;
+            for (int i = 0; i < m; ++i) kp[i] = 0;
+            for (int round = 0; round < n; ++round) {
+                int best = -1;
+                float best_mag = 0.0f;
+                for (int i = 0; i < m; ++i) {
+                    if (kp[i]) continue;
+                    float mag = fabsf(w[i]);
+                    if (best < 0 || mag > best_mag) { best = i; best_mag = mag; }
+                }
+                kp[best] = 1;
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* W_eff = t on kept positions, 0 elsewhere (quant-then-mask, [SPARSE] 3.2). */
+int oracle_apply_mask(const int8_t *t, const uint8_t *keep, int64_t count, int8_t *w_eff)
+{
+    if (!t || !keep || !w_eff || count < 0) return OR_EINVAL;
+    for (int64_t i = 0; i < count; ++i) w_eff[i] = keep[i] ? t[i] : 0;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 5: packed byte layout.                                              */
+/*                                                                          */
+/* 2-bit code c = t + 1 ([SURV] I2_S: 00 -> -1, 01 -> 0, 10 -> +1), four    */
+/* codes per byte ([2B4T] sec. 5.1).  A run of 16 codes j = 0..15 forms one */
+/* little-endian 32-bit word with code j at bit 8*(j % 4) + 2*(j / 4).      */
+/*                                                                          */
+/* Dense:  row r holds its K codes (k ascending) in K/16 words, rows back   */
+/*         to back: N*K/4 bytes.                                            */
+/* N:M (2:4 or 6:8), two regions in one buffer:                             */
+/*   values: row r holds the codes of its kept weights in increasing k,    */
+/*           K*n/m codes = K*n/(4m) bytes per row, rows back to back;       */
+/*   masks:  after all value rows, K/8 bytes per row.  For m = 4 each group */
+/*           g has a 4-bit mask in byte g/2 (even g: low nibble, odd g:     */
+/*           high nibble); for m = 8 group g has byte g.  Bit i of a mask   */
+/*           set means k = g*m + i is kept.                                 */
+/* ------------------------------------------------------------------------ */
+static void put_code(uint8_t *words_base, int64_t code_index, unsigned code)
+{
+    int64_t word = code_index / 16;
+    int j = (int)(code_index % 16);
+    int bit = 8 * (j % 4) + 2 * (j / 4);
+    /* little-endian: bit b of the word lives in byte b/8 at bit b%8 */
+    words_base[word * 4 + bit / 8] |= (uint8_t)(code << (bit % 8));
+}
+
+int64_t oracle_packed_bytes(int64_t N, int64_t K, int n, int m)
+{
+    if (N < 1 || K < 1 || K % 64) return -1;
+    if (n == 0 && m == 0) return N * K / 4;
+    if (n == 2 && m == 4) return N * (K / 8) + N * (K / 8);
+    if (n == 6 && m == 8) return N * (3 * K / 16) + N * (K / 8);
+    return -1;
+}
+
+/* dense pack of ternary values t (N x K, row-major) */
+int oracle_pack_dense(const int8_t *t, int64_t N, int64_t K, uint8_t *out)
+{
+    if (!t || !out || N < 1 || K < 1 || K % 64) return OR_EINVAL;
+    memset(out, 0, (size_t)(N * K / 4));
+    for (int64_t r = 0; r < N; ++r)
+        for (int64_t k = 0; k < K; ++k) {
+            int v = t[r * K + k];
+            if (v < -1 || v > 1) return OR_EINVAL;
+            put_code(out + r * (K / 4), k, (unsigned)(v + 1));
+        }
+    return OR_OK;
+}
+
+/* N:M pack of ternary values t with keep mask (exactly n kept per group) */
+int oracle_pack_nm(const int8_t *t, const uint8_t *keep, int64_t N, int64_t K,
+                   int n, int m, uint8_t *out)
+{
+    int64_t total = oracle_packed_bytes(N, K, n, m);
+    if (!t || !keep || !out || total < 0 || n == 0) return OR_EINVAL;
+    memset(out, 0, (size_t)total);
+    int64_t vrow = K * n / m / 4;       /* value bytes per row */
+    int64_t mrow = K / 8;               /* mask bytes per row  */
+    uint8_t *values = out;
+    uint8_t *masks = out + N * vrow;
+    for (int64_t r = 0; r < N; ++r) {
+        int64_t kept = 0;
+        for (int64_t g = 0; g < K / m; ++g) {
+            unsigned mask = 0;
+            int count = 0;
+            for (int i = 0; i < m; ++i) {
+                int64_t k = g * m + i;
+                if (!keep[r * K + k]) continue;
+                int v = t[r * K + k];
+                if (v < -1 || v > 1) return OR_EINVAL;
+                put_code(values + r * vrow, kept, (unsigned)(v + 1));
+                kept++;
+                count++;
+                mask |= 1u << i;
+            }
+            if (count != n) return OR_EINVAL;
+            if (m == 4)
+                masks[r * mrow + g / 2] |= (uint8_t)(mask << (4 * (g % 2)));
+            else
+                masks[r * mrow + g] = (uint8_t)mask;
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 6: per-token absmax int8 activation quantisation ([SURV]            */
+/* activation_quant; [2B4T] sec. 2).  g = max_k |x|; s = fl32(127/g);       */
+/* q = clamp(round(fl32(x*s)), -128, 127); x_scale = fl32(g/127);           */
+/* rowsum = sum_k q.  variant = 1 selects the form printed in the [SURV]    */
+/* listing instead: q = clamp(round(fl32(fl32(x*128) / fl32(g + 1e-5))),    */
+/* -128, 127) and x_scale = g / 128 (kept only to show the difference).     */
+/* ------------------------------------------------------------------------ */
+int oracle_quant_act(const float *X, int64_t M, int64_t K, int variant,
+                     int8_t *q, float *x_scale, int32_t *rowsum)
+{
+    if (!X || !q || !x_scale || M < 0 || K < 1) return OR_EINVAL;
+    for (int64_t r = 0; r < M; ++r) {
+        const float *x = X + r * K;
+        float g = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            if (!isfinite(x[k])) return OR_ENONFINITE;
+            float a = fabsf(x[k]);
+            if (a > g) g = a;
+        }
+        int32_t sum = 0;
+        if (variant == 0) {
+            if (g == 0.0f) {
+                for (int64_t k = 0; k < K; ++k) q[r * K + k] = 0;
+                x_scale[r] = 0.0f;
+            } else {
+                float s = 127.0f / g;
+                for (int64_t k = 0; k < K; ++k) {
+                    float v = rintf(x[k] * s);
+                    if (v > 127.0f) v = 127.0f;
+                    if (v < -128.0f) v = -128.0f;
+                    q[r * K + k] = (int8_t)v;
+                    sum += (int32_t)v;
+                }
+                x_scale[r] = g / 127.0f;
+            }
+        } else {
+            float den = g + 1e-5f;
+            for (int64_t k = 0; k < K; ++k) {
+                float v = rintf((x[k] * 128.0f) / den);
+                if (v > 127.0f) v = 127.0f;
+                if (v < -128.0f) v = -128.0f;
+                q[r * K + k] = (int8_t)v;
+                sum += (int32_t)v;
+            }
+            x_scale[r] = g / 128.0f;
+        }
+        if (rowsum) rowsum[r] = sum;
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Steps 7-8: acc[m,n] = sum_k q[m,k] * W_eff[n,k] (exact, int64), and      */
+/* Y[m,n] = acc * beta * x_scale[m] in binary64 ([SURV] BitLinear_b158      */
+/* forward: integer linear, then rescale by weight and activation scales).  */
+/* acc is written as int32 after checking |acc| <= 128*K.                   */
+/* ------------------------------------------------------------------------ */
+int oracle_forward(const int8_t *q, const float *x_scale, const int8_t *w_eff,
+                   float beta, int64_t M, int64_t N, int64_t K,
+                   int32_t *acc, double *Y)
+{
+    if (!q || !x_scale || !w_eff || M < 0 || N < 1 || K < 1) return OR_EINVAL;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t s = 0;
+            for (int64_t k = 0; k < K; ++k)
+                s += (int64_t)q[m * K + k] * (int64_t)w_eff[n * K + k];
+            if (s > 128 * K || s < -128 * K) return OR_EINVAL;
+            if (acc) acc[m * N + n] = (int32_t)s;
+            if (Y) Y[m * N + n] = (double)s * (double)beta * (double)x_scale[m];
+        }
+    return OR_OK;
+}

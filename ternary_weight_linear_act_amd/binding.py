@@ -1,0 +1,191 @@
+"""Thin ctypes binding of libbitlinear.so (declared in include/bitlinear.h).
+
+Argument marshalling only: torch tensors supply device memory and the current
+HIP stream; every step of the BitLinear path runs in the library's kernels.
+There is no fallback: if the library is missing or a call fails, this raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libbitlinear.so"
+
+NM_DENSE = (0, 0)
+NM_2_4 = (2, 4)
+NM_6_8 = (6, 8)
+
+OK, EINVAL, EUNSUPPORTED, ESIZE, EHIP = 0, -1, -2, -3, -4
+_STATUS = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ESIZE: "ESIZE", EHIP: "EHIP"}
+
+EXPORTED = (
+    "bitlinear_packed_size",
+    "bitlinear_pack_weights",
+    "bitlinear_quant_act",
+    "bitlinear_forward",
+    "bitlinear_last_error",
+    "bitlinear_last_dispatch",
+)
+
+
+class BitLinearError(RuntimeError):
+    def __init__(self, fn, status, message):
+        self.status = status
+        super().__init__("%s failed: %s (%d): %s" % (fn, _STATUS.get(status, "?"), status, message))
+
+
+class NM(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+_lib = None
+
+
+def load_library():
+    """Load libbitlinear.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libbitlinear.so is not built (%s); run __graft_entry__.build() first -- "
+            "there is no fallback implementation" % path)
+    lib = ctypes.CDLL(path)
+    i64, sz, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+    lib.bitlinear_packed_size.argtypes = [i64, i64, NM, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.bitlinear_pack_weights.argtypes = [vp, i64, i64, NM, vp, sz, vp, vp, sz, vp]
+    lib.bitlinear_quant_act.argtypes = [vp, i64, i64, vp, vp, vp, vp]
+    lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp]
+    for f in ("bitlinear_packed_size", "bitlinear_pack_weights", "bitlinear_quant_act",
+              "bitlinear_forward"):
+        getattr(lib, f).restype = ctypes.c_int
+    lib.bitlinear_last_error.restype = ctypes.c_char_p
+    lib.bitlinear_last_dispatch.restype = ctypes.c_char_p
+    lib.bitlinear_last_error.argtypes = []
+    lib.bitlinear_last_dispatch.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != OK:
+        msg = load_library().bitlinear_last_error()
+        raise BitLinearError(fn, status, msg.decode() if msg else "")
+
+
+def last_dispatch() -> str:
+    s = load_library().bitlinear_last_dispatch()
+    return s.decode() if s else ""
+
+
+def _nm(nm):
+    n, m = nm
+    return NM(int(n), int(m))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _require(t, dtype, shape, name):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor (got %s)" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def packed_size(N: int, K: int, nm=NM_DENSE):
+    """(packed_bytes, workspace_bytes) for an N x K weight matrix."""
+    lib = load_library()
+    pb, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("bitlinear_packed_size", lib.bitlinear_packed_size(N, K, _nm(nm), ctypes.byref(pb), ctypes.byref(wb)))
+    return pb.value, wb.value
+
+
+def pack_weights(W, nm=NM_DENSE, out=None, w_scale=None, workspace=None, stream=None):
+    """Ternarise and pack an N x K fp32 device matrix.  Returns (packed uint8, w_scale fp32[1])."""
+    import torch
+    _require(W, torch.float32, None, "W")
+    N, K = W.shape
+    pb, wb = packed_size(N, K, nm)
+    if out is None:
+        out = torch.empty(pb, dtype=torch.uint8, device=W.device)
+    if w_scale is None:
+        w_scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    if workspace is None and wb:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
+    _require(out, torch.uint8, None, "packed")
+    _require(w_scale, torch.float32, (1,), "w_scale")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bitlinear_pack_weights", load_library().bitlinear_pack_weights(
+        _ptr(W), N, K, _nm(nm), _ptr(out), out.numel(), _ptr(w_scale), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return out, w_scale
+
+
+def quant_act(X, Xq=None, x_scale=None, x_rowsum=None, stream=None):
+    """Per-row absmax int8 quantisation of an M x K fp32 device matrix.
+
+    Returns (Xq int8 M x K, x_scale fp32[M], x_rowsum int32[M]).
+    """
+    import torch
+    _require(X, torch.float32, None, "X")
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    if x_rowsum is None:
+        x_rowsum = torch.empty(M, dtype=torch.int32, device=X.device)
+    _require(Xq, torch.int8, (M, K), "Xq")
+    _require(x_scale, torch.float32, (M,), "x_scale")
+    _require(x_rowsum, torch.int32, (M,), "x_rowsum")
+    _check("bitlinear_quant_act", load_library().bitlinear_quant_act(
+        _ptr(X), M, K, _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _stream(stream)))
+    return Xq, x_scale, x_rowsum
+
+
+def forward(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=None, acc=None,
+            want_acc=False, stream=None):
+    """Y = (Xq . W_eff^T) * w_scale * x_scale, fp32 M x N.  Returns Y or (Y, acc)."""
+    import torch
+    _require(Xq, torch.int8, None, "Xq")
+    M, K = Xq.shape
+    _require(x_scale, torch.float32, (M,), "x_scale")
+    _require(x_rowsum, torch.int32, (M,), "x_rowsum")
+    _require(packed, torch.uint8, None, "packed")
+    _require(w_scale, torch.float32, (1,), "w_scale")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    _require(Y, torch.float32, (M, N), "Y")
+    if acc is None and want_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    if acc is not None:
+        _require(acc, torch.int32, (M, N), "acc")
+    pb, _ = packed_size(N, K, nm)
+    if packed.numel() < pb:
+        raise ValueError("packed buffer holds %d bytes, %d needed" % (packed.numel(), pb))
+    _check("bitlinear_forward", load_library().bitlinear_forward(
+        _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _ptr(packed), _ptr(w_scale), _nm(nm),
+        M, N, K, _ptr(Y), _ptr(acc), _stream(stream)))
+    return (Y, acc) if (want_acc or acc is not None) else Y

@@ -1,0 +1,58 @@
+"""The oracle pins must catch plausible slips in the oracle.
+
+Each case copies oracle/bitlinear_oracle.c, plants one mistake on the CPU
+(a dropped abs, a wrong divisor, truncation instead of round-half-even, a
+missing epsilon, a wrong tie-break, a misplaced bit, a transposed operand, a
+wrong clamp, a wrong activation constant), builds it, and runs the pin suite
+against it: the suite must fail for every mutant.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "bitlinear_oracle.c")
+
+MUTANTS = {
+    "abs_dropped": ("row += fabs((double)w);", "row += (double)w;"),
+    "divisor_N": ("double mean = total / (double)(N * K);", "double mean = total / (double)(N);"),
+    "no_eps": ("float d = beta + 1e-5f;", "float d = beta;"),
+    "trunc_not_rne_w": ("float r = rintf(W[i] / d);", "float r = truncf(W[i] / d);"),
+    "round_half_away_w": ("float r = rintf(W[i] / d);", "float r = roundf(W[i] / d);"),
+    "tie_to_higher_k": ("if (best < 0 || mag > best_mag)", "if (best < 0 || mag >= best_mag)"),
+    "rank_signed": ("float mag = fabsf(w[i]);", "float mag = w[i];"),
+    "bit_position": ("int bit = 8 * (j % 4) + 2 * (j / 4);", "int bit = 2 * j;"),
+    "code_offset": ("put_code(out + r * (K / 4), k, (unsigned)(v + 1));",
+                    "put_code(out + r * (K / 4), k, (unsigned)(1 - v));"),
+    "act_const_128": ("float s = 127.0f / g;", "float s = 128.0f / g;"),
+    "act_round_half_away": ("float v = rintf(x[k] * s);", "float v = roundf(x[k] * s);"),
+    "act_order": ("float v = rintf(x[k] * s);", "float v = rintf((x[k] * 127.0f) / g);"),
+    "xscale_inverse": ("x_scale[r] = g / 127.0f;", "x_scale[r] = 127.0f / g;"),
+    "transposed_w": ("s += (int64_t)q[m * K + k] * (int64_t)w_eff[n * K + k];",
+                     "s += (int64_t)q[m * K + k] * (int64_t)w_eff[k * N + n];"),
+    "nm_mask_nibble_order": ("masks[r * mrow + g / 2] |= (uint8_t)(mask << (4 * (g % 2)));",
+                             "masks[r * mrow + g / 2] |= (uint8_t)(mask << (4 * (1 - g % 2)));"),
+    "nm_keep_one_less": ("for (int round = 0; round < n; ++round)", "for (int round = 1; round < n; ++round)"),
+    "epilogue_no_beta": ("Y[m * N + n] = (double)s * (double)beta * (double)x_scale[m];",
+                         "Y[m * N + n] = (double)s * (double)x_scale[m];"),
+}
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor not found: %s" % old
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fno-fast-math", "-ffp-contract=off", "-fPIC",
+                           "-shared", "-o", str(lib), str(mut), "-lm"])
+    env = dict(os.environ, BITLINEAR_ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle_pins.py")],
+                       env=env, cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, "pins did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])

@@ -1,0 +1,481 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test fixes the oracle to a closed form, a hand-worked value, a brute-force
+search, a value printed on the pages (tests/golden/) or an invariant that the
+mathematics forces, so that a plausible slip in the oracle -- a dropped abs, a
+wrong divisor, a transposed operand, a wrong rounding rule, a wrong tie-break
+or a misplaced bit -- fails at least one of them.
+
+Sources:
+* "BitNet 논문 분석: 1-Bit LLM의 시대" (youngju.dev), sections "Absmean 양자화
+  함수" (absmean ternary weights, absmax int8 activations, integer linear and
+  rescale) and "bitnet.cpp 추론 프레임워크" / "I2_S 커널의 내부 동작" (2-bit
+  code, TL2 pair lookup);
+* "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 2 and sec. 5.1;
+* "Sparse-BitNet: ..." (review), sec. 3.2 (top-N |latent| per block of M,
+  quant-then-mask).
+"""
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_linear_act_amd import workloads
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F32 = np.float32
+
+
+def f32(x):
+    return F32(x)
+
+
+def ulp32(x):
+    x = abs(F32(x))
+    return float(np.nextafter(x, F32(np.inf)) - x)
+
+
+# --------------------------------------------------------------------------
+# independent reader of the packed layout (written from the format's text:
+# code j of a 16-code word at bit 8*(j%4) + 2*(j/4), little-endian words)
+# --------------------------------------------------------------------------
+def read_codes(buf, ncodes):
+    out = []
+    for c in range(ncodes):
+        word = c // 16
+        j = c % 16
+        w = int(buf[4 * word]) | int(buf[4 * word + 1]) << 8 | int(buf[4 * word + 2]) << 16 | int(buf[4 * word + 3]) << 24
+        out.append((w >> (8 * (j % 4) + 2 * (j // 4))) & 3)
+    return out
+
+
+def decode_dense(buf, N, K):
+    rows = []
+    for r in range(N):
+        codes = read_codes(buf[r * K // 4:(r + 1) * K // 4], K)
+        rows.append([c - 1 for c in codes])
+    return np.array(rows, dtype=np.int8)
+
+
+def decode_nm(buf, N, K, n, m):
+    vrow = K * n // m // 4
+    mrow = K // 8
+    masks = buf[N * vrow:]
+    out = np.zeros((N, K), np.int8)
+    for r in range(N):
+        codes = read_codes(buf[r * vrow:(r + 1) * vrow], K * n // m)
+        ci = 0
+        for g in range(K // m):
+            if m == 4:
+                mask = (int(masks[r * mrow + g // 2]) >> (4 * (g % 2))) & 0xF
+            else:
+                mask = int(masks[r * mrow + g])
+            assert bin(mask).count("1") == n
+            for i in range(m):
+                if mask >> i & 1:
+                    out[r, g * m + i] = codes[ci] - 1
+                    ci += 1
+    return out
+
+
+# ==========================================================================
+# absmean (beta)
+# ==========================================================================
+class TestAbsmean:
+    def test_constant(self):
+        W = np.full((4, 64), 0.25, np.float32)
+        assert oracle.absmean(W) == F32(0.25)
+
+    def test_signs_are_dropped(self):
+        W = np.full((4, 64), 0.5, np.float32)
+        W[:, ::2] *= -1
+        W[1::2] *= -1
+        assert oracle.absmean(W) == F32(0.5)
+
+    def test_divides_by_all_elements(self):
+        # row n holds (n+1)/8, mean over N=8 rows = (1+...+8)/64 = 36/64
+        N, K = 8, 128
+        W = np.repeat((np.arange(1, N + 1, dtype=np.float32) / 8)[:, None], K, axis=1)
+        W[:, 1::3] *= -1
+        assert oracle.absmean(W) == F32(36 / 64)
+        # a wrong divisor (N or K alone) or a missing abs would not give 0.5625
+
+    def test_matches_exact_mean(self):
+        rng = np.random.default_rng(11)
+        for shape in [(3, 64), (17, 128), (64, 1024)]:
+            W = (rng.standard_normal(shape) * 0.02).astype(np.float32)
+            exact = sum((Fraction(float(abs(v))) for v in W.ravel()), Fraction(0)) / W.size
+            beta = oracle.absmean(W)
+            assert abs(Fraction(float(beta)) - exact) <= Fraction(ulp32(beta)) * Fraction(1, 2) * Fraction(1000001, 1000000)
+
+    def test_gaussian_absmean(self):
+        # E|w| = sigma * sqrt(2/pi) for w ~ N(0, sigma^2)
+        W = workloads.normal_f32(np.random.default_rng(0), (1024, 1024), 0.02)
+        assert abs(float(oracle.absmean(W)) / (0.02 * math.sqrt(2 / math.pi)) - 1) < 0.005
+
+    def test_rejects_nonfinite(self):
+        W = np.ones((2, 64), np.float32)
+        W[1, 3] = np.nan
+        with pytest.raises(ValueError):
+            oracle.absmean(W)
+
+
+# ==========================================================================
+# ternarisation  t = clamp(round(W / (beta + 1e-5)), -1, 1)
+# ==========================================================================
+def beta_giving_unit_d():
+    """A float32 beta with fl32(beta + 1e-5f) == 1 exactly."""
+    b = F32(1) - F32(1e-5)
+    for _ in range(64):
+        d = F32(b + F32(1e-5))
+        if d == F32(1):
+            return b
+        b = np.nextafter(b, F32(0) if d > 1 else F32(2))
+    raise AssertionError("no beta found")
+
+
+class TestTernarize:
+    def test_ties_and_clamp_with_unit_d(self):
+        beta = beta_giving_unit_d()
+        W = np.array([0.0, 0.5, -0.5, np.nextafter(F32(0.5), F32(0)), np.nextafter(F32(0.5), F32(1)),
+                      1.0, 1.5, -1.5, 2.5, -7.0, 1e-30, np.nextafter(F32(-0.5), F32(-1)), 0.75, -0.25],
+                     dtype=np.float32)
+        want = [0, 0, 0, 0, 1, 1, 1, -1, 1, -1, 0, -1, 1, 0]
+        assert oracle.ternarize(W, beta).tolist() == want
+
+    def test_eps_is_added_to_beta(self):
+        # with beta = 0, d = 1e-5: W = 4e-6 -> 0.4 -> 0 ; W = 6e-6 -> 0.6 -> 1
+        W = np.array([4e-6, 6e-6, -6e-6], np.float32)
+        assert oracle.ternarize(W, 0.0).tolist() == [0, 1, -1]
+
+    def test_gaussian_zero_fraction(self):
+        # t = 0 iff |W| < d/2 with d ~= sigma*sqrt(2/pi): P = erf(sqrt(1/pi)/sqrt(2)*...) ;
+        # P(|Z| < 0.5*sqrt(2/pi)) = erf(0.5*sqrt(2/pi)/sqrt(2)) = erf(0.5/sqrt(pi))
+        W = workloads.normal_f32(np.random.default_rng(0), (1024, 1024), 0.02)
+        t = oracle.ternarize(W, oracle.absmean(W))
+        p0 = math.erf(0.5 / math.sqrt(math.pi))
+        frac0 = float(np.mean(t == 0))
+        assert abs(frac0 - p0) < 0.003
+        assert abs(float(np.mean(t == 1)) - float(np.mean(t == -1))) < 0.005
+        assert set(np.unique(t).tolist()) == {-1, 0, 1}
+
+    def test_matches_definition_elementwise(self):
+        # round-half-even on fp32 quotients, recomputed with numpy's fp32 ops
+        rng = np.random.default_rng(5)
+        W = (rng.standard_normal(4096) * 0.02).astype(np.float32)
+        beta = F32(0.016)
+        d = F32(beta + F32(1e-5))
+        want = np.clip(np.rint(W / d), -1, 1).astype(np.int8)
+        assert np.array_equal(oracle.ternarize(W, beta), want)
+
+
+# ==========================================================================
+# N:M keep mask
+# ==========================================================================
+def brute_keep(w, n):
+    """The unique n-subset whose every member outranks every non-member.
+
+    Rank key of position i: (|w_i|, -i): larger magnitude first, then lower i.
+    """
+    m = len(w)
+    key = lambda i: (abs(float(w[i])), -i)
+    found = []
+    for S in itertools.combinations(range(m), n):
+        rest = [i for i in range(m) if i not in S]
+        if not rest or min(key(i) for i in S) > max(key(i) for i in rest):
+            found.append(S)
+    assert len(found) == 1
+    return found[0]
+
+
+class TestNM:
+    @pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (1, 4), (3, 8), (7, 8), (2, 8), (5, 8)])
+    def test_brute_force_with_ties(self, n, m):
+        rng = np.random.default_rng(100 + 10 * n + m)
+        # magnitudes from a small set -> many ties
+        W = rng.choice(np.array([0.0, 0.01, -0.01, 0.02, -0.02, 0.03], np.float32), size=(6, 8 * m))
+        keep = oracle.nm_keep(W, n, m)
+        for r in range(W.shape[0]):
+            for g in range(W.shape[1] // m):
+                S = brute_keep(W[r, g * m:(g + 1) * m], n)
+                got = tuple(np.nonzero(keep[r, g * m:(g + 1) * m])[0].tolist())
+                assert got == S
+
+    def test_hand_examples(self):
+        W = np.array([[0.1, -0.3, 0.3, 0.2, 0.2, 0.2, 0.2, 0.2]], np.float32)
+        assert oracle.nm_keep(W, 2, 4).tolist() == [[0, 1, 1, 0, 1, 1, 0, 0]]
+        W = (np.arange(1, 9, dtype=np.float32) / 10)[None, :]
+        assert oracle.nm_keep(W, 6, 8).tolist() == [[0, 0, 1, 1, 1, 1, 1, 1]]
+        W = np.zeros((1, 8), np.float32)
+        assert oracle.nm_keep(W, 6, 8).tolist() == [[1, 1, 1, 1, 1, 1, 0, 0]]
+
+    def test_dense_limit(self):
+        # n = m keeps everything: the N:M forward reduces to the dense one
+        W = workloads.normal_f32(np.random.default_rng(1), (4, 64), 0.02)
+        assert oracle.nm_keep(W, 8, 8).all()
+        assert oracle.nm_keep(W, 4, 4).all()
+
+    @pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+    def test_invariants_random(self, n, m):
+        W = workloads.normal_f32(np.random.default_rng(2), (64, 256), 0.02)
+        keep = oracle.nm_keep(W, n, m).reshape(64, -1, m).astype(bool)
+        mag = np.abs(W).reshape(64, -1, m)
+        assert (keep.sum(-1) == n).all()
+        kept_min = np.where(keep, mag, np.inf).min(-1)
+        pruned_max = np.where(~keep, mag, -np.inf).max(-1)
+        assert (kept_min >= pruned_max).all()
+
+    def test_ranked_by_latent_not_ternary(self):
+        # 0.9 and 0.6 both ternarise to +1 (d = 1): the mask must still prefer 0.9
+        beta = beta_giving_unit_d()
+        W = np.array([[0.6, 0.9, 0.1, 0.0]], np.float32)
+        t = oracle.ternarize(W, beta)
+        assert t.tolist() == [[1, 1, 0, 0]]
+        assert oracle.nm_keep(W, 1, 4).tolist() == [[0, 1, 0, 0]]
+
+
+# ==========================================================================
+# packed layout
+# ==========================================================================
+def load_code_map():
+    cmap = {}
+    with open(os.path.join(GOLDEN, "i2s_code_map.txt")) as f:
+        for line in f:
+            line = line.split("#")[0].strip()
+            if not line:
+                continue
+            a, b = line.split()
+            if a == "words":
+                cmap["words"] = int(b)
+            else:
+                cmap[int(a)] = int(b, 2)
+    return cmap
+
+
+def word(buf, i):
+    return int.from_bytes(bytes(buf[4 * i:4 * i + 4]), "little")
+
+
+class TestPack:
+    def test_code_map_from_pages(self):
+        cmap = load_code_map()
+        assert cmap["words"] == 16
+        for v in (-1, 0, 1):
+            buf = oracle.pack_dense(np.full((1, 64), v, np.int8))
+            for i in range(4):
+                w = word(buf, i)
+                fields = [(w >> (2 * f)) & 3 for f in range(16)]
+                assert fields == [cmap[v]] * 16
+        assert word(oracle.pack_dense(np.full((1, 64), 1, np.int8)), 0) == 0xAAAAAAAA
+        assert word(oracle.pack_dense(np.full((1, 64), 0, np.int8)), 0) == 0x55555555
+        assert word(oracle.pack_dense(np.full((1, 64), -1, np.int8)), 0) == 0x00000000
+
+    @pytest.mark.parametrize("j,val,want", [
+        (0, 1, 0x55555556), (1, 1, 0x55555655), (3, 1, 0x56555555), (4, 1, 0x55555559),
+        (15, 1, 0x95555555), (0, -1, 0x55555554), (5, -1, 0x55555155), (10, -1, 0x55455555),
+    ])
+    def test_bit_positions(self, j, val, want):
+        # a single nonzero at k = 16 + j (second word); code j sits at bit 8*(j%4) + 2*(j/4)
+        t = np.zeros((1, 64), np.int8)
+        t[0, 16 + j] = val
+        buf = oracle.pack_dense(t)
+        assert word(buf, 0) == 0x55555555 and word(buf, 2) == 0x55555555
+        assert word(buf, 1) == want
+
+    def test_round_trip_and_no_code_3(self):
+        rng = np.random.default_rng(3)
+        t = rng.integers(-1, 2, size=(5, 192)).astype(np.int8)
+        buf = oracle.pack_dense(t)
+        assert buf.size == 5 * 192 // 4
+        assert np.array_equal(decode_dense(buf, 5, 192), t)
+        b = buf.astype(np.uint32)
+        for s in range(0, 8, 2):
+            assert not np.any(((b >> s) & 3) == 3)
+
+    def test_sizes(self):
+        assert oracle.packed_bytes(6912, 2560) == 4423680
+        assert oracle.packed_bytes(8960, 1536, 2, 4) == 3440640
+        assert oracle.packed_bytes(8960, 1536, 6, 8) == 4300800
+        assert oracle.packed_bytes(10, 96) == -1       # K % 64 != 0
+        assert oracle.packed_bytes(10, 128, 3, 4) == -1
+
+    def test_nm_hand_example_2_4(self):
+        # K = 64, one row: group g keeps positions (g % 4, (g % 4 + 1) % 4 ... ) chosen by magnitude
+        K = 64
+        W = np.zeros((1, K), np.float32)
+        t = np.zeros((1, K), np.int8)
+        # groups: keep positions {1,2} with values (+1, -1) in every group
+        for g in range(K // 4):
+            W[0, 4 * g + 1] = 0.5
+            W[0, 4 * g + 2] = -0.4
+            t[0, 4 * g + 1] = 1
+            t[0, 4 * g + 2] = -1
+        keep = oracle.nm_keep(W, 2, 4)
+        buf = oracle.pack_nm(t, keep, 2, 4)
+        assert buf.size == K // 8 + K // 8
+        # values: 32 kept codes alternating (+1 -> 2, -1 -> 0): codes j even = 2, j odd = 0
+        # word fields: code j at bit 8*(j%4) + 2*(j/4) -> bytes 0 and 2 hold 2 in every field
+        for wi in range(2):
+            assert word(buf, wi) == 0x00AA00AA
+        # masks: nibble 0b0110 for every group -> bytes 0x66
+        assert buf[K // 8:].tolist() == [0x66] * (K // 8)
+
+    @pytest.mark.parametrize("n,m", [(2, 4), (6, 8)])
+    def test_nm_decodes_to_masked_dense(self, n, m):
+        W = workloads.normal_f32(np.random.default_rng(4), (3, 128), 0.02)
+        beta, w_eff, buf = oracle.quantize_weights(W, n, m)
+        assert buf.size == oracle.packed_bytes(3, 128, n, m)
+        assert np.array_equal(decode_nm(buf, 3, 128, n, m), w_eff)
+        t = oracle.ternarize(W, beta)
+        keep = oracle.nm_keep(W, n, m).astype(bool)
+        assert np.array_equal(w_eff, np.where(keep, t, 0))
+
+
+# ==========================================================================
+# activation quantisation
+# ==========================================================================
+class TestQuantAct:
+    def test_hand_examples(self):
+        X = np.array([[1.0, -0.5, 0.25, 0.0]], np.float32)
+        q, xs, rs = oracle.quant_act(X)
+        assert q.tolist() == [[127, -64, 32, 0]]          # -63.5 -> -64 (half to even), 31.75 -> 32
+        assert xs[0] == F32(1) / F32(127) and rs[0] == 95
+        q, _, _ = oracle.quant_act(np.array([[2.0, 1.0, -1.0, 0.0]], np.float32))
+        assert q.tolist() == [[127, 64, -64, 0]]          # 63.5 -> 64
+        q, xs, _ = oracle.quant_act(np.array([[-4.0, 1.0, 0.5, 0.0]], np.float32))
+        assert q.tolist() == [[-127, 32, 16, 0]]          # s = 31.75
+        assert xs[0] == F32(4) / F32(127)
+        q, _, _ = oracle.quant_act(np.array([[254.0, 1.0, 3.0, -1.0]], np.float32))
+        assert q.tolist() == [[127, 0, 2, 0]]            # s = 0.5: 0.5 -> 0, 1.5 -> 2, -0.5 -> 0
+
+    def test_scale_computed_once(self):
+        # g = 7.5: s = fl32(127/7.5) = 8877943 * 2^-19 = 16.933332443...;
+        # 3.75 * s = 63.4999966... -> fl32 = 16646143 * 2^-18 = 63.499996... -> 63.
+        # (Multiplying by 127 first and dividing by g would give exactly 63.5 -> 64.)
+        q, _, _ = oracle.quant_act(np.array([[7.5, 3.75, -3.75, 0.0]], np.float32))
+        assert q.tolist() == [[127, 63, -63, 0]]
+
+    def test_zero_row(self):
+        q, xs, rs = oracle.quant_act(np.zeros((2, 64), np.float32))
+        assert not q.any() and not xs.any() and not rs.any()
+
+    def test_argmax_maps_to_127_and_never_minus_128(self):
+        X = workloads.activations(np.random.default_rng(6), 2000, 2560, 0.001)
+        q, xs, rs = oracle.quant_act(X)
+        am = np.argmax(np.abs(X), axis=1)
+        assert np.array_equal(np.abs(q[np.arange(2000), am].astype(int)), np.full(2000, 127))
+        assert q.min() >= -127
+        assert np.array_equal(rs, q.astype(np.int64).sum(1))
+        assert np.array_equal(xs, (np.abs(X).max(1) / F32(127)).astype(np.float32))
+
+    def test_monotone(self):
+        x = np.sort(np.random.default_rng(7).standard_normal(512)).astype(np.float32)[None, :]
+        q, _, _ = oracle.quant_act(x)
+        assert np.all(np.diff(q[0].astype(int)) >= 0)
+
+    def test_power_of_two_invariance(self):
+        X = workloads.activations(np.random.default_rng(8), 16, 256)
+        q0, xs0, _ = oracle.quant_act(X)
+        for e in (-3, 1, 5):
+            q1, xs1, _ = oracle.quant_act((X * F32(2.0 ** e)).astype(np.float32))
+            assert np.array_equal(q0, q1)
+            assert np.array_equal(xs1, (xs0 * F32(2.0 ** e)).astype(np.float32))
+
+    def test_listing_variant_differs(self):
+        # the 128/(g+1e-5) form printed in the listing can reach -128; 127/g cannot
+        X = np.array([[-1.0, 0.5]], np.float32)
+        assert oracle.quant_act(X, variant=1)[0].tolist() == [[-128, 64]]
+        assert oracle.quant_act(X, variant=0)[0].tolist() == [[-127, 64]]
+
+
+# ==========================================================================
+# contraction and epilogue
+# ==========================================================================
+class TestForward:
+    def test_exhaustive_ternary_rows(self):
+        K = 8
+        rows = np.array(list(itertools.product((-1, 0, 1), repeat=K)), np.int8)   # 3^8 rows
+        rng = np.random.default_rng(9)
+        q = rng.integers(-128, 128, size=(3, K)).astype(np.int8)
+        acc, _ = oracle.forward(q, np.ones(3, np.float32), rows, 1.0)
+        for m in range(3):
+            for n in range(0, rows.shape[0], 97):
+                assert acc[m, n] == sum(int(q[m, k]) * int(rows[n, k]) for k in range(K))
+        # permutation symmetry: each column sums to 0 because +1 and -1 rows pair up
+        assert not acc.sum(1).any()
+
+    def test_closed_forms(self):
+        K = 256
+        q = np.random.default_rng(10).integers(-128, 128, size=(2, K)).astype(np.int8)
+        W = np.zeros((4, K), np.int8)
+        W[0] = 1
+        W[1] = -1
+        W[2, 37] = 1               # one-hot: selects q[:, 37]
+        W[3, 200] = -1
+        acc, _ = oracle.forward(q, np.ones(2, np.float32), W, 1.0)
+        rs = q.astype(np.int64).sum(1)
+        assert acc[:, 0].tolist() == rs.tolist()
+        assert acc[:, 1].tolist() == (-rs).tolist()
+        assert acc[:, 2].tolist() == q[:, 37].astype(int).tolist()
+        assert acc[:, 3].tolist() == (-q[:, 200].astype(int)).tolist()
+
+    def test_transposition_is_caught(self):
+        # rows of W_eff are outputs: W[n] one-hot at k = n + 1
+        K, N = 64, 8
+        W = np.zeros((N, K), np.int8)
+        for n in range(N):
+            W[n, n + 1] = 1
+        q = np.arange(K, dtype=np.int8)[None, :]
+        acc, _ = oracle.forward(q, np.ones(1, np.float32), W, 1.0)
+        assert acc[0].tolist() == list(range(1, N + 1))
+
+    def test_extremes(self):
+        K = 11008
+        q = np.full((1, K), -128, np.int8)
+        W = np.full((1, K), -1, np.int8)
+        acc, Y = oracle.forward(q, np.ones(1, np.float32), W, 1.0)
+        assert acc[0, 0] == 1409024 == 128 * K
+
+    def test_epilogue_closed_form(self):
+        q = np.array([[1, 2, 3, 4] * 16], np.int8)
+        W = np.ones((1, 64), np.int8)
+        acc, Y = oracle.forward(q, np.array([0.5], np.float32), W, 0.25)
+        assert acc[0, 0] == 160
+        assert Y[0, 0] == 160 * 0.125
+
+    def test_tl2_pair_lookup_identity(self):
+        # TL2 description: pairs (w0, w1) index a 9-entry table of a0*w0 + a1*w1
+        with open(os.path.join(GOLDEN, "tl2_demo_weights.txt")) as f:
+            fields = {l.split()[0]: l.split()[1:] for l in f if l.strip() and not l.startswith("#")}
+        w = np.array([int(v) for v in fields["weights"]], np.int8)
+        acts = np.random.RandomState(int(fields["seed"][0])).randn(len(w)).astype(np.float32)
+        # the page's pair indices: (w0 + 1) * 3 + (w1 + 1)
+        idx = [(w[i] + 1) * 3 + (w[i + 1] + 1) for i in range(0, len(w), 2)]
+        assert idx == [2, 5, 1, 6]
+        # integer version of the lookup on the oracle's int8 activations
+        q, _, _ = oracle.quant_act(np.tile(acts, 8)[None, :])    # K = 64
+        wrow = np.tile(w, 8)[None, :]
+        acc, _ = oracle.forward(q, np.ones(1, np.float32), wrow, 1.0)
+        total = 0
+        qa = q[0].astype(int)
+        for i in range(0, 64, 2):
+            a0, a1 = qa[i], qa[i + 1]
+            lut = [-(a0 + a1), -a0, -a0 + a1, -a1, 0, a1, a0 - a1, a0, a0 + a1]
+            total += lut[(wrow[0, i] + 1) * 3 + (wrow[0, i + 1] + 1)]
+        assert acc[0, 0] == total
+
+    def test_end_to_end_tracks_float_linear(self):
+        W, X = workloads.small_case(12, 16, 64, 1024)
+        beta, w_eff, _ = oracle.quantize_weights(W)
+        q, xs, _ = oracle.quant_act(X)
+        _, Y = oracle.forward(q, xs, w_eff, beta)
+        ref = X.astype(np.float64) @ W.astype(np.float64).T
+        c = np.corrcoef(Y.ravel(), ref.ravel())[0, 1]
+        assert c > 0.85
+        # and the dequantised product equals the float product of the quantised operands
+        deq = (q.astype(np.float64) * xs[:, None].astype(np.float64)) @ (w_eff.astype(np.float64) * float(beta)).T
+        assert np.allclose(Y, deq, rtol=1e-12, atol=0)
