@@ -1,0 +1,307 @@
+"""Benchmark of the BitLinear forward on one MI355X.
+
+Headline: BitLinear GB/s at M = 1 (decode GEMV over a 2B-class FFN: gate and up
+2560 -> 6912, down 6912 -> 2560) as a fraction of HBM peak, and int8 TOPS at
+M = 2048 (prefill GEMM, K = 2560, N = 6912) as a fraction of int8 MFMA peak.
+
+A step is one pass of the hot path over one batch: for each projection,
+per-token int8 activation quantisation, then the packed-ternary forward with
+its fused dequant epilogue.  Weights are packed once, outside the timed
+region (they are stored packed).  The packed weights rotate through a pool of
+distinct buffers larger than the 256 MB Infinity Cache so that every step
+streams its weights from HBM.  Steps are captured in a HIP graph and timed
+with HIP events on the capture's stream, bracketed by device synchronisation.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Prints one JSON line on stdout; a readable summary goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+INT8_PEAK_TOPS = 5000.0        # MI355X dense int8 MFMA, published (5.0 POP/s)
+POOL_BYTES = 512 << 20         # >= 2x the 256 MB Infinity Cache
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_decode_ffn_2b.json")
+CSRC = os.path.join(ROOT, "ternary_weight_linear_act_amd", "csrc")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def fwd_bytes(M, N, K, nm=(0, 0)):
+    """Algorithmic bytes of one forward launch: packed weights, int8 activations,
+    x_scale + row sums, beta, fp32 output."""
+    wbytes = N * K * (5 / 16 if nm == (6, 8) else 1 / 4)
+    return int(wbytes + M * K + 8 * M + 4 + 4 * M * N)
+
+
+def quant_bytes(M, K):
+    """fp32 in, int8 out, x_scale and row sum."""
+    return 4 * M * K + M * K + 8 * M
+
+
+def timed_graph(torch, body, reps=1):
+    """Capture body() into a HIP graph, replay it once untimed, then time `reps`
+    replays with events on the graph's stream.  Returns ms per replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()                                   # eager warm call outside capture
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        body()
+    # replay on s and record the events on s: graph launches go to the current stream
+    with torch.cuda.stream(s):
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps, g
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ternary_weight_linear_act_amd as bl
+    from ternary_weight_linear_act_amd import workloads
+
+    bl.load_library()                      # raises if the HIP library is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    props = torch.cuda.get_device_properties(dev)
+    log("device: %s (%s), %d CUs" % (props.name, getattr(props, "gcnArchName", "?"), props.multi_processor_count))
+
+    # ------------------------------------------------------------------ decode
+    # One decode step of a 2B-class FFN at M = 1: the fused call (activation
+    # quantisation + projections sharing the input, one launch) for gate/up,
+    # then for down.  Weights rotate through a pool > 2x the Infinity Cache.
+    wl = workloads.WORKLOADS["decode_ffn_2b"]
+    d = workloads.draw("decode_ffn_2b")
+    shapes = {p.name: (p.N, p.K) for p in wl.projs}
+    groups = workloads.input_groups(wl)
+    step_w_bytes = sum(N * K // 4 for N, K in shapes.values())
+    P = max(2, -(-POOL_BYTES // step_w_bytes))
+    packed, wsc, Y = {}, {}, {}
+    for name, (N, K) in shapes.items():
+        pk, ws = bl.pack_weights(torch.from_numpy(d.W[name]).to(dev))
+        packed[name] = [pk] + [pk.clone() for _ in range(P - 1)]
+        wsc[name] = ws
+        Y[name] = torch.empty((1, N), dtype=torch.float32, device=dev)
+    Xg = {}
+    for g in groups:
+        X = torch.from_numpy(d.X[(g[0], 1)]).to(dev)
+        Xg[g] = [X] + [X.clone() for _ in range(P - 1)]
+    torch.cuda.synchronize()
+    log("decode: pool of %d weight sets, %.0f MB" % (P, P * step_w_bytes / 1e6))
+
+    def decode_step(i):
+        j = i % P
+        for g in groups:
+            bl.forward_fused(Xg[g][j], [(packed[n][j], wsc[n], shapes[n][0]) for n in g],
+                             Ys=[Y[n] for n in g])
+
+    # correctness gate before timing: kernel choice and values vs the oracle
+    import oracle
+    decode_step(0)
+    torch.cuda.synchronize()
+    dispatch = bl.last_dispatch()
+    if not dispatch.startswith("fused_decode"):
+        raise SystemExit("unexpected kernel for the M=1 decode step: %s" % dispatch)
+    for name, (N, K) in shapes.items():
+        beta, w_eff, _ = oracle.quantize_weights(d.W[name])
+        q, xso, _ = oracle.quant_act(d.X[(name, 1)])
+        _, Yo = oracle.forward(q, xso, w_eff, beta)
+        Yg = Y[name].cpu().numpy().astype(np.float64)
+        if not np.all(np.abs(Yg - Yo) <= 1e-5 * np.abs(Yo)):
+            raise SystemExit("decode output of %s does not match the oracle" % name)
+
+    def group_bytes(g):
+        N0, K = shapes[g[0]]
+        return 4 * K + 4 + sum(shapes[n][0] * K // 4 + 4 + 4 * shapes[n][0] for n in g)
+    step_bytes = sum(group_bytes(g) for g in groups)
+
+    # warmup W steps, then exactly K steps, each captured as one graph
+    if args.warmup > 0:
+        timed_graph(torch, lambda: [decode_step(i) for i in range(args.warmup)])
+    torch.cuda.synchronize()
+    ms_total, _ = timed_graph(torch, lambda: [decode_step(i) for i in range(args.steps)])
+    ms_step = ms_total / args.steps
+    value_gbs = step_bytes / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel: the fused decode kernel; R launches over the rotating pool
+    R = len(groups) * P
+    ms_fused, _ = timed_graph(torch, lambda: [decode_step(i) for i in range(P)], reps=3)
+    fused_us = ms_fused * 1e3 / R
+    fused_gbs = step_bytes * P / (ms_fused * 1e-3) / 1e9
+    per_group = {}
+    for g in groups:
+        def one(g=g):
+            for j in range(P):
+                bl.forward_fused(Xg[g][j], [(packed[n][j], wsc[n], shapes[n][0]) for n in g],
+                                 Ys=[Y[n] for n in g])
+        ms, _ = timed_graph(torch, one, reps=3)
+        per_group["+".join(g)] = {"us": round(ms * 1e3 / P, 3),
+                                  "GB/s": round(group_bytes(g) / (ms * 1e-3 / P) / 1e9, 1)}
+
+    # context: the two-call path (quant_act, then forward per projection)
+    Xq1, xs1, rs1 = {}, {}, {}
+    for g in groups:
+        K = shapes[g[0]][1]
+        Xq1[g] = torch.empty((1, K), dtype=torch.int8, device=dev)
+        xs1[g] = torch.empty(1, dtype=torch.float32, device=dev)
+        rs1[g] = torch.empty(1, dtype=torch.int32, device=dev)
+
+    def two_call_step(i):
+        j = i % P
+        for g in groups:
+            bl.quant_act(Xg[g][j], Xq1[g], xs1[g], rs1[g])
+            for n in g:
+                bl.forward(Xq1[g], xs1[g], rs1[g], packed[n][j], wsc[n], shapes[n][0], Y=Y[n])
+    ms_two, _ = timed_graph(torch, lambda: [two_call_step(i) for i in range(P)], reps=2)
+    two_call_us = ms_two * 1e3 / P
+    single = {}
+    for name in ("up", "down"):
+        N, K = shapes[name]
+        g = [gg for gg in groups if name in gg][0]
+        def fw(name=name, N=N, g=g):
+            for j in range(P):
+                bl.forward(Xq1[g], xs1[g], rs1[g], packed[name][j], wsc[name], N, Y=Y[name])
+        ms, _ = timed_graph(torch, fw, reps=3)
+        fb = N * K // 4 + K + 12 + 4 * N
+        single["%dx%d" % (K, N)] = {"kernel": bl.last_dispatch(), "us": round(ms * 1e3 / P, 3),
+                                    "GB/s": round(fb / (ms * 1e-3 / P) / 1e9, 1)}
+
+    # ------------------------------------------------------------------ prefill
+    dp = workloads.draw("prefill_2048")
+    Wp = torch.from_numpy(dp.W["up"]).to(dev)
+    Xp = torch.from_numpy(dp.X[("up", 2048)]).to(dev)
+    Mp, Np_, Kp = 2048, 6912, 2560
+    pk_p, ws_p = bl.pack_weights(Wp)
+    Xq_p, xs_p, rs_p = bl.quant_act(Xp)
+    Y_p = torch.empty((Mp, Np_), dtype=torch.float32, device=dev)
+    bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, Np_, Y=Y_p)
+    torch.cuda.synchronize()
+    gemm_dispatch = bl.last_dispatch()
+    G = 20
+    ms_gemm, _ = timed_graph(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, Np_, Y=Y_p) for _ in range(G)], reps=2)
+    gemm_us = ms_gemm * 1e3 / G
+    gemm_tops = 2.0 * Mp * Np_ * Kp / (gemm_us * 1e-6) / 1e12
+    ms_qp, _ = timed_graph(torch, lambda: [bl.quant_act(Xp, Xq_p, xs_p, rs_p) for _ in range(G)], reps=2)
+    quant_p_us = ms_qp * 1e3 / G
+
+    # ------------------------------------------------------------------ traffic
+    traffic = None
+    digest = source_digest()
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            t = json.load(open(TRAFFIC_FILE))
+            if t.get("source_digest") == digest:
+                traffic = t.get("hbm_bytes_per_launch")
+        except (ValueError, OSError):
+            traffic = None
+
+    # ------------------------------------------------------------------ CPU oracle
+    cpu = None
+    if not args.no_cpu_baseline:
+        pre = {}
+        for name in shapes:
+            beta, w_eff, _ = oracle.quantize_weights(d.W[name])
+            pre[name] = (beta, w_eff)
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            for g in groups:
+                q, xso, _ = oracle.quant_act(d.X[(g[0], 1)])
+                for name in g:
+                    oracle.forward(q, xso, pre[name][1], pre[name][0])
+            n += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
+        cpu_s = (time.perf_counter() - t0) / n
+        cpu = {"value": round(step_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": "%d oracle decode steps (quantisation of the gate/up and down inputs, forward of "
+                         "gate, up, down at M=1, the same seeded inputs), %.1f s, single-threaded C on %s" % (
+                             n, n * cpu_s, platform.processor() or "host CPU"),
+               "ms_per_step": round(cpu_s * 1e3, 3)}
+
+    out = {
+        "metric": "BitLinear GB/s @M=1 and int8 TOPS @M=2048, as % of MI355X roofline",
+        "value": round(value_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8xternary->int32->fp32",
+        "data": "synthetic (seeded N(0,0.02) latent weights, N(0,1) activations with 0.1% x20 outliers)",
+        "config": {"workload": "decode_ffn_2b: M=1, gate/up 2560->6912 (shared input), down 6912->2560; "
+                               "per step one fused launch (int8 quantisation + projections) per input group; "
+                               "weights rotating over %d buffers (%.0f MB)" % (P, P * step_w_bytes / 1e6),
+                   "M": 1, "projections": ["gate 2560x6912", "up 2560x6912", "down 6912x2560"]},
+        "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(fused_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "fused_decode_kernel", "avg_launch_us": round(fused_us, 3),
+                     "bytes_per_launch": round(step_bytes / len(groups)), "per_group": per_group},
+        "decode_two_call_path": {"step_us": round(two_call_us, 3),
+                                 "GB/s": round(step_bytes / (two_call_us * 1e-6) / 1e9, 1),
+                                 "single_forward": single},
+        "gemm": {"workload": "prefill_2048: M=2048, K=2560, N=6912", "kernel": gemm_dispatch,
+                 "avg_launch_us": round(gemm_us, 2), "TOPS": round(gemm_tops, 1),
+                 "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
+                              "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4)},
+                 "quant_act_us": round(quant_p_us, 2)},
+        "cpu_baseline": cpu,
+        "source_digest": digest,
+    }
+    log("decode step %.2f us (%.1f GB/s); fused decode launch %.3f us avg (%.1f GB/s, %.1f%% of HBM); "
+        "two-call step %.2f us; GEMM %.1f us (%.1f TOPS, %.1f%% of int8 peak)" % (
+            ms_step * 1e3, value_gbs, fused_us, fused_gbs, 100 * fused_gbs / HBM_PEAK_GBS,
+            two_call_us, gemm_us, gemm_tops, 100 * gemm_tops / INT8_PEAK_TOPS))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     pack_weights,
     quant_act,
     forward,
+    forward_fused,
     last_dispatch,
     library_path,
     load_library,

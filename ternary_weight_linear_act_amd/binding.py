@@ -24,6 +24,7 @@ EXPORTED = (
     "bitlinear_pack_weights",
     "bitlinear_quant_act",
     "bitlinear_forward",
+    "bitlinear_forward_fused",
     "bitlinear_last_error",
     "bitlinear_last_dispatch",
 )
@@ -37,6 +38,11 @@ class BitLinearError(RuntimeError):
 
 class NM(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32)]
+
+
+class Proj(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("w_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
+                ("Y", ctypes.c_void_p), ("acc", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -62,8 +68,9 @@ def load_library():
     lib.bitlinear_pack_weights.argtypes = [vp, i64, i64, NM, vp, sz, vp, vp, sz, vp]
     lib.bitlinear_quant_act.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp]
+    lib.bitlinear_forward_fused.argtypes = [vp, i64, i64, NM, ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     for f in ("bitlinear_packed_size", "bitlinear_pack_weights", "bitlinear_quant_act",
-              "bitlinear_forward"):
+              "bitlinear_forward", "bitlinear_forward_fused"):
         getattr(lib, f).restype = ctypes.c_int
     lib.bitlinear_last_error.restype = ctypes.c_char_p
     lib.bitlinear_last_dispatch.restype = ctypes.c_char_p
@@ -189,3 +196,33 @@ def forward(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=None, acc=
         _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _ptr(packed), _ptr(w_scale), _nm(nm),
         M, N, K, _ptr(Y), _ptr(acc), _stream(stream)))
     return (Y, acc) if (want_acc or acc is not None) else Y
+
+
+def forward_fused(X, projs, nm=NM_DENSE, Ys=None, accs=None, want_acc=False, x_scale=None, stream=None):
+    """Quantise X (M x K fp32, M <= 4) and apply every projection in `projs`
+    -- a list of (packed, w_scale, N) sharing X -- in one launch.
+
+    Returns the list of Y tensors, or (Ys, accs) when accumulators are wanted.
+    """
+    import torch
+    _require(X, torch.float32, None, "X")
+    M, K = X.shape
+    n = len(projs)
+    if Ys is None:
+        Ys = [torch.empty((M, N), dtype=torch.float32, device=X.device) for (_, _, N) in projs]
+    if accs is None and want_acc:
+        accs = [torch.empty((M, N), dtype=torch.int32, device=X.device) for (_, _, N) in projs]
+    arr = (Proj * max(n, 1))()
+    for i, (packed, ws, N) in enumerate(projs):
+        _require(packed, torch.uint8, None, "packed")
+        _require(ws, torch.float32, (1,), "w_scale")
+        _require(Ys[i], torch.float32, (M, N), "Y")
+        if accs is not None:
+            _require(accs[i], torch.int32, (M, N), "acc")
+        arr[i] = Proj(packed.data_ptr(), ws.data_ptr(), N, Ys[i].data_ptr(),
+                      accs[i].data_ptr() if accs is not None else None)
+    if x_scale is not None:
+        _require(x_scale, torch.float32, (M,), "x_scale")
+    _check("bitlinear_forward_fused", load_library().bitlinear_forward_fused(
+        _ptr(X), M, K, _nm(nm), arr, n, _ptr(x_scale), _stream(stream)))
+    return (Ys, accs) if accs is not None else Ys

@@ -1,0 +1,123 @@
+// Host dispatch of the fused decode forward (activation quantisation + one or
+// more projections sharing the activations, one launch).  Configuration rule
+// as for the skinny kernel: ~10 chunks per wave, KS a power of two, smallest
+// CMAX that holds a wave's range, LDS within budget.
+#include <math.h>
+#include <stdio.h>
+
+#include "fused_impl.hpp"
+
+namespace bl {
+namespace {
+
+using Fn = hipError_t (*)(const float *, int64_t, int64_t, const FusedProjArgs &, int, float *, hipStream_t);
+
+constexpr int kKS[] = {1, 2, 4, 8, 16};
+constexpr int kCM[] = {4, 8, 12, 16, 24, 32, 44};
+constexpr int kNKS = sizeof(kKS) / sizeof(kKS[0]);
+constexpr int kNCM = sizeof(kCM) / sizeof(kCM[0]);
+constexpr int64_t kLds = 160 * 1024;
+constexpr int64_t kMaxDynLds = 64 * 1024;
+
+constexpr int64_t static_lds(int ks, int cmax, int mt)
+{
+    return (int64_t)ks * 16 * (cmax + 1) * 16 + 256 + (int64_t)mt * ks * 8 +
+           (int64_t)(ks > 1 ? ks - 1 : 1) * 64 * 16;
+}
+
+template <Pattern P, int KS, int CM, int MT>
+Fn get()
+{
+    if constexpr (static_lds(KS, CM, MT) <= kLds - 1024) return fused::launch_fused<P, KS, CM, MT>;
+    else return nullptr;
+}
+
+template <Pattern P, int MT, int KS>
+Fn pick_cm(int cmi)
+{
+    switch (cmi) {
+    case 0: return get<P, KS, 4, MT>();
+    case 1: return get<P, KS, 8, MT>();
+    case 2: return get<P, KS, 12, MT>();
+    case 3: return get<P, KS, 16, MT>();
+    case 4: return get<P, KS, 24, MT>();
+    case 5: return get<P, KS, 32, MT>();
+    default: return get<P, KS, 44, MT>();
+    }
+}
+
+template <Pattern P, int MT>
+Fn pick(int ksi, int cmi)
+{
+    switch (ksi) {
+    case 0: return pick_cm<P, MT, 1>(cmi);
+    case 1: return pick_cm<P, MT, 2>(cmi);
+    case 2: return pick_cm<P, MT, 4>(cmi);
+    case 3: return pick_cm<P, MT, 8>(cmi);
+    default: return pick_cm<P, MT, 16>(cmi);
+    }
+}
+
+template <Pattern P>
+Fn pick_p(int mt, int ksi, int cmi)
+{
+    return mt == 1 ? pick<P, 1>(ksi, cmi) : pick<P, 4>(ksi, cmi);
+}
+
+thread_local char g_name[64];
+
+}  // namespace
+
+// args.block_start is filled here.  hipErrorNotSupported: no configuration
+// fits (M > 4, too many projections, or K too large for the shared row).
+hipError_t launch_fused_forward(const float *X, int64_t M, int64_t K, Pattern p, FusedProjArgs args,
+                                float *x_scale, hipStream_t stream, const char **name)
+{
+    if (M < 1 || M > 4 || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
+    const int mt = (M == 1) ? 1 : 4;
+    if ((int64_t)mt * (K + 192) > kMaxDynLds) return hipErrorNotSupported;
+    int64_t blocks = 0;
+    for (int i = 0; i < args.nproj; ++i) {
+        args.block_start[i] = (int32_t)blocks;
+        blocks += (args.N[i] + 15) / 16;
+    }
+    for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
+    if (blocks > (1LL << 30)) return hipErrorNotSupported;
+
+    const int64_t C = K / 64;
+    const double want = log2((double)C / 10.0);
+    int order[kNKS];
+    for (int i = 0; i < kNKS; ++i) order[i] = i;
+    for (int i = 0; i < kNKS; ++i)
+        for (int j = i + 1; j < kNKS; ++j)
+            if (fabs(log2((double)kKS[order[j]]) - want) < fabs(log2((double)kKS[order[i]]) - want)) {
+                const int t = order[i];
+                order[i] = order[j];
+                order[j] = t;
+            }
+    for (int oi = 0; oi < kNKS; ++oi) {
+        const int ksi = order[oi], ks = kKS[ksi];
+        if (ks > C) continue;
+        const int64_t need = (C + ks - 1) / ks;
+        int cmi = -1;
+        for (int c = 0; c < kNCM; ++c)
+            if (kCM[c] >= need) { cmi = c; break; }
+        if (cmi < 0) continue;
+        if (static_lds(ks, kCM[cmi], mt) + (int64_t)mt * (K + 192) > kLds) continue;
+        Fn f = nullptr;
+        switch (p) {
+        case Pattern::Dense: f = pick_p<Pattern::Dense>(mt, ksi, cmi); break;
+        case Pattern::NM24: f = pick_p<Pattern::NM24>(mt, ksi, cmi); break;
+        case Pattern::NM68: f = pick_p<Pattern::NM68>(mt, ksi, cmi); break;
+        }
+        if (!f) continue;
+        snprintf(g_name, sizeof g_name, "fused_decode_%s_ks%d_c%d_mt%d_p%d",
+                 p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", ks, kCM[cmi], mt,
+                 args.nproj);
+        *name = g_name;
+        return f(X, M, K, args, (int)blocks, x_scale, stream);
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace bl

@@ -1,0 +1,280 @@
+// Fused decode forward: per-token absmax int8 quantisation of the fp32
+// activations plus the skinny MFMA contraction of one or more projections that
+// share those activations (q/k/v, or gate/up), all in one launch.
+//
+// Same arithmetic as the separate calls: "BitNet b1.58 2B4T Technical Report
+// 요약 설명", sec. 2 (per-token absmax 8-bit activations) and sec. 5.1 (packed
+// weights, unpacked on chip); "BitNet 논문 분석: 1-Bit LLM의 시대", section
+// "Absmean 양자화 함수" (activation_quant, integer linear, rescale).  The
+// quantised values, row sums and scales are bit-identical to
+// bitlinear_quant_act's, so the outputs equal the unfused path's bit for bit.
+//
+// Why fuse: a decode BitLinear moves a few MB, so on MI355X a launch's fixed
+// cost (dispatch, first HBM round trip, completion) is comparable to the
+// transfer itself.  Fusing the activation quantisation removes one launch per
+// projection group, and serving several projections in one grid removes the
+// rest.  Each workgroup recomputes max|x| over the whole activation row from
+// L2 (M x K x 4 bytes, M <= 4), which costs far less than a launch.
+//
+// Workgroup layout: it owns 16 rows of one projection; KS waves split K as in
+// the skinny kernel.  Order of work: (1) issue the wave's weight loads;
+// (2) all KS waves read the fp32 activation rows once, into registers, and
+// reduce max|x| per token through wave shuffles and LDS; (3) quantise the
+// registers to int8 into a block-shared LDS row and reduce the int32 row
+// sums; (4) stage the weights in LDS; (5) MFMA, reduce across waves,
+// epilogue.
+#pragma once
+
+#include "skinny_impl.hpp"
+
+namespace bl {
+
+constexpr int kMaxFusedProj = 8;
+
+struct FusedProjArgs {
+    const uint8_t *packed[kMaxFusedProj];
+    const float *w_scale[kMaxFusedProj];
+    float *Y[kMaxFusedProj];
+    int32_t *acc[kMaxFusedProj];
+    int64_t N[kMaxFusedProj];
+    int32_t block_start[kMaxFusedProj + 1];   // first workgroup of each projection
+    int32_t nproj;
+};
+
+namespace fused {
+
+using skinny::i32x4;
+using skinny::u32x4;
+using skinny::unpack_word;
+using skinny::load_chunk;
+
+template <int KS, int CMAX, int MT>
+struct FusedLds {
+    static constexpr int kStride = (CMAX + 1) * 16;          // weight row stride
+    static constexpr int kW = 16 * kStride;                   // per wave
+    static constexpr int kZero = 256;                         // zero block (token rows >= M)
+};
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ int quant1(float x, float s)
+{
+    float r = rintf(x * s);
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return (int)r;
+}
+
+// KS waves split K; at most CMAX chunks per wave; at most MT (<= 4) tokens;
+// the activation row (K bytes per token, plus 3 zero chunks) is shared in LDS
+// and sized at launch (dynamic LDS).
+template <Pattern P, int KS, int CMAX, int MT>
+__global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict__ X, int64_t M, int64_t K,
+                                                        FusedProjArgs args, float *__restrict__ x_scale_out)
+{
+    static_assert(CMAX % 4 == 0 && MT >= 1 && MT <= 4, "config");
+    using L = FusedLds<KS, CMAX, MT>;
+    constexpr int WLOADS = CMAX / 4;
+    constexpr int T = 64 * KS;
+    __shared__ __attribute__((aligned(16))) uint8_t s_w[KS][L::kW];
+    __shared__ __attribute__((aligned(16))) uint8_t s_zero[L::kZero];
+    __shared__ float s_max[MT][KS];
+    __shared__ int s_sum[MT][KS];
+    __shared__ i32x4 s_part[KS > 1 ? KS - 1 : 1][64];
+    extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];   // MT x (K + 192) int8
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int mt = (int)M;
+    const int64_t xstride = K + 192;
+
+    // which projection and which 16 rows
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxFusedProj; ++i)
+        if (i < args.nproj && (int)blockIdx.x >= args.block_start[i]) p = i;
+    const int64_t N = args.N[p];
+    const uint8_t *packed = args.packed[p];
+    const int64_t n0 = (int64_t)(blockIdx.x - args.block_start[p]) * 16;
+    const float beta = args.w_scale[p][0];
+
+    const int64_t C = K / 64;
+    const int64_t c_lo = C * wave / KS;
+    const int cw = (int)(C * (wave + 1) / KS - c_lo);
+    uint8_t *lw = s_w[wave];
+
+    // (1) weight loads of this wave, all in flight
+    u32x4 w[WLOADS];
+    int w_off[WLOADS];
+    const float inv_cw = 1.0f / (float)cw;
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i) {
+        const int f = i * 64 + lane;
+        const int row = (int)(((float)f + 0.5f) * inv_cw);
+        const int col = f - row * cw;
+        const int64_t n = min(n0 + row, N - 1);
+        w_off[i] = (row < 16) ? row * L::kStride + col * 16 : -1;
+        w[i] = load_chunk<P>(packed, N, K, n, c_lo + (row < 16 ? col : 0));
+    }
+
+    // (2) the fp32 activation rows, read once into registers (XR float4 per
+    //     thread per token covers K: K/4 = 16 C <= 16 KS CMAX = XR T), then
+    //     max |x| per token over the whole row
+    constexpr int XR = CMAX / 4;
+    const int64_t n4 = K / 4;
+    float4 xr[MT][XR];
+    float g[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(X + (int64_t)min(m, mt - 1) * K);
+#pragma unroll
+        for (int j = 0; j < XR; ++j) {
+            const int64_t i = tid + (int64_t)j * T;
+            const float4 a = x4[i < n4 ? i : 0];
+            xr[m][j] = (m < mt && i < n4) ? a : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float v = 0.0f;
+#pragma unroll
+        for (int j = 0; j < XR; ++j) {
+            const float4 a = xr[m][j];
+            v = fmaxf(v, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+        }
+        v = wave_max(v);
+        if (lane == 0) s_max[m][wave] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        float v = s_max[m][0];
+#pragma unroll
+        for (int k2 = 1; k2 < KS; ++k2) v = fmaxf(v, s_max[m][k2]);
+        g[m] = v;
+    }
+
+    // (3) quantise into LDS, row sums
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        int sum = 0;
+        if (m < mt) {
+            int *q4 = reinterpret_cast<int *>(s_x + m * xstride);
+            const bool zero = (g[m] == 0.0f);
+            const float s = zero ? 0.0f : 127.0f / g[m];
+#pragma unroll
+            for (int j = 0; j < XR; ++j) {
+                const int64_t i = tid + (int64_t)j * T;
+                if (i < n4) {
+                    const float4 a = xr[m][j];
+                    int qa = 0, qb = 0, qc = 0, qd = 0;
+                    if (!zero) { qa = quant1(a.x, s); qb = quant1(a.y, s); qc = quant1(a.z, s); qd = quant1(a.w, s); }
+                    sum += qa + qb + qc + qd;
+                    q4[i] = (qa & 0xFF) | ((qb & 0xFF) << 8) | ((qc & 0xFF) << 16) | ((qd & 0xFF) << 24);
+                }
+            }
+            // 3 zero chunks after the row
+            if (tid < 48) q4[n4 + tid] = 0;
+        }
+        sum = wave_sum(sum);
+        if (lane == 0) s_sum[m][wave] = sum;
+    }
+    if (tid < L::kZero / 16) reinterpret_cast<u32x4 *>(s_zero)[tid] = u32x4{0u, 0u, 0u, 0u};
+
+    // (4) weights to LDS
+#pragma unroll
+    for (int i = 0; i < WLOADS; ++i)
+        if (w_off[i] >= 0) *reinterpret_cast<u32x4 *>(lw + w_off[i]) = w[i];
+    __syncthreads();
+
+    int rs[4];
+    float xsc[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = 4 * q + v;
+        int tot = 0;
+        float gm = 0.0f;
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+            if (mm == m) {
+#pragma unroll
+                for (int k2 = 0; k2 < KS; ++k2) tot += s_sum[mm][k2];
+                gm = g[mm];
+            }
+        rs[v] = tot;
+        xsc[v] = (gm == 0.0f) ? 0.0f : gm / 127.0f;
+    }
+    if (x_scale_out && blockIdx.x == 0 && tid < mt) {
+        float gm = 0.0f;
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+            if (mm == tid) gm = g[mm];
+        x_scale_out[tid] = (gm == 0.0f) ? 0.0f : gm / 127.0f;
+    }
+
+    // (5) MFMA phase
+    const uint8_t *brow = lw + r * L::kStride + q * 16;
+    const uint8_t *arow = (r < mt) ? s_x + r * xstride + (c_lo + q) * 64 : s_zero;
+    const int astep = (r < mt) ? 256 : 0;
+    i32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = i32x4{0, 0, 0, 0};
+    const int steps = (cw + 3) / 4;
+    for (int s = 0; s < steps; ++s) {
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(brow + s * 64);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            // past this wave's range the activation bytes belong to the next
+            // wave's range or the zero tail: mask them with the column test
+            const i32x4 a0 = *reinterpret_cast<const i32x4 *>(arow + s * astep + 16 * t);
+            const i32x4 a = (4 * s + q < cw) ? a0 : i32x4{0, 0, 0, 0};
+            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_word(b[t]), acc[t], 0, 0, 0);
+        }
+    }
+    i32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    if (KS > 1) {
+        if (wave > 0) s_part[wave - 1][lane] = sum;
+        __syncthreads();
+        if (wave != 0) return;
+#pragma unroll
+        for (int w2 = 1; w2 < KS; ++w2) sum += s_part[w2 - 1][lane];
+    }
+
+    const int64_t nn = n0 + r;
+    if (nn >= N) return;
+    float *Y = args.Y[p];
+    int32_t *acc_out = args.acc[p];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = 4 * q + v;
+        if (m < mt) {
+            const int av = sum[v] - rs[v];
+            Y[(int64_t)m * N + nn] = (float)av * (beta * xsc[v]);
+            if (acc_out) acc_out[(int64_t)m * N + nn] = av;
+        }
+    }
+}
+
+template <Pattern P, int KS, int CMAX, int MT>
+hipError_t launch_fused(const float *X, int64_t M, int64_t K, const FusedProjArgs &args, int blocks,
+                        float *x_scale, hipStream_t stream)
+{
+    const size_t dyn = (size_t)MT * (size_t)(K + 192);
+    hipLaunchKernelGGL((fused_kernel<P, KS, CMAX, MT>), dim3((unsigned)blocks), dim3(64 * KS), dyn, stream, X, M,
+                       K, args, x_scale);
+    return hipGetLastError();
+}
+
+}  // namespace fused
+}  // namespace bl

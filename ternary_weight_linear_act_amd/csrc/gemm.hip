@@ -1,0 +1,299 @@
+// Prefill GEMM on int8 MFMA: Y[m, n] = (sum_k Xq[m, k] * W_eff[n, k]) * beta * x_scale[m].
+//
+// "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 5.1: the GPU kernel
+// brings the packed weights (four ternary per byte) from HBM into on-chip
+// shared memory, unpacks them there and computes against 8-bit activations.
+// With many tokens the contraction is dense, so on gfx950 it runs on
+// v_mfma_i32_32x32x32_i8.
+//
+// Tiling: a workgroup owns a BM x BN output tile and walks K in 64-wide
+// slices.  The activation tile (BM x 64 int8) and the *packed* weight tile
+// (BN x 16 bytes) are staged in LDS, double-buffered: the global loads of
+// slice i+1 are issued before the MFMAs of slice i and written to the other
+// buffer afterwards, so there is one barrier per slice.  Each wave unpacks its
+// weight fragments in registers right before the MFMA ((word >> 2s) &
+// 0x03030303 gives four codes per 32-bit lane value, already in the byte order
+// the B operand wants) -- LDS holds 2 bits per weight, not 8.  Codes are
+// c = t + 1, so the int32 accumulators hold sum c*q and the fused epilogue
+// subtracts the activation row sum before the dequant scale.
+//
+// LDS layouts are padded so MFMA-side reads are conflict-free: activation
+// rows 80 bytes apart (16 consecutive rows start in 16 distinct 4-bank
+// groups), packed weight rows 24 bytes apart (32 consecutive rows read 8-byte
+// pairs from 32 distinct bank pairs).
+//
+// MFMA operand mapping (same for A and B, so any k permutation is harmless):
+// lane l, half h = l / 32, k-step s in {0, 1} of a 64-wide slice holds the
+// 16 consecutive k = 32 h + 16 s + (0..15); A row / B column = l % 32.
+// Output: lane l holds column l % 32 and rows 8 (v / 4) + 4 h + (v % 4).
+//
+// Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
+// consecutive logical tiles (which share a weight column tile) are mapped to
+// workgroups on the same XCD and reuse its L2.
+#include "kernels.hpp"
+
+namespace bl {
+namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int BK = 64;
+constexpr int LDA = BK + 16;      // bytes per staged activation row
+constexpr int LDB = 24;           // bytes per staged packed weight row (16 used)
+constexpr int kXcds = 8;
+
+// Raw packed words of weight row n for the K slice starting at k0: dense = 4
+// code words; N:M = the superblock's value words then its 2 mask words.
+template <Pattern P>
+struct RawSlice {
+    static constexpr int kWords = (P == Pattern::Dense) ? 4 : (P == Pattern::NM24 ? 2 : 3) + 2;
+    uint32_t w[kWords];
+};
+
+template <Pattern P>
+__device__ __forceinline__ void load_raw(const uint8_t *__restrict__ packed, int64_t N, int64_t K, int64_t n,
+                                         int64_t k0, RawSlice<P> &r)
+{
+    if (P == Pattern::Dense) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(packed + n * (K / 4) + k0 / 4);
+        r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
+    } else {
+        constexpr int GM = (P == Pattern::NM24) ? 4 : 8;
+        constexpr int GN = (P == Pattern::NM24) ? 2 : 6;
+        constexpr int VW = 64 * GN / GM / 16;
+        const int64_t vrow = nm_value_row_bytes(K, GN, GM);
+        const int64_t sb = k0 / 64;
+        const uint32_t *vp = reinterpret_cast<const uint32_t *>(packed + n * vrow + sb * (VW * 4));
+        const uint32_t *mp = reinterpret_cast<const uint32_t *>(packed + N * vrow + n * (K / 8) + sb * 8);
+#pragma unroll
+        for (int v = 0; v < VW; ++v) r.w[v] = vp[v];
+        r.w[VW] = mp[0];
+        r.w[VW + 1] = mp[1];
+    }
+}
+
+// 4 dense code words from a raw slice (N:M: decode the superblock)
+template <Pattern P>
+__device__ __forceinline__ u32x4 dense_words(const RawSlice<P> &r)
+{
+    if (P == Pattern::Dense) {
+        return u32x4{r.w[0], r.w[1], r.w[2], r.w[3]};
+    } else {
+        constexpr int VW = RawSlice<P>::kWords - 2;
+        uint32_t w[4];
+        decode_superblock<P>(r.w, r.w + VW, w);
+        return u32x4{w[0], w[1], w[2], w[3]};
+    }
+}
+
+__device__ __forceinline__ i32x4 unpack_word(uint32_t w)
+{
+    i32x4 b;
+    b[0] = (int)(w & kCodeMask);
+    b[1] = (int)((w >> 2) & kCodeMask);
+    b[2] = (int)((w >> 4) & kCodeMask);
+    b[3] = (int)((w >> 6) & kCodeMask);
+    return b;
+}
+
+// BM x BN tile, WM x WN waves, each wave (BM/WM) x (BN/WN) of 32x32 fragments.
+template <Pattern P, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
+    const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
+    const uint8_t *__restrict__ packed, const float *__restrict__ w_scale, int64_t M, int64_t N,
+    int64_t K, float *__restrict__ Y, int32_t *__restrict__ acc_out)
+{
+    constexpr int T = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
+    constexpr int FM = TM / 32, FN = TN / 32;          // 32x32 fragments per wave
+    static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "tile");
+    constexpr int A_PIECES = BM * 4;                   // 16-byte pieces of an activation slice
+    constexpr int A_PER_T = (A_PIECES + T - 1) / T;
+    constexpr int B_PER_T = (BN + T - 1) / T;          // packed rows (16 bytes) per thread
+    __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * LDA];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LDB];
+    __shared__ int s_rs[BM];
+    __shared__ float s_sc[BM];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int h = lane >> 5, li = lane & 31;
+
+    const int64_t tiles_m = (M + BM - 1) / BM;
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles = tiles_m * tiles_n;
+    // XCD-aware order: logical tile = xcd * per_xcd + index within the XCD
+    const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+    const int64_t b = blockIdx.x;
+    const int64_t tile = (b % kXcds) * per_xcd + b / kXcds;
+    if (tile >= tiles) return;
+    // consecutive logical tiles walk M first, so they share a weight column tile
+    const int64_t m0 = (tile % tiles_m) * BM;
+    const int64_t n0 = (tile / tiles_m) * BN;
+    const float beta = w_scale[0];
+
+    for (int i = tid; i < BM; i += T) {
+        const int64_t m = min(m0 + i, M - 1);
+        s_rs[i] = x_rowsum[m];
+        s_sc[i] = beta * x_scale[m];
+    }
+
+    // global -> register staging of one K slice
+    u32x4 ra[A_PER_T];
+    RawSlice<P> rb[B_PER_T];
+    auto load_slice = [&](int64_t k0) {
+#pragma unroll
+        for (int p = 0; p < A_PER_T; ++p) {
+            const int idx = p * T + tid;
+            const int row = idx >> 2, c = idx & 3;
+            const int64_t m = min(m0 + row, M - 1);        // rows >= M: any finite data, never stored
+            ra[p] = *reinterpret_cast<const u32x4 *>(Xq + m * K + k0 + 16 * c);
+        }
+#pragma unroll
+        for (int p = 0; p < B_PER_T; ++p) {
+            const int row = p * T + tid;
+            if (BN % T == 0 || row < BN) {                 // whole waves
+                const int64_t n = min(n0 + row, N - 1);
+                load_raw<P>(packed, N, K, n, k0, rb[p]);
+            }
+        }
+    };
+    auto store_slice = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < A_PER_T; ++p) {
+            const int idx = p * T + tid;
+            if (A_PIECES % T == 0 || idx < A_PIECES) {
+                const int row = idx >> 2, c = idx & 3;
+                *reinterpret_cast<u32x4 *>(sA[buf] + row * LDA + 16 * c) = ra[p];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < B_PER_T; ++p) {
+            const int row = p * T + tid;
+            if (BN % T == 0 || row < BN) {
+                const u32x4 d = dense_words<P>(rb[p]);
+                u32x2 *dst = reinterpret_cast<u32x2 *>(sB[buf] + row * LDB);
+                dst[0] = u32x2{d[0], d[1]};
+                dst[1] = u32x2{d[2], d[3]};
+            }
+        }
+    };
+
+    i32x16 acc[FM][FN];
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int c = 0; c < FN; ++c)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[a][c][v] = 0;
+
+    const int64_t slices = K / BK;
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+
+    for (int64_t it = 0; it < slices; ++it) {
+        const int buf = (int)(it & 1);
+        if (it + 1 < slices) load_slice((it + 1) * BK);
+
+        // B fragments: words 2h and 2h+1 of each row (k-steps s = 0, 1)
+        u32x2 bw[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            bw[fn] = *reinterpret_cast<const u32x2 *>(sB[buf] + (wn * TN + fn * 32 + li) * LDB + 8 * h);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            i32x4 a[FM], bb[FN];
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+                a[fm] = *reinterpret_cast<const i32x4 *>(sA[buf] + (wm * TM + fm * 32 + li) * LDA + 32 * h + 16 * s);
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) bb[fn] = unpack_word(bw[fn][s]);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[fm], bb[fn], acc[fm][fn], 0, 0, 0);
+        }
+
+        if (it + 1 < slices) store_slice(buf ^ 1);
+        __syncthreads();
+    }
+
+    // fused epilogue: offset-code correction and dequant scale
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int lr = wm * TM + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const int64_t m = m0 + lr;
+            if (m >= M) continue;
+            const int rs = s_rs[lr];
+            const float sc = s_sc[lr];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int64_t n = n0 + wn * TN + fn * 32 + li;
+                if (n < N) {
+                    const int av = acc[fm][fn][v] - rs;
+                    Y[m * N + n] = (float)av * sc;
+                    if (acc_out) acc_out[m * N + n] = av;
+                }
+            }
+        }
+    }
+}
+
+template <Pattern P, int BM, int BN, int WM, int WN>
+hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                  const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                  hipStream_t stream)
+{
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+    const int64_t grid = per_xcd * kXcds;
+    hipLaunchKernelGGL((gemm_kernel<P, BM, BN, WM, WN>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream,
+                       Xq, xs, rs, packed, w_scale, M, N, K, Y, acc);
+    return hipGetLastError();
+}
+
+template <Pattern P>
+hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                    const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                    hipStream_t stream, const char **name)
+{
+    static const char *names[3][3] = {
+        {"gemm_dense_256x256", "gemm_dense_128x128", "gemm_dense_64x128"},
+        {"gemm_nm24_256x256", "gemm_nm24_128x128", "gemm_nm24_64x128"},
+        {"gemm_nm68_256x256", "gemm_nm68_128x128", "gemm_nm68_64x128"}};
+    const int pi = (int)P;
+    auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
+    if (M >= 256 && tiles(256, 256) >= 128) {
+        *name = names[pi][0];
+        return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+    }
+    if (M > 64) {
+        *name = names[pi][1];
+        return launch<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+    }
+    *name = names[pi][2];
+    return launch<P, 64, 128, 1, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                       const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
+                       int32_t *acc, hipStream_t stream, const char **name)
+{
+    switch (p) {
+    case Pattern::Dense: return dispatch<Pattern::Dense>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name);
+    case Pattern::NM24: return dispatch<Pattern::NM24>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name);
+    case Pattern::NM68: return dispatch<Pattern::NM68>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace bl

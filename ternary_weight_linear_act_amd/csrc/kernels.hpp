@@ -1,0 +1,27 @@
+// Host-side launchers of the HIP kernels (internal to libbitlinear).
+// Shapes and pointers are validated by the C-ABI layer before these run.
+#pragma once
+
+#include "common.hpp"
+
+namespace bl {
+
+// Per-row absmax int8 quantisation (one workgroup per row).
+hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
+                            int32_t *x_rowsum, hipStream_t stream);
+
+// beta: per-row binary64 |W| sums into `rowsum`, then one ordered sum.
+hipError_t launch_absmean(const float *W, int64_t N, int64_t K, double *rowsum, float *w_scale,
+                          hipStream_t stream);
+
+// Ternarise (with d = beta + 1e-5 read from w_scale) and pack.
+hipError_t launch_pack(const float *W, int64_t N, int64_t K, Pattern p, const float *w_scale,
+                       uint8_t *packed, hipStream_t stream);
+
+// Forward.  Returns the name of the kernel variant in *name.
+hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
+                          const uint8_t *packed, const float *w_scale, Pattern p, int64_t M,
+                          int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream,
+                          const char **name);
+
+}  // namespace bl

@@ -1,0 +1,101 @@
+// Per-token absmax int8 activation quantisation.
+//
+// "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 2 Architecture: each
+// token's activations become 8-bit integers scaled by that token's absolute
+// maximum; "BitNet 논문 분석: 1-Bit LLM의 시대", section "Absmean 양자화 함수"
+// (activation_quant): round, then clamp to the int8 range.  Scale 127/max|x|
+// computed once per row, then multiplied in; round half to even.
+//
+// One workgroup per row.  Pass 1 reads the row with 16-byte loads and reduces
+// |x| to the row maximum (exact, order-free) through wave shuffles and LDS.
+// Pass 2 re-reads the row (L2-resident), quantises, stores four int8 per
+// 32-bit store and reduces the int32 row sum the forward kernels need.
+#include "kernels.hpp"
+
+namespace bl {
+namespace {
+
+constexpr int kQuantBlock = 256;
+constexpr int kWaves = kQuantBlock / 64;
+
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ int wave_sum(int v)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+__device__ __forceinline__ int quant1(float x, float s)
+{
+    float r = rintf(x * s);
+    r = fminf(fmaxf(r, -128.0f), 127.0f);
+    return (int)r;
+}
+
+__global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
+    const float *__restrict__ X, int64_t K, int8_t *__restrict__ Xq,
+    float *__restrict__ x_scale, int32_t *__restrict__ x_rowsum)
+{
+    __shared__ float s_max[kWaves];
+    __shared__ int s_sum[kWaves];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float4 *x4 = reinterpret_cast<const float4 *>(X + row * K);
+    int *q4 = reinterpret_cast<int *>(Xq + row * K);
+    const int64_t n4 = K / 4;
+
+    float g = 0.0f;
+    for (int64_t i = tid; i < n4; i += kQuantBlock) {
+        const float4 v = x4[i];
+        g = fmaxf(g, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    g = wave_max(g);
+    if (lane == 0) s_max[wave] = g;
+    __syncthreads();
+    g = s_max[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) g = fmaxf(g, s_max[w]);
+
+    int sum = 0;
+    if (g == 0.0f) {
+        for (int64_t i = tid; i < n4; i += kQuantBlock) q4[i] = 0;
+    } else {
+        const float s = 127.0f / g;          // IEEE binary32 division
+        for (int64_t i = tid; i < n4; i += kQuantBlock) {
+            const float4 v = x4[i];
+            const int a = quant1(v.x, s), b = quant1(v.y, s), c = quant1(v.z, s), d = quant1(v.w, s);
+            sum += a + b + c + d;
+            q4[i] = (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((d & 0xFF) << 24);
+        }
+    }
+    sum = wave_sum(sum);
+    if (lane == 0) s_sum[wave] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) total += s_sum[w];
+        x_scale[row] = (g == 0.0f) ? 0.0f : g / 127.0f;
+        if (x_rowsum) x_rowsum[row] = total;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
+                            int32_t *x_rowsum, hipStream_t stream)
+{
+    if (M == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)M), dim3(kQuantBlock), 0, stream, X, K, Xq,
+                       x_scale, x_rowsum);
+    return hipGetLastError();
+}
+
+}  // namespace bl

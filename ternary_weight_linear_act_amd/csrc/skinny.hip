@@ -1,0 +1,118 @@
+// Dispatch of the skinny (1 <= M <= 16) MFMA forward: picks how many waves
+// split K (KS) and the per-wave chunk capacity (CMAX) from the shape.
+//
+// Rule (from sweeps on MI355X over the decode shapes 2560->6912, 6912->2560,
+// 1536->8960, 2048->{256,2048,11008}, 11008->2048): about 10 chunks (640
+// weights) per wave, KS a power of two, the smallest CMAX that holds a wave's
+// range, and the first candidate whose LDS staging fits 160 KB.
+#include <math.h>
+#include <stdio.h>
+
+#include "skinny_impl.hpp"
+
+namespace bl {
+namespace {
+
+using Fn = hipError_t (*)(const int8_t *, const float *, const int32_t *, const uint8_t *, const float *,
+                          int64_t, int64_t, int64_t, float *, int32_t *, hipStream_t);
+
+constexpr int kKS[] = {1, 2, 4, 8, 16};
+constexpr int kCM[] = {4, 8, 12, 16, 24, 32, 44};
+constexpr int kNKS = sizeof(kKS) / sizeof(kKS[0]);
+constexpr int kNCM = sizeof(kCM) / sizeof(kCM[0]);
+
+constexpr int64_t lds_bytes_c(int ks, int cmax, int mt)
+{
+    return ks * (16LL * (8 * ((cmax + 7) / 8) + 1) * 16 + (int64_t)mt * (cmax + 3) * 64 + 64) +
+           (int64_t)(ks > 1 ? ks - 1 : 1) * 64 * 16;
+}
+
+// a configuration whose staging does not fit the 160 KB of LDS is never built
+template <Pattern P, int KS, int CM, int MT>
+Fn get()
+{
+    if constexpr (lds_bytes_c(KS, CM, MT) <= 160 * 1024) return skinny::launch_skinny<P, KS, CM, MT>;
+    else return nullptr;
+}
+
+template <Pattern P, int MT, int KS>
+Fn pick_cm(int cmi)
+{
+    switch (cmi) {
+    case 0: return get<P, KS, 4, MT>();
+    case 1: return get<P, KS, 8, MT>();
+    case 2: return get<P, KS, 12, MT>();
+    case 3: return get<P, KS, 16, MT>();
+    case 4: return get<P, KS, 24, MT>();
+    case 5: return get<P, KS, 32, MT>();
+    default: return get<P, KS, 44, MT>();
+    }
+}
+
+template <Pattern P, int MT>
+Fn pick(int ksi, int cmi)
+{
+    switch (ksi) {
+    case 0: return pick_cm<P, MT, 1>(cmi);
+    case 1: return pick_cm<P, MT, 2>(cmi);
+    case 2: return pick_cm<P, MT, 4>(cmi);
+    case 3: return pick_cm<P, MT, 8>(cmi);
+    default: return pick_cm<P, MT, 16>(cmi);
+    }
+}
+
+template <Pattern P>
+Fn pick_p(int mt, int ksi, int cmi)
+{
+    return mt == 1 ? pick<P, 1>(ksi, cmi) : pick<P, 16>(ksi, cmi);
+}
+
+thread_local char g_name[64];
+
+}  // namespace
+
+// Returns hipErrorNotSupported (and launches nothing) when no configuration
+// fits the shape; the caller then uses another kernel.
+hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                                 const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
+                                 int32_t *acc, hipStream_t stream, const char **name)
+{
+    if (M < 1 || M > 16) return hipErrorNotSupported;
+    const int mt = (M == 1) ? 1 : 16;
+    const int64_t C = K / 64;
+    // candidates ordered by distance (in log2) from ~10 chunks per wave
+    const double want = log2((double)C / 10.0);
+    int order[kNKS];
+    for (int i = 0; i < kNKS; ++i) order[i] = i;
+    for (int i = 0; i < kNKS; ++i)
+        for (int j = i + 1; j < kNKS; ++j)
+            if (fabs(log2((double)kKS[order[j]]) - want) < fabs(log2((double)kKS[order[i]]) - want)) {
+                const int t = order[i];
+                order[i] = order[j];
+                order[j] = t;
+            }
+    for (int oi = 0; oi < kNKS; ++oi) {
+        const int ksi = order[oi], ks = kKS[ksi];
+        if (ks > C) continue;
+        const int64_t need = (C + ks - 1) / ks;
+        int cmi = -1;
+        for (int c = 0; c < kNCM; ++c)
+            if (kCM[c] >= need) { cmi = c; break; }
+        if (cmi < 0) continue;
+        if (lds_bytes_c(ks, kCM[cmi], mt) > 160 * 1024) continue;
+        Fn f = nullptr;
+        switch (p) {
+        case Pattern::Dense: f = pick_p<Pattern::Dense>(mt, ksi, cmi); break;
+        case Pattern::NM24: f = pick_p<Pattern::NM24>(mt, ksi, cmi); break;
+        case Pattern::NM68: f = pick_p<Pattern::NM68>(mt, ksi, cmi); break;
+        }
+        if (!f) continue;
+        snprintf(g_name, sizeof g_name, "skinny_mfma_%s_ks%d_c%d_mt%d",
+                 p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", ks, kCM[cmi], mt);
+        *name = g_name;
+        return f(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+    }
+    return hipErrorNotSupported;
+}
+
+}  // namespace bl

@@ -40,6 +40,7 @@ class Workload:
     outlier_frac: float = 0.0    # fraction of activation entries scaled by outlier_mul
     outlier_mul: float = 20.0
     notes: str = ""
+    groups: tuple = ()           # projections that read the same activations (q/k/v, gate/up)
 
 
 WORKLOADS = {
@@ -52,7 +53,8 @@ WORKLOADS = {
         "decode_ffn_2b", 1,
         (Proj("gate", 2560, 6912), Proj("up", 2560, 6912), Proj("down", 6912, 2560)),
         (1,), outlier_frac=0.001,
-        notes="decode GEMV at 2B-class FFN shapes, 0.1% activation outliers x20"),
+        notes="decode GEMV at 2B-class FFN shapes, 0.1% activation outliers x20",
+        groups=(("gate", "up"), ("down",))),
     # prefill GEMM M = 2048, K = 2560, N = 6912
     "prefill_2048": Workload(
         "prefill_2048", 2, (Proj("up", 2560, 6912),), (2048,),
@@ -71,7 +73,8 @@ WORKLOADS = {
          Proj("o", 2048, 2048), Proj("gate", 2048, 11008), Proj("up", 2048, 11008),
          Proj("down", 11008, 2048)),
         (1, 8, 64),
-        notes="batched decode sweep over the seven projections of one 3B-class block"),
+        notes="batched decode sweep over the seven projections of one 3B-class block",
+        groups=(("q", "k", "v"), ("o",), ("gate", "up"), ("down",))),
 }
 
 
@@ -97,8 +100,17 @@ class Drawn:
     X: dict = field(default_factory=dict)     # (proj name, M) -> M x K fp32
 
 
+def input_groups(wl: Workload):
+    """Groups of projections sharing one activation input, in listed order."""
+    if wl.groups:
+        return [tuple(g) for g in wl.groups]
+    return [(p.name,) for p in wl.projs]
+
+
 def draw(name: str, projs=None, Ms=None) -> Drawn:
-    """Draw every weight (in listed order) then every activation (proj-major, then M).
+    """Draw every weight (in listed order), then one activation matrix per
+    input group and token count (group-major, then M).  Projections of a group
+    (q/k/v, gate/up) share the same activation array.
 
     ``projs``/``Ms`` restrict what is returned, but the generator still walks the
     full order so a subset gets the same values as the full draw.
@@ -110,11 +122,14 @@ def draw(name: str, projs=None, Ms=None) -> Drawn:
         w = normal_f32(rng, (p.N, p.K), WEIGHT_SIGMA)
         if projs is None or p.name in projs:
             out.W[p.name] = w
-    for p in wl.projs:
+    K_of = {p.name: p.K for p in wl.projs}
+    for group in input_groups(wl):
+        K = K_of[group[0]]
         for M in wl.Ms:
-            x = activations(rng, M, p.K, wl.outlier_frac, wl.outlier_mul)
-            if (projs is None or p.name in projs) and (Ms is None or M in Ms):
-                out.X[(p.name, M)] = x
+            x = activations(rng, M, K, wl.outlier_frac, wl.outlier_mul)
+            for pname in group:
+                if (projs is None or pname in projs) and (Ms is None or M in Ms):
+                    out.X[(pname, M)] = x
     return out
 
 

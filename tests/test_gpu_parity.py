@@ -1,0 +1,158 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: packed bytes, beta, Xq, x_scale, row sums and the int32
+accumulators.  fp32 Y: within 1e-5 relative of the oracle's binary64 value,
+and exactly 0 where the accumulator is 0.  Every input is seeded and
+synthetic (ternary_weight_linear_act_amd.workloads).
+"""
+import numpy as np
+import pytest
+
+from ternary_weight_linear_act_amd import workloads
+
+from gpu_helpers import full_check, hip_forward, hip_pack, hip_quant, sample_rows, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+# ---------------------------------------------------------------------------
+# the five workloads at their real shapes
+# ---------------------------------------------------------------------------
+def test_single_1024_all_tokens():
+    d = workloads.draw("single_1024")
+    for M in (1, 16):
+        full_check(d.W["linear"], d.X[("linear", M)], label="single_1024")
+
+
+@pytest.mark.parametrize("proj", ["gate", "up", "down"])
+def test_decode_ffn_2b(proj):
+    d = workloads.draw("decode_ffn_2b", projs=[proj])
+    full_check(d.W[proj], d.X[(proj, 1)], label="decode_ffn_2b/" + proj)
+
+
+def test_prefill_2048_sampled_rows():
+    d = workloads.draw("prefill_2048")
+    full_check(d.W["up"], d.X[("up", 2048)], rows=sample_rows(2048, 16), label="prefill_2048")
+
+
+@pytest.mark.parametrize("proj,nm", [("dense", (0, 0)), ("nm24", (2, 4)), ("nm68", (6, 8))])
+def test_sparse_ffn_1p5b(proj, nm):
+    d = workloads.draw("sparse_ffn_1p5b", projs=[proj])
+    full_check(d.W[proj], d.X[(proj, 1)], nm, label="sparse_ffn_1p5b/%s/M1" % proj)
+    full_check(d.W[proj], d.X[(proj, 512)], nm, rows=sample_rows(512, 16, seed=1),
+               label="sparse_ffn_1p5b/%s/M512" % proj)
+
+
+@pytest.mark.parametrize("proj", ["q", "k", "v", "o", "gate", "up", "down"])
+def test_block_3b(proj):
+    d = workloads.draw("block_3b", projs=[proj])
+    for M in (1, 8, 64):
+        full_check(d.W[proj], d.X[(proj, M)], rows=sample_rows(M, 24), label="block_3b/%s/M%d" % (proj, M))
+
+
+# ---------------------------------------------------------------------------
+# edge cases: ragged tiles, thresholds between kernels, extremes
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [
+    (1, 1, 64), (1, 37, 192), (2, 129, 320), (3, 200, 704), (4, 255, 1024),
+    (5, 33, 128), (7, 130, 256), (17, 257, 384), (31, 64, 576), (33, 100, 640),
+    (127, 129, 1088), (129, 300, 448), (200, 513, 64), (255, 31, 2048),
+])
+@pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
+def test_ragged_shapes(M, N, K, nm):
+    W, X = workloads.small_case(1000 + M * 7 + N, M, N, K, outlier_frac=0.01)
+    full_check(W, X, nm, label="ragged")
+
+
+def test_zero_rows_and_zero_weights():
+    W, X = workloads.small_case(5, 9, 70, 256)
+    X[2] = 0.0
+    X[7] = 0.0
+    W[3] = 0.0
+    W[10, :128] = 0.0
+    full_check(W, X, label="zeros")
+
+
+def test_all_zero_weight_matrix():
+    W = np.zeros((64, 128), np.float32)   # beta = 0, d = 1e-5: every weight ternarises to 0
+    _, X = workloads.small_case(6, 5, 64, 128)
+    out = full_check(W, X, label="zero-matrix")
+    assert not out["acc"].cpu().numpy().any()
+
+
+def test_extreme_accumulators():
+    # q = -127 (all equal) against t = -1 everywhere: acc = 127 * K at K = 11008
+    K = 11008
+    X = np.full((2, K), -1.0, np.float32)
+    W = np.full((8, K), -0.02, np.float32)
+    out = full_check(W, X, label="extreme")
+    assert (out["acc"].cpu().numpy() == 127 * K).all()
+
+
+def test_ties_in_ternarisation_and_masks():
+    # weights on exact multiples of a power of two: many |W| ties inside N:M
+    # groups and many quotients near the rounding boundaries
+    rng = np.random.default_rng(77)
+    W = (rng.integers(-3, 4, size=(96, 256)) * 2.0 ** -7).astype(np.float32)
+    _, X = workloads.small_case(78, 6, 96, 256)
+    for nm in [(0, 0), (2, 4), (6, 8)]:
+        full_check(W, X, nm, label="ties")
+
+
+def test_m_zero_is_noop():
+    import torch
+    import ternary_weight_linear_act_amd as bl
+    W, _ = workloads.small_case(9, 1, 64, 128)
+    packed, ws = hip_pack(W, (0, 0))
+    Xq = torch.empty((0, 128), dtype=torch.int8, device="cuda")
+    xs = torch.empty(0, dtype=torch.float32, device="cuda")
+    rs = torch.empty(0, dtype=torch.int32, device="cuda")
+    Y = bl.forward(Xq, xs, rs, packed, ws, 64)
+    torch.cuda.synchronize()
+    assert Y.shape == (0, 64)
+    assert bl.last_dispatch() == "none"
+
+
+def test_deterministic_and_dispatch():
+    import torch
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(10, 300, 384, 512)
+    packed, ws = hip_pack(W, (0, 0))
+    for M, expect in [(1, "skinny"), (4, "skinny"), (16, "skinny"), (17, "gemm"), (300, "gemm")]:
+        Xq, xs, rs = hip_quant(X[:M])
+        Y1, a1 = hip_forward(Xq, xs, rs, packed, ws, 384, (0, 0))
+        name = bl.last_dispatch()
+        Y2, a2 = hip_forward(Xq, xs, rs, packed, ws, 384, (0, 0))
+        torch.cuda.synchronize()
+        assert name.startswith(expect), name
+        assert torch.equal(a1, a2)
+        assert torch.equal(Y1.view(torch.int32), Y2.view(torch.int32))
+
+
+def test_forward_without_acc_matches():
+    import torch
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(11, 70, 256, 256)
+    packed, ws = hip_pack(W, (0, 0))
+    Xq, xs, rs = hip_quant(X)
+    Y1, _ = hip_forward(Xq, xs, rs, packed, ws, 256, (0, 0))
+    Y2 = bl.forward(Xq, xs, rs, packed, ws, 256, (0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2)
+
+
+def test_stream_argument():
+    import torch
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(12, 8, 512, 256)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        packed, ws = bl.pack_weights(to_dev(W))
+        Xq, xs, rs = bl.quant_act(to_dev(X))
+        Y, acc = bl.forward(Xq, xs, rs, packed, ws, 512, want_acc=True)
+    s.synchronize()
+    import oracle
+    beta, w_eff, _ = oracle.quantize_weights(W)
+    q, xs_o, _ = oracle.quant_act(X)
+    acc_o, _ = oracle.forward(q, xs_o, w_eff, beta)
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
