@@ -30,6 +30,8 @@
 // Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
 // consecutive logical tiles (which share a weight column tile) are mapped to
 // workgroups on the same XCD and reuse its L2.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace bl {
@@ -99,6 +101,61 @@ __device__ __forceinline__ i32x4 unpack_word(uint32_t w)
     return b;
 }
 
+// Fused epilogue of one wave's FM x FN 32x32 fragments: acc - rowsum, times
+// beta * x_scale, to Y (and acc_out).  Full tiles (the common case) take a
+// branch-free path: one 64-bit row pointer per output row, the row sums and
+// scales of 4 consecutive rows read from LDS with one 16-byte load each, and
+// the column offsets folded into the store's immediate offset.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int TM, int TN, int FM, int FN>
+__device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], const int *s_rs, const float *s_sc,
+                                           int wm, int wn, int h, int li, int64_t m0, int64_t n0, int64_t M,
+                                           int64_t N, bool full, float *__restrict__ Y,
+                                           int32_t *__restrict__ acc_out)
+{
+    if (full && !acc_out) {
+        float *yb = Y + (m0 + wm * TM + 4 * h) * N + (n0 + wn * TN + li);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int lr0 = wm * TM + fm * 32 + 8 * g + 4 * h;
+                const i32x4 rs4 = *reinterpret_cast<const i32x4 *>(s_rs + lr0);
+                const f32x4 sc4 = *reinterpret_cast<const f32x4 *>(s_sc + lr0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float *yr = yb + (int64_t)(fm * 32 + 8 * g + r) * N;
+#pragma unroll
+                    for (int fn = 0; fn < FN; ++fn)
+                        yr[fn * 32] = (float)(acc[fm][fn][4 * g + r] - rs4[r]) * sc4[r];
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int lr = wm * TM + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
+            const int64_t m = m0 + lr;
+            if (m >= M) continue;
+            const int rs = s_rs[lr];
+            const float sc = s_sc[lr];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+                const int64_t n = n0 + wn * TN + fn * 32 + li;
+                if (n < N) {
+                    const int av = acc[fm][fn][v] - rs;
+                    Y[m * N + n] = (float)av * sc;
+                    if (acc_out) acc_out[m * N + n] = av;
+                }
+            }
+        }
+    }
+}
+
 // BM x BN tile, WM x WN waves, each wave (BM/WM) x (BN/WN) of 32x32 fragments.
 template <Pattern P, int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
@@ -115,8 +172,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     constexpr int B_PER_T = (BN + T - 1) / T;          // packed rows (16 bytes) per thread
     __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * LDA];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LDB];
-    __shared__ int s_rs[BM];
-    __shared__ float s_sc[BM];
+    __shared__ __attribute__((aligned(16))) int s_rs[BM];
+    __shared__ __attribute__((aligned(16))) float s_sc[BM];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WN, wn = wave % WN;
@@ -199,24 +256,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         const int buf = (int)(it & 1);
         if (it + 1 < slices) load_slice((it + 1) * BK);
 
-        // B fragments: words 2h and 2h+1 of each row (k-steps s = 0, 1)
+        // B fragments: words 2h and 2h+1 of each row (k-steps s = 0, 1); all
+        // fragments of the slice are read into distinct registers first
         u32x2 bw[FN];
+        i32x4 a[2][FM];
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn)
             bw[fn] = *reinterpret_cast<const u32x2 *>(sB[buf] + (wn * TN + fn * 32 + li) * LDB + 8 * h);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            i32x4 a[FM], bb[FN];
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
-                a[fm] = *reinterpret_cast<const i32x4 *>(sA[buf] + (wm * TM + fm * 32 + li) * LDA + 32 * h + 16 * s);
+                a[s][fm] = *reinterpret_cast<const i32x4 *>(sA[buf] + (wm * TM + fm * 32 + li) * LDA + 32 * h + 16 * s);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            i32x4 bb[FN];
 #pragma unroll
             for (int fn = 0; fn < FN; ++fn) bb[fn] = unpack_word(bw[fn][s]);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
                 for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[fm], bb[fn], acc[fm][fn], 0, 0, 0);
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[s][fm], bb[fn], acc[fm][fn], 0, 0, 0);
         }
 
         if (it + 1 < slices) store_slice(buf ^ 1);
@@ -224,26 +286,201 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     }
 
     // fused epilogue: offset-code correction and dequant scale
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int lr = wm * TM + fm * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int64_t m = m0 + lr;
-            if (m >= M) continue;
-            const int rs = s_rs[lr];
-            const float sc = s_sc[lr];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) {
-                const int64_t n = n0 + wn * TN + fn * 32 + li;
-                if (n < N) {
-                    const int av = acc[fm][fn][v] - rs;
-                    Y[m * N + n] = (float)av * sc;
-                    if (acc_out) acc_out[m * N + n] = av;
-                }
-            }
-        }
+    store_tile<TM, TN, FM, FN>(acc, s_rs, s_sc, wm, wn, h, li, m0, n0, M, N,
+                               (m0 + BM <= M) && (n0 + BN <= N), Y, acc_out);
+}
+
+// ---------------------------------------------------------------------------
+// Dense path with a deeper pipeline: S-stage LDS ring filled by direct
+// global->LDS loads (global_load_lds_dwordx4: the data never passes through
+// VGPRs), so S-1 K slices are in flight while one is consumed; one barrier
+// per slice.  Each wave issues the same number of loads per slice (A: BM/16
+// instructions spread over the waves; B: BN / waves rows, one instruction per
+// 64 rows or one half-wave instruction for 32), which keeps the vmcnt
+// bookkeeping a compile-time constant.  The MFMA operands are double-buffered
+// in registers too: the fragments of slice i+1 are read from LDS before the
+// MFMAs of slice i are issued, so LDS latency hides behind matrix work.
+//
+// A direct load writes 64 consecutive 16-byte LDS slots per instruction, so
+// the activation tile is stored unpadded, 64 bytes per row, with the 16-byte
+// pieces XOR-swizzled: logical piece c of row r sits in slot c ^ ((r >> 2) & 3).
+// The MFMA-side read of 16 consecutive rows at one logical piece then covers
+// 16 distinct 4-bank groups.  Packed weight rows are 16 bytes apart.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glob_void_t;
+
+__device__ __forceinline__ void dma16(const void *gsrc, uint8_t *ldst)
+{
+    __builtin_amdgcn_global_load_lds((glob_void_t *)gsrc, (lds_void_t *)ldst, 16, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int BM, int BN, int WM, int WN, int S>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
+    const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
+    const uint8_t *__restrict__ packed, const float *__restrict__ w_scale, int64_t M, int64_t N,
+    int64_t K, float *__restrict__ Y, int32_t *__restrict__ acc_out)
+{
+    constexpr int NW = WM * WN;
+    constexpr int T = 64 * NW;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FM = TM / 32, FN = TN / 32;
+    static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "tile");
+    constexpr int A_INSTR = BM / 16;                   // 1 KB (16 rows) per instruction
+    static_assert(A_INSTR % NW == 0, "A loads must split evenly over the waves");
+    constexpr int A_PER_W = A_INSTR / NW;
+    constexpr int B_ROWS_W = BN / NW;                  // packed weight rows loaded per wave
+    static_assert(BN % NW == 0 && (B_ROWS_W == 32 || B_ROWS_W % 64 == 0), "B loads per wave");
+    constexpr int B_PER_W = (B_ROWS_W + 63) / 64;      // 32 rows: one half-wave instruction
+    constexpr int LOADS_PER_SLICE = A_PER_W + B_PER_W;
+    static_assert(S >= 3, "the fragment prefetch needs S >= 3");
+    constexpr int SA = BM * 64, SB = BN * 16, STAGE = SA + SB;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    int *s_rs = reinterpret_cast<int *>(smem + S * STAGE);
+    float *s_sc = reinterpret_cast<float *>(smem + S * STAGE + 4 * BM);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WN, wn = wave % WN;
+    const int h = lane >> 5, li = lane & 31;
+
+    const int64_t tiles_m = (M + BM - 1) / BM;
+    const int64_t tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles = tiles_m * tiles_n;
+    const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+    const int64_t b = blockIdx.x;
+    const int64_t tile = (b % kXcds) * per_xcd + b / kXcds;
+    if (tile >= tiles) return;
+    const int64_t m0 = (tile % tiles_m) * BM;
+    const int64_t n0 = (tile / tiles_m) * BN;
+    const float beta = w_scale[0];
+    for (int i = tid; i < BM; i += T) {
+        const int64_t m = min(m0 + i, M - 1);
+        s_rs[i] = x_rowsum[m];
+        s_sc[i] = beta * x_scale[m];
     }
+
+    // per-lane global sources of this wave's loads (advance by k0 per slice)
+    const int8_t *a_src[A_PER_W];
+#pragma unroll
+    for (int j = 0; j < A_PER_W; ++j) {
+        const int jj = wave * A_PER_W + j;
+        const int row = jj * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ ((row >> 2) & 3);
+        a_src[j] = Xq + min(m0 + row, M - 1) * K + 16 * c;
+    }
+    const uint8_t *b_src[B_PER_W];
+#pragma unroll
+    for (int j = 0; j < B_PER_W; ++j)
+        b_src[j] = packed + min(n0 + wave * B_ROWS_W + j * 64 + lane, N - 1) * (K / 4);
+
+    const int64_t slices = K / BK;
+    auto issue = [&](int64_t sl) {
+        uint8_t *st = smem + (sl % S) * STAGE;
+        const int64_t k0 = sl * BK;
+#pragma unroll
+        for (int j = 0; j < A_PER_W; ++j) dma16(a_src[j] + k0, st + (wave * A_PER_W + j) * 1024);
+#pragma unroll
+        for (int j = 0; j < B_PER_W; ++j)
+            if (B_ROWS_W >= 64 || lane < 32) dma16(b_src[j] + k0 / 4, st + SA + (wave * B_ROWS_W + j * 64) * 16);
+    };
+
+    // two register sets of fragments: slice i is multiplied while slice i+1 is read
+    i32x4 a[2][2][FM];
+    u32x2 bw[2][FN];
+    auto read_frags = [&](int64_t sl, auto set_c) {
+        constexpr int set = decltype(set_c)::value;
+        const uint8_t *st = smem + (sl % S) * STAGE;
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn)
+            bw[set][fn] = *reinterpret_cast<const u32x2 *>(st + SA + (wn * TN + fn * 32 + li) * 16 + 8 * h);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm) {
+                const int r = wm * TM + fm * 32 + li;
+                const int c = (2 * h + s2) ^ ((r >> 2) & 3);
+                a[set][s2][fm] = *reinterpret_cast<const i32x4 *>(st + r * 64 + 16 * c);
+            }
+    };
+
+    i32x16 acc[FM][FN];
+#pragma unroll
+    for (int x = 0; x < FM; ++x)
+#pragma unroll
+        for (int y = 0; y < FN; ++y)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[x][y][v] = 0;
+
+#pragma unroll
+    for (int sl = 0; sl < S - 1; ++sl)
+        if (sl < slices) issue(sl);
+    // slice 0 resident, then its fragments into set 0
+    if (S - 2 < slices) wait_vm<LOADS_PER_SLICE * (S - 2)>();
+    else wait_vm<0>();
+    __syncthreads();
+    read_frags(0, std::integral_constant<int, 0>());
+
+    // one K slice: make slice it+1 resident and read its fragments into the
+    // other register set, then multiply slice it (the register set is a
+    // compile-time index: the loop is unrolled by two)
+    auto step = [&](int64_t it, auto cur_c) {
+        constexpr int cur = decltype(cur_c)::value;
+        if (it + 1 < slices) {
+            // slice it+1 resident for every wave; the stage of slice it-1 is free
+            if (it + S - 2 < slices) wait_vm<LOADS_PER_SLICE * (S - 3)>();
+            else wait_vm<0>();
+            __syncthreads();
+            if (it + S - 1 < slices) issue(it + S - 1);
+            read_frags(it + 1, std::integral_constant<int, cur ^ 1>());
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+            i32x4 bb[FN];
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) bb[fn] = unpack_word(bw[cur][fn][s2]);
+#pragma unroll
+            for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int fn = 0; fn < FN; ++fn)
+                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[cur][s2][fm], bb[fn], acc[fm][fn], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int64_t it = 0; it < slices; it += 2) {
+        step(it, std::integral_constant<int, 0>());
+        if (it + 1 < slices) step(it + 1, std::integral_constant<int, 1>());
+    }
+
+    store_tile<TM, TN, FM, FN>(acc, s_rs, s_sc, wm, wn, h, li, m0, n0, M, N,
+                               (m0 + BM <= M) && (n0 + BN <= N), Y, acc_out);
+}
+
+template <int BM, int BN, int WM, int WN, int S>
+hipError_t launch_dma(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                      const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                      hipStream_t stream)
+{
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+    const int64_t grid = per_xcd * kXcds;
+    const size_t lds = (size_t)S * (BM * 64 + BN * 16) + 8 * BM;
+    auto kern = gemm_dma_kernel<BM, BN, WM, WN, S>;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, stream, Xq, xs, rs, packed, w_scale,
+                       M, N, K, Y, acc);
+    return hipGetLastError();
 }
 
 template <Pattern P, int BM, int BN, int WM, int WN>
@@ -271,6 +508,10 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
     const int pi = (int)P;
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (M >= 256 && tiles(256, 256) >= 128) {
+        if (P == Pattern::Dense) {
+            *name = "gemm_dense_dma_256x256_w8_s4";
+            return launch_dma<256, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+        }
         *name = names[pi][0];
         return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
     }
