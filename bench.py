@@ -12,7 +12,7 @@ distinct buffers larger than the 256 MB Infinity Cache so that every step
 streams its weights from HBM.  Steps are captured in a HIP graph and timed
 with HIP events on the capture's stream, bracketed by device synchronisation.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--traffic-probe]
 Prints one JSON line on stdout; a readable summary goes to stderr.
 """
 from __future__ import annotations
@@ -93,6 +93,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run a few eager decode steps and a copy kernel of known size, then exit "
+                         "(the command profiled with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -154,6 +157,23 @@ def main():
         Yg = Y[name].cpu().numpy().astype(np.float64)
         if not np.all(np.abs(Yg - Yo) <= 1e-5 * np.abs(Yo)):
             raise SystemExit("decode output of %s does not match the oracle" % name)
+
+    if args.traffic_probe:
+        # counters per dispatch: 2 x P eager decode steps over the rotating pool,
+        # then a byte copy of COPY_BYTES (reads and writes that many bytes) as
+        # the calibration of FETCH_SIZE / WRITE_SIZE
+        for i in range(2 * P):
+            decode_step(i)
+        copy_bytes = 256 << 20
+        src = torch.full((copy_bytes,), 7, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("traffic probe: %d fused decode launches, then a %d-byte device copy" % (2 * P * len(groups), copy_bytes))
+        print(json.dumps({"fused_launches": 2 * P * len(groups), "copy_bytes": copy_bytes,
+                          "source_digest": source_digest()}), flush=True)
+        return
 
     def group_bytes(g):
         N0, K = shapes[g[0]]

@@ -123,7 +123,9 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
         const int f = i * 64 + lane;
         const int row = (int)(((float)f + 0.5f) * inv_cw);
         const int col = f - row * cw;
-        const int64_t n = min(n0 + row, N - 1);
+        // lanes past the wave's 16 x cw chunks re-read the wave's first chunk
+        // (a line it fetches anyway) rather than another workgroup's rows
+        const int64_t n = min(n0 + (row < 16 ? row : 0), N - 1);
         w_off[i] = (row < 16) ? row * L::kStride + col * 16 : -1;
         w[i] = load_chunk<P>(packed, N, K, n, c_lo + (row < 16 ? col : 0));
     }
