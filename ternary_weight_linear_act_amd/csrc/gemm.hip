@@ -297,15 +297,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 // per slice.  Each wave issues the same number of loads per slice (A: BM/16
 // instructions spread over the waves; B: BN / waves rows, one instruction per
 // 64 rows or one half-wave instruction for 32), which keeps the vmcnt
-// bookkeeping a compile-time constant.  The MFMA operands are double-buffered
-// in registers too: the fragments of slice i+1 are read from LDS before the
-// MFMAs of slice i are issued, so LDS latency hides behind matrix work.
+// bookkeeping a compile-time constant.
 //
 // A direct load writes 64 consecutive 16-byte LDS slots per instruction, so
 // the activation tile is stored unpadded, 64 bytes per row, with the 16-byte
 // pieces XOR-swizzled: logical piece c of row r sits in slot c ^ ((r >> 2) & 3).
 // The MFMA-side read of 16 consecutive rows at one logical piece then covers
 // 16 distinct 4-bank groups.  Packed weight rows are 16 bytes apart.
+//
+// Schedule of one slice (two k-steps of 32), per wave:
+//   MFMAs of k-step 0  | then read the A fragments of k-step 1
+//   wait for slice i+1, barrier, issue the loads of slice i+S-1
+//   MFMAs of k-step 1  | then read the fragments of slice i+1, k-step 0
+// Every group of LDS reads is issued behind a group of MFMAs and consumed by
+// the next group, so LDS latency hides behind matrix work.  (LDS reads are
+// issued after the MFMAs rather than before them: the loads that write LDS
+// directly are counted like LDS operations by the compiler's wait insertion,
+// which then waits for every outstanding LDS read at the next use.)  The
+// barrier is a bare s_barrier with compiler-level fences: the wait for the
+// direct loads is explicit (vmcnt), and the fragments a wave read from the
+// stage being overwritten were consumed before it reached the barrier.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glob_void_t;
@@ -320,6 +331,13 @@ __device__ __forceinline__ void wait_vm()
 {
     static_assert(N >= 0 && N < 64, "vmcnt");
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void block_barrier()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <int BM, int BN, int WM, int WN, int S>
@@ -339,8 +357,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     constexpr int B_ROWS_W = BN / NW;                  // packed weight rows loaded per wave
     static_assert(BN % NW == 0 && (B_ROWS_W == 32 || B_ROWS_W % 64 == 0), "B loads per wave");
     constexpr int B_PER_W = (B_ROWS_W + 63) / 64;      // 32 rows: one half-wave instruction
-    constexpr int LOADS_PER_SLICE = A_PER_W + B_PER_W;
-    static_assert(S >= 3, "the fragment prefetch needs S >= 3");
+    constexpr int LPS = A_PER_W + B_PER_W;             // loads per slice per wave
+    static_assert(S >= 3, "the pipeline needs S >= 3");
     constexpr int SA = BM * 64, SB = BN * 16, STAGE = SA + SB;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     int *s_rs = reinterpret_cast<int *>(smem + S * STAGE);
@@ -391,23 +409,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
             if (B_ROWS_W >= 64 || lane < 32) dma16(b_src[j] + k0 / 4, st + SA + (wave * B_ROWS_W + j * 64) * 16);
     };
 
-    // two register sets of fragments: slice i is multiplied while slice i+1 is read
-    i32x4 a[2][2][FM];
-    u32x2 bw[2][FN];
-    auto read_frags = [&](int64_t sl, auto set_c) {
-        constexpr int set = decltype(set_c)::value;
+    // fragment offsets within a stage: A row r, logical piece 2h + k-step;
+    // B row of fragment fn, words 2h and 2h+1 (k-steps 0 and 1)
+    int fa[2][FM];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+            const int r = wm * TM + fm * 32 + li;
+            fa[s2][fm] = r * 64 + 16 * ((2 * h + s2) ^ ((r >> 2) & 3));
+        }
+    const int fb = SA + (wn * TN + li) * 16 + 8 * h;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    auto read_a = [&](int64_t sl, auto s2c, i32x4 (&dst)[FM]) {
+        constexpr int s2 = decltype(s2c)::value;
         const uint8_t *st = smem + (sl % S) * STAGE;
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            bw[set][fn] = *reinterpret_cast<const u32x2 *>(st + SA + (wn * TN + fn * 32 + li) * 16 + 8 * h);
+        for (int fm = 0; fm < FM; ++fm) dst[fm] = *reinterpret_cast<const i32x4 *>(st + fa[s2][fm]);
+    };
+    auto read_b = [&](int64_t sl, u32x2 (&dst)[FN]) {
+        const uint8_t *st = smem + (sl % S) * STAGE;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm) {
-                const int r = wm * TM + fm * 32 + li;
-                const int c = (2 * h + s2) ^ ((r >> 2) & 3);
-                a[set][s2][fm] = *reinterpret_cast<const i32x4 *>(st + r * 64 + 16 * c);
-            }
+        for (int fn = 0; fn < FN; ++fn) dst[fn] = *reinterpret_cast<const u32x2 *>(st + fb + fn * 32 * 16);
     };
 
     i32x16 acc[FM][FN];
@@ -417,46 +441,67 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
         for (int y = 0; y < FN; ++y)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[x][y][v] = 0;
+    auto mfma_k = [&](const i32x4 (&a)[FM], const u32x2 (&bw)[FN], auto s2c) {
+        constexpr int s2 = decltype(s2c)::value;
+        i32x4 bb[FN];
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) bb[fn] = unpack_word(bw[fn][s2]);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+                acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[fm], bb[fn], acc[fm][fn], 0, 0, 0);
+    };
 
+    // prologue: S-1 slices in flight, slice 0 resident, its k-step-0 fragments read
 #pragma unroll
     for (int sl = 0; sl < S - 1; ++sl)
         if (sl < slices) issue(sl);
-    // slice 0 resident, then its fragments into set 0
-    if (S - 2 < slices) wait_vm<LOADS_PER_SLICE * (S - 2)>();
+    if (S - 2 < slices) wait_vm<LPS * (S - 2)>();
     else wait_vm<0>();
-    __syncthreads();
-    read_frags(0, std::integral_constant<int, 0>());
+    block_barrier();
+    i32x4 a0[FM], a1[FM];
+    u32x2 bw0[FN], bw1[FN];
+    read_a(0, I0(), a0);
+    read_b(0, bw0);
+    // the output pointers are read only by the epilogue: complete their scalar
+    // loads here, or every LDS wait in the loop becomes a wait for everything
+    asm volatile("" ::"s"(Y), "s"(acc_out));
 
-    // one K slice: make slice it+1 resident and read its fragments into the
-    // other register set, then multiply slice it (the register set is a
-    // compile-time index: the loop is unrolled by two)
-    auto step = [&](int64_t it, auto cur_c) {
-        constexpr int cur = decltype(cur_c)::value;
-        if (it + 1 < slices) {
-            // slice it+1 resident for every wave; the stage of slice it-1 is free
-            if (it + S - 2 < slices) wait_vm<LOADS_PER_SLICE * (S - 3)>();
+    // one slice; `steady`: slices it+1 .. it+S-1 exist (no guards needed)
+    auto slice = [&](int64_t it, const u32x2 (&bcur)[FN], u32x2 (&bnext)[FN], bool steady) {
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_k(a0, bcur, I0());
+        __builtin_amdgcn_sched_barrier(0);
+        read_a(it, I1(), a1);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool more = steady || it + 1 < slices;
+        if (steady) {
+            wait_vm<LPS * (S - 3)>();                  // slice it+1 landed (this wave's loads)
+            block_barrier();                           // ... and every wave's
+            issue(it + S - 1);                         // into the stage of slice it-1
+        } else if (more) {
+            if (it + S - 2 < slices) wait_vm<LPS * (S - 3)>();
             else wait_vm<0>();
-            __syncthreads();
+            block_barrier();
             if (it + S - 1 < slices) issue(it + S - 1);
-            read_frags(it + 1, std::integral_constant<int, cur ^ 1>());
         }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-            i32x4 bb[FN];
-#pragma unroll
-            for (int fn = 0; fn < FN; ++fn) bb[fn] = unpack_word(bw[cur][fn][s2]);
-#pragma unroll
-            for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-                for (int fn = 0; fn < FN; ++fn)
-                    acc[fm][fn] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a[cur][s2][fm], bb[fn], acc[fm][fn], 0, 0, 0);
-        }
+        mfma_k(a1, bcur, I1());
         __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+            read_a(it + 1, I0(), a0);
+            read_b(it + 1, bnext);
+        }
     };
-    for (int64_t it = 0; it < slices; it += 2) {
-        step(it, std::integral_constant<int, 0>());
-        if (it + 1 < slices) step(it + 1, std::integral_constant<int, 1>());
+    int64_t it = 0;
+    for (; it + S < slices; it += 2) {                 // both slices of the pair are steady
+        slice(it, bw0, bw1, true);
+        slice(it + 1, bw1, bw0, true);
+    }
+    for (; it < slices; it += 2) {
+        slice(it, bw0, bw1, false);
+        if (it + 1 < slices) slice(it + 1, bw1, bw0, false);
     }
 
     store_tile<TM, TN, FM, FN>(acc, s_rs, s_sc, wm, wn, h, li, m0, n0, M, N,

@@ -64,6 +64,23 @@ def test_ragged_shapes(M, N, K, nm):
     full_check(W, X, nm, label="ragged")
 
 
+@pytest.mark.parametrize("M,N,K", [(1000, 8000, 64), (1000, 8000, 192), (777, 9999, 320), (2048, 6912, 128)])
+def test_prefill_pipelined_gemm_edges(M, N, K):
+    # the deep-pipeline dense GEMM with ragged M and N tiles and fewer K
+    # slices than pipeline stages
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(77 + K, M, N, K, outlier_frac=0.001)
+    full_check(W, X, rows=sample_rows(M, 16, seed=K), label="gemm-pipeline-edge")
+    assert bl.last_dispatch().startswith("gemm_dense_dma"), bl.last_dispatch()
+
+
+@pytest.mark.parametrize("M", [64, 65, 255, 256, 257])
+@pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
+def test_gemm_tile_thresholds(M, nm):
+    W, X = workloads.small_case(300 + M, M, 1000, 448)
+    full_check(W, X, nm, rows=sample_rows(M, 24, seed=M), label="gemm-threshold")
+
+
 def test_zero_rows_and_zero_weights():
     W, X = workloads.small_case(5, 9, 70, 256)
     X[2] = 0.0
