@@ -61,4 +61,45 @@ __device__ __forceinline__ void decode_superblock(const uint32_t *vals, const ui
     }
 }
 
+// ---------------------------------------------------------------------------
+// Whole-wave reductions on DPP lane moves (no LDS round trips): xor 1 and
+// xor 2 inside quads, rotations by 4 and 8 inside rows of 16, then the four
+// row results are read into scalars.  Every lane must be active.  The result
+// is wave-uniform.  Max is order-free; the integer sum is exact.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int v)
+{
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+
+constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowRor4 = 0x124;
+constexpr int kDppRowRor8 = 0x128;
+
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    v = fmaxf(v, __int_as_float(dpp_move<kDppQuadXor1>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_move<kDppQuadXor2>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_move<kDppRowRor4>(__float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_move<kDppRowRor8>(__float_as_int(v))));
+    const int b = __float_as_int(v);
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(b, 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(b, 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(b, 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(b, 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+__device__ __forceinline__ int wave_sum_dpp(int v)
+{
+    v += dpp_move<kDppQuadXor1>(v);
+    v += dpp_move<kDppQuadXor2>(v);
+    v += dpp_move<kDppRowRor4>(v);
+    v += dpp_move<kDppRowRor8>(v);
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+
 }  // namespace bl

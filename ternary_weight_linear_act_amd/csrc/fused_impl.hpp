@@ -17,12 +17,12 @@
 // L2 (M x K x 4 bytes, M <= 4), which costs far less than a launch.
 //
 // Workgroup layout: it owns 16 rows of one projection; KS waves split K as in
-// the skinny kernel.  Order of work: (1) issue the wave's weight loads;
-// (2) all KS waves read the fp32 activation rows once, into registers, and
-// reduce max|x| per token through wave shuffles and LDS; (3) quantise the
-// registers to int8 into a block-shared LDS row and reduce the int32 row
-// sums; (4) stage the weights in LDS; (5) MFMA, reduce across waves,
-// epilogue.
+// the skinny kernel.  Order of work: (1) all KS waves issue the loads of the
+// fp32 activation rows (read once, into registers), (2) then the wave's weight
+// loads; (3) as soon as the activations arrive -- the weights still in flight
+// -- reduce max|x| per token through DPP lane moves and LDS, quantise the
+// registers to int8 into a block-shared LDS row and reduce the int32 row sums;
+// (4) stage the weights in LDS; (5) MFMA, reduce across waves, epilogue.
 #pragma once
 
 #include "skinny_impl.hpp"
@@ -54,20 +54,6 @@ struct FusedLds {
     static constexpr int kW = 16 * kStride;                   // per wave
     static constexpr int kZero = 256;                         // zero block (token rows >= M)
 };
-
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 
 __device__ __forceinline__ int quant1(float x, float s)
 {
@@ -114,7 +100,30 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     const int cw = (int)(C * (wave + 1) / KS - c_lo);
     uint8_t *lw = s_w[wave];
 
-    // (1) weight loads of this wave, all in flight
+    // every argument the kernel reads in SGPRs now: a scalar load left pending
+    // would make the compiler wait for all outstanding memory operations
+    asm volatile("" ::"s"(X), "s"(packed), "s"(args.w_scale[p]), "s"(args.Y[p]), "s"(args.acc[p]));
+
+    // (1) the fp32 activation rows first, read once into registers (XR float4
+    //     per thread per token covers K: K/4 = 16 C <= 16 KS CMAX = XR T):
+    //     waiting for them below leaves the weight loads in flight
+    constexpr int XR = CMAX / 4;
+    const int64_t n4 = K / 4;
+    float4 xr[MT][XR];
+    float g[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+        const float4 *x4 = reinterpret_cast<const float4 *>(X + (int64_t)min(m, mt - 1) * K);
+#pragma unroll
+        for (int j = 0; j < XR; ++j) {
+            const int64_t i = tid + (int64_t)j * T;
+            const float4 a = x4[i < n4 ? i : 0];
+            xr[m][j] = (m < mt && i < n4) ? a : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (2) weight loads of this wave, all in flight
     u32x4 w[WLOADS];
     int w_off[WLOADS];
     const float inv_cw = 1.0f / (float)cw;
@@ -130,23 +139,9 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
         w[i] = load_chunk<P>(packed, N, K, n, c_lo + (row < 16 ? col : 0));
     }
 
-    // (2) the fp32 activation rows, read once into registers (XR float4 per
-    //     thread per token covers K: K/4 = 16 C <= 16 KS CMAX = XR T), then
-    //     max |x| per token over the whole row
-    constexpr int XR = CMAX / 4;
-    const int64_t n4 = K / 4;
-    float4 xr[MT][XR];
-    float g[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(X + (int64_t)min(m, mt - 1) * K);
-#pragma unroll
-        for (int j = 0; j < XR; ++j) {
-            const int64_t i = tid + (int64_t)j * T;
-            const float4 a = x4[i < n4 ? i : 0];
-            xr[m][j] = (m < mt && i < n4) ? a : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        }
-    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // (3a) max |x| per token over the whole row
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         float v = 0.0f;
@@ -155,7 +150,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
             const float4 a = xr[m][j];
             v = fmaxf(v, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
         }
-        v = wave_max(v);
+        v = wave_max_dpp(v);
         if (lane == 0) s_max[m][wave] = v;
     }
     __syncthreads();
@@ -167,7 +162,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
         g[m] = v;
     }
 
-    // (3) quantise into LDS, row sums
+    // (3b) quantise into LDS, row sums
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
         int sum = 0;
@@ -189,7 +184,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
             // 3 zero chunks after the row
             if (tid < 48) q4[n4 + tid] = 0;
         }
-        sum = wave_sum(sum);
+        sum = wave_sum_dpp(sum);
         if (lane == 0) s_sum[m][wave] = sum;
     }
     if (tid < L::kZero / 16) reinterpret_cast<u32x4 *>(s_zero)[tid] = u32x4{0u, 0u, 0u, 0u};

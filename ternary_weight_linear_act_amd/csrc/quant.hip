@@ -7,7 +7,7 @@
 // computed once per row, then multiplied in; round half to even.
 //
 // One workgroup per row.  Pass 1 reads the row with 16-byte loads and reduces
-// |x| to the row maximum (exact, order-free) through wave shuffles and LDS.
+// |x| to the row maximum (exact, order-free) through DPP lane moves and LDS.
 // Pass 2 re-reads the row (L2-resident), quantises, stores four int8 per
 // 32-bit store and reduces the int32 row sum the forward kernels need.
 #include "kernels.hpp"
@@ -17,20 +17,6 @@ namespace {
 
 constexpr int kQuantBlock = 256;
 constexpr int kWaves = kQuantBlock / 64;
-
-__device__ __forceinline__ float wave_max(float v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
-}
-
-__device__ __forceinline__ int wave_sum(int v)
-{
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 
 __device__ __forceinline__ int quant1(float x, float s)
 {
@@ -56,7 +42,7 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
         const float4 v = x4[i];
         g = fmaxf(g, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
     }
-    g = wave_max(g);
+    g = wave_max_dpp(g);
     if (lane == 0) s_max[wave] = g;
     __syncthreads();
     g = s_max[0];
@@ -75,7 +61,7 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
             q4[i] = (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((d & 0xFF) << 24);
         }
     }
-    sum = wave_sum(sum);
+    sum = wave_sum_dpp(sum);
     if (lane == 0) s_sum[wave] = sum;
     __syncthreads();
     if (tid == 0) {

@@ -16,8 +16,9 @@
 //
 // Data flow of one wave: it owns 16 weight rows and a K range of cw chunks
 // (a chunk = 64 weights = 16 packed bytes).
-//  1. Load: every global load of the wave is issued up front.  Weight loads
-//     go in pairs: load 2j + h brings rows 8h .. 8h+7, chunks 8j .. 8j+7
+//  1. Load: every global load of the wave is issued up front, the
+//     activations first (so that staging them waits for nothing else), then
+//     the weights, in pairs: load 2j + h brings rows 8h .. 8h+7, chunks 8j .. 8j+7
 //     (8 lanes read 128 contiguous bytes of a row, a full cache line), so
 //     each pair completes two 256-wide steps for all 16 rows.  The M x cw
 //     activation chunks are read with consecutive lanes on consecutive bytes.
@@ -120,33 +121,11 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     uint8_t *lx = lw + L::kW;
     uint8_t *lz = lx + L::kX;
 
-    // epilogue operands first: their latency hides under the main loads
-    const float beta = w_scale[0];
-    int rs[4];
-    float xsc[4];
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int m = min(4 * q + v, mt - 1);
-        rs[v] = x_rowsum[m];
-        xsc[v] = x_scale[m];
-    }
+    // every kernel argument in SGPRs now: a scalar load left pending would make
+    // the compiler wait for all outstanding memory operations at its first use
+    asm volatile("" ::"s"(Xq), "s"(x_scale), "s"(x_rowsum), "s"(packed), "s"(w_scale), "s"(Y), "s"(acc_out));
 
-    // 1. all global loads of the wave: weights in pairs (see above), then activations
-    constexpr int PAIRS = (CMAX + 7) / 8;
-    const int pairs = (cw + 7) / 8;
-    const int lrow = lane >> 3, lcol = lane & 7;
-    u32x4 w[PAIRS][2];
-#pragma unroll
-    for (int j = 0; j < PAIRS; ++j) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int col = 8 * j + lcol;
-            const int64_t n = min(n0 + 8 * h + lrow, N - 1);
-            w[j][h] = u32x4{0u, 0u, 0u, 0u};
-            if (j < pairs)                                   // wave-uniform
-                w[j][h] = load_chunk<P>(packed, N, K, n, c_lo + min(col, cw - 1));
-        }
-    }
+    // 1a. activations first: waiting for them later leaves the weights in flight
     u32x4 x[XLOADS];
     int x_off[XLOADS];
     const int xw = cw * 4;                           // 16-byte pieces per token
@@ -160,6 +139,35 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
         x[i] = *reinterpret_cast<const u32x4 *>(Xq + (int64_t)min(m, mt - 1) * K + c_lo * 64 +
                                                 (m < mt ? piece : 0) * 16);
     }
+    // epilogue operands
+    const float beta = w_scale[0];
+    int rs[4];
+    float xsc[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int m = min(4 * q + v, mt - 1);
+        rs[v] = x_rowsum[m];
+        xsc[v] = x_scale[m];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 1b. all weight loads of the wave, in pairs (see above)
+    constexpr int PAIRS = (CMAX + 7) / 8;
+    const int pairs = (cw + 7) / 8;
+    const int lrow = lane >> 3, lcol = lane & 7;
+    u32x4 w[PAIRS][2];
+#pragma unroll
+    for (int j = 0; j < PAIRS; ++j) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // unconditional (pairs past this wave's range re-read its last
+            // chunk), so the compiler can count outstanding loads exactly
+            const int col = 8 * j + lcol;
+            const int64_t n = min(n0 + 8 * h + lrow, N - 1);
+            w[j][h] = load_chunk<P>(packed, N, K, n, c_lo + min(col, cw - 1));
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     // zero chunks after each activation row (12 pieces of 16 bytes), and the zero block
     for (int f = lane; f < mt * 12 + 4; f += 64) {
         const int off = (f < mt * 12) ? (f / 12) * L::kXStride + (cw * 4 + f % 12) * 16
