@@ -16,7 +16,7 @@
 // rest.  Each workgroup recomputes max|x| over the whole activation row from
 // L2 (M x K x 4 bytes, M <= 4), which costs far less than a launch.
 //
-// Workgroup layout: it owns 16 rows of one projection; KS waves split K as in
+// Workgroup layout: it owns ROWS rows of one projection; KS waves split K as in
 // the skinny kernel.  Order of work: (1) all KS waves issue the loads of the
 // fp32 activation rows (read once, into registers), (2) then the wave's weight
 // loads; (3) as soon as the activations arrive -- the weights still in flight
@@ -48,10 +48,10 @@ using skinny::u32x4;
 using skinny::unpack_word;
 using skinny::load_chunk;
 
-template <int KS, int CMAX, int MT>
+template <int KS, int CMAX, int MT, int ROWS>
 struct FusedLds {
     static constexpr int kStride = (CMAX + 1) * 16;          // weight row stride
-    static constexpr int kW = 16 * kStride;                   // per wave
+    static constexpr int kW = ROWS * kStride;                 // per wave
     static constexpr int kZero = 256;                         // zero block (token rows >= M)
 };
 
@@ -63,21 +63,25 @@ __device__ __forceinline__ int quant1(float x, float s)
 }
 
 // KS waves split K; at most CMAX chunks per wave; at most MT (<= 4) tokens;
-// the activation row (K bytes per token, plus 3 zero chunks) is shared in LDS
-// and sized at launch (dynamic LDS).
-template <Pattern P, int KS, int CMAX, int MT>
+// ROWS weight rows per workgroup: 16 (one MFMA column block), 32 (two), or 8
+// (the MFMA's columns 8..15 repeat rows 0..7 and are not stored: twice the
+// workgroups for short matrices).  The activation row (K bytes per token, plus
+// 3 zero chunks) is shared in LDS and sized at launch (dynamic LDS).
+template <Pattern P, int KS, int CMAX, int MT, int ROWS>
 __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict__ X, int64_t M, int64_t K,
                                                         FusedProjArgs args, float *__restrict__ x_scale_out)
 {
     static_assert(CMAX % 4 == 0 && MT >= 1 && MT <= 4, "config");
-    using L = FusedLds<KS, CMAX, MT>;
-    constexpr int WLOADS = CMAX / 4;
+    static_assert(ROWS == 8 || ROWS == 16 || ROWS == 32, "rows per workgroup");
+    using L = FusedLds<KS, CMAX, MT, ROWS>;
+    constexpr int RG = (ROWS + 15) / 16;                      // MFMA column blocks
+    constexpr int WLOADS = (ROWS * CMAX + 63) / 64;
     constexpr int T = 64 * KS;
     __shared__ __attribute__((aligned(16))) uint8_t s_w[KS][L::kW];
     __shared__ __attribute__((aligned(16))) uint8_t s_zero[L::kZero];
     __shared__ float s_max[MT][KS];
     __shared__ int s_sum[MT][KS];
-    __shared__ i32x4 s_part[KS > 1 ? KS - 1 : 1][64];
+    __shared__ i32x4 s_part[RG][KS > 1 ? KS - 1 : 1][64];
     extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];   // MT x (K + 192) int8
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -85,14 +89,14 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     const int mt = (int)M;
     const int64_t xstride = K + 192;
 
-    // which projection and which 16 rows
+    // which projection and which rows
     int p = 0;
 #pragma unroll
     for (int i = 1; i < kMaxFusedProj; ++i)
         if (i < args.nproj && (int)blockIdx.x >= args.block_start[i]) p = i;
     const int64_t N = args.N[p];
     const uint8_t *packed = args.packed[p];
-    const int64_t n0 = (int64_t)(blockIdx.x - args.block_start[p]) * 16;
+    const int64_t n0 = (int64_t)(blockIdx.x - args.block_start[p]) * ROWS;
     const float beta = args.w_scale[p][0];
 
     const int64_t C = K / 64;
@@ -132,11 +136,11 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
         const int f = i * 64 + lane;
         const int row = (int)(((float)f + 0.5f) * inv_cw);
         const int col = f - row * cw;
-        // lanes past the wave's 16 x cw chunks re-read the wave's first chunk
+        // lanes past the wave's ROWS x cw chunks re-read the wave's first chunk
         // (a line it fetches anyway) rather than another workgroup's rows
-        const int64_t n = min(n0 + (row < 16 ? row : 0), N - 1);
-        w_off[i] = (row < 16) ? row * L::kStride + col * 16 : -1;
-        w[i] = load_chunk<P>(packed, N, K, n, c_lo + (row < 16 ? col : 0));
+        const int64_t n = min(n0 + (row < ROWS ? row : 0), N - 1);
+        w_off[i] = (row < ROWS) ? row * L::kStride + col * 16 : -1;
+        w[i] = load_chunk<P>(packed, N, K, n, c_lo + (row < ROWS ? col : 0));
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -220,56 +224,75 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
         x_scale_out[tid] = (gm == 0.0f) ? 0.0f : gm / 127.0f;
     }
 
-    // (5) MFMA phase
-    const uint8_t *brow = lw + r * L::kStride + q * 16;
+    // (5) MFMA phase: column block g covers weight rows 16 g + r (ROWS == 8:
+    // rows r & 7, the upper half repeating the lower)
     const uint8_t *arow = (r < mt) ? s_x + r * xstride + (c_lo + q) * 64 : s_zero;
     const int astep = (r < mt) ? 256 : 0;
-    i32x4 acc[4];
+    i32x4 acc[RG][4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = i32x4{0, 0, 0, 0};
+    for (int g2 = 0; g2 < RG; ++g2)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[g2][t] = i32x4{0, 0, 0, 0};
     const int steps = (cw + 3) / 4;
     for (int s = 0; s < steps; ++s) {
-        const u32x4 b = *reinterpret_cast<const u32x4 *>(brow + s * 64);
+        i32x4 a[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
             // past this wave's range the activation bytes belong to the next
             // wave's range or the zero tail: mask them with the column test
             const i32x4 a0 = *reinterpret_cast<const i32x4 *>(arow + s * astep + 16 * t);
-            const i32x4 a = (4 * s + q < cw) ? a0 : i32x4{0, 0, 0, 0};
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, unpack_word(b[t]), acc[t], 0, 0, 0);
+            a[t] = (4 * s + q < cw) ? a0 : i32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int g2 = 0; g2 < RG; ++g2) {
+            const int wr = (ROWS == 8) ? (r & 7) : 16 * g2 + r;
+            const u32x4 b = *reinterpret_cast<const u32x4 *>(lw + wr * L::kStride + q * 16 + s * 64);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+                acc[g2][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], unpack_word(b[t]), acc[g2][t], 0, 0, 0);
         }
     }
-    i32x4 sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    i32x4 sum[RG];
+#pragma unroll
+    for (int g2 = 0; g2 < RG; ++g2) sum[g2] = (acc[g2][0] + acc[g2][1]) + (acc[g2][2] + acc[g2][3]);
     if (KS > 1) {
-        if (wave > 0) s_part[wave - 1][lane] = sum;
+        if (wave > 0) {
+#pragma unroll
+            for (int g2 = 0; g2 < RG; ++g2) s_part[g2][wave - 1][lane] = sum[g2];
+        }
         __syncthreads();
         if (wave != 0) return;
 #pragma unroll
-        for (int w2 = 1; w2 < KS; ++w2) sum += s_part[w2 - 1][lane];
+        for (int g2 = 0; g2 < RG; ++g2)
+#pragma unroll
+            for (int w2 = 1; w2 < KS; ++w2) sum[g2] += s_part[g2][w2 - 1][lane];
     }
 
-    const int64_t nn = n0 + r;
-    if (nn >= N) return;
     float *Y = args.Y[p];
     int32_t *acc_out = args.acc[p];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-        const int m = 4 * q + v;
-        if (m < mt) {
-            const int av = sum[v] - rs[v];
-            Y[(int64_t)m * N + nn] = (float)av * (beta * xsc[v]);
-            if (acc_out) acc_out[(int64_t)m * N + nn] = av;
+    for (int g2 = 0; g2 < RG; ++g2) {
+        const int64_t nn = n0 + 16 * g2 + r;
+        if ((ROWS == 8 && r >= 8) || nn >= N) continue;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int m = 4 * q + v;
+            if (m < mt) {
+                const int av = sum[g2][v] - rs[v];
+                Y[(int64_t)m * N + nn] = (float)av * (beta * xsc[v]);
+                if (acc_out) acc_out[(int64_t)m * N + nn] = av;
+            }
         }
     }
 }
 
-template <Pattern P, int KS, int CMAX, int MT>
+template <Pattern P, int KS, int CMAX, int MT, int ROWS>
 hipError_t launch_fused(const float *X, int64_t M, int64_t K, const FusedProjArgs &args, int blocks,
                         float *x_scale, hipStream_t stream)
 {
     const size_t dyn = (size_t)MT * (size_t)(K + 192);
-    hipLaunchKernelGGL((fused_kernel<P, KS, CMAX, MT>), dim3((unsigned)blocks), dim3(64 * KS), dyn, stream, X, M,
-                       K, args, x_scale);
+    hipLaunchKernelGGL((fused_kernel<P, KS, CMAX, MT, ROWS>), dim3((unsigned)blocks), dim3(64 * KS), dyn, stream,
+                       X, M, K, args, x_scale);
     return hipGetLastError();
 }
 
