@@ -12,7 +12,8 @@ distinct buffers larger than the 256 MB Infinity Cache so that every step
 streams its weights from HBM.  Steps are captured in a HIP graph and timed
 with HIP events on the capture's stream, bracketed by device synchronisation.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--traffic-probe]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
+                       [--traffic-probe]
 Prints one JSON line on stdout; a readable summary goes to stderr.
 """
 from __future__ import annotations
@@ -86,12 +87,85 @@ def timed_graph(torch, body, reps=1):
     return e0.elapsed_time(e1) / reps, g
 
 
+def bench_configs(torch, bl, workloads, dev, log):
+    """The other workloads, reported beside the headline (not part of `value`):
+    single_1024 (M = 1, 16), sparse_ffn_1p5b (dense / 2:4 / 6:8 at M = 1 and
+    512) and block_3b (seven projections at M = 1, 8, 64).  HBM-bound cases
+    rotate weight copies through >= 512 MB; each case is checked against the
+    plain path before it is timed (fused == two-call, bit for bit)."""
+    res = {}
+
+    def case(name, wl_name, projs, M, nm_of, fused_groups=None):
+        wl = workloads.WORKLOADS[wl_name]
+        d = workloads.draw(wl_name, projs=projs, Ms=(M,))
+        shapes = {p.name: (p.N, p.K) for p in wl.projs if p.name in projs}
+        pk, ws = {}, {}
+        for n in projs:
+            pk[n], ws[n] = bl.pack_weights(torch.from_numpy(d.W[n]).to(dev), nm=nm_of(n))
+        wbytes = sum(pk[n].numel() for n in projs)
+        P = max(2, -(-POOL_BYTES // wbytes)) if M <= 64 else 1
+        pools = {n: [pk[n]] + [pk[n].clone() for _ in range(P - 1)] for n in projs}
+        X = {n: torch.from_numpy(d.X[(n, M)]).to(dev) for n in projs}
+        Y = {n: torch.empty((M, shapes[n][0]), dtype=torch.float32, device=dev) for n in projs}
+        Xq = {n: torch.empty((M, shapes[n][1]), dtype=torch.int8, device=dev) for n in projs}
+        xs = {n: torch.empty(M, dtype=torch.float32, device=dev) for n in projs}
+        rs = {n: torch.empty(M, dtype=torch.int32, device=dev) for n in projs}
+
+        def two_call(j):
+            for n in projs:
+                bl.quant_act(X[n], Xq[n], xs[n], rs[n])
+                bl.forward(Xq[n], xs[n], rs[n], pools[n][j], ws[n], shapes[n][0], nm=nm_of(n), Y=Y[n])
+        two_call(0)
+        torch.cuda.synchronize()
+        Yref = {n: Y[n].clone() for n in projs}
+        kernels = sorted({bl.last_dispatch()})
+        G = P if M <= 64 else 10
+        ms, _ = timed_graph(torch, lambda: [two_call(j % P) for j in range(G)], reps=2)
+        us = ms * 1e3 / G
+        abytes = sum(pk[n].numel() + shapes[n][1] * M * 4 + M * shapes[n][0] * 4 for n in projs)
+        ops = sum(2.0 * M * shapes[n][0] * shapes[n][1] for n in projs)
+        r = {"M": M, "projections": list(projs), "two_call_us": round(us, 3),
+             "two_call_GB/s": round(abytes / (us * 1e-6) / 1e9, 1), "TOPS": round(ops / (us * 1e-6) / 1e12, 1)}
+        if fused_groups and M <= 4:
+            def fused(j):
+                for g in fused_groups:
+                    bl.forward_fused(X[g[0]], [(pools[n][j], ws[n], shapes[n][0]) for n in g], nm=nm_of(g[0]),
+                                     Ys=[Y[n] for n in g])
+            fused(0)
+            torch.cuda.synchronize()
+            for n in projs:
+                if not torch.equal(Y[n], Yref[n]):
+                    raise SystemExit("%s: fused and two-call outputs differ for %s" % (name, n))
+            ms, _ = timed_graph(torch, lambda: [fused(j % P) for j in range(G)], reps=2)
+            fus = ms * 1e3 / G
+            fbytes = sum(pk[n].numel() + M * shapes[n][0] * 4 for n in projs) + sum(
+                4 * M * shapes[g[0]][1] for g in fused_groups)
+            r.update({"fused_us": round(fus, 3), "fused_GB/s": round(fbytes / (fus * 1e-6) / 1e9, 1),
+                      "fused_launches": len(fused_groups)})
+        res[name] = r
+        log("%-28s M=%-4d two-call %8.2f us%s" % (name, M, us, (" fused %.2f us" % r["fused_us"]) if "fused_us" in r else ""))
+
+    dense = lambda n: (0, 0)
+    case("single_1024/M1", "single_1024", ("linear",), 1, dense, [("linear",)])
+    case("single_1024/M16", "single_1024", ("linear",), 16, dense)
+    nmap = {"dense": (0, 0), "nm24": (2, 4), "nm68": (6, 8)}
+    for pn in ("dense", "nm24", "nm68"):
+        case("sparse_ffn_1p5b/%s/M1" % pn, "sparse_ffn_1p5b", (pn,), 1, lambda n: nmap[n], [(pn,)])
+        case("sparse_ffn_1p5b/%s/M512" % pn, "sparse_ffn_1p5b", (pn,), 512, lambda n: nmap[n])
+    blk = ("q", "k", "v", "o", "gate", "up", "down")
+    for M in (1, 8, 64):
+        case("block_3b/M%d" % M, "block_3b", blk, M, dense,
+             [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)])
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' timings")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a few eager decode steps and a copy kernel of known size, then exit "
@@ -260,6 +334,9 @@ def main():
         except (ValueError, OSError):
             traffic = None
 
+    # ------------------------------------------------------------------ other workloads
+    configs = None if args.no_configs else bench_configs(torch, bl, workloads, dev, log)
+
     # ------------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
@@ -314,6 +391,7 @@ def main():
                               "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4)},
                  "quant_act_us": round(quant_p_us, 2)},
         "cpu_baseline": cpu,
+        "other_workloads": configs,
         "source_digest": digest,
     }
     log("decode step %.2f us (%.1f GB/s); fused decode launch %.3f us avg (%.1f GB/s, %.1f%% of HBM); "

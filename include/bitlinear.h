@@ -48,7 +48,14 @@
  *
  * Conventions for every call:
  *   - Data pointers are device pointers (hipMalloc / torch tensors) owned by
- *     the caller; the library allocates nothing and keeps no device state.
+ *     the caller.  The one exception is internal: the first
+ *     bitlinear_forward call on a device that runs the few-token GEMM
+ *     (dense, 17 <= M <= 64, or a decode shape too large for the skinny
+ *     kernel) allocates a 64 MB split-K workspace with hipMalloc, once, and
+ *     keeps it until the process ends.  That call must not be inside HIP
+ *     graph capture (a captured call that finds no workspace uses the
+ *     unsplit kernel instead), and such calls must not overlap in time on
+ *     one device (they share the workspace).
  *   - Matrices are row-major and dense: W is N x K (out x in), X and Xq are
  *     M x K, Y and acc are M x N.
  *   - Work is enqueued on `stream` (NULL = the null stream); no call

@@ -46,7 +46,9 @@ namespace fused {
 using skinny::i32x4;
 using skinny::u32x4;
 using skinny::unpack_word;
-using skinny::load_chunk;
+using skinny::RawChunk;
+using skinny::load_raw_chunk;
+using skinny::decode_chunk;
 
 template <int KS, int CMAX, int MT, int ROWS>
 struct FusedLds {
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     __builtin_amdgcn_sched_barrier(0);
 
     // (2) weight loads of this wave, all in flight
-    u32x4 w[WLOADS];
+    RawChunk<P> w[WLOADS];
     int w_off[WLOADS];
     const float inv_cw = 1.0f / (float)cw;
 #pragma unroll
@@ -140,7 +142,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
         // (a line it fetches anyway) rather than another workgroup's rows
         const int64_t n = min(n0 + (row < ROWS ? row : 0), N - 1);
         w_off[i] = (row < ROWS) ? row * L::kStride + col * 16 : -1;
-        w[i] = load_chunk<P>(packed, N, K, n, c_lo + (row < ROWS ? col : 0));
+        w[i] = load_raw_chunk<P>(packed, N, K, n, c_lo + (row < ROWS ? col : 0));
     }
 
     __builtin_amdgcn_sched_barrier(0);
@@ -196,7 +198,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     // (4) weights to LDS
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i)
-        if (w_off[i] >= 0) *reinterpret_cast<u32x4 *>(lw + w_off[i]) = w[i];
+        if (w_off[i] >= 0) *reinterpret_cast<u32x4 *>(lw + w_off[i]) = decode_chunk<P>(w[i]);
     __syncthreads();
 
     int rs[4];

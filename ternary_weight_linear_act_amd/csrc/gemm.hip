@@ -30,6 +30,8 @@
 // Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
 // consecutive logical tiles (which share a weight column tile) are mapped to
 // workgroups on the same XCD and reuse its L2.
+#include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -175,7 +177,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     __shared__ __attribute__((aligned(16))) int s_rs[BM];
     __shared__ __attribute__((aligned(16))) float s_sc[BM];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is wave-uniform: say so, so that branches on it are scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int h = lane >> 5, li = lane & 31;
 
@@ -340,11 +343,19 @@ __device__ __forceinline__ void block_barrier()
     asm volatile("" ::: "memory");
 }
 
-template <int BM, int BN, int WM, int WN, int S>
+// SPLIT: the K slices are divided among `splits` workgroups per output tile
+// (blockIdx.x = split * tile workgroups + tile workgroup); each writes its
+// int32 partial tile to the workspace `ws` (element e of thread t at e * T + t)
+// and the epilogue kernel below, launched next on the same stream, adds the
+// partials (integer sums: the result does not depend on the order) and
+// applies the dequant scale.  Used when there are too few output tiles to fill
+// the chip (few tokens).  The kernel boundary makes the partials visible: no
+// fence or counter is needed.
+template <int BM, int BN, int WM, int WN, int S, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
     const uint8_t *__restrict__ packed, const float *__restrict__ w_scale, int64_t M, int64_t N,
-    int64_t K, float *__restrict__ Y, int32_t *__restrict__ acc_out)
+    int64_t K, float *__restrict__ Y, int32_t *__restrict__ acc_out, int32_t splits, int32_t *__restrict__ ws)
 {
     constexpr int NW = WM * WN;
     constexpr int T = 64 * NW;
@@ -364,7 +375,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     int *s_rs = reinterpret_cast<int *>(smem + S * STAGE);
     float *s_sc = reinterpret_cast<float *>(smem + S * STAGE + 4 * BM);
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // the wave index is wave-uniform: say so, so that branches on it are scalar
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int h = lane >> 5, li = lane & 31;
 
@@ -372,7 +384,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     const int64_t tiles_n = (N + BN - 1) / BN;
     const int64_t tiles = tiles_m * tiles_n;
     const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
-    const int64_t b = blockIdx.x;
+    const int64_t grid_tiles = per_xcd * kXcds;
+    const int64_t split = SPLIT ? (int64_t)blockIdx.x / grid_tiles : 0;
+    const int64_t b = (int64_t)blockIdx.x - split * grid_tiles;
     const int64_t tile = (b % kXcds) * per_xcd + b / kXcds;
     if (tile >= tiles) return;
     const int64_t m0 = (tile % tiles_m) * BM;
@@ -383,6 +397,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
         s_rs[i] = x_rowsum[m];
         s_sc[i] = beta * x_scale[m];
     }
+
+    // this workgroup's K slices [sl0, sl0 + slices)
+    const int64_t all_slices = K / BK;
+    const int64_t sl0 = SPLIT ? all_slices * split / splits : 0;
+    const int64_t slices = SPLIT ? all_slices * (split + 1) / splits - sl0 : all_slices;
 
     // per-lane global sources of this wave's loads (advance by k0 per slice)
     const int8_t *a_src[A_PER_W];
@@ -398,10 +417,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     for (int j = 0; j < B_PER_W; ++j)
         b_src[j] = packed + min(n0 + wave * B_ROWS_W + j * 64 + lane, N - 1) * (K / 4);
 
-    const int64_t slices = K / BK;
     auto issue = [&](int64_t sl) {
         uint8_t *st = smem + (sl % S) * STAGE;
-        const int64_t k0 = sl * BK;
+        const int64_t k0 = (sl0 + sl) * BK;
 #pragma unroll
         for (int j = 0; j < A_PER_W; ++j) dma16(a_src[j] + k0, st + (wave * A_PER_W + j) * 1024);
 #pragma unroll
@@ -466,7 +484,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
     read_b(0, bw0);
     // the output pointers are read only by the epilogue: complete their scalar
     // loads here, or every LDS wait in the loop becomes a wait for everything
-    asm volatile("" ::"s"(Y), "s"(acc_out));
+    asm volatile("" ::"s"(Y), "s"(acc_out), "s"(ws));
 
     // one slice; `steady`: slices it+1 .. it+S-1 exist (no guards needed)
     auto slice = [&](int64_t it, const u32x2 (&bcur)[FN], u32x2 (&bnext)[FN], bool steady) {
@@ -504,28 +522,126 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
         if (it + 1 < slices) slice(it + 1, bw1, bw0, false);
     }
 
+    if constexpr (SPLIT) {
+        constexpr int E = FM * FN * 16;
+        int32_t *mine = ws + (split * tiles + tile) * (int64_t)(E * T);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mine[((fm * FN + fn) * 16 + v) * T + tid] = acc[fm][fn][v];
+        return;
+    }
     store_tile<TM, TN, FM, FN>(acc, s_rs, s_sc, wm, wn, h, li, m0, n0, M, N,
                                (m0 + BM <= M) && (n0 + BN <= N), Y, acc_out);
 }
 
-template <int BM, int BN, int WM, int WN, int S>
+// Epilogue of the split-K GEMM, one thread per output element (m, n): find
+// the element's slot in the GEMM kernel's per-thread fragment layout, add the
+// `splits` partials (integers: order-free), subtract the row sum and scale.
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(
+    const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum, const float *__restrict__ w_scale,
+    int64_t M, int64_t N, int32_t splits, const int32_t *__restrict__ ws, float *__restrict__ Y,
+    int32_t *__restrict__ acc_out)
+{
+    constexpr int T = 64 * WM * WN;
+    constexpr int TM = BM / WM, TN = BN / WN;
+    constexpr int FN = TN / 32;
+    constexpr int E = (TM / 32) * FN * 16;
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * N) return;
+    const int64_t m = idx / N, n = idx - m * N;
+    const int64_t tiles_m = (M + BM - 1) / BM;
+    const int64_t tiles = tiles_m * ((N + BN - 1) / BN);
+    const int64_t tile = (n / BN) * tiles_m + m / BM;
+    const int lr = (int)(m % BM), lc = (int)(n % BN);
+    const int wave = (lr / TM) * WN + lc / TN;
+    const int fm = (lr % TM) / 32, fn = (lc % TN) / 32;
+    const int r32 = lr % 32;                      // row in the 32x32 fragment: 8 (v / 4) + 4 h + v % 4
+    const int hh = (r32 >> 2) & 1, v = (r32 >> 3) * 4 + (r32 & 3);
+    const int tid = wave * 64 + 32 * hh + (lc % 32);
+    const int e = (fm * FN + fn) * 16 + v;
+    int acc = 0;
+    for (int64_t o = 0; o < splits; ++o) acc += ws[(o * tiles + tile) * (int64_t)(E * T) + (int64_t)e * T + tid];
+    const int av = acc - x_rowsum[m];
+    Y[idx] = (float)av * (w_scale[0] * x_scale[m]);
+    if (acc_out) acc_out[idx] = av;
+}
+
+template <int BM, int BN, int WM, int WN, int S, bool SPLIT = false>
 hipError_t launch_dma(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                       const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                      hipStream_t stream)
+                      hipStream_t stream, int32_t splits = 1, int32_t *ws = nullptr)
 {
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
-    const int64_t grid = per_xcd * kXcds;
+    const int64_t grid = per_xcd * kXcds * (SPLIT ? splits : 1);
     const size_t lds = (size_t)S * (BM * 64 + BN * 16) + 8 * BM;
-    auto kern = gemm_dma_kernel<BM, BN, WM, WN, S>;
+    auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SPLIT>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  (int)lds);
         if (e != hipSuccess) return e;
     }
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, stream, Xq, xs, rs, packed, w_scale,
-                       M, N, K, Y, acc);
+                       M, N, K, Y, acc, splits, ws);
+    if (SPLIT) {
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t blocks = (M * N + 255) / 256;
+        hipLaunchKernelGGL((splitk_epilogue_kernel<BM, BN, WM, WN>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                           xs, rs, w_scale, M, N, splits, ws, Y, acc);
+    }
     return hipGetLastError();
+}
+
+// Split-K workspace of the few-token GEMM (int32 partial tiles): one per
+// device, created on the first call that needs it (never inside graph
+// capture: such a call falls back to the unsplit kernel), then kept for the
+// life of the process.  Calls that use it must not overlap on one device.
+constexpr int64_t kWorkspaceBytes = 64ll << 20;
+
+int32_t *split_workspace(hipStream_t stream)
+{
+    static std::mutex mu;
+    static int32_t *per_device[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (per_device[dev]) return per_device[dev];
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    void *p = nullptr;
+    if (hipMalloc(&p, (size_t)kWorkspaceBytes) != hipSuccess) return nullptr;
+    per_device[dev] = static_cast<int32_t *>(p);
+    return per_device[dev];
+}
+
+// Few tokens (dense, M <= 64): BM x 128 tiles over a deep ring, K split over
+// enough workgroups to occupy every compute unit.
+template <int BM, int WM, int WN>
+hipError_t launch_few_tokens(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                             const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                             hipStream_t stream, const char **name, const char *split_name, const char *plain_name)
+{
+    constexpr int BN = 128, S = 8;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t slices = K / BK;
+    int64_t splits = std::min<int64_t>((256 + tiles - 1) / tiles, slices / 4);   // >= 4 slices each
+    const int64_t per_split = tiles * (int64_t)BM * BN * 4;        // partial bytes per split
+    splits = std::min<int64_t>(splits, kWorkspaceBytes / per_split);
+    if (splits >= 2) {
+        int32_t *w = split_workspace(stream);
+        if (w) {
+            *name = split_name;
+            return launch_dma<BM, BN, WM, WN, S, true>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream,
+                                                       (int32_t)splits, w);
+        }
+    }
+    *name = plain_name;
+    return launch_dma<BM, BN, WM, WN, S, false>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
 }
 
 template <Pattern P, int BM, int BN, int WM, int WN>
@@ -560,6 +676,18 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
         *name = names[pi][0];
         return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
     }
+    // mid-size dense problems (e.g. 512 tokens): 128 x 128 tiles fill the
+    // chip where 256 x 256 tiles would leave most compute units idle
+    if (P == Pattern::Dense && M >= 128 && tiles(128, 128) >= 128) {
+        *name = "gemm_dense_dma_128x128_w4_s4";
+        return launch_dma<128, 128, 2, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+    }
+    if (P == Pattern::Dense && M <= 32)
+        return launch_few_tokens<32, 1, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                                           "gemm_dense_splitk_32x128", "gemm_dense_dma_32x128");
+    if (P == Pattern::Dense && M <= 64)
+        return launch_few_tokens<64, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                                           "gemm_dense_splitk_64x128", "gemm_dense_dma_64x128");
     if (M > 64) {
         *name = names[pi][1];
         return launch<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);

@@ -60,26 +60,48 @@ __device__ __forceinline__ i32x4 unpack_word(uint32_t w)
     return b;
 }
 
-// Chunk c (64 weights) of row n as 4 dense code words.
+// Chunk c (64 weights) of row n as raw packed words: dense = 4 code words;
+// N:M = the superblock's kept-code words, then its 2 mask words.  Loading
+// the raw words and decoding them later (decode_chunk) keeps every load of a
+// wave in flight at once: a decode right after each load would wait for it.
 template <Pattern P>
-__device__ __forceinline__ u32x4 load_chunk(const uint8_t *__restrict__ packed, int64_t N, int64_t K,
-                                            int64_t n, int64_t c)
+struct RawChunk {
+    static constexpr int kVals = (P == Pattern::Dense) ? 4 : (P == Pattern::NM24 ? 2 : 3);
+    static constexpr int kWords = (P == Pattern::Dense) ? 4 : kVals + 2;
+    uint32_t w[kWords];
+};
+
+template <Pattern P>
+__device__ __forceinline__ RawChunk<P> load_raw_chunk(const uint8_t *__restrict__ packed, int64_t N, int64_t K,
+                                                      int64_t n, int64_t c)
 {
-    if (P == Pattern::Dense) {
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(packed + n * (K / 4) + c * 16));
+    RawChunk<P> r;
+    if constexpr (P == Pattern::Dense) {
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(packed + n * (K / 4) + c * 16));
+        r.w[0] = v[0]; r.w[1] = v[1]; r.w[2] = v[2]; r.w[3] = v[3];
     } else {
         constexpr int GM = (P == Pattern::NM24) ? 4 : 8;
         constexpr int GN = (P == Pattern::NM24) ? 2 : 6;
-        constexpr int VW = 64 * GN / GM / 16;
+        constexpr int VW = RawChunk<P>::kVals;
         const int64_t vrow = nm_value_row_bytes(K, GN, GM);
         const uint32_t *vp = reinterpret_cast<const uint32_t *>(packed + n * vrow + c * (VW * 4));
         const uint32_t *mp = reinterpret_cast<const uint32_t *>(packed + N * vrow + n * (K / 8) + c * 8);
-        uint32_t vals[VW], masks[2], w[4];
 #pragma unroll
-        for (int v = 0; v < VW; ++v) vals[v] = vp[v];
-        masks[0] = mp[0];
-        masks[1] = mp[1];
-        decode_superblock<P>(vals, masks, w);
+        for (int v = 0; v < VW; ++v) r.w[v] = vp[v];
+        r.w[VW] = mp[0];
+        r.w[VW + 1] = mp[1];
+    }
+    return r;
+}
+
+template <Pattern P>
+__device__ __forceinline__ u32x4 decode_chunk(const RawChunk<P> &r)
+{
+    if constexpr (P == Pattern::Dense) {
+        return u32x4{r.w[0], r.w[1], r.w[2], r.w[3]};
+    } else {
+        uint32_t w[4];
+        decode_superblock<P>(r.w, r.w + RawChunk<P>::kVals, w);
         return u32x4{w[0], w[1], w[2], w[3]};
     }
 }
@@ -109,7 +131,8 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[KS][L::kBytes];
     __shared__ i32x4 s_part[KS > 1 ? KS - 1 : 1][64];
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the wave index is wave-uniform: say so, so that branches on it are scalar
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
     const int64_t C = K / 64;
@@ -155,7 +178,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     constexpr int PAIRS = (CMAX + 7) / 8;
     const int pairs = (cw + 7) / 8;
     const int lrow = lane >> 3, lcol = lane & 7;
-    u32x4 w[PAIRS][2];
+    RawChunk<P> w[PAIRS][2];
 #pragma unroll
     for (int j = 0; j < PAIRS; ++j) {
 #pragma unroll
@@ -164,7 +187,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
             // chunk), so the compiler can count outstanding loads exactly
             const int col = 8 * j + lcol;
             const int64_t n = min(n0 + 8 * h + lrow, N - 1);
-            w[j][h] = load_chunk<P>(packed, N, K, n, c_lo + min(col, cw - 1));
+            w[j][h] = load_raw_chunk<P>(packed, N, K, n, c_lo + min(col, cw - 1));
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -191,7 +214,8 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
         if (j < pairs) {                                     // wave-uniform
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                *reinterpret_cast<u32x4 *>(lw + (8 * h + lrow) * L::kStride + (8 * j + lcol) * 16) = w[j][h];
+                *reinterpret_cast<u32x4 *>(lw + (8 * h + lrow) * L::kStride + (8 * j + lcol) * 16) =
+                    decode_chunk<P>(w[j][h]);
             __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): staged
             __builtin_amdgcn_wave_barrier();
 #pragma unroll

@@ -64,7 +64,8 @@ def test_ragged_shapes(M, N, K, nm):
     full_check(W, X, nm, label="ragged")
 
 
-@pytest.mark.parametrize("M,N,K", [(1000, 8000, 64), (1000, 8000, 192), (777, 9999, 320), (2048, 6912, 128)])
+@pytest.mark.parametrize("M,N,K", [(1000, 8000, 64), (1000, 8000, 192), (777, 9999, 320), (2048, 6912, 128),
+                                   (500, 4100, 192), (512, 8960, 1536)])
 def test_prefill_pipelined_gemm_edges(M, N, K):
     # the deep-pipeline dense GEMM with ragged M and N tiles and fewer K
     # slices than pipeline stages
@@ -79,6 +80,23 @@ def test_prefill_pipelined_gemm_edges(M, N, K):
 def test_gemm_tile_thresholds(M, nm):
     W, X = workloads.small_case(300 + M, M, 1000, 448)
     full_check(W, X, nm, rows=sample_rows(M, 24, seed=M), label="gemm-threshold")
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 2048, 11008), (17, 300, 2048), (33, 2048, 2048), (64, 256, 2048),
+                                   (64, 2048, 11008), (40, 1000, 192), (64, 11008, 2048)])
+def test_few_token_gemm(M, N, K):
+    # few tokens: K split over several workgroups, partial tiles combined by a
+    # second kernel; twice in a row (the shared workspace is reused)
+    import torch
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(900 + M + K, M, N, K, outlier_frac=0.001)
+    out = full_check(W, X, rows=sample_rows(M, 12, seed=M), label="few-token")
+    name = bl.last_dispatch()
+    assert name.startswith("gemm_dense_splitk") or name.startswith("gemm_dense_dma"), name
+    Y2, acc2 = hip_forward(out["Xq"], out["xs"], out["rs"], out["packed"], out["ws"], N, (0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(acc2, out["acc"])
+    assert torch.equal(Y2.view(torch.int32), out["Y"].view(torch.int32))
 
 
 def test_zero_rows_and_zero_weights():
