@@ -351,8 +351,8 @@ __device__ __forceinline__ void block_barrier()
 // applies the dequant scale.  Used when there are too few output tiles to fill
 // the chip (few tokens).  The kernel boundary makes the partials visible: no
 // fence or counter is needed.
-template <int BM, int BN, int WM, int WN, int S, bool SPLIT>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_dma_kernel(
+template <int BM, int BN, int WM, int WN, int S, bool SPLIT, int OCC = 1>
+__global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
     const uint8_t *__restrict__ packed, const float *__restrict__ w_scale, int64_t M, int64_t N,
     int64_t K, float *__restrict__ Y, int32_t *__restrict__ acc_out, int32_t splits, int32_t *__restrict__ ws)
@@ -570,7 +570,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(
     if (acc_out) acc_out[idx] = av;
 }
 
-template <int BM, int BN, int WM, int WN, int S, bool SPLIT = false>
+template <int BM, int BN, int WM, int WN, int S, bool SPLIT = false, int OCC = 1>
 hipError_t launch_dma(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                       const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                       hipStream_t stream, int32_t splits = 1, int32_t *ws = nullptr)
@@ -579,7 +579,7 @@ hipError_t launch_dma(const int8_t *Xq, const float *xs, const int32_t *rs, cons
     const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
     const int64_t grid = per_xcd * kXcds * (SPLIT ? splits : 1);
     const size_t lds = (size_t)S * (BM * 64 + BN * 16) + 8 * BM;
-    auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SPLIT>;
+    auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SPLIT, OCC>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  (int)lds);
