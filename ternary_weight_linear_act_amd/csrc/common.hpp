@@ -32,8 +32,8 @@ enum class Pattern { Dense, NM24, NM68 };
 // N*g .. N*g+N-1 of the value stream: all word/field indices are compile-time
 // constants and only the position inside the group depends on the mask.
 template <Pattern P>
-__device__ __forceinline__ void decode_superblock(const uint32_t *vals, const uint32_t *masks,
-                                                  uint32_t dense[4])
+__host__ __device__ __forceinline__ void decode_superblock(const uint32_t *vals, const uint32_t *masks,
+                                                           uint32_t dense[4])
 {
     constexpr int M = (P == Pattern::NM24) ? 4 : 8;
     constexpr int N = (P == Pattern::NM24) ? 2 : 6;
@@ -57,6 +57,82 @@ __device__ __forceinline__ void decode_superblock(const uint32_t *vals, const ui
             const uint32_t below = __builtin_popcount(mk & ((1u << i) - 1u));
             const uint32_t code = ((mk >> i) & 1u) ? ((lin >> (2 * below)) & 3u) : 1u;
             dense[p >> 4] |= code << code_bit(p & 15);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Faster N:M decode.  The interleaved code layout above is a 4 x 4 matrix of
+// 2-bit cells (byte = row); its transpose is the linear layout, code j at
+// bits 2j.  In linear order a group's kept codes form a short run, and the
+// dense group is that run with code 01 inserted at the pruned positions:
+//  - 2:4 (16 groups per superblock): a 256-entry table, indexed by the keep
+//    nibble and the 4 bits of the two kept codes, gives the group's 8 bits;
+//  - 6:8 (8 groups): the two pruned positions p < q come from the zero bits
+//    of the keep byte, and 01 is inserted at p, then at q.
+// Same results as decode_superblock (the exhaustive and random checks in the
+// test suite compare the two paths through the forward kernels).
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ uint32_t code_transpose(uint32_t x)
+{
+    uint32_t t = (x ^ (x >> 6)) & 0x00CC00CCu;
+    x ^= t ^ (t << 6);
+    t = (x ^ (x >> 12)) & 0x0000F0F0u;
+    x ^= t ^ (t << 12);
+    return x;
+}
+
+// code 01 inserted at position p (0..7) of a linear run of 2-bit codes
+__host__ __device__ __forceinline__ uint32_t insert_zero_code(uint32_t run, uint32_t p)
+{
+    const uint32_t lo = run & ((1u << (2 * p)) - 1u);
+    return lo | (1u << (2 * p)) | ((run >> (2 * p)) << (2 * p + 2));
+}
+
+// entry idx of the 2:4 table: keep nibble idx & 15, kept codes idx >> 4
+__host__ __device__ inline uint8_t nm24_table_entry(uint32_t idx)
+{
+    const uint32_t keep = idx & 15u, run = idx >> 4;
+    uint32_t pruned[2] = {0, 0}, np = 0;
+    for (uint32_t i = 0; i < 4; ++i)
+        if (!((keep >> i) & 1u) && np < 2) pruned[np++] = i;
+    if (np != 2) return 0x55;                      // not a 2:4 mask: never produced by the packer
+    return (uint8_t)insert_zero_code(insert_zero_code(run, pruned[0]), pruned[1]);
+}
+
+template <Pattern P>
+__host__ __device__ __forceinline__ void decode_superblock_fast(const uint32_t *vals, const uint32_t *masks,
+                                                                 uint32_t dense[4], const uint8_t *table24)
+{
+    if constexpr (P == Pattern::NM24) {
+        const uint32_t v[2] = {code_transpose(vals[0]), code_transpose(vals[1])};
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint32_t vw = v[d >> 1], mw = masks[d >> 1];
+            uint32_t lin = 0;
+#pragma unroll
+            for (int gl = 0; gl < 4; ++gl) {
+                const int off = 16 * (d & 1) + 4 * gl;
+                const uint32_t idx = ((mw >> off) & 15u) | (((vw >> off) & 15u) << 4);
+                lin |= (uint32_t)table24[idx] << (8 * gl);
+            }
+            dense[d] = code_transpose(lin);
+        }
+    } else {
+        const uint64_t lo = (uint64_t)code_transpose(vals[0]) | ((uint64_t)code_transpose(vals[1]) << 32);
+        const uint64_t hi = (uint64_t)code_transpose(vals[1]) | ((uint64_t)code_transpose(vals[2]) << 32);
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint32_t lin = 0;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int g = 2 * d + h, off = 12 * g;
+                const uint32_t run = (uint32_t)((off + 12 <= 64 ? lo >> off : hi >> (off - 32)) & 0xFFFu);
+                const uint32_t pm = ~(masks[g >> 2] >> (8 * (g & 3))) & 0xFFu;
+                const uint32_t p = __builtin_ctz(pm | 0x80u), q = 31 - __builtin_clz(pm | 1u);
+                lin |= insert_zero_code(insert_zero_code(run, p), q) << (16 * h);
+            }
+            dense[d] = code_transpose(lin);
         }
     }
 }

@@ -49,6 +49,7 @@ using skinny::unpack_word;
 using skinny::RawChunk;
 using skinny::load_raw_chunk;
 using skinny::decode_chunk;
+using skinny::fill_nm24_table;
 
 template <int KS, int CMAX, int MT, int ROWS>
 struct FusedLds {
@@ -84,6 +85,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     __shared__ float s_max[MT][KS];
     __shared__ int s_sum[MT][KS];
     __shared__ i32x4 s_part[RG][KS > 1 ? KS - 1 : 1][64];
+    __shared__ uint8_t s_nm24[P == Pattern::NM24 ? 256 : 1];
     extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];   // MT x (K + 192) int8
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -146,6 +148,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     }
 
     __builtin_amdgcn_sched_barrier(0);
+    fill_nm24_table<P>(s_nm24, tid, T);              // ready after the barrier below
 
     // (3a) max |x| per token over the whole row
 #pragma unroll
@@ -198,7 +201,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     // (4) weights to LDS
 #pragma unroll
     for (int i = 0; i < WLOADS; ++i)
-        if (w_off[i] >= 0) *reinterpret_cast<u32x4 *>(lw + w_off[i]) = decode_chunk<P>(w[i]);
+        if (w_off[i] >= 0) *reinterpret_cast<u32x4 *>(lw + w_off[i]) = decode_chunk<P>(w[i], s_nm24);
     __syncthreads();
 
     int rs[4];

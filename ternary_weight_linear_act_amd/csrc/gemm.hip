@@ -79,16 +79,17 @@ __device__ __forceinline__ void load_raw(const uint8_t *__restrict__ packed, int
     }
 }
 
-// 4 dense code words from a raw slice (N:M: decode the superblock)
+// 4 dense code words from a raw slice (N:M: decode the superblock; table24 is
+// the 2:4 decode table in LDS)
 template <Pattern P>
-__device__ __forceinline__ u32x4 dense_words(const RawSlice<P> &r)
+__device__ __forceinline__ u32x4 dense_words(const RawSlice<P> &r, const uint8_t *table24)
 {
-    if (P == Pattern::Dense) {
+    if constexpr (P == Pattern::Dense) {
         return u32x4{r.w[0], r.w[1], r.w[2], r.w[3]};
     } else {
         constexpr int VW = RawSlice<P>::kWords - 2;
         uint32_t w[4];
-        decode_superblock<P>(r.w, r.w + VW, w);
+        decode_superblock_fast<P>(r.w, r.w + VW, w, table24);
         return u32x4{w[0], w[1], w[2], w[3]};
     }
 }
@@ -176,11 +177,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LDB];
     __shared__ __attribute__((aligned(16))) int s_rs[BM];
     __shared__ __attribute__((aligned(16))) float s_sc[BM];
+    __shared__ uint8_t s_nm24[P == Pattern::NM24 ? 256 : 1];
 
     // the wave index is wave-uniform: say so, so that branches on it are scalar
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int h = lane >> 5, li = lane & 31;
+    if constexpr (P == Pattern::NM24) {
+        for (int i = tid; i < 256; i += T) s_nm24[i] = nm24_table_entry((uint32_t)i);
+        __syncthreads();
+    }
 
     const int64_t tiles_m = (M + BM - 1) / BM;
     const int64_t tiles_n = (N + BN - 1) / BN;
@@ -234,7 +240,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         for (int p = 0; p < B_PER_T; ++p) {
             const int row = p * T + tid;
             if (BN % T == 0 || row < BN) {
-                const u32x4 d = dense_words<P>(rb[p]);
+                const u32x4 d = dense_words<P>(rb[p], s_nm24);
                 u32x2 *dst = reinterpret_cast<u32x2 *>(sB[buf] + row * LDB);
                 dst[0] = u32x2{d[0], d[1]};
                 dst[1] = u32x2{d[2], d[3]};

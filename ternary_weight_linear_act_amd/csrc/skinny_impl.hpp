@@ -94,16 +94,26 @@ __device__ __forceinline__ RawChunk<P> load_raw_chunk(const uint8_t *__restrict_
     return r;
 }
 
+// table24: the 2:4 decode table in LDS (fill_nm24_table), unused otherwise
 template <Pattern P>
-__device__ __forceinline__ u32x4 decode_chunk(const RawChunk<P> &r)
+__device__ __forceinline__ u32x4 decode_chunk(const RawChunk<P> &r, const uint8_t *table24)
 {
     if constexpr (P == Pattern::Dense) {
         return u32x4{r.w[0], r.w[1], r.w[2], r.w[3]};
     } else {
         uint32_t w[4];
-        decode_superblock<P>(r.w, r.w + RawChunk<P>::kVals, w);
+        decode_superblock_fast<P>(r.w, r.w + RawChunk<P>::kVals, w, table24);
         return u32x4{w[0], w[1], w[2], w[3]};
     }
+}
+
+// fill the 256-byte 2:4 decode table (all threads of the workgroup; the
+// caller places a barrier before the first decode)
+template <Pattern P>
+__device__ __forceinline__ void fill_nm24_table(uint8_t *table24, int tid, int nthreads)
+{
+    if constexpr (P == Pattern::NM24)
+        for (int i = tid; i < 256; i += nthreads) table24[i] = nm24_table_entry((uint32_t)i);
 }
 
 // LDS bytes of one wave's staging area
@@ -130,6 +140,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     constexpr int XLOADS = (MT * CMAX * 4 + 63) / 64;
     __shared__ __attribute__((aligned(16))) uint8_t s_stage[KS][L::kBytes];
     __shared__ i32x4 s_part[KS > 1 ? KS - 1 : 1][64];
+    __shared__ uint8_t s_nm24[P == Pattern::NM24 ? 256 : 1];
 
     // the wave index is wave-uniform: say so, so that branches on it are scalar
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -191,6 +202,10 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
         }
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (P == Pattern::NM24) {
+        fill_nm24_table<P>(s_nm24, threadIdx.x, 64 * KS);
+        __syncthreads();
+    }
     // zero chunks after each activation row (12 pieces of 16 bytes), and the zero block
     for (int f = lane; f < mt * 12 + 4; f += 64) {
         const int off = (f < mt * 12) ? (f / 12) * L::kXStride + (cw * 4 + f % 12) * 16
@@ -215,7 +230,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h)
                 *reinterpret_cast<u32x4 *>(lw + (8 * h + lrow) * L::kStride + (8 * j + lcol) * 16) =
-                    decode_chunk<P>(w[j][h]);
+                    decode_chunk<P>(w[j][h], s_nm24);
             __builtin_amdgcn_s_waitcnt(0xc07f);              // lgkmcnt(0): staged
             __builtin_amdgcn_wave_barrier();
 #pragma unroll
