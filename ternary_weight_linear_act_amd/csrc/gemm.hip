@@ -29,7 +29,9 @@
 //
 // Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
 // consecutive logical tiles (which share a weight column tile) are mapped to
-// workgroups on the same XCD and reuse its L2.
+// workgroups on the same XCD and reuse its L2; the pipelined dense kernel
+// instead gives each XCD one block of a 4 x 2 partition of the tile grid when
+// the grid allows it.
 #include <algorithm>
 #include <mutex>
 #include <type_traits>
@@ -357,6 +359,20 @@ __device__ __forceinline__ void block_barrier()
 // applies the dequant scale.  Used when there are too few output tiles to fill
 // the chip (few tokens).  The kernel boundary makes the partials visible: no
 // fence or counter is needed.
+// Tile placement over the 8 XCDs (each has its own L2): when the tile grid
+// splits evenly into 4 x 2 regions, one region per XCD; otherwise tiles are
+// dealt round-robin with consecutive logical tiles on one XCD.
+__host__ __device__ inline bool xcd_regions(int64_t tiles_m, int64_t tiles_n)
+{
+    return tiles_m % 4 == 0 && tiles_n >= 2;
+}
+
+__host__ __device__ inline int64_t xcd_grid(int64_t tiles_m, int64_t tiles_n)
+{
+    if (xcd_regions(tiles_m, tiles_n)) return kXcds * (tiles_m / 4) * ((tiles_n + 1) / 2);
+    return (tiles_m * tiles_n + kXcds - 1) / kXcds * kXcds;
+}
+
 template <int BM, int BN, int WM, int WN, int S, bool SPLIT, int OCC = 1>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
@@ -393,10 +409,24 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(
     const int64_t grid_tiles = per_xcd * kXcds;
     const int64_t split = SPLIT ? (int64_t)blockIdx.x / grid_tiles : 0;
     const int64_t b = (int64_t)blockIdx.x - split * grid_tiles;
-    const int64_t tile = (b % kXcds) * per_xcd + b / kXcds;
-    if (tile >= tiles) return;
-    const int64_t m0 = (tile % tiles_m) * BM;
-    const int64_t n0 = (tile / tiles_m) * BN;
+    int64_t tile, m0, n0;
+    if (!SPLIT && xcd_regions(tiles_m, tiles_n)) {
+        // each XCD owns one of 4 x 2 blocks of the tile grid: a quarter of the
+        // activation rows and half of the weight columns stay in its L2
+        const int64_t x = b % kXcds, j = b / kXcds;
+        const int64_t mc = tiles_m / 4;
+        const int64_t nlo = tiles_n * (x / 4) / 2, nhi = tiles_n * (x / 4 + 1) / 2;
+        const int64_t mt = (x % 4) * mc + j % mc, nt = nlo + j / mc;
+        if (nt >= nhi) return;
+        tile = nt * tiles_m + mt;
+        m0 = mt * BM;
+        n0 = nt * BN;
+    } else {
+        tile = (b % kXcds) * per_xcd + b / kXcds;
+        if (tile >= tiles) return;
+        m0 = (tile % tiles_m) * BM;
+        n0 = (tile / tiles_m) * BN;
+    }
     const float beta = w_scale[0];
     for (int i = tid; i < BM; i += T) {
         const int64_t m = min(m0 + i, M - 1);
@@ -581,9 +611,10 @@ hipError_t launch_dma(const int8_t *Xq, const float *xs, const int32_t *rs, cons
                       const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                       hipStream_t stream, int32_t splits = 1, int32_t *ws = nullptr)
 {
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int64_t tiles = tiles_m * tiles_n;
     const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
-    const int64_t grid = per_xcd * kXcds * (SPLIT ? splits : 1);
+    const int64_t grid = SPLIT ? per_xcd * kXcds * splits : xcd_grid(tiles_m, tiles_n);
     const size_t lds = (size_t)S * (BM * 64 + BN * 16) + 8 * BM;
     auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SPLIT, OCC>;
     if (lds > 64 * 1024) {
