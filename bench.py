@@ -380,7 +380,7 @@ def main():
                    "M": 1, "projections": ["gate 2560x6912", "up 2560x6912", "down 6912x2560"]},
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(fused_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "fused_decode_kernel", "avg_launch_us": round(fused_us, 3),
+                     "kernel": dispatch, "avg_launch_us": round(fused_us, 3),
                      "bytes_per_launch": round(step_bytes / len(groups)), "per_group": per_group},
         "decode_two_call_path": {"step_us": round(two_call_us, 3),
                                  "GB/s": round(step_bytes / (two_call_us * 1e-6) / 1e9, 1),

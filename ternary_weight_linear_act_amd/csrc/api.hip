@@ -25,6 +25,10 @@ hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_
                                  const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
                                  int32_t *acc, hipStream_t stream, const char **name);
 
+hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
+                              int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
+                              hipStream_t stream, const char **name);
+
 // Largest M served by the dot4 GEMV (the fallback when the skinny MFMA kernel
 // has no configuration for the shape); larger M runs on the MFMA GEMM.
 constexpr int64_t kGemvMaxM = 4;
@@ -36,6 +40,17 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
 {
     static const char *gemv_names[3] = {"gemv_dense", "gemv_nm24", "gemv_nm68"};
     const int pi = (int)p;
+    if (M == 1) {
+        FusedProjArgs one = {};
+        one.nproj = 1;
+        one.packed[0] = packed;
+        one.w_scale[0] = w_scale;
+        one.Y[0] = Y;
+        one.acc[0] = acc;
+        one.N[0] = N;
+        const hipError_t e = launch_decode_dot4(nullptr, Xq, x_scale, x_rowsum, M, K, p, one, nullptr, stream, name);
+        if (e != hipErrorNotSupported) return e;
+    }
     if (M <= 16) {
         const hipError_t e = launch_skinny_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc,
                                                    stream, name);
@@ -246,7 +261,8 @@ bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, b
     CHECK(check_ptr(X, 16, "X"));
     if (x_scale && !aligned(x_scale, 4)) return fail(BITLINEAR_EINVAL, "x_scale must be 4-byte aligned");
     const char *name = "";
-    hipError_t e = bl::launch_fused_forward(X, M, K, p, args, x_scale, stream, &name);
+    hipError_t e = bl::launch_decode_dot4(X, nullptr, nullptr, nullptr, M, K, p, args, x_scale, stream, &name);
+    if (e == hipErrorNotSupported) e = bl::launch_fused_forward(X, M, K, p, args, x_scale, stream, &name);
     if (e == hipErrorNotSupported)
         return fail(BITLINEAR_EUNSUPPORTED, "fused decode supports 1 <= M <= 4 and K <= %s (M = %lld, K = %lld)",
                     M == 1 ? "65344" : "16192", (long long)M, (long long)K);

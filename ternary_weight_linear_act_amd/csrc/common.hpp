@@ -153,6 +153,8 @@ constexpr int kDppQuadXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
 constexpr int kDppQuadXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
 constexpr int kDppRowRor4 = 0x124;
 constexpr int kDppRowRor8 = 0x128;
+constexpr int kDppRowMirror = 0x140;       // lane i <- lane 15 - i within each row of 16
+constexpr int kDppRowHalfMirror = 0x141;   // lane i <- lane 7 - i within each half row of 8
 
 __device__ __forceinline__ float wave_max_dpp(float v)
 {

@@ -45,6 +45,7 @@ namespace fused {
 
 using skinny::i32x4;
 using skinny::u32x4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 using skinny::unpack_word;
 using skinny::RawChunk;
 using skinny::load_raw_chunk;
@@ -117,16 +118,16 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     //     waiting for them below leaves the weight loads in flight
     constexpr int XR = CMAX / 4;
     const int64_t n4 = K / 4;
-    float4 xr[MT][XR];
-    float g[MT];
+    f32x4 xr[MT][XR];                  // ext vectors: an array of HIP's float4 structs
+    float g[MT];                       // can end up in scratch memory
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
-        const float4 *x4 = reinterpret_cast<const float4 *>(X + (int64_t)min(m, mt - 1) * K);
+        const f32x4 *x4 = reinterpret_cast<const f32x4 *>(X + (int64_t)min(m, mt - 1) * K);
 #pragma unroll
         for (int j = 0; j < XR; ++j) {
             const int64_t i = tid + (int64_t)j * T;
-            const float4 a = x4[i < n4 ? i : 0];
-            xr[m][j] = (m < mt && i < n4) ? a : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            const f32x4 a = x4[i < n4 ? i : 0];
+            xr[m][j] = (m < mt && i < n4) ? a : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -156,8 +157,8 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
         float v = 0.0f;
 #pragma unroll
         for (int j = 0; j < XR; ++j) {
-            const float4 a = xr[m][j];
-            v = fmaxf(v, fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w))));
+            const f32x4 a = xr[m][j];
+            v = fmaxf(v, fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3]))));
         }
         v = wave_max_dpp(v);
         if (lane == 0) s_max[m][wave] = v;
@@ -183,9 +184,9 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
             for (int j = 0; j < XR; ++j) {
                 const int64_t i = tid + (int64_t)j * T;
                 if (i < n4) {
-                    const float4 a = xr[m][j];
+                    const f32x4 a = xr[m][j];
                     int qa = 0, qb = 0, qc = 0, qd = 0;
-                    if (!zero) { qa = quant1(a.x, s); qb = quant1(a.y, s); qc = quant1(a.z, s); qd = quant1(a.w, s); }
+                    if (!zero) { qa = quant1(a[0], s); qb = quant1(a[1], s); qc = quant1(a[2], s); qd = quant1(a[3], s); }
                     sum += qa + qb + qc + qd;
                     q4[i] = (qa & 0xFF) | ((qb & 0xFF) << 8) | ((qc & 0xFF) << 16) | ((qd & 0xFF) << 24);
                 }

@@ -153,7 +153,7 @@ def test_deterministic_and_dispatch():
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(10, 300, 384, 512)
     packed, ws = hip_pack(W, (0, 0))
-    for M, expect in [(1, "skinny"), (4, "skinny"), (16, "skinny"), (17, "gemm"), (300, "gemm")]:
+    for M, expect in [(1, "decode_dot4"), (4, "skinny"), (16, "skinny"), (17, "gemm"), (300, "gemm")]:
         Xq, xs, rs = hip_quant(X[:M])
         Y1, a1 = hip_forward(Xq, xs, rs, packed, ws, 384, (0, 0))
         name = bl.last_dispatch()
