@@ -219,11 +219,15 @@ def main():
 
     # correctness gate before timing: kernel choice and values vs the oracle
     import oracle
-    decode_step(0)
+    group_kernel = {}
+    for g in groups:
+        bl.forward_fused(Xg[g][0], [(packed[n][0], wsc[n], shapes[n][0]) for n in g], Ys=[Y[n] for n in g])
+        group_kernel["+".join(g)] = bl.last_dispatch()
     torch.cuda.synchronize()
-    dispatch = bl.last_dispatch()
-    if not dispatch.startswith("fused_decode"):
-        raise SystemExit("unexpected kernel for the M=1 decode step: %s" % dispatch)
+    for g, k in group_kernel.items():
+        if not k.startswith("fused_decode"):
+            raise SystemExit("unexpected kernel for the M=1 decode step (%s): %s" % (g, k))
+    dispatch = ", ".join("%s: %s" % gk for gk in group_kernel.items())
     for name, (N, K) in shapes.items():
         beta, w_eff, _ = oracle.quantize_weights(d.W[name])
         q, xso, _ = oracle.quant_act(d.X[(name, 1)])
@@ -274,7 +278,7 @@ def main():
                 bl.forward_fused(Xg[g][j], [(packed[n][j], wsc[n], shapes[n][0]) for n in g],
                                  Ys=[Y[n] for n in g])
         ms, _ = timed_graph(torch, one, reps=3)
-        per_group["+".join(g)] = {"us": round(ms * 1e3 / P, 3),
+        per_group["+".join(g)] = {"kernel": group_kernel["+".join(g)], "us": round(ms * 1e3 / P, 3),
                                   "GB/s": round(group_bytes(g) / (ms * 1e-3 / P) / 1e9, 1)}
 
     # context: the two-call path (quant_act, then forward per projection)
