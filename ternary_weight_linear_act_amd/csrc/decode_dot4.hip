@@ -130,13 +130,14 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
 
     // 3. the int8 activations into LDS, with their scale and row sum
     if constexpr (FUSED) {
+        // branch-free: entries past the row (re-reads of element 0) are
+        // masked out of the max and the sum and never stored
         float g = 0.0f;
 #pragma unroll
         for (int t = 0; t < XR; ++t) {
-            if (tid + (int64_t)t * kThreads < n4) {
-                const f32x4 a = xf[t];
-                g = fmaxf(g, fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3]))));
-            }
+            const f32x4 a = xf[t];
+            const float m = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3])));
+            g = fmaxf(g, tid + (int64_t)t * kThreads < n4 ? m : 0.0f);
         }
         g = wave_max_dpp(g);
         if (lane == 0) s_max[wave] = g;
@@ -144,20 +145,18 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
         g = s_max[0];
 #pragma unroll
         for (int i = 1; i < W; ++i) g = fmaxf(g, s_max[i]);
-        const bool zero = (g == 0.0f);
-        const float s = zero ? 0.0f : 127.0f / g;
+        // g == 0: every entry is +-0 and quantises to 0 with s = 0 as well
+        const float s = (g == 0.0f) ? 0.0f : 127.0f / g;
         int sum = 0;
         int *q4 = reinterpret_cast<int *>(s_x);
 #pragma unroll
         for (int t = 0; t < XR; ++t) {
             const int64_t i = tid + (int64_t)t * kThreads;
-            if (i < n4) {
-                const f32x4 a = xf[t];
-                int qa = 0, qb = 0, qc = 0, qd = 0;
-                if (!zero) { qa = quant1(a[0], s); qb = quant1(a[1], s); qc = quant1(a[2], s); qd = quant1(a[3], s); }
-                sum += qa + qb + qc + qd;
-                q4[i] = (qa & 0xFF) | ((qb & 0xFF) << 8) | ((qc & 0xFF) << 16) | ((qd & 0xFF) << 24);
-            }
+            const f32x4 a = xf[t];
+            const int qa = quant1(a[0], s), qb = quant1(a[1], s), qc = quant1(a[2], s), qd = quant1(a[3], s);
+            const bool in = i < n4;
+            sum += in ? qa + qb + qc + qd : 0;
+            if (in) q4[i] = (qa & 0xFF) | ((qb & 0xFF) << 8) | ((qc & 0xFF) << 16) | ((qd & 0xFF) << 24);
         }
         sum = wave_sum_dpp(sum);
         if (lane == 0) s_sum[wave] = sum;
@@ -165,7 +164,7 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
         rs = s_sum[0];
 #pragma unroll
         for (int i = 1; i < W; ++i) rs += s_sum[i];
-        xsc = zero ? 0.0f : g / 127.0f;
+        xsc = (g == 0.0f) ? 0.0f : g / 127.0f;
         if (x_scale_out && blockIdx.x == 0 && tid == 0) x_scale_out[0] = xsc;
     } else {
 #pragma unroll
