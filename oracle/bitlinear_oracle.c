@@ -235,9 +235,15 @@ int oracle_quant_act(const float *X, int64_t M, int64_t K, int variant,
                 for (int64_t k = 0; k < K; ++k) q[r * K + k] = 0;
                 x_scale[r] = 0.0f;
             } else {
-                float s = 127.0f / g;
+                /* A row whose max|x| is below 2^-100 is scaled by 2^100 first:
+                 * fl32(127/g) overflows to +inf once g < 127/FLT_MAX, which
+                 * would turn x*s into +-inf, or NaN where x = 0.  Multiplying
+                 * by a power of two is exact here (|x| <= g), so q is the one
+                 * the unscaled formula gives wherever its s is finite. */
+                const float up = (g < 0x1p-100f) ? 0x1p100f : 1.0f;
+                float s = 127.0f / (g * up);
                 for (int64_t k = 0; k < K; ++k) {
-                    float v = rintf(x[k] * s);
+                    float v = rintf((x[k] * up) * s);
                     if (v > 127.0f) v = 127.0f;
                     if (v < -128.0f) v = -128.0f;
                     q[r * K + k] = (int8_t)v;

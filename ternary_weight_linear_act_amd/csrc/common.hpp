@@ -180,4 +180,35 @@ __device__ __forceinline__ int wave_sum_dpp(int v)
            __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
 }
 
+// ---------------------------------------------------------------------------
+// Per-token absmax int8 activation quantisation ("BitNet b1.58 2B4T Technical
+// Report 요약 설명", sec. 2; "BitNet 논문 분석: 1-Bit LLM의 시대", section
+// "Absmean 양자화 함수"): g = max|x|, s = fl32(127/g), q = rne(fl32(x*s)).
+//
+// A row with g < 2^-100 is first scaled by 2^100 (exact: |x| <= g), since
+// fl32(127/g) overflows to +inf once g < 127/FLT_MAX; wherever the unscaled s
+// is finite this gives the same q.  With that, |fl32(x*s)| <= 127 * (1 +
+// 2^-23) * (1 + 2^-24) < 127.5 for finite x, so the clamp to [-128, 127]
+// never binds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float act_prescale(float g) { return g < 0x1p-100f ? 0x1p100f : 1.0f; }
+
+// s for the (prescaled) row; 0 for an all-zero row, whose codes are then 0
+__device__ __forceinline__ float act_scale(float g, float up) { return g == 0.0f ? 0.0f : 127.0f / (g * up); }
+
+// rne(fl32(x*s)) for |x*s| < 2^22: adding 1.5 * 2^23 rounds half to even
+// onto the unit bits of the sum, which hold the integer in two's complement,
+// so the sum's low byte is the int8 code.  The product is rounded on its
+// own (no contraction: the library is built with -ffp-contract=off).
+__device__ __forceinline__ uint32_t act_round_bits(float x, float s) { return __float_as_uint(x * s + 0x1.8p23f); }
+
+// four codes packed little-endian into one word; *sum receives their sum
+__device__ __forceinline__ uint32_t act_quant4(float x0, float x1, float x2, float x3, float s, int *sum)
+{
+    const uint32_t b0 = act_round_bits(x0, s), b1 = act_round_bits(x1, s);
+    const uint32_t b2 = act_round_bits(x2, s), b3 = act_round_bits(x3, s);
+    *sum = (int)(b0 + b1 + b2 + b3 - 4u * 0x4B400000u);
+    return (b0 & 0xFFu) | ((b1 & 0xFFu) << 8) | ((b2 & 0xFFu) << 16) | (b3 << 24);
+}
+
 }  // namespace bl

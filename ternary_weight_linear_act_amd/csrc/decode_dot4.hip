@@ -51,13 +51,6 @@ __device__ __forceinline__ int lanes_sum(int v)
     return v;
 }
 
-__device__ __forceinline__ int quant1(float x, float s)
-{
-    float r = rintf(x * s);
-    r = fminf(fmaxf(r, -128.0f), 127.0f);
-    return (int)r;
-}
-
 // FUSED: X is the fp32 activation row (quantised here; x_scale_out, if not
 // NULL, receives its scale); otherwise Xq / x_scale / x_rowsum are the
 // quantised row.  args.block_start[i] is the first workgroup of projection i.
@@ -145,18 +138,23 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
         g = s_max[0];
 #pragma unroll
         for (int i = 1; i < W; ++i) g = fmaxf(g, s_max[i]);
-        // g == 0: every entry is +-0 and quantises to 0 with s = 0 as well
-        const float s = (g == 0.0f) ? 0.0f : 127.0f / g;
+        const float up = act_prescale(g);
+        const float s = act_scale(g, up);
+        if (up != 1.0f) {                              // workgroup-uniform, rare
+#pragma unroll
+            for (int t = 0; t < XR; ++t) xf[t] *= up;
+        }
         int sum = 0;
-        int *q4 = reinterpret_cast<int *>(s_x);
+        uint32_t *q4 = reinterpret_cast<uint32_t *>(s_x);
 #pragma unroll
         for (int t = 0; t < XR; ++t) {
             const int64_t i = tid + (int64_t)t * kThreads;
             const f32x4 a = xf[t];
-            const int qa = quant1(a[0], s), qb = quant1(a[1], s), qc = quant1(a[2], s), qd = quant1(a[3], s);
+            int s4;
+            const uint32_t packed4 = act_quant4(a[0], a[1], a[2], a[3], s, &s4);
             const bool in = i < n4;
-            sum += in ? qa + qb + qc + qd : 0;
-            if (in) q4[i] = (qa & 0xFF) | ((qb & 0xFF) << 8) | ((qc & 0xFF) << 16) | ((qd & 0xFF) << 24);
+            sum += in ? s4 : 0;
+            if (in) q4[i] = packed4;
         }
         sum = wave_sum_dpp(sum);
         if (lane == 0) s_sum[wave] = sum;

@@ -59,13 +59,6 @@ struct FusedLds {
     static constexpr int kZero = 256;                         // zero block (token rows >= M)
 };
 
-__device__ __forceinline__ int quant1(float x, float s)
-{
-    float r = rintf(x * s);
-    r = fminf(fmaxf(r, -128.0f), 127.0f);
-    return (int)r;
-}
-
 // KS waves split K; at most CMAX chunks per wave; at most MT (<= 4) tokens;
 // ROWS weight rows per workgroup: 16 (one MFMA column block), 32 (two), or 8
 // (the MFMA's columns 8..15 repeat rows 0..7 and are not stored: twice the
@@ -177,18 +170,18 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     for (int m = 0; m < MT; ++m) {
         int sum = 0;
         if (m < mt) {
-            int *q4 = reinterpret_cast<int *>(s_x + m * xstride);
-            const bool zero = (g[m] == 0.0f);
-            const float s = zero ? 0.0f : 127.0f / g[m];
+            uint32_t *q4 = reinterpret_cast<uint32_t *>(s_x + m * xstride);
+            const float up = act_prescale(g[m]);
+            const float s = act_scale(g[m], up);
 #pragma unroll
             for (int j = 0; j < XR; ++j) {
                 const int64_t i = tid + (int64_t)j * T;
+                const f32x4 a = xr[m][j] * up;             // up = 1 unless max|x| < 2^-100
+                int s4;
+                const uint32_t packed4 = act_quant4(a[0], a[1], a[2], a[3], s, &s4);
                 if (i < n4) {
-                    const f32x4 a = xr[m][j];
-                    int qa = 0, qb = 0, qc = 0, qd = 0;
-                    if (!zero) { qa = quant1(a[0], s); qb = quant1(a[1], s); qc = quant1(a[2], s); qd = quant1(a[3], s); }
-                    sum += qa + qb + qc + qd;
-                    q4[i] = (qa & 0xFF) | ((qb & 0xFF) << 8) | ((qc & 0xFF) << 16) | ((qd & 0xFF) << 24);
+                    sum += s4;
+                    q4[i] = packed4;
                 }
             }
             // 3 zero chunks after the row

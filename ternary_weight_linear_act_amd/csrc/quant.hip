@@ -4,7 +4,8 @@
 // token's activations become 8-bit integers scaled by that token's absolute
 // maximum; "BitNet 논문 분석: 1-Bit LLM의 시대", section "Absmean 양자화 함수"
 // (activation_quant): round, then clamp to the int8 range.  Scale 127/max|x|
-// computed once per row, then multiplied in; round half to even.
+// computed once per row, then multiplied in; round half to even (the
+// arithmetic and the tiny-row rule are in common.hpp).
 //
 // One workgroup per row.  Pass 1 reads the row with 16-byte loads and reduces
 // |x| to the row maximum (exact, order-free) through DPP lane moves and LDS.
@@ -17,13 +18,6 @@ namespace {
 
 constexpr int kQuantBlock = 256;
 constexpr int kWaves = kQuantBlock / 64;
-
-__device__ __forceinline__ int quant1(float x, float s)
-{
-    float r = rintf(x * s);
-    r = fminf(fmaxf(r, -128.0f), 127.0f);
-    return (int)r;
-}
 
 __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
     const float *__restrict__ X, int64_t K, int8_t *__restrict__ Xq,
@@ -50,15 +44,21 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
     for (int w = 1; w < kWaves; ++w) g = fmaxf(g, s_max[w]);
 
     int sum = 0;
-    if (g == 0.0f) {
-        for (int64_t i = tid; i < n4; i += kQuantBlock) q4[i] = 0;
-    } else {
-        const float s = 127.0f / g;          // IEEE binary32 division
+    const float up = act_prescale(g);
+    const float s = act_scale(g, up);        // IEEE binary32 division
+    if (up == 1.0f) {
         for (int64_t i = tid; i < n4; i += kQuantBlock) {
             const float4 v = x4[i];
-            const int a = quant1(v.x, s), b = quant1(v.y, s), c = quant1(v.z, s), d = quant1(v.w, s);
-            sum += a + b + c + d;
-            q4[i] = (a & 0xFF) | ((b & 0xFF) << 8) | ((c & 0xFF) << 16) | ((d & 0xFF) << 24);
+            int s4;
+            q4[i] = (int)act_quant4(v.x, v.y, v.z, v.w, s, &s4);
+            sum += s4;
+        }
+    } else {
+        for (int64_t i = tid; i < n4; i += kQuantBlock) {
+            const float4 v = x4[i];
+            int s4;
+            q4[i] = (int)act_quant4(v.x * up, v.y * up, v.z * up, v.w * up, s, &s4);
+            sum += s4;
         }
     }
     sum = wave_sum_dpp(sum);

@@ -26,9 +26,10 @@ MUTANTS = {
     "bit_position": ("int bit = 8 * (j % 4) + 2 * (j / 4);", "int bit = 2 * j;"),
     "code_offset": ("put_code(out + r * (K / 4), k, (unsigned)(v + 1));",
                     "put_code(out + r * (K / 4), k, (unsigned)(1 - v));"),
-    "act_const_128": ("float s = 127.0f / g;", "float s = 128.0f / g;"),
-    "act_round_half_away": ("float v = rintf(x[k] * s);", "float v = roundf(x[k] * s);"),
-    "act_order": ("float v = rintf(x[k] * s);", "float v = rintf((x[k] * 127.0f) / g);"),
+    "act_const_128": ("float s = 127.0f / (g * up);", "float s = 128.0f / (g * up);"),
+    "act_round_half_away": ("float v = rintf((x[k] * up) * s);", "float v = roundf((x[k] * up) * s);"),
+    "act_order": ("float v = rintf((x[k] * up) * s);", "float v = rintf((x[k] * 127.0f) / g);"),
+    "act_no_tiny_row_scaling": ("const float up = (g < 0x1p-100f) ? 0x1p100f : 1.0f;", "const float up = 1.0f;"),
     "xscale_inverse": ("x_scale[r] = g / 127.0f;", "x_scale[r] = 127.0f / g;"),
     "transposed_w": ("s += (int64_t)q[m * K + k] * (int64_t)w_eff[n * K + k];",
                      "s += (int64_t)q[m * K + k] * (int64_t)w_eff[k * N + n];"),

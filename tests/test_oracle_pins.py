@@ -385,6 +385,28 @@ class TestQuantAct:
             assert np.array_equal(q0, q1)
             assert np.array_equal(xs1, (xs0 * F32(2.0 ** e)).astype(np.float32))
 
+    def test_tiny_row_hand_example(self):
+        # g = 2^-125: fl32(127/g) would be 127 * 2^125 > FLT_MAX (+inf), so x*s
+        # would be +-inf and 0*s NaN.  The row is taken at 2^100 times its
+        # size (exact), where s = 127 * 2^25: 2^-127 / 2^-125 * 127 = 31.75 -> 32.
+        X = np.array([[2.0 ** -125, -(2.0 ** -125), 0.0, 2.0 ** -127]], np.float32)
+        q, xs, rs = oracle.quant_act(X)
+        assert q.tolist() == [[127, -127, 0, 32]]
+        assert rs[0] == 32
+        assert xs[0] == np.float32(F32(2.0 ** -125) / F32(127))
+
+    def test_power_of_two_invariance_down_to_overflow(self):
+        # entries of magnitude in [1, 2) (and zeros) stay normal down to 2^-125,
+        # so the scaling is exact; below g = 2^-121.3 the unscaled s overflows
+        rng = np.random.default_rng(9)
+        X = (rng.uniform(1.0, 2.0, (8, 256)) * rng.choice([-1.0, 1.0], (8, 256))).astype(np.float32)
+        X[:, ::17] = 0.0
+        q0, _, rs0 = oracle.quant_act(X)
+        for e in (-90, -101, -110, -122, -125):
+            q1, _, rs1 = oracle.quant_act((X * F32(2.0 ** e)).astype(np.float32))
+            assert np.array_equal(q0, q1), e
+            assert np.array_equal(rs0, rs1), e
+
     def test_listing_variant_differs(self):
         # the 128/(g+1e-5) form printed in the listing can reach -128; 127/g cannot
         X = np.array([[-1.0, 0.5]], np.float32)
