@@ -26,7 +26,10 @@
  *   N:M     = per row n and group [g*M, g*M+M): keep the N largest |W[n,k]|,
  *             equal magnitudes resolved towards the lower k
  *   g_m     = max_k |X[m,k]|;  if g_m == 0: Xq = 0, x_scale = 0
- *   s_m     = fl32(127 / g_m);  Xq[m,k] = clamp(rne(fl32(X[m,k] * s_m)), -128, 127)
+ *   u_m     = 2^100 if g_m < 2^-100, else 1   (exact rescaling of rows whose
+ *             127 / g_m would overflow; q is unchanged wherever it does not)
+ *   s_m     = fl32(127 / fl32(g_m * u_m))
+ *   Xq[m,k] = clamp(rne(fl32(fl32(X[m,k] * u_m) * s_m)), -128, 127)
  *   x_scale = fl32(g_m / 127);  x_rowsum[m] = sum_k Xq[m,k]
  *   acc     = sum_k Xq[m,k] * W_eff[n,k]          (exact int32)
  *   Y[m,n]  = fl32( fl32(acc) * fl32(beta * x_scale[m]) )
