@@ -181,6 +181,96 @@ __device__ __forceinline__ int wave_sum_dpp(int v)
 }
 
 // ---------------------------------------------------------------------------
+// One-token N:M dot product without decoding to dense codes (the one-token
+// decode kernel).  A value word's 16 kept codes c = t + 1 become 64 * t as
+// signed bytes: (c - 1) mod 4 per 2-bit field by an add that cannot carry out
+// of its field, then each field moved to the top of its byte.  Byte b of u[s]
+// holds kept code 4s + b of the word, the order of the packed layout.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline void nm_tbytes(uint32_t V, uint32_t u[4])
+{
+    const uint32_t t2 = ((V & 0x55555555u) + 0x55555555u) ^ (~V & 0xAAAAAAAAu);
+    u[0] = (t2 << 6) & 0xC0C0C0C0u;
+    u[1] = (t2 << 4) & 0xC0C0C0C0u;
+    u[2] = (t2 << 2) & 0xC0C0C0C0u;
+    u[3] = t2 & 0xC0C0C0C0u;
+}
+
+// Byte-permute selectors (v_perm_b32: values 0-3 pick a byte of the second
+// source, 4-7 of the first, 12 gives a zero byte) that spread a group's kept
+// t-bytes over its positions; pruned positions get zero bytes.
+//   2:4: entry i = the mask byte of groups 2h, 2h+1 (even group in the low
+//        nibble).  Source: the word whose bytes 0-1 are the even group's kept
+//        t-bytes and 2-3 the odd group's.  lo / hi select the even / odd
+//        group's 4 positions.
+//   6:8: entry i = mask byte | (group parity << 8).  Sources: the two t-byte
+//        words holding the group's 6 kept codes, which start at byte 0 of the
+//        first (even group) or byte 2 (odd).  lo / hi: positions 0-3 / 4-7.
+constexpr int nm_sel_entries(Pattern p) { return p == Pattern::NM24 ? 256 : 512; }
+
+template <Pattern P>
+__host__ __device__ inline void nm_sel_entry(int i, uint32_t *lo, uint32_t *hi)
+{
+    uint64_t sel = 0x0C0C0C0C0C0C0C0Cull;
+    if (P == Pattern::NM24) {
+        for (int half = 0; half < 2; ++half) {
+            const int m = (i >> (4 * half)) & 15;
+            for (int p = 0, k = 0; p < 4; ++p)
+                if ((m >> p) & 1) {
+                    const int sh = 8 * (4 * half + p);
+                    if (k < 2) sel = (sel & ~(0xFFull << sh)) | ((uint64_t)(2 * half + k) << sh);
+                    ++k;
+                }
+        }
+    } else {
+        const int m = i & 0xFF, base = ((i >> 8) & 1) ? 2 : 0;
+        for (int p = 0, k = 0; p < 8; ++p)
+            if ((m >> p) & 1) {
+                if (k < 6) sel = (sel & ~(0xFFull << (8 * p))) | ((uint64_t)(base + k) << (8 * p));
+                ++k;
+            }
+    }
+    *lo = (uint32_t)sel;
+    *hi = (uint32_t)(sel >> 32);
+}
+
+// acc[0..3] += 64 * sum over the superblock's 64 positions of t * x, with x
+// the superblock's activation bytes (16 words of 4 int8) and t = 0 at pruned
+// positions.  tab: nm_sel_entries(P) (lo, hi) word pairs.  OPS::perm(s0, s1,
+// sel) and OPS::dot4(a, b, acc) are v_perm_b32 and v_dot4_i32_i8 on the GPU
+// (an emulation in the host check).
+template <Pattern P, class OPS>
+__host__ __device__ inline void nm_dot_superblock(const uint32_t *vals, const uint32_t *masks, const uint32_t *tab,
+                                                  const int32_t *xw, int *acc)
+{
+    if constexpr (P == Pattern::NM24) {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+            uint32_t u[4];
+            nm_tbytes(vals[v], u);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const uint32_t i = (masks[v] >> (8 * s)) & 0xFFu;
+                const int g = 8 * v + 2 * s;
+                acc[s] = OPS::dot4((int)OPS::perm(u[s], u[s], tab[2 * i]), xw[g], acc[s]);
+                acc[s] = OPS::dot4((int)OPS::perm(u[s], u[s], tab[2 * i + 1]), xw[g + 1], acc[s]);
+            }
+        }
+    } else {
+        uint32_t u[12];
+#pragma unroll
+        for (int v = 0; v < 3; ++v) nm_tbytes(vals[v], u + 4 * v);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) {
+            const uint32_t i = ((masks[g >> 2] >> (8 * (g & 3))) & 0xFFu) | ((uint32_t)(g & 1) << 8);
+            const int d = (3 * g) >> 1;                  // first word of the group's 6 kept codes
+            acc[g & 3] = OPS::dot4((int)OPS::perm(u[d + 1], u[d], tab[2 * i]), xw[2 * g], acc[g & 3]);
+            acc[g & 3] = OPS::dot4((int)OPS::perm(u[d + 1], u[d], tab[2 * i + 1]), xw[2 * g + 1], acc[g & 3]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per-token absmax int8 activation quantisation ("BitNet b1.58 2B4T Technical
 // Report 요약 설명", sec. 2; "BitNet 논문 분석: 1-Bit LLM의 시대", section
 // "Absmean 양자화 함수"): g = max|x|, s = fl32(127/g), q = rne(fl32(x*s)).

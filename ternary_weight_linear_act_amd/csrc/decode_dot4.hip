@@ -31,13 +31,17 @@ namespace dot4 {
 using skinny::i32x4;
 using skinny::u32x4;
 using skinny::RawChunk;
-using skinny::decode_chunk;
-using skinny::fill_nm24_table;
 using skinny::load_raw_chunk;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxK = 16384;                 // activation row in LDS and registers
+
+// v_perm_b32 and v_dot4_i32_i8 for nm_dot_superblock
+struct DeviceOps {
+    __device__ static uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) { return __builtin_amdgcn_perm(s0, s1, sel); }
+    __device__ static int dot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+};
 
 template <int LPR>
 __device__ __forceinline__ int lanes_sum(int v)
@@ -67,7 +71,7 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
     extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];      // K int8 activations
     __shared__ float s_max[W];
     __shared__ int s_sum[W];
-    __shared__ uint8_t s_nm24[P == Pattern::NM24 ? 256 : 1];
+    __shared__ uint32_t s_sel[P == Pattern::Dense ? 1 : 2 * nm_sel_entries(P)];   // N:M byte selectors
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     int p = 0;
@@ -119,7 +123,8 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) w[u] = load_raw_chunk<P>(packed, N, K, r, min((int64_t)(j + u * LPR), C - 1));
     __builtin_amdgcn_sched_barrier(0);
-    fill_nm24_table<P>(s_nm24, tid, kThreads);
+    if constexpr (P != Pattern::Dense)                 // ready after the barrier below
+        for (int i = tid; i < nm_sel_entries(P); i += kThreads) nm_sel_entry<P>(i, &s_sel[2 * i], &s_sel[2 * i + 1]);
 
     // 3. the int8 activations into LDS, with their scale and row sum
     if constexpr (FUSED) {
@@ -174,36 +179,64 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
     }
 
     // 4. dot products, branch-free (a branch per chunk would make the
-    //    compiler wait for every weight load at the first one): 16 v_dot4
-    //    per chunk against 64 activation bytes.  In word w, code pair s of
-    //    each byte is (w >> 2s) & 0x03; pairs 1 and 2 are taken in place
-    //    (masks 0x0C, 0x30: the code times 4 or 16, still a positive int8)
-    //    into accumulators of their own, divided back exactly at the end;
-    //    pair 3 is shifted down (times 64 would not fit an int8).  Chunks
-    //    past the row (c >= C, last round only) get zero codes.
-    int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
+    //    compiler wait for every weight load at the first one), 16 v_dot4
+    //    per chunk against 64 activation bytes; chunks past the row (c >= C,
+    //    last round only) contribute nothing.
+    int acc;
+    if constexpr (P == Pattern::Dense) {
+        // In word w, code pair s of each byte is (w >> 2s) & 0x03; pairs 1
+        // and 2 are taken in place (masks 0x0C, 0x30: the code times 4 or
+        // 16, still a positive int8) into accumulators of their own, divided
+        // back exactly at the end; pair 3 is shifted down (times 64 would not
+        // fit an int8).
+        int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t c = j + u * LPR;
-        const bool in = c < C;
-        const u32x4 d = decode_chunk<P>(w[u], s_nm24);
-        const i32x4 *xp = reinterpret_cast<const i32x4 *>(s_x + (in ? c : C - 1) * 64);
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = j + u * LPR;
+            const bool in = c < C;
+            const i32x4 *xp = reinterpret_cast<const i32x4 *>(s_x + (in ? c : C - 1) * 64);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const i32x4 xx = xp[q];
-            const uint32_t word = in ? d[q] : 0u;
-            a0 = __builtin_amdgcn_sdot4((int)(word & kCodeMask), xx[0], a0, false);
-            a1 = __builtin_amdgcn_sdot4((int)(word & (kCodeMask << 2)), xx[1], a1, false);
-            a2 = __builtin_amdgcn_sdot4((int)(word & (kCodeMask << 4)), xx[2], a2, false);
-            a3 = __builtin_amdgcn_sdot4((int)((word >> 6) & kCodeMask), xx[3], a3, false);
+            for (int q = 0; q < 4; ++q) {
+                const i32x4 xx = xp[q];
+                const uint32_t word = in ? w[u].w[q] : 0u;
+                a0 = __builtin_amdgcn_sdot4((int)(word & kCodeMask), xx[0], a0, false);
+                a1 = __builtin_amdgcn_sdot4((int)(word & (kCodeMask << 2)), xx[1], a1, false);
+                a2 = __builtin_amdgcn_sdot4((int)(word & (kCodeMask << 4)), xx[2], a2, false);
+                a3 = __builtin_amdgcn_sdot4((int)((word >> 6) & kCodeMask), xx[3], a3, false);
+            }
         }
+        // a1 = 4 * S1 and a2 = 16 * S2 exactly, so the shifts are exact;
+        // |a2| <= 16 * 2 * 127 * K / 4 < 2^31 for K <= 16384
+        acc = a0 + (a1 >> 2) + (a2 >> 4) + a3;
+    } else {
+        // N:M: the kept codes are not decoded to dense words; each group's
+        // kept weights, as 64 * t bytes, are spread over its positions by a
+        // byte permute (nm_dot_superblock), pruned positions 0.  Chunks past
+        // the row get code 1 (t = 0) everywhere.
+        int a4[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t c = j + u * LPR;
+            const bool in = c < C;
+            const i32x4 *xp = reinterpret_cast<const i32x4 *>(s_x + (in ? c : C - 1) * 64);
+            int32_t xw[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const i32x4 xx = xp[q];
+                xw[4 * q] = xx[0]; xw[4 * q + 1] = xx[1]; xw[4 * q + 2] = xx[2]; xw[4 * q + 3] = xx[3];
+            }
+            uint32_t vals[RawChunk<P>::kVals];
+#pragma unroll
+            for (int v = 0; v < RawChunk<P>::kVals; ++v) vals[v] = in ? w[u].w[v] : 0x55555555u;
+            nm_dot_superblock<P, DeviceOps>(vals, w[u].w + RawChunk<P>::kVals, s_sel, xw, a4);
+        }
+        // every term is 64 * t * x: the shift is exact; |sum| <= 64 * 128 * K < 2^31
+        acc = (a4[0] + a4[1] + a4[2] + a4[3]) >> 6;
     }
-    // a1 = 4 * S1 and a2 = 16 * S2 exactly, so the shifts are exact; |a2| <=
-    // 16 * 2 * 127 * K / 4 < 2^31 for K <= 16384
-    int acc = a0 + (a1 >> 2) + (a2 >> 4) + a3;
     acc = lanes_sum<LPR>(acc);
     if (j == 0 && row < N) {
-        const int av = acc - rs;
+        // dense codes are t + 1: subtract the activation row sum
+        const int av = (P == Pattern::Dense) ? acc - rs : acc;
         Y[row] = (float)av * (wsc * xsc);
         if (acc_out) acc_out[row] = av;
     }
