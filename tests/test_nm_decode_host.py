@@ -1,9 +1,12 @@
 """CPU check of the fast N:M decode used by the forward kernels.
 
 tests/host/nm_decode_check.cpp includes the kernels' common header as host
-code and compares decode_superblock_fast (transpose + table / insertion) with
-the bit-by-bit decode_superblock on 200000 random valid superblocks per
-pattern.  The GPU parity tests then check both against the oracle.
+code and, on 200000 random valid superblocks per pattern, compares
+decode_superblock_fast (transpose + table / insertion) with the bit-by-bit
+decode_superblock, and the one-token permute dot (nm_dot_superblock, with
+v_perm_b32 and v_dot4 emulated) with sum (c - 1) * x over the reference
+decode on random int8 activations.  The GPU parity tests then check the
+kernels against the oracle.
 """
 import os
 import shutil
