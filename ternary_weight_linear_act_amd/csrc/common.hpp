@@ -234,14 +234,13 @@ __host__ __device__ inline void nm_sel_entry(int i, uint32_t *lo, uint32_t *hi)
     *hi = (uint32_t)(sel >> 32);
 }
 
-// acc[0..3] += 64 * sum over the superblock's 64 positions of t * x, with x
-// the superblock's activation bytes (16 words of 4 int8) and t = 0 at pruned
-// positions.  tab: nm_sel_entries(P) (lo, hi) word pairs.  OPS::perm(s0, s1,
-// sel) and OPS::dot4(a, b, acc) are v_perm_b32 and v_dot4_i32_i8 on the GPU
-// (an emulation in the host check).
+// The superblock's 64 positions as 64 * t signed bytes (t = 0 where pruned):
+// e[j] holds positions 4j .. 4j+3.  tab: nm_sel_entries(P) (lo, hi) word
+// pairs.  OPS::perm(s0, s1, sel) is v_perm_b32 on the GPU (an emulation in
+// the host check).
 template <Pattern P, class OPS>
-__host__ __device__ inline void nm_dot_superblock(const uint32_t *vals, const uint32_t *masks, const uint32_t *tab,
-                                                  const int32_t *xw, int *acc)
+__host__ __device__ inline void nm_expand_superblock(const uint32_t *vals, const uint32_t *masks,
+                                                     const uint32_t *tab, uint32_t *e)
 {
     if constexpr (P == Pattern::NM24) {
 #pragma unroll
@@ -252,8 +251,8 @@ __host__ __device__ inline void nm_dot_superblock(const uint32_t *vals, const ui
             for (int s = 0; s < 4; ++s) {
                 const uint32_t i = (masks[v] >> (8 * s)) & 0xFFu;
                 const int g = 8 * v + 2 * s;
-                acc[s] = OPS::dot4((int)OPS::perm(u[s], u[s], tab[2 * i]), xw[g], acc[s]);
-                acc[s] = OPS::dot4((int)OPS::perm(u[s], u[s], tab[2 * i + 1]), xw[g + 1], acc[s]);
+                e[g] = OPS::perm(u[s], u[s], tab[2 * i]);
+                e[g + 1] = OPS::perm(u[s], u[s], tab[2 * i + 1]);
             }
         }
     } else {
@@ -264,11 +263,37 @@ __host__ __device__ inline void nm_dot_superblock(const uint32_t *vals, const ui
         for (int g = 0; g < 8; ++g) {
             const uint32_t i = ((masks[g >> 2] >> (8 * (g & 3))) & 0xFFu) | ((uint32_t)(g & 1) << 8);
             const int d = (3 * g) >> 1;                  // first word of the group's 6 kept codes
-            acc[g & 3] = OPS::dot4((int)OPS::perm(u[d + 1], u[d], tab[2 * i]), xw[2 * g], acc[g & 3]);
-            acc[g & 3] = OPS::dot4((int)OPS::perm(u[d + 1], u[d], tab[2 * i + 1]), xw[2 * g + 1], acc[g & 3]);
+            e[2 * g] = OPS::perm(u[d + 1], u[d], tab[2 * i]);
+            e[2 * g + 1] = OPS::perm(u[d + 1], u[d], tab[2 * i + 1]);
         }
     }
 }
+
+// acc[0..3] += 64 * sum over the superblock's 64 positions of t * x, with x
+// the superblock's activation bytes (16 words of 4 int8).  OPS::dot4(a, b,
+// acc) is v_dot4_i32_i8 on the GPU.
+template <Pattern P, class OPS>
+__host__ __device__ inline void nm_dot_superblock(const uint32_t *vals, const uint32_t *masks, const uint32_t *tab,
+                                                  const int32_t *xw, int *acc)
+{
+    uint32_t e[16];
+    nm_expand_superblock<P, OPS>(vals, masks, tab, e);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j & 3] = OPS::dot4((int)e[j], xw[j], acc[j & 3]);
+}
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// v_perm_b32 and v_dot4_i32_i8 for nm_expand_superblock / nm_dot_superblock
+struct DeviceOps {
+    __device__ static uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) { return __builtin_amdgcn_perm(s0, s1, sel); }
+    __device__ static int dot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
+};
+#else
+struct DeviceOps {
+    __device__ static uint32_t perm(uint32_t, uint32_t, uint32_t);
+    __device__ static int dot4(int, int, int);
+};
+#endif
 
 // ---------------------------------------------------------------------------
 // Per-token absmax int8 activation quantisation ("BitNet b1.58 2B4T Technical

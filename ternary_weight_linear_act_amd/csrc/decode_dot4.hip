@@ -37,12 +37,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxK = 16384;                 // activation row in LDS and registers
 
-// v_perm_b32 and v_dot4_i32_i8 for nm_dot_superblock
-struct DeviceOps {
-    __device__ static uint32_t perm(uint32_t s0, uint32_t s1, uint32_t sel) { return __builtin_amdgcn_perm(s0, s1, sel); }
-    __device__ static int dot4(int a, int b, int c) { return __builtin_amdgcn_sdot4(a, b, c, false); }
-};
-
 template <int LPR>
 __device__ __forceinline__ int lanes_sum(int v)
 {

@@ -50,6 +50,7 @@ constexpr int BK = 64;
 constexpr int LDA = BK + 16;      // bytes per staged activation row
 constexpr int LDB = 24;           // bytes per staged packed weight row (16 used)
 constexpr int kXcds = 8;
+constexpr int64_t kTBytesMaxK = 1 << 18;   // N:M t-byte GEMM: 64 * 127 * K < 2^31
 
 // Raw packed words of weight row n for the K slice starting at k0: dense = 4
 // code words; N:M = the superblock's value words then its 2 mask words.
@@ -162,7 +163,15 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], const in
 }
 
 // BM x BN tile, WM x WN waves, each wave (BM/WM) x (BN/WN) of 32x32 fragments.
-template <Pattern P, int BM, int BN, int WM, int WN>
+//
+// TB (N:M only): instead of decoding each superblock to dense 2-bit words,
+// its kept codes are spread over their positions as 64 * t signed bytes by
+// byte permutes (nm_expand_superblock; pruned positions 0), staged in LDS as
+// 64 bytes per row and slice (80 apart), and read straight into the B
+// operand.  The accumulators then hold 64 * sum t*q: no row sum is
+// subtracted, and the exact shift by 6 precedes the epilogue.  |acc| <= 64 *
+// 127 * K, so the host uses it for K <= 2^18.
+template <Pattern P, int BM, int BN, int WM, int WN, bool TB = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
     const uint8_t *__restrict__ packed, const float *__restrict__ w_scale, int64_t M, int64_t N,
@@ -172,20 +181,26 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
     constexpr int FM = TM / 32, FN = TN / 32;          // 32x32 fragments per wave
     static_assert(FM >= 1 && FN >= 1 && TM % 32 == 0 && TN % 32 == 0, "tile");
+    static_assert(!TB || P != Pattern::Dense, "t-bytes are for N:M");
+    constexpr int LB = TB ? 80 : LDB;                  // bytes per staged weight row
     constexpr int A_PIECES = BM * 4;                   // 16-byte pieces of an activation slice
     constexpr int A_PER_T = (A_PIECES + T - 1) / T;
     constexpr int B_PER_T = (BN + T - 1) / T;          // packed rows (16 bytes) per thread
     __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * LDA];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LDB];
+    __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LB];
     __shared__ __attribute__((aligned(16))) int s_rs[BM];
     __shared__ __attribute__((aligned(16))) float s_sc[BM];
-    __shared__ uint8_t s_nm24[P == Pattern::NM24 ? 256 : 1];
+    __shared__ uint8_t s_nm24[P == Pattern::NM24 && !TB ? 256 : 1];
+    __shared__ uint32_t s_sel[TB ? 2 * nm_sel_entries(P) : 1];
 
     // the wave index is wave-uniform: say so, so that branches on it are scalar
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN, wn = wave % WN;
     const int h = lane >> 5, li = lane & 31;
-    if constexpr (P == Pattern::NM24) {
+    if constexpr (TB) {
+        for (int i = tid; i < nm_sel_entries(P); i += T) nm_sel_entry<P>(i, &s_sel[2 * i], &s_sel[2 * i + 1]);
+        __syncthreads();
+    } else if constexpr (P == Pattern::NM24) {
         for (int i = tid; i < 256; i += T) s_nm24[i] = nm24_table_entry((uint32_t)i);
         __syncthreads();
     }
@@ -205,7 +220,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 
     for (int i = tid; i < BM; i += T) {
         const int64_t m = min(m0 + i, M - 1);
-        s_rs[i] = x_rowsum[m];
+        s_rs[i] = TB ? 0 : x_rowsum[m];               // t-bytes: no offset codes
         s_sc[i] = beta * x_scale[m];
     }
 
@@ -242,10 +257,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         for (int p = 0; p < B_PER_T; ++p) {
             const int row = p * T + tid;
             if (BN % T == 0 || row < BN) {
-                const u32x4 d = dense_words<P>(rb[p], s_nm24);
-                u32x2 *dst = reinterpret_cast<u32x2 *>(sB[buf] + row * LDB);
-                dst[0] = u32x2{d[0], d[1]};
-                dst[1] = u32x2{d[2], d[3]};
+                if constexpr (TB) {
+                    constexpr int VW = RawSlice<P>::kWords - 2;
+                    uint32_t e[16];
+                    nm_expand_superblock<P, DeviceOps>(rb[p].w, rb[p].w + VW, s_sel, e);
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(sB[buf] + row * LB);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) dst[q] = u32x4{e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]};
+                } else {
+                    const u32x4 d = dense_words<P>(rb[p], s_nm24);
+                    u32x2 *dst = reinterpret_cast<u32x2 *>(sB[buf] + row * LDB);
+                    dst[0] = u32x2{d[0], d[1]};
+                    dst[1] = u32x2{d[2], d[3]};
+                }
             }
         }
     };
@@ -269,11 +293,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 
         // B fragments: words 2h and 2h+1 of each row (k-steps s = 0, 1); all
         // fragments of the slice are read into distinct registers first
+        // (t-bytes: the 32 bytes of those positions)
         u32x2 bw[FN];
+        i32x4 bt[2][FN];
         i32x4 a[2][FM];
 #pragma unroll
-        for (int fn = 0; fn < FN; ++fn)
-            bw[fn] = *reinterpret_cast<const u32x2 *>(sB[buf] + (wn * TN + fn * 32 + li) * LDB + 8 * h);
+        for (int fn = 0; fn < FN; ++fn) {
+            const uint8_t *brow = sB[buf] + (wn * TN + fn * 32 + li) * LB;
+            if constexpr (TB) {
+                bt[0][fn] = *reinterpret_cast<const i32x4 *>(brow + 32 * h);
+                bt[1][fn] = *reinterpret_cast<const i32x4 *>(brow + 32 * h + 16);
+            } else {
+                bw[fn] = *reinterpret_cast<const u32x2 *>(brow + 8 * h);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -284,7 +317,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
         for (int s = 0; s < 2; ++s) {
             i32x4 bb[FN];
 #pragma unroll
-            for (int fn = 0; fn < FN; ++fn) bb[fn] = unpack_word(bw[fn][s]);
+            for (int fn = 0; fn < FN; ++fn) bb[fn] = TB ? bt[s][fn] : unpack_word(bw[fn][s]);
 #pragma unroll
             for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -294,6 +327,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 
         if (it + 1 < slices) store_slice(buf ^ 1);
         __syncthreads();
+    }
+
+    if constexpr (TB) {                                // 64 * sum t*q: exact
+#pragma unroll
+        for (int a2 = 0; a2 < FM; ++a2)
+#pragma unroll
+            for (int c = 0; c < FN; ++c)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[a2][c][v] >>= 6;
     }
 
     // fused epilogue: offset-code correction and dequant scale
@@ -689,6 +731,13 @@ hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, const ui
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
     const int64_t grid = per_xcd * kXcds;
+    if constexpr (P != Pattern::Dense) {
+        if (K <= kTBytesMaxK) {
+            hipLaunchKernelGGL((gemm_kernel<P, BM, BN, WM, WN, true>), dim3((unsigned)grid), dim3(64 * WM * WN), 0,
+                               stream, Xq, xs, rs, packed, w_scale, M, N, K, Y, acc);
+            return hipGetLastError();
+        }
+    }
     hipLaunchKernelGGL((gemm_kernel<P, BM, BN, WM, WN>), dim3((unsigned)grid), dim3(64 * WM * WN), 0, stream,
                        Xq, xs, rs, packed, w_scale, M, N, K, Y, acc);
     return hipGetLastError();
@@ -699,18 +748,22 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
                     const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                     hipStream_t stream, const char **name)
 {
-    static const char *names[3][3] = {
-        {"gemm_dense_256x256", "gemm_dense_128x128", "gemm_dense_64x128"},
-        {"gemm_nm24_256x256", "gemm_nm24_128x128", "gemm_nm24_64x128"},
-        {"gemm_nm68_256x256", "gemm_nm68_128x128", "gemm_nm68_64x128"}};
+    static const char *names[2][3][3] = {
+        {{"gemm_dense_256x256", "gemm_dense_128x128", "gemm_dense_64x128"},
+         {"gemm_nm24_256x256", "gemm_nm24_128x128", "gemm_nm24_64x128"},
+         {"gemm_nm68_256x256", "gemm_nm68_128x128", "gemm_nm68_64x128"}},
+        {{"", "", ""},
+         {"gemm_nm24_256x256_tbytes", "gemm_nm24_128x128_tbytes", "gemm_nm24_64x128_tbytes"},
+         {"gemm_nm68_256x256_tbytes", "gemm_nm68_128x128_tbytes", "gemm_nm68_64x128_tbytes"}}};
     const int pi = (int)P;
+    const int tb = (P != Pattern::Dense && K <= kTBytesMaxK) ? 1 : 0;   // as launch() decides
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
     if (M >= 256 && tiles(256, 256) >= 128) {
         if (P == Pattern::Dense) {
             *name = "gemm_dense_dma_256x256_w8_s4";
             return launch_dma<256, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
-        *name = names[pi][0];
+        *name = names[tb][pi][0];
         return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
     }
     // mid-size dense problems (e.g. 512 tokens): 128 x 128 tiles fill the
@@ -726,10 +779,10 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
         return launch_few_tokens<64, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
                                            "gemm_dense_splitk_64x128", "gemm_dense_dma_64x128");
     if (M > 64) {
-        *name = names[pi][1];
+        *name = names[tb][pi][1];
         return launch<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
     }
-    *name = names[pi][2];
+    *name = names[tb][pi][2];
     return launch<P, 64, 128, 1, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
 }
 

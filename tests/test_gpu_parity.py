@@ -82,6 +82,31 @@ def test_gemm_tile_thresholds(M, nm):
     full_check(W, X, nm, rows=sample_rows(M, 24, seed=M), label="gemm-threshold")
 
 
+@pytest.mark.parametrize("M,N,K,tile", [(1024, 8200, 320, "256x256"), (300, 1000, 1536, "128x128"),
+                                        (40, 517, 704, "64x128")])
+@pytest.mark.parametrize("nm", [(2, 4), (6, 8)])
+def test_nm_gemm_tbytes(M, N, K, tile, nm):
+    # N:M prefill: kept codes spread over their positions as 64 * t bytes by
+    # byte permutes, read straight into the MFMA operand (K <= 2^18)
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(1200 + M + K, M, N, K, outlier_frac=0.001)
+    full_check(W, X, nm, rows=sample_rows(M, 16, seed=M), label="nm-gemm")
+    name = bl.last_dispatch()
+    assert name == "gemm_nm%d%d_%s_tbytes" % (nm[0], nm[1], tile), name
+
+
+@pytest.mark.parametrize("nm", [(2, 4), (6, 8)])
+def test_nm_gemm_past_tbytes_limit(nm):
+    # K > 2^18: 64 * 127 * K could leave int32, so the superblocks are decoded
+    # to dense codes instead
+    import ternary_weight_linear_act_amd as bl
+    M, N, K = 20, 40, (1 << 18) + 64
+    W, X = workloads.small_case(1300, M, N, K)
+    full_check(W, X, nm, label="nm-gemm-large-k")
+    name = bl.last_dispatch()
+    assert name.startswith("gemm_nm") and not name.endswith("_tbytes"), name
+
+
 @pytest.mark.parametrize("M,N,K", [(8, 2048, 11008), (17, 300, 2048), (33, 2048, 2048), (64, 256, 2048),
                                    (64, 2048, 11008), (40, 1000, 192), (64, 11008, 2048)])
 def test_few_token_gemm(M, N, K):
