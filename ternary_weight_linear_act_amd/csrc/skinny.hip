@@ -4,7 +4,9 @@
 // Rule (from sweeps on MI355X over the decode shapes 2560->6912, 6912->2560,
 // 1536->8960, 2048->{256,2048,11008}, 11008->2048): about 10 chunks (640
 // weights) per wave, KS a power of two, the smallest CMAX that holds a wave's
-// range, and the first candidate whose LDS staging fits 160 KB.
+// range, and the first candidate whose LDS staging fits 160 KB.  The staged
+// token rows are M rounded up to 1, 4, 8 or 16: fewer rows, less LDS, more
+// workgroups per compute unit and deeper K ranges that fit.
 #include <math.h>
 #include <stdio.h>
 
@@ -21,17 +23,19 @@ constexpr int kCM[] = {4, 8, 12, 16, 24, 32, 44};
 constexpr int kNKS = sizeof(kKS) / sizeof(kKS[0]);
 constexpr int kNCM = sizeof(kCM) / sizeof(kCM[0]);
 
-constexpr int64_t lds_bytes_c(int ks, int cmax, int mt)
+// LDS of a configuration: per-wave staging, the cross-wave partial sums and
+// (2:4) the decode table
+constexpr int64_t lds_bytes_c(int ks, int cmax, int mt, Pattern p)
 {
     return ks * (16LL * (8 * ((cmax + 7) / 8) + 1) * 16 + (int64_t)mt * (cmax + 3) * 64 + 64) +
-           (int64_t)(ks > 1 ? ks - 1 : 1) * 64 * 16;
+           (int64_t)(ks > 1 ? ks - 1 : 1) * 64 * 16 + (p == Pattern::NM24 ? 256 : 0);
 }
 
 // a configuration whose staging does not fit the 160 KB of LDS is never built
 template <Pattern P, int KS, int CM, int MT>
 Fn get()
 {
-    if constexpr (lds_bytes_c(KS, CM, MT) <= 160 * 1024) return skinny::launch_skinny<P, KS, CM, MT>;
+    if constexpr (lds_bytes_c(KS, CM, MT, P) <= 160 * 1024) return skinny::launch_skinny<P, KS, CM, MT>;
     else return nullptr;
 }
 
@@ -64,7 +68,12 @@ Fn pick(int ksi, int cmi)
 template <Pattern P>
 Fn pick_p(int mt, int ksi, int cmi)
 {
-    return mt == 1 ? pick<P, 1>(ksi, cmi) : pick<P, 16>(ksi, cmi);
+    switch (mt) {
+    case 1: return pick<P, 1>(ksi, cmi);
+    case 4: return pick<P, 4>(ksi, cmi);
+    case 8: return pick<P, 8>(ksi, cmi);
+    default: return pick<P, 16>(ksi, cmi);
+    }
 }
 
 thread_local char g_name[64];
@@ -78,7 +87,8 @@ hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_
                                  int32_t *acc, hipStream_t stream, const char **name)
 {
     if (M < 1 || M > 16) return hipErrorNotSupported;
-    const int mt = (M == 1) ? 1 : 16;
+    // token rows staged per wave: 1, 4, 8 or 16 (rows past M read a zero block)
+    const int mt = (M == 1) ? 1 : (M <= 4) ? 4 : (M <= 8) ? 8 : 16;
     const int64_t C = K / 64;
     // candidates ordered by distance (in log2) from ~10 chunks per wave
     const double want = log2((double)C / 10.0);
@@ -99,7 +109,7 @@ hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_
         for (int c = 0; c < kNCM; ++c)
             if (kCM[c] >= need) { cmi = c; break; }
         if (cmi < 0) continue;
-        if (lds_bytes_c(ks, kCM[cmi], mt) > 160 * 1024) continue;
+        if (lds_bytes_c(ks, kCM[cmi], mt, p) > 160 * 1024) continue;
         Fn f = nullptr;
         switch (p) {
         case Pattern::Dense: f = pick_p<Pattern::Dense>(mt, ksi, cmi); break;

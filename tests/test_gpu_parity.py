@@ -107,7 +107,19 @@ def test_nm_gemm_past_tbytes_limit(nm):
     assert name.startswith("gemm_nm") and not name.endswith("_tbytes"), name
 
 
-@pytest.mark.parametrize("M,N,K", [(8, 2048, 11008), (17, 300, 2048), (33, 2048, 2048), (64, 256, 2048),
+@pytest.mark.parametrize("M,mt,K", [(3, 4, 11008), (8, 8, 11008), (12, 16, 4096)])
+@pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
+def test_skinny_deep_k(M, mt, K, nm):
+    # 2-16 tokens over deep K: token rows staged 4, 8 or 16 at a time (16 rows
+    # of K = 11008 would not fit LDS)
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(1400 + M, M, 300, K, outlier_frac=0.001)
+    full_check(W, X, nm, label="skinny-deep-k")
+    name = bl.last_dispatch()
+    assert name.startswith("skinny_mfma_") and name.endswith("_mt%d" % mt), name
+
+
+@pytest.mark.parametrize("M,N,K", [(24, 2048, 11008), (17, 300, 2048), (33, 2048, 2048), (64, 256, 2048),
                                    (64, 2048, 11008), (40, 1000, 192), (64, 11008, 2048)])
 def test_few_token_gemm(M, N, K):
     # few tokens: K split over several workgroups, partial tiles combined by a
