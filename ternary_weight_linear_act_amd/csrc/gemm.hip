@@ -50,6 +50,7 @@ constexpr int BK = 64;
 constexpr int LDA = BK + 16;      // bytes per staged activation row
 constexpr int LDB = 24;           // bytes per staged packed weight row (16 used)
 constexpr int kXcds = 8;
+constexpr int kCus = 256;                  // MI355X compute units
 constexpr int64_t kTBytesMaxK = 1 << 18;   // N:M t-byte GEMM: 64 * 127 * K < 2^31
 
 // Raw packed words of weight row n for the K slice starting at k0: dense = 4
@@ -749,7 +750,7 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
                     hipStream_t stream, const char **name)
 {
     static const char *names[2][3][3] = {
-        {{"gemm_dense_256x256", "gemm_dense_128x128", "gemm_dense_64x128"},
+        {{"", "", ""},
          {"gemm_nm24_256x256", "gemm_nm24_128x128", "gemm_nm24_64x128"},
          {"gemm_nm68_256x256", "gemm_nm68_128x128", "gemm_nm68_64x128"}},
         {{"", "", ""},
@@ -758,32 +759,39 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
     const int pi = (int)P;
     const int tb = (P != Pattern::Dense && K <= kTBytesMaxK) ? 1 : 0;   // as launch() decides
     auto tiles = [&](int64_t bm, int64_t bn) { return ((M + bm - 1) / bm) * ((N + bn - 1) / bn); };
-    if (M >= 256 && tiles(256, 256) >= 128) {
-        if (P == Pattern::Dense) {
-            *name = "gemm_dense_dma_256x256_w8_s4";
-            return launch_dma<256, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+    if constexpr (P == Pattern::Dense) {
+        if (M > 64) {
+            // pipelined kernel; tile size by a cost model measured on MI355X
+            // over M = 100 .. 2048: one round of 256 x 256 tiles over the 256
+            // compute units costs about 4, one round of 128 x 128 tiles about
+            // 1.35 (smaller tiles: more operand traffic per MFMA), so 256 x 256
+            // wins only where 128 x 128 would take three or more rounds (e.g.
+            // 2048 x 6912: 4 vs 5.4; 1000 x 8000: 4 vs 2.7)
+            auto rounds = [&](int64_t t) { return (double)((t + kCus - 1) / kCus); };
+            if (4.0 * rounds(tiles(256, 256)) <= 1.35 * rounds(tiles(128, 128))) {
+                *name = "gemm_dense_dma_256x256_w8_s4";
+                return launch_dma<256, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+            }
+            *name = "gemm_dense_dma_128x128_w4_s4";
+            return launch_dma<128, 128, 2, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
-        *name = names[tb][pi][0];
-        return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
-    }
-    // mid-size dense problems (e.g. 512 tokens): 128 x 128 tiles fill the
-    // chip where 256 x 256 tiles would leave most compute units idle
-    if (P == Pattern::Dense && M >= 128 && tiles(128, 128) >= 128) {
-        *name = "gemm_dense_dma_128x128_w4_s4";
-        return launch_dma<128, 128, 2, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
-    }
-    if (P == Pattern::Dense && M <= 32)
-        return launch_few_tokens<32, 1, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
-                                           "gemm_dense_splitk_32x128", "gemm_dense_dma_32x128");
-    if (P == Pattern::Dense && M <= 64)
+        if (M <= 32)
+            return launch_few_tokens<32, 1, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                                               "gemm_dense_splitk_32x128", "gemm_dense_dma_32x128");
         return launch_few_tokens<64, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
                                            "gemm_dense_splitk_64x128", "gemm_dense_dma_64x128");
-    if (M > 64) {
-        *name = names[tb][pi][1];
-        return launch<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+    } else {
+        if (M >= 256 && tiles(256, 256) >= 128) {
+            *name = names[tb][pi][0];
+            return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+        }
+        if (M > 64) {
+            *name = names[tb][pi][1];
+            return launch<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+        }
+        *name = names[tb][pi][2];
+        return launch<P, 64, 128, 1, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
     }
-    *name = names[tb][pi][2];
-    return launch<P, 64, 128, 1, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
 }
 
 }  // namespace
