@@ -699,17 +699,18 @@ int32_t *split_workspace(hipStream_t stream)
     return per_device[dev];
 }
 
-// Few tokens (dense, M <= 64): BM x 128 tiles over a deep ring, K split over
-// enough workgroups to occupy every compute unit.
-template <int BM, int WM, int WN>
+// Few tokens (dense, M <= 64): BM x BN tiles over a deep ring, K split over
+// enough workgroups to occupy every compute unit (none when the tiles alone
+// do).
+template <int BM, int BN, int WM, int WN>
 hipError_t launch_few_tokens(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                              const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                              hipStream_t stream, const char **name, const char *split_name, const char *plain_name)
 {
-    constexpr int BN = 128, S = 8;
+    constexpr int S = 8;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t slices = K / BK;
-    int64_t splits = std::min<int64_t>((256 + tiles - 1) / tiles, slices / 4);   // >= 4 slices each
+    int64_t splits = std::min<int64_t>((kCus + tiles - 1) / tiles, slices / 4);   // >= 4 slices each
     const int64_t per_split = tiles * (int64_t)BM * BN * 4;        // partial bytes per split
     splits = std::min<int64_t>(splits, kWorkspaceBytes / per_split);
     if (splits >= 2) {
@@ -776,10 +777,17 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
             return launch_dma<128, 128, 2, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
         if (M <= 32)
-            return launch_few_tokens<32, 1, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
-                                               "gemm_dense_splitk_32x128", "gemm_dense_dma_32x128");
-        return launch_few_tokens<64, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
-                                           "gemm_dense_splitk_64x128", "gemm_dense_dma_64x128");
+            return launch_few_tokens<32, 128, 1, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                                                    "gemm_dense_splitk_32x128", "gemm_dense_dma_32x128");
+        // 33-64 tokens: narrow weight tiles (measured on the 3B-block shapes at
+        // 64 tokens against 64 x 128: 2048 -> 11008 17.7 -> 10.2 us, one launch
+        // with no split; 2048 -> 2048 8.9 -> 8.2 us), but 64 x 64 for deep K
+        // (11008 -> 2048: 12.9 -> 12.5 us, where 64 x 32 takes 14.4)
+        if (K <= 4096 || N >= 32 * kCus)
+            return launch_few_tokens<64, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                                                   "gemm_dense_splitk_64x32", "gemm_dense_dma_64x32");
+        return launch_few_tokens<64, 64, 2, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                                               "gemm_dense_splitk_64x64", "gemm_dense_dma_64x64");
     } else {
         if (M >= 256 && tiles(256, 256) >= 128) {
             *name = names[tb][pi][0];
