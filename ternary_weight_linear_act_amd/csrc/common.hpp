@@ -234,39 +234,46 @@ __host__ __device__ inline void nm_sel_entry(int i, uint32_t *lo, uint32_t *hi)
     *hi = (uint32_t)(sel >> 32);
 }
 
-// The superblock's 64 positions as 64 * t signed bytes (t = 0 where pruned):
-// e[j] holds positions 4j .. 4j+3.  tab: nm_sel_entries(P) (lo, hi) word
-// pairs.  OPS::perm(s0, s1, sel) is v_perm_b32 on the GPU (an emulation in
-// the host check).
+// Half H (0 or 1) of a superblock: positions 32H .. 32H+31 as 64 * t signed
+// bytes (t = 0 where pruned), e[j] = positions 32H + 4j .. +3.  vals points
+// at value word H; 2:4 reads that word (groups 8H .. 8H+7), 6:8 reads words
+// H and H+1 (groups 4H .. 4H+3).  mask = mask word H.  tab:
+// nm_sel_entries(P) (lo, hi) word pairs.  OPS::perm(s0, s1, sel) is
+// v_perm_b32 on the GPU (an emulation in the host check).
+template <Pattern P, class OPS, int H>
+__host__ __device__ inline void nm_expand_half(const uint32_t *vals, uint32_t mask, const uint32_t *tab, uint32_t *e)
+{
+    if constexpr (P == Pattern::NM24) {
+        uint32_t u[4];
+        nm_tbytes(vals[0], u);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const uint32_t i = (mask >> (8 * s)) & 0xFFu;
+            e[2 * s] = OPS::perm(u[s], u[s], tab[2 * i]);
+            e[2 * s + 1] = OPS::perm(u[s], u[s], tab[2 * i + 1]);
+        }
+    } else {
+        uint32_t u[8];                                   // t-byte words 4H .. 4H+7
+        nm_tbytes(vals[0], u);
+        nm_tbytes(vals[1], u + 4);
+#pragma unroll
+        for (int gl = 0; gl < 4; ++gl) {
+            const int g = 4 * H + gl;
+            const uint32_t i = ((mask >> (8 * gl)) & 0xFFu) | ((uint32_t)(g & 1) << 8);
+            const int d = ((3 * g) >> 1) - 4 * H;         // first word of the group's 6 kept codes
+            e[2 * gl] = OPS::perm(u[d + 1], u[d], tab[2 * i]);
+            e[2 * gl + 1] = OPS::perm(u[d + 1], u[d], tab[2 * i + 1]);
+        }
+    }
+}
+
+// The whole superblock: e[j] = positions 4j .. 4j+3.
 template <Pattern P, class OPS>
 __host__ __device__ inline void nm_expand_superblock(const uint32_t *vals, const uint32_t *masks,
                                                      const uint32_t *tab, uint32_t *e)
 {
-    if constexpr (P == Pattern::NM24) {
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-            uint32_t u[4];
-            nm_tbytes(vals[v], u);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const uint32_t i = (masks[v] >> (8 * s)) & 0xFFu;
-                const int g = 8 * v + 2 * s;
-                e[g] = OPS::perm(u[s], u[s], tab[2 * i]);
-                e[g + 1] = OPS::perm(u[s], u[s], tab[2 * i + 1]);
-            }
-        }
-    } else {
-        uint32_t u[12];
-#pragma unroll
-        for (int v = 0; v < 3; ++v) nm_tbytes(vals[v], u + 4 * v);
-#pragma unroll
-        for (int g = 0; g < 8; ++g) {
-            const uint32_t i = ((masks[g >> 2] >> (8 * (g & 3))) & 0xFFu) | ((uint32_t)(g & 1) << 8);
-            const int d = (3 * g) >> 1;                  // first word of the group's 6 kept codes
-            e[2 * g] = OPS::perm(u[d + 1], u[d], tab[2 * i]);
-            e[2 * g + 1] = OPS::perm(u[d + 1], u[d], tab[2 * i + 1]);
-        }
-    }
+    nm_expand_half<P, OPS, 0>(vals, masks[0], tab, e);
+    nm_expand_half<P, OPS, 1>(vals + 1, masks[1], tab, e + 8);
 }
 
 // acc[0..3] += 64 * sum over the superblock's 64 positions of t * x, with x

@@ -187,6 +187,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     constexpr int A_PIECES = BM * 4;                   // 16-byte pieces of an activation slice
     constexpr int A_PER_T = (A_PIECES + T - 1) / T;
     constexpr int B_PER_T = (BN + T - 1) / T;          // packed rows (16 bytes) per thread
+    // TB: a work item is half a row's superblock (32 positions); items
+    // [0, BN) are first halves, [BN, 2 BN) second halves, so the half is
+    // wave-uniform (BN is a multiple of 64)
+    constexpr int BH_PER_T = (2 * BN + T - 1) / T;
+    constexpr int VWH = (P == Pattern::NM68) ? 2 : 1;  // value words of a half
     __shared__ __attribute__((aligned(16))) int8_t sA[2][BM * LDA];
     __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * LB];
     __shared__ __attribute__((aligned(16))) int s_rs[BM];
@@ -227,7 +232,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 
     // global -> register staging of one K slice
     u32x4 ra[A_PER_T];
-    RawSlice<P> rb[B_PER_T];
+    RawSlice<P> rb[TB ? 1 : B_PER_T];
+    uint32_t hv[TB ? BH_PER_T : 1][VWH], hm[TB ? BH_PER_T : 1];
     auto load_slice = [&](int64_t k0) {
 #pragma unroll
         for (int p = 0; p < A_PER_T; ++p) {
@@ -236,12 +242,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
             const int64_t m = min(m0 + row, M - 1);        // rows >= M: any finite data, never stored
             ra[p] = *reinterpret_cast<const u32x4 *>(Xq + m * K + k0 + 16 * c);
         }
+        if constexpr (TB) {
+            constexpr int GM = (P == Pattern::NM24) ? 4 : 8, GN = (P == Pattern::NM24) ? 2 : 6;
+            constexpr int VW = 64 * GN / GM / 16;
+            const int64_t vrow = nm_value_row_bytes(K, GN, GM), sb = k0 / 64;
 #pragma unroll
-        for (int p = 0; p < B_PER_T; ++p) {
-            const int row = p * T + tid;
-            if (BN % T == 0 || row < BN) {                 // whole waves
-                const int64_t n = min(n0 + row, N - 1);
-                load_raw<P>(packed, N, K, n, k0, rb[p]);
+            for (int p = 0; p < BH_PER_T; ++p) {
+                const int idx = p * T + tid;
+                if ((2 * BN) % T == 0 || idx < 2 * BN) {
+                    const int h = idx / BN, row = idx % BN;
+                    const int64_t n = min(n0 + row, N - 1);
+                    const uint32_t *vp = reinterpret_cast<const uint32_t *>(packed + n * vrow + sb * (VW * 4)) + h;
+#pragma unroll
+                    for (int v = 0; v < VWH; ++v) hv[p][v] = vp[v];
+                    hm[p] = reinterpret_cast<const uint32_t *>(packed + N * vrow + n * (K / 8) + sb * 8)[h];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int p = 0; p < B_PER_T; ++p) {
+                const int row = p * T + tid;
+                if (BN % T == 0 || row < BN) {             // whole waves
+                    const int64_t n = min(n0 + row, N - 1);
+                    load_raw<P>(packed, N, K, n, k0, rb[p]);
+                }
             }
         }
     };
@@ -254,18 +278,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
                 *reinterpret_cast<u32x4 *>(sA[buf] + row * LDA + 16 * c) = ra[p];
             }
         }
+        if constexpr (TB) {
 #pragma unroll
-        for (int p = 0; p < B_PER_T; ++p) {
-            const int row = p * T + tid;
-            if (BN % T == 0 || row < BN) {
-                if constexpr (TB) {
-                    constexpr int VW = RawSlice<P>::kWords - 2;
-                    uint32_t e[16];
-                    nm_expand_superblock<P, DeviceOps>(rb[p].w, rb[p].w + VW, s_sel, e);
-                    u32x4 *dst = reinterpret_cast<u32x4 *>(sB[buf] + row * LB);
+            for (int p = 0; p < BH_PER_T; ++p) {
+                const int idx = p * T + tid;
+                if ((2 * BN) % T == 0 || idx < 2 * BN) {
+                    const int h = idx / BN, row = idx % BN;          // h wave-uniform
+                    uint32_t e[8];
+                    if (h == 0) nm_expand_half<P, DeviceOps, 0>(hv[p], hm[p], s_sel, e);
+                    else nm_expand_half<P, DeviceOps, 1>(hv[p], hm[p], s_sel, e);
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(sB[buf] + row * LB + 32 * h);
+                    dst[0] = u32x4{e[0], e[1], e[2], e[3]};
+                    dst[1] = u32x4{e[4], e[5], e[6], e[7]};
+                }
+            }
+        } else {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) dst[q] = u32x4{e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]};
-                } else {
+            for (int p = 0; p < B_PER_T; ++p) {
+                const int row = p * T + tid;
+                if (BN % T == 0 || row < BN) {
                     const u32x4 d = dense_words<P>(rb[p], s_nm24);
                     u32x2 *dst = reinterpret_cast<u32x2 *>(sB[buf] + row * LDB);
                     dst[0] = u32x2{d[0], d[1]};
