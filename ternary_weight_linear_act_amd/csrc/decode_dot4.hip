@@ -243,12 +243,28 @@ namespace {
 using Fn = void (*)(dim3, size_t, hipStream_t, const float *, const int8_t *, const float *, const int32_t *,
                     int64_t, const FusedProjArgs &, float *);
 
-template <Pattern P, int LPR, int U, bool FUSED>
+template <Pattern P, int LPR, int U, bool FUSED, int W = 4>
 void launch(dim3 grid, size_t lds, hipStream_t stream, const float *X, const int8_t *Xq, const float *xs,
             const int32_t *rs, int64_t K, const FusedProjArgs &args, float *x_scale_out)
 {
-    hipLaunchKernelGGL((dot4::decode_dot4_kernel<P, LPR, U, FUSED>), grid, dim3(256), lds, stream, X, Xq, xs, rs,
-                       K, args, x_scale_out);
+    hipLaunchKernelGGL((dot4::decode_dot4_kernel<P, LPR, U, FUSED, W>), grid, dim3(64 * W), lds, stream, X, Xq, xs,
+                       rs, K, args, x_scale_out);
+}
+
+// Fused, 8 lanes per row, 8 waves (64 rows per workgroup)
+template <Pattern P>
+Fn pick_w8(int u)
+{
+    switch (u) {
+    case 1: return launch<P, 8, 1, true, 8>;
+    case 2: return launch<P, 8, 2, true, 8>;
+    case 3: return launch<P, 8, 3, true, 8>;
+    case 4: return launch<P, 8, 4, true, 8>;
+    case 5: return launch<P, 8, 5, true, 8>;
+    case 6: return launch<P, 8, 6, true, 8>;
+    case 7: return launch<P, 8, 7, true, 8>;
+    default: return nullptr;
+    }
 }
 
 // The (lanes per row, chunks per lane) pairs the host rule below can pick:
@@ -296,7 +312,9 @@ thread_local char g_name[64];
 // Lanes per row: the fewest of 8, 16, 32, 64 that keep a lane's chunks U
 // <= 5, or <= 7 with the quantisation fused in (<= 4 at 64 lanes, K <= 16384).
 // The fused kernel reads and quantises the whole fp32 row in every
-// workgroup, so it prefers fewer, fuller workgroups.  Returns
+// workgroup, so it prefers fewer, fuller workgroups: at 8 lanes per row it
+// takes 8 waves (64 rows) per workgroup where 4 waves would need more than
+// 320 workgroups (gate+up of a 2B FFN: 432 -> 216, 4.1 -> 4.0 us).  Returns
 // hipErrorNotSupported when M != 1 or K is too large.
 hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
                               int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
@@ -309,7 +327,13 @@ hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs,
     int lpr = 8;
     while (lpr < 64 && (C + lpr - 1) / lpr > umax) lpr *= 2;
     const int u = (int)((C + lpr - 1) / lpr);
-    const int64_t rb = 4 * (64 / lpr);
+    auto count_blocks = [&](int64_t rb) {
+        int64_t b = 0;
+        for (int i = 0; i < args.nproj; ++i) b += (args.N[i] + rb - 1) / rb;
+        return b;
+    };
+    const bool w8 = fused && lpr == 8 && count_blocks(4 * 8) > 320;
+    const int64_t rb = (w8 ? 8 : 4) * (64 / lpr);
     int64_t blocks = 0;
     for (int i = 0; i < args.nproj; ++i) {
         args.block_start[i] = (int32_t)blocks;
@@ -319,13 +343,20 @@ hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs,
     if (blocks > (1LL << 30)) return hipErrorNotSupported;
     Fn f = nullptr;
     switch (p) {
-    case Pattern::Dense: f = fused ? pick<Pattern::Dense, true>(lpr, u) : pick<Pattern::Dense, false>(lpr, u); break;
-    case Pattern::NM24: f = fused ? pick<Pattern::NM24, true>(lpr, u) : pick<Pattern::NM24, false>(lpr, u); break;
-    case Pattern::NM68: f = fused ? pick<Pattern::NM68, true>(lpr, u) : pick<Pattern::NM68, false>(lpr, u); break;
+    case Pattern::Dense:
+        f = w8 ? pick_w8<Pattern::Dense>(u) : fused ? pick<Pattern::Dense, true>(lpr, u) : pick<Pattern::Dense, false>(lpr, u);
+        break;
+    case Pattern::NM24:
+        f = w8 ? pick_w8<Pattern::NM24>(u) : fused ? pick<Pattern::NM24, true>(lpr, u) : pick<Pattern::NM24, false>(lpr, u);
+        break;
+    case Pattern::NM68:
+        f = w8 ? pick_w8<Pattern::NM68>(u) : fused ? pick<Pattern::NM68, true>(lpr, u) : pick<Pattern::NM68, false>(lpr, u);
+        break;
     }
     if (!f) return hipErrorNotSupported;
-    snprintf(g_name, sizeof g_name, "%s_%s_lpr%d_u%d_p%d", fused ? "fused_decode_dot4" : "decode_dot4",
-             p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", lpr, u, args.nproj);
+    snprintf(g_name, sizeof g_name, "%s_%s_lpr%d_u%d_p%d%s", fused ? "fused_decode_dot4" : "decode_dot4",
+             p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", lpr, u, args.nproj,
+             w8 ? "_w8" : "");
     *name = g_name;
     f(dim3((unsigned)blocks), (size_t)K, stream, X, Xq, xs, rs, K, args, x_scale_out);
     return hipGetLastError();

@@ -74,6 +74,18 @@ def test_fused_m1(K, nm):
 
 
 @pytest.mark.parametrize("nm", NM_CASES)
+@pytest.mark.parametrize("K", [1024, 3584])
+def test_fused_m1_eight_waves(K, nm):
+    # more than 320 four-wave workgroups at 8 lanes per row: 8 waves, 64 rows
+    Ns = (9000, 2000, 70)
+    Ws = [workloads.small_case(5400 + K + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+    _, X = workloads.small_case(5500 + K, 1, 8, K, outlier_frac=0.01)
+    print("case dot4 fused 8 waves K=%d nm=%s" % (K, nm), flush=True)
+    name = fused_vs_oracle(Ws, X, nm)
+    assert name.startswith("fused_decode_dot4_") and "_lpr8_" in name and name.endswith("_p3_w8"), name
+
+
+@pytest.mark.parametrize("nm", NM_CASES)
 def test_zero_row_m1(nm):
     import torch
 
