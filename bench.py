@@ -62,9 +62,10 @@ def quant_bytes(M, K):
     return 4 * M * K + M * K + 8 * M
 
 
-def timed_graph(torch, body, reps=1):
-    """Capture body() into a HIP graph, replay it once untimed, then time `reps`
-    replays with events on the graph's stream.  Returns ms per replay."""
+def timed_graph(torch, body, reps=1, warm=1):
+    """Capture body() into a HIP graph, replay it `warm` times untimed, then
+    time `reps` replays with events on the graph's stream.  Returns ms per
+    replay."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -76,7 +77,8 @@ def timed_graph(torch, body, reps=1):
         body()
     # replay on s and record the events on s: graph launches go to the current stream
     with torch.cuda.stream(s):
-        g.replay()
+        for _ in range(warm):
+            g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(s)
@@ -321,7 +323,11 @@ def main():
     torch.cuda.synchronize()
     gemm_dispatch = bl.last_dispatch()
     G = 20
-    ms_gemm, _ = timed_graph(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, Np_, Y=Y_p) for _ in range(G)], reps=2)
+    # steady state: ~5 ms of the same GEMM untimed first (the first
+    # milliseconds of back-to-back GEMMs run a few percent slower), then 100
+    # timed launches
+    ms_gemm, _ = timed_graph(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, Np_, Y=Y_p) for _ in range(G)],
+                             reps=5, warm=5)
     gemm_us = ms_gemm * 1e3 / G
     gemm_tops = 2.0 * Mp * Np_ * Kp / (gemm_us * 1e-6) / 1e12
     ms_qp, _ = timed_graph(torch, lambda: [bl.quant_act(Xp, Xq_p, xs_p, rs_p) for _ in range(G)], reps=2)
