@@ -86,6 +86,18 @@ def test_fused_m1_eight_waves(K, nm):
 
 
 @pytest.mark.parametrize("nm", NM_CASES)
+def test_fused_m1_eight_projections(nm):
+    # the most projections one launch takes, of uneven sizes (one a single row)
+    Ns = (1, 37, 300, 64, 513, 7, 129, 2000)
+    K = 1536
+    Ws = [workloads.small_case(5600 + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+    _, X = workloads.small_case(5700, 1, 8, K, outlier_frac=0.01)
+    print("case dot4 fused 8 projections nm=%s" % (nm,), flush=True)
+    name = fused_vs_oracle(Ws, X, nm)
+    assert name.startswith("fused_decode_dot4_") and name.endswith("_p8"), name
+
+
+@pytest.mark.parametrize("nm", NM_CASES)
 def test_zero_row_m1(nm):
     import torch
 
