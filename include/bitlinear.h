@@ -52,10 +52,10 @@
  * Conventions for every call:
  *   - Data pointers are device pointers (hipMalloc / torch tensors) owned by
  *     the caller.  The one exception is internal: the first
- *     bitlinear_forward call on a device that runs the few-token GEMM
- *     (dense, 17 <= M <= 64, or a decode shape too large for the skinny
- *     kernel) allocates a 64 MB split-K workspace with hipMalloc, once, and
- *     keeps it until the process ends.  That call must not be inside HIP
+ *     bitlinear_forward call on a device that runs the few-token GEMM with K
+ *     split over workgroups (dense, M <= 64 with too few output tiles to
+ *     fill the GPU) allocates a 64 MB split-K workspace with hipMalloc,
+ *     once, and keeps it until the process ends.  That call must not be inside HIP
  *     graph capture (a captured call that finds no workspace uses the
  *     unsplit kernel instead), and such calls must not overlap in time on
  *     one device (they share the workspace).
@@ -132,8 +132,11 @@ bitlinear_status bitlinear_quant_act(const float *X, int64_t M, int64_t K,
  * unsigned codes c = t + 1 and subtract the row sum).  packed, w_scale: as
  * written by bitlinear_pack_weights with the same N, K and nm.  Y: M x N fp32
  * output.  acc: optional M x N int32 output of the exact integer sums (NULL
- * to skip).  The kernel is chosen from M (decode GEMV for small M, MFMA GEMM
- * otherwise); bitlinear_last_dispatch() names it. */
+ * to skip).  The kernel is chosen from the shape: M = 1 (K <= 16384) packed
+ * int8 dot products; 2 <= M <= 16 an MFMA kernel with the tokens as one
+ * operand; larger M the MFMA GEMM (K split over workgroups for M <= 64 when
+ * the output tiles alone cannot fill the GPU).  bitlinear_last_dispatch()
+ * names the kernel. */
 bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                                    const void *packed, const float *w_scale, bitlinear_nm nm,
                                    int64_t M, int64_t N, int64_t K,
@@ -169,7 +172,8 @@ bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, b
 const char *bitlinear_last_error(void);
 
 /* Thread-local name of the kernel(s) the last successful call on this thread
- * launched, e.g. "gemv_dense_m1" or "gemm_dense_256x128". */
+ * launched, e.g. "decode_dot4_dense_lpr8_u5_p1" or
+ * "gemm_dense_dma_256x256_w8_s4"; "none" after an M == 0 no-op. */
 const char *bitlinear_last_dispatch(void);
 
 #ifdef __cplusplus
