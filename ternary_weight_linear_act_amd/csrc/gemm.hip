@@ -807,14 +807,21 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
             *name = "gemm_dense_dma_128x128_w4_s4";
             return launch_dma<128, 128, 2, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
-        if (M <= 32)
-            return launch_few_tokens<32, 128, 1, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
-                                                    "gemm_dense_splitk_32x128", "gemm_dense_dma_32x128");
-        // 33-64 tokens: narrow weight tiles (measured on the 3B-block shapes at
-        // 64 tokens against 64 x 128: 2048 -> 11008 17.7 -> 10.2 us, one launch
-        // with no split; 2048 -> 2048 8.9 -> 8.2 us), but 64 x 64 for deep K
-        // (11008 -> 2048: 12.9 -> 12.5 us, where 64 x 32 takes 14.4)
-        if (K <= 4096 || N >= 32 * kCus)
+        // narrow weight tiles: more workgroups from N, so fewer K splits (none
+        // for wide N).  Measured against 128-wide tiles: at 64 tokens,
+        // 2048 -> 11008 17.7 -> 10.2 us (one launch) and 2048 -> 2048 8.9 ->
+        // 8.2 us; at 20-32 tokens, 1536 -> 8960 11.3 -> 7.6 us and 2048 ->
+        // 11008 12.9 -> 8.2 us.  Deep K takes 64-wide tiles (11008 -> 2048 at
+        // 64 tokens: 12.9 -> 12.5 us, where 32-wide ones take 14.4).
+        const bool narrow = K <= 4096 || N >= 32 * kCus;
+        if (M <= 32) {
+            if (narrow)
+                return launch_few_tokens<32, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                                                       "gemm_dense_splitk_32x32", "gemm_dense_dma_32x32");
+            return launch_few_tokens<32, 64, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                                                   "gemm_dense_splitk_32x64", "gemm_dense_dma_32x64");
+        }
+        if (narrow)
             return launch_few_tokens<64, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
                                                    "gemm_dense_splitk_64x32", "gemm_dense_dma_64x32");
         return launch_few_tokens<64, 64, 2, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,

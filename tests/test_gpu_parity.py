@@ -119,7 +119,7 @@ def test_skinny_deep_k(M, mt, K, nm):
     assert name.startswith("skinny_mfma_") and name.endswith("_mt%d" % mt), name
 
 
-@pytest.mark.parametrize("M,N,K", [(24, 2048, 11008), (17, 300, 2048), (33, 2048, 2048), (64, 256, 2048),
+@pytest.mark.parametrize("M,N,K", [(24, 2048, 11008), (17, 300, 2048), (20, 8960, 1536), (33, 2048, 2048), (64, 256, 2048),
                                    (64, 2048, 11008), (40, 1000, 192), (64, 11008, 2048)])
 def test_few_token_gemm(M, N, K):
     # few tokens: K split over several workgroups, partial tiles combined by a
