@@ -68,6 +68,20 @@ def test_fused_shapes(M, nm, K, Ns):
     check_against_oracle(Ws, X, nm, Ys, accs, xs)
 
 
+@pytest.mark.parametrize("M", [2, 4])
+@pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
+def test_fused_mfma_deepest_k(M, nm):
+    # the largest K the 2-4-token fused kernel takes (its widest
+    # configurations keep the activations partly in scratch)
+    K, Ns = 16192, (300, 77)
+    Ws = [workloads.small_case(800 + M + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+    _, X = workloads.small_case(850 + M, M, 8, K, outlier_frac=0.01)
+    print("case fused deepest K M=%d nm=%s" % (M, nm), flush=True)
+    _, Ys, accs, xs, name = run_fused(Ws, X, nm)
+    assert name.startswith("fused_decode_") and "dot4" not in name, name
+    check_against_oracle(Ws, X, nm, Ys, accs, xs)
+
+
 def test_fused_equals_two_call_path_bitwise():
     import torch
     d = workloads.draw("decode_ffn_2b", projs=["gate", "up"])

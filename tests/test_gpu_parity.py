@@ -119,6 +119,17 @@ def test_skinny_deep_k(M, mt, K, nm):
     assert name.startswith("skinny_mfma_") and name.endswith("_mt%d" % mt), name
 
 
+@pytest.mark.parametrize("M", [1, 3])
+@pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
+def test_gemv_fallback_very_deep_k(M, nm):
+    # 1-4 tokens past the skinny kernel's K range (44 chunks x 16 waves):
+    # the dot-product GEMV
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(1500 + M, M, 40, 65536, outlier_frac=0.001)
+    full_check(W, X, nm, label="gemv-fallback")
+    assert bl.last_dispatch().startswith("gemv_"), bl.last_dispatch()
+
+
 @pytest.mark.parametrize("M,N,K", [(24, 2048, 11008), (17, 300, 2048), (20, 8960, 1536), (33, 2048, 2048), (64, 256, 2048),
                                    (64, 2048, 11008), (40, 1000, 192), (64, 11008, 2048)])
 def test_few_token_gemm(M, N, K):
