@@ -31,10 +31,15 @@ constexpr int64_t static_lds(int ks, int cmax, int mt)
            (int64_t)((kRows + 15) / 16) * (ks > 1 ? ks - 1 : 1) * 64 * 16;
 }
 
+// 4 token rows with 16 waves, or with 44 chunks per wave, are never built:
+// the rows' activation registers would spill to scratch (at 1024 threads a
+// thread has 128 VGPRs; 44 chunks take more than 256).  8 waves of 32 chunks
+// reach K = 16384, beyond the 16192 the 4-row staging allows.
 template <Pattern P, int KS, int CM, int MT>
 Fn get()
 {
-    if constexpr (static_lds(KS, CM, MT) <= kLds - 1024) return fused::launch_fused<P, KS, CM, MT, kRows>;
+    if constexpr (MT > 1 && (KS > 8 || CM > 32)) return nullptr;
+    else if constexpr (static_lds(KS, CM, MT) <= kLds - 1024) return fused::launch_fused<P, KS, CM, MT, kRows>;
     else return nullptr;
 }
 
