@@ -2,7 +2,8 @@
  * bitlinear_oracle.c -- plain, slow, obviously-correct CPU oracle for the
  * BitNet b1.58 BitLinear forward pass and its Sparse-BitNet N:M variant.
  *
- * TEST INFRASTRUCTURE ONLY.  This file is the checker, not the product: only
+ * TEST INFRASTRUCTURE ONLY.  This file is the reference the GPU results are
+ * compared against, not the product: only
  * the test suite, the smoke check and the CPU-baseline leg of the benchmark
  * load it.  It shares no code, header, table or constant generator with the
  * HIP library; the packed byte layout is re-implemented here from its written
