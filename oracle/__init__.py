@@ -18,6 +18,7 @@ from .oracle import (  # noqa: F401
     pack_nm,
     quantize_weights,
     quant_act,
+    quant_act_ex,
     forward,
     build,
     LIB_PATH,

@@ -36,11 +36,16 @@
  *    row sums over n ascending, then divided by N*K and rounded to binary32;
  *  - d = fl32(beta + 1e-5f); the weight dequant scale is beta itself;
  *  - N:M groups run along K (the input dimension); ties keep the lower k;
- *  - a row with max|x| = 0 quantises to zeros with x_scale = 0.
+ *  - a row with max|x| = 0 quantises to zeros with x_scale = 0;
+ *  - the gated feed-forward input is ReLU(gate)^2 * up, in binary32;
+ *  - RMSNorm: eps inside the square root, mean over the K inputs, sum of
+ *    squares in binary64; its 1/rms factor is applied to the scale, not to
+ *    the row before the codes are taken (it divides out of the codes).
  */
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define OR_OK 0
@@ -266,6 +271,69 @@ int oracle_quant_act(const float *X, int64_t M, int64_t K, int variant,
         if (rowsum) rowsum[r] = sum;
     }
     return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 6b: the row a BitLinear quantises when its input is transformed     */
+/* first (the steps either side of the linear in a BitNet block).           */
+/*                                                                          */
+/* ReLU^2 gate ([2B4T] sec. 2: the feed-forward network uses squared ReLU;  */
+/* with separate gate and up projections the plain reading is              */
+/* h = ReLU(gate)^2 * up, elementwise, in binary32):                        */
+/*     h[k] = fl32( fl32(r * r) * up[k] ),   r = max(x[k], 0)               */
+/* Without `up` the row is used as it is: h = x.                            */
+/*                                                                          */
+/* RMSNorm before the quantiser ([SURV] BitLinear_b158: the input passes    */
+/* through an RMSNorm over the in-features, then activation_quant; [2B4T]   */
+/* sec. 2 names subln):  xhat[k] = h[k] * rinv * gamma[k],                  */
+/*     rinv = 1 / sqrt( (sum_k h[k]^2) / K + eps )                          */
+/* with the sum in binary64, k ascending (each square is exact there).      */
+/* The absmax codes of xhat are those of v[k] = fl32(h[k] * gamma[k]): the  */
+/* positive per-row factor rinv divides out of xhat / max|xhat|.  So the    */
+/* codes are quantised from v exactly as in step 6, and rinv goes into the  */
+/* scale:  x_scale = fl32( (double)max|v| / 127 * rinv )  (0 for a zero     */
+/* row).  Without gamma, step 6 applies to h unchanged.                     */
+/* ------------------------------------------------------------------------ */
+int oracle_quant_act_ex(const float *X, const float *up, const float *gamma, float eps,
+                        int64_t M, int64_t K, int8_t *q, float *x_scale, int32_t *rowsum)
+{
+    if (!X || !q || !x_scale || M < 0 || K < 1 || !(eps >= 0.0f)) return OR_EINVAL;
+    float *v = (float *)malloc((size_t)K * sizeof(float));
+    if (!v) return OR_EINVAL;
+    int rc = OR_OK;
+    for (int64_t r = 0; r < M && rc == OR_OK; ++r) {
+        const float *x = X + r * K;
+        for (int64_t k = 0; k < K; ++k) {
+            if (!isfinite(x[k]) || (up && !isfinite(up[r * K + k])) || (gamma && !isfinite(gamma[k]))) {
+                rc = OR_ENONFINITE;
+                break;
+            }
+            if (up) {
+                float relu = x[k] > 0.0f ? x[k] : 0.0f;
+                float sq = relu * relu;
+                v[k] = sq * up[r * K + k];
+            } else {
+                v[k] = x[k];
+            }
+        }
+        if (rc != OR_OK) break;
+        double rinv = 1.0;
+        if (gamma) {
+            double ss = 0.0;
+            for (int64_t k = 0; k < K; ++k) ss += (double)v[k] * (double)v[k];
+            rinv = 1.0 / sqrt(ss / (double)K + (double)eps);
+            for (int64_t k = 0; k < K; ++k) v[k] = v[k] * gamma[k];
+        }
+        rc = oracle_quant_act(v, 1, K, 0, q + r * K, x_scale + r, rowsum ? rowsum + r : NULL);
+        if (rc == OR_OK && gamma) {
+            float g = 0.0f;
+            for (int64_t k = 0; k < K; ++k)
+                if (fabsf(v[k]) > g) g = fabsf(v[k]);
+            x_scale[r] = (g == 0.0f) ? 0.0f : (float)((double)g / 127.0 * rinv);
+        }
+    }
+    free(v);
+    return rc;
 }
 
 /* ------------------------------------------------------------------------ */

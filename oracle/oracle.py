@@ -60,9 +60,11 @@ def _L():
         lib.oracle_pack_dense.argtypes = [vp, i64, i64, vp]
         lib.oracle_pack_nm.argtypes = [vp, vp, i64, i64, i32, i32, vp]
         lib.oracle_quant_act.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+        lib.oracle_quant_act_ex.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp]
         lib.oracle_forward.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp]
         for f in ("oracle_absmean", "oracle_ternarize", "oracle_nm_keep", "oracle_apply_mask",
-                  "oracle_pack_dense", "oracle_pack_nm", "oracle_quant_act", "oracle_forward"):
+                  "oracle_pack_dense", "oracle_pack_nm", "oracle_quant_act", "oracle_quant_act_ex",
+                  "oracle_forward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -154,6 +156,31 @@ def quant_act(X: np.ndarray, variant: int = 0):
     xs = np.empty(M, np.float32)
     rs = np.empty(M, np.int32)
     _check(_L().oracle_quant_act(_p(X), M, K, variant, _p(q), _p(xs), _p(rs)), "quant_act")
+    return q, xs, rs
+
+
+def quant_act_ex(X: np.ndarray, up=None, gamma=None, eps: float = 0.0):
+    """Absmax int8 quantisation of the transformed rows: h = ReLU(X)^2 * up when
+    `up` is given (else h = X), then RMSNorm with weight `gamma` (length K) and
+    epsilon `eps` when `gamma` is given.  Returns (q int8, x_scale fp32, rowsum
+    int32); see step 6b of the C file."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    M, K = X.shape
+    if up is not None:
+        up = np.ascontiguousarray(up, dtype=np.float32)
+        if up.shape != X.shape:
+            raise ValueError("up must have the shape of X")
+    if gamma is not None:
+        gamma = np.ascontiguousarray(gamma, dtype=np.float32)
+        if gamma.shape != (K,):
+            raise ValueError("gamma must have K entries")
+    q = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    rs = np.empty(M, np.int32)
+    null = ctypes.c_void_p(None)
+    _check(_L().oracle_quant_act_ex(_p(X), _p(up) if up is not None else null,
+                                    _p(gamma) if gamma is not None else null, float(eps), M, K,
+                                    _p(q), _p(xs), _p(rs)), "quant_act_ex")
     return q, xs, rs
 
 

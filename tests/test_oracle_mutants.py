@@ -3,7 +3,8 @@
 Each case copies oracle/bitlinear_oracle.c, plants one mistake on the CPU
 (a dropped abs, a wrong divisor, truncation instead of round-half-even, a
 missing epsilon, a wrong tie-break, a misplaced bit, a transposed operand, a
-wrong clamp, a wrong activation constant), builds it, and runs the pin suite
+wrong clamp, a wrong activation constant, a slip in the ReLU^2 gate or the
+RMSNorm), builds it, and runs the pin suite
 against it: the suite must fail for every mutant.
 """
 import os
@@ -36,6 +37,19 @@ MUTANTS = {
     "nm_mask_nibble_order": ("masks[r * mrow + g / 2] |= (uint8_t)(mask << (4 * (g % 2)));",
                              "masks[r * mrow + g / 2] |= (uint8_t)(mask << (4 * (1 - g % 2)));"),
     "nm_keep_one_less": ("for (int round = 0; round < n; ++round)", "for (int round = 1; round < n; ++round)"),
+    "gate_no_relu": ("float relu = x[k] > 0.0f ? x[k] : 0.0f;", "float relu = x[k];"),
+    "gate_no_square": ("float sq = relu * relu;", "float sq = relu;"),
+    "gate_up_dropped": ("v[k] = sq * up[r * K + k];", "v[k] = sq;"),
+    "rms_eps_outside_sqrt": ("rinv = 1.0 / sqrt(ss / (double)K + (double)eps);",
+                             "rinv = 1.0 / (sqrt(ss / (double)K) + (double)eps);"),
+    "rms_sum_not_mean": ("rinv = 1.0 / sqrt(ss / (double)K + (double)eps);",
+                         "rinv = 1.0 / sqrt(ss + (double)eps);"),
+    "rms_gamma_dropped": ("for (int64_t k = 0; k < K; ++k) v[k] = v[k] * gamma[k];",
+                          "for (int64_t k = 0; k < K; ++k) v[k] = v[k] * 1.0f;"),
+    "rms_scale_without_rinv": ("x_scale[r] = (g == 0.0f) ? 0.0f : (float)((double)g / 127.0 * rinv);",
+                               "x_scale[r] = (g == 0.0f) ? 0.0f : (float)((double)g / 127.0);"),
+    "rms_after_gamma": ("for (int64_t k = 0; k < K; ++k) ss += (double)v[k] * (double)v[k];",
+                        "for (int64_t k = 0; k < K; ++k) ss += (double)v[k] * (double)v[k] * (double)gamma[k] * (double)gamma[k];"),
     "epilogue_no_beta": ("Y[m * N + n] = (double)s * (double)beta * (double)x_scale[m];",
                          "Y[m * N + n] = (double)s * (double)x_scale[m];"),
 }

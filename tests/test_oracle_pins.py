@@ -415,6 +415,101 @@ class TestQuantAct:
 
 
 # ==========================================================================
+# transformed activation rows: ReLU^2 gate and RMSNorm before the quantiser
+# ("BitNet b1.58 2B4T Technical Report 요약 설명", sec. 2: squared ReLU in the
+# feed-forward network, subln; "BitNet 논문 분석: 1-Bit LLM의 시대", section
+# "Absmean 양자화 함수": BitLinear_b158 applies an RMSNorm over the inputs
+# before activation_quant)
+# ==========================================================================
+def torch_rms_reference(X, up, gamma, eps):
+    """xhat in binary64 from torch's own RMSNorm; the gated row h is formed
+    by torch in binary32 (relu, square, times up)."""
+    import torch
+    h = torch.from_numpy(X)
+    if up is not None:
+        h = torch.relu(h) ** 2 * torch.from_numpy(up)
+    ref = torch.nn.functional.rms_norm(h.double(), (X.shape[1],), weight=torch.from_numpy(gamma).double(),
+                                       eps=float(eps))
+    return h.numpy(), ref.numpy()
+
+
+class TestActTransform:
+    def test_gate_hand_examples(self):
+        g = np.zeros((2, 64), np.float32)
+        u = np.ones((2, 64), np.float32)
+        g[0, :4], u[0, :4] = [-1.0, 0.0, 0.5, 2.0], [3.0, 5.0, -2.0, 0.25]
+        g[1, :4], u[1, :4] = [-3.0, 1.5, -0.5, 1.0], [-1.0, 2.0, 4.0, -1.0]
+        q, xs, rs = oracle.quant_act_ex(g, u)
+        # row 0: h = [0, 0, 0.25 * -2, 4 * 0.25] = [0, 0, -0.5, 1]: s = 127, -63.5 -> -64
+        assert q[0, :4].tolist() == [0, 0, -64, 127] and xs[0] == F32(1) / F32(127) and rs[0] == 63
+        # row 1: h = [0 (not 9 * -1), 2.25 * 2, 0, -1] = [0, 4.5, 0, -1]: s = 127 / 4.5
+        assert q[1, :4].tolist() == [0, 127, 0, -28] and xs[1] == F32(4.5) / F32(127)
+        assert not q[:, 4:].any()
+
+    def test_rms_closed_forms(self):
+        # x = c * (+1, -1, ...): mean(x^2) = c^2, every code is +-127 and
+        # x_scale = c / 127 / sqrt(c^2 + eps)
+        K = 256
+        alt = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+        one = np.ones(K, np.float32)
+        q, xs, rs = oracle.quant_act_ex((2.0 * alt)[None, :].astype(np.float32), gamma=one, eps=0.0)
+        assert np.array_equal(np.abs(q[0]), np.full(K, 127)) and rs[0] == 0
+        assert xs[0] == F32(1.0 / 127.0)                    # 2 / 127 / 2
+        q, xs, _ = oracle.quant_act_ex((1.5 * alt)[None, :].astype(np.float32), gamma=one, eps=0.75)
+        assert xs[0] == F32(math.sqrt(3.0) / 254.0)        # 1.5 / 127 / sqrt(3)
+        # gamma = 2 on even k, 1 on odd k: codes 127 and -64 (63.5 to even);
+        # mean(x^2) is taken before gamma: x_scale = 2 * 1.5 / 127 / sqrt(3)
+        gam = np.where(np.arange(K) % 2 == 0, 2.0, 1.0).astype(np.float32)
+        q, xs, _ = oracle.quant_act_ex((1.5 * alt)[None, :].astype(np.float32), gamma=gam, eps=0.75)
+        assert q[0, :2].tolist() == [127, -64]
+        assert xs[0] == F32(math.sqrt(3.0) / 127.0)
+
+    def test_unit_gamma_keeps_the_plain_codes(self):
+        # the per-row factor 1/rms divides out of the absmax codes
+        X = workloads.activations(np.random.default_rng(31), 12, 512, 0.01)
+        q0, _, rs0 = oracle.quant_act(X)
+        for eps in (0.0, 1e-5, 3.0):
+            q1, _, rs1 = oracle.quant_act_ex(X, gamma=np.ones(512, np.float32), eps=eps)
+            assert np.array_equal(q0, q1) and np.array_equal(rs0, rs1)
+
+    @pytest.mark.parametrize("gated", [False, True])
+    @pytest.mark.parametrize("eps", [0.0, 1e-6, 1e-5, 0.5])
+    def test_matches_torch_rms_norm(self, gated, eps):
+        rng = np.random.default_rng(32 + int(gated))
+        M, K = 24, 384
+        X = workloads.activations(rng, M, K, 0.01)
+        X[::3] *= F32(3e-3)                                 # rows where eps matters
+        up = workloads.activations(rng, M, K) if gated else None
+        gamma = rng.uniform(0.25, 1.75, K).astype(np.float32)
+        q, xs, rs = oracle.quant_act_ex(X, up, gamma, eps)
+        h, ref = torch_rms_reference(X, up, gamma, eps)
+        # codes: exactly the plain quantiser's codes of fl32(h * gamma)
+        qp, _, rsp = oracle.quant_act((h * gamma).astype(np.float32))
+        assert np.array_equal(q, qp) and np.array_equal(rs, rsp)
+        # scale: the largest |xhat| maps to 127
+        gmax = np.abs(ref).max(1)
+        assert np.all(np.abs(xs.astype(np.float64) * 127.0 - gmax) <= 1e-6 * gmax)
+        # every dequantised value within half a step of torch's xhat
+        err = np.abs(q * xs.astype(np.float64)[:, None] - ref)
+        assert np.all(err <= xs.astype(np.float64)[:, None] * (0.5 + 1e-5) + 1e-6 * np.abs(ref))
+
+    def test_zero_rows(self):
+        X = np.zeros((2, 128), np.float32)
+        for eps in (0.0, 1e-5):
+            q, xs, rs = oracle.quant_act_ex(X, X, np.ones(128, np.float32), eps)
+            assert not q.any() and not rs.any() and not xs.any()
+        # a gate that is never positive makes the row zero too
+        g = -np.abs(workloads.activations(np.random.default_rng(33), 2, 128))
+        q, xs, _ = oracle.quant_act_ex(g, np.ones_like(g), np.ones(128, np.float32), 1e-5)
+        assert not q.any() and not xs.any()
+
+    def test_identity_transform(self):
+        X = workloads.activations(np.random.default_rng(34), 6, 256, 0.01)
+        a, b = oracle.quant_act(X), oracle.quant_act_ex(X)
+        assert all(np.array_equal(u, v) for u, v in zip(a, b))
+
+
+# ==========================================================================
 # contraction and epilogue
 # ==========================================================================
 class TestForward:
