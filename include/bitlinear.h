@@ -168,6 +168,48 @@ bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, b
                                          const bitlinear_proj *projs, int32_t nproj,
                                          float *x_scale, hipStream_t stream);
 
+/* Transform of each activation row before the absmax quantisation: the steps
+ * either side of a BitNet linear, fused into the quantiser.
+ *   up (ReLU^2 gate; "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 2:
+ *      the feed-forward network uses squared ReLU): NULL, or M x K fp32
+ *      (16-byte aligned); the row becomes h[k] = fl32(fl32(r*r) * up[k]),
+ *      r = max(X[k], 0) -- X holding the gate projection's output and `up`
+ *      the up projection's.  NULL: h = X.
+ *   gamma, eps (RMSNorm; "BitNet 논문 분석: 1-Bit LLM의 시대", section
+ *      "Absmean 양자화 함수": BitLinear_b158 applies an RMSNorm over its inputs
+ *      before activation_quant; the 2B4T report, sec. 2, names subln): NULL,
+ *      or K fp32 weights (16-byte aligned); eps finite and >= 0.  The row is
+ *      normalised to h * rinv * gamma, rinv = 1 / sqrt(sum_k h^2 / K + eps).
+ *      rinv is a positive per-row factor, so it divides out of the absmax
+ *      codes: the codes are those of v[k] = fl32(h[k] * gamma[k]) (exactly
+ *      the formulas above with v for X) and rinv goes into the scale:
+ *      x_scale = fl32(g_m / 127 * rinv) evaluated in binary64, with the sum of
+ *      squares in binary64 in an unspecified order (within one binary32 ulp of
+ *      the in-order value).  NULL: no normalisation.
+ * Xq and x_rowsum stay bit-exact with a plain CPU evaluation. */
+typedef struct {
+    const float *up;
+    const float *gamma;
+    float eps;
+} bitlinear_act_transform;
+
+/* bitlinear_quant_act on transformed rows.  tr: host pointer, or NULL for no
+ * transform (then identical to bitlinear_quant_act). */
+bitlinear_status bitlinear_quant_act_ex(const float *X, const bitlinear_act_transform *tr, int64_t M,
+                                        int64_t K, int8_t *Xq, float *x_scale, int32_t *x_rowsum,
+                                        hipStream_t stream);
+
+/* bitlinear_forward_fused on transformed rows (tr as above, NULL for none):
+ * for a gated feed-forward block at decode, the down projection's call takes
+ * X = the gate output, tr->up = the up output and tr->gamma = the subln
+ * weight, so ReLU^2, the norm, the quantisation and the projection are one
+ * launch.  With a transform, supported for M == 1 and K <= 16384 (otherwise
+ * BITLINEAR_EUNSUPPORTED: use bitlinear_quant_act_ex, then
+ * bitlinear_forward).  x_scale receives the scale defined above. */
+bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_transform *tr, int64_t M,
+                                            int64_t K, bitlinear_nm nm, const bitlinear_proj *projs,
+                                            int32_t nproj, float *x_scale, hipStream_t stream);
+
 /* Thread-local text for the last non-OK status returned on this thread. */
 const char *bitlinear_last_error(void);
 

@@ -14,8 +14,10 @@ from .binding import (  # noqa: F401
     packed_size,
     pack_weights,
     quant_act,
+    quant_act_ex,
     forward,
     forward_fused,
+    forward_fused_ex,
     last_dispatch,
     library_path,
     load_library,

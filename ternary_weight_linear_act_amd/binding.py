@@ -40,6 +40,10 @@ class NM(ctypes.Structure):
     _fields_ = [("n", ctypes.c_int32), ("m", ctypes.c_int32)]
 
 
+class ActTransform(ctypes.Structure):
+    _fields_ = [("up", ctypes.c_void_p), ("gamma", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
 class Proj(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("w_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
                 ("Y", ctypes.c_void_p), ("acc", ctypes.c_void_p)]
@@ -69,8 +73,12 @@ def load_library():
     lib.bitlinear_quant_act.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp]
     lib.bitlinear_forward_fused.argtypes = [vp, i64, i64, NM, ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
+    lib.bitlinear_quant_act_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, vp, vp, vp, vp]
+    lib.bitlinear_forward_fused_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, NM,
+                                               ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     for f in ("bitlinear_packed_size", "bitlinear_pack_weights", "bitlinear_quant_act",
-              "bitlinear_forward", "bitlinear_forward_fused"):
+              "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_quant_act_ex",
+              "bitlinear_forward_fused_ex"):
         getattr(lib, f).restype = ctypes.c_int
     lib.bitlinear_last_error.restype = ctypes.c_char_p
     lib.bitlinear_last_dispatch.restype = ctypes.c_char_p
@@ -172,6 +180,45 @@ def quant_act(X, Xq=None, x_scale=None, x_rowsum=None, stream=None):
     return Xq, x_scale, x_rowsum
 
 
+def _transform(X, up, gamma, eps):
+    """The row transform struct (None when there is none)."""
+    import torch
+    M, K = X.shape
+    if up is not None:
+        _require(up, torch.float32, (M, K), "up")
+    if gamma is not None:
+        _require(gamma, torch.float32, (K,), "gamma")
+        if eps is None:
+            raise ValueError("eps is required with gamma")
+    if up is None and gamma is None:
+        return None
+    return ActTransform(None if up is None else up.data_ptr(), None if gamma is None else gamma.data_ptr(),
+                        0.0 if eps is None else float(eps))
+
+
+def quant_act_ex(X, up=None, gamma=None, eps=None, Xq=None, x_scale=None, x_rowsum=None, stream=None):
+    """quant_act on transformed rows: h = ReLU(X)^2 * up when `up` is given,
+    then RMSNorm with weight `gamma` (K) and `eps` when `gamma` is given; the
+    codes are taken from h * gamma and 1/rms goes into x_scale."""
+    import torch
+    _require(X, torch.float32, None, "X")
+    M, K = X.shape
+    tr = _transform(X, up, gamma, eps)
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    if x_rowsum is None:
+        x_rowsum = torch.empty(M, dtype=torch.int32, device=X.device)
+    _require(Xq, torch.int8, (M, K), "Xq")
+    _require(x_scale, torch.float32, (M,), "x_scale")
+    _require(x_rowsum, torch.int32, (M,), "x_rowsum")
+    _check("bitlinear_quant_act_ex", load_library().bitlinear_quant_act_ex(
+        _ptr(X), None if tr is None else ctypes.byref(tr), M, K, _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum),
+        _stream(stream)))
+    return Xq, x_scale, x_rowsum
+
+
 def forward(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=None, acc=None,
             want_acc=False, stream=None):
     """Y = (Xq . W_eff^T) * w_scale * x_scale, fp32 M x N.  Returns Y or (Y, acc)."""
@@ -204,9 +251,19 @@ def forward_fused(X, projs, nm=NM_DENSE, Ys=None, accs=None, want_acc=False, x_s
 
     Returns the list of Y tensors, or (Ys, accs) when accumulators are wanted.
     """
+    return forward_fused_ex(X, projs, nm=nm, Ys=Ys, accs=accs, want_acc=want_acc, x_scale=x_scale,
+                            stream=stream)
+
+
+def forward_fused_ex(X, projs, up=None, gamma=None, eps=None, nm=NM_DENSE, Ys=None, accs=None, want_acc=False,
+                     x_scale=None, stream=None):
+    """forward_fused on transformed rows (see quant_act_ex): with `up` the
+    rows are ReLU(X)^2 * up, with `gamma` and `eps` they are RMS-normalised
+    before the quantiser.  A transform is served at M = 1, K <= 16384."""
     import torch
     _require(X, torch.float32, None, "X")
     M, K = X.shape
+    tr = _transform(X, up, gamma, eps)
     n = len(projs)
     if Ys is None:
         Ys = [torch.empty((M, N), dtype=torch.float32, device=X.device) for (_, _, N) in projs]
@@ -223,6 +280,10 @@ def forward_fused(X, projs, nm=NM_DENSE, Ys=None, accs=None, want_acc=False, x_s
                       accs[i].data_ptr() if accs is not None else None)
     if x_scale is not None:
         _require(x_scale, torch.float32, (M,), "x_scale")
-    _check("bitlinear_forward_fused", load_library().bitlinear_forward_fused(
-        _ptr(X), M, K, _nm(nm), arr, n, _ptr(x_scale), _stream(stream)))
+    if tr is None:
+        _check("bitlinear_forward_fused", load_library().bitlinear_forward_fused(
+            _ptr(X), M, K, _nm(nm), arr, n, _ptr(x_scale), _stream(stream)))
+    else:
+        _check("bitlinear_forward_fused_ex", load_library().bitlinear_forward_fused_ex(
+            _ptr(X), ctypes.byref(tr), M, K, _nm(nm), arr, n, _ptr(x_scale), _stream(stream)))
     return (Ys, accs) if accs is not None else Ys

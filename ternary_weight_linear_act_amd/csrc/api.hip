@@ -3,6 +3,7 @@
 //
 // Every check runs on the host before anything is launched, so a rejected
 // call touches neither the GPU nor the HIP runtime.
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -27,7 +28,7 @@ hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_
 
 hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
                               int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
-                              hipStream_t stream, const char **name);
+                              const ActTransform &tr, hipStream_t stream, const char **name);
 
 // Largest M served by the dot4 GEMV (the fallback when the skinny MFMA kernel
 // has no configuration for the shape); larger M runs on the MFMA GEMM.
@@ -48,7 +49,8 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
         one.Y[0] = Y;
         one.acc[0] = acc;
         one.N[0] = N;
-        const hipError_t e = launch_decode_dot4(nullptr, Xq, x_scale, x_rowsum, M, K, p, one, nullptr, stream, name);
+        const hipError_t e = launch_decode_dot4(nullptr, Xq, x_scale, x_rowsum, M, K, p, one, nullptr,
+                                                ActTransform{nullptr, nullptr, 0.0f}, stream, name);
         if (e != hipErrorNotSupported) return e;
     }
     if (M <= 16) {
@@ -127,6 +129,21 @@ bitlinear_status check_ptr(const void *p, uintptr_t align, const char *name)
     return BITLINEAR_OK;
 }
 
+// The row transform: NULL or an all-NULL struct is none.
+bitlinear_status check_transform(const bitlinear_act_transform *tr, bl::ActTransform *out)
+{
+    *out = bl::ActTransform{nullptr, nullptr, 0.0f};
+    if (!tr) return BITLINEAR_OK;
+    if (tr->up && !aligned(tr->up, 16)) return fail(BITLINEAR_EINVAL, "tr->up must be 16-byte aligned");
+    if (tr->gamma) {
+        if (!aligned(tr->gamma, 16)) return fail(BITLINEAR_EINVAL, "tr->gamma must be 16-byte aligned");
+        if (!(tr->eps >= 0.0f) || !isfinite(tr->eps))
+            return fail(BITLINEAR_EINVAL, "tr->eps must be finite and >= 0");
+    }
+    *out = bl::ActTransform{tr->up, tr->gamma, tr->gamma ? tr->eps : 0.0f};
+    return BITLINEAR_OK;
+}
+
 size_t packed_bytes_for(int64_t N, int64_t K, bl::Pattern p)
 {
     switch (p) {
@@ -192,16 +209,26 @@ bitlinear_status bitlinear_pack_weights(const float *W, int64_t N, int64_t K, bi
 bitlinear_status bitlinear_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
                                      int32_t *x_rowsum, hipStream_t stream)
 {
+    return bitlinear_quant_act_ex(X, nullptr, M, K, Xq, x_scale, x_rowsum, stream);
+}
+
+bitlinear_status bitlinear_quant_act_ex(const float *X, const bitlinear_act_transform *tr, int64_t M,
+                                        int64_t K, int8_t *Xq, float *x_scale, int32_t *x_rowsum,
+                                        hipStream_t stream)
+{
     CHECK(check_m(M));
     CHECK(check_k(K));
+    bl::ActTransform t;
+    CHECK(check_transform(tr, &t));
     if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }   // M-sized buffers may be NULL
     CHECK(check_ptr(X, 16, "X"));
     CHECK(check_ptr(Xq, 16, "Xq"));
     CHECK(check_ptr(x_scale, 4, "x_scale"));
     if (x_rowsum && !aligned(x_rowsum, 4)) return fail(BITLINEAR_EINVAL, "x_rowsum must be 4-byte aligned");
-    hipError_t e = bl::launch_quant_act(X, M, K, Xq, x_scale, x_rowsum, stream);
+    hipError_t e = bl::launch_quant_act_ex(X, t, M, K, Xq, x_scale, x_rowsum, stream);
     if (e != hipSuccess) return hip_fail("quant_act launch", e);
-    set_dispatch("quant_act");
+    static const char *names[4] = {"quant_act", "quant_act_gate", "quant_act_norm", "quant_act_gate_norm"};
+    set_dispatch(names[(t.up ? 1 : 0) | (t.gamma ? 2 : 0)]);
     return BITLINEAR_OK;
 }
 
@@ -234,10 +261,20 @@ bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, b
                                          const bitlinear_proj *projs, int32_t nproj, float *x_scale,
                                          hipStream_t stream)
 {
+    return bitlinear_forward_fused_ex(X, nullptr, M, K, nm, projs, nproj, x_scale, stream);
+}
+
+bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_transform *tr, int64_t M,
+                                            int64_t K, bitlinear_nm nm, const bitlinear_proj *projs,
+                                            int32_t nproj, float *x_scale, hipStream_t stream)
+{
     bl::Pattern p;
     CHECK(check_nm(nm, &p));
     CHECK(check_m(M));
     CHECK(check_k(K));
+    bl::ActTransform t;
+    CHECK(check_transform(tr, &t));
+    const bool transformed = t.up || t.gamma;
     if (!projs) return fail(BITLINEAR_EINVAL, "projs must not be NULL");
     if (nproj < 1) return fail(BITLINEAR_EINVAL, "nproj = %d must be >= 1", nproj);
     if (nproj > bl::kMaxFusedProj)
@@ -261,7 +298,10 @@ bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, b
     CHECK(check_ptr(X, 16, "X"));
     if (x_scale && !aligned(x_scale, 4)) return fail(BITLINEAR_EINVAL, "x_scale must be 4-byte aligned");
     const char *name = "";
-    hipError_t e = bl::launch_decode_dot4(X, nullptr, nullptr, nullptr, M, K, p, args, x_scale, stream, &name);
+    hipError_t e = bl::launch_decode_dot4(X, nullptr, nullptr, nullptr, M, K, p, args, x_scale, t, stream, &name);
+    if (e == hipErrorNotSupported && transformed)
+        return fail(BITLINEAR_EUNSUPPORTED, "fused decode with a row transform supports M == 1 and K <= 16384 "
+                    "(M = %lld, K = %lld)", (long long)M, (long long)K);
     if (e == hipErrorNotSupported) e = bl::launch_fused_forward(X, M, K, p, args, x_scale, stream, &name);
     if (e == hipErrorNotSupported)
         return fail(BITLINEAR_EUNSUPPORTED, "fused decode supports 1 <= M <= 4 and K <= %s (M = %lld, K = %lld)",

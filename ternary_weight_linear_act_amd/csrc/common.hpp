@@ -333,4 +333,52 @@ __device__ __forceinline__ uint32_t act_quant4(float x0, float x1, float x2, flo
     return (b0 & 0xFFu) | ((b1 & 0xFFu) << 8) | ((b2 & 0xFFu) << 16) | (b3 << 24);
 }
 
+
+// ---------------------------------------------------------------------------
+// Transform of an activation row before the quantiser, for the steps either
+// side of a BitNet linear ("BitNet b1.58 2B4T Technical Report 요약 설명",
+// sec. 2: squared ReLU in the feed-forward network, subln; "BitNet 논문
+// 분석: 1-Bit LLM의 시대", section "Absmean 양자화 함수": BitLinear_b158
+// normalises its input with an RMSNorm before activation_quant).
+//   kTrGate: h = fl32(fl32(r * r) * up), r = max(x, 0)   (else h = x)
+//   kTrNorm: RMSNorm with weight gamma.  Its per-row factor 1/rms divides
+//            out of the absmax codes, so the codes are those of
+//            v = fl32(h * gamma) and 1/rms goes into the scale:
+//            rinv = 1 / sqrt(sum h^2 / K + eps) in binary64 (each square
+//            exact), x_scale = fl32(max|v| / 127 * rinv).
+// Only the sum's order differs between evaluations: its relative error is at
+// most K * 2^-53 (non-negative terms), far below binary32's half-ulp, so
+// x_scale can differ from an in-order evaluation by one ulp at most.
+// ---------------------------------------------------------------------------
+constexpr int kTrGate = 1, kTrNorm = 2;
+
+struct ActTransform {
+    const float *up;      // M x K, kTrGate
+    const float *gamma;   // K, kTrNorm
+    float eps;
+};
+
+__device__ __forceinline__ float act_gate(float x, float u)
+{
+    const float r = fmaxf(x, 0.0f);
+    return (r * r) * u;
+}
+
+__device__ __forceinline__ double act_rinv(double ss, int64_t K, float eps)
+{
+    return 1.0 / sqrt(ss / (double)K + (double)eps);
+}
+
+__device__ __forceinline__ float act_norm_scale(float g, double rinv)
+{
+    return g == 0.0f ? 0.0f : (float)((double)g / 127.0 * rinv);
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
 }  // namespace bl

@@ -1,309 +1,10 @@
-// Decode forward for one token (M = 1) on packed int8 dot products, with or
-// without the activation quantisation fused in, for one or more projections
-// that share the activations.
-//
-// "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 2 (per-token absmax
-// 8-bit activations) and sec. 5.1 (the packed weights, four per byte, are
-// what moves from HBM; they are unpacked on chip); "BitNet 논문 분석: 1-Bit
-// LLM의 시대", section "Absmean 양자화 함수" (activation_quant, the integer
-// linear of ternary weights and int8 activations, the rescale).  Same
-// arithmetic as bitlinear_quant_act + bitlinear_forward, bit for bit.
-//
-// Why not the MFMA kernel at M = 1: with one token the MFMA's 16 token rows
-// are 15/16 padding, and staging the weights through LDS into the MFMA
-// operand layout is a second pass over every weight byte.  Here a weight
-// chunk (16 bytes = 64 codes) goes from the load straight into 16
-// v_dot4_i32_iu8 against the activation bytes, read from LDS.
-//
-// Layout: LPR lanes share a weight row, lane j takes chunks j, j + LPR, ...
-// (so a load instruction reads LPR * 16 contiguous bytes of each row), every
-// load of the lane is issued up front, the activations first.  A workgroup is
-// 4 waves, 256 / LPR rows.  The LPR partial sums meet through DPP lane moves;
-// no barrier follows the loads but the one that publishes the int8
-// activations, which the weights are most likely still in flight for.
-// Codes are c = t + 1, so the sums are sum c*q and the epilogue subtracts the
-// activation row sum.
-#include "fused_impl.hpp"
+// Host side of the one-token decode kernel (decode_dot4_impl.hpp): the
+// configuration rule and the launch.  The row-transform variants of the fused
+// form are instantiated in decode_dot4_tr.hip.
+#include "decode_dot4_impl.hpp"
 
 namespace bl {
-namespace dot4 {
-
-using skinny::i32x4;
-using skinny::u32x4;
-using skinny::RawChunk;
-using skinny::load_raw_chunk;
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kMaxK = 16384;                 // activation row in LDS and registers
-
-template <int LPR>
-__device__ __forceinline__ int lanes_sum(int v)
-{
-    v += dpp_move<kDppQuadXor1>(v);
-    v += dpp_move<kDppQuadXor2>(v);
-    if (LPR >= 8) v += dpp_move<kDppRowHalfMirror>(v);
-    if (LPR >= 16) v += dpp_move<kDppRowMirror>(v);
-    if (LPR >= 32) v += __shfl_xor(v, 16, 64);
-    if (LPR >= 64) v += __shfl_xor(v, 32, 64);
-    return v;
-}
-
-// FUSED: X is the fp32 activation row (quantised here; x_scale_out, if not
-// NULL, receives its scale); otherwise Xq / x_scale / x_rowsum are the
-// quantised row.  args.block_start[i] is the first workgroup of projection i.
-// U = chunks per lane, fixed at compile time so that every load is issued
-// unconditionally (a load under a branch makes the compiler wait for it at
-// the join); the host guarantees K <= 64 * U * LPR.  W waves per workgroup,
-// W * 64 / LPR rows.
-template <Pattern P, int LPR, int U, bool FUSED, int W = 4>
-__global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
-    const float *__restrict__ X, const int8_t *__restrict__ Xq, const float *__restrict__ x_scale,
-    const int32_t *__restrict__ x_rowsum, int64_t K, FusedProjArgs args, float *__restrict__ x_scale_out)
-{
-    constexpr int RPW = 64 / LPR, RB = W * RPW, kThreads = 64 * W;
-    extern __shared__ __attribute__((aligned(16))) uint8_t s_x[];      // K int8 activations
-    __shared__ float s_max[W];
-    __shared__ int s_sum[W];
-    __shared__ uint32_t s_sel[P == Pattern::Dense ? 1 : 2 * nm_sel_entries(P)];   // N:M byte selectors
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int p = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxFusedProj; ++i)
-        if (i < args.nproj && (int)blockIdx.x >= args.block_start[i]) p = i;
-    const int64_t N = args.N[p];
-    const uint8_t *packed = args.packed[p];
-    const int64_t row = (int64_t)(blockIdx.x - args.block_start[p]) * RB + wave * RPW + lane / LPR;
-    const int j = lane % LPR;
-    const int64_t C = K / 64;
-    float *Y = args.Y[p];
-    int32_t *acc_out = args.acc[p];
-    const float *w_scale = args.w_scale[p];
-    // every argument read later in SGPRs now (a pending scalar load would make
-    // the compiler wait for all outstanding memory operations at its use)
-    asm volatile("" ::"s"(X), "s"(Xq), "s"(x_scale), "s"(x_rowsum), "s"(packed), "s"(Y), "s"(acc_out),
-                 "s"(w_scale), "s"(x_scale_out));
-
-    // 0. the scalars the epilogue needs, issued before everything else: read
-    //    at the end, each would cost a full memory round trip there
-    const float wsc = w_scale[0];
-    float xsc = 0.0f;
-    int rs = 0;
-    if constexpr (!FUSED) {
-        xsc = x_scale[0];
-        rs = x_rowsum[0];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 1. activations: 16-byte loads, enough for K = 64 * U * LPR (indices
-    //    past the row re-read element 0 and are never used)
-    constexpr int XR = FUSED ? (16 * U * LPR + kThreads - 1) / kThreads : (4 * U * LPR + kThreads - 1) / kThreads;
-    const int64_t n4 = K / 4, n16 = K / 16;
-    f32x4 xf[FUSED ? XR : 1];          // ext vectors: HIP's float4 / uint4 structs
-    u32x4 xb[FUSED ? 1 : XR];          // in an array are not kept in registers
-#pragma unroll
-    for (int t = 0; t < XR; ++t) {
-        const int64_t i = tid + (int64_t)t * kThreads;
-        if constexpr (FUSED) xf[t] = reinterpret_cast<const f32x4 *>(X)[i < n4 ? i : 0];
-        else xb[t] = reinterpret_cast<const u32x4 *>(Xq)[i < n16 ? i : 0];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 2. the lane's weight chunks (rows past N re-read row N - 1 and chunks
-    //    past the row re-read chunk C - 1; neither is used)
-    RawChunk<P> w[U];
-    const int64_t r = min(row, N - 1);
-#pragma unroll
-    for (int u = 0; u < U; ++u) w[u] = load_raw_chunk<P>(packed, N, K, r, min((int64_t)(j + u * LPR), C - 1));
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (P != Pattern::Dense)                 // ready after the barrier below
-        for (int i = tid; i < nm_sel_entries(P); i += kThreads) nm_sel_entry<P>(i, &s_sel[2 * i], &s_sel[2 * i + 1]);
-
-    // 3. the int8 activations into LDS, with their scale and row sum
-    if constexpr (FUSED) {
-        // branch-free: entries past the row (re-reads of element 0) are
-        // masked out of the max and the sum and never stored
-        float g = 0.0f;
-#pragma unroll
-        for (int t = 0; t < XR; ++t) {
-            const f32x4 a = xf[t];
-            const float m = fmaxf(fmaxf(fabsf(a[0]), fabsf(a[1])), fmaxf(fabsf(a[2]), fabsf(a[3])));
-            g = fmaxf(g, tid + (int64_t)t * kThreads < n4 ? m : 0.0f);
-        }
-        g = wave_max_dpp(g);
-        if (lane == 0) s_max[wave] = g;
-        __syncthreads();
-        g = s_max[0];
-#pragma unroll
-        for (int i = 1; i < W; ++i) g = fmaxf(g, s_max[i]);
-        const float up = act_prescale(g);
-        const float s = act_scale(g, up);
-        if (up != 1.0f) {                              // workgroup-uniform, rare
-#pragma unroll
-            for (int t = 0; t < XR; ++t) xf[t] *= up;
-        }
-        int sum = 0;
-        uint32_t *q4 = reinterpret_cast<uint32_t *>(s_x);
-#pragma unroll
-        for (int t = 0; t < XR; ++t) {
-            const int64_t i = tid + (int64_t)t * kThreads;
-            const f32x4 a = xf[t];
-            int s4;
-            const uint32_t packed4 = act_quant4(a[0], a[1], a[2], a[3], s, &s4);
-            const bool in = i < n4;
-            sum += in ? s4 : 0;
-            if (in) q4[i] = packed4;
-        }
-        sum = wave_sum_dpp(sum);
-        if (lane == 0) s_sum[wave] = sum;
-        __syncthreads();
-        rs = s_sum[0];
-#pragma unroll
-        for (int i = 1; i < W; ++i) rs += s_sum[i];
-        xsc = (g == 0.0f) ? 0.0f : g / 127.0f;
-        if (x_scale_out && blockIdx.x == 0 && tid == 0) x_scale_out[0] = xsc;
-    } else {
-#pragma unroll
-        for (int t = 0; t < XR; ++t) {
-            const int64_t i = tid + (int64_t)t * kThreads;
-            if (i < n16) reinterpret_cast<u32x4 *>(s_x)[i] = xb[t];
-        }
-        __syncthreads();
-    }
-
-    // 4. dot products, branch-free (a branch per chunk would make the
-    //    compiler wait for every weight load at the first one), 16 v_dot4
-    //    per chunk against 64 activation bytes; chunks past the row (c >= C,
-    //    last round only) contribute nothing.
-    int acc;
-    if constexpr (P == Pattern::Dense) {
-        // In word w, code pair s of each byte is (w >> 2s) & 0x03; pairs 1
-        // and 2 are taken in place (masks 0x0C, 0x30: the code times 4 or
-        // 16, still a positive int8) into accumulators of their own, divided
-        // back exactly at the end; pair 3 is shifted down (times 64 would not
-        // fit an int8).
-        int a0 = 0, a1 = 0, a2 = 0, a3 = 0;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c = j + u * LPR;
-            const bool in = c < C;
-            const i32x4 *xp = reinterpret_cast<const i32x4 *>(s_x + (in ? c : C - 1) * 64);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const i32x4 xx = xp[q];
-                const uint32_t word = in ? w[u].w[q] : 0u;
-                a0 = __builtin_amdgcn_sdot4((int)(word & kCodeMask), xx[0], a0, false);
-                a1 = __builtin_amdgcn_sdot4((int)(word & (kCodeMask << 2)), xx[1], a1, false);
-                a2 = __builtin_amdgcn_sdot4((int)(word & (kCodeMask << 4)), xx[2], a2, false);
-                a3 = __builtin_amdgcn_sdot4((int)((word >> 6) & kCodeMask), xx[3], a3, false);
-            }
-        }
-        // a1 = 4 * S1 and a2 = 16 * S2 exactly, so the shifts are exact;
-        // |a2| <= 16 * 2 * 127 * K / 4 < 2^31 for K <= 16384
-        acc = a0 + (a1 >> 2) + (a2 >> 4) + a3;
-    } else {
-        // N:M: the kept codes are not decoded to dense words; each group's
-        // kept weights, as 64 * t bytes, are spread over its positions by a
-        // byte permute (nm_dot_superblock), pruned positions 0.  Chunks past
-        // the row get code 1 (t = 0) everywhere.
-        int a4[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t c = j + u * LPR;
-            const bool in = c < C;
-            const i32x4 *xp = reinterpret_cast<const i32x4 *>(s_x + (in ? c : C - 1) * 64);
-            int32_t xw[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const i32x4 xx = xp[q];
-                xw[4 * q] = xx[0]; xw[4 * q + 1] = xx[1]; xw[4 * q + 2] = xx[2]; xw[4 * q + 3] = xx[3];
-            }
-            uint32_t vals[RawChunk<P>::kVals];
-#pragma unroll
-            for (int v = 0; v < RawChunk<P>::kVals; ++v) vals[v] = in ? w[u].w[v] : 0x55555555u;
-            nm_dot_superblock<P, DeviceOps>(vals, w[u].w + RawChunk<P>::kVals, s_sel, xw, a4);
-        }
-        // every term is 64 * t * x: the shift is exact; |sum| <= 64 * 128 * K < 2^31
-        acc = (a4[0] + a4[1] + a4[2] + a4[3]) >> 6;
-    }
-    acc = lanes_sum<LPR>(acc);
-    if (j == 0 && row < N) {
-        // dense codes are t + 1: subtract the activation row sum
-        const int av = (P == Pattern::Dense) ? acc - rs : acc;
-        Y[row] = (float)av * (wsc * xsc);
-        if (acc_out) acc_out[row] = av;
-    }
-}
-
-}  // namespace dot4
-
 namespace {
-
-using Fn = void (*)(dim3, size_t, hipStream_t, const float *, const int8_t *, const float *, const int32_t *,
-                    int64_t, const FusedProjArgs &, float *);
-
-template <Pattern P, int LPR, int U, bool FUSED, int W = 4>
-void launch(dim3 grid, size_t lds, hipStream_t stream, const float *X, const int8_t *Xq, const float *xs,
-            const int32_t *rs, int64_t K, const FusedProjArgs &args, float *x_scale_out)
-{
-    hipLaunchKernelGGL((dot4::decode_dot4_kernel<P, LPR, U, FUSED, W>), grid, dim3(64 * W), lds, stream, X, Xq, xs,
-                       rs, K, args, x_scale_out);
-}
-
-// Fused, 8 lanes per row, 8 waves (64 rows per workgroup)
-template <Pattern P>
-Fn pick_w8(int u)
-{
-    switch (u) {
-    case 1: return launch<P, 8, 1, true, 8>;
-    case 2: return launch<P, 8, 2, true, 8>;
-    case 3: return launch<P, 8, 3, true, 8>;
-    case 4: return launch<P, 8, 4, true, 8>;
-    case 5: return launch<P, 8, 5, true, 8>;
-    case 6: return launch<P, 8, 6, true, 8>;
-    case 7: return launch<P, 8, 7, true, 8>;
-    default: return nullptr;
-    }
-}
-
-// The (lanes per row, chunks per lane) pairs the host rule below can pick:
-// plain U <= 5 (<= 4 at 64 lanes), fused U <= 7 (4 at 64 lanes).
-template <Pattern P, bool FUSED>
-Fn pick(int lpr, int u)
-{
-    switch (lpr * 16 + u) {
-    case 8 * 16 + 1: return launch<P, 8, 1, FUSED>;
-    case 8 * 16 + 2: return launch<P, 8, 2, FUSED>;
-    case 8 * 16 + 3: return launch<P, 8, 3, FUSED>;
-    case 8 * 16 + 4: return launch<P, 8, 4, FUSED>;
-    case 8 * 16 + 5: return launch<P, 8, 5, FUSED>;
-    case 16 * 16 + 4: return launch<P, 16, 4, FUSED>;
-    case 16 * 16 + 5: return launch<P, 16, 5, FUSED>;
-    case 32 * 16 + 4: return launch<P, 32, 4, FUSED>;
-    case 32 * 16 + 5: return launch<P, 32, 5, FUSED>;
-    case 64 * 16 + 4: return launch<P, 64, 4, FUSED>;
-    default: break;
-    }
-    if constexpr (FUSED) {
-        switch (lpr * 16 + u) {
-        case 8 * 16 + 6: return launch<P, 8, 6, true>;
-        case 8 * 16 + 7: return launch<P, 8, 7, true>;
-        case 16 * 16 + 6: return launch<P, 16, 6, true>;
-        case 16 * 16 + 7: return launch<P, 16, 7, true>;
-        case 32 * 16 + 6: return launch<P, 32, 6, true>;
-        case 32 * 16 + 7: return launch<P, 32, 7, true>;
-        default: return nullptr;
-        }
-    } else {
-        switch (lpr * 16 + u) {
-        case 16 * 16 + 3: return launch<P, 16, 3, false>;
-        case 32 * 16 + 3: return launch<P, 32, 3, false>;
-        case 64 * 16 + 3: return launch<P, 64, 3, false>;
-        default: return nullptr;
-        }
-    }
-}
 
 thread_local char g_name[64];
 
@@ -318,7 +19,7 @@ thread_local char g_name[64];
 // hipErrorNotSupported when M != 1 or K is too large.
 hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
                               int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
-                              hipStream_t stream, const char **name)
+                              const ActTransform &tr, hipStream_t stream, const char **name)
 {
     if (M != 1 || K > dot4::kMaxK || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
     const int64_t C = K / 64;
@@ -341,8 +42,11 @@ hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs,
     }
     for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
     if (blocks > (1LL << 30)) return hipErrorNotSupported;
+    const int trb = (tr.up ? kTrGate : 0) | (tr.gamma ? kTrNorm : 0);
+    if (trb && !fused) return hipErrorNotSupported;
     Fn f = nullptr;
-    switch (p) {
+    if (trb) f = pick_dot4_tr(p, trb, w8, lpr, u);
+    else switch (p) {
     case Pattern::Dense:
         f = w8 ? pick_w8<Pattern::Dense>(u) : fused ? pick<Pattern::Dense, true>(lpr, u) : pick<Pattern::Dense, false>(lpr, u);
         break;
@@ -354,11 +58,12 @@ hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs,
         break;
     }
     if (!f) return hipErrorNotSupported;
-    snprintf(g_name, sizeof g_name, "%s_%s_lpr%d_u%d_p%d%s", fused ? "fused_decode_dot4" : "decode_dot4",
+    static const char *trn[4] = {"", "_gate", "_norm", "_gate_norm"};
+    snprintf(g_name, sizeof g_name, "%s_%s_lpr%d_u%d_p%d%s%s", fused ? "fused_decode_dot4" : "decode_dot4",
              p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", lpr, u, args.nproj,
-             w8 ? "_w8" : "");
+             w8 ? "_w8" : "", trn[trb]);
     *name = g_name;
-    f(dim3((unsigned)blocks), (size_t)K, stream, X, Xq, xs, rs, K, args, x_scale_out);
+    f(dim3((unsigned)blocks), (size_t)K, stream, X, Xq, xs, rs, K, args, x_scale_out, tr);
     return hipGetLastError();
 }
 

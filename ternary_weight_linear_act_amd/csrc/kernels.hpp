@@ -10,6 +10,11 @@ namespace bl {
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
                             int32_t *x_rowsum, hipStream_t stream);
 
+// The same on rows transformed first (ReLU^2 gate and/or RMSNorm; tr.up and
+// tr.gamma NULL for none).
+hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64_t K, int8_t *Xq,
+                               float *x_scale, int32_t *x_rowsum, hipStream_t stream);
+
 // beta: per-row binary64 |W| sums into `rowsum`, then one ordered sum.
 hipError_t launch_absmean(const float *W, int64_t N, int64_t K, double *rowsum, float *w_scale,
                           hipStream_t stream);

@@ -11,6 +11,9 @@
 // |x| to the row maximum (exact, order-free) through DPP lane moves and LDS.
 // Pass 2 re-reads the row (L2-resident), quantises, stores four int8 per
 // 32-bit store and reduces the int32 row sum the forward kernels need.
+// Optionally the row is transformed first (ReLU^2 gate, RMSNorm; see
+// common.hpp): the same two passes over the transformed values, with the
+// norm's sum of squares reduced in binary64 beside max|v|.
 #include "kernels.hpp"
 
 namespace bl {
@@ -18,26 +21,61 @@ namespace {
 
 constexpr int kQuantBlock = 256;
 constexpr int kWaves = kQuantBlock / 64;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// TR: the row transform (kTrGate, kTrNorm bits; common.hpp).  Pass 1 forms
+// the transformed row v (and h's sum of squares for the norm) and reduces
+// max|v|; pass 2 forms v again (same operations, same values) and quantises.
+template <int TR>
 __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
-    const float *__restrict__ X, int64_t K, int8_t *__restrict__ Xq,
+    const float *__restrict__ X, ActTransform tr, int64_t K, int8_t *__restrict__ Xq,
     float *__restrict__ x_scale, int32_t *__restrict__ x_rowsum)
 {
     __shared__ float s_max[kWaves];
     __shared__ int s_sum[kWaves];
+    __shared__ double s_ss[kWaves];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const float4 *x4 = reinterpret_cast<const float4 *>(X + row * K);
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(X + row * K);
+    const f32x4 *u4 = reinterpret_cast<const f32x4 *>((TR & kTrGate) ? tr.up + row * K : X);
+    const f32x4 *g4 = reinterpret_cast<const f32x4 *>((TR & kTrNorm) ? tr.gamma : X);
     int *q4 = reinterpret_cast<int *>(Xq + row * K);
     const int64_t n4 = K / 4;
 
+    // h (gated row) and v (what the codes are taken from) of entries 4i..4i+3
+    auto row4 = [&](int64_t i, f32x4 &h) -> f32x4 {
+        h = x4[i];
+        if constexpr ((TR & kTrGate) != 0) {
+            const f32x4 u = u4[i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) h[c] = act_gate(h[c], u[c]);
+        }
+        f32x4 v = h;
+        if constexpr ((TR & kTrNorm) != 0) {
+            const f32x4 gm = g4[i];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) v[c] = h[c] * gm[c];
+        }
+        return v;
+    };
+
     float g = 0.0f;
+    double ss = 0.0;
     for (int64_t i = tid; i < n4; i += kQuantBlock) {
-        const float4 v = x4[i];
-        g = fmaxf(g, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+        f32x4 h;
+        const f32x4 v = row4(i, h);
+        g = fmaxf(g, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+        if constexpr ((TR & kTrNorm) != 0) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) ss += (double)h[c] * (double)h[c];
+        }
     }
     g = wave_max_dpp(g);
     if (lane == 0) s_max[wave] = g;
+    if constexpr ((TR & kTrNorm) != 0) {
+        ss = wave_sum_f64(ss);
+        if (lane == 0) s_ss[wave] = ss;
+    }
     __syncthreads();
     g = s_max[0];
 #pragma unroll
@@ -46,20 +84,13 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
     int sum = 0;
     const float up = act_prescale(g);
     const float s = act_scale(g, up);        // IEEE binary32 division
-    if (up == 1.0f) {
-        for (int64_t i = tid; i < n4; i += kQuantBlock) {
-            const float4 v = x4[i];
-            int s4;
-            q4[i] = (int)act_quant4(v.x, v.y, v.z, v.w, s, &s4);
-            sum += s4;
-        }
-    } else {
-        for (int64_t i = tid; i < n4; i += kQuantBlock) {
-            const float4 v = x4[i];
-            int s4;
-            q4[i] = (int)act_quant4(v.x * up, v.y * up, v.z * up, v.w * up, s, &s4);
-            sum += s4;
-        }
+    for (int64_t i = tid; i < n4; i += kQuantBlock) {
+        f32x4 h;
+        f32x4 v = row4(i, h);
+        if (up != 1.0f) v *= up;              // row-uniform, rare
+        int s4;
+        q4[i] = (int)act_quant4(v[0], v[1], v[2], v[3], s, &s4);
+        sum += s4;
     }
     sum = wave_sum_dpp(sum);
     if (lane == 0) s_sum[wave] = sum;
@@ -68,7 +99,14 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
         int total = 0;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) total += s_sum[w];
-        x_scale[row] = (g == 0.0f) ? 0.0f : g / 127.0f;
+        if constexpr ((TR & kTrNorm) != 0) {
+            double t = 0.0;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) t += s_ss[w];
+            x_scale[row] = act_norm_scale(g, act_rinv(t, K, tr.eps));
+        } else {
+            x_scale[row] = (g == 0.0f) ? 0.0f : g / 127.0f;
+        }
         if (x_rowsum) x_rowsum[row] = total;
     }
 }
@@ -78,9 +116,24 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
                             int32_t *x_rowsum, hipStream_t stream)
 {
+    return launch_quant_act_ex(X, ActTransform{nullptr, nullptr, 0.0f}, M, K, Xq, x_scale, x_rowsum, stream);
+}
+
+hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64_t K, int8_t *Xq,
+                               float *x_scale, int32_t *x_rowsum, hipStream_t stream)
+{
     if (M == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_act_kernel, dim3((unsigned)M), dim3(kQuantBlock), 0, stream, X, K, Xq,
-                       x_scale, x_rowsum);
+    const int t = (tr.up ? kTrGate : 0) | (tr.gamma ? kTrNorm : 0);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(kQuantBlock), 0, stream, X, tr, K, Xq, x_scale,
+                           x_rowsum);
+    };
+    switch (t) {
+    case 0: go(quant_act_kernel<0>); break;
+    case kTrGate: go(quant_act_kernel<kTrGate>); break;
+    case kTrNorm: go(quant_act_kernel<kTrNorm>); break;
+    default: go(quant_act_kernel<kTrGate | kTrNorm>); break;
+    }
     return hipGetLastError();
 }
 

@@ -30,7 +30,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward",
-                 "bitlinear_packed_size", "bitlinear_last_error", "bitlinear_last_dispatch"):
+                 "bitlinear_packed_size", "bitlinear_last_error", "bitlinear_last_dispatch",
+                 "bitlinear_forward_fused", "bitlinear_quant_act_ex", "bitlinear_forward_fused_ex"):
         assert want in names
 
 
@@ -129,6 +130,25 @@ def test_quant_validation(lib):
     assert q(P(), -1, 64, P(), P(), P(), None) == -1
     assert q(P(), 0, 64, P(), P(), None, None) == 0
     assert q(None, 0, 64, None, None, None, None) == 0
+
+
+def test_transform_validation(lib):
+    from ternary_weight_linear_act_amd.binding import NM, ActTransform, Proj
+    q = lib.bitlinear_quant_act_ex
+    ok = ActTransform(A, A, 1e-5)
+    assert q(P(), ctypes.byref(ActTransform(A + 4, None, 0.0)), 4, 64, P(), P(), P(), None) == -1   # up misaligned
+    assert q(P(), ctypes.byref(ActTransform(None, A + 8, 0.0)), 4, 64, P(), P(), P(), None) == -1   # gamma misaligned
+    assert q(P(), ctypes.byref(ActTransform(None, A, -1.0)), 4, 64, P(), P(), P(), None) == -1      # eps < 0
+    assert q(P(), ctypes.byref(ActTransform(None, A, float("nan"))), 4, 64, P(), P(), P(), None) == -1
+    assert q(P(), ctypes.byref(ActTransform(None, A, float("inf"))), 4, 64, P(), P(), P(), None) == -1
+    assert q(P(), ctypes.byref(ok), 4, 65, P(), P(), P(), None) == -1                               # bad K
+    assert q(None, ctypes.byref(ok), 0, 64, None, None, None, None) == 0                            # M = 0
+    f = lib.bitlinear_forward_fused_ex
+    arr = (Proj * 1)(Proj(A, A, 64, A, None))
+    assert f(P(), ctypes.byref(ok), 2, 128, NM(0, 0), arr, 1, None, None) == -2          # transform: M == 1 only
+    assert f(P(), ctypes.byref(ok), 1, 16448, NM(0, 0), arr, 1, None, None) == -2        # ... and K <= 16384
+    assert f(P(), ctypes.byref(ActTransform(None, A, -2.0)), 1, 128, NM(0, 0), arr, 1, None, None) == -1
+    assert f(None, ctypes.byref(ok), 0, 128, NM(0, 0), arr, 1, None, None) == 0
 
 
 def test_pack_validation(lib):

@@ -1,0 +1,211 @@
+"""GPU parity of the row transform in front of the quantiser: the ReLU^2 gate
+and RMSNorm ("BitNet b1.58 2B4T Technical Report 요약 설명", sec. 2; "BitNet
+논문 분석: 1-Bit LLM의 시대", section "Absmean 양자화 함수").
+Two paths are covered:
+- bitlinear_quant_act_ex at any M;
+- bitlinear_forward_fused_ex at M = 1, the one-token kernel with the
+  transform in its prologue, for every pattern and lanes-per-row
+  configuration.
+
+The bar against the CPU oracle:
+- codes, row sums and int32 accumulators are bit-exact;
+- Y is within 1e-5 relative;
+- x_scale is within one binary32 ulp.  Only the order of the binary64 sum of
+  squares differs between the two sides.  With K non-negative exact terms its
+  relative error is at most K * 2^-53, so it can move the final binary32
+  rounding of x_scale by one ulp at most.
+
+Inputs are seeded: N(0,1) activations with 1% outliers x20, and an N(0,1)
+up operand.  The RMSNorm weight is uniform in [0.25, 1.75]."""
+import numpy as np
+import pytest
+
+from ternary_weight_linear_act_amd import workloads
+
+from gpu_helpers import check_y, hip_pack, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TRANSFORMS = {"gate": (True, False), "norm": (False, True), "gate_norm": (True, True)}
+NM_CASES = [(0, 0), (2, 4), (6, 8)]
+
+
+def inputs(seed, M, K, gated, normed, tiny_rows=()):
+    rng = np.random.default_rng(seed)
+    X = workloads.activations(rng, M, K, 0.01)
+    up = workloads.activations(rng, M, K) if gated else None
+    gamma = rng.uniform(0.25, 1.75, K).astype(np.float32) if normed else None
+    for r, scale in tiny_rows:
+        X[r] *= np.float32(scale)
+    return X, up, gamma
+
+
+def assert_scale_within_ulp(xs_g, xs_o):
+    a, b = xs_g.view(np.int32).astype(np.int64), xs_o.view(np.int32).astype(np.int64)
+    assert np.all(np.abs(a - b) <= 1), "x_scale differs by more than one ulp: %s vs %s" % (
+        xs_g[np.abs(a - b) > 1][:4], xs_o[np.abs(a - b) > 1][:4])
+
+
+def hip_quant_ex(X, up, gamma, eps):
+    import ternary_weight_linear_act_amd as bl
+    return bl.quant_act_ex(to_dev(X), None if up is None else to_dev(up), None if gamma is None else to_dev(gamma),
+                           eps)
+
+
+@pytest.mark.parametrize("tr", sorted(TRANSFORMS))
+@pytest.mark.parametrize("M,K", [(1, 64), (1, 6912), (5, 2560), (37, 1088), (64, 11008)])
+def test_quant_act_ex(tr, M, K):
+    import torch
+
+    import oracle
+    import ternary_weight_linear_act_amd as bl
+    gated, normed = TRANSFORMS[tr]
+    tiny = [(M - 1, 2.0 ** -110)] if M > 2 else []
+    X, up, gamma = inputs(900 + M + K, M, K, gated, normed, tiny)
+    for eps in (1e-5, 0.5):
+        print("case quant_act_ex %s M=%d K=%d eps=%g" % (tr, M, K, eps), flush=True)
+        q, xs, rs = hip_quant_ex(X, up, gamma, eps)
+        name = bl.last_dispatch()
+        torch.cuda.synchronize()
+        q_o, xs_o, rs_o = oracle.quant_act_ex(X, up, gamma, eps)
+        assert name == "quant_act_" + tr
+        assert np.array_equal(q.cpu().numpy(), q_o)
+        assert np.array_equal(rs.cpu().numpy(), rs_o)
+        assert_scale_within_ulp(xs.cpu().numpy(), xs_o)
+
+
+def test_quant_act_ex_zero_and_negative_gate_rows():
+    import torch
+
+    import oracle
+    K = 512
+    X, up, gamma = inputs(950, 4, K, True, True)
+    X[0] = 0.0
+    X[1] = -np.abs(X[1])            # the gate is never positive: h = 0
+    for eps in (0.0, 1e-5):
+        q, xs, rs = hip_quant_ex(X, up, gamma, eps)
+        torch.cuda.synchronize()
+        q_o, xs_o, rs_o = oracle.quant_act_ex(X, up, gamma, eps)
+        assert np.array_equal(q.cpu().numpy(), q_o) and np.array_equal(rs.cpu().numpy(), rs_o)
+        assert_scale_within_ulp(xs.cpu().numpy(), xs_o)
+        assert not q_o[:2].any() and not xs_o[:2].any()
+
+
+def test_quant_act_ex_no_transform_is_quant_act():
+    import torch
+
+    import ternary_weight_linear_act_amd as bl
+    X, _, _ = inputs(951, 9, 1024, False, False)
+    a = bl.quant_act(to_dev(X))
+    b = bl.quant_act_ex(to_dev(X))
+    torch.cuda.synchronize()
+    assert all(torch.equal(u, v) for u, v in zip(a, b))
+
+
+def fused_ex_vs_oracle(Ws, X, up, gamma, eps, nm):
+    import torch
+
+    import oracle
+    import ternary_weight_linear_act_amd as bl
+    packs = [hip_pack(W, nm) for W in Ws]
+    xs = torch.empty(1, dtype=torch.float32, device="cuda")
+    Ys, accs = bl.forward_fused_ex(to_dev(X), [(pk, ws, W.shape[0]) for (pk, ws), W in zip(packs, Ws)],
+                                   up=None if up is None else to_dev(up),
+                                   gamma=None if gamma is None else to_dev(gamma), eps=eps, nm=nm,
+                                   want_acc=True, x_scale=xs)
+    name = bl.last_dispatch()
+    torch.cuda.synchronize()
+    q, xs_o, _ = oracle.quant_act_ex(X, up, gamma, eps)
+    assert_scale_within_ulp(xs.cpu().numpy(), xs_o)
+    for W, Y, acc in zip(Ws, Ys, accs):
+        beta, w_eff, _ = oracle.quantize_weights(W, *nm)
+        acc_o, Y_o = oracle.forward(q, xs_o, w_eff, beta)
+        assert np.array_equal(acc.cpu().numpy(), acc_o)
+        check_y(Y.cpu().numpy(), Y_o, acc_o)
+    return name
+
+
+def expected_config(K):
+    """(lanes per row, chunks per lane) the host picks for the fused form."""
+    C, lpr = K // 64, 8
+    while lpr < 64 and -(-C // lpr) > 7:
+        lpr *= 2
+    return lpr, -(-C // lpr)
+
+
+@pytest.mark.parametrize("tr", sorted(TRANSFORMS))
+@pytest.mark.parametrize("nm", NM_CASES)
+@pytest.mark.parametrize("K", [64, 2560, 3648, 6912, 14400, 16384])
+def test_fused_ex_m1(K, nm, tr):
+    gated, normed = TRANSFORMS[tr]
+    Ns = (70, 33) if K > 4096 else (130, 257)
+    Ws = [workloads.small_case(960 + K + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+    X, up, gamma = inputs(970 + K, 1, K, gated, normed)
+    print("case fused_ex %s K=%d nm=%s" % (tr, K, nm), flush=True)
+    name = fused_ex_vs_oracle(Ws, X, up, gamma, 1e-5, nm)
+    assert name.startswith("fused_decode_dot4_") and name.endswith("_p2_" + tr), name
+    assert ("_lpr%d_u%d_" % expected_config(K)) in name, name
+
+
+@pytest.mark.parametrize("tr", sorted(TRANSFORMS))
+def test_fused_ex_m1_eight_waves(tr):
+    # more than 320 four-wave workgroups at 8 lanes per row: 8 waves, 64 rows
+    gated, normed = TRANSFORMS[tr]
+    K, Ns = 2560, (6912, 6912)
+    Ws = [workloads.small_case(980 + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+    X, up, gamma = inputs(981, 1, K, gated, normed)
+    print("case fused_ex 8 waves %s" % tr, flush=True)
+    name = fused_ex_vs_oracle(Ws, X, up, gamma, 1e-6, (0, 0))
+    assert name.endswith("_w8_" + tr), name
+
+
+@pytest.mark.parametrize("tr", sorted(TRANSFORMS))
+def test_fused_ex_matches_two_call_path(tr):
+    # codes, row sums and accumulators equal the quant_act_ex + forward path's
+    import torch
+
+    import ternary_weight_linear_act_amd as bl
+    gated, normed = TRANSFORMS[tr]
+    K, N = 6912, 2560
+    W, _ = workloads.small_case(990, 1, N, K)
+    X, up, gamma = inputs(991, 1, K, gated, normed)
+    pk, ws = hip_pack(W, (0, 0))
+    d = lambda a: None if a is None else to_dev(a)
+    Xq, xs, rs = bl.quant_act_ex(to_dev(X), d(up), d(gamma), 1e-5)
+    Y2, acc2 = bl.forward(Xq, xs, rs, pk, ws, N, want_acc=True)
+    xs_f = torch.empty(1, dtype=torch.float32, device="cuda")
+    Ys, accs = bl.forward_fused_ex(to_dev(X), [(pk, ws, N)], up=d(up), gamma=d(gamma), eps=1e-5, want_acc=True,
+                                   x_scale=xs_f)
+    torch.cuda.synchronize()
+    assert torch.equal(accs[0], acc2)
+    assert_scale_within_ulp(xs_f.cpu().numpy(), xs.cpu().numpy())
+
+
+def test_ffn_decode_chain():
+    # a 2B-class feed-forward block at one token: RMSNorm -> gate, up (one
+    # launch); ReLU^2(gate) * up -> subln RMSNorm -> down (one launch).  Each
+    # stage is checked against the oracle on the stage's own fp32 inputs.
+    import torch
+
+    import oracle
+    import ternary_weight_linear_act_amd as bl
+    D, F = 2560, 6912
+    rng = np.random.default_rng(995)
+    Wg, Wu, Wd = (workloads.normal_f32(rng, (n, k), workloads.WEIGHT_SIGMA) for n, k in ((F, D), (F, D), (D, F)))
+    x = workloads.activations(rng, 1, D, 0.001)
+    g_in = rng.uniform(0.5, 1.5, D).astype(np.float32)
+    g_sub = rng.uniform(0.5, 1.5, F).astype(np.float32)
+    pg, pu, pd = (hip_pack(W, (0, 0)) for W in (Wg, Wu, Wd))
+    gate, up = bl.forward_fused_ex(to_dev(x), [(pg[0], pg[1], F), (pu[0], pu[1], F)], gamma=to_dev(g_in), eps=1e-5)
+    (y,) = bl.forward_fused_ex(gate, [(pd[0], pd[1], D)], up=up, gamma=to_dev(g_sub), eps=1e-5)
+    torch.cuda.synchronize()
+    q1, xs1, _ = oracle.quant_act_ex(x, None, g_in, 1e-5)
+    for W, out in ((Wg, gate), (Wu, up)):
+        beta, w_eff, _ = oracle.quantize_weights(W)
+        acc_o, Y_o = oracle.forward(q1, xs1, w_eff, beta)
+        check_y(out.cpu().numpy(), Y_o, acc_o)
+    g_h, u_h = gate.cpu().numpy(), up.cpu().numpy()
+    q2, xs2, _ = oracle.quant_act_ex(g_h, u_h, g_sub, 1e-5)
+    beta, w_eff, _ = oracle.quantize_weights(Wd)
+    acc_o, Y_o = oracle.forward(q2, xs2, w_eff, beta)
+    check_y(y.cpu().numpy(), Y_o, acc_o)
