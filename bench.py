@@ -161,6 +161,65 @@ def bench_configs(torch, bl, workloads, dev, log):
     return res
 
 
+def bench_ffn_block(torch, bl, dev, log, x_pool, shapes, packed, wsc, P):
+    """The feed-forward block of the decode step with the steps either side of
+    the linears fused in: RMSNorm -> gate, up (one launch), then ReLU^2(gate) *
+    up -> subln RMSNorm -> down (one launch), against the same on the two-call
+    path (quant_act_ex, then forward per projection: five launches).  Same
+    weight pool as the decode step; RMSNorm weights uniform in [0.5, 1.5]."""
+    import numpy as np
+    (F, D), eps = shapes["gate"], 1e-5
+    rng = np.random.default_rng(7)
+    g_in = torch.from_numpy(rng.uniform(0.5, 1.5, D).astype(np.float32)).to(dev)
+    g_sub = torch.from_numpy(rng.uniform(0.5, 1.5, F).astype(np.float32)).to(dev)
+    G = torch.empty((1, F), dtype=torch.float32, device=dev)
+    U = torch.empty_like(G)
+    Yd = torch.empty((1, D), dtype=torch.float32, device=dev)
+    names = []
+
+    def fused(j):
+        bl.forward_fused_ex(x_pool[j], [(packed["gate"][j], wsc["gate"], F), (packed["up"][j], wsc["up"], F)],
+                            gamma=g_in, eps=eps, Ys=[G, U])
+        names.append(bl.last_dispatch())
+        bl.forward_fused_ex(G, [(packed["down"][j], wsc["down"], D)], up=U, gamma=g_sub, eps=eps, Ys=[Yd])
+        names.append(bl.last_dispatch())
+
+    Xq1, Xq2 = torch.empty((1, D), dtype=torch.int8, device=dev), torch.empty((1, F), dtype=torch.int8, device=dev)
+    xs = [torch.empty(1, dtype=torch.float32, device=dev) for _ in range(2)]
+    rs = [torch.empty(1, dtype=torch.int32, device=dev) for _ in range(2)]
+    G2, U2, Y2 = torch.empty_like(G), torch.empty_like(U), torch.empty_like(Yd)
+
+    def two_call(j):
+        bl.quant_act_ex(x_pool[j], gamma=g_in, eps=eps, Xq=Xq1, x_scale=xs[0], x_rowsum=rs[0])
+        bl.forward(Xq1, xs[0], rs[0], packed["gate"][j], wsc["gate"], F, Y=G2)
+        bl.forward(Xq1, xs[0], rs[0], packed["up"][j], wsc["up"], F, Y=U2)
+        bl.quant_act_ex(G2, up=U2, gamma=g_sub, eps=eps, Xq=Xq2, x_scale=xs[1], x_rowsum=rs[1])
+        bl.forward(Xq2, xs[1], rs[1], packed["down"][j], wsc["down"], D, Y=Y2)
+
+    fused(0)
+    two_call(0)
+    torch.cuda.synchronize()
+    kernels = names[:2]
+    # the two paths agree up to the one-ulp latitude of the norm's scale (the
+    # down stage compared on the same inputs: the fused path's gate and up)
+    bl.quant_act_ex(G, up=U, gamma=g_sub, eps=eps, Xq=Xq2, x_scale=xs[1], x_rowsum=rs[1])
+    bl.forward(Xq2, xs[1], rs[1], packed["down"][0], wsc["down"], D, Y=Y2)
+    for a, b in ((G, G2), (U, U2), (Yd, Y2)):
+        if not torch.allclose(a, b, rtol=2e-6, atol=0.0):
+            raise SystemExit("ffn block: fused and two-call outputs differ")
+    ms_f, _ = timed_graph(torch, lambda: [fused(j % P) for j in range(P)], reps=3)
+    ms_t, _ = timed_graph(torch, lambda: [two_call(j % P) for j in range(P)], reps=2)
+    fus, two = ms_f * 1e3 / P, ms_t * 1e3 / P
+    wbytes = sum(shapes[n][0] * shapes[n][1] // 4 for n in ("gate", "up", "down"))
+    # weights; x and gamma_in read; gate and up written, then read with gamma_sub; y written
+    abytes = wbytes + 4 * D * 2 + 4 * F * 2 + 4 * F * 3 + 4 * D
+    log("ffn block (norm + gate/up, ReLU^2 + norm + down) fused %.2f us, two-call %.2f us" % (fus, two))
+    return {"workload": "decode_ffn_2b with RMSNorm before gate/up, ReLU^2(gate)*up and subln RMSNorm before "
+                        "down, M=1, weights rotating over %d buffers" % P,
+            "fused_us": round(fus, 3), "fused_GB/s": round(abytes / (fus * 1e-6) / 1e9, 1), "fused_launches": 2,
+            "kernels": kernels, "two_call_us": round(two, 3), "two_call_launches": 5}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -311,6 +370,8 @@ def main():
         single["%dx%d" % (K, N)] = {"kernel": bl.last_dispatch(), "us": round(ms * 1e3 / P, 3),
                                     "GB/s": round(fb / (ms * 1e-3 / P) / 1e9, 1)}
 
+    ffn_block = bench_ffn_block(torch, bl, dev, log, Xg[groups[0]], shapes, packed, wsc, P)
+
     # ------------------------------------------------------------------ prefill
     dp = workloads.draw("prefill_2048")
     Wp = torch.from_numpy(dp.W["up"]).to(dev)
@@ -400,6 +461,7 @@ def main():
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
                               "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4)},
                  "quant_act_us": round(quant_p_us, 2)},
+        "ffn_block_decode": ffn_block,
         "cpu_baseline": cpu,
         "other_workloads": configs,
         "source_digest": digest,

@@ -374,11 +374,34 @@ __device__ __forceinline__ float act_norm_scale(float g, double rinv)
     return g == 0.0f ? 0.0f : (float)((double)g / 127.0 * rinv);
 }
 
+// Whole-wave binary64 sum on the same DPP lane moves as the reductions above
+// (each half of the double moved on its own).  The association differs from
+// lane to lane, but the four row results read out are fixed by the lane
+// values, so the sum is deterministic and wave-uniform.
+template <int CTRL>
+__device__ __forceinline__ double dpp_move_f64(double v)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)dpp_move<CTRL>((int)(uint32_t)b);
+    const uint32_t hi = (uint32_t)dpp_move<CTRL>((int)(uint32_t)(b >> 32));
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 __device__ __forceinline__ double wave_sum_f64(double v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_move_f64<kDppQuadXor1>(v);
+    v += dpp_move_f64<kDppQuadXor2>(v);
+    v += dpp_move_f64<kDppRowRor4>(v);
+    v += dpp_move_f64<kDppRowRor8>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 }  // namespace bl

@@ -15,8 +15,10 @@ thread_local char g_name[64];
 // The fused kernel reads and quantises the whole fp32 row in every
 // workgroup, so it prefers fewer, fuller workgroups: at 8 lanes per row it
 // takes 8 waves (64 rows) per workgroup where 4 waves would need more than
-// 320 workgroups (gate+up of a 2B FFN: 432 -> 216, 4.1 -> 4.0 us).  Returns
-// hipErrorNotSupported when M != 1 or K is too large.
+// 320 workgroups (gate+up of a 2B FFN: 432 -> 216, 4.1 -> 4.0 us), except
+// with a row transform, where 4 waves measured faster (RMSNorm on gate+up
+// 5.35 -> 5.13 us).  Returns hipErrorNotSupported when M != 1 or K is too
+// large.
 hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
                               int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
                               const ActTransform &tr, hipStream_t stream, const char **name)
@@ -33,7 +35,8 @@ hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs,
         for (int i = 0; i < args.nproj; ++i) b += (args.N[i] + rb - 1) / rb;
         return b;
     };
-    const bool w8 = fused && lpr == 8 && count_blocks(4 * 8) > 320;
+    const int trb = (tr.up ? kTrGate : 0) | (tr.gamma ? kTrNorm : 0);
+    const bool w8 = fused && lpr == 8 && count_blocks(4 * 8) > 320 && trb == 0;
     const int64_t rb = (w8 ? 8 : 4) * (64 / lpr);
     int64_t blocks = 0;
     for (int i = 0; i < args.nproj; ++i) {
@@ -42,7 +45,6 @@ hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs,
     }
     for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
     if (blocks > (1LL << 30)) return hipErrorNotSupported;
-    const int trb = (tr.up ? kTrGate : 0) | (tr.gamma ? kTrNorm : 0);
     if (trb && !fused) return hipErrorNotSupported;
     Fn f = nullptr;
     if (trb) f = pick_dot4_tr(p, trb, w8, lpr, u);

@@ -131,10 +131,11 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
         for (int i = tid; i < nm_sel_entries(P); i += kThreads) nm_sel_entry<P>(i, &s_sel[2 * i], &s_sel[2 * i + 1]);
 
     // 3. the int8 activations into LDS, with their scale and row sum
+    double ss = 0.0;                   // the norm's sum of squares, then its block total
+    float xg = 0.0f;                   // max|v| of the normalised row
     if constexpr (FUSED) {
         // the transformed row (common.hpp): h = ReLU(x)^2 * up, then the codes
         // are taken from h * gamma and the norm's sum of squares from h
-        double ss = 0.0;
         if constexpr (TR != 0) {
 #pragma unroll
             for (int t = 0; t < XR; ++t) {
@@ -198,14 +199,17 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
 #pragma unroll
         for (int i = 1; i < W; ++i) rs += s_sum[i];
         if constexpr (NORM) {
+            // the binary64 division chain of the scale waits until after the
+            // dot products (only the epilogue reads it)
             double t = s_ss[0];
 #pragma unroll
             for (int i = 1; i < W; ++i) t += s_ss[i];
-            xsc = act_norm_scale(g, act_rinv(t, K, tr.eps));
+            ss = t;
+            xg = g;
         } else {
             xsc = (g == 0.0f) ? 0.0f : g / 127.0f;
+            if (x_scale_out && blockIdx.x == 0 && tid == 0) x_scale_out[0] = xsc;
         }
-        if (x_scale_out && blockIdx.x == 0 && tid == 0) x_scale_out[0] = xsc;
     } else {
 #pragma unroll
         for (int t = 0; t < XR; ++t) {
@@ -271,6 +275,10 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
         acc = (a4[0] + a4[1] + a4[2] + a4[3]) >> 6;
     }
     acc = lanes_sum<LPR>(acc);
+    if constexpr (NORM) {
+        xsc = act_norm_scale(xg, act_rinv(ss, K, tr.eps));
+        if (x_scale_out && blockIdx.x == 0 && tid == 0) x_scale_out[0] = xsc;
+    }
     if (j == 0 && row < N) {
         // dense codes are t + 1: subtract the activation row sum
         const int av = (P == Pattern::Dense) ? acc - rs : acc;

@@ -7,13 +7,15 @@
 namespace bl {
 namespace {
 
+// (the host rule never takes 8 waves with a transform)
 template <int TR>
 Dot4Fn pick_tr(Pattern p, bool w8, int lpr, int u)
 {
+    if (w8) return nullptr;
     switch (p) {
-    case Pattern::Dense: return w8 ? pick_w8<Pattern::Dense, TR>(u) : pick<Pattern::Dense, true, TR>(lpr, u);
-    case Pattern::NM24: return w8 ? pick_w8<Pattern::NM24, TR>(u) : pick<Pattern::NM24, true, TR>(lpr, u);
-    case Pattern::NM68: return w8 ? pick_w8<Pattern::NM68, TR>(u) : pick<Pattern::NM68, true, TR>(lpr, u);
+    case Pattern::Dense: return pick<Pattern::Dense, true, TR>(lpr, u);
+    case Pattern::NM24: return pick<Pattern::NM24, true, TR>(lpr, u);
+    case Pattern::NM68: return pick<Pattern::NM68, true, TR>(lpr, u);
     }
     return nullptr;
 }
