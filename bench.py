@@ -393,6 +393,23 @@ def main():
     gemm_tops = 2.0 * Mp * Np_ * Kp / (gemm_us * 1e-6) / 1e12
     ms_qp, _ = timed_graph(torch, lambda: [bl.quant_act(Xp, Xq_p, xs_p, rs_p) for _ in range(G)], reps=2)
     quant_p_us = ms_qp * 1e3 / G
+    # the same prefill with 2:4 weights (sparse MFMA), checked against the
+    # oracle on sampled rows first
+    pk_s, ws_s = bl.pack_weights(Wp, nm=(2, 4))
+    Y_s = torch.empty_like(Y_p)
+    acc_s = torch.empty((Mp, Np_), dtype=torch.int32, device=dev)
+    bl.forward(Xq_p, xs_p, rs_p, pk_s, ws_s, Np_, nm=(2, 4), Y=Y_s, acc=acc_s)
+    torch.cuda.synchronize()
+    gemm24_dispatch = bl.last_dispatch()
+    rows = np.array([0, 1, 777, 1500, Mp - 1])
+    beta24, w_eff24, _ = oracle.quantize_weights(dp.W["up"], 2, 4)
+    q_p, xs_po, _ = oracle.quant_act(dp.X[("up", 2048)][rows])
+    acc_o, _ = oracle.forward(q_p, xs_po, w_eff24, beta24)
+    if not np.array_equal(acc_s.cpu().numpy()[rows], acc_o):
+        raise SystemExit("2:4 prefill accumulators do not match the oracle")
+    ms_g24, _ = timed_graph(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_s, ws_s, Np_, nm=(2, 4), Y=Y_s)
+                                            for _ in range(G)], reps=5, warm=5)
+    gemm24_us = ms_g24 * 1e3 / G
 
     # ------------------------------------------------------------------ traffic
     traffic = None
@@ -460,7 +477,10 @@ def main():
                  "avg_launch_us": round(gemm_us, 2), "TOPS": round(gemm_tops, 1),
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
                               "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4)},
-                 "quant_act_us": round(quant_p_us, 2)},
+                 "quant_act_us": round(quant_p_us, 2),
+                 "nm24": {"kernel": gemm24_dispatch, "avg_launch_us": round(gemm24_us, 2),
+                          "TOPS_dense_equivalent": round(2.0 * Mp * Np_ * Kp / (gemm24_us * 1e-6) / 1e12, 1),
+                          "vs_dense": round(gemm_us / gemm24_us, 3)}},
         "ffn_block_decode": ffn_block,
         "cpu_baseline": cpu,
         "other_workloads": configs,
@@ -470,6 +490,7 @@ def main():
         "two-call step %.2f us; GEMM %.1f us (%.1f TOPS, %.1f%% of int8 peak)" % (
             ms_step * 1e3, value_gbs, fused_us, fused_gbs, 100 * fused_gbs / HBM_PEAK_GBS,
             two_call_us, gemm_us, gemm_tops, 100 * gemm_tops / INT8_PEAK_TOPS))
+    log("2:4 prefill GEMM %.1f us (%s)" % (gemm24_us, gemm24_dispatch))
     print(json.dumps(out), flush=True)
 
 

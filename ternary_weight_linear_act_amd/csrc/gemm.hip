@@ -36,6 +36,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "dma.hpp"
 #include "kernels.hpp"
 
 namespace bl {
@@ -49,7 +50,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr int BK = 64;
 constexpr int LDA = BK + 16;      // bytes per staged activation row
 constexpr int LDB = 24;           // bytes per staged packed weight row (16 used)
-constexpr int kXcds = 8;
 constexpr int kCus = 256;                  // MI355X compute units
 constexpr int64_t kTBytesMaxK = 1 << 18;   // N:M t-byte GEMM: 64 * 127 * K < 2^31
 
@@ -404,28 +404,6 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 // and the fragments a wave read from the stage being overwritten were
 // consumed before it reached the barrier.
 // ---------------------------------------------------------------------------
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glob_void_t;
-
-__device__ __forceinline__ void dma16(const void *gsrc, uint8_t *ldst)
-{
-    __builtin_amdgcn_global_load_lds((glob_void_t *)gsrc, (lds_void_t *)ldst, 16, 0, 0);
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-__device__ __forceinline__ void block_barrier()
-{
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 // SPLIT: the K slices are divided among `splits` workgroups per output tile
 // (blockIdx.x = split * tile workgroups + tile workgroup); each writes its
 // int32 partial tile to the workspace `ws` (element e of thread t at e * T + t)
@@ -434,20 +412,6 @@ __device__ __forceinline__ void block_barrier()
 // applies the dequant scale.  Used when there are too few output tiles to fill
 // the chip (few tokens).  The kernel boundary makes the partials visible: no
 // fence or counter is needed.
-// Tile placement over the 8 XCDs (each has its own L2): when the tile grid
-// splits evenly into 4 x 2 regions, one region per XCD; otherwise tiles are
-// dealt round-robin with consecutive logical tiles on one XCD.
-__host__ __device__ inline bool xcd_regions(int64_t tiles_m, int64_t tiles_n)
-{
-    return tiles_m % 4 == 0 && tiles_n >= 2;
-}
-
-__host__ __device__ inline int64_t xcd_grid(int64_t tiles_m, int64_t tiles_n)
-{
-    if (xcd_regions(tiles_m, tiles_n)) return kXcds * (tiles_m / 4) * ((tiles_n + 1) / 2);
-    return (tiles_m * tiles_n + kXcds - 1) / kXcds * kXcds;
-}
-
 template <int BM, int BN, int WM, int WN, int S, bool SPLIT, int OCC = 1>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
@@ -786,6 +750,13 @@ hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, const ui
     return hipGetLastError();
 }
 
+}  // namespace
+
+hipError_t launch_gemm_nm24_sparse(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
+                                   int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream);
+
+namespace {
+
 template <Pattern P>
 hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                     const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
@@ -837,6 +808,16 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
         return launch_few_tokens<64, 64, 2, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
                                                "gemm_dense_splitk_64x64", "gemm_dense_dma_64x64");
     } else {
+        if constexpr (P == Pattern::NM24) {
+            // 2:4 on the sparse matrix cores (gemm_sparse.hip) where K allows
+            // and the 256 x 256 tiles fill half the chip (2048 x 6912 x 2560:
+            // 42-47 us against 72; 1000 x 8000 x 2560: 58 against 62; at 512
+            // tokens the t-byte kernel's 128 x 128 tiles are faster, 25 against 28)
+            if (M >= 256 && tiles(256, 256) >= 128 && K % 128 == 0) {
+                *name = "gemm_nm24_smfmac_256x256";
+                return launch_gemm_nm24_sparse(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream);
+            }
+        }
         if (M >= 256 && tiles(256, 256) >= 128) {
             *name = names[tb][pi][0];
             return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);

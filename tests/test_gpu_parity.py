@@ -82,10 +82,12 @@ def test_gemm_tile_thresholds(M, nm):
     full_check(W, X, nm, rows=sample_rows(M, 24, seed=M), label="gemm-threshold")
 
 
-@pytest.mark.parametrize("M,N,K,tile", [(1024, 8200, 320, "256x256"), (300, 1000, 1536, "128x128"),
+@pytest.mark.parametrize("M,N,K,tile", [(1024, 8200, 320, "256x256"), (300, 1000, 1472, "128x128"),
                                         (40, 517, 704, "64x128")])
 @pytest.mark.parametrize("nm", [(2, 4), (6, 8)])
 def test_nm_gemm_tbytes(M, N, K, tile, nm):
+    # (2:4 with K % 128 == 0 and enough 256 x 256 tiles runs on the sparse
+    # matrix cores instead: these K leave 64 over)
     # N:M prefill: kept codes spread over their positions as 64 * t bytes by
     # byte permutes, read straight into the MFMA operand (K <= 2^18)
     import ternary_weight_linear_act_amd as bl
@@ -93,6 +95,37 @@ def test_nm_gemm_tbytes(M, N, K, tile, nm):
     full_check(W, X, nm, rows=sample_rows(M, 16, seed=M), label="nm-gemm")
     name = bl.last_dispatch()
     assert name == "gemm_nm%d%d_%s_tbytes" % (nm[0], nm[1], tile), name
+
+
+@pytest.mark.parametrize("M,N,K", [(2048, 6912, 2560), (1000, 8000, 128), (777, 9999, 256), (1025, 8000, 1536),
+                                   (512, 16385, 384), (1000, 8000, 640)])
+def test_nm24_sparse_mfma_gemm(M, N, K):
+    # 2:4 prefill on the sparse matrix cores (K % 128 == 0, at least 128
+    # tiles of 256 x 256): ragged token and weight tiles, one and two K slices
+    # (fewer than the pipeline's stages), N not a multiple of 4, the prefill
+    # shape
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(1400 + M + K, M, N, K, outlier_frac=0.001)
+    full_check(W, X, (2, 4), rows=sample_rows(M, 16, seed=K), label="nm24-smfmac")
+    assert bl.last_dispatch() == "gemm_nm24_smfmac_256x256", bl.last_dispatch()
+
+
+@pytest.mark.parametrize("M,N,K", [(1024, 8192, 256), (2048, 6912, 2560)])
+def test_nm24_sparse_mfma_vector_epilogue(M, N, K):
+    # full tiles, N % 4 == 0 and no accumulator output: the 16-byte store path,
+    # bit-identical to the element-wise one taken when acc is requested
+    import torch
+
+    import ternary_weight_linear_act_amd as bl
+    from gpu_helpers import hip_pack, hip_quant
+    W, X = workloads.small_case(1500 + M, M, N, K)
+    pk, ws = hip_pack(W, (2, 4))
+    Xq, xs, rs = hip_quant(X)
+    Y1 = bl.forward(Xq, xs, rs, pk, ws, N, (2, 4))
+    Y2, _ = bl.forward(Xq, xs, rs, pk, ws, N, (2, 4), want_acc=True)
+    torch.cuda.synchronize()
+    assert bl.last_dispatch() == "gemm_nm24_smfmac_256x256"
+    assert torch.equal(Y1, Y2)
 
 
 @pytest.mark.parametrize("nm", [(2, 4), (6, 8)])
