@@ -19,6 +19,8 @@ from .oracle import (  # noqa: F401
     quantize_weights,
     quant_act,
     quant_act_ex,
+    hadamard_rows,
+    quant_act_h4,
     forward,
     build,
     LIB_PATH,

@@ -26,6 +26,9 @@
  *          Semi-Structured Sparsity" (manon006 review), sec. 3.2: the N:M mask
  *          keeps the N largest |master weight| per block of M, applied after
  *          ternarisation (quant-then-mask).
+ *  [V2]    The BitNet v2 summary (brain.hanbit.co.kr): the H-BitLinear applies
+ *          an online Hadamard transform to the activations, then quantises
+ *          them to 4 bits.
  *
  * Readings where the pages are silent or disagree (each one is listed in the
  * design notes of the repository):
@@ -40,7 +43,10 @@
  *  - the gated feed-forward input is ReLU(gate)^2 * up, in binary32;
  *  - RMSNorm: eps inside the square root, mean over the K inputs, sum of
  *    squares in binary64; its 1/rms factor is applied to the scale, not to
- *    the row before the codes are taken (it divides out of the codes).
+ *    the row before the codes are taken (it divides out of the codes);
+ *  - H-BitLinear: a block-diagonal Sylvester Hadamard transform (blocks of a
+ *    power of two B dividing K) in the radix-2 butterfly order, 4-bit absmax
+ *    codes 7/max|v| stored in int8, 1/sqrt(B) applied to the scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -331,6 +337,84 @@ int oracle_quant_act_ex(const float *X, const float *up, const float *gamma, flo
                 if (fabsf(v[k]) > g) g = fabsf(v[k]);
             x_scale[r] = (g == 0.0f) ? 0.0f : (float)((double)g / 127.0 * rinv);
         }
+    }
+    free(v);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 6c: 4-bit activations after an online Hadamard transform            */
+/* ("BitNet v2" summary (brain.hanbit.co.kr), the H-BitLinear: the          */
+/* activations entering a projection are Hadamard-transformed online, then  */
+/* quantised to 4 bits, then the linear runs).                              */
+/*                                                                          */
+/* The transform is block-diagonal: blocks of B consecutive inputs (B a    */
+/* power of two dividing K), each multiplied by the Sylvester Hadamard      */
+/* matrix H_B (entries +-1) and by 1/sqrt(B), which makes it orthonormal.   */
+/* H_B x is formed with the radix-2 butterflies in the standard order: for  */
+/* h = 1, 2, 4, ..., B/2, every pair (i, i + h) with i & h == 0 becomes     */
+/* (a + b, a - b) in binary32.  Each output of a stage depends on two       */
+/* inputs only, so this fixes every rounding.                               */
+/* Then 4-bit absmax: g = max|v|, s = fl32(7 / g) (same tiny-row rule as    */
+/* step 6), q = clamp(rne(fl32(v * s)), -8, 7).  The factor 1/sqrt(B) is    */
+/* positive and common to the row, so it divides out of the codes; it goes  */
+/* into the scale: x_scale = fl32( (double)g / 7 / sqrt(B) ).  The codes    */
+/* are stored one per int8.                                                 */
+/* ------------------------------------------------------------------------ */
+int oracle_hadamard_rows(float *X, int64_t M, int64_t K, int64_t B)
+{
+    if (!X || M < 0 || K < 1 || B < 1 || (B & (B - 1)) || K % B) return OR_EINVAL;
+    for (int64_t r = 0; r < M; ++r)
+        for (int64_t b0 = 0; b0 < K; b0 += B) {
+            float *v = X + r * K + b0;
+            for (int64_t h = 1; h < B; h *= 2)
+                for (int64_t i = 0; i < B; ++i) {
+                    if (i & h) continue;
+                    float a = v[i], c = v[i + h];
+                    v[i] = a + c;
+                    v[i + h] = a - c;
+                }
+        }
+    return OR_OK;
+}
+
+int oracle_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B,
+                        int8_t *q, float *x_scale, int32_t *rowsum)
+{
+    if (!X || !q || !x_scale || M < 0 || K < 1 || B < 1 || (B & (B - 1)) || K % B) return OR_EINVAL;
+    float *v = (float *)malloc((size_t)K * sizeof(float));
+    if (!v) return OR_EINVAL;
+    int rc = OR_OK;
+    for (int64_t r = 0; r < M && rc == OR_OK; ++r) {
+        for (int64_t k = 0; k < K; ++k) {
+            if (!isfinite(X[r * K + k])) { rc = OR_ENONFINITE; break; }
+            v[k] = X[r * K + k];
+        }
+        if (rc != OR_OK) break;
+        oracle_hadamard_rows(v, 1, K, B);
+        float g = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            if (!isfinite(v[k])) { rc = OR_ENONFINITE; break; }
+            if (fabsf(v[k]) > g) g = fabsf(v[k]);
+        }
+        if (rc != OR_OK) break;
+        int32_t sum = 0;
+        if (g == 0.0f) {
+            for (int64_t k = 0; k < K; ++k) q[r * K + k] = 0;
+            x_scale[r] = 0.0f;
+        } else {
+            const float up = (g < 0x1p-100f) ? 0x1p100f : 1.0f;
+            float s = 7.0f / (g * up);
+            for (int64_t k = 0; k < K; ++k) {
+                float c = rintf((v[k] * up) * s);
+                if (c > 7.0f) c = 7.0f;
+                if (c < -8.0f) c = -8.0f;
+                q[r * K + k] = (int8_t)c;
+                sum += (int32_t)c;
+            }
+            x_scale[r] = (float)((double)g / 7.0 / sqrt((double)B));
+        }
+        if (rowsum) rowsum[r] = sum;
     }
     free(v);
     return rc;

@@ -61,10 +61,12 @@ def _L():
         lib.oracle_pack_nm.argtypes = [vp, vp, i64, i64, i32, i32, vp]
         lib.oracle_quant_act.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         lib.oracle_quant_act_ex.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp]
+        lib.oracle_hadamard_rows.argtypes = [vp, i64, i64, i64]
+        lib.oracle_quant_act_h4.argtypes = [vp, i64, i64, i64, vp, vp, vp]
         lib.oracle_forward.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp]
         for f in ("oracle_absmean", "oracle_ternarize", "oracle_nm_keep", "oracle_apply_mask",
                   "oracle_pack_dense", "oracle_pack_nm", "oracle_quant_act", "oracle_quant_act_ex",
-                  "oracle_forward"):
+                  "oracle_hadamard_rows", "oracle_quant_act_h4", "oracle_forward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -181,6 +183,27 @@ def quant_act_ex(X: np.ndarray, up=None, gamma=None, eps: float = 0.0):
     _check(_L().oracle_quant_act_ex(_p(X), _p(up) if up is not None else null,
                                     _p(gamma) if gamma is not None else null, float(eps), M, K,
                                     _p(q), _p(xs), _p(rs)), "quant_act_ex")
+    return q, xs, rs
+
+
+def hadamard_rows(X: np.ndarray, B: int) -> np.ndarray:
+    """H_B (Sylvester, entries +-1, unnormalised) applied to each block of B
+    inputs of each row, with binary32 butterflies in the fixed order."""
+    V = np.array(X, dtype=np.float32, copy=True, order="C")
+    M, K = V.shape
+    _check(_L().oracle_hadamard_rows(_p(V), M, K, int(B)), "hadamard_rows")
+    return V
+
+
+def quant_act_h4(X: np.ndarray, B: int):
+    """4-bit absmax codes (int8 storage) of the block-Hadamard-transformed rows;
+    returns (q int8, x_scale fp32 incl. 1/sqrt(B), rowsum int32)."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    M, K = X.shape
+    q = np.empty((M, K), np.int8)
+    xs = np.empty(M, np.float32)
+    rs = np.empty(M, np.int32)
+    _check(_L().oracle_quant_act_h4(_p(X), M, K, int(B), _p(q), _p(xs), _p(rs)), "quant_act_h4")
     return q, xs, rs
 
 

@@ -50,6 +50,13 @@ MUTANTS = {
                                "x_scale[r] = (g == 0.0f) ? 0.0f : (float)((double)g / 127.0);"),
     "rms_after_gamma": ("for (int64_t k = 0; k < K; ++k) ss += (double)v[k] * (double)v[k];",
                         "for (int64_t k = 0; k < K; ++k) ss += (double)v[k] * (double)v[k] * (double)gamma[k] * (double)gamma[k];"),
+    "had_butterfly_sign": ("v[i] = a + c;\n                    v[i + h] = a - c;",
+                           "v[i] = a - c;\n                    v[i + h] = a + c;"),
+    "had_skip_first_stage": ("for (int64_t h = 1; h < B; h *= 2)", "for (int64_t h = 2; h < B; h *= 2)"),
+    "h4_const_8": ("float s = 7.0f / (g * up);", "float s = 8.0f / (g * up);"),
+    "h4_scale_unnormalised": ("x_scale[r] = (float)((double)g / 7.0 / sqrt((double)B));",
+                              "x_scale[r] = (float)((double)g / 7.0);"),
+    "h4_trunc": ("float c = rintf((v[k] * up) * s);", "float c = truncf((v[k] * up) * s);"),
     "epilogue_no_beta": ("Y[m * N + n] = (double)s * (double)beta * (double)x_scale[m];",
                          "Y[m * N + n] = (double)s * (double)x_scale[m];"),
 }

@@ -510,6 +510,88 @@ class TestActTransform:
 
 
 # ==========================================================================
+# 4-bit activations after an online Hadamard transform (the BitNet v2
+# summary: the H-BitLinear transforms the activations, then quantises them to
+# 4 bits)
+# ==========================================================================
+def block_hadamard_f64(X, B):
+    """(H_B / sqrt(B)) applied blockwise, in binary64, from scipy's matrix."""
+    import scipy.linalg
+    H = scipy.linalg.hadamard(B).astype(np.float64) / math.sqrt(B)
+    M, K = X.shape
+    return (X.astype(np.float64).reshape(M, K // B, B) @ H.T).reshape(M, K)
+
+
+class TestHadamard4:
+    @pytest.mark.parametrize("B", [1, 2, 8, 256])
+    def test_transform_equals_sylvester_matrix(self, B):
+        # small integers: every butterfly is exact, so the result must equal
+        # scipy's Hadamard matrix times each block exactly
+        import scipy.linalg
+        rng = np.random.default_rng(40 + B)
+        K = 4 * B if B > 1 else 8
+        X = rng.integers(-50, 50, (3, K)).astype(np.float32)
+        H = scipy.linalg.hadamard(B)
+        want = (X.reshape(3, K // B, B) @ H.T).reshape(3, K)
+        assert np.array_equal(oracle.hadamard_rows(X, B), want.astype(np.float32))
+
+    def test_involution_and_blocks(self):
+        rng = np.random.default_rng(41)
+        X = rng.integers(-9, 9, (2, 512)).astype(np.float32)
+        # H H = B I (exact on small integers)
+        assert np.array_equal(oracle.hadamard_rows(oracle.hadamard_rows(X, 128), 128), X * 128)
+        # a change in one block leaves the others' transform alone
+        Y = X.copy()
+        Y[:, 130] += 5
+        d = oracle.hadamard_rows(Y, 128) != oracle.hadamard_rows(X, 128)
+        assert d[:, 128:256].all() and not d[:, :128].any() and not d[:, 256:].any()
+
+    @pytest.mark.parametrize("B", [64, 256])
+    def test_one_hot_rows(self, B):
+        # e_j -> column j of H_B: every code +-7 with H's signs; scale 1/(7 sqrt(B))
+        import scipy.linalg
+        H = scipy.linalg.hadamard(B)
+        X = np.zeros((3, B), np.float32)
+        for r, j in enumerate((0, 5, B - 1)):
+            X[r, j] = 2.5
+        q, xs, rs = oracle.quant_act_h4(X, B)
+        for r, j in enumerate((0, 5, B - 1)):
+            assert np.array_equal(q[r], 7 * H[:, j])
+        assert np.all(xs == F32(2.5 / 7.0 / math.sqrt(B)))
+        assert np.array_equal(rs, q.astype(np.int64).sum(1))
+
+    @pytest.mark.parametrize("K,B", [(2560, 512), (6912, 256), (1024, 1024), (192, 64)])
+    def test_matches_orthonormal_transform(self, K, B):
+        # against the binary64 product with scipy's matrix: the largest value
+        # maps to 7 and every dequantised value is within half a step, up to the
+        # binary32 butterflies' error (log2(B) roundings of partial sums bounded
+        # by the block's sum of |x|)
+        rng = np.random.default_rng(42 + K)
+        X = workloads.activations(rng, 12, K, 0.01)
+        X[5] *= F32(2.0 ** -110)                          # tiny row (prescaled)
+        q, xs, rs = oracle.quant_act_h4(X, B)
+        ref = block_hadamard_f64(X, B)
+        l1 = np.abs(X.astype(np.float64)).reshape(12, K // B, B).sum(2)
+        fp_err = (math.log2(B) + 1) * 2.0 ** -24 * np.repeat(l1, B, axis=1) / math.sqrt(B)
+        xs64 = xs.astype(np.float64)[:, None]
+        assert np.all(np.abs(q * xs64 - ref) <= xs64 * (0.5 + 1e-5) + fp_err)
+        gmax = np.abs(ref).max(1)
+        assert np.all(np.abs(7.0 * xs.astype(np.float64) - gmax) <= 1e-6 * gmax + fp_err.max(1))
+        assert q.min() >= -7 and q.max() <= 7
+        assert np.array_equal(rs, q.astype(np.int64).sum(1))
+
+    def test_power_of_two_invariance_and_zero_rows(self):
+        X = workloads.activations(np.random.default_rng(43), 6, 512)
+        X[2] = 0.0
+        q0, xs0, _ = oracle.quant_act_h4(X, 256)
+        assert not q0[2].any() and xs0[2] == 0.0
+        for e in (-7, 3):
+            q1, xs1, _ = oracle.quant_act_h4((X * F32(2.0 ** e)).astype(np.float32), 256)
+            assert np.array_equal(q0, q1)
+            assert np.array_equal(xs1, (xs0 * F32(2.0 ** e)).astype(np.float32))
+
+
+# ==========================================================================
 # contraction and epilogue
 # ==========================================================================
 class TestForward:
