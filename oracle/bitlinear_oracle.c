@@ -403,10 +403,10 @@ int oracle_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B,
             for (int64_t k = 0; k < K; ++k) q[r * K + k] = 0;
             x_scale[r] = 0.0f;
         } else {
-            const float up = (g < 0x1p-100f) ? 0x1p100f : 1.0f;
-            float s = 7.0f / (g * up);
+            const float pre = (g < 0x1p-100f) ? 0x1p100f : 1.0f;
+            float s = 7.0f / (g * pre);
             for (int64_t k = 0; k < K; ++k) {
-                float c = rintf((v[k] * up) * s);
+                float c = rintf((v[k] * pre) * s);
                 if (c > 7.0f) c = 7.0f;
                 if (c < -8.0f) c = -8.0f;
                 q[r * K + k] = (int8_t)c;

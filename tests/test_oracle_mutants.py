@@ -53,10 +53,11 @@ MUTANTS = {
     "had_butterfly_sign": ("v[i] = a + c;\n                    v[i + h] = a - c;",
                            "v[i] = a - c;\n                    v[i + h] = a + c;"),
     "had_skip_first_stage": ("for (int64_t h = 1; h < B; h *= 2)", "for (int64_t h = 2; h < B; h *= 2)"),
-    "h4_const_8": ("float s = 7.0f / (g * up);", "float s = 8.0f / (g * up);"),
+    "h4_const_8": ("float s = 7.0f / (g * pre);", "float s = 8.0f / (g * pre);"),
+    "h4_no_tiny_row_scaling": ("const float pre = (g < 0x1p-100f) ? 0x1p100f : 1.0f;", "const float pre = 1.0f;"),
     "h4_scale_unnormalised": ("x_scale[r] = (float)((double)g / 7.0 / sqrt((double)B));",
                               "x_scale[r] = (float)((double)g / 7.0);"),
-    "h4_trunc": ("float c = rintf((v[k] * up) * s);", "float c = truncf((v[k] * up) * s);"),
+    "h4_trunc": ("float c = rintf((v[k] * pre) * s);", "float c = truncf((v[k] * pre) * s);"),
     "epilogue_no_beta": ("Y[m * N + n] = (double)s * (double)beta * (double)x_scale[m];",
                          "Y[m * N + n] = (double)s * (double)x_scale[m];"),
 }

@@ -580,6 +580,18 @@ class TestHadamard4:
         assert q.min() >= -7 and q.max() <= 7
         assert np.array_equal(rs, q.astype(np.int64).sum(1))
 
+    def test_tiny_row_hand_example(self):
+        # a one-hot row of 2^-126: every transformed value is +-2^-126, where
+        # fl32(7 / g) would overflow (7 * 2^126 > FLT_MAX) -- the row is taken
+        # at 2^100 times its size and the codes are 7 times H's column
+        import scipy.linalg
+        B = 64
+        X = np.zeros((1, B), np.float32)
+        X[0, 9] = np.float32(2.0 ** -126)
+        q, xs, _ = oracle.quant_act_h4(X, B)
+        assert np.array_equal(q[0], 7 * scipy.linalg.hadamard(B)[:, 9])
+        assert xs[0] == np.float32(2.0 ** -126 / 7.0 / 8.0)
+
     def test_power_of_two_invariance_and_zero_rows(self):
         X = workloads.activations(np.random.default_rng(43), 6, 512)
         X[2] = 0.0
