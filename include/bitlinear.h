@@ -211,6 +211,26 @@ bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_
                                             int64_t K, bitlinear_nm nm, const bitlinear_proj *projs,
                                             int32_t nproj, float *x_scale, hipStream_t stream);
 
+/* H-BitLinear activation quantisation (the BitNet v2 summary
+ * (brain.hanbit.co.kr): the activations entering a projection are
+ * Hadamard-transformed online, then quantised to 4 bits).  Each row of X
+ * (M x K fp32) is split into blocks of `block` inputs (a power of two,
+ * 1 <= block <= 8192, dividing K); each block is multiplied by the Sylvester
+ * Hadamard matrix H_block (entries +-1) with radix-2 butterflies, stage
+ * h = 1, 2, 4, ..., block/2 mapping every pair (i, i + h), i & h == 0, to
+ * (a + b, a - b) in binary32.  Then, with v the transformed row:
+ *   g_m = max_k |v|;  u_m as above;  s_m = fl32(7 / fl32(g_m * u_m))
+ *   Xq[m,k] = rne(fl32(fl32(v * u_m) * s_m))   in [-7, 7], one per int8
+ *   x_scale[m] = fl32((double)g_m / 7 / sqrt(block))   (0 for a zero row)
+ *   x_rowsum[m] = sum_k Xq[m,k]
+ * The transform with its 1/sqrt(block) is orthonormal; that positive factor
+ * divides out of the codes and is applied through x_scale.  The outputs feed
+ * bitlinear_forward unchanged; the weights must be in the transformed basis
+ * (the H-BitLinear's are).  All outputs are bit-exact with a plain CPU
+ * evaluation of these formulas.  x_rowsum may be NULL. */
+bitlinear_status bitlinear_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t block, int8_t *Xq,
+                                        float *x_scale, int32_t *x_rowsum, hipStream_t stream);
+
 /* Thread-local text for the last non-OK status returned on this thread. */
 const char *bitlinear_last_error(void);
 

@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     pack_weights,
     quant_act,
     quant_act_ex,
+    quant_act_h4,
     forward,
     forward_fused,
     forward_fused_ex,

@@ -74,11 +74,12 @@ def load_library():
     lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp]
     lib.bitlinear_forward_fused.argtypes = [vp, i64, i64, NM, ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     lib.bitlinear_quant_act_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, vp, vp, vp, vp]
+    lib.bitlinear_quant_act_h4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
     lib.bitlinear_forward_fused_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, NM,
                                                ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     for f in ("bitlinear_packed_size", "bitlinear_pack_weights", "bitlinear_quant_act",
               "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_quant_act_ex",
-              "bitlinear_forward_fused_ex"):
+              "bitlinear_forward_fused_ex", "bitlinear_quant_act_h4"):
         getattr(lib, f).restype = ctypes.c_int
     lib.bitlinear_last_error.restype = ctypes.c_char_p
     lib.bitlinear_last_dispatch.restype = ctypes.c_char_p
@@ -216,6 +217,27 @@ def quant_act_ex(X, up=None, gamma=None, eps=None, Xq=None, x_scale=None, x_rows
     _check("bitlinear_quant_act_ex", load_library().bitlinear_quant_act_ex(
         _ptr(X), None if tr is None else ctypes.byref(tr), M, K, _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum),
         _stream(stream)))
+    return Xq, x_scale, x_rowsum
+
+
+def quant_act_h4(X, block, Xq=None, x_scale=None, x_rowsum=None, stream=None):
+    """H-BitLinear activations: block Hadamard transform of each row (block a
+    power of two dividing K), then 4-bit absmax codes stored one per int8.
+    Returns (Xq, x_scale, x_rowsum) for forward()."""
+    import torch
+    _require(X, torch.float32, None, "X")
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(M, dtype=torch.float32, device=X.device)
+    if x_rowsum is None:
+        x_rowsum = torch.empty(M, dtype=torch.int32, device=X.device)
+    _require(Xq, torch.int8, (M, K), "Xq")
+    _require(x_scale, torch.float32, (M,), "x_scale")
+    _require(x_rowsum, torch.int32, (M,), "x_rowsum")
+    _check("bitlinear_quant_act_h4", load_library().bitlinear_quant_act_h4(
+        _ptr(X), M, K, int(block), _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _stream(stream)))
     return Xq, x_scale, x_rowsum
 
 

@@ -232,6 +232,25 @@ bitlinear_status bitlinear_quant_act_ex(const float *X, const bitlinear_act_tran
     return BITLINEAR_OK;
 }
 
+bitlinear_status bitlinear_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t block, int8_t *Xq,
+                                        float *x_scale, int32_t *x_rowsum, hipStream_t stream)
+{
+    CHECK(check_m(M));
+    CHECK(check_k(K));
+    if (block < 1 || block > 8192 || (block & (block - 1)) || K % block)
+        return fail(BITLINEAR_EINVAL, "block = %lld must be a power of two in [1, 8192] dividing K = %lld",
+                    (long long)block, (long long)K);
+    if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }   // M-sized buffers may be NULL
+    CHECK(check_ptr(X, 16, "X"));
+    CHECK(check_ptr(Xq, 16, "Xq"));
+    CHECK(check_ptr(x_scale, 4, "x_scale"));
+    if (x_rowsum && !aligned(x_rowsum, 4)) return fail(BITLINEAR_EINVAL, "x_rowsum must be 4-byte aligned");
+    hipError_t e = bl::launch_quant_act_h4(X, M, K, block, Xq, x_scale, x_rowsum, stream);
+    if (e != hipSuccess) return hip_fail("quant_act_h4 launch", e);
+    set_dispatch("quant_act_h4");
+    return BITLINEAR_OK;
+}
+
 bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                                    const void *packed, const float *w_scale, bitlinear_nm nm, int64_t M,
                                    int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)

@@ -111,7 +111,120 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 4-bit activations after an online Hadamard transform (the BitNet v2
+// summary: the H-BitLinear transforms the activations, then quantises them to
+// 4 bits).  Blocks of B inputs (a power of two dividing K, B <= kHChunk) are
+// multiplied by the Sylvester Hadamard matrix with radix-2 butterflies, stage
+// h = 1, 2, 4, ..., B/2 turning every pair (i, i + h), i & h == 0, into
+// (a + b, a - b) in binary32: each value depends on its two inputs only, so
+// any schedule of a stage gives the same bits.  The stages h < 8 run in
+// registers on 8 consecutive values per thread, the rest in LDS.  The
+// codes are the 4-bit absmax ones, 7 / max|v| (the factor 1/sqrt(B) of the
+// orthonormal transform divides out of them and goes into the scale),
+// stored one per int8.  Rows longer than one LDS chunk are transformed twice
+// (once for the maximum, once to quantise): no scratch memory is needed.
+// ---------------------------------------------------------------------------
+constexpr int kHChunk = 8192;             // floats of a row transformed at a time
+
+__device__ void hadamard_chunk(const float *__restrict__ x, int len, int64_t B, float *s_v)
+{
+    const int tid = threadIdx.x;
+    for (int gi = tid; gi < len / 8; gi += kQuantBlock) {
+        const f32x4 lo = reinterpret_cast<const f32x4 *>(x)[2 * gi], hi = reinterpret_cast<const f32x4 *>(x)[2 * gi + 1];
+        float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+        for (int h = 1; h < 8; h *= 2) {
+            if (h >= B) break;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (!(i & h)) {
+                    const float a = v[i], b = v[i + h];
+                    v[i] = a + b;
+                    v[i + h] = a - b;
+                }
+        }
+        reinterpret_cast<f32x4 *>(s_v)[2 * gi] = f32x4{v[0], v[1], v[2], v[3]};
+        reinterpret_cast<f32x4 *>(s_v)[2 * gi + 1] = f32x4{v[4], v[5], v[6], v[7]};
+    }
+    __syncthreads();
+    for (int64_t h = 8; h < B; h *= 2) {
+        for (int p = tid; p < len / 2; p += kQuantBlock) {
+            const int i = ((p & ~(int)(h - 1)) << 1) | (p & (int)(h - 1));
+            const float a = s_v[i], b = s_v[i + h];
+            s_v[i] = a + b;
+            s_v[i + h] = a - b;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kQuantBlock) void quant_act_h4_kernel(
+    const float *__restrict__ X, int64_t K, int64_t B, int8_t *__restrict__ Xq, float *__restrict__ x_scale,
+    int32_t *__restrict__ x_rowsum)
+{
+    __shared__ __attribute__((aligned(16))) float s_v[kHChunk];
+    __shared__ float s_max[kWaves];
+    __shared__ int s_sum[kWaves];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const float *x = X + row * K;
+    const int64_t chunk = (int64_t)kHChunk / B * B;
+    const bool one = K <= chunk;
+
+    float g = 0.0f;
+    for (int64_t c0 = 0; c0 < K; c0 += chunk) {
+        const int len = (int)min(chunk, K - c0);
+        hadamard_chunk(x + c0, len, B, s_v);
+        for (int i = tid; i < len; i += kQuantBlock) g = fmaxf(g, fabsf(s_v[i]));
+        if (!one) __syncthreads();
+    }
+    g = wave_max_dpp(g);
+    if (lane == 0) s_max[wave] = g;
+    __syncthreads();
+    g = s_max[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) g = fmaxf(g, s_max[w]);
+
+    const float up = act_prescale(g);
+    const float s = (g == 0.0f) ? 0.0f : 7.0f / (g * up);
+    int sum = 0;
+    int *q4 = reinterpret_cast<int *>(Xq + row * K);
+    for (int64_t c0 = 0; c0 < K; c0 += chunk) {
+        const int len = (int)min(chunk, K - c0);
+        if (!one) hadamard_chunk(x + c0, len, B, s_v);
+        for (int i = tid; i < len / 4; i += kQuantBlock) {
+            f32x4 v = reinterpret_cast<const f32x4 *>(s_v)[i];
+            if (up != 1.0f) v *= up;              // row-uniform, rare
+            int s4;
+            q4[c0 / 4 + i] = (int)act_quant4(v[0], v[1], v[2], v[3], s, &s4);
+            sum += s4;
+        }
+        if (!one) __syncthreads();
+    }
+    sum = wave_sum_dpp(sum);
+    if (lane == 0) s_sum[wave] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) total += s_sum[w];
+        x_scale[row] = (g == 0.0f) ? 0.0f : (float)((double)g / 7.0 / sqrt((double)B));
+        if (x_rowsum) x_rowsum[row] = total;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B, int8_t *Xq, float *x_scale,
+                               int32_t *x_rowsum, hipStream_t stream)
+{
+    if (M == 0) return hipSuccess;
+    if (B < 1 || B > kHChunk || (B & (B - 1)) || K % B || K % 8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(quant_act_h4_kernel, dim3((unsigned)M), dim3(kQuantBlock), 0, stream, X, K, B, Xq, x_scale,
+                       x_rowsum);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
                             int32_t *x_rowsum, hipStream_t stream)

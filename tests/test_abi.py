@@ -24,14 +24,15 @@ def lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(bitlinear_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(bitlinear_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
     names = declared_functions()
     for want in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward",
                  "bitlinear_packed_size", "bitlinear_last_error", "bitlinear_last_dispatch",
-                 "bitlinear_forward_fused", "bitlinear_quant_act_ex", "bitlinear_forward_fused_ex"):
+                 "bitlinear_forward_fused", "bitlinear_quant_act_ex", "bitlinear_forward_fused_ex",
+                 "bitlinear_quant_act_h4"):
         assert want in names
 
 
@@ -149,6 +150,16 @@ def test_transform_validation(lib):
     assert f(P(), ctypes.byref(ok), 1, 16448, NM(0, 0), arr, 1, None, None) == -2        # ... and K <= 16384
     assert f(P(), ctypes.byref(ActTransform(None, A, -2.0)), 1, 128, NM(0, 0), arr, 1, None, None) == -1
     assert f(None, ctypes.byref(ok), 0, 128, NM(0, 0), arr, 1, None, None) == 0
+
+
+def test_h4_validation(lib):
+    q = lib.bitlinear_quant_act_h4
+    assert q(P(), 2, 256, 3, P(), P(), P(), None) == -1          # block not a power of two
+    assert q(P(), 2, 256, 512, P(), P(), P(), None) == -1        # block does not divide K
+    assert q(P(), 2, 16384, 16384, P(), P(), P(), None) == -1    # block > 8192
+    assert q(P(), 2, 256, 0, P(), P(), P(), None) == -1
+    assert q(P(4), 2, 256, 64, P(), P(), P(), None) == -1        # misaligned X
+    assert q(None, 0, 256, 64, None, None, None, None) == 0      # M = 0
 
 
 def test_pack_validation(lib):
