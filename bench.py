@@ -220,6 +220,45 @@ def bench_ffn_block(torch, bl, dev, log, x_pool, shapes, packed, wsc, P):
             "kernels": kernels, "two_call_us": round(two, 3), "two_call_launches": 5}
 
 
+def bench_h4(torch, bl, dev, log):
+    """The H-BitLinear path on the down projection of the 2B-class FFN
+    (6912 -> 2560, Hadamard blocks of 256): bitlinear_quant_act_h4, then
+    bitlinear_forward, at one token (weights rotating through >= 512 MB) and
+    at 2048 tokens, beside the 8-bit two-call path on the same shapes."""
+    import numpy as np
+    N, K, B = 2560, 6912, 256
+    rng = np.random.default_rng(11)
+    from ternary_weight_linear_act_amd import workloads
+    W = workloads.normal_f32(rng, (N, K), workloads.WEIGHT_SIGMA)
+    pk, ws = bl.pack_weights(torch.from_numpy(W).to(dev))
+    res = {}
+    for M in (1, 2048):
+        X = torch.from_numpy(workloads.activations(rng, M, K, 0.001)).to(dev)
+        P = max(2, -(-POOL_BYTES // pk.numel())) if M == 1 else 1
+        pool = [pk] + [pk.clone() for _ in range(P - 1)]
+        Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        xs = torch.empty(M, dtype=torch.float32, device=dev)
+        rs = torch.empty(M, dtype=torch.int32, device=dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        G = P if M == 1 else 10
+        t = {}
+        for name, quant in (("h4", lambda: bl.quant_act_h4(X, B, Xq, xs, rs)),
+                            ("int8", lambda: bl.quant_act(X, Xq, xs, rs))):
+            quant()
+            fw = lambda j: bl.forward(Xq, xs, rs, pool[j % P], ws, N, Y=Y)
+            fw(0)
+            torch.cuda.synchronize()
+            ms_q, _ = timed_graph(torch, lambda: [quant() for _ in range(G)], reps=2)
+            ms_f, _ = timed_graph(torch, lambda: [fw(j) for j in range(G)], reps=2)
+            ms_s, _ = timed_graph(torch, lambda: [(quant(), fw(j)) for j in range(G)], reps=2)
+            t[name] = {"quant_us": round(ms_q * 1e3 / G, 3), "forward_us": round(ms_f * 1e3 / G, 3),
+                       "step_us": round(ms_s * 1e3 / G, 3)}
+        res["down_6912x2560_M%d" % M] = t
+        log("h-bitlinear down M=%d: h4 step %.2f us (quant %.2f), int8 step %.2f us" % (
+            M, t["h4"]["step_us"], t["h4"]["quant_us"], t["int8"]["step_us"]))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -371,6 +410,7 @@ def main():
                                     "GB/s": round(fb / (ms * 1e-3 / P) / 1e9, 1)}
 
     ffn_block = bench_ffn_block(torch, bl, dev, log, Xg[groups[0]], shapes, packed, wsc, P)
+    h4 = bench_h4(torch, bl, dev, log)
 
     # ------------------------------------------------------------------ prefill
     dp = workloads.draw("prefill_2048")
@@ -482,6 +522,7 @@ def main():
                           "TOPS_dense_equivalent": round(2.0 * Mp * Np_ * Kp / (gemm24_us * 1e-6) / 1e12, 1),
                           "vs_dense": round(gemm_us / gemm24_us, 3)}},
         "ffn_block_decode": ffn_block,
+        "h_bitlinear": h4,
         "cpu_baseline": cpu,
         "other_workloads": configs,
         "source_digest": digest,
