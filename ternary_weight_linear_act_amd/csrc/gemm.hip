@@ -775,15 +775,22 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
     if constexpr (P == Pattern::Dense) {
         if (M > 64) {
             // pipelined kernel; tile size by a cost model measured on MI355X
-            // over M = 100 .. 2048: one round of 256 x 256 tiles over the 256
-            // compute units costs about 4, one round of 128 x 128 tiles about
-            // 1.35 (smaller tiles: more operand traffic per MFMA), so 256 x 256
-            // wins only where 128 x 128 would take three or more rounds (e.g.
-            // 2048 x 6912: 4 vs 5.4; 1000 x 8000: 4 vs 2.7)
+            // over M = 256 .. 3072: one round of tiles over the 256 compute
+            // units costs about 4 for 256 x 256, 2 for 128 x 256 (8 waves of
+            // 64 x 64) and 1.35 for 128 x 128 (smaller tiles: more operand
+            // traffic per MFMA).  E.g. 1000 x 8000 x 2560: 4 / 2 / 2.7, measured
+            // 40 / 27 / 32 us; 3072 x 6912: 8 / 6 / 8.1, measured 75 / 64 / 78
+            // us; 2048 x 6912: 4 / 4 / 5.4 (a tie, measured 43-44 us both).
             auto rounds = [&](int64_t t) { return (double)((t + kCus - 1) / kCus); };
-            if (4.0 * rounds(tiles(256, 256)) <= 1.35 * rounds(tiles(128, 128))) {
+            const double c256 = 4.0 * rounds(tiles(256, 256)), c12 = 2.0 * rounds(tiles(128, 256));
+            const double c128 = 1.35 * rounds(tiles(128, 128));
+            if (c256 <= c12 && c256 <= c128) {
                 *name = "gemm_dense_dma_256x256_w8_s4";
                 return launch_dma<256, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+            }
+            if (c12 <= c128) {
+                *name = "gemm_dense_dma_128x256_w8_s4";
+                return launch_dma<128, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
             }
             *name = "gemm_dense_dma_128x128_w4_s4";
             return launch_dma<128, 128, 2, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
