@@ -753,7 +753,8 @@ hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, const ui
 }  // namespace
 
 hipError_t launch_gemm_nm24_sparse(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
-                                   int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream);
+                                   int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream,
+                                   int tile_m);
 
 namespace {
 
@@ -816,13 +817,22 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
                                                "gemm_dense_splitk_64x64", "gemm_dense_dma_64x64");
     } else {
         if constexpr (P == Pattern::NM24) {
-            // 2:4 on the sparse matrix cores (gemm_sparse.hip) where K allows
-            // and the 256 x 256 tiles fill half the chip (2048 x 6912 x 2560:
-            // 42-47 us against 72; 1000 x 8000 x 2560: 58 against 62; at 512
-            // tokens the t-byte kernel's 128 x 128 tiles are faster, 25 against 28)
-            if (M >= 256 && tiles(256, 256) >= 128 && K % 128 == 0) {
-                *name = "gemm_nm24_smfmac_256x256";
-                return launch_gemm_nm24_sparse(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream);
+            // 2:4 on the sparse matrix cores (gemm_sparse.hip) where K allows;
+            // token tile by rounds over the compute units as for the dense
+            // kernel: one round costs about 4 at 256 tokens and 2 at 128
+            // (1000 x 8000 x 2560: 4 / 2, measured 56 / 34 us; 2048 x 6912 x
+            // 2560: 4 / 4, measured 40 / 46 us, ties take 256).  At 256 tokens
+            // and more this beats the t-byte GEMM everywhere measured (512 x
+            // 2560 x 6912: 41 against 75 us; 256 x 8960 x 1536: 15.7 against
+            // 18.9 us).
+            if (M >= 128 && K % 128 == 0) {
+                auto rounds = [&](int64_t t) { return (double)((t + kCus - 1) / kCus); };
+                if (4.0 * rounds(tiles(256, 256)) <= 2.0 * rounds(tiles(128, 256))) {
+                    *name = "gemm_nm24_smfmac_256x256";
+                    return launch_gemm_nm24_sparse(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream, 256);
+                }
+                *name = "gemm_nm24_smfmac_128x256";
+                return launch_gemm_nm24_sparse(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream, 128);
             }
         }
         if (M >= 256 && tiles(256, 256) >= 128) {

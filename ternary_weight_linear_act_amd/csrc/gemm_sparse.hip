@@ -31,25 +31,27 @@
 //     an 8-entry table.
 // The values are t in {-1, 0, +1}: no offset-code row sum is subtracted.
 //
-// Tiling: a workgroup owns 256 tokens x 256 weight rows, eight waves (two
-// per SIMD) of 64 tokens x 128 rows (8 fragments, 128 accumulator
-// registers).  K runs in 128-wide slices through a 3-stage LDS ring filled by
-// direct loads: per slice 32 KB of activations (128-byte rows, 16-byte pieces
-// XOR-swizzled by row) and 8 KB of packed weights (values, masks: 16 bytes
-// per row each).  Per slice and wave: 2 k-steps of 8 sparse MFMAs; the first
-// group has the second k-step's activation reads and weight expansions
-// issued between its MFMAs, the second the next slice's reads.
-// K % 128 == 0 (other K take the t-byte GEMM).
+// Tiling: a workgroup owns BM tokens x 256 weight rows (BM = 256 or 128),
+// eight waves (two per SIMD).  K runs in 128-wide slices through an LDS ring
+// of S stages filled by direct loads: per slice BM x 128 bytes of activations
+// (128-byte rows, 16-byte pieces XOR-swizzled by row) and 8 KB of packed
+// weights (values, masks: 16 bytes per row each).  Per slice and wave: 2
+// k-steps of sparse MFMAs; the first group has the second k-step's activation
+// reads and weight expansions issued between its MFMAs, the second the next
+// slice's reads.  K % 128 == 0 (other K take the t-byte GEMM).
 //
-// Measured on 2048 x 6912 x 2560 (2:4): 42-47 us against 72 us for the
-// t-byte GEMM, level with the dense kernel rather than 1.8 times faster.  The
-// matrix cores are busy about a third of the time: per slice a SIMD issues
-// 1024 cycles of sparse MFMA but about 1400 cycles of VALU, most of it the
-// expansion of each weight fragment in each of the four waves that share it
+// The kernel is VALU-bound: per slice a SIMD issues 1024 cycles of sparse
+// MFMA but, with 64-token wave tiles, about 1400 cycles of VALU, most of it
+// the expansion of each weight fragment in every wave that shares it
 // (variants built from a copy of the sources: without the expansion -4.5 us,
-// without the MFMAs at all -10 us).  One wave per SIMD with 128 x 128 tiles
-// halves that VALU but measured slower (47 us): its latencies are no longer
-// hidden by a second wave.
+// without the MFMAs at all -10 us, on 2048 x 6912 x 2560).  A fragment's
+// expansion is reused once per 32 tokens of the wave tile, so the waves take
+// tall tiles: 128 tokens x 64 rows (BM = 256, 2 x 4 waves, S = 3) or 128 x 32
+// (BM = 128, 1 x 8 waves, S = 4).  Measured against 64 x 128 wave tiles:
+// 2048 x 6912 x 2560 43.2 -> 40.0 us, 4096 x 8192 x 4096 119 -> 109 us
+// (dense: 43.5 and 133 us); BM = 128 for tile counts that leave the chip
+// half empty at BM = 256, e.g. 1000 x 8000 x 2560 59.5 -> 33.8 us (dense
+// 28.4) and 2048 x 2560 x 6912 79 -> 46 us (dense 50.8).
 #include "dma.hpp"
 #include "kernels.hpp"
 
@@ -62,10 +64,8 @@ typedef int32_t i32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSBK = 128;                 // K per slice
-constexpr int kBM = 256, kBN = 256;       // tokens x weight rows per workgroup
-constexpr int kSA = kBM * kSBK;           // activation bytes per stage
+constexpr int kBN = 256;                  // weight rows per workgroup
 constexpr int kSV = kBN * 16;             // value bytes per stage (masks the same)
-constexpr int kStage = kSA + 2 * kSV;
 
 // code c -> t byte (c = 0, 1, 2 -> 0xFF, 0x00, 0x01)
 constexpr uint32_t kCodeToT = 0x000100FFu;
@@ -84,14 +84,18 @@ __device__ __forceinline__ void expand24(uint32_t vw, uint32_t mw, i32x4 &a, int
     ix = (int)(lo | (hi << 4));
 }
 
-// WM x WN waves (tokens x weight rows), each owning (256 / WM) x (256 / WN).
-template <int WM, int WN, int S>
+// BM tokens x 256 weight rows per workgroup; WM x WN waves (tokens x weight
+// rows), each owning (BM / WM) x (256 / WN).
+template <int BM, int WM, int WN, int S>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_nm24_sparse_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const uint8_t *__restrict__ packed,
     const float *__restrict__ w_scale, int64_t M, int64_t N, int64_t K, float *__restrict__ Y,
     int32_t *__restrict__ acc_out)
 {
     static_assert(S >= 3, "the pipeline needs S >= 3");
+    constexpr int kBM = BM;
+    constexpr int kSA = kBM * kSBK;                   // activation bytes per stage
+    constexpr int kStage = kSA + 2 * kSV;
     constexpr int NW = WM * WN, T = 64 * NW;
     constexpr int kTM = kBM / WM, kTN = kBN / WN;
     constexpr int kFM = kTM / 32, kFN = kTN / 32;
@@ -286,23 +290,32 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_nm24_sparse_kernel(
     }
 }
 
-}  // namespace
-
-// 2:4 weights, K % 128 == 0; hipErrorNotSupported otherwise.
-hipError_t launch_gemm_nm24_sparse(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
-                                   int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
+template <int BM, int WM, int WN, int S>
+hipError_t launch_sparse(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale, int64_t M,
+                         int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
 {
-    constexpr int WM = 4, WN = 2, S = 3;
-    if (K % kSBK != 0 || M < 1) return hipErrorNotSupported;
-    const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+    const int64_t tiles_m = (M + BM - 1) / BM, tiles_n = (N + kBN - 1) / kBN;
     const int64_t grid = xcd_grid(tiles_m, tiles_n);
-    const size_t lds = (size_t)S * kStage + 4 * kBM;
-    auto kern = gemm_nm24_sparse_kernel<WM, WN, S>;
+    const size_t lds = (size_t)S * (BM * kSBK + 2 * kSV) + 4 * BM;
+    auto kern = gemm_nm24_sparse_kernel<BM, WM, WN, S>;
     const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WM * WN), lds, stream, Xq, xs, packed, w_scale, M, N, K,
                        Y, acc);
     return hipGetLastError();
+}
+
+}  // namespace
+
+// 2:4 weights, K % 128 == 0; hipErrorNotSupported otherwise.  tile_m: 256
+// or 128 tokens per workgroup.
+hipError_t launch_gemm_nm24_sparse(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
+                                   int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream,
+                                   int tile_m)
+{
+    if (K % kSBK != 0 || M < 1) return hipErrorNotSupported;
+    if (tile_m == 128) return launch_sparse<128, 1, 8, 4>(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream);
+    return launch_sparse<256, 2, 4, 3>(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream);
 }
 
 }  // namespace bl

@@ -97,7 +97,7 @@ def test_gemm_tile_thresholds(M, nm):
                                         (40, 517, 704, "64x128")])
 @pytest.mark.parametrize("nm", [(2, 4), (6, 8)])
 def test_nm_gemm_tbytes(M, N, K, tile, nm):
-    # (2:4 with K % 128 == 0 and enough 256 x 256 tiles runs on the sparse
+    # (2:4 with K % 128 == 0 and at least 128 tokens runs on the sparse
     # matrix cores instead: these K leave 64 over)
     # N:M prefill: kept codes spread over their positions as 64 * t bytes by
     # byte permutes, read straight into the MFMA operand (K <= 2^18)
@@ -108,23 +108,41 @@ def test_nm_gemm_tbytes(M, N, K, tile, nm):
     assert name == "gemm_nm%d%d_%s_tbytes" % (nm[0], nm[1], tile), name
 
 
+def nm24_sparse_tile(M, N):
+    """Token tile of the 2:4 sparse-MFMA GEMM: rounds of tiles over the 256
+    compute units cost 4 at 256 tokens, 2 at 128; ties take 256."""
+    rounds = lambda bm: -(-(-(-M // bm) * -(-N // 256)) // 256)
+    return "256x256" if 4 * rounds(256) <= 2 * rounds(128) else "128x256"
+
+
 @pytest.mark.parametrize("M,N,K", [(2048, 6912, 2560), (1000, 8000, 128), (777, 9999, 256), (1025, 8000, 1536),
-                                   (512, 16385, 384), (1000, 8000, 640)])
+                                   (512, 16385, 384), (1000, 8000, 640), (300, 1000, 1536), (130, 777, 256),
+                                   (3072, 6912, 2560), (2048, 2560, 6912)])
 def test_nm24_sparse_mfma_gemm(M, N, K):
-    # 2:4 prefill on the sparse matrix cores (K % 128 == 0, at least 128
-    # tiles of 256 x 256): ragged token and weight tiles, one and two K slices
-    # (fewer than the pipeline's stages), N not a multiple of 4, the prefill
-    # shape
+    # 2:4 prefill on the sparse matrix cores (K % 128 == 0, M >= 128), both
+    # token tiles: ragged token and weight tiles, one and two K slices (fewer
+    # than the pipeline's stages), N not a multiple of 4, prefill shapes
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1400 + M + K, M, N, K, outlier_frac=0.001)
     full_check(W, X, (2, 4), rows=sample_rows(M, 16, seed=K), label="nm24-smfmac")
-    assert bl.last_dispatch() == "gemm_nm24_smfmac_256x256", bl.last_dispatch()
+    assert bl.last_dispatch() == "gemm_nm24_smfmac_" + nm24_sparse_tile(M, N), bl.last_dispatch()
+
+
+@pytest.mark.parametrize("M", [127, 128, 129, 255, 256, 257])
+def test_nm24_sparse_threshold(M):
+    # below 128 tokens 2:4 stays on the t-byte GEMM
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(1450 + M, M, 1000, 512)
+    full_check(W, X, (2, 4), rows=sample_rows(M, 24, seed=M), label="nm24-threshold")
+    want = "gemm_nm24_128x128_tbytes" if M < 128 else "gemm_nm24_smfmac_" + nm24_sparse_tile(M, 1000)
+    assert bl.last_dispatch() == want, bl.last_dispatch()
 
 
 @pytest.mark.parametrize("M,N,K", [(1024, 8192, 256), (2048, 6912, 2560)])
 def test_nm24_sparse_mfma_vector_epilogue(M, N, K):
     # full tiles, N % 4 == 0 and no accumulator output: the 16-byte store path,
-    # bit-identical to the element-wise one taken when acc is requested
+    # bit-identical to the element-wise one taken when acc is requested (both
+    # token tiles: 128 for the first shape, 256 for the second)
     import torch
 
     import ternary_weight_linear_act_amd as bl
@@ -135,7 +153,7 @@ def test_nm24_sparse_mfma_vector_epilogue(M, N, K):
     Y1 = bl.forward(Xq, xs, rs, pk, ws, N, (2, 4))
     Y2, _ = bl.forward(Xq, xs, rs, pk, ws, N, (2, 4), want_acc=True)
     torch.cuda.synchronize()
-    assert bl.last_dispatch() == "gemm_nm24_smfmac_256x256"
+    assert bl.last_dispatch() == "gemm_nm24_smfmac_" + nm24_sparse_tile(M, N)
     assert torch.equal(Y1, Y2)
 
 
