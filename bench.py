@@ -317,8 +317,8 @@ def main():
             bl.forward_fused(Xg[g][j], [(packed[n][j], wsc[n], shapes[n][0]) for n in g],
                              Ys=[Y[n] for n in g])
 
-    # correctness gate before timing: kernel choice and values vs the oracle
-    import oracle
+    # gate before timing: the kernel choice; the values are checked against
+    # the oracle in the CPU leg below (and by the GPU tests)
     group_kernel = {}
     for g in groups:
         bl.forward_fused(Xg[g][0], [(packed[n][0], wsc[n], shapes[n][0]) for n in g], Ys=[Y[n] for n in g])
@@ -328,13 +328,7 @@ def main():
         if not k.startswith("fused_decode"):
             raise SystemExit("unexpected kernel for the M=1 decode step (%s): %s" % (g, k))
     dispatch = ", ".join("%s: %s" % gk for gk in group_kernel.items())
-    for name, (N, K) in shapes.items():
-        beta, w_eff, _ = oracle.quantize_weights(d.W[name])
-        q, xso, _ = oracle.quant_act(d.X[(name, 1)])
-        _, Yo = oracle.forward(q, xso, w_eff, beta)
-        Yg = Y[name].cpu().numpy().astype(np.float64)
-        if not np.all(np.abs(Yg - Yo) <= 1e-5 * np.abs(Yo)):
-            raise SystemExit("decode output of %s does not match the oracle" % name)
+    decode_Y = {name: Y[name].cpu().numpy().astype(np.float64) for name in shapes}
 
     if args.traffic_probe:
         # counters per dispatch: 2 x P eager decode steps over the rotating pool,
@@ -433,23 +427,46 @@ def main():
     gemm_tops = 2.0 * Mp * Np_ * Kp / (gemm_us * 1e-6) / 1e12
     ms_qp, _ = timed_graph(torch, lambda: [bl.quant_act(Xp, Xq_p, xs_p, rs_p) for _ in range(G)], reps=2)
     quant_p_us = ms_qp * 1e3 / G
-    # the same prefill with 2:4 weights (sparse MFMA), checked against the
-    # oracle on sampled rows first
+    # the same prefill with 2:4 weights (sparse MFMA); sampled accumulator rows
+    # of both are kept for the oracle check in the CPU leg
+    rows = np.array([0, 1, 777, 1500, Mp - 1])
+    acc_p = torch.empty((Mp, Np_), dtype=torch.int32, device=dev)
+    bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, Np_, Y=Y_p, acc=acc_p)
     pk_s, ws_s = bl.pack_weights(Wp, nm=(2, 4))
     Y_s = torch.empty_like(Y_p)
     acc_s = torch.empty((Mp, Np_), dtype=torch.int32, device=dev)
     bl.forward(Xq_p, xs_p, rs_p, pk_s, ws_s, Np_, nm=(2, 4), Y=Y_s, acc=acc_s)
     torch.cuda.synchronize()
     gemm24_dispatch = bl.last_dispatch()
-    rows = np.array([0, 1, 777, 1500, Mp - 1])
-    beta24, w_eff24, _ = oracle.quantize_weights(dp.W["up"], 2, 4)
-    q_p, xs_po, _ = oracle.quant_act(dp.X[("up", 2048)][rows])
-    acc_o, _ = oracle.forward(q_p, xs_po, w_eff24, beta24)
-    if not np.array_equal(acc_s.cpu().numpy()[rows], acc_o):
-        raise SystemExit("2:4 prefill accumulators do not match the oracle")
+    prefill_rows = {"dense": acc_p.cpu().numpy()[rows], "2:4": acc_s.cpu().numpy()[rows]}
     ms_g24, _ = timed_graph(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_s, ws_s, Np_, nm=(2, 4), Y=Y_s)
                                             for _ in range(G)], reps=5, warm=5)
     gemm24_us = ms_g24 * 1e3 / G
+    # context: the vendor int8 GEMM (hipBLASLt through torch._int_mm) on the
+    # same codes with the weights unpacked to one int8 per weight, K-major
+    # (its faster layout here); int32 out, no dequant epilogue
+    lib = None
+    try:
+        # the weights as int8, read back through the library itself: codes of
+        # an identity activation block (row k = e_k, row sum 1, scale 1) give
+        # acc[k, n] = W_eff[n, k]
+        eye = torch.eye(Kp, dtype=torch.int8, device=dev)
+        wt = torch.empty((Kp, Np_), dtype=torch.int32, device=dev)
+        bl.forward(eye, torch.ones(Kp, dtype=torch.float32, device=dev),
+                   torch.ones(Kp, dtype=torch.int32, device=dev), pk_p, ws_p, Np_, acc=wt)
+        Bm = wt.t().contiguous().to(torch.int8).t()           # K x N view of an N x K matrix
+        del wt, eye
+        C = torch._int_mm(Xq_p, Bm)
+        torch.cuda.synchronize()
+        if not torch.equal(C, acc_p):
+            raise RuntimeError("library int8 GEMM result differs from the accumulators")
+        ms_lib, _ = timed_graph(torch, lambda: [torch._int_mm(Xq_p, Bm) for _ in range(G)], reps=5, warm=5)
+        lib = {"op": "torch._int_mm (hipBLASLt), int8 x int8 -> int32, weights unpacked to int8, no epilogue",
+               "us": round(ms_lib * 1e3 / G, 2),
+               "TOPS": round(2.0 * Mp * Np_ * Kp / (ms_lib * 1e-3 / G) / 1e12, 1)}
+        del Bm, C
+    except (RuntimeError, AttributeError) as e:
+        lib = {"op": "torch._int_mm", "error": str(e)[:200]}
 
     # ------------------------------------------------------------------ traffic
     traffic = None
@@ -468,6 +485,10 @@ def main():
     # ------------------------------------------------------------------ CPU oracle
     cpu = None
     if not args.no_cpu_baseline:
+        # the oracle, timed on a bounded sample of the decode workload; its
+        # outputs on that sample (and on sampled prefill rows) are compared
+        # with what the GPU produced above
+        import oracle
         pre = {}
         for name in shapes:
             beta, w_eff, _ = oracle.quantize_weights(d.W[name])
@@ -483,6 +504,17 @@ def main():
             if time.perf_counter() - t0 >= args.cpu_seconds:
                 break
         cpu_s = (time.perf_counter() - t0) / n
+        for name in shapes:
+            q, xso, _ = oracle.quant_act(d.X[(name, 1)])
+            _, Yo = oracle.forward(q, xso, pre[name][1], pre[name][0])
+            if not np.all(np.abs(decode_Y[name] - Yo) <= 1e-5 * np.abs(Yo)):
+                raise SystemExit("decode output of %s does not match the oracle" % name)
+        q_p, xs_po, _ = oracle.quant_act(dp.X[("up", 2048)][rows])
+        for kind, (n_, m_) in (("dense", (0, 0)), ("2:4", (2, 4))):
+            beta_p, w_eff_p, _ = oracle.quantize_weights(dp.W["up"], n_, m_)
+            acc_o, _ = oracle.forward(q_p, xs_po, w_eff_p, beta_p)
+            if not np.array_equal(prefill_rows[kind], acc_o):
+                raise SystemExit("%s prefill accumulators do not match the oracle" % kind)
         cpu = {"value": round(step_bytes / cpu_s / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": "%d oracle decode steps (quantisation of the gate/up and down inputs, forward of "
                          "gate, up, down at M=1, the same seeded inputs), %.1f s, single-threaded C on %s" % (
@@ -520,7 +552,8 @@ def main():
                  "quant_act_us": round(quant_p_us, 2),
                  "nm24": {"kernel": gemm24_dispatch, "avg_launch_us": round(gemm24_us, 2),
                           "TOPS_dense_equivalent": round(2.0 * Mp * Np_ * Kp / (gemm24_us * 1e-6) / 1e12, 1),
-                          "vs_dense": round(gemm_us / gemm24_us, 3)}},
+                          "vs_dense": round(gemm_us / gemm24_us, 3)},
+                 "library_int8_gemm": lib},
         "ffn_block_decode": ffn_block,
         "h_bitlinear": h4,
         "cpu_baseline": cpu,

@@ -786,8 +786,11 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
             const double c256 = 4.0 * rounds(tiles(256, 256)), c12 = 2.0 * rounds(tiles(128, 256));
             const double c128 = 1.35 * rounds(tiles(128, 128));
             if (c256 <= c12 && c256 <= c128) {
-                *name = "gemm_dense_dma_256x256_w8_s4";
-                return launch_dma<256, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+                // six stages (120 KB of LDS): 2048 x 6912 x 2560 43.4 -> 42.7
+                // us, 4096 x 8192 x 4096 124 -> 120 us against four; the
+                // smaller tiles measured slower with more than four
+                *name = "gemm_dense_dma_256x256_w8_s6";
+                return launch_dma<256, 256, 2, 4, 6>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
             }
             if (c12 <= c128) {
                 *name = "gemm_dense_dma_128x256_w8_s4";

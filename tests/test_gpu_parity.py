@@ -75,15 +75,17 @@ def test_prefill_pipelined_gemm_edges(M, N, K):
     assert bl.last_dispatch().startswith("gemm_dense_dma"), bl.last_dispatch()
 
 
-@pytest.mark.parametrize("M,N,K,tile", [(700, 9000, 320, "128x256_w8"), (1000, 8000, 2560, "128x256_w8"),
-                                        (256, 8960, 1536, "128x128_w4"), (2048, 6912, 320, "256x256_w8")])
+@pytest.mark.parametrize("M,N,K,tile", [(700, 9000, 320, "128x256_w8_s4"), (1000, 8000, 2560, "128x256_w8_s4"),
+                                        (256, 8960, 1536, "128x128_w4_s4"), (2048, 6912, 320, "256x256_w8_s6"),
+                                        (4096, 4096, 64, "256x256_w8_s6")])
 def test_dense_gemm_tile_choice(M, N, K, tile):
     # the tile-size cost model: 128 x 256 between 128 x 128 and 256 x 256
-    # (ragged M and N in the first case)
+    # (ragged M and N in the first case; the six-stage 256 x 256 kernel with
+    # five K slices and with one)
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1600 + M, M, N, K, outlier_frac=0.001)
     full_check(W, X, rows=sample_rows(M, 16, seed=M), label="gemm-tile-choice")
-    assert bl.last_dispatch() == "gemm_dense_dma_%s_s4" % tile, bl.last_dispatch()
+    assert bl.last_dispatch() == "gemm_dense_dma_" + tile, bl.last_dispatch()
 
 
 @pytest.mark.parametrize("M", [64, 65, 255, 256, 257])
