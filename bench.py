@@ -245,13 +245,15 @@ def bench_h4(torch, bl, dev, log):
         for name, quant in (("h4", lambda: bl.quant_act_h4(X, B, Xq, xs, rs)),
                             ("int8", lambda: bl.quant_act(X, Xq, xs, rs))):
             quant()
+            qkern = bl.last_dispatch()
             fw = lambda j: bl.forward(Xq, xs, rs, pool[j % P], ws, N, Y=Y)
             fw(0)
             torch.cuda.synchronize()
             ms_q, _ = timed_graph(torch, lambda: [quant() for _ in range(G)], reps=2)
             ms_f, _ = timed_graph(torch, lambda: [fw(j) for j in range(G)], reps=2)
             ms_s, _ = timed_graph(torch, lambda: [(quant(), fw(j)) for j in range(G)], reps=2)
-            t[name] = {"quant_us": round(ms_q * 1e3 / G, 3), "forward_us": round(ms_f * 1e3 / G, 3),
+            t[name] = {"quant_kernel": qkern, "quant_us": round(ms_q * 1e3 / G, 3),
+                       "forward_us": round(ms_f * 1e3 / G, 3),
                        "step_us": round(ms_s * 1e3 / G, 3)}
         res["down_6912x2560_M%d" % M] = t
         log("h-bitlinear down M=%d: h4 step %.2f us (quant %.2f), int8 step %.2f us" % (

@@ -245,9 +245,10 @@ bitlinear_status bitlinear_quant_act_h4(const float *X, int64_t M, int64_t K, in
     CHECK(check_ptr(Xq, 16, "Xq"));
     CHECK(check_ptr(x_scale, 4, "x_scale"));
     if (x_rowsum && !aligned(x_rowsum, 4)) return fail(BITLINEAR_EINVAL, "x_rowsum must be 4-byte aligned");
-    hipError_t e = bl::launch_quant_act_h4(X, M, K, block, Xq, x_scale, x_rowsum, stream);
+    const char *name = "";
+    hipError_t e = bl::launch_quant_act_h4(X, M, K, block, Xq, x_scale, x_rowsum, stream, &name);
     if (e != hipSuccess) return hip_fail("quant_act_h4 launch", e);
-    set_dispatch("quant_act_h4");
+    set_dispatch(name);
     return BITLINEAR_OK;
 }
 

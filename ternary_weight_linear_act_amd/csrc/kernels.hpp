@@ -18,7 +18,7 @@ hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64
 // H-BitLinear activations: block Hadamard transform (block B, a power of two
 // <= 8192 dividing K), then 4-bit absmax codes in int8.
 hipError_t launch_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B, int8_t *Xq, float *x_scale,
-                               int32_t *x_rowsum, hipStream_t stream);
+                               int32_t *x_rowsum, hipStream_t stream, const char **name);
 
 // beta: per-row binary64 |W| sums into `rowsum`, then one ordered sum.
 hipError_t launch_absmean(const float *W, int64_t N, int64_t K, double *rowsum, float *w_scale,

@@ -214,13 +214,195 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_h4_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same quantiser with each block held by one wave in registers, for
+// B = 64 V (V = 1 .. 16 values per lane) and rows of at most 16 waves of
+// 16 / V blocks (K / B <= 16 * (16 / V), so K <= 16384).  Lane l
+// holds the V consecutive values l V .. l V + V - 1 of a block: the stages
+// h < V pair values inside the lane, the stages h = V d (d = 1 .. 32) pair
+// lane l with lane l ^ d, the lower element taking a + b and the upper one
+// a - b as in the LDS form -- the same binary32 operations on the same
+// operands.  Wave w of W takes blocks w, w + W, ...: no LDS pass and no
+// barrier between stages, one barrier for the row maximum, and the row is
+// read once.  The exchanges inside rows of 16 lanes are DPP moves; only
+// d = 16 and 32 go through ds_bpermute.
+// ---------------------------------------------------------------------------
+constexpr int kH4Slots = 16;               // register values per lane
+
+// the value of lane l ^ D: DPP moves inside rows of 16 lanes (D = 4: the
+// half-row mirror, i -> i ^ 7, then i -> i ^ 3 in quads; D = 8: the row
+// mirror, i -> i ^ 15, then the half-row mirror), ds_bpermute across rows
+constexpr int kDppQuadXor3 = 0x1B;   // quad_perm [3, 2, 1, 0]
+template <int D>
+__device__ __forceinline__ float lane_xor(float v)
+{
+    const int b = __float_as_int(v);
+    if constexpr (D == 1) return __int_as_float(dpp_move<kDppQuadXor1>(b));
+    if constexpr (D == 2) return __int_as_float(dpp_move<kDppQuadXor2>(b));
+    if constexpr (D == 4) return __int_as_float(dpp_move<kDppQuadXor3>(dpp_move<kDppRowHalfMirror>(b)));
+    if constexpr (D == 8) return __int_as_float(dpp_move<kDppRowHalfMirror>(dpp_move<kDppRowMirror>(b)));
+    return __shfl_xor(v, D);
+}
+
+// stage h = V D of one block: lane l pairs with lane l ^ D
+template <int V, int D>
+__device__ __forceinline__ void lane_stage(float (&v)[V], int lane)
+{
+    const bool upper = (lane & D) != 0;
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+        const float o = lane_xor<D>(v[j]);
+        v[j] = upper ? o - v[j] : v[j] + o;
+    }
+}
+
+template <int V>
+__global__ __launch_bounds__(1024) void quant_act_h4_wave_kernel(
+    const float *__restrict__ X, int64_t K, int8_t *__restrict__ Xq, float *__restrict__ x_scale,
+    int32_t *__restrict__ x_rowsum)
+{
+    constexpr int NB = kH4Slots / V;       // blocks per wave at most
+    constexpr int B = 64 * V;
+    __shared__ float s_max[16];
+    __shared__ int s_sum[16];
+    const int64_t row = blockIdx.x;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int W = blockDim.x >> 6;
+    const int nblk = (int)(K / B);
+    const float *x = X + row * K + lane * V;
+
+    float v[NB][V];
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int blk = wave + i * W;
+        if (blk < nblk) {
+            const float *src = x + (int64_t)blk * B;
+            if constexpr (V >= 4) {
+#pragma unroll
+                for (int j = 0; j < V; j += 4) {
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(src + j);
+                    v[i][j] = t[0]; v[i][j + 1] = t[1]; v[i][j + 2] = t[2]; v[i][j + 3] = t[3];
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < V; ++j) v[i][j] = src[j];
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) v[i][j] = 0.0f;
+        }
+    }
+
+    float g = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        if (wave + i * W >= nblk) continue;              // wave-uniform
+#pragma unroll
+        for (int h = 1; h < V; h *= 2)
+#pragma unroll
+            for (int j = 0; j < V; ++j)
+                if (!(j & h)) {
+                    const float a = v[i][j], b = v[i][j + h];
+                    v[i][j] = a + b;
+                    v[i][j + h] = a - b;
+                }
+        lane_stage<V, 1>(v[i], lane);
+        lane_stage<V, 2>(v[i], lane);
+        lane_stage<V, 4>(v[i], lane);
+        lane_stage<V, 8>(v[i], lane);
+        lane_stage<V, 16>(v[i], lane);
+        lane_stage<V, 32>(v[i], lane);
+#pragma unroll
+        for (int j = 0; j < V; ++j) g = fmaxf(g, fabsf(v[i][j]));
+    }
+    g = wave_max_dpp(g);
+    if (lane == 0) s_max[wave] = g;
+    __syncthreads();
+    g = s_max[0];
+    for (int w = 1; w < W; ++w) g = fmaxf(g, s_max[w]);
+
+    const float up = act_prescale(g);
+    const float s = (g == 0.0f) ? 0.0f : 7.0f / (g * up);
+    int sum = 0;
+    int8_t *q = Xq + row * K + lane * V;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+        const int blk = wave + i * W;
+        if (blk >= nblk) continue;
+        if (up != 1.0f) {                                 // row-uniform, rare
+#pragma unroll
+            for (int j = 0; j < V; ++j) v[i][j] *= up;
+        }
+        int8_t *dst = q + (int64_t)blk * B;
+        if constexpr (V >= 4) {
+#pragma unroll
+            for (int j = 0; j < V; j += 4) {
+                int s4;
+                *reinterpret_cast<uint32_t *>(dst + j) = act_quant4(v[i][j], v[i][j + 1], v[i][j + 2], v[i][j + 3], s, &s4);
+                sum += s4;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                const uint32_t b = act_round_bits(v[i][j], s);
+                dst[j] = (int8_t)(b & 0xFFu);
+                sum += (int)(b - 0x4B400000u);
+            }
+        }
+    }
+    sum = wave_sum_dpp(sum);
+    if (lane == 0) s_sum[wave] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int total = 0;
+        for (int w = 0; w < W; ++w) total += s_sum[w];
+        x_scale[row] = (g == 0.0f) ? 0.0f : (float)((double)g / 7.0 / sqrt((double)B));
+        if (x_rowsum) x_rowsum[row] = total;
+    }
+}
+
+// Waves per row: for few rows as many as there are blocks (up to 16), for the
+// row's latency; from 256 rows the fewest that hold the row, but at least 8
+// (measured at 2048 x 6912, B = 256: 7 waves 18.3 us, 8 waves 16.6, 16
+// waves 18.6; at 2048 x 2560: 3 waves 7.9, 8 waves 8.8, 10 waves 10.4).
+// One row of 6912, B = 256: 3.8 us (the LDS form: 9.5 us).
+template <int V>
+hipError_t launch_h4_wave(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale, int32_t *x_rowsum,
+                          hipStream_t stream)
+{
+    constexpr int NB = kH4Slots / V;
+    const int nblk = (int)(K / (64 * V));
+    int W = nblk < 16 ? nblk : 16;
+    if (M >= 256) {
+        W = (nblk + NB - 1) / NB;
+        if (W < 8) W = nblk < 8 ? nblk : 8;
+    }
+    hipLaunchKernelGGL(quant_act_h4_wave_kernel<V>, dim3((unsigned)M), dim3(64 * W), 0, stream, X, K, Xq, x_scale,
+                       x_rowsum);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B, int8_t *Xq, float *x_scale,
-                               int32_t *x_rowsum, hipStream_t stream)
+                               int32_t *x_rowsum, hipStream_t stream, const char **name)
 {
     if (M == 0) return hipSuccess;
     if (B < 1 || B > kHChunk || (B & (B - 1)) || K % B || K % 8) return hipErrorInvalidValue;
+    // one block per wave in registers where it fits (64 <= B <= 1024 and at
+    // most 16 waves of 16 / (B / 64) blocks each)
+    if (B >= 64 && B <= 1024 && K / B <= 16 * (kH4Slots / (B / 64))) {
+        *name = "quant_act_h4_wave";
+        switch (B) {
+        case 64: return launch_h4_wave<1>(X, M, K, Xq, x_scale, x_rowsum, stream);
+        case 128: return launch_h4_wave<2>(X, M, K, Xq, x_scale, x_rowsum, stream);
+        case 256: return launch_h4_wave<4>(X, M, K, Xq, x_scale, x_rowsum, stream);
+        case 512: return launch_h4_wave<8>(X, M, K, Xq, x_scale, x_rowsum, stream);
+        default: return launch_h4_wave<16>(X, M, K, Xq, x_scale, x_rowsum, stream);
+        }
+    }
+    *name = "quant_act_h4";
     hipLaunchKernelGGL(quant_act_h4_kernel, dim3((unsigned)M), dim3(kQuantBlock), 0, stream, X, K, B, Xq, x_scale,
                        x_rowsum);
     return hipGetLastError();

@@ -28,10 +28,24 @@ def rows(seed, M, K):
     return X
 
 
+def h4_kernel(K, B):
+    """The quantiser the library picks: one block per wave in registers for
+    64 <= B <= 1024 with at most 16 waves of 16 / (B / 64) blocks, else the
+    LDS form."""
+    if 64 <= B <= 1024 and K // B <= 16 * (16 // (B // 64)):
+        return "quant_act_h4_wave"
+    return "quant_act_h4"
+
+
 @pytest.mark.parametrize("M,K,B", [(1, 64, 64), (3, 2560, 512), (5, 6912, 256), (2, 16384, 8192),
                                    (4, 11008, 256), (7, 512, 1), (3, 512, 2), (3, 512, 4), (2, 1024, 8),
-                                   (2, 1024, 16), (3, 4096, 4096), (2, 24576, 8192)])
+                                   (2, 1024, 16), (3, 4096, 4096), (2, 24576, 8192), (3, 2048, 128),
+                                   (3, 16384, 1024), (3, 17408, 1024), (3, 16384, 64), (3, 16448, 64),
+                                   (4, 1024, 1024), (3, 8192, 512), (5, 8256, 64), (300, 6912, 256)])
 def test_quant_act_h4(M, K, B):
+    # both forms: the wave form at B = 64 .. 1024 up to its largest row (16
+    # waves of 16 / (B / 64) blocks) and one block past it (the LDS form),
+    # one-wave rows, a ragged last wave, many rows
     import torch
 
     import oracle
@@ -39,7 +53,7 @@ def test_quant_act_h4(M, K, B):
     X = rows(700 + K + B, M, K)
     print("case quant_act_h4 M=%d K=%d B=%d" % (M, K, B), flush=True)
     q, xs, rs = bl.quant_act_h4(to_dev(X), B)
-    assert bl.last_dispatch() == "quant_act_h4"
+    assert bl.last_dispatch() == h4_kernel(K, B), bl.last_dispatch()
     torch.cuda.synchronize()
     q_o, xs_o, rs_o = oracle.quant_act_h4(X, B)
     assert np.array_equal(q.cpu().numpy(), q_o)
