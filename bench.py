@@ -13,7 +13,7 @@ streams its weights from HBM.  Steps are captured in a HIP graph and timed
 with HIP events on the capture's stream, bracketed by device synchronisation.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
-                       [--traffic-probe]
+                       [--traffic-probe] [--gemm-probe]
 Prints one JSON line on stdout; a readable summary goes to stderr.
 """
 from __future__ import annotations
@@ -272,6 +272,9 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a few eager decode steps and a copy kernel of known size, then exit "
                          "(the command profiled with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="run the prefill GEMM (2048 x 2560 -> 6912, dense) five times eagerly, then exit "
+                         "(the command profiled with rocprofv3 --pmc for its SQ counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -289,6 +292,19 @@ def main():
     dev = torch.device("cuda:0")
     props = torch.cuda.get_device_properties(dev)
     log("device: %s (%s), %d CUs" % (props.name, getattr(props, "gcnArchName", "?"), props.multi_processor_count))
+
+    if args.gemm_probe:
+        dp = workloads.draw("prefill_2048")
+        pk_p, ws_p = bl.pack_weights(torch.from_numpy(dp.W["up"]).to(dev))
+        Xq_p, xs_p, rs_p = bl.quant_act(torch.from_numpy(dp.X[("up", 2048)]).to(dev))
+        Y_p = torch.empty((2048, 6912), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, 6912, Y=Y_p)
+        torch.cuda.synchronize()
+        log("gemm probe: 5 launches of %s" % bl.last_dispatch())
+        print(json.dumps({"gemm_launches": 5, "kernel": bl.last_dispatch(), "source_digest": source_digest()}),
+              flush=True)
+        return
 
     # ------------------------------------------------------------------ decode
     # One decode step of a 2B-class FFN at M = 1: the fused call (activation
