@@ -172,11 +172,12 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], const in
 // operand.  The accumulators then hold 64 * sum t*q: no row sum is
 // subtracted, and the exact shift by 6 precedes the epilogue.  |acc| <= 64 *
 // 127 * K, so the host uses it for K <= 2^18.
-template <Pattern P, int BM, int BN, int WM, int WN, bool TB = false>
+template <Pattern P, int BM, int BN, int WM, int WN, bool TB = false, bool SPLIT = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
     const uint8_t *__restrict__ packed, const float *__restrict__ w_scale, int64_t M, int64_t N,
-    int64_t K, float *__restrict__ Y, int32_t *__restrict__ acc_out)
+    int64_t K, float *__restrict__ Y, int32_t *__restrict__ acc_out, int32_t splits = 1,
+    int32_t *__restrict__ ws = nullptr)
 {
     constexpr int T = 64 * WM * WN;
     constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
@@ -216,7 +217,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
     const int64_t tiles = tiles_m * tiles_n;
     // XCD-aware order: logical tile = xcd * per_xcd + index within the XCD
     const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
-    const int64_t b = blockIdx.x;
+    // SPLIT: blockIdx.x = split * (per_xcd * kXcds) + tile workgroup, as in
+    // the pipelined kernel's split-K form (same partial layout and epilogue)
+    const int64_t split = SPLIT ? (int64_t)blockIdx.x / (per_xcd * kXcds) : 0;
+    const int64_t b = (int64_t)blockIdx.x - split * per_xcd * kXcds;
     const int64_t tile = (b % kXcds) * per_xcd + b / kXcds;
     if (tile >= tiles) return;
     // consecutive logical tiles walk M first, so they share a weight column tile
@@ -314,14 +318,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[a][c][v] = 0;
 
-    const int64_t slices = K / BK;
-    load_slice(0);
+    // this workgroup's K slices [sl0, sl0 + slices)
+    const int64_t all_slices = K / BK;
+    const int64_t sl0 = SPLIT ? all_slices * split / splits : 0;
+    const int64_t slices = SPLIT ? all_slices * (split + 1) / splits - sl0 : all_slices;
+    load_slice(sl0 * BK);
     store_slice(0);
     __syncthreads();
 
     for (int64_t it = 0; it < slices; ++it) {
         const int buf = (int)(it & 1);
-        if (it + 1 < slices) load_slice((it + 1) * BK);
+        if (it + 1 < slices) load_slice((sl0 + it + 1) * BK);
 
         // B fragments: words 2h and 2h+1 of each row (k-steps s = 0, 1); all
         // fragments of the slice are read into distinct registers first
@@ -359,6 +366,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 
         if (it + 1 < slices) store_slice(buf ^ 1);
         __syncthreads();
+    }
+
+    if constexpr (SPLIT) {                             // raw partials; the epilogue kernel finishes
+        constexpr int E = FM * FN * 16;
+        int32_t *mine = ws + (split * tiles + tile) * (int64_t)(E * T);
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) mine[((fm * FN + fn) * 16 + v) * T + tid] = acc[fm][fn][v];
+        return;
     }
 
     if constexpr (TB) {                                // 64 * sum t*q: exact
@@ -623,8 +642,9 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(
 
 // Epilogue of the split-K GEMM, one thread per output element (m, n): find
 // the element's slot in the GEMM kernel's per-thread fragment layout, add the
-// `splits` partials (integers: order-free), subtract the row sum and scale.
-template <int BM, int BN, int WM, int WN>
+// `splits` partials (integers: order-free), subtract the row sum (TB: divide
+// the 64 * t sums by 64 instead; no offset codes) and scale.
+template <int BM, int BN, int WM, int WN, bool TB = false>
 __global__ __launch_bounds__(256) void splitk_epilogue_kernel(
     const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum, const float *__restrict__ w_scale,
     int64_t M, int64_t N, int32_t splits, const int32_t *__restrict__ ws, float *__restrict__ Y,
@@ -649,7 +669,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(
     const int e = (fm * FN + fn) * 16 + v;
     int acc = 0;
     for (int64_t o = 0; o < splits; ++o) acc += ws[(o * tiles + tile) * (int64_t)(E * T) + (int64_t)e * T + tid];
-    const int av = acc - x_rowsum[m];
+    const int av = TB ? (acc >> 6) : acc - x_rowsum[m];
     Y[idx] = (float)av * (w_scale[0] * x_scale[m]);
     if (acc_out) acc_out[idx] = av;
 }
@@ -728,6 +748,37 @@ hipError_t launch_few_tokens(const int8_t *Xq, const float *xs, const int32_t *r
     }
     *name = plain_name;
     return launch_dma<BM, BN, WM, WN, S, false>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+}
+
+// N:M t-byte GEMM with too few output tiles to fill the chip (few tokens,
+// or few weight rows): K split over enough workgroups to occupy every compute
+// unit, as for the dense few-token path; partials of 64 * t sums, exact.
+// Returns hipErrorNotSupported when no split applies (the caller launches
+// the unsplit kernel).
+template <Pattern P, int BM, int BN, int WM, int WN>
+hipError_t launch_tbytes_split(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                               const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                               hipStream_t stream)
+{
+    if (K > kTBytesMaxK) return hipErrorNotSupported;
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t slices = K / BK;
+    int64_t splits = std::min<int64_t>((kCus + tiles - 1) / tiles, slices / 4);   // >= 4 slices each
+    const int64_t per_split = tiles * (int64_t)BM * BN * 4;
+    splits = std::min<int64_t>(splits, kWorkspaceBytes / per_split);
+    if (splits < 2) return hipErrorNotSupported;
+    int32_t *w = split_workspace(stream);
+    if (!w) return hipErrorNotSupported;
+    const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
+    hipLaunchKernelGGL((gemm_kernel<P, BM, BN, WM, WN, true, true>), dim3((unsigned)(per_xcd * kXcds * splits)),
+                       dim3(64 * WM * WN), 0, stream, Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, (int32_t)splits,
+                       w);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t blocks = (M * N + 255) / 256;
+    hipLaunchKernelGGL((splitk_epilogue_kernel<BM, BN, WM, WN, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                       xs, rs, w_scale, M, N, (int32_t)splits, w, Y, acc);
+    return hipGetLastError();
 }
 
 template <Pattern P, int BM, int BN, int WM, int WN>
@@ -842,9 +893,26 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
             *name = names[tb][pi][0];
             return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
+        // too few tiles for the chip: K split (t-byte form); measured at 32 and
+        // 64 tokens, 6912 -> 2560 with 2:4: 71 us unsplit
+        static const char *split_names[3][2] = {
+            {"", ""}, {"gemm_nm24_splitk_128x128_tbytes", "gemm_nm24_splitk_64x128_tbytes"},
+            {"gemm_nm68_splitk_128x128_tbytes", "gemm_nm68_splitk_64x128_tbytes"}};
         if (M > 64) {
+            const hipError_t e = launch_tbytes_split<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc,
+                                                                        stream);
+            if (e != hipErrorNotSupported) {
+                *name = split_names[pi][0];
+                return e;
+            }
             *name = names[tb][pi][1];
             return launch<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+        }
+        const hipError_t e = launch_tbytes_split<P, 64, 128, 1, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc,
+                                                                   stream);
+        if (e != hipErrorNotSupported) {
+            *name = split_names[pi][1];
+            return e;
         }
         *name = names[tb][pi][2];
         return launch<P, 64, 128, 1, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);

@@ -107,7 +107,31 @@ def test_nm_gemm_tbytes(M, N, K, tile, nm):
     W, X = workloads.small_case(1200 + M + K, M, N, K, outlier_frac=0.001)
     full_check(W, X, nm, rows=sample_rows(M, 16, seed=M), label="nm-gemm")
     name = bl.last_dispatch()
-    assert name == "gemm_nm%d%d_%s_tbytes" % (nm[0], nm[1], tile), name
+    split = "splitk_" if tile != "256x256" and tbytes_splits(M, N, K, tile) >= 2 else ""
+    assert name == "gemm_nm%d%d_%s%s_tbytes" % (nm[0], nm[1], split, tile), name
+
+
+def tbytes_splits(M, N, K, tile):
+    """K splits of the N:M t-byte GEMM: enough workgroups for the 256 compute
+    units, at least 4 slices of 64 each, partials within the 64 MB workspace."""
+    bm, bn = (int(v) for v in tile.split("x"))
+    tiles = -(-M // bm) * -(-N // bn)
+    return min(-(-256 // tiles), (K // 64) // 4, (64 << 20) // (tiles * bm * bn * 4))
+
+
+@pytest.mark.parametrize("M,N,K,nm", [(32, 2560, 6912, (2, 4)), (64, 2560, 6912, (6, 8)), (16, 2560, 6912, (2, 4)),
+                                      (100, 1000, 2560, (6, 8)), (17, 777, 512, (2, 4)), (65, 300, 1536, (2, 4)),
+                                      (64, 8960, 1536, (6, 8)), (33, 2048, 11008, (6, 8))])
+def test_nm_gemm_tbytes_splitk(M, N, K, nm):
+    # few tokens (or few weight rows) with N:M weights: K split over enough
+    # workgroups for the chip, partial 64 * t sums added by the epilogue
+    # kernel; ragged M and N, 2 to 16 splits
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(1800 + M + K, M, N, K, outlier_frac=0.001)
+    full_check(W, X, nm, rows=sample_rows(M, 16, seed=K), label="nm-gemm-splitk")
+    tile = "64x128" if M <= 64 else "128x128"
+    assert tbytes_splits(M, N, K, tile) >= 2
+    assert bl.last_dispatch() == "gemm_nm%d%d_splitk_%s_tbytes" % (nm[0], nm[1], tile), bl.last_dispatch()
 
 
 def nm24_sparse_tile(M, N):
@@ -136,7 +160,11 @@ def test_nm24_sparse_threshold(M):
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1450 + M, M, 1000, 512)
     full_check(W, X, (2, 4), rows=sample_rows(M, 24, seed=M), label="nm24-threshold")
-    want = "gemm_nm24_128x128_tbytes" if M < 128 else "gemm_nm24_smfmac_" + nm24_sparse_tile(M, 1000)
+    if M < 128:
+        split = "splitk_" if tbytes_splits(M, 1000, 512, "128x128") >= 2 else ""
+        want = "gemm_nm24_%s128x128_tbytes" % split
+    else:
+        want = "gemm_nm24_smfmac_" + nm24_sparse_tile(M, 1000)
     assert bl.last_dispatch() == want, bl.last_dispatch()
 
 
