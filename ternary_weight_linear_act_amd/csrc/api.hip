@@ -53,6 +53,18 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
                                                 ActTransform{nullptr, nullptr, 0.0f}, stream, name);
         if (e != hipErrorNotSupported) return e;
     }
+    // 2:4 at 2-16 tokens on the sparse MFMA where it measured at least as fast
+    // as the 16x16x64 kernel on dense codes: K <= 4096 (8960 x 1536, 6912 x
+    // 2560: 5.6-6.7 against 5.9-6.7 us at 2-8 tokens; 1000 x 640: 3.2 against
+    // 4.6-5.1 us), and any K past 8 tokens (6912 x 2560 at 16: 7.6 against
+    // 10.9 us; 2560 x 6912 at 16: 9.2 against 16.4 us)
+    if (p == Pattern::NM24 && M >= 2 && M <= 16 && (K <= 4096 || M > 8)) {
+        const hipError_t e = launch_skinny_nm24_smfmac(Xq, x_scale, packed, w_scale, M, N, K, Y, acc, stream);
+        if (e != hipErrorNotSupported) {
+            *name = "skinny_smfmac_nm24";
+            return e;
+        }
+    }
     if (M <= 16) {
         const hipError_t e = launch_skinny_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc,
                                                    stream, name);

@@ -290,6 +290,99 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_nm24_sparse_kernel(
     }
 }
 
+// ---------------------------------------------------------------------------
+// 2:4 weights at 1-16 tokens on the sparse matrix cores
+// (v_smfmac_i32_16x16x128_i8).  The weights are the sparse A operand (16
+// rows per workgroup), the tokens the dense B operand (16 columns, zero past
+// M): lane l holds weight row l % 16 and, as B, token l % 16; q = l / 16.
+//   A: the kept values of k in [32q, 32q + 32) of a 128-wide step -- one
+//      value word and one mask word of the packed row (expand24);
+//   B: bytes 0-15 = k in [16q, 16q + 16), bytes 16-31 = k in [64 + 16q,
+//      80 + 16q) of the step, read straight from Xq (L2-resident);
+//   D: token l % 16, weight rows 4q .. 4q + 3.
+// The workgroup's KS waves take consecutive runs of at most U steps of K;
+// every load of a wave is issued before its first MFMA; wave 0 adds the
+// other waves' partial sums (LDS) and applies beta * x_scale.  The values
+// are t in {-1, 0, +1}: no row sum is subtracted.  K % 128 == 0.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(1024) void skinny_nm24_smfmac_kernel(
+    const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const uint8_t *__restrict__ packed,
+    const float *__restrict__ w_scale, int64_t M, int64_t N, int64_t K, float *__restrict__ Y,
+    int32_t *__restrict__ acc_out)
+{
+    __shared__ i32x4 s_part[16][64];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int KS = blockDim.x >> 6;
+    const int r = lane & 15, q = lane >> 4;
+    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int64_t T = K / 128;
+    const int64_t s0 = T * wave / KS;
+    const int cnt = (int)(T * (wave + 1) / KS - s0);            // 1 .. U steps, wave-uniform
+    const int64_t n = min(n0 + r, N - 1);
+    const uint32_t *vrow = reinterpret_cast<const uint32_t *>(packed) + n * (K / 32);
+    const uint32_t *mrow = reinterpret_cast<const uint32_t *>(packed + N * (K / 8)) + n * (K / 32);
+    const bool tok = r < M;
+    const int8_t *xrow = Xq + (tok ? r : 0) * K;
+
+    // every load first: steps past this wave's run re-read its last step and
+    // contribute zero activations
+    uint32_t vw[U], mw[U];
+    i32x4 blo[U], bhi[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t st = s0 + min(u, cnt - 1);
+        vw[u] = vrow[4 * st + q];
+        mw[u] = mrow[4 * st + q];
+        blo[u] = *reinterpret_cast<const i32x4 *>(xrow + 128 * st + 16 * q);
+        bhi[u] = *reinterpret_cast<const i32x4 *>(xrow + 128 * st + 64 + 16 * q);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    i32x4 acc = {0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool live = tok && u < cnt;
+        i32x8 b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            b[j] = live ? blo[u][j] : 0;
+            b[4 + j] = live ? bhi[u][j] : 0;
+        }
+        i32x4 a;
+        int ix;
+        expand24(vw[u], mw[u], a, ix);
+        acc = __builtin_amdgcn_smfmac_i32_16x16x128_i8(a, b, acc, ix, 0, 0);
+    }
+    if (KS > 1) {
+        if (wave > 0) s_part[wave][lane] = acc;
+        __syncthreads();
+        if (wave != 0) return;
+        for (int w = 1; w < KS; ++w) acc += s_part[w][lane];
+    }
+    if (!tok) return;
+    const float sc = w_scale[0] * x_scale[r];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int64_t nn = n0 + 4 * q + v;
+        if (nn < N) {
+            Y[(int64_t)r * N + nn] = (float)acc[v] * sc;
+            if (acc_out) acc_out[(int64_t)r * N + nn] = acc[v];
+        }
+    }
+}
+
+template <int U>
+hipError_t launch_skinny_sparse(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
+                                int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
+{
+    const int64_t T = K / 128;
+    const int64_t KS = (T + U - 1) / U;
+    if (KS > 16) return hipErrorNotSupported;
+    hipLaunchKernelGGL(skinny_nm24_smfmac_kernel<U>, dim3((unsigned)((N + 15) / 16)), dim3((unsigned)(64 * KS)), 0,
+                       stream, Xq, xs, packed, w_scale, M, N, K, Y, acc);
+    return hipGetLastError();
+}
+
 template <int BM, int WM, int WN, int S>
 hipError_t launch_sparse(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale, int64_t M,
                          int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
@@ -306,6 +399,17 @@ hipError_t launch_sparse(const int8_t *Xq, const float *xs, const uint8_t *packe
 }
 
 }  // namespace
+
+// 2:4 weights at 1 <= M <= 16 tokens, K % 128 == 0 and K <= 16384;
+// hipErrorNotSupported otherwise.  At most 4 steps of 128 per wave up to
+// K = 8192 (16 waves), 8 beyond (measured: 4 is as fast or faster).
+hipError_t launch_skinny_nm24_smfmac(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
+                                     int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
+{
+    if (K % 128 != 0 || M < 1 || M > 16 || K > 16384) return hipErrorNotSupported;
+    if (K <= 8192) return launch_skinny_sparse<4>(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream);
+    return launch_skinny_sparse<8>(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream);
+}
 
 // 2:4 weights, K % 128 == 0; hipErrorNotSupported otherwise.  tile_m: 256
 // or 128 tokens per workgroup.

@@ -15,6 +15,11 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, fl
 hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64_t K, int8_t *Xq,
                                float *x_scale, int32_t *x_rowsum, hipStream_t stream);
 
+// 2:4 weights at 1-16 tokens on the sparse MFMA (K % 128 == 0, K <= 16384;
+// hipErrorNotSupported otherwise).
+hipError_t launch_skinny_nm24_smfmac(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
+                                     int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream);
+
 // H-BitLinear activations: block Hadamard transform (block B, a power of two
 // <= 8192 dividing K), then 4-bit absmax codes in int8.
 hipError_t launch_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B, int8_t *Xq, float *x_scale,

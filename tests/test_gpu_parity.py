@@ -119,7 +119,7 @@ def tbytes_splits(M, N, K, tile):
     return min(-(-256 // tiles), (K // 64) // 4, (64 << 20) // (tiles * bm * bn * 4))
 
 
-@pytest.mark.parametrize("M,N,K,nm", [(32, 2560, 6912, (2, 4)), (64, 2560, 6912, (6, 8)), (16, 2560, 6912, (2, 4)),
+@pytest.mark.parametrize("M,N,K,nm", [(32, 2560, 6912, (2, 4)), (64, 2560, 6912, (6, 8)), (16, 2560, 6912, (6, 8)),
                                       (100, 1000, 2560, (6, 8)), (17, 777, 512, (2, 4)), (65, 300, 1536, (2, 4)),
                                       (64, 8960, 1536, (6, 8)), (33, 2048, 11008, (6, 8))])
 def test_nm_gemm_tbytes_splitk(M, N, K, nm):
@@ -208,7 +208,31 @@ def test_skinny_deep_k(M, mt, K, nm):
     W, X = workloads.small_case(1400 + M, M, 300, K, outlier_frac=0.001)
     full_check(W, X, nm, label="skinny-deep-k")
     name = bl.last_dispatch()
-    assert name.startswith("skinny_mfma_") and name.endswith("_mt%d" % mt), name
+    if nm == (2, 4) and nm24_smfmac_skinny(M, K):
+        assert name == "skinny_smfmac_nm24", name
+    else:
+        assert name.startswith("skinny_mfma_") and name.endswith("_mt%d" % mt), name
+
+
+def nm24_smfmac_skinny(M, K):
+    """2:4 at 2-16 tokens runs on the sparse MFMA for K <= 4096, or past 8
+    tokens (K % 128 == 0, K <= 16384)."""
+    return 2 <= M <= 16 and K % 128 == 0 and K <= 16384 and (K <= 4096 or M > 8)
+
+
+@pytest.mark.parametrize("M,N,K", [(2, 1000, 640), (5, 6912, 2560), (8, 8960, 1536), (16, 2560, 6912),
+                                   (16, 777, 128), (9, 3000, 8192), (12, 300, 11008), (16, 33, 16384),
+                                   (3, 4095, 4096), (13, 100, 8320)])
+def test_nm24_smfmac_skinny(M, N, K):
+    # 2:4 at 2-16 tokens on v_smfmac_i32_16x16x128_i8: weights as the sparse
+    # operand, tokens as the dense one (zero columns past M); one to 16 waves
+    # of at most 4 (K <= 8192) or 8 steps of 128, uneven runs, ragged weight
+    # rows, one step, the largest K
+    import ternary_weight_linear_act_amd as bl
+    assert nm24_smfmac_skinny(M, K)
+    W, X = workloads.small_case(1900 + M + K, M, N, K, outlier_frac=0.001)
+    full_check(W, X, (2, 4), label="nm24-smfmac-skinny")
+    assert bl.last_dispatch() == "skinny_smfmac_nm24", bl.last_dispatch()
 
 
 @pytest.mark.parametrize("M", [1, 3])
