@@ -52,13 +52,16 @@
  * Conventions for every call:
  *   - Data pointers are device pointers (hipMalloc / torch tensors) owned by
  *     the caller.  The one exception is internal: the first
- *     bitlinear_forward call on a device that runs the few-token GEMM with K
- *     split over workgroups (dense, M <= 64 with too few output tiles to
- *     fill the GPU) allocates a 64 MB split-K workspace with hipMalloc,
- *     once, and keeps it until the process ends.  That call must not be inside HIP
- *     graph capture (a captured call that finds no workspace uses the
- *     unsplit kernel instead), and such calls must not overlap in time on
- *     one device (they share the workspace).
+ *     bitlinear_forward call on a device that needs scratch memory allocates
+ *     a 64 MB workspace with hipMalloc, once, and keeps it until the process
+ *     ends.  Two paths use it: the few-token GEMMs with K split over
+ *     workgroups (M <= 64 with too few output tiles to fill the GPU; int32
+ *     partial sums) and N:M weights at M >= 65 where the 2:4 sparse MFMA
+ *     does not apply (the rows expanded to dense codes, N*K/4 <= 64 MB, for
+ *     the dense GEMM).  That first call must not be inside HIP graph capture
+ *     (a captured call that finds no workspace uses the unsplit or t-byte
+ *     kernel instead, with identical results), and such calls must not
+ *     overlap in time on one device (they share the workspace).
  *   - Matrices are row-major and dense: W is N x K (out x in), X and Xq are
  *     M x K, Y and acc are M x N.
  *   - Work is enqueued on `stream` (NULL = the null stream); no call

@@ -34,6 +34,7 @@
 // the grid allows it.
 #include <algorithm>
 #include <mutex>
+#include <string_view>
 #include <type_traits>
 
 #include "dma.hpp"
@@ -96,6 +97,27 @@ __device__ __forceinline__ u32x4 dense_words(const RawSlice<P> &r, const uint8_t
         decode_superblock_fast<P>(r.w, r.w + VW, w, table24);
         return u32x4{w[0], w[1], w[2], w[3]};
     }
+}
+
+// N:M rows expanded to the dense code layout, one 64-weight chunk per thread
+// (pruned positions get code 1, t = 0), so that the pipelined dense GEMM can
+// run on them: one pass over the weights per call.
+template <Pattern P>
+__global__ __launch_bounds__(256) void nm_expand_dense_kernel(const uint8_t *__restrict__ packed, int64_t N,
+                                                              int64_t K, uint8_t *__restrict__ dense)
+{
+    __shared__ uint8_t s_nm24[P == Pattern::NM24 ? 256 : 1];
+    if constexpr (P == Pattern::NM24) {
+        s_nm24[threadIdx.x] = nm24_table_entry((uint32_t)threadIdx.x);
+        __syncthreads();
+    }
+    const int64_t C = K / 64;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= N * C) return;
+    const int64_t n = i / C, c = i - n * C;
+    RawSlice<P> r;
+    load_raw<P>(packed, N, K, n, c * 64, r);
+    *reinterpret_cast<u32x4 *>(dense + n * (K / 4) + c * 16) = dense_words<P>(r, s_nm24);
 }
 
 __device__ __forceinline__ i32x4 unpack_word(uint32_t w)
@@ -870,6 +892,37 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
         return launch_few_tokens<64, 64, 2, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
                                                "gemm_dense_splitk_64x64", "gemm_dense_dma_64x64");
     } else {
+        // 65+ tokens where the sparse MFMA does not apply (6:8; 2:4 below 128
+        // tokens or with K % 128 != 0): expand the rows to dense codes once
+        // into the workspace, then the pipelined dense GEMM.  Measured against
+        // the t-byte GEMM, 6:8 (dense beside it): 2048 x 6912 x 2560 70 ->
+        // 52 us (48), 4096 x 8192 x 4096 218 -> 141 us (137), 2048 x 2560 x
+        // 6912 88 -> 59 us (54), 128 x 8960 x 1536 18.0 -> 16.7 us (11.7).
+        // The workspace is shared with the few-token split-K path, which
+        // never runs in the same call (M <= 64).
+        const bool sparse24 = P == Pattern::NM24 && M >= 128 && K % 128 == 0;
+        if (M > 64 && !sparse24 && N * (K / 4) <= kWorkspaceBytes) {
+            int32_t *w = split_workspace(stream);
+            if (w) {
+                static const char *expand_names[3][3] = {
+                    {"", "", ""},
+                    {"gemm_nm24_expand_dense_256x256", "gemm_nm24_expand_dense_128x256",
+                     "gemm_nm24_expand_dense_128x128"},
+                    {"gemm_nm68_expand_dense_256x256", "gemm_nm68_expand_dense_128x256",
+                     "gemm_nm68_expand_dense_128x128"}};
+                const int64_t chunks = N * (K / 64);
+                hipLaunchKernelGGL(nm_expand_dense_kernel<P>, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
+                                   stream, packed, N, K, reinterpret_cast<uint8_t *>(w));
+                hipError_t e = hipGetLastError();
+                if (e != hipSuccess) return e;
+                const char *dn = "";
+                e = dispatch<Pattern::Dense>(Xq, xs, rs, reinterpret_cast<const uint8_t *>(w), w_scale, M, N, K, Y,
+                                             acc, stream, &dn);
+                const std::string_view d(dn);
+                *name = expand_names[pi][d.find("256x256") != d.npos ? 0 : d.find("128x256") != d.npos ? 1 : 2];
+                return e;
+            }
+        }
         if constexpr (P == Pattern::NM24) {
             // 2:4 on the sparse matrix cores (gemm_sparse.hip) where K allows;
             // token tile by rounds over the compute units as for the dense

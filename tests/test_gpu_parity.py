@@ -107,8 +107,38 @@ def test_nm_gemm_tbytes(M, N, K, tile, nm):
     W, X = workloads.small_case(1200 + M + K, M, N, K, outlier_frac=0.001)
     full_check(W, X, nm, rows=sample_rows(M, 16, seed=M), label="nm-gemm")
     name = bl.last_dispatch()
-    split = "splitk_" if tile != "256x256" and tbytes_splits(M, N, K, tile) >= 2 else ""
-    assert name == "gemm_nm%d%d_%s%s_tbytes" % (nm[0], nm[1], split, tile), name
+    if M > 64:
+        # from 65 tokens the rows are expanded to dense codes for the
+        # pipelined dense GEMM (these K are not multiples of 128, so 2:4 does
+        # not take the sparse MFMA either)
+        assert name == "gemm_nm%d%d_expand_dense_%s" % (nm[0], nm[1], dense_tile(M, N).split("_")[0]), name
+    else:
+        split = "splitk_" if tbytes_splits(M, N, K, tile) >= 2 else ""
+        assert name == "gemm_nm%d%d_%s%s_tbytes" % (nm[0], nm[1], split, tile), name
+
+
+@pytest.mark.parametrize("M,N,K,nm", [(2048, 6912, 2560, (6, 8)), (512, 8960, 1536, (6, 8)), (65, 777, 64, (6, 8)),
+                                      (1000, 8000, 640, (6, 8)), (300, 1000, 1472, (2, 4)), (100, 4100, 192, (2, 4)),
+                                      (129, 257, 11008, (6, 8)), (4096, 4096, 128, (6, 8))])
+def test_nm_expand_dense_gemm(M, N, K, nm):
+    # 65+ tokens with 6:8 (or 2:4 off the sparse MFMA): rows expanded to dense
+    # codes in the workspace, then the pipelined dense GEMM, all three tiles,
+    # ragged tiles, one K slice, deep K
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(2100 + M + K, M, N, K, outlier_frac=0.001)
+    full_check(W, X, nm, rows=sample_rows(M, 16, seed=K), label="nm-expand-dense")
+    want = "gemm_nm%d%d_expand_dense_%s" % (nm[0], nm[1], dense_tile(M, N).split("_")[0])
+    assert bl.last_dispatch() == want, bl.last_dispatch()
+
+
+def dense_tile(M, N):
+    """Tile of the pipelined dense GEMM: rounds of tiles over the 256 compute
+    units cost 4 (256 x 256), 2 (128 x 256), 1.35 (128 x 128)."""
+    rounds = lambda bm, bn: -(-(-(-M // bm) * -(-N // bn)) // 256)
+    c256, c12, c128 = 4 * rounds(256, 256), 2 * rounds(128, 256), 1.35 * rounds(128, 128)
+    if c256 <= c12 and c256 <= c128:
+        return "256x256_w8_s6"
+    return "128x256_w8_s4" if c12 <= c128 else "128x128_w4_s4"
 
 
 def tbytes_splits(M, N, K, tile):
@@ -120,7 +150,7 @@ def tbytes_splits(M, N, K, tile):
 
 
 @pytest.mark.parametrize("M,N,K,nm", [(32, 2560, 6912, (2, 4)), (64, 2560, 6912, (6, 8)), (16, 2560, 6912, (6, 8)),
-                                      (100, 1000, 2560, (6, 8)), (17, 777, 512, (2, 4)), (65, 300, 1536, (2, 4)),
+                                      (48, 1000, 2560, (6, 8)), (17, 777, 512, (2, 4)), (60, 300, 1536, (2, 4)),
                                       (64, 8960, 1536, (6, 8)), (33, 2048, 11008, (6, 8))])
 def test_nm_gemm_tbytes_splitk(M, N, K, nm):
     # few tokens (or few weight rows) with N:M weights: K split over enough
@@ -129,7 +159,7 @@ def test_nm_gemm_tbytes_splitk(M, N, K, nm):
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1800 + M + K, M, N, K, outlier_frac=0.001)
     full_check(W, X, nm, rows=sample_rows(M, 16, seed=K), label="nm-gemm-splitk")
-    tile = "64x128" if M <= 64 else "128x128"
+    tile = "64x128"
     assert tbytes_splits(M, N, K, tile) >= 2
     assert bl.last_dispatch() == "gemm_nm%d%d_splitk_%s_tbytes" % (nm[0], nm[1], tile), bl.last_dispatch()
 
@@ -156,13 +186,12 @@ def test_nm24_sparse_mfma_gemm(M, N, K):
 
 @pytest.mark.parametrize("M", [127, 128, 129, 255, 256, 257])
 def test_nm24_sparse_threshold(M):
-    # below 128 tokens 2:4 stays on the t-byte GEMM
+    # below 128 tokens 2:4 takes the dense GEMM on expanded rows
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1450 + M, M, 1000, 512)
     full_check(W, X, (2, 4), rows=sample_rows(M, 24, seed=M), label="nm24-threshold")
     if M < 128:
-        split = "splitk_" if tbytes_splits(M, 1000, 512, "128x128") >= 2 else ""
-        want = "gemm_nm24_%s128x128_tbytes" % split
+        want = "gemm_nm24_expand_dense_" + dense_tile(M, 1000).split("_")[0]
     else:
         want = "gemm_nm24_smfmac_" + nm24_sparse_tile(M, 1000)
     assert bl.last_dispatch() == want, bl.last_dispatch()
