@@ -137,10 +137,13 @@ bitlinear_status bitlinear_quant_act(const float *X, int64_t M, int64_t K,
  * output.  acc: optional M x N int32 output of the exact integer sums (NULL
  * to skip).  The kernel is chosen from the shape: M = 1 (K <= 16384) packed
  * int8 dot products; 2 <= M <= 16 an MFMA kernel with the tokens as one
- * operand; larger M the MFMA GEMM (K split over workgroups for M <= 64 when
- * the output tiles alone cannot fill the GPU; 2:4 with K % 128 == 0 and at
- * least 128 output tiles of 256 x 256 on the sparse MFMA).  bitlinear_last_dispatch()
- * names the kernel. */
+ * operand (2:4 with K % 128 == 0: the sparse MFMA where it measured faster);
+ * larger M the MFMA GEMM (K split over workgroups for M <= 64 when the output
+ * tiles alone cannot fill the GPU; 2:4 with K % 128 == 0 and M >= 128 on the
+ * sparse MFMA; other N:M at M >= 65 on the dense GEMM after expanding the
+ * rows to dense codes in the library's workspace).  Every path gives the
+ * same acc, bit for bit, and the same Y.  bitlinear_last_dispatch() names the
+ * kernel. */
 bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                                    const void *packed, const float *w_scale, bitlinear_nm nm,
                                    int64_t M, int64_t N, int64_t K,
