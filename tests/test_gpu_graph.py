@@ -8,7 +8,9 @@ eager call on the new inputs, so the graph reads its buffers each time rather
 than holding values from capture.  Covered: quant_act + forward (dense, 2:4,
 6:8; one token, the few-token split-K kernel, the prefill tiles, the sparse
 MFMA GEMM), the fused one-token launch with and without a row transform, the
-fused 2-4-token launch, quant_act_ex and the H-BitLinear quantiser."""
+fused 2-4-token launch, quant_act_ex and the H-BitLinear quantiser.  And, in a
+fresh process, forward calls captured before the library's workspace exists
+(the paths that need none, same bits as the eager calls afterwards)."""
 import numpy as np
 import pytest
 
@@ -137,3 +139,55 @@ def test_graph_quantisers(kind):
 
     X2 = workloads.activations(rng, M, K, 0.01)
     check_replays(body, [Xq, xs, rs], lambda: Xd.copy_(to_dev(X2)))
+
+
+_FIRST_CALL_CAPTURED = r'''
+import numpy as np
+import torch
+import ternary_weight_linear_act_amd as bl
+from ternary_weight_linear_act_amd import workloads
+cases = [(512, 8960, 1536, (6, 8)), (20, 4096, 6912, (0, 0))]
+dev = torch.device("cuda:0")
+prep = []
+for M, N, K, nm in cases:
+    W, X = workloads.small_case(2400 + M, M, N, K, outlier_frac=0.001)
+    pk, ws = bl.pack_weights(torch.from_numpy(W).to(dev), nm)
+    Xq, xs, rs = bl.quant_act(torch.from_numpy(X).to(dev))
+    prep.append((M, N, K, nm, pk, ws, Xq, xs, rs, torch.empty((M, N), dtype=torch.float32, device=dev),
+                 torch.empty((M, N), dtype=torch.int32, device=dev)))
+torch.cuda.synchronize()
+s = torch.cuda.Stream()
+s.wait_stream(torch.cuda.current_stream())
+g = torch.cuda.CUDAGraph()
+names = []
+with torch.cuda.graph(g, stream=s):                  # the first forward calls of the process
+    for M, N, K, nm, pk, ws, Xq, xs, rs, Y, acc in prep:
+        bl.forward(Xq, xs, rs, pk, ws, N, nm, Y=Y, acc=acc)
+        names.append(bl.last_dispatch())
+g.replay()
+torch.cuda.synchronize()
+for i, (M, N, K, nm, pk, ws, Xq, xs, rs, Y, acc) in enumerate(prep):
+    Yg, ag = Y.clone(), acc.clone()
+    Ye, ae = bl.forward(Xq, xs, rs, pk, ws, N, nm, want_acc=True)
+    eager = bl.last_dispatch()
+    torch.cuda.synchronize()
+    print("case", M, N, K, nm, "captured:", names[i], "eager:", eager, flush=True)
+    assert names[i] != eager, "the captured call should not find the workspace"
+    assert torch.equal(ag, ae) and torch.equal(Yg, Ye)
+print("ok", flush=True)
+'''
+
+
+def test_graph_capture_before_workspace():
+    # in a fresh process, forward calls captured before the library's
+    # workspace exists take the paths that need none (the t-byte GEMM for
+    # 6:8 prefill, the unsplit few-token GEMM) and give the same bits as the
+    # eager calls made afterwards (expanded rows, split K)
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _FIRST_CALL_CAPTURED], cwd=root, capture_output=True, text=True,
+                       timeout=300)
+    print(r.stdout[-2000:], r.stderr[-2000:])
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stderr[-2000:]
