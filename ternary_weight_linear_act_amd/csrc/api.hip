@@ -65,7 +65,11 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
             return e;
         }
     }
-    if (M <= 16) {
+    // 17-64 tokens: the skinny kernel in tiles of 16 tokens where the tiles
+    // make at most 512 workgroups (few weight rows: 2048 x 2048 at 64 tokens
+    // 8.2 -> 4.2 us, 2048 x 256 9.2 -> 3.5 us); with more, the GEMM is faster
+    // (2048 x 11008 at 64 tokens: 10.1 against 17.3 us)
+    if (M <= 16 || (M <= kSkinnyMaxM && ((N + 15) / 16) * ((M + 15) / 16) <= 512)) {
         const hipError_t e = launch_skinny_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc,
                                                    stream, name);
         if (e != hipErrorNotSupported) return e;

@@ -15,6 +15,9 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, fl
 hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64_t K, int8_t *Xq,
                                float *x_scale, int32_t *x_rowsum, hipStream_t stream);
 
+// Largest token count of the skinny MFMA forward (tiles of 16 tokens past 16).
+constexpr int64_t kSkinnyMaxM = 64;
+
 // 2:4 weights at 1-16 tokens on the sparse MFMA (K % 128 == 0, K <= 16384;
 // hipErrorNotSupported otherwise).
 hipError_t launch_skinny_nm24_smfmac(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,

@@ -10,6 +10,7 @@
 #include <math.h>
 #include <stdio.h>
 
+#include "kernels.hpp"
 #include "skinny_impl.hpp"
 
 namespace bl {
@@ -86,8 +87,9 @@ hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_
                                  const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
                                  int32_t *acc, hipStream_t stream, const char **name)
 {
-    if (M < 1 || M > 16) return hipErrorNotSupported;
-    // token rows staged per wave: 1, 4, 8 or 16 (rows past M read a zero block)
+    if (M < 1 || M > kSkinnyMaxM) return hipErrorNotSupported;
+    // token rows staged per wave: 1, 4, 8 or 16 (rows past M read a zero
+    // block); past 16 tokens, tiles of 16 along the grid's y
     const int mt = (M == 1) ? 1 : (M <= 4) ? 4 : (M <= 8) ? 8 : 16;
     const int64_t C = K / 64;
     // candidates ordered by distance (in log2) from ~10 chunks per wave

@@ -146,6 +146,15 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
     const int64_t n0 = (int64_t)blockIdx.x * 16;
+    // token tile blockIdx.y: rows 16 y .. 16 y + 15 of the call's M (then
+    // MT = 16); the tiles share nothing, and re-read the weights from L2
+    const int64_t t0 = (int64_t)blockIdx.y * 16;
+    Xq += t0 * K;
+    x_scale += t0;
+    x_rowsum += t0;
+    Y += t0 * N;
+    if (acc_out) acc_out += t0 * N;
+    M = min(M - t0, (int64_t)MT);
     const int64_t C = K / 64;
     const int mt = (int)M;                           // 1 <= M <= MT
     // this wave's chunk range [c_lo, c_lo + cw), 1 <= cw <= CMAX (the host keeps KS <= C)
@@ -280,8 +289,8 @@ hipError_t launch_skinny(const int8_t *Xq, const float *xs, const int32_t *rs, c
                          hipStream_t stream)
 {
     const int64_t blocks = (N + 15) / 16;
-    hipLaunchKernelGGL((skinny_kernel<P, KS, CMAX, MT>), dim3((unsigned)blocks), dim3(64 * KS), 0, stream,
-                       Xq, xs, rs, packed, w_scale, M, N, K, Y, acc);
+    hipLaunchKernelGGL((skinny_kernel<P, KS, CMAX, MT>), dim3((unsigned)blocks, (unsigned)((M + 15) / 16)),
+                       dim3(64 * KS), 0, stream, Xq, xs, rs, packed, w_scale, M, N, K, Y, acc);
     return hipGetLastError();
 }
 

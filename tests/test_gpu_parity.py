@@ -112,6 +112,8 @@ def test_nm_gemm_tbytes(M, N, K, tile, nm):
         # pipelined dense GEMM (these K are not multiples of 128, so 2:4 does
         # not take the sparse MFMA either)
         assert name == "gemm_nm%d%d_expand_dense_%s" % (nm[0], nm[1], dense_tile(M, N).split("_")[0]), name
+    elif skinny_tiles(M, N):
+        assert name.startswith("skinny_mfma_nm") and name.endswith("_mt16"), name
     else:
         split = "splitk_" if tbytes_splits(M, N, K, tile) >= 2 else ""
         assert name == "gemm_nm%d%d_%s%s_tbytes" % (nm[0], nm[1], split, tile), name
@@ -150,7 +152,7 @@ def tbytes_splits(M, N, K, tile):
 
 
 @pytest.mark.parametrize("M,N,K,nm", [(32, 2560, 6912, (2, 4)), (64, 2560, 6912, (6, 8)), (16, 2560, 6912, (6, 8)),
-                                      (48, 1000, 2560, (6, 8)), (17, 777, 512, (2, 4)), (60, 300, 1536, (2, 4)),
+                                      (48, 9000, 2560, (6, 8)), (17, 8300, 512, (2, 4)), (60, 3000, 1536, (2, 4)),
                                       (64, 8960, 1536, (6, 8)), (33, 2048, 11008, (6, 8))])
 def test_nm_gemm_tbytes_splitk(M, N, K, nm):
     # few tokens (or few weight rows) with N:M weights: K split over enough
@@ -275,11 +277,12 @@ def test_gemv_fallback_very_deep_k(M, nm):
     assert bl.last_dispatch().startswith("gemv_"), bl.last_dispatch()
 
 
-@pytest.mark.parametrize("M,N,K", [(24, 2048, 11008), (17, 300, 2048), (20, 8960, 1536), (33, 2048, 2048), (64, 256, 2048),
-                                   (64, 2048, 11008), (40, 1000, 192), (64, 11008, 2048)])
+@pytest.mark.parametrize("M,N,K", [(24, 2048, 11008), (17, 8200, 2048), (20, 8960, 1536), (33, 6000, 2048),
+                                   (64, 2100, 2048), (64, 2048, 11008), (40, 9000, 192), (64, 11008, 2048)])
 def test_few_token_gemm(M, N, K):
-    # few tokens: K split over several workgroups, partial tiles combined by a
-    # second kernel; twice in a row (the shared workspace is reused)
+    # few tokens with many weight rows (or K too deep for the skinny kernel):
+    # K split over several workgroups, partial tiles combined by a second
+    # kernel; twice in a row (the shared workspace is reused)
     import torch
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(900 + M + K, M, N, K, outlier_frac=0.001)
@@ -290,6 +293,26 @@ def test_few_token_gemm(M, N, K):
     torch.cuda.synchronize()
     assert torch.equal(acc2, out["acc"])
     assert torch.equal(Y2.view(torch.int32), out["Y"].view(torch.int32))
+
+
+def skinny_tiles(M, N):
+    """17-64 tokens take the skinny kernel in 16-token tiles when the tiles make
+    at most 512 workgroups."""
+    return M <= 16 or (M <= 64 and -(-N // 16) * -(-M // 16) <= 512)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 300, 2048), (33, 2048, 2048), (64, 256, 2048), (40, 1000, 192),
+                                   (64, 2048, 2048), (50, 97, 4096)])
+@pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
+def test_skinny_token_tiles(M, N, K, nm):
+    # 17-64 tokens with few weight rows: the skinny kernel over tiles of 16
+    # tokens along the grid's y (a ragged last tile, ragged weight rows)
+    import ternary_weight_linear_act_amd as bl
+    assert skinny_tiles(M, N)
+    W, X = workloads.small_case(2500 + M + K, M, N, K, outlier_frac=0.001)
+    full_check(W, X, nm, rows=sample_rows(M, 24, seed=K), label="skinny-tiles")
+    name = bl.last_dispatch()
+    assert name.startswith("skinny_mfma_") and name.endswith("_mt16"), name
 
 
 def test_zero_rows_and_zero_weights():
@@ -346,7 +369,8 @@ def test_deterministic_and_dispatch():
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(10, 300, 384, 512)
     packed, ws = hip_pack(W, (0, 0))
-    for M, expect in [(1, "decode_dot4"), (4, "skinny"), (16, "skinny"), (17, "gemm"), (300, "gemm")]:
+    for M, expect in [(1, "decode_dot4"), (4, "skinny"), (16, "skinny"), (17, "skinny"), (64, "skinny"), (65, "gemm"),
+                      (300, "gemm")]:
         Xq, xs, rs = hip_quant(X[:M])
         Y1, a1 = hip_forward(Xq, xs, rs, packed, ws, 384, (0, 0))
         name = bl.last_dispatch()
