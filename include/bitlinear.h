@@ -136,8 +136,9 @@ bitlinear_status bitlinear_quant_act(const float *X, int64_t M, int64_t K,
  * written by bitlinear_pack_weights with the same N, K and nm.  Y: M x N fp32
  * output.  acc: optional M x N int32 output of the exact integer sums (NULL
  * to skip).  The kernel is chosen from the shape: M = 1 (K <= 16384) packed
- * int8 dot products; 2 <= M <= 16 an MFMA kernel with the tokens as one
- * operand (2:4 with K % 128 == 0: the sparse MFMA where it measured faster);
+ * int8 dot products; 2 <= M <= 16 (and up to 64 with few weight rows, in
+ * tiles of 16 tokens) an MFMA kernel with the tokens as one operand (2:4 with
+ * K % 128 == 0 and M <= 16: the sparse MFMA where it measured faster);
  * larger M the MFMA GEMM (K split over workgroups for M <= 64 when the output
  * tiles alone cannot fill the GPU; 2:4 with K % 128 == 0 and M >= 128 on the
  * sparse MFMA; other N:M at M >= 65 on the dense GEMM after expanding the
