@@ -26,14 +26,15 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // TR: the row transform (kTrGate, kTrNorm bits; common.hpp).  Pass 1 forms
 // the transformed row v (and h's sum of squares for the norm) and reduces
 // max|v|; pass 2 forms v again (same operations, same values) and quantises.
-template <int TR>
-__global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
+template <int TR, int BLOCK = kQuantBlock>
+__global__ __launch_bounds__(BLOCK) void quant_act_kernel(
     const float *__restrict__ X, ActTransform tr, int64_t K, int8_t *__restrict__ Xq,
     float *__restrict__ x_scale, int32_t *__restrict__ x_rowsum)
 {
-    __shared__ float s_max[kWaves];
-    __shared__ int s_sum[kWaves];
-    __shared__ double s_ss[kWaves];
+    constexpr int W = BLOCK / 64;
+    __shared__ float s_max[W];
+    __shared__ int s_sum[W];
+    __shared__ double s_ss[W];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const f32x4 *x4 = reinterpret_cast<const f32x4 *>(X + row * K);
@@ -61,7 +62,7 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
 
     float g = 0.0f;
     double ss = 0.0;
-    for (int64_t i = tid; i < n4; i += kQuantBlock) {
+    for (int64_t i = tid; i < n4; i += BLOCK) {
         f32x4 h;
         const f32x4 v = row4(i, h);
         g = fmaxf(g, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
@@ -79,12 +80,12 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
     __syncthreads();
     g = s_max[0];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) g = fmaxf(g, s_max[w]);
+    for (int w = 1; w < W; ++w) g = fmaxf(g, s_max[w]);
 
     int sum = 0;
     const float up = act_prescale(g);
     const float s = act_scale(g, up);        // IEEE binary32 division
-    for (int64_t i = tid; i < n4; i += kQuantBlock) {
+    for (int64_t i = tid; i < n4; i += BLOCK) {
         f32x4 h;
         f32x4 v = row4(i, h);
         if (up != 1.0f) v *= up;              // row-uniform, rare
@@ -98,11 +99,11 @@ __global__ __launch_bounds__(kQuantBlock) void quant_act_kernel(
     if (tid == 0) {
         int total = 0;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) total += s_sum[w];
+        for (int w = 0; w < W; ++w) total += s_sum[w];
         if constexpr ((TR & kTrNorm) != 0) {
             double t = 0.0;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) t += s_ss[w];
+            for (int w = 0; w < W; ++w) t += s_ss[w];
             x_scale[row] = act_norm_scale(g, act_rinv(t, K, tr.eps));
         } else {
             x_scale[row] = (g == 0.0f) ? 0.0f : g / 127.0f;
@@ -419,15 +420,28 @@ hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64
 {
     if (M == 0) return hipSuccess;
     const int t = (tr.up ? kTrGate : 0) | (tr.gamma ? kTrNorm : 0);
-    auto go = [&](auto kern) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(kQuantBlock), 0, stream, X, tr, K, Xq, x_scale,
-                           x_rowsum);
+    // up to a few hundred long rows: 1024 threads per row for the row's
+    // latency (measured with 256: one row of 6912 3.7 -> 2.6 us, 8 and 64
+    // rows of 11008 5.3 -> 3.2-3.4 us; 255 rows of 6912 3.4 us against 4.5
+    // at 256 rows with 256 threads); many rows are bandwidth-bound: 256
+    const bool wide = M <= 512 && K >= 4096;
+    auto go = [&](auto kern, int threads) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(threads), 0, stream, X, tr, K, Xq, x_scale, x_rowsum);
     };
-    switch (t) {
-    case 0: go(quant_act_kernel<0>); break;
-    case kTrGate: go(quant_act_kernel<kTrGate>); break;
-    case kTrNorm: go(quant_act_kernel<kTrNorm>); break;
-    default: go(quant_act_kernel<kTrGate | kTrNorm>); break;
+    if (wide) {
+        switch (t) {
+        case 0: go(quant_act_kernel<0, 1024>, 1024); break;
+        case kTrGate: go(quant_act_kernel<kTrGate, 1024>, 1024); break;
+        case kTrNorm: go(quant_act_kernel<kTrNorm, 1024>, 1024); break;
+        default: go(quant_act_kernel<kTrGate | kTrNorm, 1024>, 1024); break;
+        }
+    } else {
+        switch (t) {
+        case 0: go(quant_act_kernel<0>, kQuantBlock); break;
+        case kTrGate: go(quant_act_kernel<kTrGate>, kQuantBlock); break;
+        case kTrNorm: go(quant_act_kernel<kTrNorm>, kQuantBlock); break;
+        default: go(quant_act_kernel<kTrGate | kTrNorm>, kQuantBlock); break;
+        }
     }
     return hipGetLastError();
 }
