@@ -112,6 +112,69 @@ __global__ __launch_bounds__(BLOCK) void quant_act_kernel(
     }
 }
 
+// The plain quantiser with the row held in registers between its two steps
+// (NV float4 per thread, K <= 4 NV BLOCK): the row is read once, where the
+// two-pass form reads it again (from L2 if it is still there, else from the
+// Infinity Cache or HBM).  Same arithmetic, same results.
+template <int BLOCK, int NV>
+__global__ __launch_bounds__(BLOCK) void quant_act_reg_kernel(const float *__restrict__ X, int64_t K,
+                                                             int8_t *__restrict__ Xq, float *__restrict__ x_scale,
+                                                             int32_t *__restrict__ x_rowsum)
+{
+    constexpr int W = BLOCK / 64;
+    __shared__ float s_max[W];
+    __shared__ int s_sum[W];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(X + row * K);
+    int *q4 = reinterpret_cast<int *>(Xq + row * K);
+    const int64_t n4 = K / 4;
+
+    // every load first (entries past the row re-read its last one and count as 0)
+    f32x4 v[NV];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int64_t i = tid + (int64_t)j * BLOCK;
+        const f32x4 a = x4[i < n4 ? i : n4 - 1];
+        v[j] = (i < n4) ? a : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    }
+    float g = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+        g = fmaxf(g, fmaxf(fmaxf(fabsf(v[j][0]), fabsf(v[j][1])), fmaxf(fabsf(v[j][2]), fabsf(v[j][3]))));
+    g = wave_max_dpp(g);
+    if (lane == 0) s_max[wave] = g;
+    __syncthreads();
+    g = s_max[0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) g = fmaxf(g, s_max[w]);
+
+    int sum = 0;
+    const float up = act_prescale(g);
+    const float s = act_scale(g, up);        // IEEE binary32 division
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int64_t i = tid + (int64_t)j * BLOCK;
+        if (i < n4) {
+            f32x4 a = v[j];
+            if (up != 1.0f) a *= up;          // row-uniform, rare
+            int s4;
+            q4[i] = (int)act_quant4(a[0], a[1], a[2], a[3], s, &s4);
+            sum += s4;
+        }
+    }
+    sum = wave_sum_dpp(sum);
+    if (lane == 0) s_sum[wave] = sum;
+    __syncthreads();
+    if (tid == 0) {
+        int total = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) total += s_sum[w];
+        x_scale[row] = (g == 0.0f) ? 0.0f : g / 127.0f;
+        if (x_rowsum) x_rowsum[row] = total;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // 4-bit activations after an online Hadamard transform (the BitNet v2
 // summary: the H-BitLinear transforms the activations, then quantises them to
@@ -428,6 +491,26 @@ hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64
     auto go = [&](auto kern, int threads) {
         hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(threads), 0, stream, X, tr, K, Xq, x_scale, x_rowsum);
     };
+    if (t == 0) {
+        // the row in registers where it fits: at most 8 (256 threads) or 4
+        // (1024 threads) float4 per thread
+        const int threads = wide ? 1024 : kQuantBlock;
+        const int64_t nv = (K / 4 + threads - 1) / threads;
+        auto reg = [&](auto kern) {
+            hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(threads), 0, stream, X, K, Xq, x_scale, x_rowsum);
+            return hipGetLastError();
+        };
+        if (wide) {
+            if (nv <= 1) return reg(quant_act_reg_kernel<1024, 1>);
+            if (nv <= 2) return reg(quant_act_reg_kernel<1024, 2>);
+            if (nv <= 4) return reg(quant_act_reg_kernel<1024, 4>);
+        } else {
+            if (nv <= 1) return reg(quant_act_reg_kernel<kQuantBlock, 1>);
+            if (nv <= 2) return reg(quant_act_reg_kernel<kQuantBlock, 2>);
+            if (nv <= 4) return reg(quant_act_reg_kernel<kQuantBlock, 4>);
+            if (nv <= 8) return reg(quant_act_reg_kernel<kQuantBlock, 8>);
+        }
+    }
     if (wide) {
         switch (t) {
         case 0: go(quant_act_kernel<0, 1024>, 1024); break;
