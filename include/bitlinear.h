@@ -51,17 +51,13 @@
  *
  * Conventions for every call:
  *   - Data pointers are device pointers (hipMalloc / torch tensors) owned by
- *     the caller.  The one exception is internal: the first
- *     bitlinear_forward call on a device that needs scratch memory allocates
- *     a 64 MB workspace with hipMalloc, once, and keeps it until the process
- *     ends.  Two paths use it: the few-token GEMMs with K split over
- *     workgroups (M <= 64 with too few output tiles to fill the GPU; int32
- *     partial sums) and N:M weights at M >= 65 where the 2:4 sparse MFMA
- *     does not apply (the rows expanded to dense codes, N*K/4 <= 64 MB, for
- *     the dense GEMM).  That first call must not be inside HIP graph capture
- *     (a captured call that finds no workspace uses the unsplit or t-byte
- *     kernel instead, with identical results), and such calls must not
- *     overlap in time on one device (they share the workspace).
+ *     the caller.  The library allocates no device memory and keeps none
+ *     between calls: scratch memory comes from the caller as a workspace
+ *     argument (bitlinear_pack_weights, bitlinear_forward), sized by a
+ *     host-only query (bitlinear_packed_size, bitlinear_forward_workspace_size).
+ *     The kernels a call launches depend on the shapes alone.  A workspace
+ *     belongs to one call until that call's work has finished on its stream;
+ *     calls on different streams need workspaces of their own.
  *   - Matrices are row-major and dense: W is N x K (out x in), X and Xq are
  *     M x K, Y and acc are M x N.
  *   - Work is enqueued on `stream` (NULL = the null stream); no call
@@ -74,7 +70,8 @@
  *     0 <= M <= 16777216.  M == 0 is a successful no-op, and then the
  *     M-sized buffers (X, Xq, x_scale, x_rowsum, Y, acc) may be NULL.
  *   - Alignment: W, X, Xq, packed, Y and acc must be 16-byte aligned;
- *     w_scale, x_scale and x_rowsum 4-byte aligned; workspace 8-byte aligned.
+ *     w_scale, x_scale and x_rowsum 4-byte aligned; the pack workspace 8-byte
+ *     aligned and the forward workspace 16-byte aligned.
  *   - Inputs must be finite; results for NaN/Inf inputs are unspecified.
  */
 #ifndef BITLINEAR_H
@@ -105,50 +102,82 @@ typedef enum {
     BITLINEAR_EHIP = -4          /* a HIP launch or runtime call failed */
 } bitlinear_status;
 
-/* Host-only size query.  *packed_bytes receives the packed-weight size for an
- * N x K matrix under `nm` (layout above); *workspace_bytes the device scratch
- * that bitlinear_pack_weights needs (8*N bytes of binary64 row sums, rounded
- * up to 256).  Either output pointer may be NULL.  Launches nothing. */
+/* Host-only size query for bitlinear_pack_weights.  *packed_bytes receives
+ * the packed-weight size for an N x K matrix under `nm` (2-bit codes, four per
+ * byte: "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 5.1; N:M values
+ * and keep masks: the layout above); *workspace_bytes the device scratch that
+ * bitlinear_pack_weights needs (8*N bytes of binary64 row sums, rounded up to
+ * 256).  Either output pointer may be NULL.  Launches nothing.  Errors:
+ * EUNSUPPORTED for another N:M pattern, EINVAL for N or K out of range. */
 bitlinear_status bitlinear_packed_size(int64_t N, int64_t K, bitlinear_nm nm,
                                        size_t *packed_bytes, size_t *workspace_bytes);
 
-/* Pack time (absmean ternarisation, optional N:M mask, 2-bit packing).
- * W: N x K fp32 latent weights.  packed: packed_bytes-byte output (see the
- * layout).  w_scale: one fp32, receives beta.  workspace: scratch of at least
- * the size bitlinear_packed_size reports; its contents on entry do not matter
- * and on exit are unspecified.  Returns BITLINEAR_ESIZE if packed_bytes or
- * workspace_bytes is too small. */
+/* Pack time: absmean ternarisation ("BitNet 논문 분석: 1-Bit LLM의 시대",
+ * section "Absmean 양자화 함수"; 2B4T summary, sec. 2), the optional N:M
+ * mask with quant-then-mask (Sparse-BitNet review, sec. 3.2) and 2-bit
+ * packing with the I2_S code map ("bitnet.cpp 추론 프레임워크").
+ * W: N x K fp32 latent weights (read only).  packed: packed_bytes-byte output
+ * (see the layout).  w_scale: one fp32, receives beta.  workspace: scratch of
+ * at least the size bitlinear_packed_size reports; its contents on entry do
+ * not matter and on exit are unspecified.  Errors: ESIZE if packed_bytes or
+ * workspace_bytes is too small; EINVAL for a bad shape or a null or
+ * misaligned pointer; EUNSUPPORTED for another N:M pattern. */
 bitlinear_status bitlinear_pack_weights(const float *W, int64_t N, int64_t K, bitlinear_nm nm,
                                         void *packed, size_t packed_bytes, float *w_scale,
                                         void *workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
-/* Per-token absmax int8 quantisation of X (M x K fp32).
- * Xq: M x K int8.  x_scale: M fp32 (g_m / 127).  x_rowsum: M int32 row sums
- * of Xq; may be NULL when not wanted (bitlinear_forward needs it). */
+/* Per-token absmax int8 quantisation of X (M x K fp32): 2B4T summary, sec. 2
+ * (8-bit activations, absmax per token); "BitNet 논문 분석", section
+ * "Absmean 양자화 함수" (activation_quant).  Xq: M x K int8 output.
+ * x_scale: M fp32 (g_m / 127).  x_rowsum: M int32 row sums of Xq; may be NULL
+ * when not wanted (bitlinear_forward needs it).  Errors: EINVAL for a bad
+ * shape or a null or misaligned pointer. */
 bitlinear_status bitlinear_quant_act(const float *X, int64_t M, int64_t K,
                                      int8_t *Xq, float *x_scale, int32_t *x_rowsum,
                                      hipStream_t stream);
 
-/* The forward contraction and rescale.  Xq, x_scale, x_rowsum: as written by
+/* Host-only size query for bitlinear_forward: *workspace_bytes receives the
+ * device scratch that an M x N x K call under `nm` needs (0 for most shapes;
+ * at most 32 MiB for the few-token GEMMs that split K, whose int32 partial
+ * tiles it holds; N*K/4 bytes for N:M weights at 65+ tokens where the 2:4
+ * sparse MFMA does not apply, for the rows expanded to dense codes).
+ * Launches nothing.  Errors: EINVAL for a bad shape or NULL output,
+ * EUNSUPPORTED for another N:M pattern. */
+bitlinear_status bitlinear_forward_workspace_size(int64_t M, int64_t N, int64_t K, bitlinear_nm nm,
+                                                  size_t *workspace_bytes);
+
+/* The forward contraction and rescale: the integer matmul of the ternary
+ * weights and the int8 activations with int32 accumulation, then the
+ * dequantisation by beta and x_scale (2B4T summary, sec. 2 and 5.1; "BitNet
+ * 논문 분석", section "Absmean 양자화 함수", BitLinear's forward; N:M:
+ * Sparse-BitNet review, sec. 3.2).  Xq, x_scale, x_rowsum: as written by
  * bitlinear_quant_act (x_rowsum is required: the kernels accumulate with the
  * unsigned codes c = t + 1 and subtract the row sum).  packed, w_scale: as
  * written by bitlinear_pack_weights with the same N, K and nm.  Y: M x N fp32
  * output.  acc: optional M x N int32 output of the exact integer sums (NULL
- * to skip).  The kernel is chosen from the shape: M = 1 (K <= 16384) packed
- * int8 dot products; 2 <= M <= 16 (and up to 64 with few weight rows, in
- * tiles of 16 tokens) an MFMA kernel with the tokens as one operand (2:4 with
- * K % 128 == 0 and M <= 16: the sparse MFMA where it measured faster);
- * larger M the MFMA GEMM (K split over workgroups for M <= 64 when the output
- * tiles alone cannot fill the GPU; 2:4 with K % 128 == 0 and M >= 128 on the
- * sparse MFMA; other N:M at M >= 65 on the dense GEMM after expanding the
- * rows to dense codes in the library's workspace).  Every path gives the
- * same acc, bit for bit, and the same Y.  bitlinear_last_dispatch() names the
- * kernel. */
+ * to skip).  workspace: device scratch of workspace_bytes bytes, at least
+ * what bitlinear_forward_workspace_size reports for the shape (NULL with 0
+ * when that is 0); its contents on entry do not matter and on exit are
+ * unspecified; it must not be used by other work until this call's work on
+ * `stream` has finished.  The kernel is chosen from the shape: M = 1
+ * (K <= 16384) packed int8 dot products; 2 <= M <= 16 (and up to 64 with few
+ * weight rows, in tiles of 16 tokens) an MFMA kernel with the tokens as one
+ * operand (2:4 with K % 128 == 0 and M <= 16: the sparse MFMA where it
+ * measured faster); larger M the MFMA GEMM (K split over workgroups for
+ * M <= 64 when the output tiles alone cannot fill the GPU; 2:4 with
+ * K % 128 == 0 and M >= 128 on the sparse MFMA; other N:M at M >= 65 on the
+ * dense GEMM after expanding the rows to dense codes in the workspace).
+ * Every path gives the same acc, bit for bit, and the same Y.
+ * bitlinear_last_dispatch() names the kernel.  Errors: ESIZE when the
+ * workspace is smaller than the shape needs (nothing is launched); EINVAL for
+ * a bad shape or a null or misaligned pointer; EUNSUPPORTED for another N:M
+ * pattern; EHIP when a launch fails. */
 bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                                    const void *packed, const float *w_scale, bitlinear_nm nm,
                                    int64_t M, int64_t N, int64_t K,
-                                   float *Y, int32_t *acc, hipStream_t stream);
+                                   float *Y, int32_t *acc, void *workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 /* One projection of a fused decode call: packed weights and beta as written
  * by bitlinear_pack_weights (same K and nm as the call), N output features,
@@ -238,12 +267,18 @@ bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_
 bitlinear_status bitlinear_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t block, int8_t *Xq,
                                         float *x_scale, int32_t *x_rowsum, hipStream_t stream);
 
-/* Thread-local text for the last non-OK status returned on this thread. */
+/* Thread-local text for the last non-OK status returned on this thread (the
+ * errors of a kernel path are part of what a deployment has to check: "BitNet
+ * b1.58은 GPU 없이도 빠를까?", section "전용 커널은 무엇을 비교해야 하나").
+ * Never NULL; the string lives until the thread's next failing call. */
 const char *bitlinear_last_error(void);
 
 /* Thread-local name of the kernel(s) the last successful call on this thread
  * launched, e.g. "decode_dot4_dense_lpr8_u5_p1" or
- * "gemm_dense_dma_256x256_w8_s4"; "none" after an M == 0 no-op. */
+ * "gemm_dense_dma_256x256_w8_s4"; "none" after an M == 0 no-op.  The same
+ * page, section "도입 순서는 어떻게 잡을까", warns that a runtime can drop to
+ * a slow generic path without saying so; this names the path that ran.
+ * Never NULL. */
 const char *bitlinear_last_dispatch(void);
 
 #ifdef __cplusplus

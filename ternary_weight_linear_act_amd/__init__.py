@@ -17,6 +17,7 @@ from .binding import (  # noqa: F401
     quant_act_ex,
     quant_act_h4,
     forward,
+    forward_workspace_size,
     forward_fused,
     forward_fused_ex,
     last_dispatch,

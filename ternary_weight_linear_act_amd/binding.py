@@ -19,12 +19,17 @@ NM_6_8 = (6, 8)
 OK, EINVAL, EUNSUPPORTED, ESIZE, EHIP = 0, -1, -2, -3, -4
 _STATUS = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ESIZE: "ESIZE", EHIP: "EHIP"}
 
+# every entry point include/bitlinear.h declares
 EXPORTED = (
     "bitlinear_packed_size",
     "bitlinear_pack_weights",
     "bitlinear_quant_act",
+    "bitlinear_quant_act_ex",
+    "bitlinear_quant_act_h4",
+    "bitlinear_forward_workspace_size",
     "bitlinear_forward",
     "bitlinear_forward_fused",
+    "bitlinear_forward_fused_ex",
     "bitlinear_last_error",
     "bitlinear_last_dispatch",
 )
@@ -71,16 +76,16 @@ def load_library():
     lib.bitlinear_packed_size.argtypes = [i64, i64, NM, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.bitlinear_pack_weights.argtypes = [vp, i64, i64, NM, vp, sz, vp, vp, sz, vp]
     lib.bitlinear_quant_act.argtypes = [vp, i64, i64, vp, vp, vp, vp]
-    lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp]
+    lib.bitlinear_forward_workspace_size.argtypes = [i64, i64, i64, NM, ctypes.POINTER(sz)]
+    lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.bitlinear_forward_fused.argtypes = [vp, i64, i64, NM, ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     lib.bitlinear_quant_act_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, vp, vp, vp, vp]
     lib.bitlinear_quant_act_h4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
     lib.bitlinear_forward_fused_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, NM,
                                                ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
-    for f in ("bitlinear_packed_size", "bitlinear_pack_weights", "bitlinear_quant_act",
-              "bitlinear_forward", "bitlinear_forward_fused", "bitlinear_quant_act_ex",
-              "bitlinear_forward_fused_ex", "bitlinear_quant_act_h4"):
-        getattr(lib, f).restype = ctypes.c_int
+    for f in EXPORTED:
+        if f not in ("bitlinear_last_error", "bitlinear_last_dispatch"):
+            getattr(lib, f).restype = ctypes.c_int
     lib.bitlinear_last_error.restype = ctypes.c_char_p
     lib.bitlinear_last_dispatch.restype = ctypes.c_char_p
     lib.bitlinear_last_error.argtypes = []
@@ -241,9 +246,22 @@ def quant_act_h4(X, block, Xq=None, x_scale=None, x_rowsum=None, stream=None):
     return Xq, x_scale, x_rowsum
 
 
+def forward_workspace_size(M: int, N: int, K: int, nm=NM_DENSE) -> int:
+    """Device scratch bytes bitlinear_forward needs for an M x N x K call (often 0)."""
+    wb = ctypes.c_size_t(0)
+    _check("bitlinear_forward_workspace_size", load_library().bitlinear_forward_workspace_size(
+        M, N, K, _nm(nm), ctypes.byref(wb)))
+    return wb.value
+
+
 def forward(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=None, acc=None,
-            want_acc=False, stream=None):
-    """Y = (Xq . W_eff^T) * w_scale * x_scale, fp32 M x N.  Returns Y or (Y, acc)."""
+            want_acc=False, workspace=None, stream=None):
+    """Y = (Xq . W_eff^T) * w_scale * x_scale, fp32 M x N.  Returns Y or (Y, acc).
+
+    `workspace`: a uint8 device tensor for the call's scratch; when None, one
+    of the size forward_workspace_size() reports is taken from torch's
+    allocator on the call's device (none when that size is 0).
+    """
     import torch
     _require(Xq, torch.int8, None, "Xq")
     M, K = Xq.shape
@@ -261,9 +279,16 @@ def forward(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=None, acc=
     pb, _ = packed_size(N, K, nm)
     if packed.numel() < pb:
         raise ValueError("packed buffer holds %d bytes, %d needed" % (packed.numel(), pb))
+    if workspace is None:
+        wb = forward_workspace_size(M, N, K, nm)
+        if wb:
+            workspace = torch.empty(wb, dtype=torch.uint8, device=Xq.device)
+    if workspace is not None:
+        _require(workspace, torch.uint8, None, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel()
     _check("bitlinear_forward", load_library().bitlinear_forward(
         _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _ptr(packed), _ptr(w_scale), _nm(nm),
-        M, N, K, _ptr(Y), _ptr(acc), _stream(stream)))
+        M, N, K, _ptr(Y), _ptr(acc), _ptr(workspace), ws_bytes, _stream(stream)))
     return (Y, acc) if (want_acc or acc is not None) else Y
 
 

@@ -20,15 +20,15 @@ hipError_t launch_gemv(const int8_t *Xq, const float *xs, const int32_t *rs, con
                        int32_t *acc, hipStream_t stream);
 hipError_t launch_gemm(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                        const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
-                       int32_t *acc, hipStream_t stream, const char **name);
+                       int32_t *acc, Scratch &scratch, hipStream_t stream, const char **name);
 
 hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                                  const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
-                                 int32_t *acc, hipStream_t stream, const char **name);
+                                 int32_t *acc, hipStream_t stream, const char **name, bool query);
 
 hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
                               int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
-                              const ActTransform &tr, hipStream_t stream, const char **name);
+                              const ActTransform &tr, hipStream_t stream, const char **name, bool query);
 
 // Largest M served by the dot4 GEMV (the fallback when the skinny MFMA kernel
 // has no configuration for the shape); larger M runs on the MFMA GEMM.
@@ -36,9 +36,10 @@ constexpr int64_t kGemvMaxM = 4;
 
 hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                           const uint8_t *packed, const float *w_scale, Pattern p, int64_t M,
-                          int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream,
-                          const char **name)
+                          int64_t N, int64_t K, float *Y, int32_t *acc, Scratch &scratch,
+                          hipStream_t stream, const char **name)
 {
+    const bool query = scratch.query;
     static const char *gemv_names[3] = {"gemv_dense", "gemv_nm24", "gemv_nm68"};
     const int pi = (int)p;
     if (M == 1) {
@@ -50,7 +51,7 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
         one.acc[0] = acc;
         one.N[0] = N;
         const hipError_t e = launch_decode_dot4(nullptr, Xq, x_scale, x_rowsum, M, K, p, one, nullptr,
-                                                ActTransform{nullptr, nullptr, 0.0f}, stream, name);
+                                                ActTransform{nullptr, nullptr, 0.0f}, stream, name, query);
         if (e != hipErrorNotSupported) return e;
     }
     // 2:4 at 2-16 tokens on the sparse MFMA where it measured at least as fast
@@ -59,7 +60,7 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
     // 4.6-5.1 us), and any K past 8 tokens (6912 x 2560 at 16: 7.6 against
     // 10.9 us; 2560 x 6912 at 16: 9.2 against 16.4 us)
     if (p == Pattern::NM24 && M >= 2 && M <= 16 && (K <= 4096 || M > 8)) {
-        const hipError_t e = launch_skinny_nm24_smfmac(Xq, x_scale, packed, w_scale, M, N, K, Y, acc, stream);
+        const hipError_t e = launch_skinny_nm24_smfmac(Xq, x_scale, packed, w_scale, M, N, K, Y, acc, stream, query);
         if (e != hipErrorNotSupported) {
             *name = "skinny_smfmac_nm24";
             return e;
@@ -71,14 +72,15 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
     // (2048 x 11008 at 64 tokens: 10.1 against 17.3 us)
     if (M <= 16 || (M <= kSkinnyMaxM && ((N + 15) / 16) * ((M + 15) / 16) <= 512)) {
         const hipError_t e = launch_skinny_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc,
-                                                   stream, name);
+                                                   stream, name, query);
         if (e != hipErrorNotSupported) return e;
     }
     if (M <= kGemvMaxM) {
         *name = gemv_names[pi];
+        if (query) return hipSuccess;
         return launch_gemv(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc, stream);
     }
-    return launch_gemm(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc, stream, name);
+    return launch_gemm(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc, scratch, stream, name);
 }
 
 }  // namespace bl
@@ -171,6 +173,36 @@ size_t packed_bytes_for(int64_t N, int64_t K, bl::Pattern p)
 }
 
 size_t workspace_bytes_for(int64_t N) { return (size_t)((N * 8 + 255) / 256 * 256); }
+
+// Workspace bytes of a forward call: the dispatch run as a size query.
+size_t forward_need(bl::Pattern p, int64_t M, int64_t N, int64_t K)
+{
+    if (M == 0) return 0;
+    bl::Scratch q;
+    q.query = true;
+    const char *name = "";
+    bl::launch_forward(nullptr, nullptr, nullptr, nullptr, nullptr, p, M, N, K, nullptr, nullptr, q, nullptr,
+                       &name);
+    return q.need;
+}
+
+// The forward launch on validated arguments, with the workspace in
+// `scratch`; a workspace short of what the kernels for this shape use is
+// BITLINEAR_ESIZE, and then nothing has been launched.
+bitlinear_status run_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum, const void *packed,
+                             const float *w_scale, bl::Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
+                             int32_t *acc, bl::Scratch &scratch, hipStream_t stream)
+{
+    const char *name = "";
+    const hipError_t e = bl::launch_forward(Xq, x_scale, x_rowsum, static_cast<const uint8_t *>(packed), w_scale,
+                                            p, M, N, K, Y, acc, scratch, stream, &name);
+    if (scratch.need > scratch.bytes)
+        return fail(BITLINEAR_ESIZE, "workspace has %zu bytes, %zu needed for M = %lld, N = %lld, K = %lld (%s)",
+                    scratch.bytes, scratch.need, (long long)M, (long long)N, (long long)K, name);
+    if (e != hipSuccess) return hip_fail("forward launch", e);
+    set_dispatch(name);
+    return BITLINEAR_OK;
+}
 
 #define CHECK(expr)                                   \
     do {                                              \
@@ -268,9 +300,23 @@ bitlinear_status bitlinear_quant_act_h4(const float *X, int64_t M, int64_t K, in
     return BITLINEAR_OK;
 }
 
+bitlinear_status bitlinear_forward_workspace_size(int64_t M, int64_t N, int64_t K, bitlinear_nm nm,
+                                                  size_t *workspace_bytes)
+{
+    bl::Pattern p;
+    CHECK(check_nm(nm, &p));
+    CHECK(check_m(M));
+    CHECK(check_n(N));
+    CHECK(check_k(K));
+    if (!workspace_bytes) return fail(BITLINEAR_EINVAL, "workspace_bytes must not be NULL");
+    *workspace_bytes = forward_need(p, M, N, K);
+    return BITLINEAR_OK;
+}
+
 bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                                    const void *packed, const float *w_scale, bitlinear_nm nm, int64_t M,
-                                   int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
+                                   int64_t N, int64_t K, float *Y, int32_t *acc, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream)
 {
     bl::Pattern p;
     CHECK(check_nm(nm, &p));
@@ -285,12 +331,11 @@ bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const
     CHECK(check_ptr(x_rowsum, 4, "x_rowsum"));
     CHECK(check_ptr(Y, 16, "Y"));
     if (acc && !aligned(acc, 16)) return fail(BITLINEAR_EINVAL, "acc must be 16-byte aligned");
-    const char *name = "";
-    hipError_t e = bl::launch_forward(Xq, x_scale, x_rowsum, static_cast<const uint8_t *>(packed), w_scale, p,
-                                      M, N, K, Y, acc, stream, &name);
-    if (e != hipSuccess) return hip_fail("forward launch", e);
-    set_dispatch(name);
-    return BITLINEAR_OK;
+    if (workspace && !aligned(workspace, 16)) return fail(BITLINEAR_EINVAL, "workspace must be 16-byte aligned");
+    bl::Scratch scratch;
+    scratch.ptr = static_cast<uint8_t *>(workspace);
+    scratch.bytes = workspace ? workspace_bytes : 0;
+    return run_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc, scratch, stream);
 }
 
 bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, bitlinear_nm nm,
@@ -334,7 +379,8 @@ bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_
     CHECK(check_ptr(X, 16, "X"));
     if (x_scale && !aligned(x_scale, 4)) return fail(BITLINEAR_EINVAL, "x_scale must be 4-byte aligned");
     const char *name = "";
-    hipError_t e = bl::launch_decode_dot4(X, nullptr, nullptr, nullptr, M, K, p, args, x_scale, t, stream, &name);
+    hipError_t e = bl::launch_decode_dot4(X, nullptr, nullptr, nullptr, M, K, p, args, x_scale, t, stream, &name,
+                                          false);
     if (e == hipErrorNotSupported && transformed)
         return fail(BITLINEAR_EUNSUPPORTED, "fused decode with a row transform supports M == 1 and K <= 16384 "
                     "(M = %lld, K = %lld)", (long long)M, (long long)K);

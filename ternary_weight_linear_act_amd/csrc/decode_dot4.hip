@@ -18,10 +18,11 @@ thread_local char g_name[64];
 // 320 workgroups (gate+up of a 2B FFN: 432 -> 216, 4.1 -> 4.0 us), except
 // with a row transform, where 4 waves measured faster (RMSNorm on gate+up
 // 5.35 -> 5.13 us).  Returns hipErrorNotSupported when M != 1 or K is too
-// large.
+// large.  With `query` set, launches nothing and returns hipSuccess where it
+// would launch.
 hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
                               int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
-                              const ActTransform &tr, hipStream_t stream, const char **name)
+                              const ActTransform &tr, hipStream_t stream, const char **name, bool query)
 {
     if (M != 1 || K > dot4::kMaxK || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
     const int64_t C = K / 64;
@@ -65,6 +66,7 @@ hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs,
              p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", lpr, u, args.nproj,
              w8 ? "_w8" : "", trn[trb]);
     *name = g_name;
+    if (query) return hipSuccess;
     f(dim3((unsigned)blocks), (size_t)K, stream, X, Xq, xs, rs, K, args, x_scale_out, tr);
     return hipGetLastError();
 }

@@ -33,7 +33,6 @@
 // instead gives each XCD one block of a 4 x 2 partition of the tile grid when
 // the grid allows it.
 #include <algorithm>
-#include <mutex>
 #include <string_view>
 #include <type_traits>
 
@@ -724,27 +723,10 @@ hipError_t launch_dma(const int8_t *Xq, const float *xs, const int32_t *rs, cons
     return hipGetLastError();
 }
 
-// Split-K workspace of the few-token GEMM (int32 partial tiles): one per
-// device, created on the first call that needs it (never inside graph
-// capture: such a call falls back to the unsplit kernel), then kept for the
-// life of the process.  Calls that use it must not overlap on one device.
-constexpr int64_t kWorkspaceBytes = 64ll << 20;
-
-int32_t *split_workspace(hipStream_t stream)
-{
-    static std::mutex mu;
-    static int32_t *per_device[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
-    std::lock_guard<std::mutex> lock(mu);
-    if (per_device[dev]) return per_device[dev];
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-    void *p = nullptr;
-    if (hipMalloc(&p, (size_t)kWorkspaceBytes) != hipSuccess) return nullptr;
-    per_device[dev] = static_cast<int32_t *>(p);
-    return per_device[dev];
-}
+// Largest split-K partial-sum area (int32 partial tiles) a few-token GEMM
+// takes from the caller's workspace: bounds the splits, so the workspace of
+// such a call stays within 32 MiB.
+constexpr int64_t kMaxSplitBytes = 32ll << 20;
 
 // Few tokens (dense, M <= 64): BM x BN tiles over a deep ring, K split over
 // enough workgroups to occupy every compute unit (none when the tiles alone
@@ -752,23 +734,23 @@ int32_t *split_workspace(hipStream_t stream)
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_few_tokens(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                              const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                             hipStream_t stream, const char **name, const char *split_name, const char *plain_name)
+                             Scratch &scratch, hipStream_t stream, const char **name, const char *split_name,
+                             const char *plain_name)
 {
     constexpr int S = 8;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t slices = K / BK;
     int64_t splits = std::min<int64_t>((kCus + tiles - 1) / tiles, slices / 4);   // >= 4 slices each
     const int64_t per_split = tiles * (int64_t)BM * BN * 4;        // partial bytes per split
-    splits = std::min<int64_t>(splits, kWorkspaceBytes / per_split);
+    splits = std::min<int64_t>(splits, kMaxSplitBytes / per_split);
     if (splits >= 2) {
-        int32_t *w = split_workspace(stream);
-        if (w) {
-            *name = split_name;
-            return launch_dma<BM, BN, WM, WN, S, true>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream,
-                                                       (int32_t)splits, w);
-        }
+        *name = split_name;
+        if (!scratch.take((size_t)(splits * per_split))) return scratch.query ? hipSuccess : hipErrorOutOfMemory;
+        return launch_dma<BM, BN, WM, WN, S, true>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream,
+                                                   (int32_t)splits, reinterpret_cast<int32_t *>(scratch.ptr));
     }
     *name = plain_name;
+    if (scratch.query) return hipSuccess;
     return launch_dma<BM, BN, WM, WN, S, false>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
 }
 
@@ -780,17 +762,17 @@ hipError_t launch_few_tokens(const int8_t *Xq, const float *xs, const int32_t *r
 template <Pattern P, int BM, int BN, int WM, int WN>
 hipError_t launch_tbytes_split(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                                const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                               hipStream_t stream)
+                               Scratch &scratch, hipStream_t stream)
 {
     if (K > kTBytesMaxK) return hipErrorNotSupported;
     const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
     const int64_t slices = K / BK;
     int64_t splits = std::min<int64_t>((kCus + tiles - 1) / tiles, slices / 4);   // >= 4 slices each
     const int64_t per_split = tiles * (int64_t)BM * BN * 4;
-    splits = std::min<int64_t>(splits, kWorkspaceBytes / per_split);
+    splits = std::min<int64_t>(splits, kMaxSplitBytes / per_split);
     if (splits < 2) return hipErrorNotSupported;
-    int32_t *w = split_workspace(stream);
-    if (!w) return hipErrorNotSupported;
+    if (!scratch.take((size_t)(splits * per_split))) return scratch.query ? hipSuccess : hipErrorOutOfMemory;
+    int32_t *w = reinterpret_cast<int32_t *>(scratch.ptr);
     const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
     hipLaunchKernelGGL((gemm_kernel<P, BM, BN, WM, WN, true, true>), dim3((unsigned)(per_xcd * kXcds * splits)),
                        dim3(64 * WM * WN), 0, stream, Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, (int32_t)splits,
@@ -834,7 +816,7 @@ namespace {
 template <Pattern P>
 hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                     const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                    hipStream_t stream, const char **name)
+                    Scratch &scratch, hipStream_t stream, const char **name)
 {
     static const char *names[2][3][3] = {
         {{"", "", ""},
@@ -863,13 +845,16 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
                 // us, 4096 x 8192 x 4096 124 -> 120 us against four; the
                 // smaller tiles measured slower with more than four
                 *name = "gemm_dense_dma_256x256_w8_s6";
+                if (scratch.query) return hipSuccess;
                 return launch_dma<256, 256, 2, 4, 6>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
             }
             if (c12 <= c128) {
                 *name = "gemm_dense_dma_128x256_w8_s4";
+                if (scratch.query) return hipSuccess;
                 return launch_dma<128, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
             }
             *name = "gemm_dense_dma_128x128_w4_s4";
+            if (scratch.query) return hipSuccess;
             return launch_dma<128, 128, 2, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
         // narrow weight tiles: more workgroups from N, so fewer K splits (none
@@ -881,47 +866,48 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
         const bool narrow = K <= 4096 || N >= 32 * kCus;
         if (M <= 32) {
             if (narrow)
-                return launch_few_tokens<32, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+                return launch_few_tokens<32, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
                                                        "gemm_dense_splitk_32x32", "gemm_dense_dma_32x32");
-            return launch_few_tokens<32, 64, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+            return launch_few_tokens<32, 64, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
                                                    "gemm_dense_splitk_32x64", "gemm_dense_dma_32x64");
         }
         if (narrow)
-            return launch_few_tokens<64, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+            return launch_few_tokens<64, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
                                                    "gemm_dense_splitk_64x32", "gemm_dense_dma_64x32");
-        return launch_few_tokens<64, 64, 2, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name,
+        return launch_few_tokens<64, 64, 2, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
                                                "gemm_dense_splitk_64x64", "gemm_dense_dma_64x64");
     } else {
         // 65+ tokens where the sparse MFMA does not apply (6:8; 2:4 below 128
         // tokens or with K % 128 != 0): expand the rows to dense codes once
-        // into the workspace, then the pipelined dense GEMM.  Measured against
-        // the t-byte GEMM, 6:8 (dense beside it): 2048 x 6912 x 2560 70 ->
-        // 52 us (48), 4096 x 8192 x 4096 218 -> 141 us (137), 2048 x 2560 x
-        // 6912 88 -> 59 us (54), 128 x 8960 x 1536 18.0 -> 16.7 us (11.7).
-        // The workspace is shared with the few-token split-K path, which
-        // never runs in the same call (M <= 64).
+        // into the caller's workspace, then the pipelined dense GEMM.
+        // Measured against the t-byte GEMM, 6:8 (dense beside it): 2048 x
+        // 6912 x 2560 70 -> 52 us (48), 4096 x 8192 x 4096 218 -> 141 us
+        // (137), 2048 x 2560 x 6912 88 -> 59 us (54), 128 x 8960 x 1536 18.0
+        // -> 16.7 us (11.7).
         const bool sparse24 = P == Pattern::NM24 && M >= 128 && K % 128 == 0;
-        if (M > 64 && !sparse24 && N * (K / 4) <= kWorkspaceBytes) {
-            int32_t *w = split_workspace(stream);
-            if (w) {
-                static const char *expand_names[3][3] = {
-                    {"", "", ""},
-                    {"gemm_nm24_expand_dense_256x256", "gemm_nm24_expand_dense_128x256",
-                     "gemm_nm24_expand_dense_128x128"},
-                    {"gemm_nm68_expand_dense_256x256", "gemm_nm68_expand_dense_128x256",
-                     "gemm_nm68_expand_dense_128x128"}};
+        if (M > 64 && !sparse24) {
+            static const char *expand_names[3][3] = {
+                {"", "", ""},
+                {"gemm_nm24_expand_dense_256x256", "gemm_nm24_expand_dense_128x256", "gemm_nm24_expand_dense_128x128"},
+                {"gemm_nm68_expand_dense_256x256", "gemm_nm68_expand_dense_128x256", "gemm_nm68_expand_dense_128x128"}};
+            const bool go = scratch.take((size_t)N * (size_t)(K / 4));
+            if (!go && !scratch.query) return hipErrorOutOfMemory;
+            if (go) {
                 const int64_t chunks = N * (K / 64);
                 hipLaunchKernelGGL(nm_expand_dense_kernel<P>, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
-                                   stream, packed, N, K, reinterpret_cast<uint8_t *>(w));
-                hipError_t e = hipGetLastError();
+                                   stream, packed, N, K, scratch.ptr);
+                const hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
-                const char *dn = "";
-                e = dispatch<Pattern::Dense>(Xq, xs, rs, reinterpret_cast<const uint8_t *>(w), w_scale, M, N, K, Y,
-                                             acc, stream, &dn);
-                const std::string_view d(dn);
-                *name = expand_names[pi][d.find("256x256") != d.npos ? 0 : d.find("128x256") != d.npos ? 1 : 2];
-                return e;
             }
+            // the dense GEMM at 65+ tokens uses no workspace of its own
+            Scratch dense_scratch;
+            dense_scratch.query = scratch.query;
+            const char *dn = "";
+            const hipError_t e = dispatch<Pattern::Dense>(Xq, xs, rs, scratch.ptr, w_scale, M, N, K, Y, acc,
+                                                          dense_scratch, stream, &dn);
+            const std::string_view d(dn);
+            *name = expand_names[pi][d.find("256x256") != d.npos ? 0 : d.find("128x256") != d.npos ? 1 : 2];
+            return e;
         }
         if constexpr (P == Pattern::NM24) {
             // 2:4 on the sparse matrix cores (gemm_sparse.hip) where K allows;
@@ -936,14 +922,17 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
                 auto rounds = [&](int64_t t) { return (double)((t + kCus - 1) / kCus); };
                 if (4.0 * rounds(tiles(256, 256)) <= 2.0 * rounds(tiles(128, 256))) {
                     *name = "gemm_nm24_smfmac_256x256";
+                    if (scratch.query) return hipSuccess;
                     return launch_gemm_nm24_sparse(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream, 256);
                 }
                 *name = "gemm_nm24_smfmac_128x256";
+                if (scratch.query) return hipSuccess;
                 return launch_gemm_nm24_sparse(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream, 128);
             }
         }
         if (M >= 256 && tiles(256, 256) >= 128) {
             *name = names[tb][pi][0];
+            if (scratch.query) return hipSuccess;
             return launch<P, 256, 256, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
         // too few tiles for the chip: K split (t-byte form); measured at 32 and
@@ -953,21 +942,23 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
             {"gemm_nm68_splitk_128x128_tbytes", "gemm_nm68_splitk_64x128_tbytes"}};
         if (M > 64) {
             const hipError_t e = launch_tbytes_split<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc,
-                                                                        stream);
+                                                                        scratch, stream);
             if (e != hipErrorNotSupported) {
                 *name = split_names[pi][0];
                 return e;
             }
             *name = names[tb][pi][1];
+            if (scratch.query) return hipSuccess;
             return launch<P, 128, 128, 2, 2>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
         const hipError_t e = launch_tbytes_split<P, 64, 128, 1, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc,
-                                                                   stream);
+                                                                   scratch, stream);
         if (e != hipErrorNotSupported) {
             *name = split_names[pi][1];
             return e;
         }
         *name = names[tb][pi][2];
+        if (scratch.query) return hipSuccess;
         return launch<P, 64, 128, 1, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
     }
 }
@@ -976,12 +967,15 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
 
 hipError_t launch_gemm(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                        const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
-                       int32_t *acc, hipStream_t stream, const char **name)
+                       int32_t *acc, Scratch &scratch, hipStream_t stream, const char **name)
 {
     switch (p) {
-    case Pattern::Dense: return dispatch<Pattern::Dense>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name);
-    case Pattern::NM24: return dispatch<Pattern::NM24>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name);
-    case Pattern::NM68: return dispatch<Pattern::NM68>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream, name);
+    case Pattern::Dense:
+        return dispatch<Pattern::Dense>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name);
+    case Pattern::NM24:
+        return dispatch<Pattern::NM24>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name);
+    case Pattern::NM68:
+        return dispatch<Pattern::NM68>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name);
     }
     return hipErrorInvalidValue;
 }

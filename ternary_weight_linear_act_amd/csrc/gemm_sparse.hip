@@ -373,11 +373,13 @@ __global__ __launch_bounds__(1024) void skinny_nm24_smfmac_kernel(
 
 template <int U>
 hipError_t launch_skinny_sparse(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
-                                int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
+                                int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream,
+                                bool query)
 {
     const int64_t T = K / 128;
     const int64_t KS = (T + U - 1) / U;
     if (KS > 16) return hipErrorNotSupported;
+    if (query) return hipSuccess;
     hipLaunchKernelGGL(skinny_nm24_smfmac_kernel<U>, dim3((unsigned)((N + 15) / 16)), dim3((unsigned)(64 * KS)), 0,
                        stream, Xq, xs, packed, w_scale, M, N, K, Y, acc);
     return hipGetLastError();
@@ -402,13 +404,15 @@ hipError_t launch_sparse(const int8_t *Xq, const float *xs, const uint8_t *packe
 
 // 2:4 weights at 1 <= M <= 16 tokens, K % 128 == 0 and K <= 16384;
 // hipErrorNotSupported otherwise.  At most 4 steps of 128 per wave up to
-// K = 8192 (16 waves), 8 beyond (measured: 4 is as fast or faster).
+// K = 8192 (16 waves), 8 beyond (measured: 4 is as fast or faster).  With
+// `query` set, launches nothing and returns hipSuccess where it would launch.
 hipError_t launch_skinny_nm24_smfmac(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
-                                     int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
+                                     int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream,
+                                     bool query)
 {
     if (K % 128 != 0 || M < 1 || M > 16 || K > 16384) return hipErrorNotSupported;
-    if (K <= 8192) return launch_skinny_sparse<4>(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream);
-    return launch_skinny_sparse<8>(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream);
+    if (K <= 8192) return launch_skinny_sparse<4>(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream, query);
+    return launch_skinny_sparse<8>(Xq, xs, packed, w_scale, M, N, K, Y, acc, stream, query);
 }
 
 // 2:4 weights, K % 128 == 0; hipErrorNotSupported otherwise.  tile_m: 256

@@ -15,13 +15,34 @@ hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, fl
 hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64_t K, int8_t *Xq,
                                float *x_scale, int32_t *x_rowsum, hipStream_t stream);
 
+// Device scratch of one forward call: the caller's workspace (int32 split-K
+// partial tiles; N:M rows expanded to dense codes).  The kernel choice is a
+// function of the shape alone; `take` is called by a launcher before its
+// first launch with the bytes its kernels use.  In a size query nothing is
+// launched and `need` collects the bytes.
+struct Scratch {
+    uint8_t *ptr = nullptr;   // device memory, 16-byte aligned (may be null)
+    size_t bytes = 0;         // bytes at ptr
+    bool query = false;       // size query: launch nothing
+    size_t need = 0;          // bytes the chosen kernels use
+
+    // Records the need; true when the launcher may go on and launch (not a
+    // size query, and the workspace is large enough).
+    bool take(size_t n)
+    {
+        if (n > need) need = n;
+        return !query && n <= bytes;
+    }
+};
+
 // Largest token count of the skinny MFMA forward (tiles of 16 tokens past 16).
 constexpr int64_t kSkinnyMaxM = 64;
 
 // 2:4 weights at 1-16 tokens on the sparse MFMA (K % 128 == 0, K <= 16384;
 // hipErrorNotSupported otherwise).
 hipError_t launch_skinny_nm24_smfmac(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,
-                                     int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream);
+                                     int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream,
+                                     bool query);
 
 // H-BitLinear activations: block Hadamard transform (block B, a power of two
 // <= 8192 dividing K), then 4-bit absmax codes in int8.
@@ -36,10 +57,13 @@ hipError_t launch_absmean(const float *W, int64_t N, int64_t K, double *rowsum, 
 hipError_t launch_pack(const float *W, int64_t N, int64_t K, Pattern p, const float *w_scale,
                        uint8_t *packed, hipStream_t stream);
 
-// Forward.  Returns the name of the kernel variant in *name.
+// Forward.  Returns the name of the kernel variant in *name.  With
+// scratch.query set nothing is launched and scratch.need receives the
+// workspace bytes; otherwise a workspace smaller than the chosen kernels need
+// makes it return hipErrorOutOfMemory before anything is launched.
 hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                           const uint8_t *packed, const float *w_scale, Pattern p, int64_t M,
-                          int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream,
-                          const char **name);
+                          int64_t N, int64_t K, float *Y, int32_t *acc, Scratch &scratch,
+                          hipStream_t stream, const char **name);
 
 }  // namespace bl

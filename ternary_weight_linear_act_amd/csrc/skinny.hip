@@ -82,10 +82,11 @@ thread_local char g_name[64];
 }  // namespace
 
 // Returns hipErrorNotSupported (and launches nothing) when no configuration
-// fits the shape; the caller then uses another kernel.
+// fits the shape; the caller then uses another kernel.  With `query` set,
+// launches nothing and returns hipSuccess where it would launch.
 hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                                  const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
-                                 int32_t *acc, hipStream_t stream, const char **name)
+                                 int32_t *acc, hipStream_t stream, const char **name, bool query)
 {
     if (M < 1 || M > kSkinnyMaxM) return hipErrorNotSupported;
     // token rows staged per wave: 1, 4, 8 or 16 (rows past M read a zero
@@ -122,6 +123,7 @@ hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_
         snprintf(g_name, sizeof g_name, "skinny_mfma_%s_ks%d_c%d_mt%d",
                  p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", ks, kCM[cmi], mt);
         *name = g_name;
+        if (query) return hipSuccess;
         return f(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
     }
     return hipErrorNotSupported;

@@ -34,12 +34,25 @@ def hip_forward(Xq, xs, rs, packed, ws, N, nm):
     return bl.forward(Xq, xs, rs, packed, ws, N, nm, want_acc=True)
 
 
-def sample_rows(M, k=16, seed=0):
-    if M <= k:
+def cover_rows(M):
+    """Rows compared at full size: every row up to 64 tokens; beyond, rows
+    chosen so that every 32-row block of the output (and so every tile of any
+    kernel here: 32 to 256 rows, the XCD regions of the tile grid) holds at
+    least one, all 32 residues mod 32 (the row positions inside an MFMA
+    fragment) occur, and the first and last rows are included."""
+    if M <= 64:
         return np.arange(M)
-    rng = np.random.default_rng(seed)
-    mid = rng.choice(np.arange(1, M - 1), size=k - 2, replace=False)
-    return np.unique(np.concatenate([[0, M - 1], mid]))
+    blocks = -(-M // 32)
+    per = -(-32 // blocks)                 # rows per block so that the residues cover 0..31
+    rows = [0, M - 1]
+    for i in range(blocks):
+        for j in range(per):
+            r = 32 * i + (i * per + j) % 32
+            if r < M:
+                rows.append(r)
+    # a ragged last block can drop residues: take those from the first block
+    rows += [r for r in range(32) if r not in {x % 32 for x in rows}]
+    return np.unique(np.array(rows))
 
 
 def check_y(Yg, Yo, acc_o):

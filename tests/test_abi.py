@@ -29,11 +29,14 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
+    from ternary_weight_linear_act_amd import binding
     for want in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward",
                  "bitlinear_packed_size", "bitlinear_last_error", "bitlinear_last_dispatch",
                  "bitlinear_forward_fused", "bitlinear_quant_act_ex", "bitlinear_forward_fused_ex",
-                 "bitlinear_quant_act_h4"):
+                 "bitlinear_quant_act_h4", "bitlinear_forward_workspace_size"):
         assert want in names
+    # the binding's list is the header's
+    assert sorted(binding.EXPORTED) == names
 
 
 def test_exports_every_declared_symbol(lib):
@@ -44,6 +47,17 @@ def test_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
+
+
+def test_library_allocates_no_device_memory():
+    # the caller owns every buffer: the library imports no HIP allocator
+    from ternary_weight_linear_act_amd import binding
+    out = subprocess.run(["nm", "-D", "--undefined-only", binding.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    imported = set(re.findall(r"\bU\s+(\S+)", out))
+    for name in ("hipMalloc", "hipFree", "hipMallocAsync", "hipExtMallocWithFlags", "hipMallocManaged",
+                 "hipHostMalloc", "hipMallocPitch"):
+        assert not any(i.split("@")[0] == name for i in imported), name
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -103,7 +117,7 @@ def test_forward_validation(lib):
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["Xq"], a["xs"], a["rs"], a["packed"], a["ws"], a["nm"], a["M"], a["N"], a["K"], a["Y"],
-                 a["acc"], None)
+                 a["acc"], a.get("work"), a.get("work_bytes", 0), None)
 
     assert call(Xq=None) == -1
     assert call(rs=None) == -1                # the row sums are required
@@ -120,6 +134,52 @@ def test_forward_validation(lib):
     assert lib.bitlinear_last_dispatch() == b"none"
     assert call(M=0, Xq=None, xs=None, rs=None, Y=None) == 0     # M-sized buffers may be NULL
     assert call(M=0, packed=None) == -1
+    assert call(work=P(8), work_bytes=1 << 20) == -1     # misaligned workspace
+
+
+def work_size(lib, M, N, K, nm):
+    from ternary_weight_linear_act_amd.binding import NM
+    wb = ctypes.c_size_t(12345)
+    st = lib.bitlinear_forward_workspace_size(M, N, K, NM(*nm), ctypes.byref(wb))
+    return st, wb.value
+
+
+def test_forward_workspace_size(lib):
+    # no scratch: one token, the skinny kernels, the prefill tiles, the 2:4
+    # sparse MFMA
+    for (M, N, K, nm) in [(1, 6912, 2560, (0, 0)), (1, 2560, 6912, (6, 8)), (8, 2048, 11008, (0, 0)),
+                          (64, 2048, 2048, (2, 4)), (2048, 6912, 2560, (0, 0)), (2048, 6912, 2560, (2, 4)),
+                          (0, 6912, 2560, (6, 8))]:
+        assert work_size(lib, M, N, K, nm) == (0, 0), (M, N, K, nm)
+    # N:M rows expanded to dense codes at 65+ tokens off the sparse MFMA:
+    # N * K / 4 bytes
+    assert work_size(lib, 512, 8960, 1536, (6, 8)) == (0, 8960 * 1536 // 4)
+    assert work_size(lib, 100, 4100, 192, (2, 4)) == (0, 4100 * 192 // 4)
+    # a few-token GEMM splitting K: 64 x 64 tiles (K > 4096, N < 8192), 64
+    # tiles, 4 splits of 64 * 64 * 64 int32 partials
+    assert work_size(lib, 40, 4096, 8192, (0, 0)) == (0, 4 * 64 * 64 * 64 * 4)
+    # split partials stay within 32 MiB
+    for M in (17, 33, 64):
+        for N in (8192, 30000):
+            st, wb = work_size(lib, M, N, 2048, (0, 0))
+            assert st == 0 and wb <= 32 << 20
+    assert work_size(lib, 4, 64, 100, (0, 0))[0] == -1        # K % 64
+    assert work_size(lib, 4, 64, 128, (3, 4))[0] == -2
+    from ternary_weight_linear_act_amd.binding import NM
+    assert lib.bitlinear_forward_workspace_size(4, 64, 128, NM(0, 0), None) == -1
+
+
+def test_forward_short_workspace_is_rejected_on_the_host(lib):
+    # ESIZE before anything is launched: fake device addresses are never
+    # touched
+    from ternary_weight_linear_act_amd.binding import NM
+    f = lib.bitlinear_forward
+    need = work_size(lib, 512, 8960, 1536, (6, 8))[1]
+    assert f(P(), P(), P(), P(), P(), NM(6, 8), 512, 8960, 1536, P(), None, P(), need - 1, None) == -3
+    assert b"needed" in lib.bitlinear_last_error()
+    assert f(P(), P(), P(), P(), P(), NM(6, 8), 512, 8960, 1536, P(), None, None, 0, None) == -3
+    need = work_size(lib, 40, 4096, 8192, (0, 0))[1]
+    assert f(P(), P(), P(), P(), P(), NM(0, 0), 40, 4096, 8192, P(), None, P(), need - 16, None) == -3
 
 
 def test_quant_validation(lib):

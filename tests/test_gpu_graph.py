@@ -9,8 +9,8 @@ than holding values from capture.  Covered: quant_act + forward (dense, 2:4,
 6:8; one token, the few-token split-K kernel, the prefill tiles, the sparse
 MFMA GEMM), the fused one-token launch with and without a row transform, the
 fused 2-4-token launch, quant_act_ex and the H-BitLinear quantiser.  And, in a
-fresh process, forward calls captured before the library's workspace exists
-(the paths that need none, same bits as the eager calls afterwards)."""
+fresh process, forward calls captured before any eager call: the same kernels
+and the same bits as the eager calls afterwards."""
 import numpy as np
 import pytest
 
@@ -146,6 +146,8 @@ import numpy as np
 import torch
 import ternary_weight_linear_act_amd as bl
 from ternary_weight_linear_act_amd import workloads
+# a 6:8 prefill (rows expanded in the workspace) and a few-token GEMM with K
+# split over workgroups (partial sums in the workspace)
 cases = [(512, 8960, 1536, (6, 8)), (20, 4096, 6912, (0, 0))]
 dev = torch.device("cuda:0")
 prep = []
@@ -155,6 +157,7 @@ for M, N, K, nm in cases:
     Xq, xs, rs = bl.quant_act(torch.from_numpy(X).to(dev))
     prep.append((M, N, K, nm, pk, ws, Xq, xs, rs, torch.empty((M, N), dtype=torch.float32, device=dev),
                  torch.empty((M, N), dtype=torch.int32, device=dev)))
+    assert bl.forward_workspace_size(M, N, K, nm) > 0
 torch.cuda.synchronize()
 s = torch.cuda.Stream()
 s.wait_stream(torch.cuda.current_stream())
@@ -172,17 +175,18 @@ for i, (M, N, K, nm, pk, ws, Xq, xs, rs, Y, acc) in enumerate(prep):
     eager = bl.last_dispatch()
     torch.cuda.synchronize()
     print("case", M, N, K, nm, "captured:", names[i], "eager:", eager, flush=True)
-    assert names[i] != eager, "the captured call should not find the workspace"
+    assert names[i] == eager, "the captured call took another kernel"
+    assert "splitk" in eager or "expand" in eager, eager
     assert torch.equal(ag, ae) and torch.equal(Yg, Ye)
 print("ok", flush=True)
 '''
 
 
-def test_graph_capture_before_workspace():
-    # in a fresh process, forward calls captured before the library's
-    # workspace exists take the paths that need none (the t-byte GEMM for
-    # 6:8 prefill, the unsplit few-token GEMM) and give the same bits as the
-    # eager calls made afterwards (expanded rows, split K)
+def test_graph_first_call_same_kernel():
+    # in a fresh process, forward calls captured before any eager call take
+    # the same kernels as the eager calls made afterwards (the kernel choice
+    # depends on the shape alone; the workspace comes from the caller, here
+    # torch's graph pool) and give the same bits
     import os
     import subprocess
     import sys

@@ -10,7 +10,7 @@ import pytest
 
 from ternary_weight_linear_act_amd import workloads
 
-from gpu_helpers import full_check, hip_forward, hip_pack, hip_quant, sample_rows, to_dev
+from gpu_helpers import cover_rows, full_check, hip_forward, hip_pack, hip_quant, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -30,16 +30,32 @@ def test_decode_ffn_2b(proj):
     full_check(d.W[proj], d.X[(proj, 1)], label="decode_ffn_2b/" + proj)
 
 
-def test_prefill_2048_sampled_rows():
+def test_prefill_2048_covering_rows():
+    # every 256-row tile and every MFMA fragment row position of the full-size
+    # prefill, in the kernel bench.py times
+    import ternary_weight_linear_act_amd as bl
     d = workloads.draw("prefill_2048")
-    full_check(d.W["up"], d.X[("up", 2048)], rows=sample_rows(2048, 16), label="prefill_2048")
+    full_check(d.W["up"], d.X[("up", 2048)], rows=cover_rows(2048), label="prefill_2048")
+    assert bl.last_dispatch() == "gemm_dense_dma_256x256_w8_s6", bl.last_dispatch()
+
+
+@pytest.mark.parametrize("nm,K,kernel", [((0, 0), 64, "gemm_dense_dma_256x256_w8_s6"),
+                                         ((2, 4), 128, "gemm_nm24_smfmac_256x256"),
+                                         ((6, 8), 64, "gemm_nm68_expand_dense_256x256")])
+def test_prefill_2048_grid_all_rows(nm, K, kernel):
+    # the exact tile grid of the 2048 x 6912 prefill (216 tiles of 256 x 256,
+    # the 4 x 2 XCD regions) at small K, every output compared with the oracle
+    import ternary_weight_linear_act_amd as bl
+    W, X = workloads.small_case(4100 + K, 2048, 6912, K, outlier_frac=0.001)
+    full_check(W, X, nm, label="prefill-grid-all-rows")
+    assert bl.last_dispatch() == kernel, bl.last_dispatch()
 
 
 @pytest.mark.parametrize("proj,nm", [("dense", (0, 0)), ("nm24", (2, 4)), ("nm68", (6, 8))])
 def test_sparse_ffn_1p5b(proj, nm):
     d = workloads.draw("sparse_ffn_1p5b", projs=[proj])
     full_check(d.W[proj], d.X[(proj, 1)], nm, label="sparse_ffn_1p5b/%s/M1" % proj)
-    full_check(d.W[proj], d.X[(proj, 512)], nm, rows=sample_rows(512, 16, seed=1),
+    full_check(d.W[proj], d.X[(proj, 512)], nm, rows=cover_rows(512),
                label="sparse_ffn_1p5b/%s/M512" % proj)
 
 
@@ -47,7 +63,7 @@ def test_sparse_ffn_1p5b(proj, nm):
 def test_block_3b(proj):
     d = workloads.draw("block_3b", projs=[proj])
     for M in (1, 8, 64):
-        full_check(d.W[proj], d.X[(proj, M)], rows=sample_rows(M, 24), label="block_3b/%s/M%d" % (proj, M))
+        full_check(d.W[proj], d.X[(proj, M)], rows=cover_rows(M), label="block_3b/%s/M%d" % (proj, M))
 
 
 # ---------------------------------------------------------------------------
@@ -71,7 +87,7 @@ def test_prefill_pipelined_gemm_edges(M, N, K):
     # slices than pipeline stages
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(77 + K, M, N, K, outlier_frac=0.001)
-    full_check(W, X, rows=sample_rows(M, 16, seed=K), label="gemm-pipeline-edge")
+    full_check(W, X, rows=cover_rows(M), label="gemm-pipeline-edge")
     assert bl.last_dispatch().startswith("gemm_dense_dma"), bl.last_dispatch()
 
 
@@ -84,7 +100,7 @@ def test_dense_gemm_tile_choice(M, N, K, tile):
     # five K slices and with one)
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1600 + M, M, N, K, outlier_frac=0.001)
-    full_check(W, X, rows=sample_rows(M, 16, seed=M), label="gemm-tile-choice")
+    full_check(W, X, rows=cover_rows(M), label="gemm-tile-choice")
     assert bl.last_dispatch() == "gemm_dense_dma_" + tile, bl.last_dispatch()
 
 
@@ -92,7 +108,7 @@ def test_dense_gemm_tile_choice(M, N, K, tile):
 @pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
 def test_gemm_tile_thresholds(M, nm):
     W, X = workloads.small_case(300 + M, M, 1000, 448)
-    full_check(W, X, nm, rows=sample_rows(M, 24, seed=M), label="gemm-threshold")
+    full_check(W, X, nm, rows=cover_rows(M), label="gemm-threshold")
 
 
 @pytest.mark.parametrize("M,N,K,tile", [(1024, 8200, 320, "256x256"), (300, 1000, 1472, "128x128"),
@@ -105,7 +121,7 @@ def test_nm_gemm_tbytes(M, N, K, tile, nm):
     # byte permutes, read straight into the MFMA operand (K <= 2^18)
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1200 + M + K, M, N, K, outlier_frac=0.001)
-    full_check(W, X, nm, rows=sample_rows(M, 16, seed=M), label="nm-gemm")
+    full_check(W, X, nm, rows=cover_rows(M), label="nm-gemm")
     name = bl.last_dispatch()
     if M > 64:
         # from 65 tokens the rows are expanded to dense codes for the
@@ -128,7 +144,7 @@ def test_nm_expand_dense_gemm(M, N, K, nm):
     # ragged tiles, one K slice, deep K
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(2100 + M + K, M, N, K, outlier_frac=0.001)
-    full_check(W, X, nm, rows=sample_rows(M, 16, seed=K), label="nm-expand-dense")
+    full_check(W, X, nm, rows=cover_rows(M), label="nm-expand-dense")
     want = "gemm_nm%d%d_expand_dense_%s" % (nm[0], nm[1], dense_tile(M, N).split("_")[0])
     assert bl.last_dispatch() == want, bl.last_dispatch()
 
@@ -145,10 +161,10 @@ def dense_tile(M, N):
 
 def tbytes_splits(M, N, K, tile):
     """K splits of the N:M t-byte GEMM: enough workgroups for the 256 compute
-    units, at least 4 slices of 64 each, partials within the 64 MB workspace."""
+    units, at least 4 slices of 64 each, partials within 32 MiB."""
     bm, bn = (int(v) for v in tile.split("x"))
     tiles = -(-M // bm) * -(-N // bn)
-    return min(-(-256 // tiles), (K // 64) // 4, (64 << 20) // (tiles * bm * bn * 4))
+    return min(-(-256 // tiles), (K // 64) // 4, (32 << 20) // (tiles * bm * bn * 4))
 
 
 @pytest.mark.parametrize("M,N,K,nm", [(32, 2560, 6912, (2, 4)), (64, 2560, 6912, (6, 8)), (16, 2560, 6912, (6, 8)),
@@ -160,7 +176,7 @@ def test_nm_gemm_tbytes_splitk(M, N, K, nm):
     # kernel; ragged M and N, 2 to 16 splits
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1800 + M + K, M, N, K, outlier_frac=0.001)
-    full_check(W, X, nm, rows=sample_rows(M, 16, seed=K), label="nm-gemm-splitk")
+    full_check(W, X, nm, rows=cover_rows(M), label="nm-gemm-splitk")
     tile = "64x128"
     assert tbytes_splits(M, N, K, tile) >= 2
     assert bl.last_dispatch() == "gemm_nm%d%d_splitk_%s_tbytes" % (nm[0], nm[1], tile), bl.last_dispatch()
@@ -182,7 +198,7 @@ def test_nm24_sparse_mfma_gemm(M, N, K):
     # than the pipeline's stages), N not a multiple of 4, prefill shapes
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1400 + M + K, M, N, K, outlier_frac=0.001)
-    full_check(W, X, (2, 4), rows=sample_rows(M, 16, seed=K), label="nm24-smfmac")
+    full_check(W, X, (2, 4), rows=cover_rows(M), label="nm24-smfmac")
     assert bl.last_dispatch() == "gemm_nm24_smfmac_" + nm24_sparse_tile(M, N), bl.last_dispatch()
 
 
@@ -191,7 +207,7 @@ def test_nm24_sparse_threshold(M):
     # below 128 tokens 2:4 takes the dense GEMM on expanded rows
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(1450 + M, M, 1000, 512)
-    full_check(W, X, (2, 4), rows=sample_rows(M, 24, seed=M), label="nm24-threshold")
+    full_check(W, X, (2, 4), rows=cover_rows(M), label="nm24-threshold")
     if M < 128:
         want = "gemm_nm24_expand_dense_" + dense_tile(M, 1000).split("_")[0]
     else:
@@ -282,11 +298,11 @@ def test_gemv_fallback_very_deep_k(M, nm):
 def test_few_token_gemm(M, N, K):
     # few tokens with many weight rows (or K too deep for the skinny kernel):
     # K split over several workgroups, partial tiles combined by a second
-    # kernel; twice in a row (the shared workspace is reused)
+    # kernel; twice in a row, bit-identical
     import torch
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(900 + M + K, M, N, K, outlier_frac=0.001)
-    out = full_check(W, X, rows=sample_rows(M, 12, seed=M), label="few-token")
+    out = full_check(W, X, rows=cover_rows(M), label="few-token")
     name = bl.last_dispatch()
     assert name.startswith("gemm_dense_splitk") or name.startswith("gemm_dense_dma"), name
     Y2, acc2 = hip_forward(out["Xq"], out["xs"], out["rs"], out["packed"], out["ws"], N, (0, 0))
@@ -310,7 +326,7 @@ def test_skinny_token_tiles(M, N, K, nm):
     import ternary_weight_linear_act_amd as bl
     assert skinny_tiles(M, N)
     W, X = workloads.small_case(2500 + M + K, M, N, K, outlier_frac=0.001)
-    full_check(W, X, nm, rows=sample_rows(M, 24, seed=K), label="skinny-tiles")
+    full_check(W, X, nm, rows=cover_rows(M), label="skinny-tiles")
     name = bl.last_dispatch()
     assert name.startswith("skinny_mfma_") and name.endswith("_mt16"), name
 
