@@ -179,6 +179,22 @@ bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const
                                    float *Y, int32_t *acc, void *workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/* bitlinear_forward for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments without the workspace, the same kernels and
+ * the same results, bit for bit.  Its scratch is a fixed 32 MiB array in the
+ * library's device code, one copy per GPU, held until the process ends; its
+ * address is looked up on the first call on each device.  Calls whose shape
+ * needs more scratch than that (bitlinear_forward_workspace_size) return
+ * ESIZE and launch nothing.  Every call on a GPU shares that GPU's array: such
+ * calls must not overlap in time on one GPU (they race on it), whatever
+ * their streams.  `stream` must belong to the current device (EINVAL
+ * otherwise).  Other errors as bitlinear_forward. */
+bitlinear_status bitlinear_forward_noalloc(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
+                                           const void *packed, const float *w_scale, bitlinear_nm nm,
+                                           int64_t M, int64_t N, int64_t K,
+                                           float *Y, int32_t *acc, hipStream_t stream);
+
 /* One projection of a fused decode call: packed weights and beta as written
  * by bitlinear_pack_weights (same K and nm as the call), N output features,
  * Y the M x N fp32 output, acc an optional M x N int32 output (NULL to skip). */

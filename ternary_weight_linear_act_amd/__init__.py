@@ -18,6 +18,7 @@ from .binding import (  # noqa: F401
     quant_act_h4,
     forward,
     forward_workspace_size,
+    forward_noalloc,
     forward_fused,
     forward_fused_ex,
     last_dispatch,

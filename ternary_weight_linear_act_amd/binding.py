@@ -28,6 +28,7 @@ EXPORTED = (
     "bitlinear_quant_act_h4",
     "bitlinear_forward_workspace_size",
     "bitlinear_forward",
+    "bitlinear_forward_noalloc",
     "bitlinear_forward_fused",
     "bitlinear_forward_fused_ex",
     "bitlinear_last_error",
@@ -78,6 +79,7 @@ def load_library():
     lib.bitlinear_quant_act.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.bitlinear_forward_workspace_size.argtypes = [i64, i64, i64, NM, ctypes.POINTER(sz)]
     lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp, sz, vp]
+    lib.bitlinear_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp]
     lib.bitlinear_forward_fused.argtypes = [vp, i64, i64, NM, ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     lib.bitlinear_quant_act_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, vp, vp, vp, vp]
     lib.bitlinear_quant_act_h4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
@@ -290,6 +292,30 @@ def forward(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=None, acc=
         _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _ptr(packed), _ptr(w_scale), _nm(nm),
         M, N, K, _ptr(Y), _ptr(acc), _ptr(workspace), ws_bytes, _stream(stream)))
     return (Y, acc) if (want_acc or acc is not None) else Y
+
+
+def forward_noalloc(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=None, acc=None, stream=None):
+    """forward() through bitlinear_forward_noalloc: the library's fixed
+    per-GPU scratch instead of a workspace (at most 32 MiB of it; calls must
+    not overlap on one GPU).  Y and acc must be given (this allocates nothing);
+    returns Y, or (Y, acc) with acc."""
+    import torch
+    _require(Xq, torch.int8, None, "Xq")
+    M, K = Xq.shape
+    _require(x_scale, torch.float32, (M,), "x_scale")
+    _require(x_rowsum, torch.int32, (M,), "x_rowsum")
+    _require(packed, torch.uint8, None, "packed")
+    _require(w_scale, torch.float32, (1,), "w_scale")
+    _require(Y, torch.float32, (M, N), "Y")
+    if acc is not None:
+        _require(acc, torch.int32, (M, N), "acc")
+    pb, _ = packed_size(N, K, nm)
+    if packed.numel() < pb:
+        raise ValueError("packed buffer holds %d bytes, %d needed" % (packed.numel(), pb))
+    _check("bitlinear_forward_noalloc", load_library().bitlinear_forward_noalloc(
+        _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _ptr(packed), _ptr(w_scale), _nm(nm),
+        M, N, K, _ptr(Y), _ptr(acc), _stream(stream)))
+    return (Y, acc) if acc is not None else Y
 
 
 def forward_fused(X, projs, nm=NM_DENSE, Ys=None, accs=None, want_acc=False, x_scale=None, stream=None):

@@ -338,6 +338,37 @@ bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const
     return run_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc, scratch, stream);
 }
 
+bitlinear_status bitlinear_forward_noalloc(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
+                                           const void *packed, const float *w_scale, bitlinear_nm nm, int64_t M,
+                                           int64_t N, int64_t K, float *Y, int32_t *acc, hipStream_t stream)
+{
+    bl::Pattern p;
+    CHECK(check_nm(nm, &p));
+    CHECK(check_m(M));
+    CHECK(check_n(N));
+    CHECK(check_k(K));
+    CHECK(check_ptr(packed, 16, "packed"));
+    CHECK(check_ptr(w_scale, 4, "w_scale"));
+    if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }   // M-sized buffers may be NULL
+    CHECK(check_ptr(Xq, 16, "Xq"));
+    CHECK(check_ptr(x_scale, 4, "x_scale"));
+    CHECK(check_ptr(x_rowsum, 4, "x_rowsum"));
+    CHECK(check_ptr(Y, 16, "Y"));
+    if (acc && !aligned(acc, 16)) return fail(BITLINEAR_EINVAL, "acc must be 16-byte aligned");
+    const size_t need = forward_need(p, M, N, K);
+    if (need > bl::kNoAllocScratchBytes)
+        return fail(BITLINEAR_ESIZE, "M = %lld, N = %lld, K = %lld needs %zu bytes of scratch, more than the %zu "
+                    "this entry point holds; use bitlinear_forward with a workspace", (long long)M, (long long)N,
+                    (long long)K, need, bl::kNoAllocScratchBytes);
+    bl::Scratch scratch;
+    const hipError_t e = bl::noalloc_scratch(stream, &scratch.ptr);
+    if (e == hipErrorInvalidDevice)
+        return fail(BITLINEAR_EINVAL, "the stream's device must be the current device");
+    if (e != hipSuccess) return hip_fail("scratch address", e);
+    scratch.bytes = bl::kNoAllocScratchBytes;
+    return run_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc, scratch, stream);
+}
+
 bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, bitlinear_nm nm,
                                          const bitlinear_proj *projs, int32_t nproj, float *x_scale,
                                          hipStream_t stream)

@@ -35,6 +35,13 @@ struct Scratch {
     }
 };
 
+// Scratch of bitlinear_forward_noalloc: a fixed device array per GPU.
+constexpr size_t kNoAllocScratchBytes = 32u << 20;
+
+// Device address of that array on the current device (looked up once per
+// device).  hipErrorInvalidDevice when `stream` belongs to another device.
+hipError_t noalloc_scratch(hipStream_t stream, uint8_t **ptr);
+
 // Largest token count of the skinny MFMA forward (tiles of 16 tokens past 16).
 constexpr int64_t kSkinnyMaxM = 64;
 

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     for want in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward",
                  "bitlinear_packed_size", "bitlinear_last_error", "bitlinear_last_dispatch",
                  "bitlinear_forward_fused", "bitlinear_quant_act_ex", "bitlinear_forward_fused_ex",
-                 "bitlinear_quant_act_h4", "bitlinear_forward_workspace_size"):
+                 "bitlinear_quant_act_h4", "bitlinear_forward_workspace_size", "bitlinear_forward_noalloc"):
         assert want in names
     # the binding's list is the header's
     assert sorted(binding.EXPORTED) == names
@@ -180,6 +180,19 @@ def test_forward_short_workspace_is_rejected_on_the_host(lib):
     assert f(P(), P(), P(), P(), P(), NM(6, 8), 512, 8960, 1536, P(), None, None, 0, None) == -3
     need = work_size(lib, 40, 4096, 8192, (0, 0))[1]
     assert f(P(), P(), P(), P(), P(), NM(0, 0), 40, 4096, 8192, P(), None, P(), need - 16, None) == -3
+
+
+def test_noalloc_validation(lib):
+    # host-side checks of the no-allocation forward: nothing reaches the GPU
+    from ternary_weight_linear_act_amd.binding import NM
+    f = lib.bitlinear_forward_noalloc
+    assert f(None, P(), P(), P(), P(), NM(0, 0), 4, 8, 64, P(), None, None) == -1
+    assert f(P(), P(), P(), P(), P(), NM(0, 0), 4, 8, 100, P(), None, None) == -1
+    assert f(P(), P(), P(), P(), P(), NM(2, 8), 4, 8, 64, P(), None, None) == -2
+    assert f(None, None, None, P(), P(), NM(0, 0), 0, 8, 64, None, None, None) == 0
+    # more scratch than the fixed array holds (6:8 rows expanded: 64 MiB)
+    assert f(P(), P(), P(), P(), P(), NM(6, 8), 100, 16384, 16384, P(), None, None) == -3
+    assert b"32" in lib.bitlinear_last_error() or b"33554432" in lib.bitlinear_last_error()
 
 
 def test_quant_validation(lib):
