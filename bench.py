@@ -178,11 +178,27 @@ def bench_configs(torch, bl, workloads, dev, log):
         ops = sum(2.0 * M * shapes[n][0] * shapes[n][1] for n in projs)
         r = {"M": M, "projections": list(projs), "two_call_us": round(us, 3),
              "two_call_GB/s": round(abytes / (us * 1e-6) / 1e9, 1), "TOPS": round(ops / (us * 1e-6) / 1e12, 1)}
-        if fused_groups and M <= 4:
+        if fused_groups and M <= 16:
+            # one call per input group: the fused launch (quantisation and
+            # projections) for narrow groups and at up to 4 tokens; past 4
+            # tokens, groups of many weight rows (each fused workgroup would
+            # re-quantise the whole input) take quant_act, then the grouped
+            # forward (one launch for the group)
+            def narrow(g):
+                return M <= 4 or sum(shapes[n][0] for n in g) <= 4096
+            Xq_g = {g: torch.empty((M, shapes[g[0]][1]), dtype=torch.int8, device=dev) for g in fused_groups}
+            xs_g = {g: torch.empty(M, dtype=torch.float32, device=dev) for g in fused_groups}
+            rs_g = {g: torch.empty(M, dtype=torch.int32, device=dev) for g in fused_groups}
+
             def fused(j):
                 for g in fused_groups:
-                    bl.forward_fused(X[g[0]], [(pools[n][j], ws[n], shapes[n][0]) for n in g], nm=nm_of(g[0]),
-                                     Ys=[Y[n] for n in g])
+                    projs_j = [(pools[n][j], ws[n], shapes[n][0]) for n in g]
+                    if narrow(g):
+                        bl.forward_fused(X[g[0]], projs_j, nm=nm_of(g[0]), Ys=[Y[n] for n in g])
+                    else:
+                        bl.quant_act(X[g[0]], Xq_g[g], xs_g[g], rs_g[g])
+                        bl.forward_grouped(Xq_g[g], xs_g[g], rs_g[g], projs_j, nm=nm_of(g[0]),
+                                           Ys=[Y[n] for n in g])
             fused(0)
             torch.cuda.synchronize()
             for n in projs:
@@ -192,14 +208,17 @@ def bench_configs(torch, bl, workloads, dev, log):
             fus = ms * 1e3 / G
             fbytes = sum(pk[n].numel() + M * shapes[n][0] * 4 for n in projs) + sum(
                 4 * M * shapes[g[0]][1] for g in fused_groups)
+            launches = sum(1 if narrow(g) else 2 for g in fused_groups)
             r.update({"fused_us": round(fus, 3), "fused_GB/s": round(fbytes / (fus * 1e-6) / 1e9, 1),
-                      "fused_launches": len(fused_groups)})
+                      "fused_launches": launches,
+                      "fused_groups": ["+".join(g) + (" fused" if narrow(g) else " quant_act+grouped")
+                                       for g in fused_groups]})
         res[name] = r
         log("%-28s M=%-4d two-call %8.2f us%s" % (name, M, us, (" fused %.2f us" % r["fused_us"]) if "fused_us" in r else ""))
 
     dense = lambda n: (0, 0)
     case("single_1024/M1", "single_1024", ("linear",), 1, dense, [("linear",)])
-    case("single_1024/M16", "single_1024", ("linear",), 16, dense)
+    case("single_1024/M16", "single_1024", ("linear",), 16, dense, [("linear",)])
     nmap = {"dense": (0, 0), "nm24": (2, 4), "nm68": (6, 8)}
     for pn in ("dense", "nm24", "nm68"):
         case("sparse_ffn_1p5b/%s/M1" % pn, "sparse_ffn_1p5b", (pn,), 1, lambda n: nmap[n], [(pn,)])

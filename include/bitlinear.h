@@ -214,12 +214,32 @@ typedef struct {
  * 요약 설명", sec. 2 and 5.1; "BitNet 논문 분석: 1-Bit LLM의 시대", section
  * "Absmean 양자화 함수").  `projs` is a host array of nproj entries.
  * x_scale: optional M fp32 output (g_m / 127), NULL to skip.
- * Supported: 1 <= M <= 4, 1 <= nproj <= 8, K <= 16192 (K <= 65344 when
+ * Supported: 1 <= M <= 16, 1 <= nproj <= 8, K <= 16192 (K <= 65344 when
  * M == 1); anything else returns BITLINEAR_EUNSUPPORTED and launches
- * nothing -- use the two-call path then. */
+ * nothing -- use the two-call path then.  Past 4 tokens the tokens run in
+ * tiles of 4 along the grid, each tile quantising its own rows (for wide
+ * projection groups bitlinear_quant_act then bitlinear_forward_grouped is
+ * the faster form). */
 bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, bitlinear_nm nm,
                                          const bitlinear_proj *projs, int32_t nproj,
                                          float *x_scale, hipStream_t stream);
+
+/* Forward of several projections that share one quantised input (q/k/v, or
+ * gate/up of a feed-forward block) in one launch: the same contraction and
+ * rescale as bitlinear_forward for each projection, bit for bit (2B4T
+ * summary, sec. 2 and 5.1; "BitNet 논문 분석", section "Absmean 양자화
+ * 함수"; the Sparse-BitNet review's Table 5 discussion notes that decode
+ * gains are diluted by launch overhead at small batches).  Xq, x_scale,
+ * x_rowsum: as written by bitlinear_quant_act for the shared input (M x K).
+ * `projs`: host array of nproj entries (packed, w_scale, N, Y, acc as in
+ * bitlinear_proj).  Supported: 1 <= nproj <= 8 and M <= 16, or
+ * 17 <= M <= 64 while the 16-token tiles times the 16-row weight blocks of
+ * all projections make at most 512 workgroups, and K within the kernels'
+ * range; anything else returns BITLINEAR_EUNSUPPORTED and launches nothing
+ * (call bitlinear_forward per projection then).  Needs no workspace. */
+bitlinear_status bitlinear_forward_grouped(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
+                                           int64_t M, int64_t K, bitlinear_nm nm, const bitlinear_proj *projs,
+                                           int32_t nproj, hipStream_t stream);
 
 /* Transform of each activation row before the absmax quantisation: the steps
  * either side of a BitNet linear, fused into the quantiser.

@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     forward_workspace_size,
     forward_noalloc,
     forward_fused,
+    forward_grouped,
     forward_fused_ex,
     last_dispatch,
     library_path,

@@ -29,6 +29,7 @@ EXPORTED = (
     "bitlinear_forward_workspace_size",
     "bitlinear_forward",
     "bitlinear_forward_noalloc",
+    "bitlinear_forward_grouped",
     "bitlinear_forward_fused",
     "bitlinear_forward_fused_ex",
     "bitlinear_last_error",
@@ -80,6 +81,7 @@ def load_library():
     lib.bitlinear_forward_workspace_size.argtypes = [i64, i64, i64, NM, ctypes.POINTER(sz)]
     lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp, sz, vp]
     lib.bitlinear_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp]
+    lib.bitlinear_forward_grouped.argtypes = [vp, vp, vp, i64, i64, NM, ctypes.POINTER(Proj), ctypes.c_int32, vp]
     lib.bitlinear_forward_fused.argtypes = [vp, i64, i64, NM, ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     lib.bitlinear_quant_act_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, vp, vp, vp, vp]
     lib.bitlinear_quant_act_h4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
@@ -318,8 +320,43 @@ def forward_noalloc(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=No
     return (Y, acc) if acc is not None else Y
 
 
+def _proj_array(projs, M, Ys, accs, device):
+    """Proj structs for (packed, w_scale, N) triples, with their outputs."""
+    import torch
+    n = len(projs)
+    if Ys is None:
+        Ys = [torch.empty((M, N), dtype=torch.float32, device=device) for (_, _, N) in projs]
+    arr = (Proj * max(n, 1))()
+    for i, (packed, ws, N) in enumerate(projs):
+        _require(packed, torch.uint8, None, "packed")
+        _require(ws, torch.float32, (1,), "w_scale")
+        _require(Ys[i], torch.float32, (M, N), "Y")
+        if accs is not None:
+            _require(accs[i], torch.int32, (M, N), "acc")
+        arr[i] = Proj(packed.data_ptr(), ws.data_ptr(), N, Ys[i].data_ptr(),
+                      accs[i].data_ptr() if accs is not None else None)
+    return arr, Ys
+
+
+def forward_grouped(Xq, x_scale, x_rowsum, projs, nm=NM_DENSE, Ys=None, accs=None, want_acc=False, stream=None):
+    """forward() of every projection in `projs` -- a list of (packed, w_scale,
+    N) sharing the quantised input -- in one launch.  Returns the list of Y
+    tensors, or (Ys, accs) when accumulators are wanted."""
+    import torch
+    _require(Xq, torch.int8, None, "Xq")
+    M, K = Xq.shape
+    _require(x_scale, torch.float32, (M,), "x_scale")
+    _require(x_rowsum, torch.int32, (M,), "x_rowsum")
+    if accs is None and want_acc:
+        accs = [torch.empty((M, N), dtype=torch.int32, device=Xq.device) for (_, _, N) in projs]
+    arr, Ys = _proj_array(projs, M, Ys, accs, Xq.device)
+    _check("bitlinear_forward_grouped", load_library().bitlinear_forward_grouped(
+        _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), M, K, _nm(nm), arr, len(projs), _stream(stream)))
+    return (Ys, accs) if accs is not None else Ys
+
+
 def forward_fused(X, projs, nm=NM_DENSE, Ys=None, accs=None, want_acc=False, x_scale=None, stream=None):
-    """Quantise X (M x K fp32, M <= 4) and apply every projection in `projs`
+    """Quantise X (M x K fp32, M <= 16) and apply every projection in `projs`
     -- a list of (packed, w_scale, N) sharing X -- in one launch.
 
     Returns the list of Y tensors, or (Ys, accs) when accumulators are wanted.

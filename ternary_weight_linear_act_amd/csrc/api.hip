@@ -22,9 +22,8 @@ hipError_t launch_gemm(const int8_t *Xq, const float *xs, const int32_t *rs, con
                        const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
                        int32_t *acc, Scratch &scratch, hipStream_t stream, const char **name);
 
-hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
-                                 const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
-                                 int32_t *acc, hipStream_t stream, const char **name, bool query);
+hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_t *rs, FusedProjArgs args,
+                                 Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);
 
 hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
                               int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
@@ -42,14 +41,14 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
     const bool query = scratch.query;
     static const char *gemv_names[3] = {"gemv_dense", "gemv_nm24", "gemv_nm68"};
     const int pi = (int)p;
+    FusedProjArgs one = {};
+    one.nproj = 1;
+    one.packed[0] = packed;
+    one.w_scale[0] = w_scale;
+    one.Y[0] = Y;
+    one.acc[0] = acc;
+    one.N[0] = N;
     if (M == 1) {
-        FusedProjArgs one = {};
-        one.nproj = 1;
-        one.packed[0] = packed;
-        one.w_scale[0] = w_scale;
-        one.Y[0] = Y;
-        one.acc[0] = acc;
-        one.N[0] = N;
         const hipError_t e = launch_decode_dot4(nullptr, Xq, x_scale, x_rowsum, M, K, p, one, nullptr,
                                                 ActTransform{nullptr, nullptr, 0.0f}, stream, name, query);
         if (e != hipErrorNotSupported) return e;
@@ -71,8 +70,7 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
     // 8.2 -> 4.2 us, 2048 x 256 9.2 -> 3.5 us); with more, the GEMM is faster
     // (2048 x 11008 at 64 tokens: 10.1 against 17.3 us)
     if (M <= 16 || (M <= kSkinnyMaxM && ((N + 15) / 16) * ((M + 15) / 16) <= 512)) {
-        const hipError_t e = launch_skinny_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc,
-                                                   stream, name, query);
+        const hipError_t e = launch_skinny_forward(Xq, x_scale, x_rowsum, one, p, M, K, stream, name, query);
         if (e != hipErrorNotSupported) return e;
     }
     if (M <= kGemvMaxM) {
@@ -209,6 +207,31 @@ bitlinear_status run_forward(const int8_t *Xq, const float *x_scale, const int32
         bitlinear_status st_ = (expr);                \
         if (st_ != BITLINEAR_OK) return st_;          \
     } while (0)
+
+// The projections of a fused or grouped call, checked and copied into the
+// kernels' argument block.
+bitlinear_status check_projs(const bitlinear_proj *projs, int32_t nproj, int64_t M, bl::FusedProjArgs *args)
+{
+    if (!projs) return fail(BITLINEAR_EINVAL, "projs must not be NULL");
+    if (nproj < 1) return fail(BITLINEAR_EINVAL, "nproj = %d must be >= 1", nproj);
+    if (nproj > bl::kMaxFusedProj)
+        return fail(BITLINEAR_EUNSUPPORTED, "nproj = %d: at most %d projections per call", nproj, bl::kMaxFusedProj);
+    args->nproj = nproj;
+    for (int i = 0; i < nproj; ++i) {
+        CHECK(check_n(projs[i].N));
+        CHECK(check_ptr(projs[i].packed, 16, "projs[i].packed"));
+        CHECK(check_ptr(projs[i].w_scale, 4, "projs[i].w_scale"));
+        if (M > 0) CHECK(check_ptr(projs[i].Y, 16, "projs[i].Y"));
+        if (projs[i].acc && !aligned(projs[i].acc, 16))
+            return fail(BITLINEAR_EINVAL, "projs[i].acc must be 16-byte aligned");
+        args->packed[i] = static_cast<const uint8_t *>(projs[i].packed);
+        args->w_scale[i] = projs[i].w_scale;
+        args->N[i] = projs[i].N;
+        args->Y[i] = projs[i].Y;
+        args->acc[i] = projs[i].acc;
+    }
+    return BITLINEAR_OK;
+}
 
 }  // namespace
 
@@ -369,6 +392,40 @@ bitlinear_status bitlinear_forward_noalloc(const int8_t *Xq, const float *x_scal
     return run_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc, scratch, stream);
 }
 
+bitlinear_status bitlinear_forward_grouped(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
+                                           int64_t M, int64_t K, bitlinear_nm nm, const bitlinear_proj *projs,
+                                           int32_t nproj, hipStream_t stream)
+{
+    bl::Pattern p;
+    CHECK(check_nm(nm, &p));
+    CHECK(check_m(M));
+    CHECK(check_k(K));
+    bl::FusedProjArgs args = {};
+    CHECK(check_projs(projs, nproj, M, &args));
+    if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }
+    CHECK(check_ptr(Xq, 16, "Xq"));
+    CHECK(check_ptr(x_scale, 4, "x_scale"));
+    CHECK(check_ptr(x_rowsum, 4, "x_rowsum"));
+    int64_t rows16 = 0;
+    for (int i = 0; i < nproj; ++i) rows16 += (projs[i].N + 15) / 16;
+    const char *name = "";
+    hipError_t e = hipErrorNotSupported;
+    if (M == 1)
+        e = bl::launch_decode_dot4(nullptr, Xq, x_scale, x_rowsum, M, K, p, args, nullptr,
+                                   bl::ActTransform{nullptr, nullptr, 0.0f}, stream, &name, false);
+    // 17-64 tokens in tiles of 16 while the tiles make at most 512 workgroups
+    // (the rule of the single forward)
+    else if (M <= 16 || (M <= bl::kSkinnyMaxM && rows16 * ((M + 15) / 16) <= 512))
+        e = bl::launch_skinny_forward(Xq, x_scale, x_rowsum, args, p, M, K, stream, &name, false);
+    if (e == hipErrorNotSupported)
+        return fail(BITLINEAR_EUNSUPPORTED, "grouped forward: no one-launch kernel for M = %lld, K = %lld and %lld "
+                    "rows of 16 (call bitlinear_forward per projection)", (long long)M, (long long)K,
+                    (long long)rows16);
+    if (e != hipSuccess) return hip_fail("grouped forward launch", e);
+    set_dispatch(name);
+    return BITLINEAR_OK;
+}
+
 bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, bitlinear_nm nm,
                                          const bitlinear_proj *projs, int32_t nproj, float *x_scale,
                                          hipStream_t stream)
@@ -387,25 +444,8 @@ bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_
     bl::ActTransform t;
     CHECK(check_transform(tr, &t));
     const bool transformed = t.up || t.gamma;
-    if (!projs) return fail(BITLINEAR_EINVAL, "projs must not be NULL");
-    if (nproj < 1) return fail(BITLINEAR_EINVAL, "nproj = %d must be >= 1", nproj);
-    if (nproj > bl::kMaxFusedProj)
-        return fail(BITLINEAR_EUNSUPPORTED, "nproj = %d: at most %d projections per fused call", nproj,
-                    bl::kMaxFusedProj);
     bl::FusedProjArgs args = {};
-    args.nproj = nproj;
-    for (int i = 0; i < nproj; ++i) {
-        CHECK(check_n(projs[i].N));
-        CHECK(check_ptr(projs[i].packed, 16, "projs[i].packed"));
-        CHECK(check_ptr(projs[i].w_scale, 4, "projs[i].w_scale"));
-        if (M > 0) CHECK(check_ptr(projs[i].Y, 16, "projs[i].Y"));
-        if (projs[i].acc && !aligned(projs[i].acc, 16)) return fail(BITLINEAR_EINVAL, "projs[i].acc must be 16-byte aligned");
-        args.packed[i] = static_cast<const uint8_t *>(projs[i].packed);
-        args.w_scale[i] = projs[i].w_scale;
-        args.N[i] = projs[i].N;
-        args.Y[i] = projs[i].Y;
-        args.acc[i] = projs[i].acc;
-    }
+    CHECK(check_projs(projs, nproj, M, &args));
     if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }
     CHECK(check_ptr(X, 16, "X"));
     if (x_scale && !aligned(x_scale, 4)) return fail(BITLINEAR_EINVAL, "x_scale must be 4-byte aligned");
@@ -417,7 +457,7 @@ bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_
                     "(M = %lld, K = %lld)", (long long)M, (long long)K);
     if (e == hipErrorNotSupported) e = bl::launch_fused_forward(X, M, K, p, args, x_scale, stream, &name);
     if (e == hipErrorNotSupported)
-        return fail(BITLINEAR_EUNSUPPORTED, "fused decode supports 1 <= M <= 4 and K <= %s (M = %lld, K = %lld)",
+        return fail(BITLINEAR_EUNSUPPORTED, "fused decode supports 1 <= M <= 16 and K <= %s (M = %lld, K = %lld)",
                     M == 1 ? "65344" : "16192", (long long)M, (long long)K);
     if (e != hipSuccess) return hip_fail("fused forward launch", e);
     set_dispatch(name);

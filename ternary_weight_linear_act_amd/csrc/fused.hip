@@ -78,26 +78,13 @@ Fn pick_p(int mt, int ksi, int cmi)
 
 thread_local char g_name[64];
 
-}  // namespace
-
-// args.block_start is filled here.  hipErrorNotSupported: no configuration
-// fits (M > 4, too many projections, or K too large for the shared row).
-hipError_t launch_fused_forward(const float *X, int64_t M, int64_t K, Pattern p, FusedProjArgs args,
-                                float *x_scale, hipStream_t stream, const char **name)
+// Picks KS and CMAX for MT staged token rows (`chunks`: the chunks per wave
+// aimed at); nullptr when none fits.
+Fn choose(Pattern p, int64_t K, int mt, double chunks, int *ks_out, int *cm_out)
 {
-    if (M < 1 || M > 4 || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
-    const int mt = (M == 1) ? 1 : 4;
-    if ((int64_t)mt * (K + 192) > kMaxDynLds) return hipErrorNotSupported;
-    int64_t blocks = 0;
-    for (int i = 0; i < args.nproj; ++i) {
-        args.block_start[i] = (int32_t)blocks;
-        blocks += (args.N[i] + kRows - 1) / kRows;
-    }
-    for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
-    if (blocks > (1LL << 30)) return hipErrorNotSupported;
-
+    if ((int64_t)mt * (K + 192) > kMaxDynLds) return nullptr;
     const int64_t C = K / 64;
-    const double want = log2((double)C / (blocks >= 512 ? 20.0 : 12.0));
+    const double want = log2((double)C / chunks);
     int order[kNKS];
     for (int i = 0; i < kNKS; ++i) order[i] = i;
     for (int i = 0; i < kNKS; ++i)
@@ -111,25 +98,58 @@ hipError_t launch_fused_forward(const float *X, int64_t M, int64_t K, Pattern p,
         const int ksi = order[oi], ks = kKS[ksi];
         if (ks > C) continue;
         const int64_t need = (C + ks - 1) / ks;
-        int cmi = -1;
-        for (int c = 0; c < kNCM; ++c)
-            if (kCM[c] >= need) { cmi = c; break; }
-        if (cmi < 0) continue;
-        if (static_lds(ks, kCM[cmi], mt) + (int64_t)mt * (K + 192) > kLds) continue;
-        Fn f = nullptr;
-        switch (p) {
-        case Pattern::Dense: f = pick_p<Pattern::Dense>(mt, ksi, cmi); break;
-        case Pattern::NM24: f = pick_p<Pattern::NM24>(mt, ksi, cmi); break;
-        case Pattern::NM68: f = pick_p<Pattern::NM68>(mt, ksi, cmi); break;
+        for (int cmi = 0; cmi < kNCM; ++cmi) {
+            if (kCM[cmi] < need) continue;
+            if (static_lds(ks, kCM[cmi], mt) + (int64_t)mt * (K + 192) > kLds) break;
+            Fn f = nullptr;
+            switch (p) {
+            case Pattern::Dense: f = pick_p<Pattern::Dense>(mt, ksi, cmi); break;
+            case Pattern::NM24: f = pick_p<Pattern::NM24>(mt, ksi, cmi); break;
+            case Pattern::NM68: f = pick_p<Pattern::NM68>(mt, ksi, cmi); break;
+            }
+            if (f) {
+                *ks_out = ks;
+                *cm_out = kCM[cmi];
+                return f;
+            }
+            break;                                     // the smallest CMAX that holds the range, or none
         }
-        if (!f) continue;
-        snprintf(g_name, sizeof g_name, "fused_decode_%s_ks%d_c%d_mt%d_p%d",
-                 p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", ks, kCM[cmi], mt,
-                 args.nproj);
-        *name = g_name;
-        return f(X, M, K, args, (int)blocks, x_scale, stream);
     }
-    return hipErrorNotSupported;
+    return nullptr;
+}
+
+}  // namespace
+
+// args.block_start is filled here.  Tokens are staged one (M = 1) or four
+// at a time, more than four in tiles of 4 along the grid's y.  Chunks per
+// wave aimed at: about 20 with many workgroups (>= 512), 12 with few, and 6
+// for tiles (each tile quantises its own rows, so fewer chunks per wave spread
+// that work: at 8 tokens, 2048 -> 2048 5.3 -> 5.0 us and 2048 -> 2560 in
+// three projections 6.1 us, against 8.7 and 8.8 us with 8 staged rows and
+// 16 chunks per wave).  hipErrorNotSupported: no configuration fits (M > 16,
+// too many projections, or K too large for the shared row).
+hipError_t launch_fused_forward(const float *X, int64_t M, int64_t K, Pattern p, FusedProjArgs args,
+                                float *x_scale, hipStream_t stream, const char **name)
+{
+    if (M < 1 || M > 16 || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
+    int64_t blocks = 0;
+    for (int i = 0; i < args.nproj; ++i) {
+        args.block_start[i] = (int32_t)blocks;
+        blocks += (args.N[i] + kRows - 1) / kRows;
+    }
+    for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
+    if (blocks > (1LL << 30)) return hipErrorNotSupported;
+
+    const int mt = (M == 1) ? 1 : 4;
+    const double chunks = M > 4 ? 6.0 : blocks >= 512 ? 20.0 : 12.0;
+    int ks = 0, cm = 0;
+    Fn f = choose(p, K, mt, chunks, &ks, &cm);
+    if (!f) return hipErrorNotSupported;
+    snprintf(g_name, sizeof g_name, "fused_decode_%s_ks%d_c%d_mt%d%s_p%d",
+             p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", ks, cm, mt, M > 4 ? "_tiles" : "",
+             args.nproj);
+    *name = g_name;
+    return f(X, M, K, args, (int)blocks, x_scale, stream);
 }
 
 }  // namespace bl

@@ -29,18 +29,6 @@
 
 namespace bl {
 
-constexpr int kMaxFusedProj = 8;
-
-struct FusedProjArgs {
-    const uint8_t *packed[kMaxFusedProj];
-    const float *w_scale[kMaxFusedProj];
-    float *Y[kMaxFusedProj];
-    int32_t *acc[kMaxFusedProj];
-    int64_t N[kMaxFusedProj];
-    int32_t block_start[kMaxFusedProj + 1];   // first workgroup of each projection
-    int32_t nproj;
-};
-
 namespace fused {
 
 using skinny::i32x4;
@@ -59,7 +47,9 @@ struct FusedLds {
     static constexpr int kZero = 256;                         // zero block (token rows >= M)
 };
 
-// KS waves split K; at most CMAX chunks per wave; at most MT (<= 4) tokens;
+// KS waves split K; at most CMAX chunks per wave; at most MT (<= 4) tokens
+// per workgroup: more tokens run in tiles of MT along the grid's y (each tile
+// quantises its own token rows and re-reads the weights, mostly from L2);
 // ROWS weight rows per workgroup: 16 (one MFMA column block), 32 (two), or 8
 // (the MFMA's columns 8..15 repeat rows 0..7 and are not stored: twice the
 // workgroups for short matrices).  The activation row (K bytes per token, plus
@@ -84,7 +74,11 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int r = lane & 15, q = lane >> 4;
-    const int mt = (int)M;
+    // token tile blockIdx.y: tokens MT y .. MT y + MT - 1 of the call
+    const int64_t t0 = (int64_t)blockIdx.y * MT;
+    X += t0 * K;
+    if (x_scale_out) x_scale_out += t0;
+    const int mt = (int)min(M - t0, (int64_t)MT);
     const int64_t xstride = K + 192;
 
     // which projection and which rows
@@ -267,8 +261,8 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
             for (int w2 = 1; w2 < KS; ++w2) sum[g2] += s_part[g2][w2 - 1][lane];
     }
 
-    float *Y = args.Y[p];
-    int32_t *acc_out = args.acc[p];
+    float *Y = args.Y[p] + t0 * N;
+    int32_t *acc_out = args.acc[p] ? args.acc[p] + t0 * N : nullptr;
 #pragma unroll
     for (int g2 = 0; g2 < RG; ++g2) {
         const int64_t nn = n0 + 16 * g2 + r;
@@ -290,8 +284,8 @@ hipError_t launch_fused(const float *X, int64_t M, int64_t K, const FusedProjArg
                         float *x_scale, hipStream_t stream)
 {
     const size_t dyn = (size_t)MT * (size_t)(K + 192);
-    hipLaunchKernelGGL((fused_kernel<P, KS, CMAX, MT, ROWS>), dim3((unsigned)blocks), dim3(64 * KS), dyn, stream,
-                       X, M, K, args, x_scale);
+    hipLaunchKernelGGL((fused_kernel<P, KS, CMAX, MT, ROWS>), dim3((unsigned)blocks, (unsigned)((M + MT - 1) / MT)),
+                       dim3(64 * KS), dyn, stream, X, M, K, args, x_scale);
     return hipGetLastError();
 }
 

@@ -16,8 +16,8 @@
 namespace bl {
 namespace {
 
-using Fn = hipError_t (*)(const int8_t *, const float *, const int32_t *, const uint8_t *, const float *,
-                          int64_t, int64_t, int64_t, float *, int32_t *, hipStream_t);
+using Fn = hipError_t (*)(const int8_t *, const float *, const int32_t *, const FusedProjArgs &, int64_t, int64_t,
+                          int64_t, hipStream_t);
 
 constexpr int kKS[] = {1, 2, 4, 8, 16};
 constexpr int kCM[] = {4, 8, 12, 16, 24, 32, 44};
@@ -81,14 +81,22 @@ thread_local char g_name[64];
 
 }  // namespace
 
-// Returns hipErrorNotSupported (and launches nothing) when no configuration
-// fits the shape; the caller then uses another kernel.  With `query` set,
-// launches nothing and returns hipSuccess where it would launch.
-hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
-                                 const float *w_scale, Pattern p, int64_t M, int64_t N, int64_t K, float *Y,
-                                 int32_t *acc, hipStream_t stream, const char **name, bool query)
+// One or more projections sharing Xq (args.block_start is filled here: 16
+// weight rows per workgroup).  Returns hipErrorNotSupported (and launches
+// nothing) when no configuration fits the shape; the caller then uses another
+// kernel.  With `query` set, launches nothing and returns hipSuccess where it
+// would launch.
+hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_t *rs, FusedProjArgs args,
+                                 Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query)
 {
-    if (M < 1 || M > kSkinnyMaxM) return hipErrorNotSupported;
+    if (M < 1 || M > kSkinnyMaxM || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
+    int64_t blocks = 0;
+    for (int i = 0; i < args.nproj; ++i) {
+        args.block_start[i] = (int32_t)blocks;
+        blocks += (args.N[i] + 15) / 16;
+    }
+    for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
+    if (blocks > (1LL << 30)) return hipErrorNotSupported;
     // token rows staged per wave: 1, 4, 8 or 16 (rows past M read a zero
     // block); past 16 tokens, tiles of 16 along the grid's y
     const int mt = (M == 1) ? 1 : (M <= 4) ? 4 : (M <= 8) ? 8 : 16;
@@ -120,11 +128,12 @@ hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_
         case Pattern::NM68: f = pick_p<Pattern::NM68>(mt, ksi, cmi); break;
         }
         if (!f) continue;
-        snprintf(g_name, sizeof g_name, "skinny_mfma_%s_ks%d_c%d_mt%d",
-                 p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", ks, kCM[cmi], mt);
+        snprintf(g_name, sizeof g_name, "skinny_mfma_%s_ks%d_c%d_mt%d%s",
+                 p == Pattern::Dense ? "dense" : p == Pattern::NM24 ? "nm24" : "nm68", ks, kCM[cmi], mt,
+                 args.nproj > 1 ? "_grouped" : "");
         *name = g_name;
         if (query) return hipSuccess;
-        return f(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
+        return f(Xq, xs, rs, args, blocks, M, K, stream);
     }
     return hipErrorNotSupported;
 }

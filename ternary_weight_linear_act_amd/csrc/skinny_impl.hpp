@@ -45,6 +45,32 @@
 #include "common.hpp"
 
 namespace bl {
+
+// Projections served by one launch (q/k/v, or gate/up, sharing their
+// activations): per projection its packed weights, beta, output rows and
+// outputs; block_start[i] is the first workgroup of projection i.
+constexpr int kMaxFusedProj = 8;
+
+struct FusedProjArgs {
+    const uint8_t *packed[kMaxFusedProj];
+    const float *w_scale[kMaxFusedProj];
+    float *Y[kMaxFusedProj];
+    int32_t *acc[kMaxFusedProj];
+    int64_t N[kMaxFusedProj];
+    int32_t block_start[kMaxFusedProj + 1];
+    int32_t nproj;
+};
+
+// the projection of workgroup `block`
+__device__ __forceinline__ int proj_of_block(const FusedProjArgs &args, int block)
+{
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxFusedProj; ++i)
+        if (i < args.nproj && block >= args.block_start[i]) p = i;
+    return p;
+}
+
 namespace skinny {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
@@ -128,12 +154,12 @@ struct SkinnyLds {
 };
 
 // KS waves per workgroup split K; each wave covers at most CMAX chunks; at
-// most MT tokens (M <= MT <= 16).
+// most MT tokens (M <= MT <= 16).  One or more projections that share the
+// activations (args), 16 weight rows per workgroup.
 template <Pattern P, int KS, int CMAX, int MT>
 __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
-    const uint8_t *__restrict__ packed, const float *__restrict__ w_scale, int64_t M, int64_t N,
-    int64_t K, float *__restrict__ Y, int32_t *__restrict__ acc_out)
+    FusedProjArgs args, int64_t M, int64_t K)
 {
     static_assert(CMAX % 4 == 0 && MT >= 1 && MT <= 16, "config");
     using L = SkinnyLds<CMAX, MT>;
@@ -145,15 +171,19 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     // the wave index is wave-uniform: say so, so that branches on it are scalar
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
-    const int64_t n0 = (int64_t)blockIdx.x * 16;
+    const int p = proj_of_block(args, (int)blockIdx.x);
+    const int64_t N = args.N[p];
+    const uint8_t *packed = args.packed[p];
+    const float *w_scale = args.w_scale[p];
+    const int64_t n0 = (int64_t)(blockIdx.x - args.block_start[p]) * 16;
     // token tile blockIdx.y: rows 16 y .. 16 y + 15 of the call's M (then
     // MT = 16); the tiles share nothing, and re-read the weights from L2
     const int64_t t0 = (int64_t)blockIdx.y * 16;
     Xq += t0 * K;
     x_scale += t0;
     x_rowsum += t0;
-    Y += t0 * N;
-    if (acc_out) acc_out += t0 * N;
+    float *Y = args.Y[p] + t0 * N;
+    int32_t *acc_out = args.acc[p] ? args.acc[p] + t0 * N : nullptr;
     M = min(M - t0, (int64_t)MT);
     const int64_t C = K / 64;
     const int mt = (int)M;                           // 1 <= M <= MT
@@ -283,14 +313,14 @@ __global__ __launch_bounds__(64 * KS) void skinny_kernel(
     }
 }
 
+// args.block_start filled by the caller (16 weight rows per workgroup);
+// `blocks` workgroups along x, the 16-token tiles along y
 template <Pattern P, int KS, int CMAX, int MT>
-hipError_t launch_skinny(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
-                         const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
-                         hipStream_t stream)
+hipError_t launch_skinny(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
+                         int64_t blocks, int64_t M, int64_t K, hipStream_t stream)
 {
-    const int64_t blocks = (N + 15) / 16;
     hipLaunchKernelGGL((skinny_kernel<P, KS, CMAX, MT>), dim3((unsigned)blocks, (unsigned)((M + 15) / 16)),
-                       dim3(64 * KS), 0, stream, Xq, xs, rs, packed, w_scale, M, N, K, Y, acc);
+                       dim3(64 * KS), 0, stream, Xq, xs, rs, args, M, K);
     return hipGetLastError();
 }
 

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     for want in ("bitlinear_pack_weights", "bitlinear_quant_act", "bitlinear_forward",
                  "bitlinear_packed_size", "bitlinear_last_error", "bitlinear_last_dispatch",
                  "bitlinear_forward_fused", "bitlinear_quant_act_ex", "bitlinear_forward_fused_ex",
-                 "bitlinear_quant_act_h4", "bitlinear_forward_workspace_size", "bitlinear_forward_noalloc"):
+                 "bitlinear_quant_act_h4", "bitlinear_forward_workspace_size", "bitlinear_forward_noalloc",
+                 "bitlinear_forward_grouped"):
         assert want in names
     # the binding's list is the header's
     assert sorted(binding.EXPORTED) == names
@@ -195,6 +196,22 @@ def test_noalloc_validation(lib):
     assert b"32" in lib.bitlinear_last_error() or b"33554432" in lib.bitlinear_last_error()
 
 
+def test_grouped_validation(lib):
+    from ternary_weight_linear_act_amd.binding import NM, Proj
+    f = lib.bitlinear_forward_grouped
+    arr = (Proj * 9)(*[Proj(A, A, 64, A, None) for _ in range(9)])
+    assert f(P(), P(), P(), 4, 128, NM(0, 0), None, 1, None) == -1           # projs NULL
+    assert f(P(), P(), P(), 4, 128, NM(0, 0), arr, 0, None) == -1            # nproj 0
+    assert f(P(), P(), P(), 4, 128, NM(0, 0), arr, 9, None) == -2            # too many projections
+    assert f(P(), P(), None, 4, 128, NM(0, 0), arr, 1, None) == -1           # row sums required
+    assert f(P(8), P(), P(), 4, 128, NM(0, 0), arr, 1, None) == -1           # misaligned Xq
+    assert f(P(), P(), P(), 4, 100, NM(0, 0), arr, 1, None) == -1            # K % 64
+    assert f(P(), P(), P(), 65, 128, NM(0, 0), arr, 1, None) == -2           # M > 64
+    big = (Proj * 2)(Proj(A, A, 11008, A, None), Proj(A, A, 11008, A, None))
+    assert f(P(), P(), P(), 64, 2048, NM(0, 0), big, 2, None) == -2         # 4 x 1376 workgroups
+    assert f(None, None, None, 0, 128, NM(0, 0), arr, 1, None) == 0          # M = 0: no-op
+
+
 def test_quant_validation(lib):
     q = lib.bitlinear_quant_act
     assert q(None, 4, 64, P(), P(), P(), None) == -1
@@ -264,8 +281,9 @@ def test_fused_validation(lib):
     assert f(P(), 1, 128, NM(0, 0), None, 1, None, None) == -1           # projs NULL
     assert f(P(), 1, 128, NM(0, 0), arr, 0, None, None) == -1            # nproj 0
     assert f(P(), 1, 128, NM(0, 0), arr, 9, None, None) == -2            # too many projections
-    assert f(P(), 5, 128, NM(0, 0), arr, 1, None, None) == -2            # M > 4: use the two-call path
+    assert f(P(), 17, 128, NM(0, 0), arr, 1, None, None) == -2           # M > 16: use the two-call path
     assert f(P(), 2, 16384 + 64, NM(0, 0), arr, 1, None, None) == -2     # shared row too large
+    assert f(P(), 9, 16384 + 64, NM(0, 0), arr, 1, None, None) == -2
     assert f(P(4), 1, 128, NM(0, 0), arr, 1, None, None) == -1           # misaligned X
     assert f(P(), 1, 128, NM(3, 4), arr, 1, None, None) == -2
     bad = (Proj * 1)(Proj(A + 4, A, 64, A, None))

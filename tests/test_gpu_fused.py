@@ -105,13 +105,48 @@ def test_fused_zero_row_and_eight_projections():
     assert not accs[0].cpu().numpy()[0].any()
 
 
+@pytest.mark.parametrize("M", [5, 8, 9, 13, 16])
+@pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
+@pytest.mark.parametrize("K,Ns", [(320, (37, 129)), (2048, (256, 300, 33)), (7936, (100,)), (11008, (70,))])
+def test_fused_token_tiles(M, nm, K, Ns):
+    # 5-16 tokens: tiles of 4 tokens along the grid's y, a ragged last tile,
+    # several projections; against the oracle and bit for bit against the
+    # two-call path
+    import torch
+    seed = 1300 + M * 7 + K + sum(Ns)
+    Ws = [workloads.small_case(seed + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+    _, X = workloads.small_case(seed + 99, M, 8, K, outlier_frac=0.01)
+    print("case fused tiles M=%d K=%d Ns=%s nm=%s" % (M, K, Ns, nm), flush=True)
+    packs, Ys, accs, xs, name = run_fused(Ws, X, nm)
+    assert name.startswith("fused_decode_") and "_mt4_tiles_" in name, name
+    check_against_oracle(Ws, X, nm, Ys, accs, xs)
+    Xq, xs2, rs2 = hip_quant(X)
+    for (pk, ws), W, Y, acc in zip(packs, Ws, Ys, accs):
+        Y2, acc2 = hip_forward(Xq, xs2, rs2, pk, ws, W.shape[0], nm)
+        torch.cuda.synchronize()
+        assert torch.equal(acc, acc2)
+        assert torch.equal(Y.view(torch.int32), Y2.view(torch.int32))
+
+
+@pytest.mark.parametrize("group", [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)])
+def test_block_3b_fused_m8(group):
+    # the 3B block at 8 tokens, one fused launch per input group
+    d = workloads.draw("block_3b", projs=list(group), Ms=(8,))
+    Ws = [d.W[g] for g in group]
+    X = d.X[(group[0], 8)]
+    print("case fused block_3b M=8 %s" % (group,), flush=True)
+    _, Ys, accs, xs, name = run_fused(Ws, X)
+    assert name.startswith("fused_decode_dense"), name
+    check_against_oracle(Ws, X, (0, 0), Ys, accs, xs)
+
+
 def test_fused_unsupported_shapes_raise():
     import torch
     import ternary_weight_linear_act_amd as bl
-    W, X = workloads.small_case(700, 5, 64, 128)
+    W, X = workloads.small_case(700, 17, 64, 128)
     pk, ws = hip_pack(W, (0, 0))
     with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
-        bl.forward_fused(to_dev(X), [(pk, ws, 64)])            # M = 5 > 4
+        bl.forward_fused(to_dev(X), [(pk, ws, 64)])            # M = 17 > 16
     with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
         bl.forward_fused(to_dev(X[:1]), [(pk, ws, 64)] * 9)    # 9 projections
     torch.cuda.synchronize()
