@@ -21,7 +21,9 @@ from .oracle import (  # noqa: F401
     quant_act_ex,
     hadamard_rows,
     quant_act_h4,
+    quant_act_a48,
     forward,
+    forward_a48,
     build,
     LIB_PATH,
 )

@@ -29,6 +29,9 @@
  *  [V2]    The BitNet v2 summary (brain.hanbit.co.kr): the H-BitLinear applies
  *          an online Hadamard transform to the activations, then quantises
  *          them to 4 bits.
+ *  [A48]   [SURV], section "BitNet a4.8: 하이브리드 양자화 전략": the largest
+ *          activation values are split off and kept at 8 bits, the rest is
+ *          quantised to 4 bits, each part with its own scale.
  *
  * Readings where the pages are silent or disagree (each one is listed in the
  * design notes of the repository):
@@ -46,7 +49,13 @@
  *    the row before the codes are taken (it divides out of the codes);
  *  - H-BitLinear: a block-diagonal Sylvester Hadamard transform (blocks of a
  *    power of two B dividing K) in the radix-2 butterfly order, 4-bit absmax
- *    codes 7/max|v| stored in int8, 1/sqrt(B) applied to the scale.
+ *    codes 7/max|v| stored in int8, 1/sqrt(B) applied to the scale;
+ *  - a4.8: the caller gives the number T of outliers per token row (the
+ *    page gives no fraction); they are the T largest |x| of the row, equal
+ *    magnitudes resolved towards the lower k; each part gets its own
+ *    per-row absmax scale (the page's per-channel scaling, read as one scale
+ *    per part and token row: a scale per input channel would not factor out
+ *    of the integer contraction with a per-tensor weight scale).
  */
 #include <math.h>
 #include <stdint.h>
@@ -417,6 +426,98 @@ int oracle_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B,
         if (rowsum) rowsum[r] = sum;
     }
     free(v);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Step 6d: BitNet a4.8's hybrid activations ([A48]: the top values of the  */
+/* activation tensor are separated and handled at 8 bits, the rest is       */
+/* quantised to 4 bits, each part with its own scale).                      */
+/*                                                                          */
+/* For each token row x (K values) and a caller-given outlier count T:      */
+/*  - S = the T largest |x[k]|, found the plain way: T rounds, each taking   */
+/*    the largest not-yet-taken entry, scanning k upwards with a strict '>' */
+/*    (equal magnitudes: the lower k wins);                                 */
+/*  - hi = x on S, 0 elsewhere; lo = x off S, 0 on S (hi + lo = x);          */
+/*  - hi takes the 8-bit quantiser of step 6 (codes in [-127, 127],         */
+/*    x_scale = max|hi| / 127);                                             */
+/*  - lo takes the 4-bit absmax quantiser: g = max|lo|, s = fl32(7 / g)     */
+/*    (same tiny-row rule as step 6), q = rne(fl32(lo * s)) in [-7, 7],      */
+/*    x_scale = fl32(g / 7); a zero part quantises to zeros with scale 0.   */
+/* Outputs: 2M rows, row 2m the hi codes of token m, row 2m+1 its lo codes, */
+/* with their scales and row sums; sel (optional, M x K) marks S.  The      */
+/* linear then runs on the 2M rows, and output m is the sum of rows 2m and  */
+/* 2m+1 of the rescaled result: y = beta (x_hi acc_hi + x_lo acc_lo).        */
+/* ------------------------------------------------------------------------ */
+static void quant4_row(const float *v, int64_t K, int8_t *q, float *x_scale, int32_t *rowsum)
+{
+    float g = 0.0f;
+    for (int64_t k = 0; k < K; ++k)
+        if (fabsf(v[k]) > g) g = fabsf(v[k]);
+    int32_t sum = 0;
+    if (g == 0.0f) {
+        for (int64_t k = 0; k < K; ++k) q[k] = 0;
+        *x_scale = 0.0f;
+    } else {
+        const float pre = (g < 0x1p-100f) ? 0x1p100f : 1.0f;
+        float s = 7.0f / (g * pre);
+        for (int64_t k = 0; k < K; ++k) {
+            float c = rintf((v[k] * pre) * s);
+            if (c > 7.0f) c = 7.0f;
+            if (c < -7.0f) c = -7.0f;
+            q[k] = (int8_t)c;
+            sum += (int32_t)c;
+        }
+        *x_scale = g / 7.0f;
+    }
+    if (rowsum) *rowsum = sum;
+}
+
+int oracle_quant_act_a48(const float *X, int64_t M, int64_t K, int64_t T, int8_t *q, float *x_scale,
+                         int32_t *rowsum, uint8_t *sel)
+{
+    if (!X || !q || !x_scale || M < 0 || K < 1 || T < 0 || T > K) return OR_EINVAL;
+    float *hi = (float *)malloc((size_t)K * sizeof(float));
+    float *lo = (float *)malloc((size_t)K * sizeof(float));
+    uint8_t *taken = (uint8_t *)malloc((size_t)K);
+    if (!hi || !lo || !taken) {
+        free(hi);
+        free(lo);
+        free(taken);
+        return OR_EINVAL;
+    }
+    int rc = OR_OK;
+    for (int64_t r = 0; r < M && rc == OR_OK; ++r) {
+        const float *x = X + r * K;
+        for (int64_t k = 0; k < K; ++k) {
+            if (!isfinite(x[k])) { rc = OR_ENONFINITE; break; }
+            taken[k] = 0;
+        }
+        if (rc != OR_OK) break;
+        for (int64_t round = 0; round < T; ++round) {
+            int64_t best = -1;
+            float best_mag = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                if (taken[k]) continue;
+                float mag = fabsf(x[k]);
+                if (best < 0 || mag > best_mag) {
+                    best = k;
+                    best_mag = mag;
+                }
+            }
+            taken[best] = 1;
+        }
+        for (int64_t k = 0; k < K; ++k) {
+            hi[k] = taken[k] ? x[k] : 0.0f;
+            lo[k] = taken[k] ? 0.0f : x[k];
+            if (sel) sel[r * K + k] = taken[k];
+        }
+        rc = oracle_quant_act(hi, 1, K, 0, q + (2 * r) * K, x_scale + 2 * r, rowsum ? rowsum + 2 * r : NULL);
+        quant4_row(lo, K, q + (2 * r + 1) * K, x_scale + 2 * r + 1, rowsum ? rowsum + 2 * r + 1 : NULL);
+    }
+    free(hi);
+    free(lo);
+    free(taken);
     return rc;
 }
 

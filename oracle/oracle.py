@@ -63,10 +63,11 @@ def _L():
         lib.oracle_quant_act_ex.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp]
         lib.oracle_hadamard_rows.argtypes = [vp, i64, i64, i64]
         lib.oracle_quant_act_h4.argtypes = [vp, i64, i64, i64, vp, vp, vp]
+        lib.oracle_quant_act_a48.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
         lib.oracle_forward.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, i64, vp, vp]
         for f in ("oracle_absmean", "oracle_ternarize", "oracle_nm_keep", "oracle_apply_mask",
                   "oracle_pack_dense", "oracle_pack_nm", "oracle_quant_act", "oracle_quant_act_ex",
-                  "oracle_hadamard_rows", "oracle_quant_act_h4", "oracle_forward"):
+                  "oracle_hadamard_rows", "oracle_quant_act_h4", "oracle_quant_act_a48", "oracle_forward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -205,6 +206,28 @@ def quant_act_h4(X: np.ndarray, B: int):
     rs = np.empty(M, np.int32)
     _check(_L().oracle_quant_act_h4(_p(X), M, K, int(B), _p(q), _p(xs), _p(rs)), "quant_act_h4")
     return q, xs, rs
+
+
+def quant_act_a48(X: np.ndarray, T: int):
+    """BitNet a4.8 hybrid activations with T outliers per row: returns
+    (q int8 2M x K, x_scale fp32 2M, rowsum int32 2M, sel uint8 M x K); row
+    2m holds token m's 8-bit outlier codes, row 2m+1 its 4-bit codes, sel
+    marks the outliers.  See step 6d of the C file."""
+    X = np.ascontiguousarray(X, dtype=np.float32)
+    M, K = X.shape
+    q = np.empty((2 * M, K), np.int8)
+    xs = np.empty(2 * M, np.float32)
+    rs = np.empty(2 * M, np.int32)
+    sel = np.empty((M, K), np.uint8)
+    _check(_L().oracle_quant_act_a48(_p(X), M, K, int(T), _p(q), _p(xs), _p(rs), _p(sel)), "quant_act_a48")
+    return q, xs, rs, sel
+
+
+def forward_a48(q2: np.ndarray, xs2: np.ndarray, w_eff: np.ndarray, beta):
+    """The linear on the 2M hybrid rows, each pair summed: returns (acc int32
+    2M x N, Y binary64 M x N, Y_parts binary64 2M x N)."""
+    acc, Yp = forward(q2, xs2, w_eff, beta)
+    return acc, Yp[0::2] + Yp[1::2], Yp
 
 
 def forward(q: np.ndarray, x_scale: np.ndarray, w_eff: np.ndarray, beta):

@@ -3,8 +3,8 @@
 Each case copies oracle/bitlinear_oracle.c, plants one mistake on the CPU
 (a dropped abs, a wrong divisor, truncation instead of round-half-even, a
 missing epsilon, a wrong tie-break, a misplaced bit, a transposed operand, a
-wrong clamp, a wrong activation constant, a slip in the ReLU^2 gate or the
-RMSNorm), builds it, and runs the pin suite
+wrong clamp, a wrong activation constant, a slip in the ReLU^2 gate, the
+RMSNorm or the a4.8 outlier split), builds it, and runs the pin suite
 against it: the suite must fail for every mutant.
 """
 import os
@@ -22,7 +22,7 @@ MUTANTS = {
     "no_eps": ("float d = beta + 1e-5f;", "float d = beta;"),
     "trunc_not_rne_w": ("float r = rintf(W[i] / d);", "float r = truncf(W[i] / d);"),
     "round_half_away_w": ("float r = rintf(W[i] / d);", "float r = roundf(W[i] / d);"),
-    "tie_to_higher_k": ("if (best < 0 || mag > best_mag)", "if (best < 0 || mag >= best_mag)"),
+    "tie_to_higher_k": ("if (best < 0 || mag > best_mag) { best = i;", "if (best < 0 || mag >= best_mag) { best = i;"),
     "rank_signed": ("float mag = fabsf(w[i]);", "float mag = w[i];"),
     "bit_position": ("int bit = 8 * (j % 4) + 2 * (j / 4);", "int bit = 2 * j;"),
     "code_offset": ("put_code(out + r * (K / 4), k, (unsigned)(v + 1));",
@@ -58,6 +58,16 @@ MUTANTS = {
     "h4_scale_unnormalised": ("x_scale[r] = (float)((double)g / 7.0 / sqrt((double)B));",
                               "x_scale[r] = (float)((double)g / 7.0);"),
     "h4_trunc": ("float c = rintf((v[k] * pre) * s);", "float c = truncf((v[k] * pre) * s);"),
+    "a48_tie_to_higher_k": ("if (best < 0 || mag > best_mag) {\n                    best = k;",
+                            "if (best < 0 || mag >= best_mag) {\n                    best = k;"),
+    "a48_rank_signed": ("float mag = fabsf(x[k]);", "float mag = x[k];"),
+    "a48_one_less": ("for (int64_t round = 0; round < T; ++round)", "for (int64_t round = 1; round < T; ++round)"),
+    "a48_lo_keeps_outliers": ("lo[k] = taken[k] ? 0.0f : x[k];", "lo[k] = x[k];"),
+    "a48_lo_const_8": ("float s = 7.0f / (g * pre);\n        for (int64_t k = 0; k < K; ++k) {\n            float c",
+                       "float s = 8.0f / (g * pre);\n        for (int64_t k = 0; k < K; ++k) {\n            float c"),
+    "a48_lo_scale": ("*x_scale = g / 7.0f;", "*x_scale = g / 8.0f;"),
+    "a48_rows_swapped": ("rc = oracle_quant_act(hi, 1, K, 0, q + (2 * r) * K, x_scale + 2 * r, rowsum ? rowsum + 2 * r : NULL);",
+                         "rc = oracle_quant_act(hi, 1, K, 0, q + (2 * r + 1) * K, x_scale + 2 * r, rowsum ? rowsum + 2 * r : NULL);"),
     "epilogue_no_beta": ("Y[m * N + n] = (double)s * (double)beta * (double)x_scale[m];",
                          "Y[m * N + n] = (double)s * (double)x_scale[m];"),
 }

@@ -721,3 +721,111 @@ class TestForward:
         # and the dequantised product equals the float product of the quantised operands
         deq = (q.astype(np.float64) * xs[:, None].astype(np.float64)) @ (w_eff.astype(np.float64) * float(beta)).T
         assert np.allclose(Y, deq, rtol=1e-12, atol=0)
+
+
+# ==========================================================================
+# BitNet a4.8's hybrid activations ("BitNet 논문 분석", section "BitNet a4.8:
+# 하이브리드 양자화 전략": the top values of the activation tensor are
+# separated and kept at 8 bits, the rest quantised to 4 bits, each part with
+# its own scale).  T outliers per token row, given by the caller.
+# ==========================================================================
+class TestA48:
+    def test_hand_example(self):
+        # x = [0.1, -3, 0.5, 2, -0.25, 0.75, 3, 1].  T = 2: |-3| and |3| tie,
+        # the lower k (1) is taken first, then k = 6.  hi: g = 3, codes
+        # rne(+-3 * fl32(127/3)) = +-127.  lo: g = 2, s = 3.5, codes of
+        # [0.35, 0, 1.75, 7, -0.875, 2.625, 0, 3.5] = [0, 0, 2, 7, -1, 3, 0, 4]
+        # (2.625 -> 3 and 3.5 -> 4: half to even), x_scale 2/7.
+        x = np.array([[0.1, -3.0, 0.5, 2.0, -0.25, 0.75, 3.0, 1.0]], np.float32)
+        q, xs, rs, sel = oracle.quant_act_a48(x, 2)
+        assert q[0].tolist() == [0, -127, 0, 0, 0, 0, 127, 0]
+        assert q[1].tolist() == [0, 0, 2, 7, -1, 3, 0, 4]
+        assert sel[0].tolist() == [0, 1, 0, 0, 0, 0, 1, 0]
+        assert xs[0] == F32(3.0) / F32(127.0) and xs[1] == F32(2.0) / F32(7.0)
+        assert rs.tolist() == [0, 15]
+        # T = 1: only k = 1 (the tie goes to the lower k); lo's max is then 3
+        # (k = 6): s = fl32(7/3), codes of [0.233, 0, 1.167, 4.667, -0.583,
+        # 1.75, 7, 2.333] = [0, 0, 1, 5, -1, 2, 7, 2]
+        q, xs, rs, sel = oracle.quant_act_a48(x, 1)
+        assert sel[0].tolist() == [0, 1, 0, 0, 0, 0, 0, 0]
+        assert q[0].tolist() == [0, -127, 0, 0, 0, 0, 0, 0]
+        assert q[1].tolist() == [0, 0, 1, 5, -1, 2, 7, 2]
+        assert xs[1] == F32(3.0) / F32(7.0)
+
+    def test_selection_brute_force(self):
+        # rows of few distinct magnitudes (many ties), every T: the outliers
+        # are the first T indices ordered by (-|x|, k)
+        rng = np.random.default_rng(41)
+        for K in (1, 2, 5, 8, 13):
+            X = (rng.integers(-3, 4, size=(40, K)) * 0.5).astype(np.float32)
+            for T in range(K + 1):
+                _, _, _, sel = oracle.quant_act_a48(X, T)
+                for m in range(X.shape[0]):
+                    order = sorted(range(K), key=lambda k: (-abs(float(X[m, k])), k))
+                    want = np.zeros(K, np.uint8)
+                    want[order[:T]] = 1
+                    assert np.array_equal(sel[m], want), (K, T, X[m], sel[m])
+
+    def test_no_outliers_is_the_4bit_quantiser(self):
+        # T = 0: the hi rows are zero with scale 0; the lo rows are the 4-bit
+        # absmax codes, which the H-BitLinear quantiser with blocks of 1 (an
+        # identity transform) computes independently
+        X = workloads.activations(np.random.default_rng(42), 16, 320, 0.01)
+        q, xs, rs, _ = oracle.quant_act_a48(X, 0)
+        assert not q[0::2].any() and not xs[0::2].any() and not rs[0::2].any()
+        q4, xs4, rs4 = oracle.quant_act_h4(X, 1)
+        assert np.array_equal(q[1::2], q4) and np.array_equal(rs[1::2], rs4)
+        assert np.array_equal(xs[1::2].view(np.uint32), xs4.view(np.uint32))
+        assert q[1::2].min() >= -7 and q[1::2].max() <= 7
+
+    def test_all_outliers_is_the_8bit_quantiser(self):
+        X = workloads.activations(np.random.default_rng(43), 9, 192, 0.01)
+        q, xs, rs, sel = oracle.quant_act_a48(X, 192)
+        q8, xs8, rs8 = oracle.quant_act(X)
+        assert sel.all()
+        assert np.array_equal(q[0::2], q8) and np.array_equal(rs[0::2], rs8)
+        assert np.array_equal(xs[0::2].view(np.uint32), xs8.view(np.uint32))
+        assert not q[1::2].any() and not xs[1::2].any()
+
+    @pytest.mark.parametrize("T", [1, 3, 26, 100])
+    def test_split_and_reconstruction(self, T):
+        X = workloads.activations(np.random.default_rng(44 + T), 32, 2560, 0.001)
+        q, xs, rs, sel = oracle.quant_act_a48(X, T)
+        a = np.abs(X.astype(np.float64))
+        s = sel.astype(bool)
+        assert np.all(s.sum(1) == T)
+        # every outlier at least as large as every other value of its row
+        assert np.all(np.where(s, a, np.inf).min(1) >= np.where(s, -np.inf, a).max(1))
+        qh, ql = q[0::2].astype(np.float64), q[1::2].astype(np.float64)
+        assert not qh[~s].any() and not ql[s].any()
+        assert np.abs(qh).max() == 127 and np.abs(ql).max(1).min() == 7
+        # each value within half a step of its part's dequantised code
+        sh, sl = xs[0::2].astype(np.float64)[:, None], xs[1::2].astype(np.float64)[:, None]
+        rec = qh * sh + ql * sl
+        step = np.where(s, sh, sl)
+        assert np.all(np.abs(rec - X) <= step * (0.5 + 1e-5))
+        assert np.array_equal(rs[0::2], q[0::2].sum(1, dtype=np.int64))
+        assert np.array_equal(rs[1::2], q[1::2].sum(1, dtype=np.int64))
+
+    def test_zero_and_tiny_rows(self):
+        X = np.zeros((2, 64), np.float32)
+        X[1, 5] = 2.0 ** -126
+        X[1, 9] = -(2.0 ** -127)
+        q, xs, rs, _ = oracle.quant_act_a48(X, 1)
+        assert not q[0:2].any() and not xs[0:2].any()
+        # row 1: the outlier is k = 5; the rest has max 2^-127 at k = 9 and
+        # quantises to -7 (the 2^100 pre-scale keeps 7/g finite)
+        assert q[2, 5] == 127 and q[3, 9] == -7 and q[3, 5] == 0
+        assert xs[3] == F32(2.0 ** -127) / F32(7.0)
+
+    def test_forward_pairs(self):
+        # through an identity weight matrix (t = I), output k of token m is
+        # beta * (x_hi q_hi + x_lo q_lo)[k]: the pairing of rows 2m, 2m+1
+        X = workloads.activations(np.random.default_rng(45), 6, 64, 0.01)
+        q, xs, _, sel = oracle.quant_act_a48(X, 5)
+        w_eff = np.eye(64, dtype=np.int8)
+        acc, Y, Yp = oracle.forward_a48(q, xs, w_eff, 0.5)
+        want = 0.5 * (q[0::2] * xs[0::2].astype(np.float64)[:, None] + q[1::2] * xs[1::2].astype(np.float64)[:, None])
+        assert np.allclose(Y, want, rtol=1e-15, atol=0)
+        assert np.array_equal(acc, q.astype(np.int32))
+        assert np.all(np.abs(Y - 0.5 * X) <= 0.5 * np.where(sel.astype(bool), xs[0::2][:, None], xs[1::2][:, None]) * 0.5 * (1 + 1e-5))
