@@ -330,6 +330,48 @@ def bench_h4(torch, bl, dev, log):
     return res
 
 
+def bench_a48(torch, bl, dev, log):
+    """BitNet a4.8's hybrid activations on the down projection of the
+    2B-class FFN (6912 -> 2560), 1% of each row's values (69) as 8-bit
+    outliers: bitlinear_quant_act_a48, bitlinear_forward on the 2M rows,
+    bitlinear_combine_a48, at one token (weights rotating) and at 2048 tokens;
+    the 8-bit two-call step beside it is in h_bitlinear."""
+    import numpy as np
+    N, K, T = 2560, 6912, 69
+    rng = np.random.default_rng(12)
+    from ternary_weight_linear_act_amd import workloads
+    W = workloads.normal_f32(rng, (N, K), workloads.WEIGHT_SIGMA)
+    pk, ws = bl.pack_weights(torch.from_numpy(W).to(dev))
+    res = {}
+    for M in (1, 2048):
+        X = torch.from_numpy(workloads.activations(rng, M, K, 0.001)).to(dev)
+        P = max(2, -(-POOL_BYTES // pk.numel())) if M == 1 else 1
+        pool = [pk] + [pk.clone() for _ in range(P - 1)]
+        Xq = torch.empty((2 * M, K), dtype=torch.int8, device=dev)
+        xs = torch.empty(2 * M, dtype=torch.float32, device=dev)
+        rs = torch.empty(2 * M, dtype=torch.int32, device=dev)
+        Y2 = torch.empty((2 * M, N), dtype=torch.float32, device=dev)
+        Y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        G = P if M == 1 else 10
+        quant = lambda: bl.quant_act_a48(X, T, Xq, xs, rs)
+        quant()
+        qkern = bl.last_dispatch()
+        fw = lambda j: bl.forward(Xq, xs, rs, pool[j % P], ws, N, Y=Y2)
+        fw(0)
+        fkern = bl.last_dispatch()
+        comb = lambda: bl.combine_a48(Y2, Y)
+        torch.cuda.synchronize()
+        ms_q, _ = timed_graph(torch, lambda: [quant() for _ in range(G)], reps=2)
+        ms_f, _ = timed_graph(torch, lambda: [fw(j) for j in range(G)], reps=2)
+        ms_s, _ = timed_graph(torch, lambda: [(quant(), fw(j), comb()) for j in range(G)], reps=2)
+        res["down_6912x2560_M%d" % M] = {"outliers_per_row": T, "quant_kernel": qkern, "forward_kernel": fkern,
+                                         "quant_us": round(ms_q * 1e3 / G, 3), "forward_us": round(ms_f * 1e3 / G, 3),
+                                         "step_us": round(ms_s * 1e3 / G, 3)}
+        log("a4.8 down M=%d: step %.2f us (quant %.2f, forward of 2M rows %.2f)" % (
+            M, ms_s * 1e3 / G, ms_q * 1e3 / G, ms_f * 1e3 / G))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -543,6 +585,7 @@ def main():
 
     ffn_block = bench_ffn_block(torch, bl, dev, log, Xg[groups[0]], shapes, packed, wsc, P)
     h4 = bench_h4(torch, bl, dev, log)
+    a48 = bench_a48(torch, bl, dev, log)
 
     # ------------------------------------------------------------------ prefill
     dp = workloads.draw("prefill_2048")
@@ -711,6 +754,7 @@ def main():
                  "library_int8_gemm": lib},
         "ffn_block_decode": ffn_block,
         "h_bitlinear": h4,
+        "a4.8": a48,
         "cpu_baseline": cpu,
         "other_workloads": configs,
         "source_digest": digest,

@@ -303,6 +303,32 @@ bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_
 bitlinear_status bitlinear_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t block, int8_t *Xq,
                                         float *x_scale, int32_t *x_rowsum, hipStream_t stream);
 
+/* BitNet a4.8's hybrid activations ("BitNet 논문 분석: 1-Bit LLM의 시대",
+ * section "BitNet a4.8: 하이브리드 양자화 전략": the largest activation
+ * values are split off and kept at 8 bits, the rest is quantised to 4 bits,
+ * each part with its own scale).  For each token row x of X (M x K fp32):
+ *   S = the n_outliers largest |x[k]| (equal magnitudes: the lower k first);
+ *   hi = x on S, 0 elsewhere;  lo = x off S, 0 on S;
+ *   hi -> 8-bit codes exactly as bitlinear_quant_act (scale max|hi| / 127);
+ *   lo -> 4-bit codes: g = max|lo|, s = fl32(7 / fl32(g * u)) (u the tiny-row
+ *         factor above), q = rne(fl32(fl32(lo * u) * s)) in [-7, 7],
+ *         scale fl32(g / 7); a zero part gives zeros and scale 0.
+ * Outputs, 2M rows: Xq row 2m = token m's hi codes, row 2m + 1 its lo codes
+ * (2M x K int8), x_scale and x_rowsum (2M entries; x_rowsum may be NULL).
+ * The two parts share no position, so the linear of token m is the sum of
+ * the linears of rows 2m and 2m + 1: run bitlinear_forward with 2M rows into
+ * a 2M x N output, then bitlinear_combine_a48.  0 <= n_outliers <= K (the
+ * pages give no fraction: the caller chooses it); K <= 16384
+ * (BITLINEAR_EUNSUPPORTED beyond).  Bit-exact with a plain CPU evaluation. */
+bitlinear_status bitlinear_quant_act_a48(const float *X, int64_t M, int64_t K, int64_t n_outliers, int8_t *Xq,
+                                         float *x_scale, int32_t *x_rowsum, hipStream_t stream);
+
+/* Y[m, n] = fl32(Y2[2m, n] + Y2[2m + 1, n]) for the 2M x N output of
+ * bitlinear_forward on bitlinear_quant_act_a48's rows: token m's output is
+ * beta * (x_scale_hi * acc_hi + x_scale_lo * acc_lo).  Within 1e-5 of that
+ * value evaluated in binary64, relative to |hi part| + |lo part|. */
+bitlinear_status bitlinear_combine_a48(const float *Y2, int64_t M, int64_t N, float *Y, hipStream_t stream);
+
 /* Thread-local text for the last non-OK status returned on this thread (the
  * errors of a kernel path are part of what a deployment has to check: "BitNet
  * b1.58은 GPU 없이도 빠를까?", section "전용 커널은 무엇을 비교해야 하나").

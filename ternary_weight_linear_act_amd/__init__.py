@@ -16,6 +16,8 @@ from .binding import (  # noqa: F401
     quant_act,
     quant_act_ex,
     quant_act_h4,
+    quant_act_a48,
+    combine_a48,
     forward,
     forward_workspace_size,
     forward_noalloc,

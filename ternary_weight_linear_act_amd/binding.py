@@ -26,6 +26,8 @@ EXPORTED = (
     "bitlinear_quant_act",
     "bitlinear_quant_act_ex",
     "bitlinear_quant_act_h4",
+    "bitlinear_quant_act_a48",
+    "bitlinear_combine_a48",
     "bitlinear_forward_workspace_size",
     "bitlinear_forward",
     "bitlinear_forward_noalloc",
@@ -85,6 +87,8 @@ def load_library():
     lib.bitlinear_forward_fused.argtypes = [vp, i64, i64, NM, ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     lib.bitlinear_quant_act_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, vp, vp, vp, vp]
     lib.bitlinear_quant_act_h4.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+    lib.bitlinear_quant_act_a48.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp]
+    lib.bitlinear_combine_a48.argtypes = [vp, i64, i64, vp, vp]
     lib.bitlinear_forward_fused_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, NM,
                                                ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     for f in EXPORTED:
@@ -256,6 +260,42 @@ def forward_workspace_size(M: int, N: int, K: int, nm=NM_DENSE) -> int:
     _check("bitlinear_forward_workspace_size", load_library().bitlinear_forward_workspace_size(
         M, N, K, _nm(nm), ctypes.byref(wb)))
     return wb.value
+
+
+def quant_act_a48(X, n_outliers, Xq=None, x_scale=None, x_rowsum=None, stream=None):
+    """BitNet a4.8 hybrid activations: for each row the n_outliers largest |x|
+    at 8 bits, the rest at 4 bits.  Returns (Xq int8 2M x K, x_scale fp32 2M,
+    x_rowsum int32 2M): rows 2m / 2m+1 are token m's 8-bit / 4-bit parts."""
+    import torch
+    _require(X, torch.float32, None, "X")
+    M, K = X.shape
+    if Xq is None:
+        Xq = torch.empty((2 * M, K), dtype=torch.int8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty(2 * M, dtype=torch.float32, device=X.device)
+    if x_rowsum is None:
+        x_rowsum = torch.empty(2 * M, dtype=torch.int32, device=X.device)
+    _require(Xq, torch.int8, (2 * M, K), "Xq")
+    _require(x_scale, torch.float32, (2 * M,), "x_scale")
+    _require(x_rowsum, torch.int32, (2 * M,), "x_rowsum")
+    _check("bitlinear_quant_act_a48", load_library().bitlinear_quant_act_a48(
+        _ptr(X), M, K, int(n_outliers), _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _stream(stream)))
+    return Xq, x_scale, x_rowsum
+
+
+def combine_a48(Y2, Y=None, stream=None):
+    """Y[m] = Y2[2m] + Y2[2m+1]: token m's output from the forward of its two parts."""
+    import torch
+    _require(Y2, torch.float32, None, "Y2")
+    M2, N = Y2.shape
+    if M2 % 2:
+        raise ValueError("Y2 must have an even number of rows")
+    if Y is None:
+        Y = torch.empty((M2 // 2, N), dtype=torch.float32, device=Y2.device)
+    _require(Y, torch.float32, (M2 // 2, N), "Y")
+    _check("bitlinear_combine_a48", load_library().bitlinear_combine_a48(
+        _ptr(Y2), M2 // 2, N, _ptr(Y), _stream(stream)))
+    return Y
 
 
 def forward(Xq, x_scale, x_rowsum, packed, w_scale, N, nm=NM_DENSE, Y=None, acc=None,

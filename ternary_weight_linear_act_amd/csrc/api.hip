@@ -323,6 +323,39 @@ bitlinear_status bitlinear_quant_act_h4(const float *X, int64_t M, int64_t K, in
     return BITLINEAR_OK;
 }
 
+bitlinear_status bitlinear_quant_act_a48(const float *X, int64_t M, int64_t K, int64_t n_outliers, int8_t *Xq,
+                                         float *x_scale, int32_t *x_rowsum, hipStream_t stream)
+{
+    CHECK(check_m(M));
+    CHECK(check_k(K));
+    if (n_outliers < 0 || n_outliers > K)
+        return fail(BITLINEAR_EINVAL, "n_outliers = %lld must be in [0, K = %lld]", (long long)n_outliers,
+                    (long long)K);
+    if (K > 16384) return fail(BITLINEAR_EUNSUPPORTED, "a4.8 activations support K <= 16384 (K = %lld)", (long long)K);
+    if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }
+    CHECK(check_ptr(X, 16, "X"));
+    CHECK(check_ptr(Xq, 16, "Xq"));
+    CHECK(check_ptr(x_scale, 4, "x_scale"));
+    if (x_rowsum && !aligned(x_rowsum, 4)) return fail(BITLINEAR_EINVAL, "x_rowsum must be 4-byte aligned");
+    const hipError_t e = bl::launch_quant_act_a48(X, M, K, n_outliers, Xq, x_scale, x_rowsum, stream);
+    if (e != hipSuccess) return hip_fail("quant_act_a48 launch", e);
+    set_dispatch(K <= 4096 ? "quant_act_a48_256" : "quant_act_a48_1024");
+    return BITLINEAR_OK;
+}
+
+bitlinear_status bitlinear_combine_a48(const float *Y2, int64_t M, int64_t N, float *Y, hipStream_t stream)
+{
+    CHECK(check_m(M));
+    CHECK(check_n(N));
+    if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }
+    CHECK(check_ptr(Y2, 4, "Y2"));
+    CHECK(check_ptr(Y, 4, "Y"));
+    const hipError_t e = bl::launch_a48_combine(Y2, M, N, Y, stream);
+    if (e != hipSuccess) return hip_fail("combine_a48 launch", e);
+    set_dispatch("a48_combine");
+    return BITLINEAR_OK;
+}
+
 bitlinear_status bitlinear_forward_workspace_size(int64_t M, int64_t N, int64_t K, bitlinear_nm nm,
                                                   size_t *workspace_bytes)
 {

@@ -56,6 +56,13 @@ hipError_t launch_skinny_nm24_smfmac(const int8_t *Xq, const float *xs, const ui
 hipError_t launch_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B, int8_t *Xq, float *x_scale,
                                int32_t *x_rowsum, hipStream_t stream, const char **name);
 
+// BitNet a4.8 hybrid activations: 2M rows (hi, lo per token), K <= 16384
+// (hipErrorNotSupported beyond); and the sum of each row pair of the
+// rescaled result.
+hipError_t launch_quant_act_a48(const float *X, int64_t M, int64_t K, int64_t T, int8_t *Xq, float *x_scale,
+                                int32_t *x_rowsum, hipStream_t stream);
+hipError_t launch_a48_combine(const float *Y2, int64_t M, int64_t N, float *Y, hipStream_t stream);
+
 // beta: per-row binary64 |W| sums into `rowsum`, then one ordered sum.
 hipError_t launch_absmean(const float *W, int64_t N, int64_t K, double *rowsum, float *w_scale,
                           hipStream_t stream);

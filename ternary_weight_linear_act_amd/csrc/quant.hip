@@ -447,7 +447,295 @@ hipError_t launch_h4_wave(const float *X, int64_t M, int64_t K, int8_t *Xq, floa
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// BitNet a4.8's hybrid activations ("BitNet 논문 분석: 1-Bit LLM의 시대",
+// section "BitNet a4.8: 하이브리드 양자화 전략": the largest values of the
+// activation tensor are split off and kept at 8 bits, the rest is quantised
+// to 4 bits, each part with its own scale).  Per token row x and a
+// caller-given outlier count T: S = the T largest |x| (equal magnitudes: the
+// lower k first); hi = x on S, lo = x off S; hi gets the 8-bit quantiser
+// (127 / max|hi|), lo the 4-bit one (7 / max|lo|, codes in [-7, 7]), both
+// with the tiny-row rule of common.hpp.  Row 2m of Xq receives token m's hi
+// codes, row 2m + 1 its lo codes, with scales max/127 and max/7.
+//
+// One workgroup per row, the row in registers.  S is found by a radix
+// select over the bit patterns of |x| (for finite values their order as
+// unsigned integers is the order of the magnitudes): four passes of 8 bits,
+// most significant first, each a 256-bin histogram in LDS of the keys that
+// match the digits found so far, then a suffix scan over the bins that finds
+// the digit holding the T-th largest key.  After the last pass the
+// threshold key t and the number r of keys equal to t that belong to S are
+// known; keys above t are in S.  When fewer than all the keys equal to t
+// belong to S (ties at the threshold), the first r in k order are taken: a
+// block-wide exclusive count of the equal keys in k order.
+// ---------------------------------------------------------------------------
+template <int BLOCK>
+__device__ __forceinline__ int block_exclusive_count(int v, int *s_tmp, int *total)
+{
+    constexpr int W = BLOCK / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += o;
+    }
+    if (lane == 63) s_tmp[wave] = incl;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < W; ++w) {
+        const int t = s_tmp[w];
+        before += (w < wave) ? t : 0;
+        all += t;
+    }
+    __syncthreads();
+    *total = all;
+    return before + incl - v;
+}
+
+template <int BLOCK, int NV>
+__global__ __launch_bounds__(BLOCK) void quant_act_a48_kernel(const float *__restrict__ X, int64_t K, int64_t T,
+                                                             int8_t *__restrict__ Xq, float *__restrict__ x_scale,
+                                                             int32_t *__restrict__ x_rowsum)
+{
+    constexpr int W = BLOCK / 64;
+    __shared__ int s_hist[256];
+    __shared__ int s_pick[2];
+    __shared__ int s_tmp[W];
+    __shared__ float s_max[2][W];
+    __shared__ int s_sum[2][W];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const f32x4 *x4 = reinterpret_cast<const f32x4 *>(X + row * K);
+    const int64_t n4 = K / 4;
+
+    f32x4 v[NV];
+    uint32_t key[NV][4];
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int64_t i = tid + (int64_t)j * BLOCK;
+        const f32x4 a = x4[i < n4 ? i : n4 - 1];
+        v[j] = (i < n4) ? a : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) key[j][c] = __float_as_uint(v[j][c]) & 0x7FFFFFFFu;
+    }
+
+    // radix select of the T-th largest key (1 <= T < K; T = 0 selects none,
+    // T = K all)
+    uint32_t thr = 0xFFFFFFFFu;        // keys > thr are selected (none yet)
+    int rank = 0;                      // keys == thr to select, in k order
+    bool ties_split = false;
+    if (T >= K) {
+        thr = 0u;
+        rank = 0;
+        // every key >= 0 selected: treat as "all keys above" by selecting ties too
+    } else if (T > 0) {
+        uint32_t prefix = 0u, mask = 0u;
+        int r = (int)T;
+        int eq_count = 0;
+#pragma unroll
+        for (int pass = 0; pass < 4; ++pass) {
+            const int shift = 24 - 8 * pass;
+            for (int b = tid; b < 256; b += BLOCK) s_hist[b] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int j = 0; j < NV; ++j) {
+                const int64_t i = tid + (int64_t)j * BLOCK;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (i < n4 && (key[j][c] & mask) == prefix) atomicAdd(&s_hist[(key[j][c] >> shift) & 0xFF], 1);
+            }
+            __syncthreads();
+            if (wave == 0) {
+                // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
+                int h[4], own = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    h[c] = s_hist[4 * lane + c];
+                    own += h[c];
+                }
+                int incl = own;           // sum of lanes >= lane
+#pragma unroll
+                for (int d = 1; d < 64; d *= 2) {
+                    const int o = __shfl_down(incl, d, 64);
+                    if (lane + d < 64) incl += o;
+                }
+                int above = incl - own;   // keys in bins of higher lanes
+#pragma unroll
+                for (int c = 3; c >= 0; --c) {
+                    if (above < r && r <= above + h[c]) {
+                        s_pick[0] = 4 * lane + c;
+                        s_pick[1] = r - above;
+                    }
+                    above += h[c];
+                }
+            }
+            __syncthreads();
+            const int digit = s_pick[0];
+            r = s_pick[1];
+            eq_count = s_hist[digit];
+            prefix |= (uint32_t)digit << shift;
+            mask |= 0xFFu << shift;
+            __syncthreads();
+        }
+        thr = prefix;
+        rank = r;
+        ties_split = rank < eq_count;  // workgroup-uniform
+    }
+
+    // selection flags; ties at the threshold split in k order when needed
+    uint32_t selbits[NV];
+    {
+        int base = 0;                  // equal keys in earlier j blocks
+#pragma unroll
+        for (int j = 0; j < NV; ++j) {
+            const int64_t i = tid + (int64_t)j * BLOCK;
+            uint32_t sb = 0;
+            int eqn = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const bool in = i < n4;
+                const bool above = T >= K ? true : (T > 0 && key[j][c] > thr);
+                const bool eq = T > 0 && T < K && key[j][c] == thr;
+                if (in && above) sb |= 1u << c;
+                if (in && eq) eqn++;
+            }
+            if (ties_split) {
+                int tot = 0;
+                const int before = base + block_exclusive_count<BLOCK>(eqn, s_tmp, &tot);
+                int seen = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const bool eq = i < n4 && key[j][c] == thr;
+                    if (eq && before + seen < rank) sb |= 1u << c;
+                    seen += eq ? 1 : 0;
+                }
+                base += tot;
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    if (i < n4 && T > 0 && T < K && key[j][c] == thr) sb |= 1u << c;
+            }
+            selbits[j] = sb;
+        }
+    }
+
+    // the two maxima
+    float gh = 0.0f, gl = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float a = fabsf(v[j][c]);
+            if ((selbits[j] >> c) & 1u) gh = fmaxf(gh, a);
+            else gl = fmaxf(gl, a);
+        }
+    gh = wave_max_dpp(gh);
+    gl = wave_max_dpp(gl);
+    if (lane == 0) {
+        s_max[0][wave] = gh;
+        s_max[1][wave] = gl;
+    }
+    __syncthreads();
+    gh = s_max[0][0];
+    gl = s_max[1][0];
+#pragma unroll
+    for (int w = 1; w < W; ++w) {
+        gh = fmaxf(gh, s_max[0][w]);
+        gl = fmaxf(gl, s_max[1][w]);
+    }
+    const float uph = act_prescale(gh), upl = act_prescale(gl);
+    const float sh = act_scale(gh, uph);                       // 127 / (g * up)
+    const float sl = gl == 0.0f ? 0.0f : 7.0f / (gl * upl);     // 7 / (g * up)
+
+    int *qh4 = reinterpret_cast<int *>(Xq + (2 * row) * K);
+    int *ql4 = reinterpret_cast<int *>(Xq + (2 * row + 1) * K);
+    int sumh = 0, suml = 0;
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+        const int64_t i = tid + (int64_t)j * BLOCK;
+        uint32_t wh = 0, wl = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bool sel = (selbits[j] >> c) & 1u;
+            const uint32_t bh = act_round_bits(v[j][c] * uph, sh);
+            const uint32_t bl = act_round_bits(v[j][c] * upl, sl);
+            const int ch = sel ? (int)(bh - 0x4B400000u) : 0;
+            const int cl = sel ? 0 : (int)(bl - 0x4B400000u);
+            wh |= ((uint32_t)ch & 0xFFu) << (8 * c);
+            wl |= ((uint32_t)cl & 0xFFu) << (8 * c);
+            sumh += ch;
+            suml += cl;
+        }
+        if (i < n4) {
+            qh4[i] = (int)wh;
+            ql4[i] = (int)wl;
+        }
+    }
+    sumh = wave_sum_dpp(sumh);
+    suml = wave_sum_dpp(suml);
+    if (lane == 0) {
+        s_sum[0][wave] = sumh;
+        s_sum[1][wave] = suml;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int th = 0, tl = 0;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            th += s_sum[0][w];
+            tl += s_sum[1][w];
+        }
+        x_scale[2 * row] = (gh == 0.0f) ? 0.0f : gh / 127.0f;
+        x_scale[2 * row + 1] = (gl == 0.0f) ? 0.0f : gl / 7.0f;
+        if (x_rowsum) {
+            x_rowsum[2 * row] = th;
+            x_rowsum[2 * row + 1] = tl;
+        }
+    }
+}
+
+// y[m, n] = Y2[2m, n] + Y2[2m + 1, n]: the rescaled outlier and 4-bit parts
+__global__ __launch_bounds__(256) void a48_combine_kernel(const float *__restrict__ Y2, int64_t M, int64_t N,
+                                                          float *__restrict__ Y)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * N) return;
+    const int64_t m = idx / N, n = idx - m * N;
+    Y[idx] = Y2[(2 * m) * N + n] + Y2[(2 * m + 1) * N + n];
+}
+
 }  // namespace
+
+// The row in registers: K <= 8192 with 256 threads (K <= 2048: one float4
+// each ... 8), K <= 16384 with 1024 threads.  hipErrorNotSupported beyond.
+hipError_t launch_quant_act_a48(const float *X, int64_t M, int64_t K, int64_t T, int8_t *Xq, float *x_scale,
+                                int32_t *x_rowsum, hipStream_t stream)
+{
+    if (M == 0) return hipSuccess;
+    auto go = [&](auto kern, int threads) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)M), dim3(threads), 0, stream, X, K, T, Xq, x_scale, x_rowsum);
+        return hipGetLastError();
+    };
+    const int64_t nv256 = (K / 4 + 255) / 256, nv1024 = (K / 4 + 1023) / 1024;
+    if (K <= 4096) {
+        if (nv256 <= 1) return go(quant_act_a48_kernel<256, 1>, 256);
+        if (nv256 <= 2) return go(quant_act_a48_kernel<256, 2>, 256);
+        return go(quant_act_a48_kernel<256, 4>, 256);
+    }
+    if (nv1024 <= 2) return go(quant_act_a48_kernel<1024, 2>, 1024);
+    if (nv1024 <= 4) return go(quant_act_a48_kernel<1024, 4>, 1024);
+    return hipErrorNotSupported;
+}
+
+hipError_t launch_a48_combine(const float *Y2, int64_t M, int64_t N, float *Y, hipStream_t stream)
+{
+    if (M == 0) return hipSuccess;
+    const int64_t blocks = (M * N + 255) / 256;
+    hipLaunchKernelGGL(a48_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, Y2, M, N, Y);
+    return hipGetLastError();
+}
 
 hipError_t launch_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B, int8_t *Xq, float *x_scale,
                                int32_t *x_rowsum, hipStream_t stream, const char **name)

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
                  "bitlinear_packed_size", "bitlinear_last_error", "bitlinear_last_dispatch",
                  "bitlinear_forward_fused", "bitlinear_quant_act_ex", "bitlinear_forward_fused_ex",
                  "bitlinear_quant_act_h4", "bitlinear_forward_workspace_size", "bitlinear_forward_noalloc",
-                 "bitlinear_forward_grouped"):
+                 "bitlinear_forward_grouped", "bitlinear_quant_act_a48", "bitlinear_combine_a48"):
         assert want in names
     # the binding's list is the header's
     assert sorted(binding.EXPORTED) == names
@@ -210,6 +210,20 @@ def test_grouped_validation(lib):
     big = (Proj * 2)(Proj(A, A, 11008, A, None), Proj(A, A, 11008, A, None))
     assert f(P(), P(), P(), 64, 2048, NM(0, 0), big, 2, None) == -2         # 4 x 1376 workgroups
     assert f(None, None, None, 0, 128, NM(0, 0), arr, 1, None) == 0          # M = 0: no-op
+
+
+def test_a48_validation(lib):
+    q = lib.bitlinear_quant_act_a48
+    assert q(P(), 2, 256, -1, P(), P(), P(), None) == -1         # negative outlier count
+    assert q(P(), 2, 256, 257, P(), P(), P(), None) == -1        # more outliers than inputs
+    assert q(P(), 2, 16448, 10, P(), P(), P(), None) == -2       # K > 16384
+    assert q(P(4), 2, 256, 3, P(), P(), P(), None) == -1         # misaligned X
+    assert q(P(), 2, 100, 3, P(), P(), P(), None) == -1          # K % 64
+    assert q(None, 0, 256, 3, None, None, None, None) == 0       # M = 0
+    c = lib.bitlinear_combine_a48
+    assert c(None, 2, 8, P(), None) == -1
+    assert c(P(), 2, 0, P(), None) == -1
+    assert c(None, 0, 8, None, None) == 0
 
 
 def test_quant_validation(lib):
