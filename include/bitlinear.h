@@ -139,9 +139,11 @@ bitlinear_status bitlinear_quant_act(const float *X, int64_t M, int64_t K,
 
 /* Host-only size query for bitlinear_forward: *workspace_bytes receives the
  * device scratch that an M x N x K call under `nm` needs (0 for most shapes;
- * at most 32 MiB for the few-token GEMMs that split K, whose int32 partial
- * tiles it holds; N*K/4 bytes for N:M weights at 65+ tokens where the 2:4
- * sparse MFMA does not apply, for the rows expanded to dense codes).
+ * at most 32 MiB for the GEMMs that split K -- few tokens, or prefill with
+ * fewer than 128 output tiles of 128 x 128 -- whose int32 partial tiles it
+ * holds; for N:M weights at 65+ tokens where the 2:4 sparse MFMA does not
+ * apply, N*K/4 bytes rounded up to 256 for the rows expanded to dense codes,
+ * plus the partial tiles if the dense GEMM on them splits K).
  * Launches nothing.  Errors: EINVAL for a bad shape or NULL output,
  * EUNSUPPORTED for another N:M pattern. */
 bitlinear_status bitlinear_forward_workspace_size(int64_t M, int64_t N, int64_t K, bitlinear_nm nm,
@@ -165,7 +167,8 @@ bitlinear_status bitlinear_forward_workspace_size(int64_t M, int64_t N, int64_t 
  * weight rows, in tiles of 16 tokens) an MFMA kernel with the tokens as one
  * operand (2:4 with K % 128 == 0 and M <= 16: the sparse MFMA where it
  * measured faster); larger M the MFMA GEMM (K split over workgroups for
- * M <= 64 when the output tiles alone cannot fill the GPU; 2:4 with
+ * M <= 64, or past 64 with fewer than 128 tiles of 128 x 128, when the output
+ * tiles alone cannot fill the GPU; 2:4 with
  * K % 128 == 0 and M >= 128 on the sparse MFMA; other N:M at M >= 65 on the
  * dense GEMM after expanding the rows to dense codes in the workspace).
  * Every path gives the same acc, bit for bit, and the same Y.

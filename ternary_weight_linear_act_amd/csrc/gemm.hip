@@ -840,6 +840,22 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
             auto rounds = [&](int64_t t) { return (double)((t + kCus - 1) / kCus); };
             const double c256 = 4.0 * rounds(tiles(256, 256)), c12 = 2.0 * rounds(tiles(128, 256));
             const double c128 = 1.35 * rounds(tiles(128, 128));
+            // too few 128 x 128 tiles for the chip (deep K, few weight rows:
+            // 512 x 2560 x 6912 has 80): K split over enough workgroups, the
+            // partial tiles in the workspace, as for few tokens
+            if (tiles(128, 128) < kCus / 2 && K / BK >= 8) {
+                const int64_t t = tiles(128, 128);
+                int64_t splits = std::min<int64_t>((kCus + t - 1) / t, (K / BK) / 4);
+                splits = std::min<int64_t>(splits, kMaxSplitBytes / (t * 128 * 128 * 4));
+                if (splits >= 2) {
+                    *name = "gemm_dense_splitk_128x128_w4_s4";
+                    if (!scratch.take((size_t)(splits * t * 128 * 128 * 4)))
+                        return scratch.query ? hipSuccess : hipErrorOutOfMemory;
+                    return launch_dma<128, 128, 2, 2, 4, true>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream,
+                                                               (int32_t)splits,
+                                                               reinterpret_cast<int32_t *>(scratch.ptr));
+                }
+            }
             if (c256 <= c12 && c256 <= c128) {
                 // six stages (120 KB of LDS): 2048 x 6912 x 2560 43.4 -> 42.7
                 // us, 4096 x 8192 x 4096 124 -> 120 us against four; the
@@ -886,27 +902,37 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
         // -> 16.7 us (11.7).
         const bool sparse24 = P == Pattern::NM24 && M >= 128 && K % 128 == 0;
         if (M > 64 && !sparse24) {
-            static const char *expand_names[3][3] = {
-                {"", "", ""},
-                {"gemm_nm24_expand_dense_256x256", "gemm_nm24_expand_dense_128x256", "gemm_nm24_expand_dense_128x128"},
-                {"gemm_nm68_expand_dense_256x256", "gemm_nm68_expand_dense_128x256", "gemm_nm68_expand_dense_128x128"}};
-            const bool go = scratch.take((size_t)N * (size_t)(K / 4));
+            static const char *expand_names[3][4] = {
+                {"", "", "", ""},
+                {"gemm_nm24_expand_dense_256x256", "gemm_nm24_expand_dense_128x256", "gemm_nm24_expand_dense_128x128",
+                 "gemm_nm24_expand_dense_splitk_128x128"},
+                {"gemm_nm68_expand_dense_256x256", "gemm_nm68_expand_dense_128x256", "gemm_nm68_expand_dense_128x128",
+                 "gemm_nm68_expand_dense_splitk_128x128"}};
+            // the expanded rows first, then (256-byte aligned) whatever the
+            // dense GEMM on them needs (K split: its partial tiles)
+            const size_t rows_bytes = ((size_t)N * (size_t)(K / 4) + 255) / 256 * 256;
+            Scratch dense_need;
+            dense_need.query = true;
+            const char *dn = "";
+            dispatch<Pattern::Dense>(Xq, xs, rs, nullptr, w_scale, M, N, K, Y, acc, dense_need, stream, &dn);
+            const bool go = scratch.take(rows_bytes + dense_need.need);
             if (!go && !scratch.query) return hipErrorOutOfMemory;
+            Scratch dense_scratch;
+            dense_scratch.query = scratch.query;
             if (go) {
                 const int64_t chunks = N * (K / 64);
                 hipLaunchKernelGGL(nm_expand_dense_kernel<P>, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0,
                                    stream, packed, N, K, scratch.ptr);
                 const hipError_t e = hipGetLastError();
                 if (e != hipSuccess) return e;
+                dense_scratch.ptr = scratch.ptr + rows_bytes;
+                dense_scratch.bytes = scratch.bytes - rows_bytes;
             }
-            // the dense GEMM at 65+ tokens uses no workspace of its own
-            Scratch dense_scratch;
-            dense_scratch.query = scratch.query;
-            const char *dn = "";
             const hipError_t e = dispatch<Pattern::Dense>(Xq, xs, rs, scratch.ptr, w_scale, M, N, K, Y, acc,
                                                           dense_scratch, stream, &dn);
             const std::string_view d(dn);
-            *name = expand_names[pi][d.find("256x256") != d.npos ? 0 : d.find("128x256") != d.npos ? 1 : 2];
+            *name = expand_names[pi][d.find("256x256") != d.npos ? 0 : d.find("128x256") != d.npos ? 1
+                                     : d.find("splitk") != d.npos ? 3 : 2];
             return e;
         }
         if constexpr (P == Pattern::NM24) {

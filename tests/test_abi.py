@@ -153,9 +153,14 @@ def test_forward_workspace_size(lib):
                           (0, 6912, 2560, (6, 8))]:
         assert work_size(lib, M, N, K, nm) == (0, 0), (M, N, K, nm)
     # N:M rows expanded to dense codes at 65+ tokens off the sparse MFMA:
-    # N * K / 4 bytes
+    # N * K / 4 bytes rounded up to 256 (plus the partial tiles when the
+    # dense GEMM on them splits K)
     assert work_size(lib, 512, 8960, 1536, (6, 8)) == (0, 8960 * 1536 // 4)
-    assert work_size(lib, 100, 4100, 192, (2, 4)) == (0, 4100 * 192 // 4)
+    assert work_size(lib, 100, 4100, 192, (2, 4)) == (0, -(-4100 * 192 // 4 // 256) * 256)
+    rows = -(-512 * 6912 // 4 // 256) * 256
+    assert work_size(lib, 600, 512, 6912, (6, 8)) == (0, rows + 13 * 20 * 128 * 128 * 4)   # 13 splits of 20 tiles
+    # past 64 tokens with fewer than 128 tiles of 128 x 128: K split
+    assert work_size(lib, 512, 2560, 6912, (0, 0)) == (0, 4 * 80 * 128 * 128 * 4)
     # a few-token GEMM splitting K: 64 x 64 tiles (K > 4096, N < 8192), 64
     # tiles, 4 splits of 64 * 64 * 64 int32 partials
     assert work_size(lib, 40, 4096, 8192, (0, 0)) == (0, 4 * 64 * 64 * 64 * 4)

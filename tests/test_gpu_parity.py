@@ -127,7 +127,7 @@ def test_nm_gemm_tbytes(M, N, K, tile, nm):
         # from 65 tokens the rows are expanded to dense codes for the
         # pipelined dense GEMM (these K are not multiples of 128, so 2:4 does
         # not take the sparse MFMA either)
-        assert name == "gemm_nm%d%d_expand_dense_%s" % (nm[0], nm[1], dense_tile(M, N).split("_")[0]), name
+        assert name == "gemm_nm%d%d_expand_dense_%s" % (nm[0], nm[1], expand_tile(M, N, K)), name
     elif skinny_tiles(M, N):
         assert name.startswith("skinny_mfma_nm") and name.endswith("_mt16"), name
     else:
@@ -145,13 +145,44 @@ def test_nm_expand_dense_gemm(M, N, K, nm):
     import ternary_weight_linear_act_amd as bl
     W, X = workloads.small_case(2100 + M + K, M, N, K, outlier_frac=0.001)
     full_check(W, X, nm, rows=cover_rows(M), label="nm-expand-dense")
-    want = "gemm_nm%d%d_expand_dense_%s" % (nm[0], nm[1], dense_tile(M, N).split("_")[0])
+    want = "gemm_nm%d%d_expand_dense_%s" % (nm[0], nm[1], expand_tile(M, N, K))
     assert bl.last_dispatch() == want, bl.last_dispatch()
 
 
-def dense_tile(M, N):
+def expand_tile(M, N, K):
+    t = dense_tile(M, N, K)
+    return "splitk_128x128" if t.startswith("splitk") else t.split("_")[0]
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 2560, 6912), (129, 1000, 4096), (256, 640, 11008), (300, 2000, 512)])
+def test_prefill_split_k(M, N, K):
+    # past 64 tokens with fewer than 128 tiles of 128 x 128: K split over
+    # workgroups, int32 partial tiles in the workspace, a second kernel adds
+    # them; every covering row compared with the oracle
+    import ternary_weight_linear_act_amd as bl
+    assert dense_split(M, N, K) >= 2
+    W, X = workloads.small_case(5100 + M + K, M, N, K, outlier_frac=0.001)
+    full_check(W, X, rows=cover_rows(M), label="prefill-splitk")
+    assert bl.last_dispatch() == "gemm_dense_splitk_128x128_w4_s4", bl.last_dispatch()
+    assert bl.forward_workspace_size(M, N, K) == dense_split(M, N, K) * (-(-M // 128) * -(-N // 128)) * 65536
+
+
+def dense_split(M, N, K):
+    """K splits of the dense GEMM past 64 tokens: fewer than 128 tiles of
+    128 x 128 and at least 8 K slices of 64 -> enough workgroups for the 256
+    compute units, >= 4 slices each, partials within 32 MiB."""
+    t = -(-M // 128) * -(-N // 128)
+    if t >= 128 or K // 64 < 8:
+        return 0
+    return min(-(-256 // t), (K // 64) // 4, (32 << 20) // (t * 128 * 128 * 4))
+
+
+def dense_tile(M, N, K=None):
     """Tile of the pipelined dense GEMM: rounds of tiles over the 256 compute
-    units cost 4 (256 x 256), 2 (128 x 256), 1.35 (128 x 128)."""
+    units cost 4 (256 x 256), 2 (128 x 256), 1.35 (128 x 128); too few 128 x
+    128 tiles split K."""
+    if K is not None and dense_split(M, N, K) >= 2:
+        return "splitk_128x128_w4_s4"
     rounds = lambda bm, bn: -(-(-(-M // bm) * -(-N // bn)) // 256)
     c256, c12, c128 = 4 * rounds(256, 256), 2 * rounds(128, 256), 1.35 * rounds(128, 128)
     if c256 <= c12 and c256 <= c128:
@@ -209,7 +240,7 @@ def test_nm24_sparse_threshold(M):
     W, X = workloads.small_case(1450 + M, M, 1000, 512)
     full_check(W, X, (2, 4), rows=cover_rows(M), label="nm24-threshold")
     if M < 128:
-        want = "gemm_nm24_expand_dense_" + dense_tile(M, 1000).split("_")[0]
+        want = "gemm_nm24_expand_dense_" + expand_tile(M, 1000, 512)
     else:
         want = "gemm_nm24_smfmac_" + nm24_sparse_tile(M, 1000)
     assert bl.last_dispatch() == want, bl.last_dispatch()
