@@ -213,8 +213,48 @@ def bench_configs(torch, bl, workloads, dev, log):
                       "fused_launches": launches,
                       "fused_groups": ["+".join(g) + (" fused" if narrow(g) else " quant_act+grouped")
                                        for g in fused_groups]})
+        if fused_groups and M > 16:
+            # past 16 tokens: one quant_act per input group (not per
+            # projection), then the grouped forward where one launch serves
+            # the group, else the forward per projection
+            Xq_g = {g: torch.empty((M, shapes[g[0]][1]), dtype=torch.int8, device=dev) for g in fused_groups}
+            xs_g = {g: torch.empty(M, dtype=torch.float32, device=dev) for g in fused_groups}
+            rs_g = {g: torch.empty(M, dtype=torch.int32, device=dev) for g in fused_groups}
+            grouped_ok = {}
+            for g in fused_groups:
+                bl.quant_act(X[g[0]], Xq_g[g], xs_g[g], rs_g[g])
+                try:
+                    bl.forward_grouped(Xq_g[g], xs_g[g], rs_g[g], [(pools[n][0], ws[n], shapes[n][0]) for n in g],
+                                       nm=nm_of(g[0]), Ys=[Y[n] for n in g])
+                    grouped_ok[g] = len(g) > 1
+                except bl.BitLinearError:
+                    grouped_ok[g] = False
+
+            def shared(j):
+                for g in fused_groups:
+                    bl.quant_act(X[g[0]], Xq_g[g], xs_g[g], rs_g[g])
+                    if grouped_ok[g]:
+                        bl.forward_grouped(Xq_g[g], xs_g[g], rs_g[g], [(pools[n][j], ws[n], shapes[n][0]) for n in g],
+                                           nm=nm_of(g[0]), Ys=[Y[n] for n in g])
+                    else:
+                        for n in g:
+                            bl.forward(Xq_g[g], xs_g[g], rs_g[g], pools[n][j], ws[n], shapes[n][0], nm=nm_of(n),
+                                       Y=Y[n])
+            shared(0)
+            torch.cuda.synchronize()
+            for n in projs:
+                if not torch.equal(Y[n], Yref[n]):
+                    raise SystemExit("%s: shared-quantisation and two-call outputs differ for %s" % (name, n))
+            ms, _ = timed_graph(torch, lambda: [shared(j % P) for j in range(G)], reps=2)
+            sh = ms * 1e3 / G
+            r.update({"shared_quant_us": round(sh, 3),
+                      "shared_quant_launches": sum(1 + (1 if grouped_ok[g] else len(g)) for g in fused_groups),
+                      "shared_quant_groups": ["+".join(g) + (" quant_act+grouped" if grouped_ok[g] else
+                                                             " quant_act+forward each") for g in fused_groups]})
         res[name] = r
-        log("%-28s M=%-4d two-call %8.2f us%s" % (name, M, us, (" fused %.2f us" % r["fused_us"]) if "fused_us" in r else ""))
+        log("%-28s M=%-4d two-call %8.2f us%s%s" % (name, M, us, (" fused %.2f us" % r["fused_us"]) if "fused_us" in r else "",
+                                                     (" shared quant %.2f us" % r["shared_quant_us"])
+                                                     if "shared_quant_us" in r else ""))
 
     dense = lambda n: (0, 0)
     case("single_1024/M1", "single_1024", ("linear",), 1, dense, [("linear",)])

@@ -337,9 +337,10 @@ bitlinear_status bitlinear_quant_act_a48(const float *X, int64_t M, int64_t K, i
     CHECK(check_ptr(Xq, 16, "Xq"));
     CHECK(check_ptr(x_scale, 4, "x_scale"));
     if (x_rowsum && !aligned(x_rowsum, 4)) return fail(BITLINEAR_EINVAL, "x_rowsum must be 4-byte aligned");
-    const hipError_t e = bl::launch_quant_act_a48(X, M, K, n_outliers, Xq, x_scale, x_rowsum, stream);
+    const char *name = "";
+    const hipError_t e = bl::launch_quant_act_a48(X, M, K, n_outliers, Xq, x_scale, x_rowsum, stream, &name);
     if (e != hipSuccess) return hip_fail("quant_act_a48 launch", e);
-    set_dispatch(K <= 4096 ? "quant_act_a48_256" : "quant_act_a48_1024");
+    set_dispatch(name);
     return BITLINEAR_OK;
 }
 

@@ -60,7 +60,7 @@ hipError_t launch_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B, 
 // (hipErrorNotSupported beyond); and the sum of each row pair of the
 // rescaled result.
 hipError_t launch_quant_act_a48(const float *X, int64_t M, int64_t K, int64_t T, int8_t *Xq, float *x_scale,
-                                int32_t *x_rowsum, hipStream_t stream);
+                                int32_t *x_rowsum, hipStream_t stream, const char **name);
 hipError_t launch_a48_combine(const float *Y2, int64_t M, int64_t N, float *Y, hipStream_t stream);
 
 // beta: per-row binary64 |W| sums into `rowsum`, then one ordered sum.

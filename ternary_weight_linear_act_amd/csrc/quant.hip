@@ -460,10 +460,10 @@ hipError_t launch_h4_wave(const float *X, int64_t M, int64_t K, int8_t *Xq, floa
 //
 // One workgroup per row, the row in registers.  S is found by a radix
 // select over the bit patterns of |x| (for finite values their order as
-// unsigned integers is the order of the magnitudes): four passes of 8 bits,
-// most significant first, each a 256-bin histogram in LDS of the keys that
-// match the digits found so far, then a suffix scan over the bins that finds
-// the digit holding the T-th largest key.  After the last pass the
+// unsigned integers is the order of the magnitudes): three passes of 11, 10
+// and 10 bits, most significant first, each a histogram in LDS of the keys
+// that match the digits found so far, then a suffix scan over the bins that
+// finds the digit holding the T-th largest key.  After the last pass the
 // threshold key t and the number r of keys equal to t that belong to S are
 // known; keys above t are in S.  When fewer than all the keys equal to t
 // belong to S (ties at the threshold), the first r in k order are taken: a
@@ -500,7 +500,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_a48_kernel(const float *__res
                                                              int32_t *__restrict__ x_rowsum)
 {
     constexpr int W = BLOCK / 64;
-    __shared__ int s_hist[256];
+    __shared__ int s_hist[2048];
     __shared__ int s_pick[2];
     __shared__ int s_tmp[W];
     __shared__ float s_max[2][W];
@@ -522,53 +522,60 @@ __global__ __launch_bounds__(BLOCK) void quant_act_a48_kernel(const float *__res
     }
 
     // radix select of the T-th largest key (1 <= T < K; T = 0 selects none,
-    // T = K all)
-    uint32_t thr = 0xFFFFFFFFu;        // keys > thr are selected (none yet)
+    // T = K all): digits of 11, 10 and 10 bits, most significant first (the
+    // keys' top bits are the exponent: 11 bits spread a row's values over
+    // enough bins to keep the LDS atomics from piling onto a few addresses)
+    uint32_t thr = 0xFFFFFFFFu;        // keys > thr are selected
     int rank = 0;                      // keys == thr to select, in k order
     bool ties_split = false;
-    if (T >= K) {
-        thr = 0u;
-        rank = 0;
-        // every key >= 0 selected: treat as "all keys above" by selecting ties too
-    } else if (T > 0) {
+    if (T > 0 && T < K) {
         uint32_t prefix = 0u, mask = 0u;
         int r = (int)T;
         int eq_count = 0;
 #pragma unroll
-        for (int pass = 0; pass < 4; ++pass) {
-            const int shift = 24 - 8 * pass;
-            for (int b = tid; b < 256; b += BLOCK) s_hist[b] = 0;
+        for (int pass = 0; pass < 3; ++pass) {
+            const int shift = pass == 0 ? 20 : pass == 1 ? 10 : 0;
+            const int nbins = pass == 0 ? 2048 : 1024;
+            for (int b = tid; b < nbins; b += BLOCK) s_hist[b] = 0;
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < NV; ++j) {
                 const int64_t i = tid + (int64_t)j * BLOCK;
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    if (i < n4 && (key[j][c] & mask) == prefix) atomicAdd(&s_hist[(key[j][c] >> shift) & 0xFF], 1);
+                    if (i < n4 && (key[j][c] & mask) == prefix)
+                        atomicAdd(&s_hist[(key[j][c] >> shift) & (uint32_t)(nbins - 1)], 1);
             }
             __syncthreads();
             if (wave == 0) {
-                // lane l holds bins 4l .. 4l+3; suffix sums from the top bin down
-                int h[4], own = 0;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    h[c] = s_hist[4 * lane + c];
-                    own += h[c];
-                }
-                int incl = own;           // sum of lanes >= lane
+                // lane l holds bins [l * per, l * per + per): suffix sums over
+                // the lanes find the lane whose bins hold the r-th largest
+                // key, then the lanes take one bin each of that lane's range
+                const int per = nbins / 64;
+                int own = 0;
+                // rotated by the lane, so that the 64 lanes' reads spread over the banks
+                for (int c = 0; c < per; ++c) own += s_hist[lane * per + ((c + lane) & (per - 1))];
+                int incl = own;           // keys in bins of lanes >= lane
 #pragma unroll
                 for (int d = 1; d < 64; d *= 2) {
                     const int o = __shfl_down(incl, d, 64);
                     if (lane + d < 64) incl += o;
                 }
-                int above = incl - own;   // keys in bins of higher lanes
+                const int above = incl - own;
+                const unsigned long long hit = __ballot(above < r && r <= incl);   // exactly one lane
+                const int tl = __ffsll(hit) - 1;
+                const int above_t = __shfl(above, tl, 64);
+                const int h = lane < per ? s_hist[tl * per + lane] : 0;
+                int incl2 = h;
 #pragma unroll
-                for (int c = 3; c >= 0; --c) {
-                    if (above < r && r <= above + h[c]) {
-                        s_pick[0] = 4 * lane + c;
-                        s_pick[1] = r - above;
-                    }
-                    above += h[c];
+                for (int d = 1; d < 64; d *= 2) {
+                    const int o = __shfl_down(incl2, d, 64);
+                    if (lane + d < 64) incl2 += o;
+                }
+                const int above2 = above_t + incl2 - h;
+                if (lane < per && above2 < r && r <= above2 + h) {
+                    s_pick[0] = tl * per + lane;
+                    s_pick[1] = r - above2;
                 }
             }
             __syncthreads();
@@ -576,7 +583,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_a48_kernel(const float *__res
             r = s_pick[1];
             eq_count = s_hist[digit];
             prefix |= (uint32_t)digit << shift;
-            mask |= 0xFFu << shift;
+            mask |= (uint32_t)(nbins - 1) << shift;
             __syncthreads();
         }
         thr = prefix;
@@ -708,10 +715,12 @@ __global__ __launch_bounds__(256) void a48_combine_kernel(const float *__restric
 
 }  // namespace
 
-// The row in registers: K <= 8192 with 256 threads (K <= 2048: one float4
-// each ... 8), K <= 16384 with 1024 threads.  hipErrorNotSupported beyond.
+// The row in registers: up to 8 float4 per thread with 256 threads (K <=
+// 8192), 4 with 1024; 1024 threads per row for up to 512 rows of K >= 4096
+// (latency), else 256 (many rows side by side).  hipErrorNotSupported past
+// K = 16384.
 hipError_t launch_quant_act_a48(const float *X, int64_t M, int64_t K, int64_t T, int8_t *Xq, float *x_scale,
-                                int32_t *x_rowsum, hipStream_t stream)
+                                int32_t *x_rowsum, hipStream_t stream, const char **name)
 {
     if (M == 0) return hipSuccess;
     auto go = [&](auto kern, int threads) {
@@ -719,10 +728,13 @@ hipError_t launch_quant_act_a48(const float *X, int64_t M, int64_t K, int64_t T,
         return hipGetLastError();
     };
     const int64_t nv256 = (K / 4 + 255) / 256, nv1024 = (K / 4 + 1023) / 1024;
-    if (K <= 4096) {
+    const bool wide = (M <= 512 && K >= 4096) || K > 8192;
+    *name = wide ? "quant_act_a48_1024" : "quant_act_a48_256";
+    if (!wide) {
         if (nv256 <= 1) return go(quant_act_a48_kernel<256, 1>, 256);
         if (nv256 <= 2) return go(quant_act_a48_kernel<256, 2>, 256);
-        return go(quant_act_a48_kernel<256, 4>, 256);
+        if (nv256 <= 4) return go(quant_act_a48_kernel<256, 4>, 256);
+        return go(quant_act_a48_kernel<256, 8>, 256);
     }
     if (nv1024 <= 2) return go(quant_act_a48_kernel<1024, 2>, 1024);
     if (nv1024 <= 4) return go(quant_act_a48_kernel<1024, 4>, 1024);
