@@ -147,13 +147,18 @@ def bench_configs(torch, bl, workloads, dev, log):
     plain path before it is timed (fused == two-call, bit for bit)."""
     res = {}
 
-    def case(name, wl_name, projs, M, nm_of, fused_groups=None):
+    def case(name, wl_name, projs, M, nm_of, fused_groups=None, masked=None):
+        # masked: the N:M pattern of weights packed in the dense layout
+        # (bitlinear_pack_weights_masked; nm_of then gives (0, 0))
         wl = workloads.WORKLOADS[wl_name]
         d = workloads.draw(wl_name, projs=projs, Ms=(M,))
         shapes = {p.name: (p.N, p.K) for p in wl.projs if p.name in projs}
         pk, ws = {}, {}
         for n in projs:
-            pk[n], ws[n] = bl.pack_weights(torch.from_numpy(d.W[n]).to(dev), nm=nm_of(n))
+            if masked:
+                pk[n], ws[n] = bl.pack_weights_masked(torch.from_numpy(d.W[n]).to(dev), masked)
+            else:
+                pk[n], ws[n] = bl.pack_weights(torch.from_numpy(d.W[n]).to(dev), nm=nm_of(n))
         wbytes = sum(pk[n].numel() for n in projs)
         P = max(2, -(-POOL_BYTES // wbytes)) if M <= 64 else 1
         pools = {n: [pk[n]] + [pk[n].clone() for _ in range(P - 1)] for n in projs}
@@ -263,6 +268,12 @@ def bench_configs(torch, bl, workloads, dev, log):
     for pn in ("dense", "nm24", "nm68"):
         case("sparse_ffn_1p5b/%s/M1" % pn, "sparse_ffn_1p5b", (pn,), 1, lambda n: nmap[n], [(pn,)])
         case("sparse_ffn_1p5b/%s/M512" % pn, "sparse_ffn_1p5b", (pn,), 512, lambda n: nmap[n])
+        if pn != "dense":
+            # the same N:M weights packed in the dense layout
+            case("sparse_ffn_1p5b/%s_dense_layout/M1" % pn, "sparse_ffn_1p5b", (pn,), 1, dense, [(pn,)],
+                 masked=nmap[pn])
+            case("sparse_ffn_1p5b/%s_dense_layout/M512" % pn, "sparse_ffn_1p5b", (pn,), 512, dense,
+                 masked=nmap[pn])
     blk = ("q", "k", "v", "o", "gate", "up", "down")
     for M in (1, 8, 64):
         case("block_3b/M%d" % M, "block_3b", blk, M, dense,

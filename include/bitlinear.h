@@ -127,6 +127,19 @@ bitlinear_status bitlinear_pack_weights(const float *W, int64_t N, int64_t K, bi
                                         void *workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* N:M weights stored in the dense layout: the same beta, ternary values and
+ * N:M mask as bitlinear_pack_weights with `nm` (quant-then-mask, Sparse-BitNet
+ * review, sec. 3.2), with the pruned positions written as code 01 (t = 0) in
+ * the dense 2-bit layout (N*K/4 bytes: fewer than the 6:8 values+masks
+ * format, as many as 2:4's).  The result feeds bitlinear_forward and the
+ * fused and grouped calls with nm = {0, 0} -- the dense kernels, with no
+ * decoding of masks per call -- and gives the same acc, bit for bit, as the
+ * N:M format.  `nm` must be {2,4} or {6,8} (EINVAL for {0,0}, EUNSUPPORTED
+ * for others); packed_bytes >= N*K/4; workspace as bitlinear_pack_weights. */
+bitlinear_status bitlinear_pack_weights_masked(const float *W, int64_t N, int64_t K, bitlinear_nm nm,
+                                               void *packed, size_t packed_bytes, float *w_scale,
+                                               void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Per-token absmax int8 quantisation of X (M x K fp32): 2B4T summary, sec. 2
  * (8-bit activations, absmax per token); "BitNet 논문 분석", section
  * "Absmean 양자화 함수" (activation_quant).  Xq: M x K int8 output.

@@ -13,6 +13,7 @@ from .binding import (  # noqa: F401
     NM_6_8,
     packed_size,
     pack_weights,
+    pack_weights_masked,
     quant_act,
     quant_act_ex,
     quant_act_h4,

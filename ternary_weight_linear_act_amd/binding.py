@@ -23,6 +23,7 @@ _STATUS = {OK: "OK", EINVAL: "EINVAL", EUNSUPPORTED: "EUNSUPPORTED", ESIZE: "ESI
 EXPORTED = (
     "bitlinear_packed_size",
     "bitlinear_pack_weights",
+    "bitlinear_pack_weights_masked",
     "bitlinear_quant_act",
     "bitlinear_quant_act_ex",
     "bitlinear_quant_act_h4",
@@ -79,6 +80,7 @@ def load_library():
     i64, sz, vp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
     lib.bitlinear_packed_size.argtypes = [i64, i64, NM, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.bitlinear_pack_weights.argtypes = [vp, i64, i64, NM, vp, sz, vp, vp, sz, vp]
+    lib.bitlinear_pack_weights_masked.argtypes = [vp, i64, i64, NM, vp, sz, vp, vp, sz, vp]
     lib.bitlinear_quant_act.argtypes = [vp, i64, i64, vp, vp, vp, vp]
     lib.bitlinear_forward_workspace_size.argtypes = [i64, i64, i64, NM, ctypes.POINTER(sz)]
     lib.bitlinear_forward.argtypes = [vp, vp, vp, vp, vp, NM, i64, i64, i64, vp, vp, vp, sz, vp]
@@ -169,6 +171,27 @@ def pack_weights(W, nm=NM_DENSE, out=None, w_scale=None, workspace=None, stream=
     _check("bitlinear_pack_weights", load_library().bitlinear_pack_weights(
         _ptr(W), N, K, _nm(nm), _ptr(out), out.numel(), _ptr(w_scale), _ptr(workspace), ws_bytes,
         _stream(stream)))
+    return out, w_scale
+
+
+def pack_weights_masked(W, nm, out=None, w_scale=None, workspace=None, stream=None):
+    """N:M-masked ternary weights (nm = (2, 4) or (6, 8)) in the dense 2-bit
+    layout, for forward() with nm = (0, 0).  Returns (packed uint8, w_scale)."""
+    import torch
+    _require(W, torch.float32, None, "W")
+    N, K = W.shape
+    pb, wb = packed_size(N, K, NM_DENSE)
+    if out is None:
+        out = torch.empty(pb, dtype=torch.uint8, device=W.device)
+    if w_scale is None:
+        w_scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    if workspace is None and wb:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
+    _require(out, torch.uint8, None, "packed")
+    _require(w_scale, torch.float32, (1,), "w_scale")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bitlinear_pack_weights_masked", load_library().bitlinear_pack_weights_masked(
+        _ptr(W), N, K, _nm(nm), _ptr(out), out.numel(), _ptr(w_scale), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, w_scale
 
 

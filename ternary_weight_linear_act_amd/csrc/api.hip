@@ -277,6 +277,32 @@ bitlinear_status bitlinear_pack_weights(const float *W, int64_t N, int64_t K, bi
     return BITLINEAR_OK;
 }
 
+bitlinear_status bitlinear_pack_weights_masked(const float *W, int64_t N, int64_t K, bitlinear_nm nm, void *packed,
+                                               size_t packed_bytes, float *w_scale, void *workspace,
+                                               size_t workspace_bytes, hipStream_t stream)
+{
+    bl::Pattern p;
+    CHECK(check_nm(nm, &p));
+    if (p == bl::Pattern::Dense)
+        return fail(BITLINEAR_EINVAL, "bitlinear_pack_weights_masked needs an N:M pattern (2:4 or 6:8)");
+    CHECK(check_n(N));
+    CHECK(check_k(K));
+    CHECK(check_ptr(W, 16, "W"));
+    CHECK(check_ptr(packed, 16, "packed"));
+    CHECK(check_ptr(w_scale, 4, "w_scale"));
+    const size_t need = packed_bytes_for(N, K, bl::Pattern::Dense);
+    if (packed_bytes < need) return fail(BITLINEAR_ESIZE, "packed buffer has %zu bytes, %zu needed", packed_bytes, need);
+    if (workspace_bytes < workspace_bytes_for(N))
+        return fail(BITLINEAR_ESIZE, "workspace has %zu bytes, %zu needed", workspace_bytes, workspace_bytes_for(N));
+    CHECK(check_ptr(workspace, 8, "workspace"));
+    hipError_t e = bl::launch_absmean(W, N, K, static_cast<double *>(workspace), w_scale, stream);
+    if (e != hipSuccess) return hip_fail("absmean launch", e);
+    e = bl::launch_pack_nm_dense(W, N, K, p, w_scale, static_cast<uint8_t *>(packed), stream);
+    if (e != hipSuccess) return hip_fail("pack launch", e);
+    set_dispatch(p == bl::Pattern::NM24 ? "absmean+pack_nm24_dense" : "absmean+pack_nm68_dense");
+    return BITLINEAR_OK;
+}
+
 bitlinear_status bitlinear_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
                                      int32_t *x_rowsum, hipStream_t stream)
 {

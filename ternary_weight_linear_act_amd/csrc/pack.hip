@@ -147,6 +147,53 @@ __global__ __launch_bounds__(kBlock) void pack_nm_kernel(const float *__restrict
     }
 }
 
+// N:M-masked weights in the dense layout: the same mask as pack_nm_kernel
+// (the N largest magnitudes per group of M, ties to the lower k), the kept
+// weights' codes c = t + 1 and code 1 (t = 0) at the pruned positions, 16
+// codes per word.  One thread per (row, 64-weight superblock).
+template <Pattern P>
+__global__ __launch_bounds__(kBlock) void pack_nm_dense_kernel(const float *__restrict__ W, int64_t N, int64_t K,
+                                                               const float *__restrict__ w_scale,
+                                                               uint32_t *__restrict__ out)
+{
+    constexpr int GM = (P == Pattern::NM24) ? 4 : 8;
+    constexpr int GN = (P == Pattern::NM24) ? 2 : 6;
+    const int64_t sbs = K / 64;
+    const float d = w_scale[0] + 1e-5f;
+    for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < N * sbs;
+         idx += (int64_t)gridDim.x * kBlock) {
+        const float4 *w4 = reinterpret_cast<const float4 *>(W + idx * 64);   // row n, superblock sb: contiguous
+        float w[64];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const float4 v = w4[q];
+            w[4 * q + 0] = v.x;
+            w[4 * q + 1] = v.y;
+            w[4 * q + 2] = v.z;
+            w[4 * q + 3] = v.w;
+        }
+        uint32_t words[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int g = 0; g < 64 / GM; ++g) {
+#pragma unroll
+            for (int i = 0; i < GM; ++i) {
+                const float mi = fabsf(w[g * GM + i]);
+                int rank = 0;
+#pragma unroll
+                for (int j = 0; j < GM; ++j) {
+                    const float mj = fabsf(w[g * GM + j]);
+                    rank += (mj > mi) || (j < i && mj == mi);
+                }
+                const int k = g * GM + i;
+                const uint32_t code = rank < GN ? ternary_code(w[k], d) : 1u;
+                words[k >> 4] |= code << code_bit(k & 15);
+            }
+        }
+        uint4 *o = reinterpret_cast<uint4 *>(out + idx * 4);
+        *o = make_uint4(words[0], words[1], words[2], words[3]);
+    }
+}
+
 unsigned grid_for(int64_t items)
 {
     int64_t blocks = (items + kBlock - 1) / kBlock;
@@ -155,6 +202,21 @@ unsigned grid_for(int64_t items)
 }
 
 }  // namespace
+
+hipError_t launch_pack_nm_dense(const float *W, int64_t N, int64_t K, Pattern p, const float *w_scale,
+                                uint8_t *packed, hipStream_t stream)
+{
+    uint32_t *o = reinterpret_cast<uint32_t *>(packed);
+    if (p == Pattern::NM24)
+        hipLaunchKernelGGL(pack_nm_dense_kernel<Pattern::NM24>, dim3(grid_for(N * (K / 64))), dim3(kBlock), 0,
+                           stream, W, N, K, w_scale, o);
+    else if (p == Pattern::NM68)
+        hipLaunchKernelGGL(pack_nm_dense_kernel<Pattern::NM68>, dim3(grid_for(N * (K / 64))), dim3(kBlock), 0,
+                           stream, W, N, K, w_scale, o);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
 
 hipError_t launch_absmean(const float *W, int64_t N, int64_t K, double *rowsum, float *w_scale,
                           hipStream_t stream)

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
                  "bitlinear_packed_size", "bitlinear_last_error", "bitlinear_last_dispatch",
                  "bitlinear_forward_fused", "bitlinear_quant_act_ex", "bitlinear_forward_fused_ex",
                  "bitlinear_quant_act_h4", "bitlinear_forward_workspace_size", "bitlinear_forward_noalloc",
-                 "bitlinear_forward_grouped", "bitlinear_quant_act_a48", "bitlinear_combine_a48"):
+                 "bitlinear_forward_grouped", "bitlinear_quant_act_a48", "bitlinear_combine_a48",
+                 "bitlinear_pack_weights_masked"):
         assert want in names
     # the binding's list is the header's
     assert sorted(binding.EXPORTED) == names
@@ -283,6 +284,16 @@ def test_pack_validation(lib):
     assert p(P(), 8, 64, NM(6, 8), P(), 8 * 16, P(), P(), 256, None) == -3   # 6:8 needs 5/16 bytes per weight
     assert p(P(), 8, 64, NM(7, 8), P(), 8 * 16, P(), P(), 256, None) == -2
     assert p(None, 8, 64, NM(0, 0), P(), 8 * 16, P(), P(), 256, None) == -1
+
+
+def test_pack_masked_validation(lib):
+    from ternary_weight_linear_act_amd.binding import NM
+    p = lib.bitlinear_pack_weights_masked
+    assert p(P(), 8, 64, NM(0, 0), P(), 8 * 16, P(), P(), 256, None) == -1      # needs an N:M pattern
+    assert p(P(), 8, 64, NM(3, 8), P(), 8 * 16, P(), P(), 256, None) == -2
+    assert p(P(), 8, 64, NM(6, 8), P(), 8 * 16 - 1, P(), P(), 256, None) == -3  # dense layout: N*K/4 bytes
+    assert p(P(), 8, 64, NM(6, 8), P(), 8 * 16, P(), P(), 8, None) == -3        # workspace
+    assert p(P(4), 8, 64, NM(2, 4), P(), 8 * 16, P(), P(), 256, None) == -1     # misaligned W
 
 
 def test_binding_has_no_fallback(monkeypatch, tmp_path):

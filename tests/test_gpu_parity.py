@@ -455,3 +455,35 @@ def test_stream_argument():
     q, xs_o, _ = oracle.quant_act(X)
     acc_o, _ = oracle.forward(q, xs_o, w_eff, beta)
     assert np.array_equal(acc.cpu().numpy(), acc_o)
+
+
+@pytest.mark.parametrize("nm", [(2, 4), (6, 8)])
+@pytest.mark.parametrize("N,K,Ms", [(8960, 1536, (1, 8, 512)), (6912, 2560, (1, 64)), (37, 192, (1, 5, 70))])
+def test_pack_masked_dense_layout(nm, N, K, Ms):
+    # N:M weights stored in the dense layout (pruned positions t = 0): the
+    # packed bytes are the oracle's dense packing of W_eff, and the dense
+    # forward on them gives the oracle's accumulators and those of the N:M
+    # format, bit for bit
+    import torch
+
+    import oracle
+    import ternary_weight_linear_act_amd as bl
+    W, _ = workloads.small_case(5300 + N + K, 1, N, K)
+    print("case masked dense layout N=%d K=%d nm=%s" % (N, K, nm), flush=True)
+    pk, ws = bl.pack_weights_masked(to_dev(W), nm)
+    pk_nm, ws_nm = hip_pack(W, nm)
+    torch.cuda.synchronize()
+    beta, w_eff, _ = oracle.quantize_weights(W, *nm)
+    assert np.array_equal(pk.cpu().numpy(), oracle.pack_dense(w_eff))
+    assert ws.cpu().numpy().view(np.uint32)[0] == np.float32(beta).view(np.uint32)
+    for M in Ms:
+        _, X = workloads.small_case(5400 + M, M, 8, K, outlier_frac=0.001)
+        Xq, xs, rs = hip_quant(X)
+        Y, acc = hip_forward(Xq, xs, rs, pk, ws, N, (0, 0))
+        Y2, acc2 = hip_forward(Xq, xs, rs, pk_nm, ws_nm, N, nm)
+        torch.cuda.synchronize()
+        assert torch.equal(acc, acc2), "dense layout and N:M format differ (M=%d)" % M
+        rows = cover_rows(M)
+        q, xs_o, _ = oracle.quant_act(X[rows])
+        acc_o, Y_o = oracle.forward(q, xs_o, w_eff, beta)
+        assert np.array_equal(acc.cpu().numpy()[rows], acc_o)
