@@ -128,14 +128,18 @@ bitlinear_status bitlinear_pack_weights(const float *W, int64_t N, int64_t K, bi
                                         hipStream_t stream);
 
 /* N:M weights stored in the dense layout: the same beta, ternary values and
- * N:M mask as bitlinear_pack_weights with `nm` (quant-then-mask, Sparse-BitNet
+ * N:M mask as bitlinear_pack_weights with `nm` (quant-then-mask, the N
+ * largest |W| per group of M inputs, ties to the lower k; Sparse-BitNet
  * review, sec. 3.2), with the pruned positions written as code 01 (t = 0) in
  * the dense 2-bit layout (N*K/4 bytes: fewer than the 6:8 values+masks
- * format, as many as 2:4's).  The result feeds bitlinear_forward and the
- * fused and grouped calls with nm = {0, 0} -- the dense kernels, with no
- * decoding of masks per call -- and gives the same acc, bit for bit, as the
- * N:M format.  `nm` must be {2,4} or {6,8} (EINVAL for {0,0}, EUNSUPPORTED
- * for others); packed_bytes >= N*K/4; workspace as bitlinear_pack_weights. */
+ * format, as many as 2:4's).  Any 1 <= N <= M with M in {4, 8, 16}: the
+ * review's N:8 sweep (sec. 6.3, Table 7) as well as 2:4 and 6:8.  The result
+ * feeds bitlinear_forward and the fused and grouped calls with nm = {0, 0}
+ * -- the dense kernels, with no decoding of masks per call -- and for 2:4
+ * and 6:8 gives the same acc, bit for bit, as their N:M format.  Errors:
+ * EINVAL for {0,0}, EUNSUPPORTED for another M or N out of range, ESIZE if
+ * packed_bytes < N*K/4 or the workspace (as bitlinear_pack_weights) is
+ * short. */
 bitlinear_status bitlinear_pack_weights_masked(const float *W, int64_t N, int64_t K, bitlinear_nm nm,
                                                void *packed, size_t packed_bytes, float *w_scale,
                                                void *workspace, size_t workspace_bytes, hipStream_t stream);

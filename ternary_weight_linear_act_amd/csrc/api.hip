@@ -281,10 +281,11 @@ bitlinear_status bitlinear_pack_weights_masked(const float *W, int64_t N, int64_
                                                size_t packed_bytes, float *w_scale, void *workspace,
                                                size_t workspace_bytes, hipStream_t stream)
 {
-    bl::Pattern p;
-    CHECK(check_nm(nm, &p));
-    if (p == bl::Pattern::Dense)
-        return fail(BITLINEAR_EINVAL, "bitlinear_pack_weights_masked needs an N:M pattern (2:4 or 6:8)");
+    if (nm.n == 0 && nm.m == 0)
+        return fail(BITLINEAR_EINVAL, "bitlinear_pack_weights_masked needs an N:M pattern");
+    if (!(nm.m == 4 || nm.m == 8 || nm.m == 16) || nm.n < 1 || nm.n > nm.m)
+        return fail(BITLINEAR_EUNSUPPORTED, "masked N:M pattern %d:%d: M must be 4, 8 or 16 and 1 <= N <= M", nm.n,
+                    nm.m);
     CHECK(check_n(N));
     CHECK(check_k(K));
     CHECK(check_ptr(W, 16, "W"));
@@ -297,9 +298,9 @@ bitlinear_status bitlinear_pack_weights_masked(const float *W, int64_t N, int64_
     CHECK(check_ptr(workspace, 8, "workspace"));
     hipError_t e = bl::launch_absmean(W, N, K, static_cast<double *>(workspace), w_scale, stream);
     if (e != hipSuccess) return hip_fail("absmean launch", e);
-    e = bl::launch_pack_nm_dense(W, N, K, p, w_scale, static_cast<uint8_t *>(packed), stream);
+    e = bl::launch_pack_nm_dense(W, N, K, nm.n, nm.m, w_scale, static_cast<uint8_t *>(packed), stream);
     if (e != hipSuccess) return hip_fail("pack launch", e);
-    set_dispatch(p == bl::Pattern::NM24 ? "absmean+pack_nm24_dense" : "absmean+pack_nm68_dense");
+    snprintf(g_dispatch, sizeof g_dispatch, "absmean+pack_nm%d%d_dense", nm.n, nm.m);
     return BITLINEAR_OK;
 }
 

@@ -71,8 +71,9 @@ hipError_t launch_absmean(const float *W, int64_t N, int64_t K, double *rowsum, 
 hipError_t launch_pack(const float *W, int64_t N, int64_t K, Pattern p, const float *w_scale,
                        uint8_t *packed, hipStream_t stream);
 
-// N:M-masked ternary weights in the dense 2-bit layout (pruned: code 1).
-hipError_t launch_pack_nm_dense(const float *W, int64_t N, int64_t K, Pattern p, const float *w_scale,
+// N:M-masked ternary weights (1 <= n <= m, m in {4, 8, 16}) in the dense
+// 2-bit layout (pruned: code 1).
+hipError_t launch_pack_nm_dense(const float *W, int64_t N, int64_t K, int n, int m, const float *w_scale,
                                 uint8_t *packed, hipStream_t stream);
 
 // Forward.  Returns the name of the kernel variant in *name.  With

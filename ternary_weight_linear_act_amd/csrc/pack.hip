@@ -147,17 +147,16 @@ __global__ __launch_bounds__(kBlock) void pack_nm_kernel(const float *__restrict
     }
 }
 
-// N:M-masked weights in the dense layout: the same mask as pack_nm_kernel
-// (the N largest magnitudes per group of M, ties to the lower k), the kept
-// weights' codes c = t + 1 and code 1 (t = 0) at the pruned positions, 16
-// codes per word.  One thread per (row, 64-weight superblock).
-template <Pattern P>
+// N:M-masked weights in the dense layout, for any N <= M with M in {4, 8,
+// 16}: the mask of pack_nm_kernel (the N largest magnitudes per group of M,
+// ties to the lower k), the kept weights' codes c = t + 1 and code 1 (t = 0)
+// at the pruned positions, 16 codes per word.  One thread per (row,
+// 64-weight superblock).
+template <int GM>
 __global__ __launch_bounds__(kBlock) void pack_nm_dense_kernel(const float *__restrict__ W, int64_t N, int64_t K,
-                                                               const float *__restrict__ w_scale,
+                                                               int gn, const float *__restrict__ w_scale,
                                                                uint32_t *__restrict__ out)
 {
-    constexpr int GM = (P == Pattern::NM24) ? 4 : 8;
-    constexpr int GN = (P == Pattern::NM24) ? 2 : 6;
     const int64_t sbs = K / 64;
     const float d = w_scale[0] + 1e-5f;
     for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < N * sbs;
@@ -185,7 +184,7 @@ __global__ __launch_bounds__(kBlock) void pack_nm_dense_kernel(const float *__re
                     rank += (mj > mi) || (j < i && mj == mi);
                 }
                 const int k = g * GM + i;
-                const uint32_t code = rank < GN ? ternary_code(w[k], d) : 1u;
+                const uint32_t code = rank < gn ? ternary_code(w[k], d) : 1u;
                 words[k >> 4] |= code << code_bit(k & 15);
             }
         }
@@ -203,18 +202,17 @@ unsigned grid_for(int64_t items)
 
 }  // namespace
 
-hipError_t launch_pack_nm_dense(const float *W, int64_t N, int64_t K, Pattern p, const float *w_scale,
+hipError_t launch_pack_nm_dense(const float *W, int64_t N, int64_t K, int n, int m, const float *w_scale,
                                 uint8_t *packed, hipStream_t stream)
 {
     uint32_t *o = reinterpret_cast<uint32_t *>(packed);
-    if (p == Pattern::NM24)
-        hipLaunchKernelGGL(pack_nm_dense_kernel<Pattern::NM24>, dim3(grid_for(N * (K / 64))), dim3(kBlock), 0,
-                           stream, W, N, K, w_scale, o);
-    else if (p == Pattern::NM68)
-        hipLaunchKernelGGL(pack_nm_dense_kernel<Pattern::NM68>, dim3(grid_for(N * (K / 64))), dim3(kBlock), 0,
-                           stream, W, N, K, w_scale, o);
-    else
-        return hipErrorInvalidValue;
+    const dim3 grid(grid_for(N * (K / 64)));
+    switch (m) {
+    case 4: hipLaunchKernelGGL(pack_nm_dense_kernel<4>, grid, dim3(kBlock), 0, stream, W, N, K, n, w_scale, o); break;
+    case 8: hipLaunchKernelGGL(pack_nm_dense_kernel<8>, grid, dim3(kBlock), 0, stream, W, N, K, n, w_scale, o); break;
+    case 16: hipLaunchKernelGGL(pack_nm_dense_kernel<16>, grid, dim3(kBlock), 0, stream, W, N, K, n, w_scale, o); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -290,7 +290,9 @@ def test_pack_masked_validation(lib):
     from ternary_weight_linear_act_amd.binding import NM
     p = lib.bitlinear_pack_weights_masked
     assert p(P(), 8, 64, NM(0, 0), P(), 8 * 16, P(), P(), 256, None) == -1      # needs an N:M pattern
-    assert p(P(), 8, 64, NM(3, 8), P(), 8 * 16, P(), P(), 256, None) == -2
+    assert p(P(), 8, 64, NM(3, 6), P(), 8 * 16, P(), P(), 256, None) == -2      # M not 4, 8 or 16
+    assert p(P(), 8, 64, NM(9, 8), P(), 8 * 16, P(), P(), 256, None) == -2      # N > M
+    assert p(P(), 8, 64, NM(0, 8), P(), 8 * 16, P(), P(), 256, None) == -2      # N = 0
     assert p(P(), 8, 64, NM(6, 8), P(), 8 * 16 - 1, P(), P(), 256, None) == -3  # dense layout: N*K/4 bytes
     assert p(P(), 8, 64, NM(6, 8), P(), 8 * 16, P(), P(), 8, None) == -3        # workspace
     assert p(P(4), 8, 64, NM(2, 4), P(), 8 * 16, P(), P(), 256, None) == -1     # misaligned W

@@ -487,3 +487,33 @@ def test_pack_masked_dense_layout(nm, N, K, Ms):
         q, xs_o, _ = oracle.quant_act(X[rows])
         acc_o, Y_o = oracle.forward(q, xs_o, w_eff, beta)
         assert np.array_equal(acc.cpu().numpy()[rows], acc_o)
+
+
+@pytest.mark.parametrize("n,m", [(1, 8), (2, 8), (3, 8), (4, 8), (5, 8), (7, 8), (8, 8), (1, 4), (3, 4),
+                                 (4, 16), (12, 16)])
+def test_nm_sweep_dense_layout(n, m):
+    # the N:8 sweep (and other N:M) on the dense layout: packed bytes equal the
+    # oracle's dense packing of its masked ternary weights; one token and 512
+    # tokens through the dense kernels, accumulators bit-exact
+    import torch
+
+    import oracle
+    import ternary_weight_linear_act_amd as bl
+    N, K = 8960, 1536
+    W, _ = workloads.small_case(5500 + 10 * n + m, 1, N, K)
+    print("case N:M sweep %d:%d" % (n, m), flush=True)
+    pk, ws = bl.pack_weights_masked(to_dev(W), (n, m))
+    torch.cuda.synchronize()
+    beta = oracle.absmean(W)
+    w_eff = oracle.apply_mask(oracle.ternarize(W, beta), oracle.nm_keep(W, n, m))
+    assert np.array_equal(pk.cpu().numpy(), oracle.pack_dense(w_eff))
+    assert ws.cpu().numpy().view(np.uint32)[0] == np.float32(beta).view(np.uint32)
+    for M in (1, 512):
+        _, X = workloads.small_case(5600 + M, M, 8, K, outlier_frac=0.001)
+        Xq, xs, rs = hip_quant(X)
+        Y, acc = hip_forward(Xq, xs, rs, pk, ws, N, (0, 0))
+        torch.cuda.synchronize()
+        rows = cover_rows(M)
+        q, xs_o, _ = oracle.quant_act(X[rows])
+        acc_o, Y_o = oracle.forward(q, xs_o, w_eff, beta)
+        assert np.array_equal(acc.cpu().numpy()[rows], acc_o)

@@ -193,7 +193,8 @@ def brute_keep(w, n):
 
 
 class TestNM:
-    @pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (1, 4), (3, 8), (7, 8), (2, 8), (5, 8)])
+    @pytest.mark.parametrize("n,m", [(2, 4), (6, 8), (1, 4), (3, 8), (7, 8), (2, 8), (5, 8), (1, 8), (4, 8),
+                                     (4, 16), (12, 16)])
     def test_brute_force_with_ties(self, n, m):
         rng = np.random.default_rng(100 + 10 * n + m)
         # magnitudes from a small set -> many ties
