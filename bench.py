@@ -127,6 +127,45 @@ def replay_times(torch, g, n):
     return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
 
 
+def stream_floor(torch, dev, sizes, pool_bytes):
+    """The streaming-read floor per launch at each size: a graph of launches
+    of the probe kernel (ternary_weight_linear_act_amd/probe) over a pool of
+    distinct buffers (pool_bytes in all), best shape; µs per launch."""
+    import ctypes
+    import numpy as np
+    from ternary_weight_linear_act_amd import build as hipbuild
+    if not os.path.exists(hipbuild.PROBE_LIB):
+        raise SystemExit("the streaming probe is not built (%s): run __graft_entry__.build()" % hipbuild.PROBE_LIB)
+    lib = ctypes.CDLL(hipbuild.PROBE_LIB)
+    lib.stream_probe_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    lib.stream_probe_launch.restype = ctypes.c_int64
+    lib.stream_probe_out_words.argtypes = [ctypes.c_int64]
+    lib.stream_probe_out_words.restype = ctypes.c_int64
+    res = {}
+    for nbytes in sizes:
+        nbytes = (nbytes + 15) // 16 * 16
+        P = max(2, pool_bytes // nbytes)
+        pool = torch.ones((P, nbytes), dtype=torch.uint8, device=dev)
+        out = torch.empty(lib.stream_probe_out_words(nbytes), dtype=torch.int32, device=dev)
+        best = None
+        for shape in range(6):
+            def body(shape=shape):
+                s = torch.cuda.current_stream()
+                for j in range(P):
+                    if lib.stream_probe_launch(shape, pool[j].data_ptr(), nbytes, out.data_ptr(),
+                                               ctypes.c_void_p(s.cuda_stream)) < 0:
+                        raise SystemExit("stream probe launch failed")
+            _, g = timed_graph(torch, body, reps=1)
+            us = float(np.median(replay_times(torch, g, 5))) * 1e3 / P
+            if best is None or us < best[0]:
+                best = (us, shape)
+        res[nbytes] = {"us": round(best[0], 3), "GB/s": round(nbytes / (best[0] * 1e-6) / 1e9, 1),
+                       "shape": ["256x7", "256x4", "256x2", "256x1", "512x2", "1024x1"][best[1]]}
+        del pool
+    return res
+
+
 def cpu_model() -> str:
     """The host CPU's model name (lscpu's, from /proc/cpuinfo)."""
     try:
@@ -439,6 +478,9 @@ def main():
     ap.add_argument("--trace-probe", action="store_true",
                     help="replay the decode step's graph over the whole weight pool %d times, then exit "
                          "(the command profiled with rocprofv3 --kernel-trace --stats)" % TRACE_REPLAYS)
+    ap.add_argument("--stream-probe", action="store_true",
+                    help="the streaming-read floor at the decode launches' byte counts beside the fused decode "
+                         "kernels' per-launch times, then exit")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="run the prefill GEMM (2048 x 2560 -> 6912, dense) five times eagerly, then exit "
                          "(the command profiled with rocprofv3 --pmc for its SQ counters)")
@@ -537,6 +579,26 @@ def main():
         return 4 * K + 4 + sum(shapes[n][0] * K // 4 + 4 + 4 * shapes[n][0] for n in g)
     step_bytes = sum(group_bytes(g) for g in groups)
 
+    if args.stream_probe:
+        floor = stream_floor(torch, dev, [group_bytes(g) for g in groups], args.pool_mb << 20)
+        rows = {}
+        for g in groups:
+            def one(g=g):
+                for j in range(P):
+                    bl.forward_fused(Xg[g][j], [(packed[n][j], wsc[n], shapes[n][0]) for n in g],
+                                     Ys=[Y[n] for n in g])
+            _, gg = timed_graph(torch, one, reps=1)
+            us = float(np.median(replay_times(torch, gg, 5))) * 1e3 / P
+            fb = floor[(group_bytes(g) + 15) // 16 * 16]
+            rows["+".join(g)] = {"kernel": group_kernel["+".join(g)], "bytes": group_bytes(g), "us": round(us, 3),
+                                 "floor_us": fb["us"], "floor_shape": fb["shape"],
+                                 "floor_fraction": round(fb["us"] / us, 3)}
+            log("%s: %.3f us per launch; streaming-read floor %.3f us (%s): %.0f%% of the floor's speed" % (
+                "+".join(g), us, fb["us"], fb["shape"], 100 * fb["us"] / us))
+        print(json.dumps({"stream_probe": rows, "pool_MB": args.pool_mb, "source_digest": source_digest()}),
+              flush=True)
+        return
+
     if args.trace_probe:
         # the bench's graph form, for rocprofv3 --kernel-trace: a graph of P
         # decode steps over the whole pool, replayed TRACE_REPLAYS times
@@ -605,6 +667,14 @@ def main():
                                   "bytes": group_bytes(g)}
     fused_us = float(np.mean(launch_us))
     fused_gbs = step_bytes / (sum(launch_us) * 1e-6) / 1e9
+    # the streaming-read floor at the same byte counts (a kernel that only
+    # reads them), measured the same way
+    floor = stream_floor(torch, dev, [group_bytes(g) for g in groups], args.pool_mb << 20)
+    for g in groups:
+        fb = floor[(group_bytes(g) + 15) // 16 * 16]
+        pg = per_group["+".join(g)]
+        pg.update({"floor_us": fb["us"], "floor_fraction": round(fb["us"] / pg["us"], 3)})
+    floor_step_us = sum(floor[(group_bytes(g) + 15) // 16 * 16]["us"] for g in groups)
 
     # context: the two-call path (quant_act, then forward per projection)
     Xq1, xs1, rs1 = {}, {}, {}
@@ -788,6 +858,7 @@ def main():
                      "frac_source": "HIP events: a graph of one launch per pool entry per input group, "
                                     "replayed for >= 20 ms, median per launch (inter-launch gaps included)",
                      "frac_trace": frac_trace, "trace_avg_us": trace_us,
+                     "frac_streaming_floor": round(step_bytes / (floor_step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "kernel": dispatch, "avg_launch_us": round(fused_us, 3),
                      "bytes_per_launch": round(step_bytes / len(groups)), "per_group": per_group},
         "protocol": protocol,

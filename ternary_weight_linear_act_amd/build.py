@@ -40,6 +40,22 @@ CFLAGS = [
 ]
 
 
+PROBE_SRC = os.path.join(HERE, "probe", "stream_probe.hip")
+PROBE_LIB = os.path.join(HERE, "probe", "libstreamprobe.so")
+
+
+def build_probe(verbose: bool = True) -> str:
+    """The streaming-read probe bench.py's --stream-probe leg loads (not part
+    of the BitLinear path)."""
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *CFLAGS, "-shared", "-o", tmp, PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.check_call(cmd, stderr=subprocess.DEVNULL if not verbose else None)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     procs = []
@@ -67,6 +83,7 @@ def build(verbose: bool = True) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 
