@@ -13,7 +13,7 @@ streams its weights from HBM.  Steps are captured in a HIP graph and timed
 with HIP events on the capture's stream, bracketed by device synchronisation.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
-                       [--traffic-probe] [--gemm-probe]
+                       [--pool-mb MB] [--traffic-probe] [--trace-probe] [--stream-probe] [--gemm-probe]
 Prints one JSON line on stdout; a readable summary goes to stderr.
 """
 from __future__ import annotations
