@@ -14,6 +14,9 @@ with HIP events on the capture's stream, bracketed by device synchronisation.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
                        [--pool-mb MB] [--traffic-probe] [--trace-probe] [--stream-probe] [--gemm-probe]
+       python bench.py --trace-summary TRACE_DIR PROBE_OUT
+       python bench.py --traffic-summary FETCH_DIR WRITE_DIR PROBE_OUT
+       python bench.py --stats-summary TRACE_DIR OUT_MD TITLE COMMAND
 Prints one JSON line on stdout; a readable summary goes to stderr.
 """
 from __future__ import annotations
@@ -49,12 +52,224 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# The files the fused one-token decode kernel is built from (and its build
+# flags): the committed kernel trace and HBM traffic describe that kernel only
+# while these are unchanged.
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode_dot4.hip", "decode_dot4_impl.hpp", "fused_impl.hpp",
+                                                  "skinny_impl.hpp", "common.hpp")] + [
+    os.path.join(ROOT, "include", "bitlinear.h"), os.path.join(ROOT, "ternary_weight_linear_act_amd", "build.py")]
+
+
 def source_digest() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
+    for path in DECODE_SOURCES:
+        with open(path, "rb") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# Summaries of rocprofv3 output (CSV) into the files under profiles/ that the
+# bench line reads: the kernel trace of --trace-probe, the FETCH_SIZE /
+# WRITE_SIZE counters of --traffic-probe.
+
+def _csv_rows(dirpath, suffix):
+    import csv
+    for root, _, files in sorted(os.walk(dirpath)):
+        for f in sorted(files):
+            if f.endswith(suffix):
+                with open(os.path.join(root, f), newline="") as fh:
+                    return list(csv.DictReader(fh))
+    raise SystemExit("no *%s under %s" % (suffix, dirpath))
+
+
+def _probe_json(path):
+    for line in reversed(open(path).read().splitlines()):
+        line = line.strip()
+        if line.startswith("{"):
+            return json.loads(line)
+    raise SystemExit("no JSON line in %s" % path)
+
+
+def _dot4_args(text):
+    """Template arguments (pattern, LPR, U, fused, W, TR) of a decode_dot4
+    kernel, from a demangled symbol or from a dispatch name such as
+    fused_decode_dot4_dense_lpr8_u5_p2_w8; None for other kernels."""
+    import re
+    m = re.match(r"(fused_)?decode_dot4_(dense|nm24|nm68)_lpr(\d+)_u(\d+)_p\d+(_w8)?(_gate_norm|_gate|_norm)?$", text)
+    if m:
+        tr = {None: 0, "_gate": 1, "_norm": 2, "_gate_norm": 3}[m.group(6)]
+        return (m.group(2), int(m.group(3)), int(m.group(4)), m.group(1) is not None, 8 if m.group(5) else 4, tr)
+    i = text.find("decode_dot4_kernel<")
+    if i < 0:
+        return None
+    a = [x.strip() for x in text[i + len("decode_dot4_kernel<"):].split(">")[0].split(",")]
+    if len(a) != 6:
+        return None
+    pat = "dense" if (a[0].endswith("Dense") or a[0].endswith(")0")) else \
+          "nm24" if (a[0].endswith("NM24") or a[0].endswith(")1")) else "nm68"
+    return (pat, int(a[1]), int(a[2]), a[3] == "true", int(a[4]), int(a[5]))
+
+
+def _symbol(name):
+    """A demangled kernel name without its parameter list (the balanced
+    parenthesised group at its end)."""
+    name = name.strip()
+    if not name.endswith(")"):
+        return name
+    depth = 0
+    for i in range(len(name) - 1, -1, -1):
+        depth += {")": 1, "(": -1}.get(name[i], 0)
+        if depth == 0:
+            return name[:i]
+    return name
+
+
+def _kernel_name(row):
+    for k in ("Kernel_Name", "Kernel-Name", "KernelName", "Name"):
+        if k in row:
+            return row[k]
+    raise KeyError("kernel name column")
+
+
+def trace_summary(trace_dir, probe_out):
+    """profiles/trace_fused_decode_ffn_2b.{json,md} from the kernel trace of
+    `rocprofv3 --kernel-trace --stats --output-format csv -- python3 bench.py
+    --trace-probe` (trace_dir) and that run's JSON line (probe_out)."""
+    import numpy as np
+    probe = _probe_json(probe_out)
+    rows = _csv_rows(trace_dir, "kernel_trace.csv")
+    stats = {_kernel_name(r): r for r in _csv_rows(trace_dir, "kernel_stats.csv")}
+    groups = dict(x.split(": ") for x in probe["kernel"].split(", "))
+    kernels = {}
+    for g, disp in groups.items():
+        want = _dot4_args(disp)
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows
+                if _dot4_args(_kernel_name(r)) == want]
+        syms = sorted({_kernel_name(r) for r in rows if _dot4_args(_kernel_name(r)) == want})
+        if not durs:
+            raise SystemExit("no traced dispatch of %s" % disp)
+        st = stats.get(syms[0], {})
+        kernels[disp] = {"group": g, "symbol": _symbol(syms[0]), "dispatches": len(durs),
+                         "avg_us": round(float(np.mean(durs)), 3), "median_us": round(float(np.median(durs)), 3),
+                         "p10_us": round(float(np.percentile(durs, 10)), 3),
+                         "p90_us": round(float(np.percentile(durs, 90)), 3),
+                         "stats_avg_us": round(float(st["AverageNs"]) / 1e3, 3) if "AverageNs" in st else None}
+    cmd = ("rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/trace_probe -o trace "
+           "-- python3 $R/bench.py --trace-probe > $R/gpurun_out/trace_probe.out")
+    out = {"workload": "decode_ffn_2b M=1: the bench's graph of whole-pool decode steps, replayed %d times"
+                       % probe["replays"],
+           "command": cmd, "source_digest": probe["source_digest"],
+           "us_per_step_events": probe["us_per_step_events"], "kernels": kernels}
+    with open(TRACE_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    md = ["# Kernel trace of the fused decode kernel, decode_ffn_2b at M=1", "",
+          "Command (run from /tmp with TMPDIR=/tmp, repository at $R), then the summary:", "",
+          "    " + cmd,
+          "    python3 $R/bench.py --trace-summary $R/gpurun_out/trace_probe $R/gpurun_out/trace_probe.out", "",
+          "Source digest of the decode kernel's sources: %s" % probe["source_digest"], "",
+          "The probe replays the bench's graph (%d decode steps over the rotating weight pool) %d times; "
+          "HIP events over those replays gave %.3f us per step.  Kernel-trace durations time each "
+          "dispatch alone (first wave start to last wave end)." % (probe["steps_per_replay"], probe["replays"],
+                                                                  probe["us_per_step_events"]), "",
+          "| group | dispatch | kernel | dispatches | avg us | median us | p10 us | p90 us |",
+          "|---|---|---|---:|---:|---:|---:|---:|"]
+    for disp, k in kernels.items():
+        md.append("| %s | `%s` | `%s` | %d | %.3f | %.3f | %.3f | %.3f |" % (
+            k["group"], disp, k["symbol"], k["dispatches"], k["avg_us"], k["median_us"], k["p10_us"], k["p90_us"]))
+    with open(TRACE_FILE[:-5] + ".md", "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(out))
+
+
+def stats_summary(trace_dir, out_md, title, command):
+    """A Markdown table of rocprofv3's kernel statistics (`--stats`, CSV) for
+    the kernels of this library, with the command that made them."""
+    rows = _csv_rows(trace_dir, "kernel_stats.csv")
+    md = ["# " + title, "", "Command (run from /tmp with TMPDIR=/tmp, repository at $R), then the summary:", "",
+          "    " + command,
+          "    python3 $R/bench.py --stats-summary %s %s '%s' '%s'" % (trace_dir, out_md, title, command), "",
+          "Every dispatch of the run (warm-up, eager checks, graph replays); kernel-trace durations time each "
+          "dispatch alone.  Kernels of this library (`bl::`) and the vendor GEMM (`Cijk_`):", "",
+          "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
+    for r in rows:
+        name = _symbol(r["Name"]).replace("void ", "")
+        if not (name.startswith("bl::") or name.startswith("Cijk_")):
+            continue
+        if name.startswith("Cijk_"):
+            name = name[:40] + "..."
+        md.append("| `%s` | %s | %.3f | %.3f | %.3f |" % (name, r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                          float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+
+
+def traffic_summary(fetch_dir, write_dir, probe_out):
+    """profiles/traffic_fused_decode_ffn_2b.{json,md} from `rocprofv3 --pmc
+    FETCH_SIZE` and `--pmc WRITE_SIZE` runs of `bench.py --traffic-probe`:
+    HBM bytes per dispatch of the fused decode kernels, each counter scaled by
+    its reading for the probe's device copy of copy_bytes (read and written
+    once)."""
+    import numpy as np
+    probe = _probe_json(probe_out)
+    copy_bytes = probe["copy_bytes"]
+    groups = dict(x.split(": ") for x in probe["kernel"].split(", "))
+
+    def per_kernel(dirpath, counter):
+        vals = {}
+        for r in _csv_rows(dirpath, "counter_collection.csv"):
+            if r.get("Counter_Name") == counter:
+                vals.setdefault(_kernel_name(r), []).append(float(r["Counter_Value"]) * 1024.0)
+        return vals
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    # the calibration copy is the largest device copy of the run (the others
+    # are the clones that fill the weight pool)
+    copy_f = [x for k, v in fetch.items() if "copyBuffer" in k for x in v]
+    copy_w = [x for k, v in write.items() if "copyBuffer" in k for x in v]
+    if not copy_f or not copy_w:
+        raise SystemExit("the calibration copy was not counted")
+    fetch_scale = copy_bytes / max(copy_f)
+    write_scale = copy_bytes / max(copy_w)
+    per = {}
+    for g, disp in groups.items():
+        want = _dot4_args(disp)
+        fk = [k for k in fetch if _dot4_args(k) == want]
+        wk = [k for k in write if _dot4_args(k) == want]
+        if not fk or not wk:
+            raise SystemExit("no counted dispatch of %s" % disp)
+        fb = float(np.mean(fetch[fk[0]])) * fetch_scale
+        wb = float(np.mean(write[wk[0]])) * write_scale
+        per[disp] = {"group": g, "symbol": _symbol(fk[0]), "dispatches": len(fetch[fk[0]]),
+                     "fetch_bytes": round(fb), "write_bytes": round(wb), "hbm_bytes": round(fb + wb)}
+    cmds = ["rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/pmc_fetch -o p "
+            "-- python3 $R/bench.py --traffic-probe > $R/gpurun_out/pmc_fetch.out",
+            "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/pmc_write -o p "
+            "-- python3 $R/bench.py --traffic-probe > $R/gpurun_out/pmc_write.out"]
+    out = {"workload": "decode_ffn_2b M=1", "commands": cmds, "source_digest": probe["source_digest"],
+           "fetch_scale": fetch_scale, "write_scale": write_scale, "per_kernel": per,
+           "hbm_bytes_per_launch": round(float(np.mean([v["hbm_bytes"] for v in per.values()])))}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    md = ["# HBM traffic of the fused decode kernel, decode_ffn_2b at M=1", "",
+          "Commands (run from /tmp with TMPDIR=/tmp, repository at $R), then the summary:", ""] + \
+         ["    " + c for c in cmds] + \
+         ["    python3 $R/bench.py --traffic-summary $R/gpurun_out/pmc_fetch $R/gpurun_out/pmc_write "
+          "$R/gpurun_out/pmc_fetch.out", "",
+          "Source digest of the decode kernel's sources: %s" % probe["source_digest"], "",
+          "Calibration: the probe's device copy of %d bytes reads FETCH_SIZE scale %.4f and WRITE_SIZE "
+          "scale %.4f (bytes per counted byte)." % (copy_bytes, fetch_scale, write_scale), "",
+          "| group | dispatch | dispatches | HBM read B | HBM write B | total B per launch |",
+          "|---|---|---:|---:|---:|---:|"]
+    for disp, k in per.items():
+        md.append("| %s | `%s` | %d | %d | %d | %d |" % (k["group"], disp, k["dispatches"], k["fetch_bytes"],
+                                                         k["write_bytes"], k["hbm_bytes"]))
+    md += ["", "Average over the launches of a step: %d B of HBM traffic per launch (the `traffic` field of "
+               "the bench line's roofline object while the decode kernel's sources are unchanged)."
+           % out["hbm_bytes_per_launch"]]
+    with open(TRAFFIC_FILE[:-5] + ".md", "w") as f:
+        f.write("\n".join(md) + "\n")
+    print(json.dumps(out))
 
 
 def fwd_bytes(M, N, K, nm=(0, 0)):
@@ -125,6 +340,18 @@ def replay_times(torch, g, n):
     torch.cuda.synchronize()
     import numpy as np
     return np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+
+
+def steady_us(torch, body, per_replay, warm_ms=20.0, timed_ms=PROTOCOL_MS):
+    """Steady-state time of one launch: body() (per_replay launches) captured
+    into a graph, replayed untimed for >= warm_ms (the clocks settle under a
+    sustained matrix-core load), then replayed for >= timed_ms with each
+    replay timed on its own; the median replay / per_replay, in us."""
+    import numpy as np
+    ms1, g = timed_graph(torch, body, reps=1)
+    replay_times(torch, g, max(1, int(math.ceil(warm_ms / ms1))))
+    t = replay_times(torch, g, max(10, int(math.ceil(timed_ms / ms1))))
+    return float(np.median(t)) * 1e3 / per_replay
 
 
 def stream_floor(torch, dev, sizes, pool_bytes):
@@ -484,7 +711,26 @@ def main():
     ap.add_argument("--gemm-probe", action="store_true",
                     help="run the prefill GEMM (2048 x 2560 -> 6912, dense) five times eagerly, then exit "
                          "(the command profiled with rocprofv3 --pmc for its SQ counters)")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("TRACE_DIR", "PROBE_OUT"),
+                    help="write profiles/trace_fused_decode_ffn_2b.{json,md} from rocprofv3's CSV output of a "
+                         "--trace-probe run and that run's stdout, then exit (no GPU)")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_OUT"),
+                    help="write profiles/traffic_fused_decode_ffn_2b.{json,md} from rocprofv3's CSV output of "
+                         "the FETCH_SIZE and WRITE_SIZE runs of --traffic-probe and one run's stdout, then exit "
+                         "(no GPU)")
+    ap.add_argument("--stats-summary", nargs=4, metavar=("TRACE_DIR", "OUT_MD", "TITLE", "COMMAND"),
+                    help="write a Markdown table of rocprofv3's kernel statistics (CSV) under TRACE_DIR, then exit "
+                         "(no GPU)")
     args = ap.parse_args()
+    if args.stats_summary:
+        stats_summary(*args.stats_summary)
+        return
+    if args.trace_summary:
+        trace_summary(*args.trace_summary)
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -570,7 +816,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log("traffic probe: %d fused decode launches, then a %d-byte device copy" % (2 * P * len(groups), copy_bytes))
-        print(json.dumps({"fused_launches": 2 * P * len(groups), "copy_bytes": copy_bytes,
+        print(json.dumps({"fused_launches": 2 * P * len(groups), "copy_bytes": copy_bytes, "kernel": dispatch,
                           "source_digest": source_digest()}), flush=True)
         return
 
@@ -720,12 +966,10 @@ def main():
     torch.cuda.synchronize()
     gemm_dispatch = bl.last_dispatch()
     G = 20
-    # steady state: ~5 ms of the same GEMM untimed first (the first
-    # milliseconds of back-to-back GEMMs run a few percent slower), then 100
-    # timed launches
-    ms_gemm, _ = timed_graph(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, Np_, Y=Y_p) for _ in range(G)],
-                             reps=5, warm=5)
-    gemm_us = ms_gemm * 1e3 / G
+    # steady state: graphs of G back-to-back GEMMs replayed untimed for 20 ms
+    # (the first milliseconds of a sustained matrix-core load run slower while
+    # the clocks settle), then for >= 50 ms, each replay timed; the median
+    gemm_us = steady_us(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, Np_, Y=Y_p) for _ in range(G)], G)
     gemm_tops = 2.0 * Mp * Np_ * Kp / (gemm_us * 1e-6) / 1e12
     ms_qp, _ = timed_graph(torch, lambda: [bl.quant_act(Xp, Xq_p, xs_p, rs_p) for _ in range(G)], reps=2)
     quant_p_us = ms_qp * 1e3 / G
@@ -741,9 +985,8 @@ def main():
     torch.cuda.synchronize()
     gemm24_dispatch = bl.last_dispatch()
     prefill_rows = {"dense": acc_p.cpu().numpy()[rows], "2:4": acc_s.cpu().numpy()[rows]}
-    ms_g24, _ = timed_graph(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_s, ws_s, Np_, nm=(2, 4), Y=Y_s)
-                                            for _ in range(G)], reps=5, warm=5)
-    gemm24_us = ms_g24 * 1e3 / G
+    gemm24_us = steady_us(torch, lambda: [bl.forward(Xq_p, xs_p, rs_p, pk_s, ws_s, Np_, nm=(2, 4), Y=Y_s)
+                                          for _ in range(G)], G)
     # context: the vendor int8 GEMM (hipBLASLt through torch._int_mm) on the
     # same codes with the weights unpacked to one int8 per weight, K-major
     # (its faster layout here); int32 out, no dequant epilogue
@@ -762,10 +1005,10 @@ def main():
         torch.cuda.synchronize()
         if not torch.equal(C, acc_p):
             raise RuntimeError("library int8 GEMM result differs from the accumulators")
-        ms_lib, _ = timed_graph(torch, lambda: [torch._int_mm(Xq_p, Bm) for _ in range(G)], reps=5, warm=5)
+        lib_us = steady_us(torch, lambda: [torch._int_mm(Xq_p, Bm) for _ in range(G)], G)
         lib = {"op": "torch._int_mm (hipBLASLt), int8 x int8 -> int32, weights unpacked to int8, no epilogue",
-               "us": round(ms_lib * 1e3 / G, 2),
-               "TOPS": round(2.0 * Mp * Np_ * Kp / (ms_lib * 1e-3 / G) / 1e12, 1)}
+               "us": round(lib_us, 2),
+               "TOPS": round(2.0 * Mp * Np_ * Kp / (lib_us * 1e-6) / 1e12, 1)}
         del Bm, C
     except (RuntimeError, AttributeError) as e:
         lib = {"op": "torch._int_mm", "error": str(e)[:200]}
@@ -867,6 +1110,8 @@ def main():
                                  "single_forward": single},
         "gemm": {"workload": "prefill_2048: M=2048, K=2560, N=6912", "kernel": gemm_dispatch,
                  "avg_launch_us": round(gemm_us, 2), "TOPS": round(gemm_tops, 1),
+                 "timing": "graphs of 20 launches, replayed 20 ms untimed, then >= 50 ms with each replay timed; "
+                           "the median per launch (the same for 2:4 and the vendor GEMM)",
                  "roofline": {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": INT8_PEAK_TOPS,
                               "unit": "TOPS", "frac": round(gemm_tops / INT8_PEAK_TOPS, 4)},
                  "quant_act_us": round(quant_p_us, 2),

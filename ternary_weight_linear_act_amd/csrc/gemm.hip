@@ -914,7 +914,7 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
             Scratch dense_need;
             dense_need.query = true;
             const char *dn = "";
-            dispatch<Pattern::Dense>(Xq, xs, rs, nullptr, w_scale, M, N, K, Y, acc, dense_need, stream, &dn);
+            (void)dispatch<Pattern::Dense>(Xq, xs, rs, nullptr, w_scale, M, N, K, Y, acc, dense_need, stream, &dn);
             const bool go = scratch.take(rows_bytes + dense_need.need);
             if (!go && !scratch.query) return hipErrorOutOfMemory;
             Scratch dense_scratch;

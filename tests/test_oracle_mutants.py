@@ -53,11 +53,14 @@ MUTANTS = {
     "had_butterfly_sign": ("v[i] = a + c;\n                    v[i + h] = a - c;",
                            "v[i] = a - c;\n                    v[i + h] = a + c;"),
     "had_skip_first_stage": ("for (int64_t h = 1; h < B; h *= 2)", "for (int64_t h = 2; h < B; h *= 2)"),
-    "h4_const_8": ("float s = 7.0f / (g * pre);", "float s = 8.0f / (g * pre);"),
-    "h4_no_tiny_row_scaling": ("const float pre = (g < 0x1p-100f) ? 0x1p100f : 1.0f;", "const float pre = 1.0f;"),
+    # the H-BitLinear's block quantiser sits one level deeper than a4.8's
+    # 4-bit part, which has lines of the same text: anchor by indentation
+    "h4_const_8": ("\n            float s = 7.0f / (g * pre);", "\n            float s = 8.0f / (g * pre);"),
+    "h4_no_tiny_row_scaling": ("\n            const float pre = (g < 0x1p-100f) ? 0x1p100f : 1.0f;",
+                               "\n            const float pre = 1.0f;"),
     "h4_scale_unnormalised": ("x_scale[r] = (float)((double)g / 7.0 / sqrt((double)B));",
                               "x_scale[r] = (float)((double)g / 7.0);"),
-    "h4_trunc": ("float c = rintf((v[k] * pre) * s);", "float c = truncf((v[k] * pre) * s);"),
+    "h4_trunc": ("\n                float c = rintf((v[k] * pre) * s);", "\n                float c = truncf((v[k] * pre) * s);"),
     "a48_tie_to_higher_k": ("if (best < 0 || mag > best_mag) {\n                    best = k;",
                             "if (best < 0 || mag >= best_mag) {\n                    best = k;"),
     "a48_rank_signed": ("float mag = fabsf(x[k]);", "float mag = x[k];"),
