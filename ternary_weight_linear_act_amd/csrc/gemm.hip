@@ -133,10 +133,14 @@ __device__ __forceinline__ i32x4 unpack_word(uint32_t w)
 // beta * x_scale, to Y (and acc_out).  Full tiles (the common case) take a
 // branch-free path: one 64-bit row pointer per output row, the row sums and
 // scales of 4 consecutive rows read from LDS with one 16-byte load each, and
-// the column offsets folded into the store's immediate offset.
+// the column offsets folded into the store's immediate offset.  NT: the
+// full tiles' outputs go out as non-temporal stores -- where every tile of the
+// grid ends at once (one round of tiles over the compute units) their output
+// leaves in one burst at the end, and streaming stores drain it faster
+// (512 x 8960 x 1536: 17.2 -> 15.5 us; 1024 x 8192 x 2048: 23.5 -> 22.3 us).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-template <int TM, int TN, int FM, int FN>
+template <int TM, int TN, int FM, int FN, bool NT = false>
 __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], const int *s_rs, const float *s_sc,
                                            int wm, int wn, int h, int li, int64_t m0, int64_t n0, int64_t M,
                                            int64_t N, bool full, float *__restrict__ Y,
@@ -155,8 +159,11 @@ __device__ __forceinline__ void store_tile(const i32x16 (&acc)[FM][FN], const in
                 for (int r = 0; r < 4; ++r) {
                     float *yr = yb + (int64_t)(fm * 32 + 8 * g + r) * N;
 #pragma unroll
-                    for (int fn = 0; fn < FN; ++fn)
-                        yr[fn * 32] = (float)(acc[fm][fn][4 * g + r] - rs4[r]) * sc4[r];
+                    for (int fn = 0; fn < FN; ++fn) {
+                        const float y = (float)(acc[fm][fn][4 * g + r] - rs4[r]) * sc4[r];
+                        if constexpr (NT) __builtin_nontemporal_store(y, &yr[fn * 32]);
+                        else yr[fn * 32] = y;
+                    }
                 }
             }
         }
@@ -452,7 +459,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(
 // applies the dequant scale.  Used when there are too few output tiles to fill
 // the chip (few tokens).  The kernel boundary makes the partials visible: no
 // fence or counter is needed.
-template <int BM, int BN, int WM, int WN, int S, bool SPLIT, int OCC = 1>
+template <int BM, int BN, int WM, int WN, int S, bool SPLIT, int OCC = 1, bool NT = false>
 __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(
     const int8_t *__restrict__ Xq, const float *__restrict__ x_scale, const int32_t *__restrict__ x_rowsum,
     const uint8_t *__restrict__ packed, const float *__restrict__ w_scale, int64_t M, int64_t N,
@@ -657,8 +664,8 @@ __global__ __launch_bounds__(64 * WM * WN, OCC) void gemm_dma_kernel(
                 for (int v = 0; v < 16; ++v) mine[((fm * FN + fn) * 16 + v) * T + tid] = acc[fm][fn][v];
         return;
     }
-    store_tile<TM, TN, FM, FN>(acc, s_rs, s_sc, wm, wn, h, li, m0, n0, M, N,
-                               (m0 + BM <= M) && (n0 + BN <= N), Y, acc_out);
+    store_tile<TM, TN, FM, FN, NT>(acc, s_rs, s_sc, wm, wn, h, li, m0, n0, M, N,
+                                   (m0 + BM <= M) && (n0 + BN <= N), Y, acc_out);
 }
 
 // Epilogue of the split-K GEMM, one thread per output element (m, n): find
@@ -695,7 +702,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(
     if (acc_out) acc_out[idx] = av;
 }
 
-template <int BM, int BN, int WM, int WN, int S, bool SPLIT = false, int OCC = 1>
+template <int BM, int BN, int WM, int WN, int S, bool SPLIT = false, int OCC = 1, bool NT = false>
 hipError_t launch_dma(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
                       const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
                       hipStream_t stream, int32_t splits = 1, int32_t *ws = nullptr)
@@ -705,7 +712,7 @@ hipError_t launch_dma(const int8_t *Xq, const float *xs, const int32_t *rs, cons
     const int64_t per_xcd = (tiles + kXcds - 1) / kXcds;
     const int64_t grid = SPLIT ? per_xcd * kXcds * splits : xcd_grid(tiles_m, tiles_n);
     const size_t lds = (size_t)S * (BM * 64 + BN * 16) + 8 * BM;
-    auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SPLIT, OCC>;
+    auto kern = gemm_dma_kernel<BM, BN, WM, WN, S, SPLIT, OCC, NT>;
     if (lds > 64 * 1024) {
         const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
                                                  (int)lds);
@@ -864,13 +871,20 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
                 if (scratch.query) return hipSuccess;
                 return launch_dma<256, 256, 2, 4, 6>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
             }
+            // one round of tiles: streaming stores for the output (see store_tile)
             if (c12 <= c128) {
                 *name = "gemm_dense_dma_128x256_w8_s4";
                 if (scratch.query) return hipSuccess;
+                if (tiles(128, 256) <= kCus)
+                    return launch_dma<128, 256, 2, 4, 4, false, 1, true>(Xq, xs, rs, packed, w_scale, M, N, K, Y,
+                                                                         acc, stream);
                 return launch_dma<128, 256, 2, 4, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
             }
             *name = "gemm_dense_dma_128x128_w4_s4";
             if (scratch.query) return hipSuccess;
+            if (tiles(128, 128) <= kCus)
+                return launch_dma<128, 128, 2, 2, 4, false, 1, true>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc,
+                                                                     stream);
             return launch_dma<128, 128, 2, 2, 4>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, stream);
         }
         // narrow weight tiles: more workgroups from N, so fewer K splits (none
