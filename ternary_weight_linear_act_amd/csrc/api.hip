@@ -476,8 +476,10 @@ bitlinear_status bitlinear_forward_grouped(const int8_t *Xq, const float *x_scal
         e = bl::launch_decode_dot4(nullptr, Xq, x_scale, x_rowsum, M, K, p, args, nullptr,
                                    bl::ActTransform{nullptr, nullptr, 0.0f}, stream, &name, false);
     // 17-64 tokens in tiles of 16 while the tiles make at most 512 workgroups
-    // (the rule of the single forward)
-    else if (M <= 16 || (M <= bl::kSkinnyMaxM && rows16 * ((M + 15) / 16) <= 512))
+    // (the rule of the single forward), 1024 for two or more projections: one
+    // launch then replaces several (q, k, v of a 3B block at 64 tokens, 640
+    // workgroups: 12.8 us in three launches, one grouped launch less than half)
+    else if (M <= 16 || (M <= bl::kSkinnyMaxM && rows16 * ((M + 15) / 16) <= (nproj > 1 ? 1024 : 512)))
         e = bl::launch_skinny_forward(Xq, x_scale, x_rowsum, args, p, M, K, stream, &name, false);
     if (e == hipErrorNotSupported)
         return fail(BITLINEAR_EUNSUPPORTED, "grouped forward: no one-launch kernel for M = %lld, K = %lld and %lld "

@@ -75,6 +75,20 @@ def test_block_3b_gate_up_grouped(M):
     check(Ws, X, (0, 0), packs, xq, Ys, accs)
 
 
+@pytest.mark.parametrize("M,nm", [(40, (0, 0)), (64, (0, 0)), (64, (2, 4)), (64, (6, 8))])
+def test_block_3b_qkv_grouped_many_workgroups(M, nm):
+    # q, k, v of the 3B block past 16 tokens: 160 rows of 16 in 3 or 4 token
+    # tiles, 480 or 640 workgroups (a grouped call of several projections
+    # takes up to 1024)
+    d = workloads.draw("block_3b", projs=["q", "k", "v"], Ms=(64,))
+    Ws = [d.W["q"], d.W["k"], d.W["v"]]
+    X = d.X[("q", 64)][:M]
+    print("case grouped block_3b q+k+v M=%d nm=%s" % (M, nm), flush=True)
+    packs, xq, Ys, accs, name = run_grouped(Ws, X, nm)
+    assert name.startswith("skinny_mfma") and name.endswith("_grouped"), name
+    check(Ws, X, nm, packs, xq, Ys, accs)
+
+
 def test_grouped_unsupported_raises():
     import torch
 
@@ -82,6 +96,13 @@ def test_grouped_unsupported_raises():
     W, X = workloads.small_case(4500, 64, 11008, 2048)
     pk, ws = hip_pack(W, (0, 0))
     Xq, xs, rs = hip_quant(X)
+    # 2 x 688 rows of 16 in 4 token tiles: 5504 workgroups, past the limit
     with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
         bl.forward_grouped(Xq, xs, rs, [(pk, ws, 11008), (pk, ws, 11008)])
+    # one projection of 2048 rows: 512 workgroups at 64 tokens are allowed,
+    # 520 (2080 rows) are not for a single projection
+    W2, _ = workloads.small_case(4501, 1, 2080, 2048)
+    pk2, ws2 = hip_pack(W2, (0, 0))
+    with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
+        bl.forward_grouped(Xq, xs, rs, [(pk2, ws2, 2080)])
     torch.cuda.synchronize()
