@@ -451,12 +451,15 @@ def bench_configs(torch, bl, workloads, dev, log):
              "two_call_GB/s": round(abytes / (us * 1e-6) / 1e9, 1), "TOPS": round(ops / (us * 1e-6) / 1e12, 1)}
         if fused_groups and M <= 16:
             # one call per input group: the fused launch (quantisation and
-            # projections) for narrow groups and at up to 4 tokens; past 4
-            # tokens, groups of many weight rows (each fused workgroup would
-            # re-quantise the whole input) take quant_act, then the grouped
-            # forward (one launch for the group)
+            # projections) at up to 4 tokens, and past 4 tokens for groups of
+            # at most 2048 weight rows over K <= 4096; other groups (each fused
+            # workgroup would re-quantise the whole input, and deep K leaves
+            # the fused kernel few waves) take quant_act, then the grouped
+            # forward (one launch for the group).  3B block at 8 tokens: q k v
+            # fused 6.1 us against 5.5; o fused 5.3 against 5.5; down fused
+            # 10.1 against 9.2
             def narrow(g):
-                return M <= 4 or sum(shapes[n][0] for n in g) <= 4096
+                return M <= 4 or (sum(shapes[n][0] for n in g) <= 2048 and shapes[g[0]][1] <= 4096)
             Xq_g = {g: torch.empty((M, shapes[g[0]][1]), dtype=torch.int8, device=dev) for g in fused_groups}
             xs_g = {g: torch.empty(M, dtype=torch.float32, device=dev) for g in fused_groups}
             rs_g = {g: torch.empty(M, dtype=torch.int32, device=dev) for g in fused_groups}

@@ -45,6 +45,14 @@ hipError_t noalloc_scratch(hipStream_t stream, uint8_t **ptr);
 // Largest token count of the skinny MFMA forward (tiles of 16 tokens past 16).
 constexpr int64_t kSkinnyMaxM = 64;
 
+struct FusedProjArgs;                // skinny_impl.hpp
+
+// The skinny MFMA forward with the weights read straight into the MFMA
+// operand (dense weights at 5-64 tokens, the shapes where it measured faster
+// than the staged kernel); hipErrorNotSupported for every other shape.
+hipError_t launch_skinny_direct(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
+                                Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);
+
 // 2:4 weights at 1-16 tokens on the sparse MFMA (K % 128 == 0, K <= 16384;
 // hipErrorNotSupported otherwise).
 hipError_t launch_skinny_nm24_smfmac(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,

@@ -90,6 +90,9 @@ hipError_t launch_skinny_forward(const int8_t *Xq, const float *xs, const int32_
                                  Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query)
 {
     if (M < 1 || M > kSkinnyMaxM || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
+    // the weights straight into the MFMA operand where that measured faster
+    const hipError_t ed = launch_skinny_direct(Xq, xs, rs, args, p, M, K, stream, name, query);
+    if (ed != hipErrorNotSupported) return ed;
     int64_t blocks = 0;
     for (int i = 0; i < args.nproj; ++i) {
         args.block_start[i] = (int32_t)blocks;

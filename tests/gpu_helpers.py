@@ -93,3 +93,15 @@ def full_check(W, X, nm=(0, 0), rows=None, label=""):
         assert np.array_equal(acc_g, acc_o), "int32 accumulators differ in %d places" % int((acc_g != acc_o).sum())
         check_y(Y.cpu().numpy()[rows], Y_o, acc_o)
     return dict(packed=packed, ws=ws, Xq=Xq, xs=xs, rs=rs, Y=Y, acc=acc)
+
+
+def skinny_direct(M, K, rows, nproj=1, nm=(0, 0)):
+    """Dense weights at 5-64 tokens where the library reads the weights
+    straight into the MFMA operand (the shapes where that measured faster)."""
+    C = K // 64
+    if nm != (0, 0):
+        return False
+    wide = rows >= 8192
+    return ((5 <= M <= 8 and 8 <= C <= 32 and wide) or (9 <= M <= 16 and 8 <= C <= 32 and wide)
+            or (5 <= M <= 8 and 32 < C <= 40 and wide) or (5 <= M <= 8 and 128 < C <= 192)
+            or (17 <= M <= 64 and nproj >= 2 and 8 <= C <= 32))

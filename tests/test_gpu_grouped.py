@@ -6,7 +6,7 @@ import pytest
 
 from ternary_weight_linear_act_amd import workloads
 
-from gpu_helpers import check_y, cover_rows, hip_forward, hip_pack, hip_quant
+from gpu_helpers import check_y, cover_rows, hip_forward, hip_pack, hip_quant, skinny_direct
 
 pytestmark = pytest.mark.gpu
 
@@ -59,6 +59,8 @@ def test_grouped_shapes(M, nm, K, Ns):
     packs, xq, Ys, accs, name = run_grouped(Ws, X, nm)
     if M == 1:
         assert name.startswith("decode_dot4") and name.endswith("_p%d" % len(Ns)), name
+    elif skinny_direct(M, K, sum(Ns), len(Ns), nm):
+        assert name.startswith("skinny_direct_dense_") and name.endswith("_grouped"), name
     else:
         assert name.startswith("skinny_mfma") and name.endswith("_grouped"), name
     check(Ws, X, nm, packs, xq, Ys, accs)
@@ -85,7 +87,8 @@ def test_block_3b_qkv_grouped_many_workgroups(M, nm):
     X = d.X[("q", 64)][:M]
     print("case grouped block_3b q+k+v M=%d nm=%s" % (M, nm), flush=True)
     packs, xq, Ys, accs, name = run_grouped(Ws, X, nm)
-    assert name.startswith("skinny_mfma") and name.endswith("_grouped"), name
+    family = "skinny_direct_dense_" if nm == (0, 0) else "skinny_mfma"
+    assert name.startswith(family) and name.endswith("_grouped"), name
     check(Ws, X, nm, packs, xq, Ys, accs)
 
 

@@ -10,7 +10,7 @@ import pytest
 
 from ternary_weight_linear_act_amd import workloads
 
-from gpu_helpers import cover_rows, full_check, hip_forward, hip_pack, hip_quant, to_dev
+from gpu_helpers import cover_rows, full_check, hip_forward, hip_pack, hip_quant, skinny_direct, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -288,6 +288,8 @@ def test_skinny_deep_k(M, mt, K, nm):
     name = bl.last_dispatch()
     if nm == (2, 4) and nm24_smfmac_skinny(M, K):
         assert name == "skinny_smfmac_nm24", name
+    elif skinny_direct(M, K, 300, 1, nm):
+        assert name.startswith("skinny_direct_dense_") and "_mt%d_" % mt in name, name
     else:
         assert name.startswith("skinny_mfma_") and name.endswith("_mt%d" % mt), name
 
