@@ -893,17 +893,17 @@ hipError_t dispatch(const int8_t *Xq, const float *xs, const int32_t *rs, const 
         // 8.2 us; at 20-32 tokens, 1536 -> 8960 11.3 -> 7.6 us and 2048 ->
         // 11008 12.9 -> 8.2 us.  Deep K takes 64-wide tiles (11008 -> 2048 at
         // 64 tokens: 12.9 -> 12.5 us, where 32-wide ones take 14.4).
+        // Narrow tiles take 32 tokens also at 33-64 tokens: twice the
+        // workgroups of one-wave tiles, for a latency-bound chain of K slices
+        // (64 x 11008 x 2048: 10.1 -> 8.5 us against 64 x 32 tiles; 48 x 8960
+        // x 1536: 9.9 -> 7.5 us).
         const bool narrow = K <= 4096 || N >= 32 * kCus;
-        if (M <= 32) {
-            if (narrow)
-                return launch_few_tokens<32, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
-                                                       "gemm_dense_splitk_32x32", "gemm_dense_dma_32x32");
+        if (narrow)
+            return launch_few_tokens<32, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
+                                                   "gemm_dense_splitk_32x32", "gemm_dense_dma_32x32");
+        if (M <= 32)
             return launch_few_tokens<32, 64, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
                                                    "gemm_dense_splitk_32x64", "gemm_dense_dma_32x64");
-        }
-        if (narrow)
-            return launch_few_tokens<64, 32, 1, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
-                                                   "gemm_dense_splitk_64x32", "gemm_dense_dma_64x32");
         return launch_few_tokens<64, 64, 2, 1>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, scratch, stream, name,
                                                "gemm_dense_splitk_64x64", "gemm_dense_dma_64x64");
     } else {
