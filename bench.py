@@ -52,19 +52,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-# The files the fused one-token decode kernel is built from (and its build
-# flags): the committed kernel trace and HBM traffic describe that kernel only
+# The files the fused one-token decode kernel is built from, and the compiler
+# flags: the committed kernel trace and HBM traffic describe that kernel only
 # while these are unchanged.
 DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode_dot4.hip", "decode_dot4_impl.hpp", "fused_impl.hpp",
                                                   "skinny_impl.hpp", "common.hpp")] + [
-    os.path.join(ROOT, "include", "bitlinear.h"), os.path.join(ROOT, "ternary_weight_linear_act_amd", "build.py")]
+    os.path.join(ROOT, "include", "bitlinear.h")]
 
 
 def source_digest() -> str:
+    from ternary_weight_linear_act_amd import build
     h = hashlib.sha256()
     for path in DECODE_SOURCES:
         with open(path, "rb") as fh:
             h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+    # the flags without the include path (the checkout's location differs
+    # between machines)
+    h.update(" ".join(f for f in build.CFLAGS if not os.path.isabs(f)).encode())
     return h.hexdigest()[:16]
 
 
