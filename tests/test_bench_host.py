@@ -1,0 +1,150 @@
+"""Host-side parts of bench.py (no GPU): the refusal of more than one GPU,
+the profile summaries written from rocprofv3's CSV output (kernel trace,
+FETCH_SIZE / WRITE_SIZE counters, kernel statistics), the parsing of the
+decode kernel's dispatch names and demangled symbols, and the digest that
+ties a committed profile to the kernel's sources."""
+import csv
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+GATE = "void bl::dot4::decode_dot4_kernel<(bl::Pattern)0, 8, 5, true, 8, 0>(float const*, signed char const*, " \
+       "float const*, int const*, long, bl::FusedProjArgs, float*, bl::ActTransform)"
+DOWN = "void bl::dot4::decode_dot4_kernel<(bl::Pattern)0, 16, 7, true, 4, 0>(float const*, signed char const*, " \
+       "float const*, int const*, long, bl::FusedProjArgs, float*, bl::ActTransform)"
+PROBE_KERNEL = "gate+up: fused_decode_dot4_dense_lpr8_u5_p2_w8, down: fused_decode_dot4_dense_lpr16_u7_p1"
+
+
+def write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f, quoting=csv.QUOTE_NONNUMERIC)
+        w.writerow(header)
+        for r in rows:
+            w.writerow(r)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_dispatch_names_and_symbols(bench):
+    assert bench._dot4_args("fused_decode_dot4_dense_lpr8_u5_p2_w8") == ("dense", 8, 5, True, 8, 0)
+    assert bench._dot4_args("fused_decode_dot4_dense_lpr16_u7_p1") == ("dense", 16, 7, True, 4, 0)
+    assert bench._dot4_args("decode_dot4_nm68_lpr32_u4_p1") == ("nm68", 32, 4, False, 4, 0)
+    assert bench._dot4_args("fused_decode_dot4_dense_lpr8_u5_p2_gate_norm") == ("dense", 8, 5, True, 4, 3)
+    assert bench._dot4_args(GATE) == ("dense", 8, 5, True, 8, 0)
+    assert bench._dot4_args("void bl::dot4::decode_dot4_kernel<bl::Pattern::NM24, 16, 7, true, 4, 2>(x)") == \
+        ("nm24", 16, 7, True, 4, 2)
+    assert bench._dot4_args("bl::(anonymous namespace)::gemm_dma_kernel<256, 256, 2, 4, 6, false, 1>(int)") is None
+    assert bench._symbol(GATE) == "void bl::dot4::decode_dot4_kernel<(bl::Pattern)0, 8, 5, true, 8, 0>"
+    assert bench._symbol("bl::(anonymous namespace)::beta_kernel(double const*, long)") == \
+        "bl::(anonymous namespace)::beta_kernel"
+    assert bench._symbol("__amd_rocclr_copyBuffer") == "__amd_rocclr_copyBuffer"
+
+
+def test_digest_ignores_the_checkout_location(bench, monkeypatch):
+    from ternary_weight_linear_act_amd import build
+    d1 = bench.source_digest()
+    flags = [f if not os.path.isabs(f) else "/elsewhere/include" for f in build.CFLAGS]
+    monkeypatch.setattr(build, "CFLAGS", flags)
+    assert bench.source_digest() == d1
+    monkeypatch.setattr(build, "CFLAGS", flags + ["-O0"])
+    assert bench.source_digest() != d1
+
+
+def test_trace_summary(bench, tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRACE_FILE", str(tmp_path / "trace.json"))
+    tdir = tmp_path / "trace"
+    hdr = ["Kind", "Agent_Id", "Queue_Id", "Stream_Id", "Thread_Id", "Dispatch_Id", "Kernel_Id", "Kernel_Name",
+           "Correlation_Id", "Start_Timestamp", "End_Timestamp"]
+    rows = []
+    t = 1000
+    for i in range(10):
+        rows.append(["KERNEL_DISPATCH", "Agent 1", 1, 0, 1, 2 * i, 1, GATE, 2 * i, t, t + 4000 + 100 * i])
+        t += 10000
+        rows.append(["KERNEL_DISPATCH", "Agent 1", 1, 0, 1, 2 * i + 1, 2, DOWN, 2 * i + 1, t, t + 3000])
+        t += 10000
+    rows.append(["KERNEL_DISPATCH", "Agent 1", 1, 0, 1, 99, 3, "__amd_rocclr_copyBuffer", 99, t, t + 500])
+    write_csv(str(tdir / "trace_kernel_trace.csv"), hdr, rows)
+    write_csv(str(tdir / "trace_kernel_stats.csv"),
+              ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+              [[GATE, 10, 44500, 4450.0, 50.0, 4000, 4900, 1.0], [DOWN, 10, 30000, 3000.0, 40.0, 3000, 3000, 0.0]])
+    probe = tmp_path / "probe.out"
+    probe.write_text("noise\n" + json.dumps({"trace_probe": True, "replays": 20, "steps_per_replay": 162,
+                                             "us_per_step_events": 9.0, "kernel": PROBE_KERNEL,
+                                             "source_digest": "abc"}) + "\n")
+    bench.trace_summary(str(tdir), str(probe))
+    out = json.load(open(tmp_path / "trace.json"))
+    k = out["kernels"]
+    assert out["source_digest"] == "abc"
+    assert k["fused_decode_dot4_dense_lpr8_u5_p2_w8"]["dispatches"] == 10
+    assert k["fused_decode_dot4_dense_lpr8_u5_p2_w8"]["avg_us"] == pytest.approx(4.45)
+    assert k["fused_decode_dot4_dense_lpr8_u5_p2_w8"]["stats_avg_us"] == pytest.approx(4.45)
+    assert k["fused_decode_dot4_dense_lpr16_u7_p1"]["avg_us"] == pytest.approx(3.0)
+    assert k["fused_decode_dot4_dense_lpr16_u7_p1"]["group"] == "down"
+    md = open(tmp_path / "trace.md").read()
+    assert "--trace-summary" in md and "rocprofv3 --kernel-trace --stats" in md
+
+
+def test_traffic_summary(bench, tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "traffic.json"))
+    hdr = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+           "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+           "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    copy_bytes = 1 << 28
+
+    def rows(counter, gate_kib, down_kib, copy_kib):
+        out = []
+        for i, (name, v) in enumerate([(GATE, gate_kib), (DOWN, down_kib)] * 3 +
+                                      [("__amd_rocclr_copyBuffer", 100.0), ("__amd_rocclr_copyBuffer", copy_kib)]):
+            out.append([i, i, "Agent 1", 1, 1, 1, 64, 1, name, 256, 0, 0, 8, 0, 16, counter, v, 0, 1])
+        return out
+    # FETCH_SIZE reads half the bytes (scale 2), WRITE_SIZE reads them exactly
+    write_csv(str(tmp_path / "f" / "p_counter_collection.csv"), hdr,
+              rows("FETCH_SIZE", 8800.0, 4400.0, copy_bytes / 1024 / 2))
+    write_csv(str(tmp_path / "w" / "p_counter_collection.csv"), hdr,
+              rows("WRITE_SIZE", 54.0, 10.0, copy_bytes / 1024))
+    probe = tmp_path / "probe.out"
+    probe.write_text(json.dumps({"fused_launches": 6, "copy_bytes": copy_bytes, "kernel": PROBE_KERNEL,
+                                 "source_digest": "abc"}) + "\n")
+    bench.traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(probe))
+    out = json.load(open(tmp_path / "traffic.json"))
+    assert out["fetch_scale"] == pytest.approx(2.0) and out["write_scale"] == pytest.approx(1.0)
+    g = out["per_kernel"]["fused_decode_dot4_dense_lpr8_u5_p2_w8"]
+    d = out["per_kernel"]["fused_decode_dot4_dense_lpr16_u7_p1"]
+    assert g["dispatches"] == 3
+    assert g["fetch_bytes"] == 8800 * 1024 * 2 and g["write_bytes"] == 54 * 1024
+    assert d["hbm_bytes"] == 4400 * 1024 * 2 + 10 * 1024
+    assert out["hbm_bytes_per_launch"] == round((g["hbm_bytes"] + d["hbm_bytes"]) / 2)
+
+
+def test_stats_summary(bench, tmp_path):
+    write_csv(str(tmp_path / "t" / "b_kernel_stats.csv"),
+              ["Name", "Calls", "TotalDurationNs", "AverageNs", "Percentage", "MinNs", "MaxNs", "StdDev"],
+              [[GATE, 10, 44500, 4450.0, 50.0, 4000, 4900, 1.0],
+               ["bl::(anonymous namespace)::gemm_dma_kernel<256, 256, 2, 4, 6, false, 1>(signed char const*)",
+                5, 200000, 40000.0, 40.0, 39000, 41000, 1.0],
+               ["at::native::vectorized_elementwise_kernel<4>(int)", 3, 10, 3.0, 0.1, 3, 3, 0.0]])
+    out = tmp_path / "s.md"
+    bench.stats_summary(str(tmp_path / "t"), str(out), "title", "cmd")
+    md = out.read_text()
+    assert "| `bl::(anonymous namespace)::gemm_dma_kernel<256, 256, 2, 4, 6, false, 1>` | 5 | 40.000 |" in md
+    assert "vectorized_elementwise" not in md
