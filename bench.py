@@ -17,6 +17,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [
        python bench.py --trace-summary TRACE_DIR PROBE_OUT
        python bench.py --traffic-summary FETCH_DIR WRITE_DIR PROBE_OUT
        python bench.py --stats-summary TRACE_DIR OUT_MD TITLE COMMAND
+       python bench.py --gemm-counters-summary PMC_DIR PROBE_OUT OUT_MD COMMAND
 Prints one JSON line on stdout; a readable summary goes to stderr.
 """
 from __future__ import annotations
@@ -184,6 +185,55 @@ def trace_summary(trace_dir, probe_out):
     with open(TRACE_FILE[:-5] + ".md", "w") as f:
         f.write("\n".join(md) + "\n")
     print(json.dumps(out))
+
+
+def gemm_counters_summary(pmc_dir, probe_out, out_md, command):
+    """A Markdown summary of the SQ / GRBM counters of `bench.py --gemm-probe`
+    under `rocprofv3 --pmc` (CSV under pmc_dir; the probe's JSON line in
+    probe_out), with the derived MFMA busy fraction and clock."""
+    import numpy as np
+    probe = _probe_json(probe_out)
+    M, N, K = probe["M"], probe["N"], probe["K"]
+    vals, durs = {}, {}
+    for r in _csv_rows(pmc_dir, "counter_collection.csv"):
+        name = _kernel_name(r)
+        if "gemm_dma_kernel<256, 256" not in name:
+            continue
+        vals.setdefault(r["Counter_Name"], {})[r["Dispatch_Id"]] = float(r["Counter_Value"])
+        durs[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+    if not vals:
+        raise SystemExit("no counted dispatch of the prefill GEMM")
+    avg = {c: float(np.mean(list(v.values()))) for c, v in vals.items()}
+    dur = float(np.mean(list(durs.values())))
+    mfmas = M * N * K / 32 ** 3
+    md = ["# SQ counters: prefill GEMM, %d x %d -> %d, dense (`%s`)" % (M, K, N, probe["kernel"]), "",
+          "Command (run from /tmp with TMPDIR=/tmp, repository at $R), then the summary:", "",
+          "    " + command,
+          "    python3 $R/bench.py --gemm-counters-summary %s %s %s '%s'" % (pmc_dir, probe_out, out_md, command), "",
+          "Average over the %d dispatches (durations under counter collection):" % len(durs), "",
+          "| counter | value |", "|---|---:|"]
+    md += ["| %s | %.4g |" % (c, v) for c, v in sorted(avg.items())] + ["| dur_us | %.2f |" % dur, "", "Derived:", ""]
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+        md.append("- MFMAs: %d·%d·%d / 32³ = %d `v_mfma_i32_32x32x32_i8`; SQ_VALU_MFMA_BUSY_CYCLES / MFMAs = %.2f "
+                  "busy cycles per MFMA." % (M, N, K, mfmas, avg["SQ_VALU_MFMA_BUSY_CYCLES"] / mfmas))
+    if "GRBM_GUI_ACTIVE" in avg:
+        clk = avg["GRBM_GUI_ACTIVE"] / 8 / (dur * 1e-6) / 1e9
+        md.append("- GPU clock during the kernel: GRBM_GUI_ACTIVE / 8 XCDs / duration = %.2f GHz (taking the counter "
+                  "as the sum of one count per XCD)." % clk)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg:
+            busy = avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * avg["GRBM_GUI_ACTIVE"] / 8)
+            tiles = ((M + 255) // 256) * ((N + 255) // 256)
+            md.append("- MFMA pipes busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8) = %.1f%% of all "
+                      "SIMDs; the %d tiles of 256 x 256 occupy %d of the 256 CUs, so %.1f%% of the busy ones."
+                      % (100 * busy, tiles, min(tiles, 256), 100 * busy * 256 / min(tiles, 256)))
+    if "SQ_WAIT_ANY" in avg and "SQ_WAVE_CYCLES" in avg:
+        md.append("- SQ_WAIT_ANY / SQ_WAVE_CYCLES = %.1f%% of wave time waiting on dependencies."
+                  % (100 * avg["SQ_WAIT_ANY"] / avg["SQ_WAVE_CYCLES"]))
+    if "SQ_LDS_BANK_CONFLICT" in avg and "SQ_INSTS_LDS" in avg:
+        md.append("- LDS bank conflicts: SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS = %.2f cycles per LDS instruction."
+                  % (avg["SQ_LDS_BANK_CONFLICT"] / avg["SQ_INSTS_LDS"]))
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
 
 
 def stats_summary(trace_dir, out_md, title, command):
@@ -728,7 +778,13 @@ def main():
     ap.add_argument("--stats-summary", nargs=4, metavar=("TRACE_DIR", "OUT_MD", "TITLE", "COMMAND"),
                     help="write a Markdown table of rocprofv3's kernel statistics (CSV) under TRACE_DIR, then exit "
                          "(no GPU)")
+    ap.add_argument("--gemm-counters-summary", nargs=4, metavar=("PMC_DIR", "PROBE_OUT", "OUT_MD", "COMMAND"),
+                    help="write a Markdown summary of rocprofv3's counters (CSV) of a --gemm-probe run, then exit "
+                         "(no GPU)")
     args = ap.parse_args()
+    if args.gemm_counters_summary:
+        gemm_counters_summary(*args.gemm_counters_summary)
+        return
     if args.stats_summary:
         stats_summary(*args.stats_summary)
         return
@@ -764,7 +820,8 @@ def main():
             bl.forward(Xq_p, xs_p, rs_p, pk_p, ws_p, 6912, Y=Y_p)
         torch.cuda.synchronize()
         log("gemm probe: 5 launches of %s" % bl.last_dispatch())
-        print(json.dumps({"gemm_launches": 5, "kernel": bl.last_dispatch(), "source_digest": source_digest()}),
+        print(json.dumps({"gemm_launches": 5, "kernel": bl.last_dispatch(), "M": 2048, "N": 6912, "K": 2560,
+                          "source_digest": source_digest()}),
               flush=True)
         return
 

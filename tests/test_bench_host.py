@@ -148,3 +148,31 @@ def test_stats_summary(bench, tmp_path):
     md = out.read_text()
     assert "| `bl::(anonymous namespace)::gemm_dma_kernel<256, 256, 2, 4, 6, false, 1>` | 5 | 40.000 |" in md
     assert "vectorized_elementwise" not in md
+
+
+def test_gemm_counters_summary(bench, tmp_path):
+    hdr = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+           "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+           "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    gemm = "void bl::(anonymous namespace)::gemm_dma_kernel<256, 256, 2, 4, 6, false, 1, false>(signed char const*)"
+    M, N, K = 2048, 6912, 2560
+    mfmas = M * N * K // 32 ** 3
+    rows = []
+    for d in range(2):
+        for c, v in [("SQ_VALU_MFMA_BUSY_CYCLES", 32.0 * mfmas), ("GRBM_GUI_ACTIVE", 8 * 2.5e3 * 40),
+                     ("SQ_WAIT_ANY", 10.0), ("SQ_WAVE_CYCLES", 40.0), ("SQ_LDS_BANK_CONFLICT", 1.0),
+                     ("SQ_INSTS_LDS", 4.0)]:
+            rows.append([d, d, "Agent 1", 1, 1, 1, 64, 1, gemm, 512, 0, 0, 8, 0, 16, c, v, 0, 40000])
+    rows.append([9, 9, "Agent 1", 1, 1, 1, 64, 1, "bl::beta_kernel(double const*)", 64, 0, 0, 8, 0, 16,
+                 "SQ_WAVES", 1.0, 0, 5])
+    write_csv(str(tmp_path / "p" / "p1_counter_collection.csv"), hdr, rows)
+    probe = tmp_path / "probe.out"
+    probe.write_text(json.dumps({"gemm_launches": 2, "kernel": "gemm_dense_dma_256x256_w8_s6", "M": M, "N": N,
+                                 "K": K}) + "\n")
+    out = tmp_path / "c.md"
+    bench.gemm_counters_summary(str(tmp_path / "p"), str(probe), str(out), "cmd")
+    md = out.read_text()
+    assert "32.00 busy cycles per MFMA" in md
+    assert "= 2.50 GHz" in md                       # 8 XCDs x 2.5e3 counts per us over 40 us
+    assert "25.0% of wave time" in md and "0.25 cycles per LDS instruction" in md
+    assert "| dur_us | 40.00 |" in md and "SQ_WAVES" not in md
