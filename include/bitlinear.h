@@ -254,9 +254,10 @@ bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, b
  * `projs`: host array of nproj entries (packed, w_scale, N, Y, acc as in
  * bitlinear_proj).  Supported: 1 <= nproj <= 8 and M <= 16, or
  * 17 <= M <= 64 while the 16-token tiles times the 16-row weight blocks of
- * all projections make at most 512 workgroups, and K within the kernels'
- * range; anything else returns BITLINEAR_EUNSUPPORTED and launches nothing
- * (call bitlinear_forward per projection then).  Needs no workspace. */
+ * all projections make at most 1024 workgroups (512 for one projection), and
+ * K within the kernels' range; anything else returns BITLINEAR_EUNSUPPORTED
+ * and launches nothing (call bitlinear_forward per projection then).  Needs
+ * no workspace. */
 bitlinear_status bitlinear_forward_grouped(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
                                            int64_t M, int64_t K, bitlinear_nm nm, const bitlinear_proj *projs,
                                            int32_t nproj, hipStream_t stream);
