@@ -61,12 +61,21 @@ DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode_dot4.hip", "decode_dot
     os.path.join(ROOT, "include", "bitlinear.h")]
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without its comments and with whitespace runs collapsed:
+    an edit of a comment leaves the digest (and the kernel) unchanged."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest() -> str:
     from ternary_weight_linear_act_amd import build
     h = hashlib.sha256()
     for path in DECODE_SOURCES:
-        with open(path, "rb") as fh:
-            h.update(os.path.basename(path).encode() + b"\0" + fh.read())
+        with open(path, encoding="utf-8") as fh:
+            h.update(os.path.basename(path).encode() + b"\0" + _code_only(fh.read()).encode())
     # the flags without the include path (the checkout's location differs
     # between machines)
     h.update(" ".join(f for f in build.CFLAGS if not os.path.isabs(f)).encode())

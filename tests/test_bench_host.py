@@ -176,3 +176,10 @@ def test_gemm_counters_summary(bench, tmp_path):
     assert "= 2.50 GHz" in md                       # 8 XCDs x 2.5e3 counts per us over 40 us
     assert "25.0% of wave time" in md and "0.25 cycles per LDS instruction" in md
     assert "| dur_us | 40.00 |" in md and "SQ_WAVES" not in md
+
+
+def test_digest_ignores_comments(bench):
+    a = "int f(int x) { // add one\n  return x + 1; /* done */ }\n"
+    b = "int f(int x) {\n    return x + 1;\n}\n"
+    c = "int f(int x) { return x + 2; }"
+    assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
