@@ -8,7 +8,8 @@ eager call on the new inputs, so the graph reads its buffers each time rather
 than holding values from capture.  Covered: quant_act + forward (dense, 2:4,
 6:8; one token, the few-token split-K kernel, the prefill tiles, the sparse
 MFMA GEMM), the fused one-token launch with and without a row transform, the
-fused 2-4-token launch, quant_act_ex and the H-BitLinear quantiser.  And, in a
+fused 2-4-token launch, quant_act + the grouped forward (both skinny
+kernels), quant_act_ex and the H-BitLinear quantiser.  And, in a
 fresh process, forward calls captured before any eager call: the same kernels
 and the same bits as the eager calls afterwards."""
 import numpy as np
@@ -114,6 +115,33 @@ def test_graph_fused(M, tr):
 
     X2 = workloads.activations(rng, M, K, 0.001)
     check_replays(body, Ys + accs + [xs], lambda: Xd.copy_(to_dev(X2)))
+
+
+@pytest.mark.parametrize("M,Ns,K", [(8, (11008, 11008), 2048), (64, (2048, 256, 256), 2048), (16, (300, 17), 512)])
+def test_graph_grouped(M, Ns, K):
+    # quant_act + the grouped forward (one launch per input group), as the
+    # bench runs the 3B block past 4 tokens: the direct-load kernel at 8 and
+    # 64 tokens, the staged one at 16
+    import torch
+
+    import ternary_weight_linear_act_amd as bl
+    rng = np.random.default_rng(2250 + M)
+    Ws = [workloads.normal_f32(rng, (N, K), workloads.WEIGHT_SIGMA) for N in Ns]
+    print("case graph grouped M=%d Ns=%s K=%d" % (M, Ns, K), flush=True)
+    packs = [hip_pack(W, (0, 0)) for W in Ws]
+    Xd = to_dev(workloads.activations(rng, M, K, 0.001))
+    Xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    xs = torch.empty(M, dtype=torch.float32, device="cuda")
+    rs = torch.empty(M, dtype=torch.int32, device="cuda")
+    Ys = [torch.empty((M, N), dtype=torch.float32, device="cuda") for N in Ns]
+    accs = [torch.empty((M, N), dtype=torch.int32, device="cuda") for N in Ns]
+
+    def body():
+        bl.quant_act(Xd, Xq, xs, rs)
+        bl.forward_grouped(Xq, xs, rs, [(pk, ws, N) for (pk, ws), N in zip(packs, Ns)], Ys=Ys, accs=accs)
+
+    X2 = workloads.activations(rng, M, K, 0.001)
+    check_replays(body, Ys + accs + [Xq, xs, rs], lambda: Xd.copy_(to_dev(X2)))
 
 
 @pytest.mark.parametrize("kind", ["quant_act_ex", "quant_act_h4"])
