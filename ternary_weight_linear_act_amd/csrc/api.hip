@@ -481,6 +481,9 @@ bitlinear_status bitlinear_forward_grouped(const int8_t *Xq, const float *x_scal
     // workgroups: 12.8 us in three launches, one grouped launch less than half)
     else if (M <= 16 || (M <= bl::kSkinnyMaxM && rows16 * ((M + 15) / 16) <= (nproj > 1 ? 1024 : 512)))
         e = bl::launch_skinny_forward(Xq, x_scale, x_rowsum, args, p, M, K, stream, &name, false);
+    // past that, several wide projections in one launch of the few-token GEMM
+    if (e == hipErrorNotSupported && M > 16)
+        e = bl::launch_gemm_grouped(Xq, x_scale, x_rowsum, args, p, M, K, stream, &name, false);
     if (e == hipErrorNotSupported)
         return fail(BITLINEAR_EUNSUPPORTED, "grouped forward: no one-launch kernel for M = %lld, K = %lld and %lld "
                     "rows of 16 (call bitlinear_forward per projection)", (long long)M, (long long)K,

@@ -53,6 +53,12 @@ struct FusedProjArgs;                // skinny_impl.hpp
 hipError_t launch_skinny_direct(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
                                 Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);
 
+// Several dense projections at 17-64 tokens in one launch of the few-token
+// GEMM's 32 x 32 tiles (where each alone would take them unsplit);
+// hipErrorNotSupported for every other shape.
+hipError_t launch_gemm_grouped(const int8_t *Xq, const float *xs, const int32_t *rs, FusedProjArgs args, Pattern p,
+                               int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);
+
 // 2:4 weights at 1-16 tokens on the sparse MFMA (K % 128 == 0, K <= 16384;
 // hipErrorNotSupported otherwise).
 hipError_t launch_skinny_nm24_smfmac(const int8_t *Xq, const float *xs, const uint8_t *packed, const float *w_scale,

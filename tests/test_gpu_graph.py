@@ -117,11 +117,12 @@ def test_graph_fused(M, tr):
     check_replays(body, Ys + accs + [xs], lambda: Xd.copy_(to_dev(X2)))
 
 
-@pytest.mark.parametrize("M,Ns,K", [(8, (11008, 11008), 2048), (64, (2048, 256, 256), 2048), (16, (300, 17), 512)])
+@pytest.mark.parametrize("M,Ns,K", [(8, (11008, 11008), 2048), (64, (2048, 256, 256), 2048), (16, (300, 17), 512),
+                                    (64, (11008, 11008), 2048)])
 def test_graph_grouped(M, Ns, K):
     # quant_act + the grouped forward (one launch per input group), as the
     # bench runs the 3B block past 4 tokens: the direct-load kernel at 8 and
-    # 64 tokens, the staged one at 16
+    # 64 tokens, the staged one at 16, the few-token GEMM for gate + up at 64
     import torch
 
     import ternary_weight_linear_act_amd as bl

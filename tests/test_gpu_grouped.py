@@ -99,13 +99,46 @@ def test_grouped_unsupported_raises():
     W, X = workloads.small_case(4500, 64, 11008, 2048)
     pk, ws = hip_pack(W, (0, 0))
     Xq, xs, rs = hip_quant(X)
-    # 2 x 688 rows of 16 in 4 token tiles: 5504 workgroups, past the limit
-    with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
-        bl.forward_grouped(Xq, xs, rs, [(pk, ws, 11008), (pk, ws, 11008)])
     # one projection of 2048 rows: 512 workgroups at 64 tokens are allowed,
-    # 520 (2080 rows) are not for a single projection
+    # 520 (2080 rows) are not for a single projection (and the grouped GEMM
+    # takes two or more)
     W2, _ = workloads.small_case(4501, 1, 2080, 2048)
     pk2, ws2 = hip_pack(W2, (0, 0))
     with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
         bl.forward_grouped(Xq, xs, rs, [(pk2, ws2, 2080)])
+    # a wide projection beside one of too few GEMM tiles (2080 rows: 130 of
+    # 32 x 32 at 64 tokens, below one per compute unit)
+    with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
+        bl.forward_grouped(Xq, xs, rs, [(pk, ws, 11008), (pk2, ws2, 2080)])
+    # deep K over few rows: neither the skinny tiles (LDS) nor the grouped GEMM
+    W3, X3 = workloads.small_case(4502, 64, 2048, 11008)
+    pk3, ws3 = hip_pack(W3, (0, 0))
+    Xq3, xs3, rs3 = hip_quant(X3)
+    with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
+        bl.forward_grouped(Xq3, xs3, rs3, [(pk3, ws3, 2048), (pk3, ws3, 2048)])
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("M,K,Ns", [(64, 2048, (11008, 11008)), (17, 1024, (8192, 8300)), (33, 512, (8200, 12000, 8192)),
+                                    (48, 4096, (8200, 8200)), (64, 6144, (8192, 8200))])
+def test_grouped_gemm(M, K, Ns):
+    # past the skinny kernel's workgroup limit: one launch of the few-token
+    # GEMM's 32 x 32 tiles for all projections (ragged weight rows, a ragged
+    # last token tile)
+    seed = 4600 + M + K + sum(Ns)
+    Ws = [workloads.small_case(seed + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+    _, X = workloads.small_case(seed + 77, M, 8, K, outlier_frac=0.01)
+    print("case grouped GEMM M=%d K=%d Ns=%s" % (M, K, Ns), flush=True)
+    packs, xq, Ys, accs, name = run_grouped(Ws, X, (0, 0))
+    assert name == "gemm_dense_dma_32x32_grouped", name
+    check(Ws, X, (0, 0), packs, xq, Ys, accs)
+
+
+def test_block_3b_gate_up_grouped_gemm_full_size():
+    d = workloads.draw("block_3b", projs=["gate", "up"], Ms=(64,))
+    Ws = [d.W["gate"], d.W["up"]]
+    X = d.X[("gate", 64)]
+    print("case grouped GEMM block_3b gate+up M=64", flush=True)
+    packs, xq, Ys, accs, name = run_grouped(Ws, X, (0, 0))
+    assert name == "gemm_dense_dma_32x32_grouped", name
+    check(Ws, X, (0, 0), packs, xq, Ys, accs)

@@ -4,7 +4,8 @@ measured faster than the staged kernel): every rule of its dispatch at its
 edges, with ragged weight rows (a partial last column block), against the
 CPU oracle (acc bit-exact, Y within 1e-5) and bit-identical to the forward
 of each projection alone.  Next to each rule, a shape just outside it takes
-the staged kernel."""
+the staged kernel.  Grouped calls past the skinny tiles' workgroup limit take
+the few-token GEMM's grouped launch where its rule holds."""
 import numpy as np
 import pytest
 
@@ -67,15 +68,20 @@ def test_direct_grouped(M, K, Ns):
     packs = [hip_pack(W, (0, 0)) for W in Ws]
     Xq, xs, rs = hip_quant(X)
     projs = [(pk, ws, W.shape[0]) for (pk, ws), W in zip(packs, Ws)]
-    if M > 16 and sum(-(-N // 16) for N in Ns) * -(-M // 16) > 1024:
-        # past 16 tokens a grouped call takes at most 1024 workgroups
+    past_skinny = M > 16 and sum(-(-N // 16) for N in Ns) * -(-M // 16) > 1024
+    gemm = M > 16 and len(Ns) > 1 and all((K <= 4096 or N >= 8192) and -(-M // 32) * -(-N // 32) >= 256 for N in Ns)
+    if past_skinny and not gemm:
+        # past 16 tokens the skinny tiles take at most 1024 workgroups, and
+        # the grouped GEMM wants a tile per compute unit in every projection
         with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
             bl.forward_grouped(Xq, xs, rs, projs)
         return
     Ys, accs = bl.forward_grouped(Xq, xs, rs, projs, want_acc=True)
     name = bl.last_dispatch()
     torch.cuda.synchronize()
-    if skinny_direct(M, K, sum(Ns), len(Ns)):
+    if past_skinny:
+        assert name == "gemm_dense_dma_32x32_grouped", name
+    elif skinny_direct(M, K, sum(Ns), len(Ns)):
         assert name.startswith("skinny_direct_dense_") and name.endswith("_grouped"), name
     else:
         assert not name.startswith("skinny_direct"), name
