@@ -255,10 +255,13 @@ bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, b
  * bitlinear_proj).  Supported: 1 <= nproj <= 8 and M <= 16, or
  * 17 <= M <= 64 while the 16-token tiles times the 16-row weight blocks of
  * all projections make at most 1024 workgroups (512 for one projection), and
- * K within the kernels' range; past that limit, at 17-64 tokens, dense
- * weights (nm = {0, 0}) and two or more projections, each with K <= 4096 or
- * N >= 8192 and at least 256 output tiles of 32 x 32, run as one grouped
- * launch of the few-token GEMM.  Anything else returns
+ * K within the kernels' range.  Dense weights (nm = {0, 0}) at 9-64 tokens
+ * over at least 6912 rows in all, with 256 <= K <= 3072, run on the
+ * direct-load kernel with several token tiles per workgroup (at 33-64 tokens:
+ * fewer than 13824 rows, or at least 16384 with K <= 2048).  Past those, at
+ * 17-64 tokens, dense weights and two or more projections, each with
+ * K <= 4096 or N >= 8192 and at least 256 output tiles of 32 x 32, run as one
+ * grouped launch of the few-token GEMM.  Anything else returns
  * BITLINEAR_EUNSUPPORTED and launches nothing (call bitlinear_forward per
  * projection then).  Needs no workspace. */
 bitlinear_status bitlinear_forward_grouped(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,

@@ -65,6 +65,12 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
             return e;
         }
     }
+    // 9-64 tokens over wide dense projections: several token tiles per
+    // workgroup on the direct-load kernel
+    if (M >= 9 && M <= kSkinnyMaxM) {
+        const hipError_t e = launch_skinny_direct_tiles(Xq, x_scale, x_rowsum, one, p, M, K, stream, name, query);
+        if (e != hipErrorNotSupported) return e;
+    }
     // 17-64 tokens: the skinny kernel in tiles of 16 tokens where the tiles
     // make at most 512 workgroups (few weight rows: 2048 x 2048 at 64 tokens
     // 8.2 -> 4.2 us, 2048 x 256 9.2 -> 3.5 us); with more, the GEMM is faster
@@ -475,11 +481,15 @@ bitlinear_status bitlinear_forward_grouped(const int8_t *Xq, const float *x_scal
     if (M == 1)
         e = bl::launch_decode_dot4(nullptr, Xq, x_scale, x_rowsum, M, K, p, args, nullptr,
                                    bl::ActTransform{nullptr, nullptr, 0.0f}, stream, &name, false);
+    // wide dense projections at 9-64 tokens: several token tiles per workgroup
+    else if (M >= 9)
+        e = bl::launch_skinny_direct_tiles(Xq, x_scale, x_rowsum, args, p, M, K, stream, &name, false);
     // 17-64 tokens in tiles of 16 while the tiles make at most 512 workgroups
     // (the rule of the single forward), 1024 for two or more projections: one
     // launch then replaces several (q, k, v of a 3B block at 64 tokens, 640
     // workgroups: 12.8 us in three launches, one grouped launch less than half)
-    else if (M <= 16 || (M <= bl::kSkinnyMaxM && rows16 * ((M + 15) / 16) <= (nproj > 1 ? 1024 : 512)))
+    if (e == hipErrorNotSupported && M > 1 &&
+        (M <= 16 || (M <= bl::kSkinnyMaxM && rows16 * ((M + 15) / 16) <= (nproj > 1 ? 1024 : 512))))
         e = bl::launch_skinny_forward(Xq, x_scale, x_rowsum, args, p, M, K, stream, &name, false);
     // past that, several wide projections in one launch of the few-token GEMM
     if (e == hipErrorNotSupported && M > 16)

@@ -53,6 +53,12 @@ struct FusedProjArgs;                // skinny_impl.hpp
 hipError_t launch_skinny_direct(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
                                 Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);
 
+// The direct-load skinny MFMA forward with several 16-token tiles per
+// workgroup (dense weights at 9-64 tokens over at least 6912 weight rows, the
+// shapes where it measured faster); hipErrorNotSupported for every other shape.
+hipError_t launch_skinny_direct_tiles(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
+                               Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);
+
 // Several dense projections at 17-64 tokens in one launch of the few-token
 // GEMM's 32 x 32 tiles (where each alone would take them unsplit);
 // hipErrorNotSupported for every other shape.

@@ -22,11 +22,12 @@
 //
 // Where it is used (measured on MI355X against the staged kernel, dense
 // weights, us): gate + up of a 3B block (2 x 11008 rows, K = 2048) at 8
-// tokens 7.0 -> 6.3 and at 16 tokens 10.7 -> 7.5; gate + up of a 2B FFN
-// (2 x 6912, K = 2560) at 8 tokens 7.2 -> 6.2; the 3B down projection
-// (11008 -> 2048) at 8 tokens 7.6 -> 6.2; q, k, v of a 3B block at 64 tokens
-// (one grouped launch) 6.8 -> 5.3.  At 4 tokens and for narrow projections
-// (<= 2560 rows) at 8-16 tokens the staged kernel measured as fast or faster.
+// tokens 7.0 -> 6.3; gate + up of a 2B FFN (2 x 6912, K = 2560) at 8 tokens
+// 7.2 -> 6.2; the 3B down projection (11008 -> 2048) at 8 tokens 7.6 -> 6.2;
+// q, k, v of a 3B block at 64 tokens (one grouped launch) 6.8 -> 5.3.  At 4
+// tokens and for narrow projections (<= 2560 rows) at 8-16 tokens the staged
+// kernel measured as fast or faster.  Wide projections at 9-64 tokens take
+// the form with several token tiles per workgroup (skinny_direct_tiles.hip) first.
 #include <stdio.h>
 
 #include "kernels.hpp"
@@ -246,8 +247,6 @@ hipError_t launch_skinny_direct(const int8_t *Xq, const float *xs, const int32_t
     const bool wide = rows >= 8192;
     if (M >= 5 && M <= 8 && C >= 8 && C <= 32 && wide)
         return launch<4, 8, 8, 2>(Xq, xs, rs, args, M, K, stream, name, query);
-    if (M >= 9 && M <= 16 && C >= 8 && C <= 32 && wide)
-        return launch<2, 16, 16, 2>(Xq, xs, rs, args, M, K, stream, name, query);
     if (M >= 5 && M <= 8 && C > 32 && C <= 40 && wide)
         return launch<2, 20, 8, 1>(Xq, xs, rs, args, M, K, stream, name, query);
     if (M >= 5 && M <= 8 && C > 128 && C <= 192)

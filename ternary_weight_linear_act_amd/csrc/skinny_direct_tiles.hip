@@ -1,0 +1,285 @@
+// Few-token forward (9 to 64 tokens) over wide projections: the packed
+// weights straight from the load registers into the MFMA operand, as in the
+// direct-load skinny kernel, with TT tiles of 16 tokens sharing every weight
+// fragment a lane loads.
+//
+// "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 5.1: the packed ternary
+// weights (four per byte) are what moves from HBM and are unpacked on chip;
+// "BitNet 논문 분석: 1-Bit LLM의 시대", section "Absmean 양자화 함수": the
+// integer linear of the ternary weights with the int8 activations, then the
+// rescale by the weight and activation scales.  Same arithmetic as the other
+// skinny kernels, bit for bit.
+//
+// Workgroup: KS = 4 waves, 16 * RG weight rows, TT * 16 token rows.  Wave w
+// takes the w-th quarter of K's 64-wide chunks: its activation range of the
+// tile's token rows is staged in LDS by coalesced loads, and lane (r, q) loads
+// chunk 4 s + q of weight row 16 g + r for step s and column block g (64
+// bytes of each of 16 rows per load instruction), which is its B operand for
+// the step's four MFMAs against every token tile.  Codes of chunks past the
+// wave's range are masked to 0 (zero products: the offset code 0 times any
+// activation), so K needs no padding.  The four partial tiles of each output
+// tile meet in LDS, in the activation area, at the tile's owner wave, which
+// applies the offset-code correction and the dequant scale.  Token groups
+// (16 * TT tokens each) of one row block run on one XCD (workgroup ids 8
+// apart), so the second group's weight reads hit that XCD's L2.
+//
+// Where it is used (dense weights, measured on MI355X against the library's
+// previous kernel for the shape, us):
+//   9-16 tokens, >= 6912 rows (TT 1, RG 2): gate + up of a 3B block (2 x 11008,
+//     K 2048) at 16 tokens 7.6 -> 6.9; a 2B FFN's gate + up (2 x 6912, K 2560)
+//     14.5 -> 6.8; one 6912-row projection 8.0 -> 5.3
+//   17-32 tokens, >= 13824 rows (TT 1, RG 4): 3B gate + up at 32 tokens
+//     10.4 -> 8.7; 2B gate + up 21.1 -> 9.2
+//   17-32 tokens, 6912-13823 rows (TT 1, RG 2): 11008 rows at 32 tokens
+//     8.3 -> 6.4; 6912 rows 10.5 -> 6.3
+//   33-64 tokens, >= 16384 rows, K <= 2048 (TT 2, RG 6): 3B gate + up at 64
+//     tokens 16.0 -> 11.4, at 48 15.8 -> 11.1
+//   33-64 tokens, 6912-13823 rows (TT 1, RG 4): 11008 rows at 64 tokens
+//     8.9 -> 8.2; 6912 rows (K 2560) 9.5 -> 8.5
+// Non-temporal stores of Y: the outputs leave in one burst at the end.
+#include <stdio.h>
+
+#include "kernels.hpp"
+#include "skinny_impl.hpp"
+
+namespace bl {
+namespace skinny_direct_tiles {
+
+using skinny::i32x4;
+using skinny::u32x4;
+
+constexpr int KS = 4;
+
+template <int TT, int RG, int S>
+struct Lds {
+    static constexpr int kRow = S * 256 + 16;                      // staged token row (16-byte pad: banks)
+    static constexpr int kWave = TT * 16 * kRow;
+    static constexpr int kAct = KS * kWave;
+    static constexpr int kPart = (KS - 1) * TT * RG * 64 * 16;     // [tile][slot][lane] i32x4
+    static constexpr int kBytes = kAct > kPart ? kAct : kPart;
+};
+
+// Dense weights.  The host keeps KS <= K / 64 <= 4 * S * KS, M <= 64 and
+// ty = ceil(M / (16 TT)) token groups; grid = ceil(blocks / 8) * 8 * ty.
+template <int TT, int RG, int S>
+__global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8_t *__restrict__ Xq,
+                                                               const float *__restrict__ x_scale,
+                                                               const int32_t *__restrict__ x_rowsum,
+                                                               FusedProjArgs args, int64_t M, int64_t K)
+{
+    using L = Lds<TT, RG, S>;
+    constexpr int XLOADS = TT * 16 * S * 16 / 64;                 // 16-byte pieces per lane
+    __shared__ __attribute__((aligned(16))) uint8_t s_x[L::kBytes];
+    __shared__ int32_t s_rs[64];
+    __shared__ float s_xs[64];
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 15, q = lane >> 4;
+
+    // workgroup id -> (row block, token group): ids 8 apart share an XCD
+    const int ty = (int)((M + 16 * TT - 1) / (16 * TT));
+    const int id = (int)blockIdx.x;
+    const int by = (id / 8) % ty;
+    const int bx = (id / (8 * ty)) * 8 + id % 8;
+    if (bx >= args.block_start[args.nproj]) return;                // whole workgroup, before any barrier
+    const int p = proj_of_block(args, bx);
+    const int64_t N = args.N[p];
+    const uint8_t *packed = args.packed[p];
+    const float *w_scale = args.w_scale[p];
+    const int64_t t0 = (int64_t)by * TT * 16;
+    Xq += t0 * K;
+    x_scale += t0;
+    x_rowsum += t0;
+    const int64_t mg = M - t0;                                     // tokens of this group (>= 1)
+    float *Y = args.Y[p] + t0 * N;
+    int32_t *acc_out = args.acc[p] ? args.acc[p] + t0 * N : nullptr;
+    const int64_t n0 = (int64_t)(bx - args.block_start[p]) * 16 * RG;
+    const int64_t C = K / 64;
+    const int64_t c_lo = C * wave / KS;
+    const int cw = (int)(C * (wave + 1) / KS - c_lo);              // 1 <= cw <= 4 S
+    uint8_t *lx = s_x + wave * L::kWave;
+    // every kernel argument in SGPRs now: a scalar load left pending would make
+    // the compiler wait for all outstanding memory operations at its first use
+    asm volatile("" ::"s"(Xq), "s"(x_scale), "s"(x_rowsum), "s"(packed), "s"(w_scale), "s"(Y), "s"(acc_out));
+
+    // 1. the wave's activation range: consecutive lanes, consecutive 16-byte
+    //    pieces of a token row (rows past the group are not staged: they only
+    //    feed outputs that are not stored)
+    const int mt = (int)min(mg, (int64_t)(TT * 16));
+    u32x4 x[XLOADS];
+    int x_off[XLOADS];
+    const int xw = cw * 4;
+    const float inv_xw = 1.0f / (float)xw;
+#pragma unroll
+    for (int i = 0; i < XLOADS; ++i) {
+        const int f = i * 64 + lane;
+        const int m = (int)(((float)f + 0.5f) * inv_xw);           // exact: f < 2^24
+        const int piece = f - m * xw;
+        x_off[i] = (m < mt) ? m * L::kRow + piece * 16 : -1;
+        x[i] = *reinterpret_cast<const u32x4 *>(Xq + (int64_t)min(m, mt - 1) * K + c_lo * 64 +
+                                                (m < mt ? piece : 0) * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. every weight chunk of the lane, all in flight (chunks past the range
+    //    re-read its last one, rows past N re-read row N - 1)
+    u32x4 w[S][RG];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int64_t n = min(n0 + 16 * g + r, N - 1);
+            w[s][g] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(packed + n * (K / 4) + (c_lo + min(4 * s + q, cw - 1)) * 16));
+        }
+    // the epilogue's per-token values last: waited for only at the end
+    const int mrow = min(lane, (int)mg - 1);
+    const int rs_l = x_rowsum[mrow];
+    const float xs_l = x_scale[mrow];
+    const float beta = w_scale[0];
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. activations to LDS; the wave reads only its own area
+#pragma unroll
+    for (int i = 0; i < XLOADS; ++i)
+        if (x_off[i] >= 0) *reinterpret_cast<u32x4 *>(lx + x_off[i]) = x[i];
+    __builtin_amdgcn_s_waitcnt(0xc07f);                            // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+
+    // 4. MFMA: per step and token tile, the lane's four activation words
+    //    against each column block's weight words, as the weights arrive
+    i32x4 acc[TT][RG];
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int g = 0; g < RG; ++g) acc[tt][g] = i32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const bool live = 4 * s + q < cw;
+        const uint32_t cm = live ? kCodeMask : 0u;
+        const int aoff = r * L::kRow + (live ? (4 * s + q) * 64 : 0);
+#pragma unroll
+        for (int tt = 0; tt < TT; ++tt) {
+            i32x4 a[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) a[t] = *reinterpret_cast<const i32x4 *>(lx + tt * 16 * L::kRow + aoff + 16 * t);
+#pragma unroll
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int g = 0; g < RG; ++g) {
+                    const uint32_t wv = w[s][g][t];
+                    i32x4 b;
+                    b[0] = (int)(wv & cm);
+                    b[1] = (int)((wv >> 2) & cm);
+                    b[2] = (int)((wv >> 4) & cm);
+                    b[3] = (int)((wv >> 6) & cm);
+                    acc[tt][g] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[t], b, acc[tt][g], 0, 0, 0);
+                }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 5. partial tiles to their owner wave (tile j = tt RG + g, owner j % KS),
+    //    in the activation area once every wave is done with it
+    __syncthreads();
+    if (wave == 0) {
+        s_rs[lane] = rs_l;
+        s_xs[lane] = xs_l;
+    }
+    i32x4 *part = reinterpret_cast<i32x4 *>(s_x);
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int j = tt * RG + g, owner = j % KS;
+            if (owner != wave) part[(j * (KS - 1) + wave - (wave > owner ? 1 : 0)) * 64 + lane] = acc[tt][g];
+        }
+    __syncthreads();
+
+    // 6. epilogue: lane (r, q) holds tokens 4 q .. 4 q + 3 of the token tile,
+    //    weight row 16 g + r
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int j = tt * RG + g;
+            if (j % KS != wave) continue;
+            i32x4 sum = acc[tt][g];
+#pragma unroll
+            for (int sl = 0; sl < KS - 1; ++sl) sum += part[(j * (KS - 1) + sl) * 64 + lane];
+            const int64_t n = n0 + 16 * g + r;
+            if (n >= N) continue;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int m = 16 * tt + 4 * q + v;
+                if (m < mg) {
+                    const int av = sum[v] - s_rs[m];
+                    __builtin_nontemporal_store((float)av * (beta * s_xs[m]), &Y[(int64_t)m * N + n]);
+                    if (acc_out) acc_out[(int64_t)m * N + n] = av;
+                }
+            }
+        }
+}
+
+}  // namespace skinny_direct_tiles
+
+namespace {
+
+thread_local char g_name[80];
+
+template <int TT, int RG, int S>
+hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, FusedProjArgs args, int64_t M, int64_t K,
+                  hipStream_t stream, const char **name, bool query)
+{
+    using L = skinny_direct_tiles::Lds<TT, RG, S>;
+    static_assert(L::kBytes + 512 <= 160 * 1024, "LDS");
+    constexpr int KS = skinny_direct_tiles::KS;
+    const int64_t C = K / 64;
+    const int64_t ty = (M + 16 * TT - 1) / (16 * TT);
+    if (C < KS || C > (int64_t)4 * S * KS || ty < 1 || ty > 4) return hipErrorNotSupported;
+    int64_t blocks = 0;
+    for (int i = 0; i < args.nproj; ++i) {
+        args.block_start[i] = (int32_t)blocks;
+        blocks += (args.N[i] + 16 * RG - 1) / (16 * RG);
+    }
+    for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
+    const int64_t grid = (blocks + 7) / 8 * 8 * ty;
+    if (grid > (1LL << 30)) return hipErrorNotSupported;
+    snprintf(g_name, sizeof g_name, "skinny_direct_tiles_dense_t%d_rg%d_s%d%s", TT, RG, S, args.nproj > 1 ? "_grouped" : "");
+    *name = g_name;
+    if (query) return hipSuccess;
+    hipLaunchKernelGGL((skinny_direct_tiles::skinny_direct_tiles_kernel<TT, RG, S>), dim3((unsigned)grid), dim3(64 * KS), 0, stream,
+                       Xq, xs, rs, args, M, K);
+    return hipGetLastError();
+}
+
+template <int TT, int RG>
+hipError_t launch_k(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args, int64_t M,
+                    int64_t K, hipStream_t stream, const char **name, bool query)
+{
+    if (K / 64 <= 32) return launch<TT, RG, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+    return launch<TT, RG, 3>(Xq, xs, rs, args, M, K, stream, name, query);
+}
+
+}  // namespace
+
+// The measured cases of the file comment (dense weights, 9-64 tokens, K 256 to
+// 3072); hipErrorNotSupported (nothing launched) for every other shape.
+hipError_t launch_skinny_direct_tiles(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
+                               Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query)
+{
+    if (p != Pattern::Dense || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
+    int64_t rows = 0;
+    for (int i = 0; i < args.nproj; ++i) rows += args.N[i];
+    const int64_t C = K / 64;
+    if (M < 9 || M > 64 || C < skinny_direct_tiles::KS || C > 48 || rows < 6912) return hipErrorNotSupported;
+    if (M <= 16) return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+    if (M <= 32) {
+        if (rows >= 13824) return launch_k<1, 4>(Xq, xs, rs, args, M, K, stream, name, query);
+        return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+    }
+    if (rows < 13824) return launch_k<1, 4>(Xq, xs, rs, args, M, K, stream, name, query);
+    if (rows >= 16384 && C <= 32) return launch<2, 6, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+    return hipErrorNotSupported;
+}
+
+}  // namespace bl

@@ -102,6 +102,28 @@ def skinny_direct(M, K, rows, nproj=1, nm=(0, 0)):
     if nm != (0, 0):
         return False
     wide = rows >= 8192
-    return ((5 <= M <= 8 and 8 <= C <= 32 and wide) or (9 <= M <= 16 and 8 <= C <= 32 and wide)
+    return ((5 <= M <= 8 and 8 <= C <= 32 and wide)
             or (5 <= M <= 8 and 32 < C <= 40 and wide) or (5 <= M <= 8 and 128 < C <= 192)
-            or (17 <= M <= 64 and nproj >= 2 and 8 <= C <= 32))
+            or (17 <= M <= 64 and nproj >= 2 and 8 <= C <= 32 and not direct_tiles(M, K, rows)))
+
+
+def direct_tiles(M, K, rows, nm=(0, 0)):
+    """Dense weights at 9-64 tokens over at least 6912 weight rows (all
+    projections of a call together), K of 4 to 48 chunks of 64: the direct-load
+    kernel with several 16-token tiles per workgroup.  Its dispatch name
+    (without the "_grouped" of a grouped call), or None."""
+    C = K // 64
+    if nm != (0, 0) or not (9 <= M <= 64) or not (4 <= C <= 48) or rows < 6912:
+        return None
+    s = 2 if C <= 32 else 3
+    if M <= 16:
+        tt, rg = 1, 2
+    elif M <= 32:
+        tt, rg = (1, 4) if rows >= 13824 else (1, 2)
+    elif rows < 13824:
+        tt, rg = 1, 4
+    elif rows >= 16384 and C <= 32:
+        tt, rg = 2, 6
+    else:
+        return None
+    return "skinny_direct_tiles_dense_t%d_rg%d_s%d" % (tt, rg, s)

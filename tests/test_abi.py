@@ -214,9 +214,10 @@ def test_grouped_validation(lib):
     assert f(P(), P(), P(), 4, 100, NM(0, 0), arr, 1, None) == -1            # K % 64
     assert f(P(), P(), P(), 65, 128, NM(0, 0), arr, 1, None) == -2           # M > 64
     big = (Proj * 2)(Proj(A, A, 11008, A, None), Proj(A, A, 11008, A, None))
-    # 4 x 1376 skinny workgroups and past what the grouped GEMM takes: one
-    # projection, an N:M pattern, or K > 4096 with fewer than 8192 rows
-    assert f(P(), P(), P(), 64, 2048, NM(0, 0), big, 1, None) == -2
+    # past the skinny tiles' workgroups, the token-tile kernel's K (48 chunks)
+    # and what the grouped GEMM takes: one projection, an N:M pattern, or
+    # K > 4096 with fewer than 8192 rows
+    assert f(P(), P(), P(), 64, 4096, NM(0, 0), big, 1, None) == -2
     assert f(P(), P(), P(), 64, 2048, NM(2, 4), big, 2, None) == -2
     deep = (Proj * 2)(Proj(A, A, 4096, A, None), Proj(A, A, 4096, A, None))
     assert f(P(), P(), P(), 64, 8192, NM(0, 0), deep, 2, None) == -2

@@ -67,6 +67,7 @@ def check_replays(body, outs, refill):
 
 @pytest.mark.parametrize("M,N,K,nm", [(1, 2560, 6912, (0, 0)), (1, 6912, 2560, (2, 4)), (1, 2048, 2048, (6, 8)),
                                       (8, 2048, 11008, (0, 0)), (20, 4096, 6912, (0, 0)), (3, 300, 11008, (6, 8)),
+                                      (40, 8200, 2048, (0, 0)),
                                       (64, 2048, 2048, (2, 4)), (512, 8960, 1536, (6, 8)),
                                       (2048, 6912, 2560, (0, 0)), (2048, 6912, 2560, (2, 4)),
                                       (1000, 8000, 640, (2, 4)), (300, 1000, 1472, (0, 0))])

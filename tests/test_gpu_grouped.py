@@ -6,7 +6,7 @@ import pytest
 
 from ternary_weight_linear_act_amd import workloads
 
-from gpu_helpers import check_y, cover_rows, hip_forward, hip_pack, hip_quant, skinny_direct
+from gpu_helpers import check_y, cover_rows, direct_tiles, hip_forward, hip_pack, hip_quant, skinny_direct
 
 pytestmark = pytest.mark.gpu
 
@@ -106,10 +106,13 @@ def test_grouped_unsupported_raises():
     pk2, ws2 = hip_pack(W2, (0, 0))
     with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
         bl.forward_grouped(Xq, xs, rs, [(pk2, ws2, 2080)])
-    # a wide projection beside one of too few GEMM tiles (2080 rows: 130 of
-    # 32 x 32 at 64 tokens, below one per compute unit)
+    # a wide projection beside one of too few GEMM tiles (3000 rows: 188 of
+    # 32 x 32 at 64 tokens, below one per compute unit); 14008 rows in all is
+    # outside the token-tile kernel's rules at 33-64 tokens
+    W4, _ = workloads.small_case(4503, 1, 3000, 2048)
+    pk4, ws4 = hip_pack(W4, (0, 0))
     with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
-        bl.forward_grouped(Xq, xs, rs, [(pk, ws, 11008), (pk2, ws2, 2080)])
+        bl.forward_grouped(Xq, xs, rs, [(pk, ws, 11008), (pk4, ws4, 3000)])
     # deep K over few rows: neither the skinny tiles (LDS) nor the grouped GEMM
     W3, X3 = workloads.small_case(4502, 64, 2048, 11008)
     pk3, ws3 = hip_pack(W3, (0, 0))
@@ -119,12 +122,13 @@ def test_grouped_unsupported_raises():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("M,K,Ns", [(64, 2048, (11008, 11008)), (17, 1024, (8192, 8300)), (33, 512, (8200, 12000, 8192)),
+@pytest.mark.parametrize("M,K,Ns", [(64, 2560, (6912, 6912)), (17, 3136, (8192, 8300)), (33, 3200, (8200, 12000, 8192)),
                                     (48, 4096, (8200, 8200)), (64, 6144, (8192, 8200))])
 def test_grouped_gemm(M, K, Ns):
-    # past the skinny kernel's workgroup limit: one launch of the few-token
-    # GEMM's 32 x 32 tiles for all projections (ragged weight rows, a ragged
-    # last token tile)
+    # past the skinny kernel's workgroup limit and outside the token-tile
+    # kernel's rules: one launch of the few-token GEMM's 32 x 32 tiles for all
+    # projections (ragged weight rows, a ragged last token tile)
+    assert direct_tiles(M, K, sum(Ns)) is None
     seed = 4600 + M + K + sum(Ns)
     Ws = [workloads.small_case(seed + i, 1, N, K)[0] for i, N in enumerate(Ns)]
     _, X = workloads.small_case(seed + 77, M, 8, K, outlier_frac=0.01)
@@ -134,11 +138,14 @@ def test_grouped_gemm(M, K, Ns):
     check(Ws, X, (0, 0), packs, xq, Ys, accs)
 
 
-def test_block_3b_gate_up_grouped_gemm_full_size():
+@pytest.mark.parametrize("M", [16, 32, 64])
+def test_block_3b_gate_up_grouped_full_size(M):
+    # gate + up of the 3B block (2 x 11008 rows, K = 2048) in one launch of the
+    # direct-load kernel with several token tiles per workgroup
     d = workloads.draw("block_3b", projs=["gate", "up"], Ms=(64,))
     Ws = [d.W["gate"], d.W["up"]]
-    X = d.X[("gate", 64)]
-    print("case grouped GEMM block_3b gate+up M=64", flush=True)
+    X = d.X[("gate", 64)][:M]
+    print("case grouped block_3b gate+up M=%d" % M, flush=True)
     packs, xq, Ys, accs, name = run_grouped(Ws, X, (0, 0))
-    assert name == "gemm_dense_dma_32x32_grouped", name
+    assert name == direct_tiles(M, 2048, 22016) + "_grouped", name
     check(Ws, X, (0, 0), packs, xq, Ys, accs)

@@ -4,14 +4,16 @@ measured faster than the staged kernel): every rule of its dispatch at its
 edges, with ragged weight rows (a partial last column block), against the
 CPU oracle (acc bit-exact, Y within 1e-5) and bit-identical to the forward
 of each projection alone.  Next to each rule, a shape just outside it takes
-the staged kernel.  Grouped calls past the skinny tiles' workgroup limit take
-the few-token GEMM's grouped launch where its rule holds."""
+the staged kernel.  Wide projections at 9-64 tokens take the form with
+several token tiles per workgroup (tested on its own); grouped calls past
+the skinny tiles' workgroup limit take the few-token GEMM's grouped launch
+where its rule holds."""
 import numpy as np
 import pytest
 
 from ternary_weight_linear_act_amd import workloads
 
-from gpu_helpers import check_y, cover_rows, full_check, hip_forward, hip_pack, hip_quant, skinny_direct
+from gpu_helpers import check_y, cover_rows, direct_tiles, full_check, hip_forward, hip_pack, hip_quant, skinny_direct
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +21,6 @@ pytestmark = pytest.mark.gpu
 # (M, N, K): each rule at its smallest and largest K and token count
 SINGLE = [
     (5, 8200, 512), (8, 8200, 2048), (6, 8192, 1024),          # 5-8 tokens, K <= 2048, >= 8192 rows
-    (9, 8200, 512), (16, 8200, 2048), (12, 9000, 1536),        # 9-16 tokens, same K range
     (5, 8200, 2112), (8, 8200, 2560),                          # 5-8 tokens, K 2112-2560
     (5, 300, 8256), (8, 300, 12288), (7, 2048, 11008),         # 5-8 tokens, deep K
 ]
@@ -35,11 +36,11 @@ def test_direct_single(M, N, K):
     assert name.startswith("skinny_direct_dense_"), name
 
 
-@pytest.mark.parametrize("M,N,K", [(4, 8200, 2048), (8, 8191, 2048), (8, 8200, 448), (17, 8200, 2048),
-                                   (8, 8200, 2624), (8, 300, 8192), (8, 300, 12352)])
+@pytest.mark.parametrize("M,N,K", [(4, 8200, 2048), (8, 8191, 2048), (8, 8200, 448), (17, 6900, 2048),
+                                   (8, 8200, 2624), (8, 300, 8192), (8, 300, 12352), (12, 6900, 2048)])
 def test_outside_rules_take_the_staged_kernel(M, N, K):
     import ternary_weight_linear_act_amd as bl
-    assert not skinny_direct(M, K, N)
+    assert not skinny_direct(M, K, N) and not direct_tiles(M, K, N)
     W, X = workloads.small_case(5200 + M + K + N, M, N, K)
     full_check(W, X, (0, 0), rows=cover_rows(M), label="skinny-direct-outside")
     assert not bl.last_dispatch().startswith("skinny_direct"), bl.last_dispatch()
@@ -68,9 +69,10 @@ def test_direct_grouped(M, K, Ns):
     packs = [hip_pack(W, (0, 0)) for W in Ws]
     Xq, xs, rs = hip_quant(X)
     projs = [(pk, ws, W.shape[0]) for (pk, ws), W in zip(packs, Ws)]
+    tiles = direct_tiles(M, K, sum(Ns))
     past_skinny = M > 16 and sum(-(-N // 16) for N in Ns) * -(-M // 16) > 1024
     gemm = M > 16 and len(Ns) > 1 and all((K <= 4096 or N >= 8192) and -(-M // 32) * -(-N // 32) >= 256 for N in Ns)
-    if past_skinny and not gemm:
+    if not tiles and past_skinny and not gemm:
         # past 16 tokens the skinny tiles take at most 1024 workgroups, and
         # the grouped GEMM wants a tile per compute unit in every projection
         with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
@@ -79,7 +81,9 @@ def test_direct_grouped(M, K, Ns):
     Ys, accs = bl.forward_grouped(Xq, xs, rs, projs, want_acc=True)
     name = bl.last_dispatch()
     torch.cuda.synchronize()
-    if past_skinny:
+    if tiles:
+        assert name == tiles + "_grouped", name
+    elif past_skinny:
         assert name == "gemm_dense_dma_32x32_grouped", name
     elif skinny_direct(M, K, sum(Ns), len(Ns)):
         assert name.startswith("skinny_direct_dense_") and name.endswith("_grouped"), name
