@@ -79,6 +79,13 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
         const hipError_t e = launch_skinny_forward(Xq, x_scale, x_rowsum, one, p, M, K, stream, name, query);
         if (e != hipErrorNotSupported) return e;
     }
+    // deep K at 9-64 tokens: the token-tile kernel with K split over the
+    // workgroups
+    if (M >= 9 && M <= kSkinnyMaxM) {
+        const hipError_t e = launch_skinny_direct_tiles_split(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y,
+                                                              acc, scratch, stream, name);
+        if (e != hipErrorNotSupported) return e;
+    }
     if (M <= kGemvMaxM) {
         *name = gemv_names[pi];
         if (query) return hipSuccess;

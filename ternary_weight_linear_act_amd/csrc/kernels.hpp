@@ -54,10 +54,21 @@ hipError_t launch_skinny_direct(const int8_t *Xq, const float *xs, const int32_t
                                 Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);
 
 // The direct-load skinny MFMA forward with several 16-token tiles per
-// workgroup (dense weights at 9-64 tokens over at least 6912 weight rows, the
-// shapes where it measured faster); hipErrorNotSupported for every other shape.
+// workgroup (dense weights at 9-64 tokens over at least 6912 weight rows, or
+// 2560 from 17 tokens: the shapes where it measured faster);
+// hipErrorNotSupported for every other shape.
 hipError_t launch_skinny_direct_tiles(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
                                Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);
+
+// The same kernel for one dense projection with K split over the workgroups
+// (9-64 tokens, 49-384 chunks of 64, 1024-4096 weight rows, 2560 past 32
+// tokens): int32 partials
+// in the caller's workspace, then an elementwise pass; hipErrorNotSupported
+// for every other shape.
+hipError_t launch_skinny_direct_tiles_split(const int8_t *Xq, const float *xs, const int32_t *rs,
+                                            const uint8_t *packed, const float *w_scale, Pattern p, int64_t M,
+                                            int64_t N, int64_t K, float *Y, int32_t *acc, Scratch &scratch,
+                                            hipStream_t stream, const char **name);
 
 // Several dense projections at 17-64 tokens in one launch of the few-token
 // GEMM's 32 x 32 tiles (where each alone would take them unsplit);

@@ -23,8 +23,8 @@
 // (16 * TT tokens each) of one row block run on one XCD (workgroup ids 8
 // apart), so the second group's weight reads hit that XCD's L2.
 //
-// Where it is used (dense weights, measured on MI355X against the library's
-// previous kernel for the shape, us):
+// Where it is used (dense weights; a call's projections together; measured
+// on MI355X against the library's previous kernel for the shape, us):
 //   9-16 tokens, >= 6912 rows (TT 1, RG 2): gate + up of a 3B block (2 x 11008,
 //     K 2048) at 16 tokens 7.6 -> 6.9; a 2B FFN's gate + up (2 x 6912, K 2560)
 //     14.5 -> 6.8; one 6912-row projection 8.0 -> 5.3
@@ -36,6 +36,10 @@
 //     tokens 16.0 -> 11.4, at 48 15.8 -> 11.1
 //   33-64 tokens, 6912-13823 rows (TT 1, RG 4): 11008 rows at 64 tokens
 //     8.9 -> 8.2; 6912 rows (K 2560) 9.5 -> 8.5
+//   17-64 tokens, 2560-6911 rows (TT 1, RG 2): 2560 x 2560 at 64 tokens
+//     10.1 -> 6.0, at 17 6.7 -> 4.9; 3072 x 3072 at 48 tokens 10.6 -> 5.9;
+//     5120 rows (K 2048) at 32 tokens 9.4 -> 5.2; q, k, v of a 3B block
+//     (2560 rows in all) at 64 tokens 5.4 -> 5.0
 // Non-temporal stores of Y: the outputs leave in one burst at the end.
 #include <stdio.h>
 
@@ -59,13 +63,17 @@ struct Lds {
     static constexpr int kBytes = kAct > kPart ? kAct : kPart;
 };
 
-// Dense weights.  The host keeps KS <= K / 64 <= 4 * S * KS, M <= 64 and
-// ty = ceil(M / (16 TT)) token groups; grid = ceil(blocks / 8) * 8 * ty.
-template <int TT, int RG, int S>
+// Dense weights.  ty = ceil(M / (16 TT)) token groups (M <= 64) and `parts`
+// K parts (1 unless SPLIT); grid = ceil(blocks / 8) * 8 * ty * parts.  The
+// host keeps KS <= (chunks of a K part) <= 4 * S * KS.  SPLIT (one
+// projection): each workgroup writes the raw int32 sums of its K part to
+// ws[part][m][n] (M x N per part) and split_epilogue_kernel finishes.
+template <int TT, int RG, int S, bool SPLIT>
 __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8_t *__restrict__ Xq,
-                                                               const float *__restrict__ x_scale,
-                                                               const int32_t *__restrict__ x_rowsum,
-                                                               FusedProjArgs args, int64_t M, int64_t K)
+                                                                      const float *__restrict__ x_scale,
+                                                                      const int32_t *__restrict__ x_rowsum,
+                                                                      FusedProjArgs args, int64_t M, int64_t K,
+                                                                      int32_t parts, int32_t *__restrict__ ws)
 {
     using L = Lds<TT, RG, S>;
     constexpr int XLOADS = TT * 16 * S * 16 / 64;                 // 16-byte pieces per lane
@@ -75,11 +83,14 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
 
-    // workgroup id -> (row block, token group): ids 8 apart share an XCD
+    // workgroup id -> (row block, token group, K part): ids 8 apart share an XCD
     const int ty = (int)((M + 16 * TT - 1) / (16 * TT));
+    const int ny = SPLIT ? ty * parts : ty;
     const int id = (int)blockIdx.x;
-    const int by = (id / 8) % ty;
-    const int bx = (id / (8 * ty)) * 8 + id % 8;
+    const int yy = (id / 8) % ny;
+    const int bx = (id / (8 * ny)) * 8 + id % 8;
+    const int by = yy % ty;
+    const int kp = SPLIT ? yy / ty : 0;
     if (bx >= args.block_start[args.nproj]) return;                // whole workgroup, before any barrier
     const int p = proj_of_block(args, bx);
     const int64_t N = args.N[p];
@@ -94,8 +105,10 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8
     int32_t *acc_out = args.acc[p] ? args.acc[p] + t0 * N : nullptr;
     const int64_t n0 = (int64_t)(bx - args.block_start[p]) * 16 * RG;
     const int64_t C = K / 64;
-    const int64_t c_lo = C * wave / KS;
-    const int cw = (int)(C * (wave + 1) / KS - c_lo);              // 1 <= cw <= 4 S
+    const int64_t cp_lo = SPLIT ? C * kp / parts : 0;              // the part's chunks
+    const int64_t cp = SPLIT ? C * (kp + 1) / parts - cp_lo : C;
+    const int64_t c_lo = cp_lo + cp * wave / KS;
+    const int cw = (int)(cp_lo + cp * (wave + 1) / KS - c_lo);     // 1 <= cw <= 4 S
     uint8_t *lx = s_x + wave * L::kWave;
     // every kernel argument in SGPRs now: a scalar load left pending would make
     // the compiler wait for all outstanding memory operations at its first use
@@ -208,6 +221,15 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8
             for (int sl = 0; sl < KS - 1; ++sl) sum += part[(j * (KS - 1) + sl) * 64 + lane];
             const int64_t n = n0 + 16 * g + r;
             if (n >= N) continue;
+            if constexpr (SPLIT) {
+                int32_t *wp = ws + ((int64_t)kp * M + t0) * N + n;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = 16 * tt + 4 * q + v;
+                    if (m < mg) wp[(int64_t)m * N] = sum[v];
+                }
+                continue;
+            }
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int m = 16 * tt + 4 * q + v;
@@ -218,6 +240,24 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8
                 }
             }
         }
+}
+
+// Sum of the K parts' int32 partials (integer sums: exact in any order),
+// offset-code correction and dequant scale; one output per thread.
+__global__ __launch_bounds__(256) void split_epilogue_kernel(const float *__restrict__ x_scale,
+                                                             const int32_t *__restrict__ x_rowsum,
+                                                             const float *__restrict__ w_scale, int64_t M, int64_t N,
+                                                             int32_t parts, const int32_t *__restrict__ ws,
+                                                             float *__restrict__ Y, int32_t *__restrict__ acc_out)
+{
+    const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= M * N) return;
+    const int64_t m = idx / N;
+    int acc = 0;
+    for (int o = 0; o < parts; ++o) acc += ws[(int64_t)o * M * N + idx];
+    const int av = acc - x_rowsum[m];
+    Y[idx] = (float)av * (w_scale[0] * x_scale[m]);
+    if (acc_out) acc_out[idx] = av;
 }
 
 }  // namespace skinny_direct_tiles
@@ -247,8 +287,48 @@ hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, FusedPro
     snprintf(g_name, sizeof g_name, "skinny_direct_tiles_dense_t%d_rg%d_s%d%s", TT, RG, S, args.nproj > 1 ? "_grouped" : "");
     *name = g_name;
     if (query) return hipSuccess;
-    hipLaunchKernelGGL((skinny_direct_tiles::skinny_direct_tiles_kernel<TT, RG, S>), dim3((unsigned)grid), dim3(64 * KS), 0, stream,
-                       Xq, xs, rs, args, M, K);
+    hipLaunchKernelGGL((skinny_direct_tiles::skinny_direct_tiles_kernel<TT, RG, S, false>), dim3((unsigned)grid),
+                       dim3(64 * KS), 0, stream, Xq, xs, rs, args, M, K, 1, nullptr);
+    return hipGetLastError();
+}
+
+// One projection with K split into `parts` parts over the workgroups: int32
+// partials (parts x M x N) in the caller's workspace, then the epilogue kernel.
+template <int TT, int RG, int S>
+hipError_t launch_split(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                        const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc, int parts,
+                        Scratch &scratch, hipStream_t stream, const char **name)
+{
+    using L = skinny_direct_tiles::Lds<TT, RG, S>;
+    static_assert(L::kBytes + 512 <= 160 * 1024, "LDS");
+    constexpr int KS = skinny_direct_tiles::KS;
+    const int64_t C = K / 64;
+    const int64_t ty = (M + 16 * TT - 1) / (16 * TT);
+    // every K part holds between KS and 4 S KS chunks
+    if (parts < 2 || C / parts < KS || (C + parts - 1) / parts > (int64_t)4 * S * KS || ty < 1 || ty > 4)
+        return hipErrorNotSupported;
+    const int64_t blocks = (N + 16 * RG - 1) / (16 * RG);
+    const int64_t grid = (blocks + 7) / 8 * 8 * ty * parts;
+    if (grid > (1LL << 30) || blocks > (1LL << 30)) return hipErrorNotSupported;
+    snprintf(g_name, sizeof g_name, "skinny_direct_tiles_dense_t%d_rg%d_s%d_splitk%d", TT, RG, S, parts);
+    *name = g_name;
+    if (!scratch.take((size_t)parts * (size_t)(M * N) * 4)) return scratch.query ? hipSuccess : hipErrorOutOfMemory;
+    FusedProjArgs args = {};
+    args.nproj = 1;
+    args.packed[0] = packed;
+    args.w_scale[0] = w_scale;
+    args.N[0] = N;
+    args.Y[0] = Y;
+    args.acc[0] = acc;
+    args.block_start[0] = 0;
+    for (int i = 1; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
+    int32_t *ws = reinterpret_cast<int32_t *>(scratch.ptr);
+    hipLaunchKernelGGL((skinny_direct_tiles::skinny_direct_tiles_kernel<TT, RG, S, true>), dim3((unsigned)grid),
+                       dim3(64 * KS), 0, stream, Xq, xs, rs, args, M, K, (int32_t)parts, ws);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(skinny_direct_tiles::split_epilogue_kernel, dim3((unsigned)((M * N + 255) / 256)), dim3(256), 0,
+                       stream, xs, rs, w_scale, M, N, (int32_t)parts, ws, Y, acc);
     return hipGetLastError();
 }
 
@@ -271,7 +351,11 @@ hipError_t launch_skinny_direct_tiles(const int8_t *Xq, const float *xs, const i
     int64_t rows = 0;
     for (int i = 0; i < args.nproj; ++i) rows += args.N[i];
     const int64_t C = K / 64;
-    if (M < 9 || M > 64 || C < skinny_direct_tiles::KS || C > 48 || rows < 6912) return hipErrorNotSupported;
+    if (M < 9 || M > 64 || C < skinny_direct_tiles::KS || C > 48 || rows < 2560) return hipErrorNotSupported;
+    if (rows < 6912) {
+        if (M >= 17) return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+        return hipErrorNotSupported;
+    }
     if (M <= 16) return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
     if (M <= 32) {
         if (rows >= 13824) return launch_k<1, 4>(Xq, xs, rs, args, M, K, stream, name, query);
@@ -280,6 +364,31 @@ hipError_t launch_skinny_direct_tiles(const int8_t *Xq, const float *xs, const i
     if (rows < 13824) return launch_k<1, 4>(Xq, xs, rs, args, M, K, stream, name, query);
     if (rows >= 16384 && C <= 32) return launch<2, 6, 2>(Xq, xs, rs, args, M, K, stream, name, query);
     return hipErrorNotSupported;
+}
+
+// One dense projection at 9-64 tokens with K too deep for one workgroup's
+// staging (49 to 384 chunks of 64) and 1024 to 4096 weight rows (2560 past
+// 32 tokens): K split into ceil(C / 48) parts over the workgroups, int32
+// partials in the caller's workspace (parts x M x N), then one elementwise
+// pass.  Measured on MI355X against the few-token GEMM with K split (us):
+// 2560 x 6912 at 16 tokens 11.9 -> 7.8, at 32 12.5 -> 9.5, at 64 15.7 ->
+// 11.6; 2048 x 11008 at 9 tokens 11.3 -> 7.9, at 32 11.3 -> 10.1, at 64
+// 12.4 -> 12.2; 4096 x 11008 at 16 tokens 15.8 -> 10.8 (at 64: 18.8
+// against 20.5, hence the narrower row range there).  The forward tries the
+// staged skinny kernel first (1024 x 4096 at 16-64 tokens: 4.5 us there).
+// hipErrorNotSupported (nothing launched) for every other shape.
+hipError_t launch_skinny_direct_tiles_split(const int8_t *Xq, const float *xs, const int32_t *rs,
+                                            const uint8_t *packed, const float *w_scale, Pattern p, int64_t M,
+                                            int64_t N, int64_t K, float *Y, int32_t *acc, Scratch &scratch,
+                                            hipStream_t stream, const char **name)
+{
+    const int64_t C = K / 64;
+    if (p != Pattern::Dense || M < 9 || M > 64 || C <= 48 || C > 384 || N < 1024 || N > (M <= 32 ? 4096 : 2560))
+        return hipErrorNotSupported;
+    const int parts = (int)((C + 47) / 48);
+    if (M <= 32)
+        return launch_split<1, 2, 3>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, parts, scratch, stream, name);
+    return launch_split<2, 4, 3>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, parts, scratch, stream, name);
 }
 
 }  // namespace bl

@@ -109,14 +109,19 @@ def skinny_direct(M, K, rows, nproj=1, nm=(0, 0)):
 
 def direct_tiles(M, K, rows, nm=(0, 0)):
     """Dense weights at 9-64 tokens over at least 6912 weight rows (all
-    projections of a call together), K of 4 to 48 chunks of 64: the direct-load
-    kernel with several 16-token tiles per workgroup.  Its dispatch name
-    (without the "_grouped" of a grouped call), or None."""
+    projections of a call together), or 2560 from 17 tokens, K of 4 to 48
+    chunks of 64: the direct-load kernel with several 16-token tiles per
+    workgroup.  Its dispatch name (without the "_grouped" of a grouped call),
+    or None."""
     C = K // 64
-    if nm != (0, 0) or not (9 <= M <= 64) or not (4 <= C <= 48) or rows < 6912:
+    if nm != (0, 0) or not (9 <= M <= 64) or not (4 <= C <= 48) or rows < 2560:
         return None
     s = 2 if C <= 32 else 3
-    if M <= 16:
+    if rows < 6912:
+        if M < 17:
+            return None
+        tt, rg = 1, 2
+    elif M <= 16:
         tt, rg = 1, 2
     elif M <= 32:
         tt, rg = (1, 4) if rows >= 13824 else (1, 2)
@@ -127,3 +132,15 @@ def direct_tiles(M, K, rows, nm=(0, 0)):
     else:
         return None
     return "skinny_direct_tiles_dense_t%d_rg%d_s%d" % (tt, rg, s)
+
+
+def direct_tiles_split(M, K, N, nm=(0, 0)):
+    """One dense projection at 9-64 tokens with K of 49 to 384 chunks of 64 and
+    1024 to 4096 weight rows (2560 past 32 tokens): the token-tile kernel with
+    K split into ceil(C / 48) parts over the workgroups, where the staged
+    skinny kernel does not take the shape first.  Its dispatch name, or None."""
+    C = K // 64
+    if nm != (0, 0) or not (9 <= M <= 64) or not (48 < C <= 384) or not (1024 <= N <= (4096 if M <= 32 else 2560)):
+        return None
+    tt, rg = (1, 2) if M <= 32 else (2, 4)
+    return "skinny_direct_tiles_dense_t%d_rg%d_s3_splitk%d" % (tt, rg, -(-C // 48))

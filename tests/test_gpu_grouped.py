@@ -79,16 +79,19 @@ def test_block_3b_gate_up_grouped(M):
 
 @pytest.mark.parametrize("M,nm", [(40, (0, 0)), (64, (0, 0)), (64, (2, 4)), (64, (6, 8))])
 def test_block_3b_qkv_grouped_many_workgroups(M, nm):
-    # q, k, v of the 3B block past 16 tokens: 160 rows of 16 in 3 or 4 token
-    # tiles, 480 or 640 workgroups (a grouped call of several projections
-    # takes up to 1024)
+    # q, k, v of the 3B block past 16 tokens (2560 rows in all): dense on the
+    # direct-load token-tile kernel; N:M on the skinny kernel's 160 rows of 16
+    # in 3 or 4 token tiles, 480 or 640 workgroups (a grouped call of several
+    # projections takes up to 1024)
     d = workloads.draw("block_3b", projs=["q", "k", "v"], Ms=(64,))
     Ws = [d.W["q"], d.W["k"], d.W["v"]]
     X = d.X[("q", 64)][:M]
     print("case grouped block_3b q+k+v M=%d nm=%s" % (M, nm), flush=True)
     packs, xq, Ys, accs, name = run_grouped(Ws, X, nm)
-    family = "skinny_direct_dense_" if nm == (0, 0) else "skinny_mfma"
-    assert name.startswith(family) and name.endswith("_grouped"), name
+    if nm == (0, 0):
+        assert name == direct_tiles(M, 2048, 2560) + "_grouped", name
+    else:
+        assert name.startswith("skinny_mfma") and name.endswith("_grouped"), name
     check(Ws, X, nm, packs, xq, Ys, accs)
 
 

@@ -10,7 +10,7 @@ import pytest
 
 from ternary_weight_linear_act_amd import workloads
 
-from gpu_helpers import cover_rows, direct_tiles, full_check, hip_forward, hip_pack, hip_quant, skinny_direct, to_dev
+from gpu_helpers import cover_rows, direct_tiles, direct_tiles_split, full_check, hip_forward, hip_pack, hip_quant, skinny_direct, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -326,8 +326,8 @@ def test_gemv_fallback_very_deep_k(M, nm):
     assert bl.last_dispatch().startswith("gemv_"), bl.last_dispatch()
 
 
-@pytest.mark.parametrize("M,N,K", [(24, 2048, 11008), (17, 8200, 3136), (20, 6900, 1536), (33, 6000, 2048),
-                                   (64, 2100, 2048), (64, 2048, 11008), (40, 9000, 192), (64, 11008, 4096)])
+@pytest.mark.parametrize("M,N,K", [(24, 4200, 11008), (17, 8200, 3136), (20, 4200, 3136), (33, 6000, 3200),
+                                   (64, 2100, 2048), (64, 800, 11008), (40, 9000, 192), (64, 11008, 4096)])
 def test_few_token_gemm(M, N, K):
     # few tokens with many weight rows (or K too deep for the skinny kernel),
     # outside the direct-load token-tile kernel's rules: K split over several
@@ -335,7 +335,7 @@ def test_few_token_gemm(M, N, K):
     # bit-identical
     import torch
     import ternary_weight_linear_act_amd as bl
-    assert direct_tiles(M, K, N) is None
+    assert direct_tiles(M, K, N) is None and direct_tiles_split(M, K, N) is None
     W, X = workloads.small_case(900 + M + K, M, N, K, outlier_frac=0.001)
     out = full_check(W, X, rows=cover_rows(M), label="few-token")
     name = bl.last_dispatch()

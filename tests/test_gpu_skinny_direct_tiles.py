@@ -3,13 +3,16 @@ workgroup (dense weights at 9-64 tokens over at least 6912 weight rows, K of
 4 to 48 chunks of 64): every dispatch rule at its token, row and K edges,
 with ragged weight rows and a ragged last token group, against the CPU oracle
 (acc bit-exact, Y within 1e-5); grouped calls bit-identical to the forward of
-each projection alone; shapes just outside each rule take another kernel."""
+each projection alone; shapes just outside each rule take another kernel.
+The form with K split over the workgroups (one projection, deep K): its K
+range and row range at their edges, int32 partials in the caller's
+workspace."""
 import numpy as np
 import pytest
 
 from ternary_weight_linear_act_amd import workloads
 
-from gpu_helpers import check_y, cover_rows, direct_tiles, full_check, hip_forward, hip_pack, hip_quant
+from gpu_helpers import check_y, cover_rows, direct_tiles, direct_tiles_split, full_check, hip_forward, hip_pack, hip_quant
 
 pytestmark = pytest.mark.gpu
 
@@ -21,6 +24,7 @@ SINGLE = [
     (17, 6912, 2048), (32, 13823, 2560), (20, 9000, 320),                       # 17-32, 6912-13823 rows
     (33, 16384, 256), (64, 16400, 2048), (48, 20000, 1088),                     # 33-64, >= 16384 rows
     (33, 6912, 3072), (64, 13823, 2560), (50, 8000, 512), (64, 11008, 2048),    # 33-64, 6912-13823 rows
+    (17, 2560, 2560), (64, 6911, 3072), (40, 3000, 256), (64, 2560, 2560),      # 17-64, 2560-6911 rows
 ]
 
 
@@ -35,6 +39,7 @@ def test_tiles_single(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,nm", [(8, 8200, 2048, (0, 0)), (9, 6911, 2048, (0, 0)), (16, 8200, 3136, (0, 0)),
+                                      (17, 2559, 2048, (0, 0)), (16, 6000, 2048, (0, 0)),
                                       (33, 13824, 2048, (0, 0)), (33, 16384, 2112, (0, 0)), (65, 16384, 2048, (0, 0)),
                                       (24, 8200, 192, (0, 0)), (16, 8200, 2048, (2, 4)), (40, 8200, 2048, (6, 8))])
 def test_tiles_outside_rules(M, N, K, nm):
@@ -100,3 +105,37 @@ def test_tiles_extreme_accumulators_and_zero_rows(M, N):
     assert not bool(Y[19].any())
     beta = ws.cpu().numpy()[0]
     assert np.all(Y.cpu().numpy()[np.arange(M) != 19] == np.float32(128 * K) * np.float32(beta))
+
+
+# (M, N, K): 50, 108 and 384 chunks (2, 3 and 8 K parts), 1024 to 4096 rows
+# (2560 past 32 tokens), ragged rows, 9 / 32 / 33 / 64 tokens, the 2B and 3B
+# down projections (shapes the staged skinny kernel does not take)
+SPLIT = [(9, 1024, 6912), (32, 1100, 24576), (32, 4096, 6912), (49, 2560, 3200), (33, 2049, 6912), (64, 2048, 11008),
+         (16, 2560, 6912), (64, 2560, 6912), (20, 3000, 8192), (57, 1500, 7040)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLIT)
+def test_tiles_split(M, N, K):
+    import torch
+
+    import ternary_weight_linear_act_amd as bl
+    want = direct_tiles_split(M, K, N)
+    assert want is not None and direct_tiles(M, K, N) is None
+    W, X = workloads.small_case(6500 + M + K + N, M, N, K, outlier_frac=0.001)
+    out = full_check(W, X, (0, 0), rows=cover_rows(M), label="skinny-direct-tiles-split")
+    assert bl.last_dispatch() == want, bl.last_dispatch()
+    # the partials live in the caller's workspace: the size query names it
+    assert bl.forward_workspace_size(M, N, K, (0, 0)) >= int(want.rsplit("splitk", 1)[1]) * M * N * 4
+    Y2, acc2 = hip_forward(out["Xq"], out["xs"], out["rs"], out["packed"], out["ws"], N, (0, 0))
+    torch.cuda.synchronize()
+    assert torch.equal(acc2, out["acc"]) and torch.equal(Y2.view(torch.int32), out["Y"].view(torch.int32))
+
+
+@pytest.mark.parametrize("M,N,K", [(8, 2048, 11008), (65, 2048, 11008), (16, 1023, 6912), (16, 4097, 6912),
+                                   (64, 2048, 3072), (16, 2048, 24640), (33, 2561, 6912)])
+def test_tiles_split_outside_rules(M, N, K):
+    import ternary_weight_linear_act_amd as bl
+    assert direct_tiles_split(M, K, N) is None
+    W, X = workloads.small_case(6600 + M + K + N, M, N, K, outlier_frac=0.001)
+    full_check(W, X, (0, 0), rows=cover_rows(M), label="skinny-direct-tiles-split-outside")
+    assert not bl.last_dispatch().startswith("skinny_direct_tiles"), bl.last_dispatch()
