@@ -256,10 +256,10 @@ bitlinear_status bitlinear_forward_fused(const float *X, int64_t M, int64_t K, b
  * 17 <= M <= 64 while the 16-token tiles times the 16-row weight blocks of
  * all projections make at most 1024 workgroups (512 for one projection), and
  * K within the kernels' range.  Dense weights (nm = {0, 0}) with
- * 256 <= K <= 3072 over at least 6912 rows in all at 9-64 tokens, or 2560 at
- * 17-64 tokens, run on the direct-load kernel with several token tiles per
- * workgroup (at 33-64 tokens: fewer than 13824 rows, or at least 16384 with
- * K <= 2048).  Past those, at
+ * 256 <= K <= 3072 over at least 6912 rows in all at 9-64 tokens, 2560 at
+ * 17-64 tokens or 2048 at 33-64 tokens, run on the direct-load kernel with
+ * several token tiles per workgroup (at 33-64 tokens: fewer than 13824 rows,
+ * or at least 16384 with K <= 2048).  Past those, at
  * 17-64 tokens, dense weights and two or more projections, each with
  * K <= 4096 or N >= 8192 and at least 256 output tiles of 32 x 32, run as one
  * grouped launch of the few-token GEMM.  Anything else returns

@@ -55,7 +55,7 @@ hipError_t launch_skinny_direct(const int8_t *Xq, const float *xs, const int32_t
 
 // The direct-load skinny MFMA forward with several 16-token tiles per
 // workgroup (dense weights at 9-64 tokens over at least 6912 weight rows, or
-// 2560 from 17 tokens: the shapes where it measured faster);
+// 2560 from 17 tokens, 2048 from 33: the shapes where it measured faster);
 // hipErrorNotSupported for every other shape.
 hipError_t launch_skinny_direct_tiles(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
                                Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query);

@@ -40,6 +40,8 @@
 //     10.1 -> 6.0, at 17 6.7 -> 4.9; 3072 x 3072 at 48 tokens 10.6 -> 5.9;
 //     5120 rows (K 2048) at 32 tokens 9.4 -> 5.2; q, k, v of a 3B block
 //     (2560 rows in all) at 64 tokens 5.4 -> 5.0
+//   33-64 tokens, 2048-2559 rows (TT 1, RG 2): 2048 x 2048 at 64 tokens
+//     4.6 -> 4.3 (at 17-32 tokens the staged kernel is as fast)
 // Non-temporal stores of Y: the outputs leave in one burst at the end.
 #include <stdio.h>
 
@@ -351,9 +353,9 @@ hipError_t launch_skinny_direct_tiles(const int8_t *Xq, const float *xs, const i
     int64_t rows = 0;
     for (int i = 0; i < args.nproj; ++i) rows += args.N[i];
     const int64_t C = K / 64;
-    if (M < 9 || M > 64 || C < skinny_direct_tiles::KS || C > 48 || rows < 2560) return hipErrorNotSupported;
+    if (M < 9 || M > 64 || C < skinny_direct_tiles::KS || C > 48 || rows < 2048) return hipErrorNotSupported;
     if (rows < 6912) {
-        if (M >= 17) return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+        if (M >= (rows < 2560 ? 33 : 17)) return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
         return hipErrorNotSupported;
     }
     if (M <= 16) return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);

@@ -109,16 +109,16 @@ def skinny_direct(M, K, rows, nproj=1, nm=(0, 0)):
 
 def direct_tiles(M, K, rows, nm=(0, 0)):
     """Dense weights at 9-64 tokens over at least 6912 weight rows (all
-    projections of a call together), or 2560 from 17 tokens, K of 4 to 48
+    projections of a call together), 2560 from 17 tokens or 2048 from 33, K of 4 to 48
     chunks of 64: the direct-load kernel with several 16-token tiles per
     workgroup.  Its dispatch name (without the "_grouped" of a grouped call),
     or None."""
     C = K // 64
-    if nm != (0, 0) or not (9 <= M <= 64) or not (4 <= C <= 48) or rows < 2560:
+    if nm != (0, 0) or not (9 <= M <= 64) or not (4 <= C <= 48) or rows < 2048:
         return None
     s = 2 if C <= 32 else 3
     if rows < 6912:
-        if M < 17:
+        if M < (33 if rows < 2560 else 17):
             return None
         tt, rg = 1, 2
     elif M <= 16:

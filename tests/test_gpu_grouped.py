@@ -102,13 +102,14 @@ def test_grouped_unsupported_raises():
     W, X = workloads.small_case(4500, 64, 11008, 2048)
     pk, ws = hip_pack(W, (0, 0))
     Xq, xs, rs = hip_quant(X)
-    # one projection of 2048 rows: 512 workgroups at 64 tokens are allowed,
-    # 520 (2080 rows) are not for a single projection (and the grouped GEMM
-    # takes two or more)
-    W2, _ = workloads.small_case(4501, 1, 2080, 2048)
+    # one projection of 2080 rows over K = 3136 (49 chunks, past the
+    # token-tile kernel): 520 skinny workgroups at 64 tokens are too many for
+    # a single projection (512), and the grouped GEMM takes two or more
+    W2, X2 = workloads.small_case(4501, 64, 2080, 3136)
     pk2, ws2 = hip_pack(W2, (0, 0))
+    Xq2, xs2, rs2 = hip_quant(X2)
     with pytest.raises(bl.BitLinearError, match="EUNSUPPORTED"):
-        bl.forward_grouped(Xq, xs, rs, [(pk2, ws2, 2080)])
+        bl.forward_grouped(Xq2, xs2, rs2, [(pk2, ws2, 2080)])
     # a wide projection beside one of too few GEMM tiles (3000 rows: 188 of
     # 32 x 32 at 64 tokens, below one per compute unit); 14008 rows in all is
     # outside the token-tile kernel's rules at 33-64 tokens

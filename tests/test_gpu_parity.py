@@ -327,7 +327,7 @@ def test_gemv_fallback_very_deep_k(M, nm):
 
 
 @pytest.mark.parametrize("M,N,K", [(24, 4200, 11008), (17, 8200, 3136), (20, 4200, 3136), (33, 6000, 3200),
-                                   (64, 2100, 2048), (64, 800, 11008), (40, 9000, 192), (64, 11008, 4096)])
+                                   (64, 2600, 3136), (64, 800, 11008), (40, 9000, 192), (64, 11008, 4096)])
 def test_few_token_gemm(M, N, K):
     # few tokens with many weight rows (or K too deep for the skinny kernel),
     # outside the direct-load token-tile kernel's rules: K split over several
@@ -352,14 +352,14 @@ def skinny_tiles(M, N):
     return M <= 16 or (M <= 64 and -(-N // 16) * -(-M // 16) <= 512)
 
 
-@pytest.mark.parametrize("M,N,K", [(17, 300, 2048), (33, 2048, 2048), (64, 256, 2048), (40, 1000, 192),
-                                   (64, 2048, 2048), (50, 97, 4096)])
+@pytest.mark.parametrize("M,N,K", [(17, 300, 2048), (33, 2040, 2048), (64, 256, 2048), (40, 1000, 192),
+                                   (64, 2040, 2048), (50, 97, 4096), (32, 2048, 2048)])
 @pytest.mark.parametrize("nm", [(0, 0), (2, 4), (6, 8)])
 def test_skinny_token_tiles(M, N, K, nm):
     # 17-64 tokens with few weight rows: the skinny kernel over tiles of 16
     # tokens along the grid's y (a ragged last tile, ragged weight rows)
     import ternary_weight_linear_act_amd as bl
-    assert skinny_tiles(M, N)
+    assert skinny_tiles(M, N) and direct_tiles(M, K, N, nm) is None
     W, X = workloads.small_case(2500 + M + K, M, N, K, outlier_frac=0.001)
     full_check(W, X, nm, rows=cover_rows(M), label="skinny-tiles")
     name = bl.last_dispatch()

@@ -25,6 +25,7 @@ SINGLE = [
     (33, 16384, 256), (64, 16400, 2048), (48, 20000, 1088),                     # 33-64, >= 16384 rows
     (33, 6912, 3072), (64, 13823, 2560), (50, 8000, 512), (64, 11008, 2048),    # 33-64, 6912-13823 rows
     (17, 2560, 2560), (64, 6911, 3072), (40, 3000, 256), (64, 2560, 2560),      # 17-64, 2560-6911 rows
+    (33, 2048, 2048), (64, 2559, 1024), (48, 2100, 3072),                       # 33-64, 2048-2559 rows
 ]
 
 
@@ -39,7 +40,8 @@ def test_tiles_single(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K,nm", [(8, 8200, 2048, (0, 0)), (9, 6911, 2048, (0, 0)), (16, 8200, 3136, (0, 0)),
-                                      (17, 2559, 2048, (0, 0)), (16, 6000, 2048, (0, 0)),
+                                      (17, 2559, 2048, (0, 0)), (16, 6000, 2048, (0, 0)), (32, 2048, 2048, (0, 0)),
+                                      (64, 2047, 2048, (0, 0)),
                                       (33, 13824, 2048, (0, 0)), (33, 16384, 2112, (0, 0)), (65, 16384, 2048, (0, 0)),
                                       (24, 8200, 192, (0, 0)), (16, 8200, 2048, (2, 4)), (40, 8200, 2048, (6, 8))])
 def test_tiles_outside_rules(M, N, K, nm):
@@ -138,4 +140,6 @@ def test_tiles_split_outside_rules(M, N, K):
     assert direct_tiles_split(M, K, N) is None
     W, X = workloads.small_case(6600 + M + K + N, M, N, K, outlier_frac=0.001)
     full_check(W, X, (0, 0), rows=cover_rows(M), label="skinny-direct-tiles-split-outside")
-    assert not bl.last_dispatch().startswith("skinny_direct_tiles"), bl.last_dispatch()
+    name = bl.last_dispatch()
+    assert "splitk" not in name or not name.startswith("skinny_direct_tiles"), name
+    assert direct_tiles(M, K, N) is None or name == direct_tiles(M, K, N), name
