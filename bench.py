@@ -245,13 +245,22 @@ def gemm_counters_summary(pmc_dir, probe_out, out_md, command):
         f.write("\n".join(md) + "\n")
 
 
+def _repo_path(path):
+    """`path` as $R/... when it lies in this repository (the root it is run
+    from may be reached through a link), else unchanged."""
+    root = os.path.realpath(os.path.dirname(os.path.abspath(__file__)))
+    real = os.path.realpath(path)
+    return "$R" + real[len(root):] if real == root or real.startswith(root + os.sep) else path
+
+
 def stats_summary(trace_dir, out_md, title, command):
     """A Markdown table of rocprofv3's kernel statistics (`--stats`, CSV) for
     the kernels of this library, with the command that made them."""
     rows = _csv_rows(trace_dir, "kernel_stats.csv")
     md = ["# " + title, "", "Command (run from /tmp with TMPDIR=/tmp, repository at $R), then the summary:", "",
           "    " + command,
-          "    python3 $R/bench.py --stats-summary %s %s '%s' '%s'" % (trace_dir, out_md, title, command), "",
+          "    python3 $R/bench.py --stats-summary %s %s '%s' '%s'" % (_repo_path(trace_dir), _repo_path(out_md), title,
+                                                                      command), "",
           "Every dispatch of the run (warm-up, eager checks, graph replays); kernel-trace durations time each "
           "dispatch alone.  Kernels of this library (`bl::`) and the vendor GEMM (`Cijk_`):", "",
           "| kernel | calls | avg us | min us | max us |", "|---|---:|---:|---:|---:|"]
@@ -768,6 +777,8 @@ def main():
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run a few eager decode steps and a copy kernel of known size, then exit "
                          "(the command profiled with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--block-probe", type=int, default=0, metavar="M",
+                    help="replay the 3B block at M tokens (grouped form) for a kernel trace, then exit")
     ap.add_argument("--trace-probe", action="store_true",
                     help="replay the decode step's graph over the whole weight pool %d times, then exit "
                          "(the command profiled with rocprofv3 --kernel-trace --stats)" % TRACE_REPLAYS)
@@ -832,6 +843,62 @@ def main():
         print(json.dumps({"gemm_launches": 5, "kernel": bl.last_dispatch(), "M": 2048, "N": 6912, "K": 2560,
                           "source_digest": source_digest()}),
               flush=True)
+        return
+
+    if args.block_probe:
+        # the 3B block at M tokens in the bench's form past 16 tokens, for
+        # rocprofv3 --kernel-trace: one quant_act per input group, then the
+        # grouped forward (or the forward per projection); a graph of P block
+        # steps over a rotating weight pool, replayed TRACE_REPLAYS times
+        M = args.block_probe
+        blk = ("q", "k", "v", "o", "gate", "up", "down")
+        bgroups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+        wlb = workloads.WORKLOADS["block_3b"]
+        db = workloads.draw("block_3b", projs=blk, Ms=(M,))
+        bshapes = {p.name: (p.N, p.K) for p in wlb.projs}
+        bpk, bws = {}, {}
+        for n in blk:
+            bpk[n], bws[n] = bl.pack_weights(torch.from_numpy(db.W[n]).to(dev))
+        PB = max(2, -(-(args.pool_mb << 20) // sum(bpk[n].numel() for n in blk)))
+        bpool = {n: [bpk[n]] + [bpk[n].clone() for _ in range(PB - 1)] for n in blk}
+        bX = {g: torch.from_numpy(db.X[(g[0], M)]).to(dev) for g in bgroups}
+        bXq = {g: torch.empty((M, bshapes[g[0]][1]), dtype=torch.int8, device=dev) for g in bgroups}
+        bxs = {g: torch.empty(M, dtype=torch.float32, device=dev) for g in bgroups}
+        brs = {g: torch.empty(M, dtype=torch.int32, device=dev) for g in bgroups}
+        bY = {n: torch.empty((M, bshapes[n][0]), dtype=torch.float32, device=dev) for n in blk}
+        need = max(bl.forward_workspace_size(M, bshapes[n][0], bshapes[n][1]) for n in blk)
+        bwork = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+        grouped, kernels = {}, {}
+        for g in bgroups:
+            bl.quant_act(bX[g], bXq[g], bxs[g], brs[g])
+            grouped[g] = False
+            if len(g) > 1:
+                try:
+                    bl.forward_grouped(bXq[g], bxs[g], brs[g], [(bpool[n][0], bws[n], bshapes[n][0]) for n in g],
+                                       Ys=[bY[n] for n in g])
+                    grouped[g] = True
+                except bl.BitLinearError:
+                    pass
+            if not grouped[g]:
+                for n in g:
+                    bl.forward(bXq[g], bxs[g], brs[g], bpool[n][0], bws[n], bshapes[n][0], Y=bY[n], workspace=bwork)
+            kernels["+".join(g)] = bl.last_dispatch()
+
+        def block_step(j):
+            for g in bgroups:
+                bl.quant_act(bX[g], bXq[g], bxs[g], brs[g])
+                if grouped[g]:
+                    bl.forward_grouped(bXq[g], bxs[g], brs[g], [(bpool[n][j], bws[n], bshapes[n][0]) for n in g],
+                                       Ys=[bY[n] for n in g])
+                else:
+                    for n in g:
+                        bl.forward(bXq[g], bxs[g], brs[g], bpool[n][j], bws[n], bshapes[n][0], Y=bY[n],
+                                   workspace=bwork)
+        ms, _ = timed_graph(torch, lambda: [block_step(j) for j in range(PB)], reps=TRACE_REPLAYS)
+        log("block probe: %d replays of %d block steps at M=%d, %.3f us per step" % (TRACE_REPLAYS, PB, M,
+                                                                                      ms * 1e3 / PB))
+        print(json.dumps({"block_probe": M, "replays": TRACE_REPLAYS, "steps_per_replay": PB,
+                          "us_per_step_events": round(ms * 1e3 / PB, 4), "kernels": kernels}), flush=True)
         return
 
     # ------------------------------------------------------------------ decode
