@@ -42,7 +42,8 @@
 //     (2560 rows in all) at 64 tokens 5.4 -> 5.0
 //   33-64 tokens, 2048-2559 rows (TT 1, RG 2): 2048 x 2048 at 64 tokens
 //     4.6 -> 4.3 (at 17-32 tokens the staged kernel is as fast)
-// Non-temporal stores of Y: the outputs leave in one burst at the end.
+// Non-temporal stores of Y, whole token rows from an LDS tile: the outputs
+// leave in one burst at the end.
 #include <stdio.h>
 
 #include "kernels.hpp"
@@ -62,8 +63,12 @@ struct Lds {
     static constexpr int kWave = TT * 16 * kRow;
     static constexpr int kAct = KS * kWave;
     static constexpr int kPart = (KS - 1) * TT * RG * 64 * 16;     // [tile][slot][lane] i32x4
-    static constexpr int kBytes = kAct > kPart ? kAct : kPart;
+    static constexpr int kYRow = 16 * RG + 4;                      // staged output row (words, padded)
+    static constexpr int kY = TT * 16 * kYRow * 4;                 // the Y tile, then the acc tile, after
+    static constexpr int kBytes = kAct > kPart + 2 * kY ? kAct : kPart + 2 * kY;   // the partials
 };
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Dense weights.  ty = ceil(M / (16 TT)) token groups (M <= 64) and `parts`
 // K parts (1 unless SPLIT); grid = ceil(blocks / 8) * 8 * ty * parts.  The
@@ -211,7 +216,12 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8
     __syncthreads();
 
     // 6. epilogue: lane (r, q) holds tokens 4 q .. 4 q + 3 of the token tile,
-    //    weight row 16 g + r
+    //    weight row 16 g + r.  Y goes to an LDS tile first and leaves as
+    //    whole token rows of 16 RG outputs (16-byte non-temporal stores where
+    //    N and Y allow): the fragment layout would write 64-byte pieces of
+    //    four rows per instruction (3B gate + up at 64 tokens 11.3 -> 10.5 us).
+    float *yt = reinterpret_cast<float *>(s_x + L::kPart);
+    int32_t *at = reinterpret_cast<int32_t *>(s_x + L::kPart + L::kY);
 #pragma unroll
     for (int tt = 0; tt < TT; ++tt)
 #pragma unroll
@@ -222,6 +232,20 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8
 #pragma unroll
             for (int sl = 0; sl < KS - 1; ++sl) sum += part[(j * (KS - 1) + sl) * 64 + lane];
             const int64_t n = n0 + 16 * g + r;
+            if constexpr (!SPLIT) {
+                int av[4];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    const int m = 16 * tt + 4 * q + v;
+                    av[v] = sum[v] - s_rs[m];
+                    yt[m * L::kYRow + 16 * g + r] = (float)av[v] * (beta * s_xs[m]);
+                }
+                if (acc_out) {
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) at[(16 * tt + 4 * q + v) * L::kYRow + 16 * g + r] = av[v];
+                }
+                continue;
+            }
             if (n >= N) continue;
             if constexpr (SPLIT) {
                 int32_t *wp = ws + ((int64_t)kp * M + t0) * N + n;
@@ -232,16 +256,35 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8
                 }
                 continue;
             }
+        }
+    if constexpr (!SPLIT) {
+        __syncthreads();
+        constexpr int W4 = 4 * RG;                                 // 16-byte pieces per token row
+        const int ncols = (int)min((int64_t)(16 * RG), N - n0);
+        const int mrows = (int)min(mg, (int64_t)(TT * 16));
+        const bool vec = (N % 4 == 0) && (reinterpret_cast<uintptr_t>(Y) % 16 == 0);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = 16 * tt + 4 * q + v;
-                if (m < mg) {
-                    const int av = sum[v] - s_rs[m];
-                    __builtin_nontemporal_store((float)av * (beta * s_xs[m]), &Y[(int64_t)m * N + n]);
-                    if (acc_out) acc_out[(int64_t)m * N + n] = av;
-                }
+        for (int i0 = 0; i0 < TT * 16 * W4; i0 += 64 * KS) {
+            const int i = i0 + threadIdx.x;
+            const int m = i / W4, c = 4 * (i % W4);
+            if (i >= TT * 16 * W4 || m >= mrows) continue;
+            const float *src = yt + m * L::kYRow + c;
+            float *dst = Y + (int64_t)m * N + n0 + c;
+            if (vec && c + 4 <= ncols) {
+                __builtin_nontemporal_store(*reinterpret_cast<const f32x4 *>(src), reinterpret_cast<f32x4 *>(dst));
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (c + e < ncols) __builtin_nontemporal_store(src[e], dst + e);
             }
         }
+        if (acc_out) {
+            for (int i = threadIdx.x; i < mrows * 16 * RG; i += 64 * KS) {
+                const int m = i / (16 * RG), c = i % (16 * RG);
+                if (c < ncols) acc_out[(int64_t)m * N + n0 + c] = at[m * L::kYRow + c];
+            }
+        }
+    }
 }
 
 // Sum of the K parts' int32 partials (integer sums: exact in any order),
