@@ -344,6 +344,61 @@ def traffic_summary(fetch_dir, write_dir, probe_out):
     print(json.dumps(out))
 
 
+def block_traffic_summary(fetch_dir, write_dir, probe_out, out_md, commands):
+    """HBM bytes per dispatch of each step position of `bench.py
+    --block-traffic-probe`, from a `--pmc FETCH_SIZE` and a `--pmc WRITE_SIZE`
+    run of it: the probe's eager steps are the last steps x positions
+    dispatches of this library before the calibration copy; each counter is
+    scaled by its reading for that copy (copy_bytes read and written once).
+    `commands`: the two rocprofv3 commands, separated by ' ;; '."""
+    import numpy as np
+    probe = _probe_json(probe_out)
+    pos, steps, copy_bytes = probe["positions"], probe["steps"], probe["copy_bytes"]
+
+    def dispatches(dirpath, counter):
+        rows = [r for r in _csv_rows(dirpath, "counter_collection.csv") if r.get("Counter_Name") == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        copies = [float(r["Counter_Value"]) * 1024.0 for r in rows if "copyBuffer" in _kernel_name(r)]
+        ours = [(_symbol(_kernel_name(r)), float(r["Counter_Value"]) * 1024.0) for r in rows
+                if _kernel_name(r).startswith(("bl::", "void bl::"))]
+        need = steps * len(pos)
+        if not copies or len(ours) < need:
+            raise SystemExit("%s: %d dispatches of this library, %d wanted; %d calibration copies" % (
+                counter, len(ours), need, len(copies)))
+        return max(copies), ours[-need:]
+
+    cf, fetch = dispatches(fetch_dir, "FETCH_SIZE")
+    cw, write = dispatches(write_dir, "WRITE_SIZE")
+    fs, ws = copy_bytes / cf, copy_bytes / cw
+    rows = []
+    for i, p in enumerate(pos):
+        fsym = {fetch[j][0] for j in range(i, len(fetch), len(pos))}
+        wsym = {write[j][0] for j in range(i, len(write), len(pos))}
+        if len(fsym) != 1 or fsym != wsym:
+            raise SystemExit("position %d: kernels %s / %s" % (i, sorted(fsym), sorted(wsym)))
+        fb = float(np.mean([fetch[j][1] for j in range(i, len(fetch), len(pos))])) * fs
+        wb = float(np.mean([write[j][1] for j in range(i, len(write), len(pos))])) * ws
+        rows.append((p["group"], p["role"], fsym.pop(), fb, wb, p["bytes"]))
+    md = ["# HBM traffic per dispatch, 3B block at %d tokens (grouped form)" % probe["block_traffic_probe"], "",
+          "Commands (run from /tmp with TMPDIR=/tmp, repository at $R), then the summary:", ""] + \
+         ["    " + c.strip() for c in commands.split(" ;; ")] + \
+         ["    python3 $R/bench.py --block-traffic-summary %s %s %s %s '%s'" % (
+             _repo_path(fetch_dir), _repo_path(write_dir), _repo_path(probe_out), _repo_path(out_md), commands), "",
+          "Calibration: the probe's device copy of %d bytes reads FETCH_SIZE scale %.4f and WRITE_SIZE scale %.4f "
+          "(bytes per counted byte).  Averages over %d eager steps; the weights rotate through a pool larger "
+          "than the caches, the activations do not." % (copy_bytes, fs, ws, steps), "",
+          "| group | dispatch | kernel | HBM read B | HBM write B | algorithmic B | HBM / algorithmic |",
+          "|---|---|---|---:|---:|---:|---:|"]
+    for g, role, sym, fb, wb, ab in rows:
+        md.append("| %s | %s | `%s` | %d | %d | %d | %.3f |" % (g, role, sym, fb, wb, ab, (fb + wb) / ab))
+    md += ["", "Algorithmic bytes: quant_act 5 M K + 8 M (fp32 in, int8 out, scale and row sum); a forward the "
+               "packed weights, the int8 activations, scales and row sums, beta and the fp32 output; with K split, "
+               "the int32 partials in the workspace are counted where they are written and read."]
+    with open(out_md, "w") as f:
+        f.write("\n".join(md) + "\n")
+    print("\n".join(md))
+
+
 def fwd_bytes(M, N, K, nm=(0, 0)):
     """Algorithmic bytes of one forward launch: packed weights, int8 activations,
     x_scale + row sums, beta, fp32 output."""
@@ -779,6 +834,11 @@ def main():
                          "(the command profiled with rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)")
     ap.add_argument("--block-probe", type=int, default=0, metavar="M",
                     help="replay the 3B block at M tokens (grouped form) for a kernel trace, then exit")
+    ap.add_argument("--block-traffic-probe", type=int, default=0, metavar="M",
+                    help="eager steps of the 3B block at M tokens, then a calibration copy, for --pmc runs")
+    ap.add_argument("--block-traffic-summary", nargs=5, metavar=("FETCH_DIR", "WRITE_DIR", "PROBE_OUT", "OUT_MD",
+                                                                   "COMMANDS"),
+                    help="summarise two --pmc runs of --block-traffic-probe into OUT_MD (no GPU)")
     ap.add_argument("--trace-probe", action="store_true",
                     help="replay the decode step's graph over the whole weight pool %d times, then exit "
                          "(the command profiled with rocprofv3 --kernel-trace --stats)" % TRACE_REPLAYS)
@@ -814,6 +874,9 @@ def main():
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
         return
+    if args.block_traffic_summary:
+        block_traffic_summary(*args.block_traffic_summary)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
@@ -845,12 +908,14 @@ def main():
               flush=True)
         return
 
-    if args.block_probe:
-        # the 3B block at M tokens in the bench's form past 16 tokens, for
-        # rocprofv3 --kernel-trace: one quant_act per input group, then the
-        # grouped forward (or the forward per projection); a graph of P block
-        # steps over a rotating weight pool, replayed TRACE_REPLAYS times
-        M = args.block_probe
+    if args.block_probe or args.block_traffic_probe:
+        # the 3B block at M tokens in the bench's form past 16 tokens: one
+        # quant_act per input group, then the grouped forward (or the forward
+        # per projection).  --block-probe (for rocprofv3 --kernel-trace): a
+        # graph of P block steps over a rotating weight pool, replayed
+        # TRACE_REPLAYS times.  --block-traffic-probe (for --pmc FETCH_SIZE /
+        # WRITE_SIZE): 2 P eager steps, then a device copy of known size
+        M = args.block_probe or args.block_traffic_probe
         blk = ("q", "k", "v", "o", "gate", "up", "down")
         bgroups = [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
         wlb = workloads.WORKLOADS["block_3b"]
@@ -894,6 +959,41 @@ def main():
                     for n in g:
                         bl.forward(bXq[g], bxs[g], brs[g], bpool[n][j], bws[n], bshapes[n][0], Y=bY[n],
                                    workspace=bwork)
+        if args.block_traffic_probe:
+            # each step's dispatches in order, with their algorithmic bytes
+            positions = []
+            for g in bgroups:
+                K = bshapes[g[0]][1]
+                positions.append({"group": "+".join(g), "role": "quant_act", "bytes": quant_bytes(M, K)})
+                name = kernels["+".join(g)]
+                if "splitk" in name:
+                    n = g[0]
+                    N = bshapes[n][0]
+                    parts = int(name.rsplit("splitk", 1)[1])
+                    positions.append({"group": "+".join(g), "role": "forward, K parts (partials to the workspace)",
+                                      "bytes": N * K // 4 + 4 + M * K + 8 * M + 4 * parts * M * N})
+                    positions.append({"group": "+".join(g), "role": "forward, sum of the parts and epilogue",
+                                      "bytes": 4 * parts * M * N + 8 * M + 4 + 4 * M * N})
+                elif grouped[g]:
+                    nb = sum(bshapes[n][0] * K // 4 + 4 + 4 * M * bshapes[n][0] for n in g) + M * K + 8 * M
+                    positions.append({"group": "+".join(g), "role": "forward", "bytes": nb})
+                else:
+                    for n in g:
+                        positions.append({"group": "+".join(g), "role": "forward (%s)" % n,
+                                          "bytes": fwd_bytes(M, bshapes[n][0], K)})
+            for j in range(2 * PB):
+                block_step(j % PB)
+            copy_bytes = 256 << 20
+            src = torch.full((copy_bytes,), 7, dtype=torch.uint8, device=dev)
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            log("block traffic probe: %d eager block steps at M=%d, then a %d-byte device copy" % (2 * PB, M,
+                                                                                                 copy_bytes))
+            print(json.dumps({"block_traffic_probe": M, "steps": 2 * PB, "positions": positions,
+                              "copy_bytes": copy_bytes, "kernels": kernels}), flush=True)
+            return
         ms, _ = timed_graph(torch, lambda: [block_step(j) for j in range(PB)], reps=TRACE_REPLAYS)
         log("block probe: %d replays of %d block steps at M=%d, %.3f us per step" % (TRACE_REPLAYS, PB, M,
                                                                                       ms * 1e3 / PB))

@@ -183,3 +183,53 @@ def test_digest_ignores_comments(bench):
     b = "int f(int x) {\n    return x + 1;\n}\n"
     c = "int f(int x) { return x + 2; }"
     assert bench._code_only(a) == bench._code_only(b) != bench._code_only(c)
+
+
+def test_block_traffic_summary(bench, tmp_path):
+    # two steps of three positions (a quant and two forwards, one of them the
+    # same kernel as another position), after a pack dispatch of this library;
+    # FETCH_SIZE counts half the bytes (scale 2), WRITE_SIZE all of them
+    hdr = ["Correlation_Id", "Dispatch_Id", "Agent_Id", "Queue_Id", "Process_Id", "Thread_Id", "Grid_Size",
+           "Kernel_Id", "Kernel_Name", "Workgroup_Size", "LDS_Block_Size", "Scratch_Size", "VGPR_Count",
+           "Accum_VGPR_Count", "SGPR_Count", "Counter_Name", "Counter_Value", "Start_Timestamp", "End_Timestamp"]
+    copy_bytes = 1 << 28
+    Q = "void bl::(anonymous namespace)::quant_act_reg_kernel<256, 2>(float const*, long)"
+    T = "void bl::skinny_direct_tiles::skinny_direct_tiles_kernel<1, 2, 2, false>(signed char const*, long)"
+    seq = [("bl::(anonymous namespace)::pack_dense_kernel(float const*)", 1.0)] + \
+        [(Q, 10.0), (T, 100.0), (T, 300.0)] * 2
+
+    def rows(counter, copy_kib):
+        out = []
+        for i, (name, v) in enumerate(seq + [("__amd_rocclr_copyBuffer", copy_kib)]):
+            out.append([i, i + 1, "Agent 1", 1, 1, 1, 64, 1, name, 256, 0, 0, 8, 0, 16, counter, v, 0, 1])
+        return out[::-1]                                   # the summary orders by dispatch id
+    write_csv(str(tmp_path / "f" / "p_counter_collection.csv"), hdr, rows("FETCH_SIZE", copy_bytes / 1024 / 2))
+    write_csv(str(tmp_path / "w" / "p_counter_collection.csv"), hdr, rows("WRITE_SIZE", copy_bytes / 1024))
+    probe = tmp_path / "probe.out"
+    pos = [{"group": "a", "role": "quant_act", "bytes": 40960}, {"group": "a", "role": "forward", "bytes": 409600},
+           {"group": "b", "role": "forward", "bytes": 1 << 20}]
+    probe.write_text(json.dumps({"block_traffic_probe": 64, "steps": 2, "positions": pos, "copy_bytes": copy_bytes,
+                                 "kernels": {}}) + "\n")
+    out = tmp_path / "t.md"
+    bench.block_traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(probe), str(out), "c1 ;; c2")
+    md = out.read_text()
+    assert "scale 2.0000 and WRITE_SIZE scale 1.0000" in md
+    assert "| a | quant_act | `void bl::(anonymous namespace)::quant_act_reg_kernel<256, 2>` | 20480 | 10240 | " \
+           "40960 | 0.750 |" in md
+    assert "| b | forward | `void bl::skinny_direct_tiles::skinny_direct_tiles_kernel<1, 2, 2, false>` | 614400 | " \
+           "307200 | 1048576 | 0.879 |" in md
+    assert "    c1\n    c2\n" in md
+
+
+def test_block_traffic_summary_refuses_short_runs(bench, tmp_path):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    write_csv(str(tmp_path / "f" / "p_counter_collection.csv"), hdr,
+              [[1, "void bl::x<1>(int)", "FETCH_SIZE", 1.0], [2, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 4.0]])
+    write_csv(str(tmp_path / "w" / "p_counter_collection.csv"), hdr,
+              [[1, "void bl::x<1>(int)", "WRITE_SIZE", 1.0], [2, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 4.0]])
+    probe = tmp_path / "probe.out"
+    probe.write_text(json.dumps({"block_traffic_probe": 8, "steps": 2, "positions": [{"group": "a", "role": "r",
+                                                                                       "bytes": 1}],
+                                 "copy_bytes": 4096, "kernels": {}}) + "\n")
+    with pytest.raises(SystemExit):
+        bench.block_traffic_summary(str(tmp_path / "f"), str(tmp_path / "w"), str(probe), str(tmp_path / "o.md"), "c")
