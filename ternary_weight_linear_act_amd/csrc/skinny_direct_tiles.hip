@@ -21,7 +21,10 @@
 // tile meet in LDS, in the activation area, at the tile's owner wave, which
 // applies the offset-code correction and the dequant scale.  Token groups
 // (16 * TT tokens each) of one row block run on one XCD (workgroup ids 8
-// apart), so the second group's weight reads hit that XCD's L2.
+// apart), so a later group's weight reads can hit that XCD's L2.  Counted
+// HBM traffic at 64 tokens: 1.07x the algorithmic bytes with two groups
+// (gate + up of a 3B block), 1.5-1.6x with four, where the non-temporal
+// weight loads leave little in L2 (cached loads measured slower all the same).
 //
 // Where it is used (dense weights; a call's projections together; measured
 // on MI355X against the library's previous kernel for the shape, us):
