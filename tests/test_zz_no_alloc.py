@@ -38,6 +38,7 @@ def run_pair(M, N, K, nm, seed):
     ((512, 8960, 1536, (6, 8)), (100, 2000, 1536, (6, 8))),     # N:M rows expanded in the scratch
     ((40, 4096, 8192, (0, 0)), (20, 4096, 6912, (0, 0))),       # K split, partial tiles in the scratch
     ((32, 2560, 6912, (2, 4)), (17, 8300, 512, (2, 4))),        # N:M t-byte GEMM with K split
+    ((64, 2560, 6912, (0, 0)), (16, 2048, 11008, (0, 0))),      # token-tile kernel, K parts in the scratch
 ])
 def test_noalloc_matches_forward_twice(first, second):
     # the second call is the smaller problem (its scratch use may differ: a
