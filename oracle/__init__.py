@@ -16,6 +16,10 @@ from .oracle import (  # noqa: F401
     packed_bytes,
     pack_dense,
     pack_nm,
+    packed_bytes_trit24,
+    pack_trit24,
+    unpack_trit24,
+    quantize_weights_trit24,
     quantize_weights,
     quant_act,
     quant_act_ex,

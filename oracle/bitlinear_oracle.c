@@ -231,6 +231,77 @@ int oracle_pack_nm(const int8_t *t, const uint8_t *keep, int64_t N, int64_t K,
 }
 
 /* ------------------------------------------------------------------------ */
+/* 2:4 trit pack: the 2:4 weights in 6 bits per group of 4 ([SPARSE] sec.  */
+/* 3.2 keeps 2 of every 4; [SURV] section "I2_S 커널의 내부 동작": TL2      */
+/* indexes a pair of ternary weights by its 3 x 3 = 9 combinations).  A    */
+/* group keeps exactly two inputs i0 < i1; its code is                     */
+/*   9 p + 3 (t[i0] + 1) + (t[i1] + 1)   (0 .. 53),                         */
+/* p the index of (i0, i1) in the list (0,1) (0,2) (0,3) (1,2) (1,3) (2,3). */
+/* The 16 groups of 64 consecutive inputs form one 96-bit little-endian    */
+/* string, group g at bits 6 g .. 6 g + 5 (12 bytes); row r holds its      */
+/* K / 64 strings in k order, rows back to back: 3 N K / 16 bytes.         */
+/* ------------------------------------------------------------------------ */
+static const int kPairLo[6] = {0, 0, 0, 1, 1, 2};
+static const int kPairHi[6] = {1, 2, 3, 2, 3, 3};
+
+int64_t oracle_packed_bytes_trit24(int64_t N, int64_t K)
+{
+    if (N < 1 || K < 1 || K % 64) return -1;
+    return N * (3 * K / 16);
+}
+
+int oracle_pack_trit24(const int8_t *t, const uint8_t *keep, int64_t N, int64_t K, uint8_t *out)
+{
+    int64_t total = oracle_packed_bytes_trit24(N, K);
+    if (!t || !keep || !out || total < 0) return OR_EINVAL;
+    memset(out, 0, (size_t)total);
+    for (int64_t r = 0; r < N; ++r) {
+        uint8_t *row = out + r * (3 * K / 16);
+        for (int64_t g = 0; g < K / 4; ++g) {
+            int kept[4], nk = 0;
+            for (int i = 0; i < 4; ++i)
+                if (keep[r * K + 4 * g + i]) {
+                    if (nk == 2) return OR_EINVAL;
+                    kept[nk++] = i;
+                }
+            if (nk != 2) return OR_EINVAL;
+            int p = -1;
+            for (int j = 0; j < 6; ++j)
+                if (kPairLo[j] == kept[0] && kPairHi[j] == kept[1]) p = j;
+            int v0 = t[r * K + 4 * g + kept[0]], v1 = t[r * K + 4 * g + kept[1]];
+            if (p < 0 || v0 < -1 || v0 > 1 || v1 < -1 || v1 > 1) return OR_EINVAL;
+            unsigned code = (unsigned)(9 * p + 3 * (v0 + 1) + (v1 + 1));
+            /* group g of string s = g / 16 at bit 6 (g % 16) of that string */
+            int64_t bit = (g / 16) * 96 + 6 * (g % 16);
+            for (int b = 0; b < 6; ++b)
+                if (code & (1u << b)) row[(bit + b) / 8] |= (uint8_t)(1u << ((bit + b) % 8));
+        }
+    }
+    return OR_OK;
+}
+
+/* The ternary matrix the trit-packed bytes hold (pruned positions 0). */
+int oracle_unpack_trit24(const uint8_t *packed, int64_t N, int64_t K, int8_t *w_eff)
+{
+    if (!packed || !w_eff || oracle_packed_bytes_trit24(N, K) < 0) return OR_EINVAL;
+    for (int64_t r = 0; r < N; ++r) {
+        const uint8_t *row = packed + r * (3 * K / 16);
+        for (int64_t g = 0; g < K / 4; ++g) {
+            int64_t bit = (g / 16) * 96 + 6 * (g % 16);
+            unsigned code = 0;
+            for (int b = 0; b < 6; ++b)
+                code |= (unsigned)((row[(bit + b) / 8] >> ((bit + b) % 8)) & 1u) << b;
+            if (code > 53) return OR_EINVAL;
+            int p = (int)code / 9, v = (int)code % 9;
+            for (int i = 0; i < 4; ++i) w_eff[r * K + 4 * g + i] = 0;
+            w_eff[r * K + 4 * g + kPairLo[p]] = (int8_t)(v / 3 - 1);
+            w_eff[r * K + 4 * g + kPairHi[p]] = (int8_t)(v % 3 - 1);
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Step 6: per-token absmax int8 activation quantisation ([SURV]            */
 /* activation_quant; [2B4T] sec. 2).  g = max_k |x|; s = fl32(127/g);       */
 /* q = clamp(round(fl32(x*s)), -128, 127); x_scale = fl32(g/127);           */

@@ -58,6 +58,10 @@ def _L():
         lib.oracle_packed_bytes.argtypes = [i64, i64, i32, i32]
         lib.oracle_packed_bytes.restype = i64
         lib.oracle_pack_dense.argtypes = [vp, i64, i64, vp]
+        lib.oracle_packed_bytes_trit24.argtypes = [i64, i64]
+        lib.oracle_packed_bytes_trit24.restype = i64
+        lib.oracle_pack_trit24.argtypes = [vp, vp, i64, i64, vp]
+        lib.oracle_unpack_trit24.argtypes = [vp, i64, i64, vp]
         lib.oracle_pack_nm.argtypes = [vp, vp, i64, i64, i32, i32, vp]
         lib.oracle_quant_act.argtypes = [vp, i64, i64, i32, vp, vp, vp]
         lib.oracle_quant_act_ex.argtypes = [vp, vp, vp, ctypes.c_float, i64, i64, vp, vp, vp]
@@ -135,6 +139,36 @@ def pack_nm(t: np.ndarray, keep: np.ndarray, n: int, m: int) -> np.ndarray:
     out = np.empty(packed_bytes(N, K, n, m), np.uint8)
     _check(_L().oracle_pack_nm(_p(t), _p(keep), N, K, n, m, _p(out)), "pack_nm")
     return out
+
+
+def packed_bytes_trit24(N: int, K: int) -> int:
+    return int(_L().oracle_packed_bytes_trit24(N, K))
+
+
+def pack_trit24(t: np.ndarray, keep: np.ndarray) -> np.ndarray:
+    """2:4 trit pack: one 6-bit code per group of 4 (the pair of kept inputs
+    and their two ternary values), 16 codes per 12 bytes."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    keep = np.ascontiguousarray(keep, dtype=np.uint8)
+    N, K = t.shape
+    out = np.empty(packed_bytes_trit24(N, K), np.uint8)
+    _check(_L().oracle_pack_trit24(_p(t), _p(keep), N, K, _p(out)), "pack_trit24")
+    return out
+
+
+def unpack_trit24(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    out = np.empty((N, K), np.int8)
+    _check(_L().oracle_unpack_trit24(_p(packed), N, K, _p(out)), "unpack_trit24")
+    return out
+
+
+def quantize_weights_trit24(W: np.ndarray):
+    """The 2:4 pack-time path in the trit-packed storage: (beta, w_eff, bytes)."""
+    beta = absmean(W)
+    t = ternarize(W, beta)
+    keep = nm_keep(W, 2, 4)
+    return beta, apply_mask(t, keep), pack_trit24(t, keep)
 
 
 def quantize_weights(W: np.ndarray, n: int = 0, m: int = 0):

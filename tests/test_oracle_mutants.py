@@ -4,7 +4,7 @@ Each case copies oracle/bitlinear_oracle.c, plants one mistake on the CPU
 (a dropped abs, a wrong divisor, truncation instead of round-half-even, a
 missing epsilon, a wrong tie-break, a misplaced bit, a transposed operand, a
 wrong clamp, a wrong activation constant, a slip in the ReLU^2 gate, the
-RMSNorm or the a4.8 outlier split), builds it, and runs the pin suite
+RMSNorm, the a4.8 outlier split or the 2:4 trit code), builds it, and runs the pin suite
 against it: the suite must fail for every mutant.
 """
 import os
@@ -71,6 +71,16 @@ MUTANTS = {
     "a48_lo_scale": ("*x_scale = g / 7.0f;", "*x_scale = g / 8.0f;"),
     "a48_rows_swapped": ("rc = oracle_quant_act(hi, 1, K, 0, q + (2 * r) * K, x_scale + 2 * r, rowsum ? rowsum + 2 * r : NULL);",
                          "rc = oracle_quant_act(hi, 1, K, 0, q + (2 * r + 1) * K, x_scale + 2 * r, rowsum ? rowsum + 2 * r : NULL);"),
+    "trit_pair_order": ("static const int kPairLo[6] = {0, 0, 0, 1, 1, 2};\nstatic const int kPairHi[6] = {1, 2, 3, 2, 3, 3};",
+                        "static const int kPairLo[6] = {0, 0, 1, 0, 1, 2};\nstatic const int kPairHi[6] = {1, 2, 2, 3, 3, 3};"),
+    "trit_value_order": ("unsigned code = (unsigned)(9 * p + 3 * (v0 + 1) + (v1 + 1));",
+                         "unsigned code = (unsigned)(9 * p + (v0 + 1) + 3 * (v1 + 1));"),
+    "trit_bit_stride": ("int64_t bit = (g / 16) * 96 + 6 * (g % 16);\n            for (int b = 0; b < 6; ++b)\n                if (code",
+                        "int64_t bit = (g / 16) * 96 + 6 * (g % 15);\n            for (int b = 0; b < 6; ++b)\n                if (code"),
+    "trit_string_stride": ("int64_t bit = (g / 16) * 96 + 6 * (g % 16);\n            for (int b = 0; b < 6; ++b)\n                if (code",
+                           "int64_t bit = (g / 16) * 90 + 6 * (g % 16);\n            for (int b = 0; b < 6; ++b)\n                if (code"),
+    "trit_unpack_swapped": ("w_eff[r * K + 4 * g + kPairLo[p]] = (int8_t)(v / 3 - 1);\n            w_eff[r * K + 4 * g + kPairHi[p]] = (int8_t)(v % 3 - 1);",
+                            "w_eff[r * K + 4 * g + kPairLo[p]] = (int8_t)(v % 3 - 1);\n            w_eff[r * K + 4 * g + kPairHi[p]] = (int8_t)(v / 3 - 1);"),
     "epilogue_no_beta": ("Y[m * N + n] = (double)s * (double)beta * (double)x_scale[m];",
                          "Y[m * N + n] = (double)s * (double)x_scale[m];"),
 }

@@ -830,3 +830,94 @@ class TestA48:
         assert np.allclose(Y, want, rtol=1e-15, atol=0)
         assert np.array_equal(acc, q.astype(np.int32))
         assert np.all(np.abs(Y - 0.5 * X) <= 0.5 * np.where(sel.astype(bool), xs[0::2][:, None], xs[1::2][:, None]) * 0.5 * (1 + 1e-5))
+
+
+# ---------------------------------------------------------------------------
+# 2:4 trit pack: the 2:4 weights as one 6-bit code per group of 4 (the kept
+# pair of inputs and their two ternary values; TL2's 3 x 3 value index,
+# "I2_S 커널의 내부 동작", times the 6 pairs a 2:4 group can keep), 16 codes
+# in 12 bytes.
+
+TRIT_PAIRS = [(0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3)]
+
+
+def _trit_example():
+    # a hand-worked row of 64 inputs: groups 0, 5, 10 and 15 as listed, the
+    # others keep (0, 1) with values (0, 0); pruned positions hold nonzero t
+    # (the mask drops them)
+    special = {0: ((1, 3), (1, -1)), 5: ((2, 3), (-1, 1)), 10: ((0, 2), (1, 1)), 15: ((0, 3), (-1, 0))}
+    t = np.ones((1, 64), np.int8)
+    keep = np.zeros((1, 64), np.uint8)
+    for g in range(16):
+        (i0, i1), (v0, v1) = special.get(g, ((0, 1), (0, 0)))
+        keep[0, 4 * g + i0] = keep[0, 4 * g + i1] = 1
+        t[0, 4 * g + i0], t[0, 4 * g + i1] = v0, v1
+    return t, keep
+
+
+def test_trit24_hand_example():
+    # codes: group 0 keeps (1, 3) = pair 4 with (+1, -1): 36 + 6 + 0 = 42;
+    # group 5 (2, 3) = pair 5 with (-1, +1): 45 + 0 + 2 = 47; group 10 (0, 2)
+    # = pair 1 with (+1, +1): 9 + 6 + 2 = 17; group 15 (0, 3) = pair 2 with
+    # (-1, 0): 18 + 0 + 1 = 19; the rest (0, 1) = pair 0 with (0, 0): 4.
+    # Bits 6g..6g+5 of a little-endian 96-bit string, worked by hand: byte 0
+    # = 42 = 0x2a; byte 1 = code 1's bits 2-5 (0b0001) + code 2's bits 0-3
+    # (0b0100) << 4 = 0x41; byte 3 = code 4 (4) + code 5's low two bits
+    # (0b11) << 6 = 0xc4, code 5 straddling bytes 3 and 4; byte 4 = code 5's
+    # bits 2-5 (0b1011) + code 6's bits 0-3 << 4 = 0x4b.
+    t, keep = _trit_example()
+    got = oracle.pack_trit24(t, keep)
+    assert got.tobytes().hex() == "2a4110c44b1004111104414c"
+    assert oracle.packed_bytes_trit24(1, 64) == 12
+
+
+def test_trit24_all_codes_brute_force():
+    # every pair and value combination of one group, alone in a row of 64
+    # (the other groups keep (0, 1) with values (0, 0), code 4): the code at
+    # bits 0-5 is 9 p + 3 (v0 + 1) + (v1 + 1), the 54 codes are distinct and
+    # below 64, and the bytes decode back to the masked ternary row
+    seen = set()
+    for p, (i0, i1) in enumerate(TRIT_PAIRS):
+        for v0, v1 in itertools.product((-1, 0, 1), repeat=2):
+            t = np.zeros((1, 64), np.int8)
+            keep = np.zeros((1, 64), np.uint8)
+            keep[0, 0::4] = keep[0, 1::4] = 1
+            keep[0, 0:4] = 0
+            keep[0, i0] = keep[0, i1] = 1
+            t[0, i0], t[0, i1] = v0, v1
+            b = oracle.pack_trit24(t, keep)
+            code = int(b[0]) & 63
+            assert code == 9 * p + 3 * (v0 + 1) + (v1 + 1)
+            seen.add(code)
+            w = oracle.unpack_trit24(b, 1, 64)
+            assert np.array_equal(w, t * keep.astype(np.int8))
+    assert seen == set(range(54))
+
+
+def test_trit24_round_trip_against_the_2_4_path():
+    # quant-then-mask through the trit bytes gives the 2:4 path's W_eff and
+    # beta, at 3/4 of the dense bytes (1.5 bits per weight)
+    for seed, (N, K) in enumerate([(3, 64), (17, 192), (64, 1536)]):
+        W, _ = workloads.small_case(7000 + seed, 1, N, K)
+        beta, w_eff, packed = oracle.quantize_weights_trit24(W)
+        beta2, w_eff2, _ = oracle.quantize_weights(W, 2, 4)
+        assert beta == beta2
+        assert np.array_equal(w_eff, w_eff2)
+        assert packed.size == 3 * N * K // 16 == 3 * oracle.packed_bytes(N, K) // 4
+        assert np.array_equal(oracle.unpack_trit24(packed, N, K), w_eff)
+        # exactly two kept per group, as the format assumes
+        assert np.all((w_eff.reshape(N, K // 4, 4) != 0).sum(axis=2) <= 2)
+
+
+def test_trit24_rejects_groups_not_2_of_4():
+    t = np.zeros((1, 64), np.int8)
+    keep = np.zeros((1, 64), np.uint8)
+    keep[0, 0::2] = 1                       # 2 per group: fine
+    oracle.pack_trit24(t, keep)
+    keep[0, 1] = 1                          # 3 in group 0
+    with pytest.raises(Exception):
+        oracle.pack_trit24(t, keep)
+    keep = np.zeros((1, 64), np.uint8)
+    keep[0, 0::4] = 1                       # 1 per group
+    with pytest.raises(Exception):
+        oracle.pack_trit24(t, keep)
