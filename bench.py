@@ -532,17 +532,22 @@ def cpu_model() -> str:
     return platform.processor() or "unknown"
 
 
-def bench_configs(torch, bl, workloads, dev, log):
+def bench_configs(torch, bl, workloads, dev, log, only=None):
     """The other workloads, reported beside the headline (not part of `value`):
     single_1024 (M = 1, 16), sparse_ffn_1p5b (dense / 2:4 / 6:8 at M = 1 and
     512) and block_3b (seven projections at M = 1, 8, 64).  HBM-bound cases
     rotate weight copies through >= 512 MB; each case is checked against the
-    plain path before it is timed (fused == two-call, bit for bit)."""
+    plain path before it is timed (fused == two-call, bit for bit; the
+    trit-packed 2:4 forward == the 2:4 forward).  `only`: run just the cases
+    whose name holds this string."""
     res = {}
 
-    def case(name, wl_name, projs, M, nm_of, fused_groups=None, masked=None):
+    def case(name, wl_name, projs, M, nm_of, fused_groups=None, masked=None, trit24=False):
         # masked: the N:M pattern of weights packed in the dense layout
-        # (bitlinear_pack_weights_masked; nm_of then gives (0, 0))
+        # (bitlinear_pack_weights_masked; nm_of then gives (0, 0)); trit24:
+        # 2:4 weights in the trit-packed layout (bitlinear_forward_trit24)
+        if only and only not in name:
+            return
         wl = workloads.WORKLOADS[wl_name]
         d = workloads.draw(wl_name, projs=projs, Ms=(M,))
         shapes = {p.name: (p.N, p.K) for p in wl.projs if p.name in projs}
@@ -550,6 +555,8 @@ def bench_configs(torch, bl, workloads, dev, log):
         for n in projs:
             if masked:
                 pk[n], ws[n] = bl.pack_weights_masked(torch.from_numpy(d.W[n]).to(dev), masked)
+            elif trit24:
+                pk[n], ws[n] = bl.pack_weights_trit24(torch.from_numpy(d.W[n]).to(dev))
             else:
                 pk[n], ws[n] = bl.pack_weights(torch.from_numpy(d.W[n]).to(dev), nm=nm_of(n))
         wbytes = sum(pk[n].numel() for n in projs)
@@ -561,12 +568,25 @@ def bench_configs(torch, bl, workloads, dev, log):
         xs = {n: torch.empty(M, dtype=torch.float32, device=dev) for n in projs}
         rs = {n: torch.empty(M, dtype=torch.int32, device=dev) for n in projs}
 
+        work = {n: torch.empty(max(1, bl.forward_trit24_workspace_size(M, *shapes[n])), dtype=torch.uint8,
+                               device=dev) for n in projs} if trit24 else {}
+
         def two_call(j):
             for n in projs:
                 bl.quant_act(X[n], Xq[n], xs[n], rs[n])
-                bl.forward(Xq[n], xs[n], rs[n], pools[n][j], ws[n], shapes[n][0], nm=nm_of(n), Y=Y[n])
+                if trit24:
+                    bl.forward_trit24(Xq[n], xs[n], rs[n], pools[n][j], ws[n], shapes[n][0], Y=Y[n],
+                                      workspace=work[n])
+                else:
+                    bl.forward(Xq[n], xs[n], rs[n], pools[n][j], ws[n], shapes[n][0], nm=nm_of(n), Y=Y[n])
         two_call(0)
         torch.cuda.synchronize()
+        if trit24:
+            # the same weights in the 2:4 values + masks layout give the same Y
+            for n in projs:
+                p24, w24 = bl.pack_weights(torch.from_numpy(d.W[n]).to(dev), nm=(2, 4))
+                if not torch.equal(bl.forward(Xq[n], xs[n], rs[n], p24, w24, shapes[n][0], nm=(2, 4)), Y[n]):
+                    raise SystemExit("%s: trit-packed and 2:4 outputs differ for %s" % (name, n))
         Yref = {n: Y[n].clone() for n in projs}
         kernels = sorted({bl.last_dispatch()})
         G = P if M <= 64 else 10
@@ -670,6 +690,9 @@ def bench_configs(torch, bl, workloads, dev, log):
                  masked=nmap[pn])
             case("sparse_ffn_1p5b/%s_dense_layout/M512" % pn, "sparse_ffn_1p5b", (pn,), 512, dense,
                  masked=nmap[pn])
+    # the 2:4 weights in the trit-packed layout (1.5 bits per weight)
+    case("sparse_ffn_1p5b/nm24_trit_packed/M1", "sparse_ffn_1p5b", ("nm24",), 1, dense, trit24=True)
+    case("sparse_ffn_1p5b/nm24_trit_packed/M512", "sparse_ffn_1p5b", ("nm24",), 512, dense, trit24=True)
     blk = ("q", "k", "v", "o", "gate", "up", "down")
     for M in (1, 8, 64):
         case("block_3b/M%d" % M, "block_3b", blk, M, dense,
@@ -826,6 +849,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the other workloads' timings")
+    ap.add_argument("--configs-only", default=None, metavar="SUBSTR",
+                    help="time only the other workloads' cases whose name holds SUBSTR and print them as JSON")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pool-mb", type=int, default=POOL_BYTES >> 20,
                     help="size of the decode step's rotating weight pool (default 2 GiB, 8x the Infinity Cache)")
@@ -906,6 +931,10 @@ def main():
         print(json.dumps({"gemm_launches": 5, "kernel": bl.last_dispatch(), "M": 2048, "N": 6912, "K": 2560,
                           "source_digest": source_digest()}),
               flush=True)
+        return
+
+    if args.configs_only is not None:
+        print(json.dumps(bench_configs(torch, bl, workloads, dev, log, only=args.configs_only)), flush=True)
         return
 
     if args.block_probe or args.block_traffic_probe:

@@ -48,6 +48,12 @@
  *             4-bit mask in byte g/2 (even g in the low nibble); for M_=8
  *             group g has byte g; bit i set = k = g*M_ + i kept.
  *   sizes: dense and 2:4 = N*K/4 bytes; 6:8 = 5*N*K/16 bytes.
+ *   2:4 trit-packed (bitlinear_pack_weights_trit24): per group g of 4
+ *     inputs, kept inputs i0 < i1, one 6-bit code 9*p + 3*(t[i0]+1) +
+ *     (t[i1]+1), p the index of (i0, i1) in (0,1) (0,2) (0,3) (1,2) (1,3)
+ *     (2,3); the 16 codes of inputs 64s..64s+63 form string s, 96 bits
+ *     little-endian with group g%16 at bit 6*(g%16) (12 bytes); row n is
+ *     its K/64 strings in k order at byte offset n*3*K/16: 3*N*K/16 bytes.
  *
  * Conventions for every call:
  *   - Data pointers are device pointers (hipMalloc / torch tensors) owned by
@@ -214,6 +220,52 @@ bitlinear_status bitlinear_forward_noalloc(const int8_t *Xq, const float *x_scal
                                            const void *packed, const float *w_scale, bitlinear_nm nm,
                                            int64_t M, int64_t N, int64_t K,
                                            float *Y, int32_t *acc, hipStream_t stream);
+
+/* Host-only size query for bitlinear_pack_weights_trit24: *packed_bytes
+ * receives 3*N*K/16 (1.5 bits per weight: the trit-packed layout above),
+ * *workspace_bytes the pack's scratch (as bitlinear_packed_size).  Either
+ * output pointer may be NULL.  Launches nothing.  Errors: EINVAL for N or K
+ * out of range. */
+bitlinear_status bitlinear_packed_size_trit24(int64_t N, int64_t K, size_t *packed_bytes,
+                                              size_t *workspace_bytes);
+
+/* 2:4 weights in the trit-packed layout: the same beta, ternary values and
+ * 2:4 mask as bitlinear_pack_weights with nm = {2,4} (quant-then-mask, the
+ * two largest |W| per group of 4 inputs, ties to the lower k; Sparse-BitNet
+ * review, sec. 3.2), stored as one 6-bit code per group, which names the
+ * kept pair and its two ternary values out of 6 x 3 x 3 = 54 (the pair index
+ * over the 3 x 3 values, as bitnet.cpp's TL2 indexes a pair of ternary
+ * weights by its 9 combinations: "bitnet.cpp 추론 프레임워크", section "I2_S
+ * 커널의 내부 동작").  3*N*K/16 bytes: a quarter fewer than the 2:4 values +
+ * masks.  Arguments and workspace as bitlinear_pack_weights.  Errors: ESIZE
+ * if packed_bytes < 3*N*K/16 or the workspace is short; EINVAL for a bad
+ * shape or a null or misaligned pointer. */
+bitlinear_status bitlinear_pack_weights_trit24(const float *W, int64_t N, int64_t K, void *packed,
+                                               size_t packed_bytes, float *w_scale, void *workspace,
+                                               size_t workspace_bytes, hipStream_t stream);
+
+/* Host-only size query for bitlinear_forward_trit24: *workspace_bytes
+ * receives the device scratch of an M x N x K call (0 for one token with
+ * K <= 16384; otherwise N*K/4 bytes rounded up to 256 for the rows expanded
+ * to dense codes, plus what bitlinear_forward needs for the dense shape).
+ * Launches nothing.  Errors: EINVAL for a bad shape or NULL output. */
+bitlinear_status bitlinear_forward_trit24_workspace_size(int64_t M, int64_t N, int64_t K,
+                                                         size_t *workspace_bytes);
+
+/* The forward contraction and rescale (as bitlinear_forward: 2B4T summary,
+ * sec. 2 and 5.1; Sparse-BitNet review, sec. 3.2) on weights written by
+ * bitlinear_pack_weights_trit24 with the same N and K.  Arguments, outputs,
+ * workspace rules and errors as bitlinear_forward with nm = {2,4}; acc and Y
+ * are bit-identical to bitlinear_forward on the same weights packed by
+ * bitlinear_pack_weights with nm = {2,4}.  One token with K <= 16384 runs a
+ * kernel that reads the 6-bit codes and looks up their four weights in a
+ * table in LDS (x_rowsum is then not read); otherwise the rows are expanded
+ * to dense codes in the workspace and the dense kernels run on them.  Codes
+ * 54-63, which the packer never writes, count as four zero weights. */
+bitlinear_status bitlinear_forward_trit24(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
+                                          const void *packed, const float *w_scale, int64_t M, int64_t N,
+                                          int64_t K, float *Y, int32_t *acc, void *workspace,
+                                          size_t workspace_bytes, hipStream_t stream);
 
 /* One projection of a fused decode call: packed weights and beta as written
  * by bitlinear_pack_weights (same K and nm as the call), N output features,

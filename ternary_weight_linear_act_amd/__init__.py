@@ -14,6 +14,10 @@ from .binding import (  # noqa: F401
     packed_size,
     pack_weights,
     pack_weights_masked,
+    packed_size_trit24,
+    pack_weights_trit24,
+    forward_trit24,
+    forward_trit24_workspace_size,
     quant_act,
     quant_act_ex,
     quant_act_h4,

@@ -35,6 +35,10 @@ EXPORTED = (
     "bitlinear_forward_grouped",
     "bitlinear_forward_fused",
     "bitlinear_forward_fused_ex",
+    "bitlinear_packed_size_trit24",
+    "bitlinear_pack_weights_trit24",
+    "bitlinear_forward_trit24_workspace_size",
+    "bitlinear_forward_trit24",
     "bitlinear_last_error",
     "bitlinear_last_dispatch",
 )
@@ -93,6 +97,10 @@ def load_library():
     lib.bitlinear_combine_a48.argtypes = [vp, i64, i64, vp, vp]
     lib.bitlinear_forward_fused_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, NM,
                                                ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
+    lib.bitlinear_packed_size_trit24.argtypes = [i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
+    lib.bitlinear_pack_weights_trit24.argtypes = [vp, i64, i64, vp, sz, vp, vp, sz, vp]
+    lib.bitlinear_forward_trit24_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
+    lib.bitlinear_forward_trit24.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp, vp, sz, vp]
     for f in EXPORTED:
         if f not in ("bitlinear_last_error", "bitlinear_last_dispatch"):
             getattr(lib, f).restype = ctypes.c_int
@@ -193,6 +201,77 @@ def pack_weights_masked(W, nm, out=None, w_scale=None, workspace=None, stream=No
     _check("bitlinear_pack_weights_masked", load_library().bitlinear_pack_weights_masked(
         _ptr(W), N, K, _nm(nm), _ptr(out), out.numel(), _ptr(w_scale), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, w_scale
+
+
+def packed_size_trit24(N: int, K: int):
+    """(packed bytes, pack workspace bytes) of the trit-packed 2:4 layout."""
+    pb, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("bitlinear_packed_size_trit24", load_library().bitlinear_packed_size_trit24(
+        N, K, ctypes.byref(pb), ctypes.byref(wb)))
+    return pb.value, wb.value
+
+
+def pack_weights_trit24(W, out=None, w_scale=None, workspace=None, stream=None):
+    """2:4 ternary weights of an N x K fp32 device matrix, one 6-bit code per
+    group of 4 (3*N*K/16 bytes), for forward_trit24().  Returns (packed uint8,
+    w_scale fp32[1])."""
+    import torch
+    _require(W, torch.float32, None, "W")
+    N, K = W.shape
+    pb, wb = packed_size_trit24(N, K)
+    if out is None:
+        out = torch.empty(pb, dtype=torch.uint8, device=W.device)
+    if w_scale is None:
+        w_scale = torch.empty(1, dtype=torch.float32, device=W.device)
+    if workspace is None and wb:
+        workspace = torch.empty(wb, dtype=torch.uint8, device=W.device)
+    _require(out, torch.uint8, None, "packed")
+    _require(w_scale, torch.float32, (1,), "w_scale")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("bitlinear_pack_weights_trit24", load_library().bitlinear_pack_weights_trit24(
+        _ptr(W), N, K, _ptr(out), out.numel(), _ptr(w_scale), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, w_scale
+
+
+def forward_trit24_workspace_size(M: int, N: int, K: int) -> int:
+    """Device scratch bytes bitlinear_forward_trit24 needs for an M x N x K call."""
+    wb = ctypes.c_size_t(0)
+    _check("bitlinear_forward_trit24_workspace_size", load_library().bitlinear_forward_trit24_workspace_size(
+        M, N, K, ctypes.byref(wb)))
+    return wb.value
+
+
+def forward_trit24(Xq, x_scale, x_rowsum, packed, w_scale, N, Y=None, acc=None, want_acc=False, workspace=None,
+                   stream=None):
+    """forward() on weights packed by pack_weights_trit24.  Returns Y or (Y, acc)."""
+    import torch
+    _require(Xq, torch.int8, None, "Xq")
+    M, K = Xq.shape
+    _require(x_scale, torch.float32, (M,), "x_scale")
+    _require(x_rowsum, torch.int32, (M,), "x_rowsum")
+    _require(packed, torch.uint8, None, "packed")
+    _require(w_scale, torch.float32, (1,), "w_scale")
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=Xq.device)
+    _require(Y, torch.float32, (M, N), "Y")
+    if acc is None and want_acc:
+        acc = torch.empty((M, N), dtype=torch.int32, device=Xq.device)
+    if acc is not None:
+        _require(acc, torch.int32, (M, N), "acc")
+    pb, _ = packed_size_trit24(N, K)
+    if packed.numel() < pb:
+        raise ValueError("packed buffer holds %d bytes, %d needed" % (packed.numel(), pb))
+    if workspace is None:
+        wb = forward_trit24_workspace_size(M, N, K)
+        if wb:
+            workspace = torch.empty(wb, dtype=torch.uint8, device=Xq.device)
+    if workspace is not None:
+        _require(workspace, torch.uint8, None, "workspace")
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check("bitlinear_forward_trit24", load_library().bitlinear_forward_trit24(
+        _ptr(Xq), _ptr(x_scale), _ptr(x_rowsum), _ptr(packed), _ptr(w_scale), M, N, K, _ptr(Y), _ptr(acc),
+        _ptr(workspace), ws_bytes, _stream(stream)))
+    return (Y, acc) if (want_acc or acc is not None) else Y
 
 
 def quant_act(X, Xq=None, x_scale=None, x_rowsum=None, stream=None):

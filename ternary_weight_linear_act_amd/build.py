@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
-SOURCES = ["api.hip", "quant.hip", "pack.hip", "gemv.hip", "gemm.hip", "gemm_sparse.hip", "skinny.hip", "skinny_direct.hip", "skinny_direct_tiles.hip", "fused.hip", "decode_dot4.hip",
+SOURCES = ["api.hip", "quant.hip", "pack.hip", "gemv.hip", "gemm.hip", "gemm_sparse.hip", "skinny.hip", "skinny_direct.hip", "skinny_direct_tiles.hip", "trit24.hip", "fused.hip", "decode_dot4.hip",
            "decode_dot4_tr.hip", "noalloc.hip"]
 
 ARCH = "gfx950"

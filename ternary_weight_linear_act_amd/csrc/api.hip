@@ -183,6 +183,8 @@ size_t packed_bytes_for(int64_t N, int64_t K, bl::Pattern p)
     return 0;
 }
 
+size_t packed_bytes_trit24(int64_t N, int64_t K) { return (size_t)(N * (3 * K / 16)); }
+
 size_t workspace_bytes_for(int64_t N) { return (size_t)((N * 8 + 255) / 256 * 256); }
 
 // Workspace bytes of a forward call: the dispatch run as a size query.
@@ -318,6 +320,38 @@ bitlinear_status bitlinear_pack_weights_masked(const float *W, int64_t N, int64_
     return BITLINEAR_OK;
 }
 
+bitlinear_status bitlinear_packed_size_trit24(int64_t N, int64_t K, size_t *packed_bytes, size_t *workspace_bytes)
+{
+    CHECK(check_n(N));
+    CHECK(check_k(K));
+    if (packed_bytes) *packed_bytes = packed_bytes_trit24(N, K);
+    if (workspace_bytes) *workspace_bytes = workspace_bytes_for(N);
+    return BITLINEAR_OK;
+}
+
+bitlinear_status bitlinear_pack_weights_trit24(const float *W, int64_t N, int64_t K, void *packed,
+                                               size_t packed_bytes, float *w_scale, void *workspace,
+                                               size_t workspace_bytes, hipStream_t stream)
+{
+    CHECK(check_n(N));
+    CHECK(check_k(K));
+    CHECK(check_ptr(W, 16, "W"));
+    CHECK(check_ptr(packed, 16, "packed"));
+    CHECK(check_ptr(w_scale, 4, "w_scale"));
+    if (packed_bytes < packed_bytes_trit24(N, K))
+        return fail(BITLINEAR_ESIZE, "packed buffer has %zu bytes, %zu needed", packed_bytes,
+                    packed_bytes_trit24(N, K));
+    if (workspace_bytes < workspace_bytes_for(N))
+        return fail(BITLINEAR_ESIZE, "workspace has %zu bytes, %zu needed", workspace_bytes, workspace_bytes_for(N));
+    CHECK(check_ptr(workspace, 8, "workspace"));
+    hipError_t e = bl::launch_absmean(W, N, K, static_cast<double *>(workspace), w_scale, stream);
+    if (e != hipSuccess) return hip_fail("absmean launch", e);
+    e = bl::launch_pack_trit24(W, N, K, w_scale, static_cast<uint8_t *>(packed), stream);
+    if (e != hipSuccess) return hip_fail("pack launch", e);
+    set_dispatch("absmean+pack_trit24");
+    return BITLINEAR_OK;
+}
+
 bitlinear_status bitlinear_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
                                      int32_t *x_rowsum, hipStream_t stream)
 {
@@ -434,6 +468,55 @@ bitlinear_status bitlinear_forward(const int8_t *Xq, const float *x_scale, const
     scratch.ptr = static_cast<uint8_t *>(workspace);
     scratch.bytes = workspace ? workspace_bytes : 0;
     return run_forward(Xq, x_scale, x_rowsum, packed, w_scale, p, M, N, K, Y, acc, scratch, stream);
+}
+
+bitlinear_status bitlinear_forward_trit24_workspace_size(int64_t M, int64_t N, int64_t K, size_t *workspace_bytes)
+{
+    CHECK(check_m(M));
+    CHECK(check_n(N));
+    CHECK(check_k(K));
+    if (!workspace_bytes) return fail(BITLINEAR_EINVAL, "workspace_bytes must not be NULL");
+    *workspace_bytes = 0;
+    if (M == 0) return BITLINEAR_OK;
+    bl::Scratch q;
+    q.query = true;
+    const char *name = "";
+    // a query launches nothing; its status only repeats what validation found
+    (void)bl::launch_forward_trit24(nullptr, nullptr, nullptr, nullptr, nullptr, M, N, K, nullptr, nullptr, q,
+                                    nullptr, &name);
+    *workspace_bytes = q.need;
+    return BITLINEAR_OK;
+}
+
+bitlinear_status bitlinear_forward_trit24(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,
+                                          const void *packed, const float *w_scale, int64_t M, int64_t N, int64_t K,
+                                          float *Y, int32_t *acc, void *workspace, size_t workspace_bytes,
+                                          hipStream_t stream)
+{
+    CHECK(check_m(M));
+    CHECK(check_n(N));
+    CHECK(check_k(K));
+    CHECK(check_ptr(packed, 16, "packed"));
+    CHECK(check_ptr(w_scale, 4, "w_scale"));
+    if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }   // M-sized buffers may be NULL
+    CHECK(check_ptr(Xq, 16, "Xq"));
+    CHECK(check_ptr(x_scale, 4, "x_scale"));
+    CHECK(check_ptr(x_rowsum, 4, "x_rowsum"));
+    CHECK(check_ptr(Y, 16, "Y"));
+    if (acc && !aligned(acc, 16)) return fail(BITLINEAR_EINVAL, "acc must be 16-byte aligned");
+    if (workspace && !aligned(workspace, 16)) return fail(BITLINEAR_EINVAL, "workspace must be 16-byte aligned");
+    bl::Scratch scratch;
+    scratch.ptr = static_cast<uint8_t *>(workspace);
+    scratch.bytes = workspace ? workspace_bytes : 0;
+    const char *name = "";
+    const hipError_t e = bl::launch_forward_trit24(Xq, x_scale, x_rowsum, static_cast<const uint8_t *>(packed),
+                                                   w_scale, M, N, K, Y, acc, scratch, stream, &name);
+    if (scratch.need > scratch.bytes)
+        return fail(BITLINEAR_ESIZE, "workspace has %zu bytes, %zu needed for M = %lld, N = %lld, K = %lld (%s)",
+                    scratch.bytes, scratch.need, (long long)M, (long long)N, (long long)K, name);
+    if (e != hipSuccess) return hip_fail("forward launch", e);
+    set_dispatch(name);
+    return BITLINEAR_OK;
 }
 
 bitlinear_status bitlinear_forward_noalloc(const int8_t *Xq, const float *x_scale, const int32_t *x_rowsum,

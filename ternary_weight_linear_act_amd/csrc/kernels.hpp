@@ -107,6 +107,19 @@ hipError_t launch_pack(const float *W, int64_t N, int64_t K, Pattern p, const fl
 hipError_t launch_pack_nm_dense(const float *W, int64_t N, int64_t K, int n, int m, const float *w_scale,
                                 uint8_t *packed, hipStream_t stream);
 
+// 2:4 weights in the trit-packed storage (a 6-bit code per group of 4
+// inputs, 16 codes in 12 bytes; trit24.hip), with d = beta + 1e-5 read from
+// w_scale.
+hipError_t launch_pack_trit24(const float *W, int64_t N, int64_t K, const float *w_scale, uint8_t *packed,
+                              hipStream_t stream);
+
+// Forward on the trit-packed 2:4 weights: the one-token kernel (M = 1,
+// K <= 16384), else the strings expanded to dense codes in the workspace and
+// the dense forward.  Workspace and query handling as launch_forward.
+hipError_t launch_forward_trit24(const int8_t *Xq, const float *xs, const int32_t *rs, const uint8_t *packed,
+                                 const float *w_scale, int64_t M, int64_t N, int64_t K, float *Y, int32_t *acc,
+                                 Scratch &scratch, hipStream_t stream, const char **name);
+
 // Forward.  Returns the name of the kernel variant in *name.  With
 // scratch.query set nothing is launched and scratch.need receives the
 // workspace bytes; otherwise a workspace smaller than the chosen kernels need

@@ -251,6 +251,60 @@ __global__ __launch_bounds__(kBlock) void pack_nm_dense_kernel(const float *__re
     }
 }
 
+// 2:4 weights in the trit-packed storage: per group of 4 inputs the mask of
+// pack_nm_kernel (the two largest |w|, ties to the lower k), kept inputs
+// i0 < i1, and one 6-bit code 9 p + 3 c(i0) + c(i1), with c = t + 1 and p the
+// index of (i0, i1) in (0,1) (0,2) (0,3) (1,2) (1,3) (2,3).  The 16 codes of
+// 64 consecutive inputs form one 96-bit little-endian string (group g at bit
+// 6 g), 12 bytes; a row is its K / 64 strings in k order, rows back to back,
+// so string i of the matrix sits at byte 12 i.  One thread per string.
+__global__ __launch_bounds__(kBlock) void pack_trit24_kernel(const float *__restrict__ W, int64_t strings,
+                                                             const float *__restrict__ w_scale,
+                                                             uint32_t *__restrict__ out)
+{
+    const float d = w_scale[0] + 1e-5f;
+    for (int64_t idx = (int64_t)blockIdx.x * kBlock + threadIdx.x; idx < strings;
+         idx += (int64_t)gridDim.x * kBlock) {
+        const float4 *w4 = reinterpret_cast<const float4 *>(W + idx * 64);
+        uint32_t words[3] = {0u, 0u, 0u};
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            const float4 v = w4[g];
+            const float w[4] = {v.x, v.y, v.z, v.w};
+            uint32_t mk = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float mi = fabsf(w[i]);
+                int rank = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float mj = fabsf(w[j]);
+                    rank += (mj > mi) || (j < i && mj == mi);
+                }
+                mk |= (rank < 2 ? 1u : 0u) << i;
+            }
+            // the ranks are a permutation of 0..3: exactly two bits are set
+            const int i0 = __builtin_ctz(mk), i1 = 31 - __builtin_clz(mk);
+            const uint32_t p = (uint32_t)(i0 == 0 ? i1 - 1 : i0 == 1 ? i1 + 1 : 5);
+            uint32_t c0 = 0u, c1 = 0u;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t c = ternary_code(w[i], d);
+                c0 = (i == i0) ? c : c0;
+                c1 = (i == i1) ? c : c1;
+            }
+            const uint32_t code = 9u * p + 3u * c0 + c1;
+            const int bit = 6 * g, wi = bit >> 5, o = bit & 31;
+            words[wi] |= code << o;
+            if (o > 26) words[wi + 1] |= code >> (32 - o);
+        }
+        uint32_t *o = out + idx * 3;
+        o[0] = words[0];
+        o[1] = words[1];
+        o[2] = words[2];
+    }
+}
+
 unsigned grid_for(int64_t items)
 {
     int64_t blocks = (items + kBlock - 1) / kBlock;
@@ -271,6 +325,15 @@ hipError_t launch_pack_nm_dense(const float *W, int64_t N, int64_t K, int n, int
     case 16: hipLaunchKernelGGL(pack_nm_dense_kernel<16>, grid, dim3(kBlock), 0, stream, W, N, K, n, w_scale, o); break;
     default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_trit24(const float *W, int64_t N, int64_t K, const float *w_scale, uint8_t *packed,
+                              hipStream_t stream)
+{
+    const int64_t strings = N * (K / 64);
+    hipLaunchKernelGGL(pack_trit24_kernel, dim3(grid_for(strings)), dim3(kBlock), 0, stream, W, strings, w_scale,
+                       reinterpret_cast<uint32_t *>(packed));
     return hipGetLastError();
 }
 

@@ -327,3 +327,58 @@ def test_fused_validation(lib):
     bad = (Proj * 1)(Proj(A + 4, A, 64, A, None))
     assert f(P(), 1, 128, NM(0, 0), bad, 1, None, None) == -1            # misaligned packed
     assert f(None, 0, 128, NM(0, 0), arr, 1, None, None) == 0            # M = 0: no-op
+
+
+def test_trit24_sizes_and_validation(lib):
+    # the trit-packed 2:4 layout: 12 bytes per 64 weights, as the oracle's
+    # layout arithmetic counts them
+    import oracle
+    pb, wb = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    for (N, K) in [(8960, 1536), (1, 64), (3, 192), (2560, 6912)]:
+        assert lib.bitlinear_packed_size_trit24(N, K, ctypes.byref(pb), ctypes.byref(wb)) == 0
+        assert pb.value == oracle.packed_bytes_trit24(N, K) == 3 * N * K // 16
+        assert wb.value == -(-8 * N // 256) * 256
+    assert lib.bitlinear_packed_size_trit24(8, 96, None, None) == -1          # K % 64
+    assert lib.bitlinear_packed_size_trit24(0, 64, None, None) == -1          # N < 1
+    p = lib.bitlinear_pack_weights_trit24
+    assert p(P(), 8, 64, P(), 8 * 12 - 1, P(), P(), 256, None) == -3          # packed one byte short
+    assert p(P(), 8, 64, P(), 8 * 12, P(), P(), 8, None) == -3                # workspace short
+    assert p(P(), 8, 64, P(), 8 * 12, P(), None, 256, None) == -1             # workspace missing
+    assert p(P(4), 8, 64, P(), 8 * 12, P(), P(), 256, None) == -1             # misaligned W
+    assert p(P(), 8, 100, P(), 8 * 12, P(), P(), 256, None) == -1             # K % 64
+
+
+def test_trit24_forward_workspace_and_validation(lib):
+    ws = ctypes.c_size_t(0)
+
+    def need(M, N, K):
+        st = lib.bitlinear_forward_trit24_workspace_size(M, N, K, ctypes.byref(ws))
+        return st, ws.value
+    # one token on the table-lookup kernel: no scratch up to K = 16384
+    assert need(1, 8960, 1536) == (0, 0)
+    assert need(1, 100, 16384) == (0, 0)
+    assert need(0, 100, 1536) == (0, 0)
+    # otherwise the rows expanded to dense codes (N * K / 4 rounded up to
+    # 256) plus what the dense forward needs for the shape
+    rows = -(-8960 * 1536 // 4 // 256) * 256
+    assert need(512, 8960, 1536) == (0, rows + work_size(lib, 512, 8960, 1536, (0, 0))[1])
+    assert need(5, 8960, 1536) == (0, rows + work_size(lib, 5, 8960, 1536, (0, 0))[1])
+    rows = -(-40 * 16448 // 4 // 256) * 256
+    assert need(1, 40, 16448) == (0, rows + work_size(lib, 1, 40, 16448, (0, 0))[1])
+    rows = -(-2560 * 6912 // 4 // 256) * 256
+    assert need(512, 2560, 6912) == (0, rows + 4 * 80 * 128 * 128 * 4)     # the dense GEMM splits K
+    assert need(4, 64, 100)[0] == -1
+    assert lib.bitlinear_forward_trit24_workspace_size(4, 64, 128, None) == -1
+    f = lib.bitlinear_forward_trit24
+    # a short workspace is ESIZE before anything is launched
+    n = need(512, 8960, 1536)[1]
+    assert f(P(), P(), P(), P(), P(), 512, 8960, 1536, P(), None, P(), n - 1, None) == -3
+    assert b"needed" in lib.bitlinear_last_error()
+    assert f(P(), P(), P(), P(), P(), 512, 8960, 1536, P(), None, None, 0, None) == -3
+    # M == 0 is a no-op with NULL token buffers
+    assert f(None, None, None, P(), P(), 0, 8960, 1536, None, None, None, 0, None) == 0
+    assert lib.bitlinear_last_dispatch() == b"none"
+    assert f(P(), P(), None, P(), P(), 1, 64, 64, P(), None, None, 0, None) == -1     # x_rowsum required
+    assert f(P(), P(), P(), P(4), P(), 1, 64, 64, P(), None, None, 0, None) == -1     # misaligned packed
+    assert f(P(), P(), P(), P(), P(), 1, 64, 64, P(), P(4), None, 0, None) == -1      # misaligned acc
+    assert f(P(), P(), P(), P(), P(), 1, 0, 64, P(), None, None, 0, None) == -1       # N < 1
