@@ -56,8 +56,8 @@ def log(*a):
 # The files the fused one-token decode kernel is built from, and the compiler
 # flags: the committed kernel trace and HBM traffic describe that kernel only
 # while these are unchanged.
-DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode_dot4.hip", "decode_dot4_impl.hpp", "fused_impl.hpp",
-                                                  "skinny_impl.hpp", "common.hpp")] + [
+DECODE_SOURCES = [os.path.join(CSRC, f) for f in ("decode_dot4.hip", "decode_dot4_impl.hpp", "decode_multi.hip",
+                                                  "fused_impl.hpp", "skinny_impl.hpp", "common.hpp")] + [
     os.path.join(ROOT, "include", "bitlinear.h")]
 
 
@@ -108,8 +108,12 @@ def _probe_json(path):
 def _dot4_args(text):
     """Template arguments (pattern, LPR, U, fused, W, TR) of a decode_dot4
     kernel, from a demangled symbol or from a dispatch name such as
-    fused_decode_dot4_dense_lpr8_u5_p2_w8; None for other kernels."""
+    fused_decode_dot4_dense_lpr8_u5_p2_w8; ("multi",) for the multi-group
+    kernel (decode_multi_kernel, dispatched as fused_decode_multi_...); None
+    for other kernels."""
     import re
+    if text.startswith("fused_decode_multi_") or "decode_multi_kernel" in text:
+        return ("multi",)
     m = re.match(r"(fused_)?decode_dot4_(dense|nm24|nm68)_lpr(\d+)_u(\d+)_p\d+(_w8)?(_gate_norm|_gate|_norm)?$", text)
     if m:
         tr = {None: 0, "_gate": 1, "_norm": 2, "_gate_norm": 3}[m.group(6)]
@@ -634,6 +638,20 @@ def bench_configs(torch, bl, workloads, dev, log, only=None):
                       "fused_launches": launches,
                       "fused_groups": ["+".join(g) + (" fused" if narrow(g) else " quant_act+grouped")
                                        for g in fused_groups]})
+            if M == 1 and len(fused_groups) > 1 and all(nm_of(n) == (0, 0) for n in projs) and not masked:
+                # every input group in one launch (the groups' inputs given)
+                margs = [[(X[g[0]], [(pools[n][j], ws[n], shapes[n][0]) for n in g], [Y[n] for n in g], None,
+                           None) for g in fused_groups] for j in range(P)]
+                bl.forward_fused_multi(margs[0])
+                mk = bl.last_dispatch()
+                torch.cuda.synchronize()
+                for n in projs:
+                    if not torch.equal(Y[n], Yref[n]):
+                        raise SystemExit("%s: multi-group and two-call outputs differ for %s" % (name, n))
+                ms, _ = timed_graph(torch, lambda: [bl.forward_fused_multi(margs[j % P]) for j in range(G)], reps=2)
+                mus = ms * 1e3 / G
+                r.update({"multi_us": round(mus, 3), "multi_GB/s": round(fbytes / (mus * 1e-6) / 1e9, 1),
+                          "multi_launches": 1, "multi_kernel": mk})
         if fused_groups and M > 16:
             # past 16 tokens: one quant_act per input group (not per
             # projection), then the grouped forward where one launch serves
@@ -1053,11 +1071,14 @@ def main():
     torch.cuda.synchronize()
     log("decode: pool of %d weight sets, %.0f MB" % (P, P * step_w_bytes / 1e6))
 
+    # One step: every input group's quantisation and projections in one
+    # launch (the inputs of the two groups are given and independent).  The
+    # per-group launches (one per input group) are timed beside it.
+    multi_args = [[(Xg[g][j], [(packed[n][j], wsc[n], shapes[n][0]) for n in g], [Y[n] for n in g], None, None)
+                   for g in groups] for j in range(P)]
+
     def decode_step(i):
-        j = i % P
-        for g in groups:
-            bl.forward_fused(Xg[g][j], [(packed[n][j], wsc[n], shapes[n][0]) for n in g],
-                             Ys=[Y[n] for n in g])
+        bl.forward_fused_multi(multi_args[i % P])
 
     # gate before timing: the kernel choice; the values are checked against
     # the oracle in the CPU leg below (and by the GPU tests)
@@ -1069,7 +1090,14 @@ def main():
     for g, k in group_kernel.items():
         if not k.startswith("fused_decode"):
             raise SystemExit("unexpected kernel for the M=1 decode step (%s): %s" % (g, k))
-    dispatch = ", ".join("%s: %s" % gk for gk in group_kernel.items())
+    decode_step(0)
+    step_kernel = bl.last_dispatch()
+    torch.cuda.synchronize()
+    if not step_kernel.startswith("fused_decode_multi"):
+        raise SystemExit("unexpected kernel for the M=1 decode step: %s" % step_kernel)
+    step_label = ";".join("+".join(g) for g in groups)
+    dispatch = "%s: %s" % (step_label, step_kernel)
+    group_dispatch = ", ".join("%s: %s" % gk for gk in group_kernel.items())
     decode_Y = {name: Y[name].cpu().numpy().astype(np.float64) for name in shapes}
 
     if args.traffic_probe:
@@ -1084,8 +1112,8 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        log("traffic probe: %d fused decode launches, then a %d-byte device copy" % (2 * P * len(groups), copy_bytes))
-        print(json.dumps({"fused_launches": 2 * P * len(groups), "copy_bytes": copy_bytes, "kernel": dispatch,
+        log("traffic probe: %d fused decode launches, then a %d-byte device copy" % (2 * P, copy_bytes))
+        print(json.dumps({"fused_launches": 2 * P, "copy_bytes": copy_bytes, "kernel": dispatch,
                           "source_digest": source_digest()}), flush=True)
         return
 
@@ -1095,8 +1123,15 @@ def main():
     step_bytes = sum(group_bytes(g) for g in groups)
 
     if args.stream_probe:
-        floor = stream_floor(torch, dev, [group_bytes(g) for g in groups], args.pool_mb << 20)
+        floor = stream_floor(torch, dev, [group_bytes(g) for g in groups] + [step_bytes], args.pool_mb << 20)
         rows = {}
+        _, gg = timed_graph(torch, lambda: [decode_step(j) for j in range(P)], reps=1)
+        us = float(np.median(replay_times(torch, gg, 5))) * 1e3 / P
+        fb = floor[(step_bytes + 15) // 16 * 16]
+        rows[step_label] = {"kernel": step_kernel, "bytes": step_bytes, "us": round(us, 3), "floor_us": fb["us"],
+                            "floor_shape": fb["shape"], "floor_fraction": round(fb["us"] / us, 3)}
+        log("%s: %.3f us per launch; streaming-read floor %.3f us (%s): %.0f%% of the floor's speed" % (
+            step_label, us, fb["us"], fb["shape"], 100 * fb["us"] / us))
         for g in groups:
             def one(g=g):
                 for j in range(P):
@@ -1180,16 +1215,21 @@ def main():
         per_group["+".join(g)] = {"kernel": group_kernel["+".join(g)], "us": round(us, 3),
                                   "GB/s": round(group_bytes(g) / (us * 1e-6) / 1e9, 1),
                                   "bytes": group_bytes(g)}
-    fused_us = float(np.mean(launch_us))
-    fused_gbs = step_bytes / (sum(launch_us) * 1e-6) / 1e9
+    groups_step_us = float(np.sum(launch_us))
+    # the dominant kernel: the multi-group launch, timed the same way
+    ms1, gg = timed_graph(torch, lambda: [decode_step(j) for j in range(P)], reps=1)
+    reps = replay_times(torch, gg, max(10, int(math.ceil(20.0 / ms1))))
+    fused_us = float(np.median(reps)) * 1e3 / P
+    fused_gbs = step_bytes / (fused_us * 1e-6) / 1e9
     # the streaming-read floor at the same byte counts (a kernel that only
     # reads them), measured the same way
-    floor = stream_floor(torch, dev, [group_bytes(g) for g in groups], args.pool_mb << 20)
+    floor = stream_floor(torch, dev, [group_bytes(g) for g in groups] + [step_bytes], args.pool_mb << 20)
     for g in groups:
         fb = floor[(group_bytes(g) + 15) // 16 * 16]
         pg = per_group["+".join(g)]
         pg.update({"floor_us": fb["us"], "floor_fraction": round(fb["us"] / pg["us"], 3)})
-    floor_step_us = sum(floor[(group_bytes(g) + 15) // 16 * 16]["us"] for g in groups)
+    floor_step_us = floor[(step_bytes + 15) // 16 * 16]["us"]
+    floor_groups_us = sum(floor[(group_bytes(g) + 15) // 16 * 16]["us"] for g in groups)
 
     # context: the two-call path (quant_act, then forward per projection)
     Xq1, xs1, rs1 = {}, {}, {}
@@ -1300,8 +1340,7 @@ def main():
             t = json.load(open(TRACE_FILE))
             if t.get("source_digest") == digest:
                 trace_us = {k: v["avg_us"] for k, v in t["kernels"].items()}
-                tot = sum(trace_us[group_kernel["+".join(g)]] for g in groups)
-                frac_trace = round(step_bytes / (tot * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                frac_trace = round(step_bytes / (trace_us[step_kernel] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
         except (ValueError, OSError, KeyError):
             frac_trace, trace_us = None, None
 
@@ -1361,18 +1400,23 @@ def main():
         "vs_baseline": None,
         "dtype": "int8xternary->int32->fp32",
         "data": "synthetic (seeded N(0,0.02) latent weights, N(0,1) activations with 0.1% x20 outliers)",
-        "config": {"workload": "decode_ffn_2b: M=1, gate/up 2560->6912 (shared input), down 6912->2560; "
-                               "per step one fused launch (int8 quantisation + projections) per input group; "
-                               "weights rotating over %d buffers (%.0f MB)" % (P, P * step_w_bytes / 1e6),
+        "config": {"workload": "decode_ffn_2b: M=1, gate/up 2560->6912 (shared input), down 6912->2560 (its own "
+                               "input); per step one fused launch (int8 quantisation + the three projections, "
+                               "both input groups); weights rotating over %d buffers (%.0f MB)"
+                               % (P, P * step_w_bytes / 1e6),
                    "M": 1, "projections": ["gate 2560x6912", "up 2560x6912", "down 6912x2560"]},
         "roofline": {"bound": "hbm", "achieved": round(fused_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(fused_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "frac_source": "HIP events: a graph of one launch per pool entry per input group, "
-                                    "replayed for >= 20 ms, median per launch (inter-launch gaps included)",
+                     "frac_source": "HIP events: a graph of one launch per pool entry, replayed for >= 20 ms, "
+                                    "median per launch (inter-launch gaps included)",
                      "frac_trace": frac_trace, "trace_avg_us": trace_us,
                      "frac_streaming_floor": round(step_bytes / (floor_step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                     "floor_us": floor_step_us, "floor_fraction": round(floor_step_us / fused_us, 3),
                      "kernel": dispatch, "avg_launch_us": round(fused_us, 3),
-                     "bytes_per_launch": round(step_bytes / len(groups)), "per_group": per_group},
+                     "bytes_per_launch": step_bytes,
+                     "one_launch_per_group": {"kernels": group_dispatch, "step_us": round(groups_step_us, 3),
+                                              "GB/s": round(step_bytes / (groups_step_us * 1e-6) / 1e9, 1),
+                                              "floor_us": round(floor_groups_us, 3), "per_group": per_group}},
         "protocol": protocol,
         "decode_two_call_path": {"step_us": round(two_call_us, 3),
                                  "GB/s": round(step_bytes / (two_call_us * 1e-6) / 1e9, 1),

@@ -363,6 +363,37 @@ bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_
                                             int64_t K, bitlinear_nm nm, const bitlinear_proj *projs,
                                             int32_t nproj, float *x_scale, hipStream_t stream);
 
+/* One token, several input groups, one launch.  Group g is an fp32 row X
+ * (1 x K, 16-byte aligned) with the nproj projections that read it (a host
+ * array, as for bitlinear_forward_fused) and an optional x_scale output (one
+ * fp32, NULL to skip). */
+typedef struct {
+    const float *X;
+    int64_t K;
+    const bitlinear_proj *projs;
+    int32_t nproj;
+    float *x_scale;
+} bitlinear_input_group;
+
+/* bitlinear_forward_fused for M = 1 over `ngroups` input groups whose inputs
+ * do not depend on one another (the layers of independent sequences, several
+ * experts' down projections, the projections of a step whose activations are
+ * all given): per group, the per-token absmax int8 quantisation and every
+ * projection's integer linear and rescale ("BitNet b1.58 2B4T Technical
+ * Report 요약 설명", sec. 2 and 5.1; "BitNet 논문 분석: 1-Bit LLM의 시대",
+ * section "Absmean 양자화 함수"), each group's outputs bit-identical to its
+ * own bitlinear_forward_fused call.  The Sparse-BitNet review's Table 5
+ * discussion notes that decode gains are diluted by launch overhead; here the
+ * groups share one launch.  `groups` is a host array; no two groups' outputs
+ * may overlap one another or any input.  nm applies to every group.  Dense
+ * weights with every K <= 16384 run as one launch; otherwise (N:M weights, or
+ * a K past 16384) each group runs as its own bitlinear_forward_fused launch,
+ * with the same results.  Errors: EINVAL for a bad group (as
+ * bitlinear_forward_fused) or ngroups < 1; EUNSUPPORTED for ngroups > 4 or a
+ * K past 65344. */
+bitlinear_status bitlinear_forward_fused_multi(const bitlinear_input_group *groups, int32_t ngroups,
+                                               bitlinear_nm nm, hipStream_t stream);
+
 /* H-BitLinear activation quantisation (the BitNet v2 summary
  * (brain.hanbit.co.kr): the activations entering a projection are
  * Hadamard-transformed online, then quantised to 4 bits).  Each row of X

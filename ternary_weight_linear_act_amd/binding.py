@@ -35,6 +35,7 @@ EXPORTED = (
     "bitlinear_forward_grouped",
     "bitlinear_forward_fused",
     "bitlinear_forward_fused_ex",
+    "bitlinear_forward_fused_multi",
     "bitlinear_packed_size_trit24",
     "bitlinear_pack_weights_trit24",
     "bitlinear_forward_trit24_workspace_size",
@@ -61,6 +62,11 @@ class ActTransform(ctypes.Structure):
 class Proj(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("w_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
                 ("Y", ctypes.c_void_p), ("acc", ctypes.c_void_p)]
+
+
+class InputGroup(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("K", ctypes.c_int64), ("projs", ctypes.POINTER(Proj)),
+                ("nproj", ctypes.c_int32), ("x_scale", ctypes.c_void_p)]
 
 
 def library_path() -> str:
@@ -97,6 +103,7 @@ def load_library():
     lib.bitlinear_combine_a48.argtypes = [vp, i64, i64, vp, vp]
     lib.bitlinear_forward_fused_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, NM,
                                                ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
+    lib.bitlinear_forward_fused_multi.argtypes = [ctypes.POINTER(InputGroup), ctypes.c_int32, NM, vp]
     lib.bitlinear_packed_size_trit24.argtypes = [i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.bitlinear_pack_weights_trit24.argtypes = [vp, i64, i64, vp, sz, vp, vp, sz, vp]
     lib.bitlinear_forward_trit24_workspace_size.argtypes = [i64, i64, i64, ctypes.POINTER(sz)]
@@ -539,3 +546,34 @@ def forward_fused_ex(X, projs, up=None, gamma=None, eps=None, nm=NM_DENSE, Ys=No
         _check("bitlinear_forward_fused_ex", load_library().bitlinear_forward_fused_ex(
             _ptr(X), ctypes.byref(tr), M, K, _nm(nm), arr, n, _ptr(x_scale), _stream(stream)))
     return (Ys, accs) if accs is not None else Ys
+
+
+def forward_fused_multi(groups, nm=NM_DENSE, stream=None):
+    """forward_fused at M = 1 for several input groups in one call: `groups`
+    is a list of (X, projs, Ys, accs, x_scale), X a 1 x K fp32 row, projs a
+    list of (packed, w_scale, N) reading X, Ys their 1 x N outputs, accs None
+    or their 1 x N int32 accumulators, x_scale None or a 1-element fp32
+    output.  Dense weights run as one launch (each K <= 16384)."""
+    import torch
+    keep = []
+    garr = (InputGroup * max(len(groups), 1))()
+    for g, (X, projs, Ys, accs, x_scale) in enumerate(groups):
+        _require(X, torch.float32, None, "X")
+        M, K = X.shape
+        if M != 1:
+            raise ValueError("forward_fused_multi takes one token per group (X is %d x %d)" % (M, K))
+        arr = (Proj * max(len(projs), 1))()
+        for i, (packed, ws, N) in enumerate(projs):
+            _require(packed, torch.uint8, None, "packed")
+            _require(ws, torch.float32, (1,), "w_scale")
+            _require(Ys[i], torch.float32, (1, N), "Y")
+            if accs is not None:
+                _require(accs[i], torch.int32, (1, N), "acc")
+            arr[i] = Proj(packed.data_ptr(), ws.data_ptr(), N, Ys[i].data_ptr(),
+                          accs[i].data_ptr() if accs is not None else None)
+        if x_scale is not None:
+            _require(x_scale, torch.float32, (1,), "x_scale")
+        keep.append(arr)
+        garr[g] = InputGroup(_ptr(X), K, arr, len(projs), _ptr(x_scale))
+    _check("bitlinear_forward_fused_multi", load_library().bitlinear_forward_fused_multi(
+        garr, len(groups), _nm(nm), _stream(stream)))

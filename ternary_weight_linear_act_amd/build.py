@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libbitlinear.so")
 SOURCES = ["api.hip", "quant.hip", "pack.hip", "gemv.hip", "gemm.hip", "gemm_sparse.hip", "skinny.hip", "skinny_direct.hip", "skinny_direct_tiles.hip", "trit24.hip", "fused.hip", "decode_dot4.hip",
-           "decode_dot4_tr.hip", "noalloc.hip"]
+           "decode_dot4_tr.hip", "decode_multi.hip", "noalloc.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC") or shutil.which("hipcc") or "/opt/rocm/bin/hipcc"

@@ -99,7 +99,7 @@ hipError_t launch_forward(const int8_t *Xq, const float *x_scale, const int32_t 
 namespace {
 
 thread_local char g_error[512] = "";
-thread_local char g_dispatch[128] = "";
+thread_local char g_dispatch[256] = "";
 
 constexpr int64_t kMaxK = 1048576;
 constexpr int64_t kMaxN = 16777216;
@@ -628,6 +628,55 @@ bitlinear_status bitlinear_forward_fused_ex(const float *X, const bitlinear_act_
                     M == 1 ? "65344" : "16192", (long long)M, (long long)K);
     if (e != hipSuccess) return hip_fail("fused forward launch", e);
     set_dispatch(name);
+    return BITLINEAR_OK;
+}
+
+bitlinear_status bitlinear_forward_fused_multi(const bitlinear_input_group *groups, int32_t ngroups,
+                                               bitlinear_nm nm, hipStream_t stream)
+{
+    bl::Pattern p;
+    CHECK(check_nm(nm, &p));
+    if (!groups) return fail(BITLINEAR_EINVAL, "groups must not be NULL");
+    if (ngroups < 1) return fail(BITLINEAR_EINVAL, "ngroups = %d must be >= 1", ngroups);
+    if (ngroups > bl::kMaxInputGroups)
+        return fail(BITLINEAR_EUNSUPPORTED, "ngroups = %d: at most %d input groups per call", ngroups,
+                    bl::kMaxInputGroups);
+    bl::MultiGroupArgs mg = {};
+    mg.ngroups = ngroups;
+    bool one_launch = (p == bl::Pattern::Dense);
+    for (int g = 0; g < ngroups; ++g) {
+        CHECK(check_k(groups[g].K));
+        if (groups[g].K > 65344)
+            return fail(BITLINEAR_EUNSUPPORTED, "one-token fused decode supports K <= 65344 (group %d: K = %lld)", g,
+                        (long long)groups[g].K);
+        CHECK(check_projs(groups[g].projs, groups[g].nproj, 1, &mg.args[g]));
+        CHECK(check_ptr(groups[g].X, 16, "groups[g].X"));
+        if (groups[g].x_scale && !aligned(groups[g].x_scale, 4))
+            return fail(BITLINEAR_EINVAL, "groups[g].x_scale must be 4-byte aligned");
+        mg.X[g] = groups[g].X;
+        mg.K[g] = groups[g].K;
+        mg.x_scale_out[g] = groups[g].x_scale;
+        if (groups[g].K > 16384) one_launch = false;
+    }
+    const char *name = "";
+    if (one_launch) {
+        const hipError_t e = bl::launch_decode_multi(mg, stream, &name, false);
+        if (e == hipSuccess) { set_dispatch(name); return BITLINEAR_OK; }
+        if (e != hipErrorNotSupported) return hip_fail("multi-group decode launch", e);
+    }
+    // one launch per group
+    char names[sizeof g_dispatch] = "";
+    size_t len = 0;
+    for (int g = 0; g < ngroups; ++g) {
+        hipError_t e = bl::launch_decode_dot4(mg.X[g], nullptr, nullptr, nullptr, 1, mg.K[g], p, mg.args[g],
+                                              mg.x_scale_out[g], bl::ActTransform{nullptr, nullptr, 0.0f}, stream,
+                                              &name, false);
+        if (e == hipErrorNotSupported)
+            e = bl::launch_fused_forward(mg.X[g], 1, mg.K[g], p, mg.args[g], mg.x_scale_out[g], stream, &name);
+        if (e != hipSuccess) return hip_fail("fused forward launch", e);
+        if (len < sizeof names) len += snprintf(names + len, sizeof names - len, "%s%s", g ? " + " : "", name);
+    }
+    set_dispatch(names);
     return BITLINEAR_OK;
 }
 

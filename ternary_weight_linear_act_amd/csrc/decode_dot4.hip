@@ -10,41 +10,20 @@ thread_local char g_name[64];
 
 }  // namespace
 
-// Lanes per row: the fewest of 8, 16, 32, 64 that keep a lane's chunks U
-// <= 5, or <= 7 with the quantisation fused in (<= 4 at 64 lanes, K <= 16384).
-// The fused kernel reads and quantises the whole fp32 row in every
-// workgroup, so it prefers fewer, fuller workgroups: at 8 lanes per row it
-// takes 8 waves (64 rows) per workgroup where 4 waves would need more than
-// 320 workgroups (gate+up of a 2B FFN: 432 -> 216, 4.1 -> 4.0 us), except
-// with a row transform, where 4 waves measured faster (RMSNorm on gate+up
-// 5.35 -> 5.13 us).  Returns hipErrorNotSupported when M != 1 or K is too
-// large.  With `query` set, launches nothing and returns hipSuccess where it
-// would launch.
+// The configuration comes from dot4_config (decode_dot4_impl.hpp).  Returns
+// hipErrorNotSupported when M != 1 or K is too large.  With `query` set,
+// launches nothing and returns hipSuccess where it would launch.
 hipError_t launch_decode_dot4(const float *X, const int8_t *Xq, const float *xs, const int32_t *rs,
                               int64_t M, int64_t K, Pattern p, FusedProjArgs args, float *x_scale_out,
                               const ActTransform &tr, hipStream_t stream, const char **name, bool query)
 {
     if (M != 1 || K > dot4::kMaxK || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
-    const int64_t C = K / 64;
     const bool fused = (X != nullptr);
-    const int64_t umax = fused ? 7 : 5;
-    int lpr = 8;
-    while (lpr < 64 && (C + lpr - 1) / lpr > umax) lpr *= 2;
-    const int u = (int)((C + lpr - 1) / lpr);
-    auto count_blocks = [&](int64_t rb) {
-        int64_t b = 0;
-        for (int i = 0; i < args.nproj; ++i) b += (args.N[i] + rb - 1) / rb;
-        return b;
-    };
     const int trb = (tr.up ? kTrGate : 0) | (tr.gamma ? kTrNorm : 0);
-    const bool w8 = fused && lpr == 8 && count_blocks(4 * 8) > 320 && trb == 0;
-    const int64_t rb = (w8 ? 8 : 4) * (64 / lpr);
-    int64_t blocks = 0;
-    for (int i = 0; i < args.nproj; ++i) {
-        args.block_start[i] = (int32_t)blocks;
-        blocks += (args.N[i] + rb - 1) / rb;
-    }
-    for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
+    const Dot4Config cfg = dot4_config(K, fused, trb, args);
+    const int lpr = cfg.lpr, u = cfg.u;
+    const bool w8 = cfg.w8;
+    const int64_t blocks = dot4_block_starts(args, cfg.rb);
     if (blocks > (1LL << 30)) return hipErrorNotSupported;
     if (trb && !fused) return hipErrorNotSupported;
     Fn f = nullptr;

@@ -58,11 +58,14 @@ __device__ __forceinline__ int lanes_sum(int v)
 // unconditionally (a load under a branch makes the compiler wait for it at
 // the join); the host guarantees K <= 64 * U * LPR.  W waves per workgroup,
 // W * 64 / LPR rows.
+// `block` is the workgroup's index within this launch's share of the grid
+// (blockIdx.x for a launch of one input; the multi-input kernel passes the
+// index within its group).  Only threads below 64 * W may enter.
 template <Pattern P, int LPR, int U, bool FUSED, int W = 4, int TR = 0>
-__global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
+__device__ __forceinline__ void decode_dot4_body(
     const float *__restrict__ X, const int8_t *__restrict__ Xq, const float *__restrict__ x_scale,
-    const int32_t *__restrict__ x_rowsum, int64_t K, FusedProjArgs args, float *__restrict__ x_scale_out,
-    ActTransform tr)
+    const int32_t *__restrict__ x_rowsum, int64_t K, const FusedProjArgs &args, float *__restrict__ x_scale_out,
+    const ActTransform &tr, int block)
 {
     static_assert(TR == 0 || FUSED, "the row transform belongs to the fused form");
     constexpr bool GATE = (TR & kTrGate) != 0, NORM = (TR & kTrNorm) != 0;
@@ -77,10 +80,10 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
     int p = 0;
 #pragma unroll
     for (int i = 1; i < kMaxFusedProj; ++i)
-        if (i < args.nproj && (int)blockIdx.x >= args.block_start[i]) p = i;
+        if (i < args.nproj && block >= args.block_start[i]) p = i;
     const int64_t N = args.N[p];
     const uint8_t *packed = args.packed[p];
-    const int64_t row = (int64_t)(blockIdx.x - args.block_start[p]) * RB + wave * RPW + lane / LPR;
+    const int64_t row = (int64_t)(block - args.block_start[p]) * RB + wave * RPW + lane / LPR;
     const int j = lane % LPR;
     const int64_t C = K / 64;
     float *Y = args.Y[p];
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
             xg = g;
         } else {
             xsc = (g == 0.0f) ? 0.0f : g / 127.0f;
-            if (x_scale_out && blockIdx.x == 0 && tid == 0) x_scale_out[0] = xsc;
+            if (x_scale_out && block == 0 && tid == 0) x_scale_out[0] = xsc;
         }
     } else {
 #pragma unroll
@@ -277,7 +280,7 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
     acc = lanes_sum<LPR>(acc);
     if constexpr (NORM) {
         xsc = act_norm_scale(xg, act_rinv(ss, K, tr.eps));
-        if (x_scale_out && blockIdx.x == 0 && tid == 0) x_scale_out[0] = xsc;
+        if (x_scale_out && block == 0 && tid == 0) x_scale_out[0] = xsc;
     }
     if (j == 0 && row < N) {
         // dense codes are t + 1: subtract the activation row sum
@@ -287,7 +290,58 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
     }
 }
 
+template <Pattern P, int LPR, int U, bool FUSED, int W = 4, int TR = 0>
+__global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
+    const float *__restrict__ X, const int8_t *__restrict__ Xq, const float *__restrict__ x_scale,
+    const int32_t *__restrict__ x_rowsum, int64_t K, FusedProjArgs args, float *__restrict__ x_scale_out,
+    ActTransform tr)
+{
+    decode_dot4_body<P, LPR, U, FUSED, W, TR>(X, Xq, x_scale, x_rowsum, K, args, x_scale_out, tr, (int)blockIdx.x);
+}
+
 }  // namespace dot4
+
+// The host rule of the one-token kernel's configuration, for K and the
+// projections of one input group: lanes per row, the fewest of 8, 16, 32, 64
+// that keep a lane's chunks U <= 5, or <= 7 with the quantisation fused in
+// (<= 4 at 64 lanes, K <= 16384).  The fused kernel reads and quantises the
+// whole fp32 row in every workgroup, so it prefers fewer, fuller workgroups:
+// at 8 lanes per row it takes 8 waves (64 rows) per workgroup where 4 waves
+// would need more than 320 workgroups (gate+up of a 2B FFN: 432 -> 216,
+// 4.1 -> 4.0 us), except with a row transform (trb != 0), where 4 waves
+// measured faster (RMSNorm on gate+up 5.35 -> 5.13 us).
+struct Dot4Config {
+    int lpr;          // lanes per weight row
+    int u;            // chunks of 64 codes per lane
+    bool w8;          // 8 waves per workgroup (else 4)
+    int64_t rb;       // weight rows per workgroup
+};
+
+inline Dot4Config dot4_config(int64_t K, bool fused, int trb, const FusedProjArgs &args)
+{
+    const int64_t C = K / 64;
+    const int64_t umax = fused ? 7 : 5;
+    int lpr = 8;
+    while (lpr < 64 && (C + lpr - 1) / lpr > umax) lpr *= 2;
+    const int u = (int)((C + lpr - 1) / lpr);
+    int64_t b4 = 0;
+    for (int i = 0; i < args.nproj; ++i) b4 += (args.N[i] + 31) / 32;
+    const bool w8 = fused && lpr == 8 && b4 > 320 && trb == 0;
+    return Dot4Config{lpr, u, w8, (w8 ? 8 : 4) * (64 / lpr)};
+}
+
+// Fills args.block_start for rows of `rb` per workgroup; returns the
+// workgroup count.
+inline int64_t dot4_block_starts(FusedProjArgs &args, int64_t rb)
+{
+    int64_t blocks = 0;
+    for (int i = 0; i < args.nproj; ++i) {
+        args.block_start[i] = (int32_t)blocks;
+        blocks += (args.N[i] + rb - 1) / rb;
+    }
+    for (int i = args.nproj; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
+    return blocks;
+}
 
 using Dot4Fn = void (*)(dim3, size_t, hipStream_t, const float *, const int8_t *, const float *, const int32_t *,
                         int64_t, const FusedProjArgs &, float *, const ActTransform &);

@@ -1,0 +1,134 @@
+// One-token decode of several input groups in one launch: each group is an
+// fp32 activation row with the projections that read it (q/k/v; gate/up; a
+// down projection), and the grid holds every group's workgroups.  A
+// workgroup finds its group, then runs the one-token fused kernel's body
+// (decode_dot4_impl.hpp) in the configuration the host rule picks for that
+// group alone, so each group's outputs are bit for bit those of its own
+// bitlinear_forward_fused call: per-token absmax int8 quantisation ("BitNet
+// b1.58 2B4T Technical Report 요약 설명", sec. 2), the packed ternary weights
+// streamed from HBM and unpacked on chip (sec. 5.1), the integer linear and
+// the rescale ("BitNet 논문 분석: 1-Bit LLM의 시대", section "Absmean 양자화
+// 함수").
+//
+// Why: at one token a launch costs a fixed ~2 us (dispatch, the first HBM
+// round trip, the drain) on top of its bytes, about as much as streaming
+// 8 MB.  Groups whose inputs do not depend on one another (independent
+// sequences' layers, the down projections of several experts, the
+// projections of a step whose activations are given) need not pay it once
+// each.
+//
+// Workgroups are 512 threads; a group whose configuration has 4 waves runs
+// them in waves 0-3 and waves 4-7 end at once.  A barrier waits only for the
+// waves of the workgroup that have not ended, so the body's barriers are
+// those of its own launch.
+#include "decode_dot4_impl.hpp"
+
+namespace bl {
+namespace {
+
+thread_local char g_name[160];
+
+// The configurations of the menu, numbered: 8 waves at 8 lanes per row
+// (u = 1..7), then 4 waves at 8 lanes (u = 1..7), 16 and 32 lanes (u = 4..7),
+// 64 lanes (u = 4).  These are all the dense fused ones dot4_config can
+// pick.
+int menu_index(const Dot4Config &c)
+{
+    if (c.w8) return (c.lpr == 8 && c.u >= 1 && c.u <= 7) ? c.u - 1 : -1;
+    switch (c.lpr) {
+    case 8: return (c.u >= 1 && c.u <= 7) ? 7 + c.u - 1 : -1;
+    case 16: return (c.u >= 4 && c.u <= 7) ? 14 + c.u - 4 : -1;
+    case 32: return (c.u >= 4 && c.u <= 7) ? 18 + c.u - 4 : -1;
+    case 64: return c.u == 4 ? 22 : -1;
+    default: return -1;
+    }
+}
+
+}  // namespace
+
+namespace dot4 {
+
+#define BL_MULTI_CASE(ID, LPR, U, W)                                                                            \
+    case ID:                                                                                                    \
+        if (wave < (W))                                                                                         \
+            decode_dot4_body<Pattern::Dense, LPR, U, true, W, 0>(X, nullptr, nullptr, nullptr, K, a, xso, tr,  \
+                                                                 blk);                                          \
+        return;
+
+// The argument is read in place in the kernel-argument segment (it is the
+// launch's only argument, at offset 0): indexed by the group, a by-value
+// copy of it would live in scratch memory.
+__global__ __launch_bounds__(512) void decode_multi_kernel(MultiGroupArgs)
+{
+    const MultiGroupArgs &mg = *(const MultiGroupArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxInputGroups; ++i)
+        if (i < mg.ngroups && (int)blockIdx.x >= mg.group_start[i]) gi = i;
+    const int blk = (int)blockIdx.x - mg.group_start[gi];
+    const FusedProjArgs &a = mg.args[gi];
+    const float *X = mg.X[gi];
+    float *xso = mg.x_scale_out[gi];
+    const int64_t K = mg.K[gi];
+    const ActTransform tr{nullptr, nullptr, 0.0f};
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // uniform: a scalar branch
+    switch (mg.cfg[gi]) {
+        BL_MULTI_CASE(0, 8, 1, 8)
+        BL_MULTI_CASE(1, 8, 2, 8)
+        BL_MULTI_CASE(2, 8, 3, 8)
+        BL_MULTI_CASE(3, 8, 4, 8)
+        BL_MULTI_CASE(4, 8, 5, 8)
+        BL_MULTI_CASE(5, 8, 6, 8)
+        BL_MULTI_CASE(6, 8, 7, 8)
+        BL_MULTI_CASE(7, 8, 1, 4)
+        BL_MULTI_CASE(8, 8, 2, 4)
+        BL_MULTI_CASE(9, 8, 3, 4)
+        BL_MULTI_CASE(10, 8, 4, 4)
+        BL_MULTI_CASE(11, 8, 5, 4)
+        BL_MULTI_CASE(12, 8, 6, 4)
+        BL_MULTI_CASE(13, 8, 7, 4)
+        BL_MULTI_CASE(14, 16, 4, 4)
+        BL_MULTI_CASE(15, 16, 5, 4)
+        BL_MULTI_CASE(16, 16, 6, 4)
+        BL_MULTI_CASE(17, 16, 7, 4)
+        BL_MULTI_CASE(18, 32, 4, 4)
+        BL_MULTI_CASE(19, 32, 5, 4)
+        BL_MULTI_CASE(20, 32, 6, 4)
+        BL_MULTI_CASE(21, 32, 7, 4)
+        BL_MULTI_CASE(22, 64, 4, 4)
+    default: return;
+    }
+}
+
+#undef BL_MULTI_CASE
+
+}  // namespace dot4
+
+hipError_t launch_decode_multi(MultiGroupArgs mg, hipStream_t stream, const char **name, bool query)
+{
+    if (mg.ngroups < 1 || mg.ngroups > kMaxInputGroups) return hipErrorNotSupported;
+    int64_t blocks = 0, kmax = 0;
+    int len = snprintf(g_name, sizeof g_name, "fused_decode_multi_dense");
+    for (int g = 0; g < mg.ngroups; ++g) {
+        FusedProjArgs &a = mg.args[g];
+        if (mg.K[g] > dot4::kMaxK || a.nproj < 1 || a.nproj > kMaxFusedProj) return hipErrorNotSupported;
+        const Dot4Config c = dot4_config(mg.K[g], true, 0, a);
+        const int id = menu_index(c);
+        if (id < 0) return hipErrorNotSupported;
+        mg.cfg[g] = id;
+        mg.group_start[g] = (int32_t)blocks;
+        blocks += dot4_block_starts(a, c.rb);
+        if (blocks > (1LL << 30)) return hipErrorNotSupported;
+        if (mg.K[g] > kmax) kmax = mg.K[g];
+        if (len < (int)sizeof g_name)
+            len += snprintf(g_name + len, sizeof g_name - len, "%slpr%d_u%d_p%d%s", g ? "+" : "_", c.lpr, c.u,
+                            a.nproj, c.w8 ? "_w8" : "");
+    }
+    for (int g = mg.ngroups; g <= kMaxInputGroups; ++g) mg.group_start[g] = (int32_t)blocks;
+    *name = g_name;
+    if (query) return hipSuccess;
+    hipLaunchKernelGGL(dot4::decode_multi_kernel, dim3((unsigned)blocks), dim3(512), (size_t)kmax, stream, mg);
+    return hipGetLastError();
+}
+
+}  // namespace bl

@@ -46,6 +46,13 @@ hipError_t noalloc_scratch(hipStream_t stream, uint8_t **ptr);
 constexpr int64_t kSkinnyMaxM = 64;
 
 struct FusedProjArgs;                // skinny_impl.hpp
+struct MultiGroupArgs;               // skinny_impl.hpp
+
+// One-token fused decode of several input groups, dense weights, in one
+// launch (K <= 16384 per group); hipErrorNotSupported otherwise.  The host
+// fills X, x_scale_out, K, ngroups and each group's projections; the
+// launcher fills the rest.
+hipError_t launch_decode_multi(MultiGroupArgs mg, hipStream_t stream, const char **name, bool query);
 
 // The skinny MFMA forward with the weights read straight into the MFMA
 // operand (dense weights at 5-64 tokens, the shapes where it measured faster

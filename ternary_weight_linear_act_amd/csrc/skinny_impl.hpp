@@ -61,6 +61,22 @@ struct FusedProjArgs {
     int32_t nproj;
 };
 
+// Several input groups in one one-token launch (decode_multi.hip): group g
+// is the fp32 row X[g] of K[g] inputs with the projections args[g]; its
+// workgroups are [group_start[g], group_start[g + 1]) of the grid and run
+// configuration cfg[g] of the kernel's menu.
+constexpr int kMaxInputGroups = 4;
+
+struct MultiGroupArgs {
+    const float *X[kMaxInputGroups];
+    float *x_scale_out[kMaxInputGroups];
+    int64_t K[kMaxInputGroups];
+    int32_t cfg[kMaxInputGroups];
+    int32_t group_start[kMaxInputGroups + 1];
+    int32_t ngroups;
+    FusedProjArgs args[kMaxInputGroups];
+};
+
 // the projection of workgroup `block`
 __device__ __forceinline__ int proj_of_block(const FusedProjArgs &args, int block)
 {

@@ -329,6 +329,29 @@ def test_fused_validation(lib):
     assert f(None, 0, 128, NM(0, 0), arr, 1, None, None) == 0            # M = 0: no-op
 
 
+def test_fused_multi_validation(lib):
+    from ternary_weight_linear_act_amd.binding import NM, Proj, InputGroup
+    f = lib.bitlinear_forward_fused_multi
+    arr = (Proj * 9)(*[Proj(A, A, 64, A, None) for _ in range(9)])
+
+    def groups(*gs):
+        return (InputGroup * max(len(gs), 1))(*[InputGroup(x, k, a, n, xs) for (x, k, a, n, xs) in gs])
+    ok = (P(), 128, arr, 1, None)
+    assert f(None, 1, NM(0, 0), None) == -1                                   # groups NULL
+    assert f(groups(ok), 0, NM(0, 0), None) == -1                             # ngroups 0
+    assert f(groups(*[ok] * 5), 5, NM(0, 0), None) == -2                      # more than 4 groups
+    assert f(groups(ok), 1, NM(3, 4), None) == -2                             # unsupported N:M
+    assert f(groups(ok, (P(4), 128, arr, 1, None)), 2, NM(0, 0), None) == -1  # misaligned X
+    assert f(groups(ok, (P(), 100, arr, 1, None)), 2, NM(0, 0), None) == -1   # K not a multiple of 64
+    assert f(groups(ok, (P(), 65344 + 64, arr, 1, None)), 2, NM(0, 0), None) == -2   # K past one token's range
+    assert f(groups(ok, (P(), 128, None, 1, None)), 2, NM(0, 0), None) == -1  # projs NULL
+    assert f(groups(ok, (P(), 128, arr, 0, None)), 2, NM(0, 0), None) == -1   # nproj 0
+    assert f(groups(ok, (P(), 128, arr, 9, None)), 2, NM(0, 0), None) == -2   # too many projections
+    assert f(groups(ok, (P(), 128, arr, 1, P(2))), 2, NM(0, 0), None) == -1   # misaligned x_scale
+    bad = (Proj * 1)(Proj(A, A, 64, None, None))
+    assert f(groups(ok, (P(), 128, bad, 1, None)), 2, NM(0, 0), None) == -1   # Y NULL
+
+
 def test_trit24_sizes_and_validation(lib):
     # the trit-packed 2:4 layout: 12 bytes per 64 weights, as the oracle's
     # layout arithmetic counts them
