@@ -690,10 +690,52 @@ def bench_configs(torch, bl, workloads, dev, log, only=None):
                       "shared_quant_launches": sum(1 + (1 if grouped_ok[g] else len(g)) for g in fused_groups),
                       "shared_quant_groups": ["+".join(g) + (" quant_act+grouped" if grouped_ok[g] else
                                                              " quant_act+forward each") for g in fused_groups]})
+        if fused_groups and M > 1 and len(fused_groups) > 1:
+            # every input group quantised in one launch, then the grouped
+            # forward per group where one launch serves it, else the forward
+            # per projection
+            Xq_m = {g: torch.empty((M, shapes[g[0]][1]), dtype=torch.int8, device=dev) for g in fused_groups}
+            xs_m = {g: torch.empty(M, dtype=torch.float32, device=dev) for g in fused_groups}
+            rs_m = {g: torch.empty(M, dtype=torch.int32, device=dev) for g in fused_groups}
+            qgroups = [(X[g[0]], Xq_m[g], xs_m[g], rs_m[g]) for g in fused_groups]
+            bl.quant_act_multi(qgroups)
+            qk = bl.last_dispatch()
+            grouped_m = {}
+            for g in fused_groups:
+                try:
+                    bl.forward_grouped(Xq_m[g], xs_m[g], rs_m[g], [(pools[n][0], ws[n], shapes[n][0]) for n in g],
+                                       nm=nm_of(g[0]), Ys=[Y[n] for n in g])
+                    grouped_m[g] = len(g) > 1
+                except bl.BitLinearError:
+                    grouped_m[g] = False
+
+            def one_quant(j):
+                bl.quant_act_multi(qgroups)
+                for g in fused_groups:
+                    if grouped_m[g]:
+                        bl.forward_grouped(Xq_m[g], xs_m[g], rs_m[g], [(pools[n][j], ws[n], shapes[n][0]) for n in g],
+                                           nm=nm_of(g[0]), Ys=[Y[n] for n in g])
+                    else:
+                        for n in g:
+                            bl.forward(Xq_m[g], xs_m[g], rs_m[g], pools[n][j], ws[n], shapes[n][0], nm=nm_of(n),
+                                       Y=Y[n])
+            one_quant(0)
+            torch.cuda.synchronize()
+            for n in projs:
+                if not torch.equal(Y[n], Yref[n]):
+                    raise SystemExit("%s: one-quantisation and two-call outputs differ for %s" % (name, n))
+            ms, _ = timed_graph(torch, lambda: [one_quant(j % P) for j in range(G)], reps=2)
+            oq = ms * 1e3 / G
+            r.update({"one_quant_us": round(oq, 3), "one_quant_kernel": qk,
+                      "one_quant_launches": 1 + sum(1 if grouped_m[g] else len(g) for g in fused_groups),
+                      "one_quant_groups": ["+".join(g) + (" grouped" if grouped_m[g] else " forward each")
+                                           for g in fused_groups]})
         res[name] = r
-        log("%-28s M=%-4d two-call %8.2f us%s%s" % (name, M, us, (" fused %.2f us" % r["fused_us"]) if "fused_us" in r else "",
+        log("%-28s M=%-4d two-call %8.2f us%s%s%s" % (name, M, us, (" fused %.2f us" % r["fused_us"]) if "fused_us" in r else "",
                                                      (" shared quant %.2f us" % r["shared_quant_us"])
-                                                     if "shared_quant_us" in r else ""))
+                                                     if "shared_quant_us" in r else "",
+                                                     (" one quant %.2f us" % r["one_quant_us"])
+                                                     if "one_quant_us" in r else ""))
 
     dense = lambda n: (0, 0)
     case("single_1024/M1", "single_1024", ("linear",), 1, dense, [("linear",)])

@@ -321,6 +321,31 @@ bitlinear_status bitlinear_forward_grouped(const int8_t *Xq, const float *x_scal
                                            int64_t M, int64_t K, bitlinear_nm nm, const bitlinear_proj *projs,
                                            int32_t nproj, hipStream_t stream);
 
+/* One input of bitlinear_quant_act_multi: M x K fp32 rows X and their
+ * outputs, each as in bitlinear_quant_act (x_rowsum may be NULL). */
+typedef struct {
+    const float *X;
+    int64_t M;
+    int64_t K;
+    int8_t *Xq;
+    float *x_scale;
+    int32_t *x_rowsum;
+} bitlinear_quant_group;
+
+/* bitlinear_quant_act for several independent inputs in one launch (the
+ * inputs of a block's projection groups, each then fed to
+ * bitlinear_forward or bitlinear_forward_grouped): each group's outputs are
+ * bit-identical to its own bitlinear_quant_act call (2B4T summary, sec. 2;
+ * "BitNet 논문 분석", section "Absmean 양자화 함수").  `groups` is a host
+ * array of 1 <= ngroups <= 8 entries; no group's outputs may overlap another
+ * group's or any input.  One launch while every row fits the kernel's
+ * registers (K <= 16384 when the groups hold at most 512 rows in all and
+ * some K >= 4096, else K <= 8192); otherwise one bitlinear_quant_act launch
+ * per group, with the same results.  Errors: EINVAL for a bad group (as
+ * bitlinear_quant_act) or ngroups < 1, EUNSUPPORTED for ngroups > 8. */
+bitlinear_status bitlinear_quant_act_multi(const bitlinear_quant_group *groups, int32_t ngroups,
+                                           hipStream_t stream);
+
 /* Transform of each activation row before the absmax quantisation: the steps
  * either side of a BitNet linear, fused into the quantiser.
  *   up (ReLU^2 gate; "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 2:

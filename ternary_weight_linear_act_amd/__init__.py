@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     forward_trit24_workspace_size,
     quant_act,
     quant_act_ex,
+    quant_act_multi,
     quant_act_h4,
     quant_act_a48,
     combine_a48,

@@ -26,6 +26,7 @@ EXPORTED = (
     "bitlinear_pack_weights_masked",
     "bitlinear_quant_act",
     "bitlinear_quant_act_ex",
+    "bitlinear_quant_act_multi",
     "bitlinear_quant_act_h4",
     "bitlinear_quant_act_a48",
     "bitlinear_combine_a48",
@@ -62,6 +63,11 @@ class ActTransform(ctypes.Structure):
 class Proj(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("w_scale", ctypes.c_void_p), ("N", ctypes.c_int64),
                 ("Y", ctypes.c_void_p), ("acc", ctypes.c_void_p)]
+
+
+class QuantGroup(ctypes.Structure):
+    _fields_ = [("X", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("Xq", ctypes.c_void_p),
+                ("x_scale", ctypes.c_void_p), ("x_rowsum", ctypes.c_void_p)]
 
 
 class InputGroup(ctypes.Structure):
@@ -103,6 +109,7 @@ def load_library():
     lib.bitlinear_combine_a48.argtypes = [vp, i64, i64, vp, vp]
     lib.bitlinear_forward_fused_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, NM,
                                                ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
+    lib.bitlinear_quant_act_multi.argtypes = [ctypes.POINTER(QuantGroup), ctypes.c_int32, vp]
     lib.bitlinear_forward_fused_multi.argtypes = [ctypes.POINTER(InputGroup), ctypes.c_int32, NM, vp]
     lib.bitlinear_packed_size_trit24.argtypes = [i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.bitlinear_pack_weights_trit24.argtypes = [vp, i64, i64, vp, sz, vp, vp, sz, vp]
@@ -577,3 +584,21 @@ def forward_fused_multi(groups, nm=NM_DENSE, stream=None):
         garr[g] = InputGroup(_ptr(X), K, arr, len(projs), _ptr(x_scale))
     _check("bitlinear_forward_fused_multi", load_library().bitlinear_forward_fused_multi(
         garr, len(groups), _nm(nm), _stream(stream)))
+
+
+def quant_act_multi(groups, stream=None):
+    """quant_act for several independent inputs in one call: `groups` is a
+    list of (X, Xq, x_scale, x_rowsum) with X an M x K fp32 tensor and the
+    outputs preallocated (M x K int8, M fp32, M int32 or None)."""
+    import torch
+    arr = (QuantGroup * max(len(groups), 1))()
+    for g, (X, Xq, xs, rs) in enumerate(groups):
+        _require(X, torch.float32, None, "X")
+        M, K = X.shape
+        _require(Xq, torch.int8, (M, K), "Xq")
+        _require(xs, torch.float32, (M,), "x_scale")
+        if rs is not None:
+            _require(rs, torch.int32, (M,), "x_rowsum")
+        arr[g] = QuantGroup(_ptr(X), M, K, _ptr(Xq), _ptr(xs), _ptr(rs))
+    _check("bitlinear_quant_act_multi", load_library().bitlinear_quant_act_multi(arr, len(groups),
+                                                                                 _stream(stream)))

@@ -378,6 +378,47 @@ bitlinear_status bitlinear_quant_act_ex(const float *X, const bitlinear_act_tran
     return BITLINEAR_OK;
 }
 
+bitlinear_status bitlinear_quant_act_multi(const bitlinear_quant_group *groups, int32_t ngroups,
+                                           hipStream_t stream)
+{
+    if (!groups) return fail(BITLINEAR_EINVAL, "groups must not be NULL");
+    if (ngroups < 1) return fail(BITLINEAR_EINVAL, "ngroups = %d must be >= 1", ngroups);
+    if (ngroups > bl::kMaxQuantGroups)
+        return fail(BITLINEAR_EUNSUPPORTED, "ngroups = %d: at most %d input groups per call", ngroups,
+                    bl::kMaxQuantGroups);
+    bl::QuantGroupArgs qa = {};
+    for (int g = 0; g < ngroups; ++g) {
+        const bitlinear_quant_group &q = groups[g];
+        CHECK(check_m(q.M));
+        CHECK(check_k(q.K));
+        if (q.M > 0) {
+            CHECK(check_ptr(q.X, 16, "groups[g].X"));
+            CHECK(check_ptr(q.Xq, 16, "groups[g].Xq"));
+            CHECK(check_ptr(q.x_scale, 4, "groups[g].x_scale"));
+            if (q.x_rowsum && !aligned(q.x_rowsum, 4))
+                return fail(BITLINEAR_EINVAL, "groups[g].x_rowsum must be 4-byte aligned");
+        }
+        qa.X[g] = q.X;
+        qa.Xq[g] = q.Xq;
+        qa.x_scale[g] = q.x_scale;
+        qa.x_rowsum[g] = q.x_rowsum;
+        qa.M[g] = q.M;
+        qa.K[g] = q.K;
+    }
+    qa.ngroups = ngroups;
+    hipError_t e = bl::launch_quant_act_multi(qa, stream);
+    if (e == hipSuccess) { set_dispatch("quant_act_multi"); return BITLINEAR_OK; }
+    if (e != hipErrorNotSupported) return hip_fail("quant_act_multi launch", e);
+    // one launch per group
+    for (int g = 0; g < ngroups; ++g) {
+        if (qa.M[g] == 0) continue;
+        e = bl::launch_quant_act(qa.X[g], qa.M[g], qa.K[g], qa.Xq[g], qa.x_scale[g], qa.x_rowsum[g], stream);
+        if (e != hipSuccess) return hip_fail("quant_act launch", e);
+    }
+    set_dispatch("quant_act per group");
+    return BITLINEAR_OK;
+}
+
 bitlinear_status bitlinear_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t block, int8_t *Xq,
                                         float *x_scale, int32_t *x_rowsum, hipStream_t stream)
 {

@@ -30,11 +30,16 @@ thread_local char g_name[160];
 
 // The configurations of the menu, numbered: 8 waves at 8 lanes per row
 // (u = 1..7), then 4 waves at 8 lanes (u = 1..7), 16 and 32 lanes (u = 4..7),
-// 64 lanes (u = 4).  These are all the dense fused ones dot4_config can
-// pick.
-int menu_index(const Dot4Config &c)
+// 64 lanes (u = 4): all the dense fused ones dot4_config can pick; then
+// 4 lanes per row (u = 1..8) with 4, 6 or 8 waves.
+int menu_index(const Dot4Config &c, int waves)
 {
-    if (c.w8) return (c.lpr == 8 && c.u >= 1 && c.u <= 7) ? c.u - 1 : -1;
+    if (c.lpr == 4) {
+        const int wi = waves == 4 ? 0 : waves == 6 ? 1 : waves == 8 ? 2 : -1;
+        return (wi >= 0 && c.u >= 1 && c.u <= 8) ? 23 + 10 * wi + c.u - 1 : -1;
+    }
+    if (waves == 8) return (c.lpr == 8 && c.u >= 1 && c.u <= 7) ? c.u - 1 : -1;
+    if (waves != 4) return -1;
     switch (c.lpr) {
     case 8: return (c.u >= 1 && c.u <= 7) ? 7 + c.u - 1 : -1;
     case 16: return (c.u >= 4 && c.u <= 7) ? 14 + c.u - 4 : -1;
@@ -42,6 +47,34 @@ int menu_index(const Dot4Config &c)
     case 64: return c.u == 4 ? 22 : -1;
     default: return -1;
     }
+}
+
+// A group's configuration in the multi-input launch.  Rows of K <= 2048
+// (at most 32 chunks) take 4 lanes per row (16 rows per wave) and the fewest
+// of 4, 6 or 8 waves that keep the group within kMultiMaxBlocks workgroups:
+// every workgroup reads and quantises its group's whole input row, so fewer,
+// fuller workgroups cost less, while the chip still holds the other groups'
+// workgroups beside them.  Measured, one launch of the 3B block's four
+// groups: q/k/v, o, gate+up (K = 2048) on 4 lanes (40, 32, 172 workgroups)
+// against 8 lanes (80, 64, 344) 8.7 -> 8.1 us.  The 2B gate+up (K = 2560,
+// 10 chunks per lane on 4 lanes) measured slower that way (the step 6.8 ->
+// 8.9 us), so from 33 chunks the one-input rule (dot4_config) applies.
+constexpr int64_t kMultiMaxBlocks = 180;
+
+Dot4Config multi_config(int64_t K, const FusedProjArgs &args, int *waves)
+{
+    const int64_t C = K / 64;
+    if (C <= 32) {
+        int64_t rows16 = 0;
+        for (int i = 0; i < args.nproj; ++i) rows16 += (args.N[i] + 15) / 16;
+        int w = 4;
+        while (w < 8 && (rows16 + w - 1) / w > kMultiMaxBlocks) w += 2;
+        *waves = w;
+        return Dot4Config{4, (int)((C + 3) / 4), w == 8, (int64_t)w * 16};
+    }
+    const Dot4Config c = dot4_config(K, true, 0, args);
+    *waves = c.w8 ? 8 : 4;
+    return c;
 }
 
 }  // namespace
@@ -96,6 +129,30 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(MultiGroupArgs)
         BL_MULTI_CASE(20, 32, 6, 4)
         BL_MULTI_CASE(21, 32, 7, 4)
         BL_MULTI_CASE(22, 64, 4, 4)
+        BL_MULTI_CASE(23, 4, 1, 4)
+        BL_MULTI_CASE(24, 4, 2, 4)
+        BL_MULTI_CASE(25, 4, 3, 4)
+        BL_MULTI_CASE(26, 4, 4, 4)
+        BL_MULTI_CASE(27, 4, 5, 4)
+        BL_MULTI_CASE(28, 4, 6, 4)
+        BL_MULTI_CASE(29, 4, 7, 4)
+        BL_MULTI_CASE(30, 4, 8, 4)
+        BL_MULTI_CASE(33, 4, 1, 6)
+        BL_MULTI_CASE(34, 4, 2, 6)
+        BL_MULTI_CASE(35, 4, 3, 6)
+        BL_MULTI_CASE(36, 4, 4, 6)
+        BL_MULTI_CASE(37, 4, 5, 6)
+        BL_MULTI_CASE(38, 4, 6, 6)
+        BL_MULTI_CASE(39, 4, 7, 6)
+        BL_MULTI_CASE(40, 4, 8, 6)
+        BL_MULTI_CASE(43, 4, 1, 8)
+        BL_MULTI_CASE(44, 4, 2, 8)
+        BL_MULTI_CASE(45, 4, 3, 8)
+        BL_MULTI_CASE(46, 4, 4, 8)
+        BL_MULTI_CASE(47, 4, 5, 8)
+        BL_MULTI_CASE(48, 4, 6, 8)
+        BL_MULTI_CASE(49, 4, 7, 8)
+        BL_MULTI_CASE(50, 4, 8, 8)
     default: return;
     }
 }
@@ -112,8 +169,9 @@ hipError_t launch_decode_multi(MultiGroupArgs mg, hipStream_t stream, const char
     for (int g = 0; g < mg.ngroups; ++g) {
         FusedProjArgs &a = mg.args[g];
         if (mg.K[g] > dot4::kMaxK || a.nproj < 1 || a.nproj > kMaxFusedProj) return hipErrorNotSupported;
-        const Dot4Config c = dot4_config(mg.K[g], true, 0, a);
-        const int id = menu_index(c);
+        int waves = 4;
+        const Dot4Config c = multi_config(mg.K[g], a, &waves);
+        const int id = menu_index(c, waves);
         if (id < 0) return hipErrorNotSupported;
         mg.cfg[g] = id;
         mg.group_start[g] = (int32_t)blocks;
@@ -122,7 +180,7 @@ hipError_t launch_decode_multi(MultiGroupArgs mg, hipStream_t stream, const char
         if (mg.K[g] > kmax) kmax = mg.K[g];
         if (len < (int)sizeof g_name)
             len += snprintf(g_name + len, sizeof g_name - len, "%slpr%d_u%d_p%d%s", g ? "+" : "_", c.lpr, c.u,
-                            a.nproj, c.w8 ? "_w8" : "");
+                            a.nproj, waves == 4 ? "" : waves == 6 ? "_w6" : "_w8");
     }
     for (int g = mg.ngroups; g <= kMaxInputGroups; ++g) mg.group_start[g] = (int32_t)blocks;
     *name = g_name;

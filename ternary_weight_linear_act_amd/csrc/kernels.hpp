@@ -10,6 +10,25 @@ namespace bl {
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,
                             int32_t *x_rowsum, hipStream_t stream);
 
+// Several independent inputs in one launch (group g: M[g] rows of K[g]
+// inputs, outputs as launch_quant_act's); the launcher fills row_start.
+// hipErrorNotSupported when a row does not fit the registers (K > 16384 with
+// 1024 threads per row, K > 8192 with 256).
+constexpr int kMaxQuantGroups = 8;
+
+struct QuantGroupArgs {
+    const float *X[kMaxQuantGroups];
+    int8_t *Xq[kMaxQuantGroups];
+    float *x_scale[kMaxQuantGroups];
+    int32_t *x_rowsum[kMaxQuantGroups];
+    int64_t M[kMaxQuantGroups];
+    int64_t K[kMaxQuantGroups];
+    int64_t row_start[kMaxQuantGroups + 1];
+    int32_t ngroups;
+};
+
+hipError_t launch_quant_act_multi(QuantGroupArgs qa, hipStream_t stream);
+
 // The same on rows transformed first (ReLU^2 gate and/or RMSNorm; tr.up and
 // tr.gamma NULL for none).
 hipError_t launch_quant_act_ex(const float *X, ActTransform tr, int64_t M, int64_t K, int8_t *Xq,

@@ -117,14 +117,13 @@ __global__ __launch_bounds__(BLOCK) void quant_act_kernel(
 // two-pass form reads it again (from L2 if it is still there, else from the
 // Infinity Cache or HBM).  Same arithmetic, same results.
 template <int BLOCK, int NV>
-__global__ __launch_bounds__(BLOCK) void quant_act_reg_kernel(const float *__restrict__ X, int64_t K,
-                                                             int8_t *__restrict__ Xq, float *__restrict__ x_scale,
-                                                             int32_t *__restrict__ x_rowsum)
+__device__ __forceinline__ void quant_act_reg_body(const float *__restrict__ X, int64_t K,
+                                                   int8_t *__restrict__ Xq, float *__restrict__ x_scale,
+                                                   int32_t *__restrict__ x_rowsum, int64_t row)
 {
     constexpr int W = BLOCK / 64;
     __shared__ float s_max[W];
     __shared__ int s_sum[W];
-    const int64_t row = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const f32x4 *x4 = reinterpret_cast<const f32x4 *>(X + row * K);
     int *q4 = reinterpret_cast<int *>(Xq + row * K);
@@ -173,6 +172,32 @@ __global__ __launch_bounds__(BLOCK) void quant_act_reg_kernel(const float *__res
         x_scale[row] = (g == 0.0f) ? 0.0f : g / 127.0f;
         if (x_rowsum) x_rowsum[row] = total;
     }
+}
+
+template <int BLOCK, int NV>
+__global__ __launch_bounds__(BLOCK) void quant_act_reg_kernel(const float *__restrict__ X, int64_t K,
+                                                             int8_t *__restrict__ Xq, float *__restrict__ x_scale,
+                                                             int32_t *__restrict__ x_rowsum)
+{
+    quant_act_reg_body<BLOCK, NV>(X, K, Xq, x_scale, x_rowsum, blockIdx.x);
+}
+
+// Several independent inputs quantised in one launch: group g's rows are
+// workgroups [row_start[g], row_start[g + 1]), each quantised exactly as
+// quant_act_reg_kernel does (the row's maximum is exact, codes and row sums
+// are integers: the thread count does not change a bit).  The argument is
+// read in place in the kernel-argument segment (indexed by the group, a copy
+// would live in scratch memory).
+template <int BLOCK, int NV>
+__global__ __launch_bounds__(BLOCK) void quant_act_multi_kernel(QuantGroupArgs)
+{
+    const QuantGroupArgs &qa = *(const QuantGroupArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxQuantGroups; ++i)
+        if (i < qa.ngroups && (int64_t)blockIdx.x >= qa.row_start[i]) gi = i;
+    quant_act_reg_body<BLOCK, NV>(qa.X[gi], qa.K[gi], qa.Xq[gi], qa.x_scale[gi], qa.x_rowsum[gi],
+                                  (int64_t)blockIdx.x - qa.row_start[gi]);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,6 +795,41 @@ hipError_t launch_quant_act_h4(const float *X, int64_t M, int64_t K, int64_t B, 
     hipLaunchKernelGGL(quant_act_h4_kernel, dim3((unsigned)M), dim3(kQuantBlock), 0, stream, X, K, B, Xq, x_scale,
                        x_rowsum);
     return hipGetLastError();
+}
+
+hipError_t launch_quant_act_multi(QuantGroupArgs qa, hipStream_t stream)
+{
+    if (qa.ngroups < 1 || qa.ngroups > kMaxQuantGroups) return hipErrorNotSupported;
+    int64_t rows = 0, n4max = 0;
+    for (int g = 0; g < qa.ngroups; ++g) {
+        qa.row_start[g] = rows;
+        rows += qa.M[g];
+        if (qa.K[g] / 4 > n4max) n4max = qa.K[g] / 4;
+    }
+    for (int g = qa.ngroups; g <= kMaxQuantGroups; ++g) qa.row_start[g] = rows;
+    if (rows == 0) return hipSuccess;
+    if (rows > (1LL << 31) - 1) return hipErrorNotSupported;
+    // the single-input rule: 1024 threads per row for up to a few hundred
+    // long rows, else 256; the row in registers (at most 4 or 8 float4 per
+    // thread)
+    const bool wide = rows <= 512 && n4max >= 1024;
+    const int threads = wide ? 1024 : kQuantBlock;
+    const int64_t nv = (n4max + threads - 1) / threads;
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)rows), dim3(threads), 0, stream, qa);
+        return hipGetLastError();
+    };
+    if (wide) {
+        if (nv <= 1) return go(quant_act_multi_kernel<1024, 1>);
+        if (nv <= 2) return go(quant_act_multi_kernel<1024, 2>);
+        if (nv <= 4) return go(quant_act_multi_kernel<1024, 4>);
+    } else {
+        if (nv <= 1) return go(quant_act_multi_kernel<kQuantBlock, 1>);
+        if (nv <= 2) return go(quant_act_multi_kernel<kQuantBlock, 2>);
+        if (nv <= 4) return go(quant_act_multi_kernel<kQuantBlock, 4>);
+        if (nv <= 8) return go(quant_act_multi_kernel<kQuantBlock, 8>);
+    }
+    return hipErrorNotSupported;
 }
 
 hipError_t launch_quant_act(const float *X, int64_t M, int64_t K, int8_t *Xq, float *x_scale,

@@ -352,6 +352,24 @@ def test_fused_multi_validation(lib):
     assert f(groups(ok, (P(), 128, bad, 1, None)), 2, NM(0, 0), None) == -1   # Y NULL
 
 
+def test_quant_multi_validation(lib):
+    from ternary_weight_linear_act_amd.binding import QuantGroup
+    f = lib.bitlinear_quant_act_multi
+
+    def groups(*gs):
+        return (QuantGroup * max(len(gs), 1))(*[QuantGroup(*g) for g in gs])
+    ok = (P(), 2, 128, P(), P(), P())
+    assert f(None, 1, None) == -1                                             # groups NULL
+    assert f(groups(ok), 0, None) == -1                                       # ngroups 0
+    assert f(groups(*[ok] * 9), 9, None) == -2                                # more than 8 groups
+    assert f(groups(ok, (P(4), 2, 128, P(), P(), P())), 2, None) == -1        # misaligned X
+    assert f(groups(ok, (P(), 2, 100, P(), P(), P())), 2, None) == -1         # K not a multiple of 64
+    assert f(groups(ok, (P(), -1, 128, P(), P(), P())), 2, None) == -1        # negative M
+    assert f(groups(ok, (P(), 2, 128, None, P(), P())), 2, None) == -1        # Xq NULL
+    assert f(groups(ok, (P(), 2, 128, P(), P(2), P())), 2, None) == -1        # misaligned x_scale
+    assert f(groups(ok, (P(), 2, 128, P(), P(), P(2))), 2, None) == -1        # misaligned x_rowsum
+
+
 def test_trit24_sizes_and_validation(lib):
     # the trit-packed 2:4 layout: 12 bytes per 64 weights, as the oracle's
     # layout arithmetic counts them

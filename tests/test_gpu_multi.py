@@ -95,17 +95,20 @@ def test_block_3b_m1_one_launch():
     check_same_as_single(call, out, (0, 0))
 
 
-# K values that reach every lanes-per-row class of the menu: 8 lanes with
-# 1-7 chunks (64, 320: 1; 1024: 2; 1536: 3; 2048: 4 in the block above;
-# 2560: 5; 3072: 6; 3584: 7); 16 lanes (4160: 5 chunks; 6912: 7 above);
-# 32 lanes (8192: 4; 12288: 6); 64 lanes (16384); 10300 rows at K = 320 and
-# 2 x 6912 rows at K = 2560 take the 8-wave form
+# K values that reach every class of the kernel's menu: 4 lanes per row for
+# K <= 2048 (64, 256: 1 chunk per lane; 320: 2; 640: 3; 1024: 4; 1280: 5;
+# 1536: 6; 1792: 7; 2048: 8 in the block above), with 6 waves for 13000 rows
+# of 1024 and 8 for the 3B gate+up; past that the one-input rule: 8 lanes
+# (2304, 2560: 5 chunks; 3072: 6; 3584: 7; 8 waves for 2 x 6912 and 10300
+# rows), 16 lanes (4160: 5; 6912: 7 above), 32 lanes (8192: 4; 12288: 6;
+# 11008 above), 64 lanes (16384)
 MULTI_CASES = [
     [(64, (1,)), (320, (37, 129)), (1536, (300,))],
     [(3584, (16, 17)), (4160, (48,)), (8192, (77, 5))],
     [(12288, (33,)), (16384, (21,)), (1024, (256, 17, 300)), (3072, (64,))],
-    [(320, (10300,)), (4160, (100,))],
+    [(1024, (13000,)), (2304, (10300,)), (4160, (100,))],     # 4 lanes x 6 waves; 8 lanes x 8 waves
     [(2560, (6912, 6912))],
+    [(640, (50,)), (1280, (33, 9)), (1792, (70,)), (2304, (129,))],
 ]
 
 
