@@ -164,8 +164,9 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(MultiGroupArgs)
 // The groups take the grid in order of decreasing K (stable): the deepest
 // rows' workgroups, which read the longest input rows, get compute units of
 // their own first, and the shallower groups' workgroups fill in beside them.
-// Measured against the callers' order (gate+up first): the 2B decode step
-// 6.41 -> 6.04 us, the 3B block at one token 7.9 -> 7.2 us.
+// Measured against the callers' order, inputs and weights rotating through
+// a 2 GiB pool: the 3B block at one token 8.7 -> 7.9 us; the 2B decode step
+// (two groups) 6.85 against 6.93 us, level within the runs' spread.
 void order_by_depth(MultiGroupArgs &mg)
 {
     MultiGroupArgs in = mg;
