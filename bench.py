@@ -730,12 +730,31 @@ def bench_configs(torch, bl, workloads, dev, log, only=None):
                       "one_quant_launches": 1 + sum(1 if grouped_m[g] else len(g) for g in fused_groups),
                       "one_quant_groups": ["+".join(g) + (" grouped" if grouped_m[g] else " forward each")
                                            for g in fused_groups]})
+            if 5 <= M <= 8 and all(nm_of(n) == (0, 0) for n in projs) and not masked:
+                # and every group's forward in one launch: two launches a step
+                fgroups = [[(Xq_m[g], xs_m[g], rs_m[g], [(pools[n][j], ws[n], shapes[n][0]) for n in g],
+                             [Y[n] for n in g], None) for g in fused_groups] for j in range(P)]
+                bl.quant_act_multi(qgroups)
+                bl.forward_grouped_multi(fgroups[0])
+                fk = bl.last_dispatch()
+                torch.cuda.synchronize()
+                for n in projs:
+                    if not torch.equal(Y[n], Yref[n]):
+                        raise SystemExit("%s: two-launch and two-call outputs differ for %s" % (name, n))
+
+                def two_launch(j):
+                    bl.quant_act_multi(qgroups)
+                    bl.forward_grouped_multi(fgroups[j])
+                ms, _ = timed_graph(torch, lambda: [two_launch(j % P) for j in range(G)], reps=2)
+                tl = ms * 1e3 / G
+                r.update({"two_launch_us": round(tl, 3), "two_launch_kernels": [qk, fk]})
         res[name] = r
         log("%-28s M=%-4d two-call %8.2f us%s%s%s" % (name, M, us, (" fused %.2f us" % r["fused_us"]) if "fused_us" in r else "",
                                                      (" shared quant %.2f us" % r["shared_quant_us"])
                                                      if "shared_quant_us" in r else "",
                                                      (" one quant %.2f us" % r["one_quant_us"])
-                                                     if "one_quant_us" in r else ""))
+                                                     if "one_quant_us" in r else "") +
+            ((" two launches %.2f us" % r["two_launch_us"]) if "two_launch_us" in r else ""))
 
     dense = lambda n: (0, 0)
     case("single_1024/M1", "single_1024", ("linear",), 1, dense, [("linear",)])

@@ -346,6 +346,34 @@ typedef struct {
 bitlinear_status bitlinear_quant_act_multi(const bitlinear_quant_group *groups, int32_t ngroups,
                                            hipStream_t stream);
 
+/* One quantised input of bitlinear_forward_grouped_multi: Xq, x_scale,
+ * x_rowsum as written by bitlinear_quant_act (M x K), and the nproj
+ * projections that read it (a host array, as for bitlinear_forward_grouped). */
+typedef struct {
+    const int8_t *Xq;
+    const float *x_scale;
+    const int32_t *x_rowsum;
+    int64_t K;
+    const bitlinear_proj *projs;
+    int32_t nproj;
+} bitlinear_act_group;
+
+/* bitlinear_forward_grouped for several quantised inputs in one launch (the
+ * projection groups of a block at a few tokens, quantised together by
+ * bitlinear_quant_act_multi): each projection's acc and Y bit-identical to
+ * its own bitlinear_forward (2B4T summary, sec. 2 and 5.1; "BitNet 논문
+ * 분석", section "Absmean 양자화 함수"; the Sparse-BitNet review's Table 5
+ * discussion: decode gains are diluted by launch overhead at small batches).
+ * `groups` is a host array of 1 <= ngroups <= 4 entries; no output may
+ * overlap another output or any input.  Supported: dense weights
+ * (nm = {0, 0}), 5 <= M <= 8, every K in [256, 12288], up to 8 projections
+ * per group; anything else returns BITLINEAR_EUNSUPPORTED and launches
+ * nothing (call bitlinear_forward_grouped or bitlinear_forward per group
+ * then).  Needs no workspace.  Errors: EINVAL for a bad group (as
+ * bitlinear_forward_grouped) or ngroups < 1. */
+bitlinear_status bitlinear_forward_grouped_multi(const bitlinear_act_group *groups, int32_t ngroups, int64_t M,
+                                                 bitlinear_nm nm, hipStream_t stream);
+
 /* Transform of each activation row before the absmax quantisation: the steps
  * either side of a BitNet linear, fused into the quantiser.
  *   up (ReLU^2 gate; "BitNet b1.58 2B4T Technical Report 요약 설명", sec. 2:

@@ -29,6 +29,7 @@ from .binding import (  # noqa: F401
     forward_noalloc,
     forward_fused,
     forward_grouped,
+    forward_grouped_multi,
     forward_fused_ex,
     forward_fused_multi,
     last_dispatch,

@@ -37,6 +37,7 @@ EXPORTED = (
     "bitlinear_forward_fused",
     "bitlinear_forward_fused_ex",
     "bitlinear_forward_fused_multi",
+    "bitlinear_forward_grouped_multi",
     "bitlinear_packed_size_trit24",
     "bitlinear_pack_weights_trit24",
     "bitlinear_forward_trit24_workspace_size",
@@ -68,6 +69,11 @@ class Proj(ctypes.Structure):
 class QuantGroup(ctypes.Structure):
     _fields_ = [("X", ctypes.c_void_p), ("M", ctypes.c_int64), ("K", ctypes.c_int64), ("Xq", ctypes.c_void_p),
                 ("x_scale", ctypes.c_void_p), ("x_rowsum", ctypes.c_void_p)]
+
+
+class ActGroup(ctypes.Structure):
+    _fields_ = [("Xq", ctypes.c_void_p), ("x_scale", ctypes.c_void_p), ("x_rowsum", ctypes.c_void_p),
+                ("K", ctypes.c_int64), ("projs", ctypes.POINTER(Proj)), ("nproj", ctypes.c_int32)]
 
 
 class InputGroup(ctypes.Structure):
@@ -110,6 +116,8 @@ def load_library():
     lib.bitlinear_forward_fused_ex.argtypes = [vp, ctypes.POINTER(ActTransform), i64, i64, NM,
                                                ctypes.POINTER(Proj), ctypes.c_int32, vp, vp]
     lib.bitlinear_quant_act_multi.argtypes = [ctypes.POINTER(QuantGroup), ctypes.c_int32, vp]
+    lib.bitlinear_forward_grouped_multi.argtypes = [ctypes.POINTER(ActGroup), ctypes.c_int32, ctypes.c_int64, NM,
+                                                    vp]
     lib.bitlinear_forward_fused_multi.argtypes = [ctypes.POINTER(InputGroup), ctypes.c_int32, NM, vp]
     lib.bitlinear_packed_size_trit24.argtypes = [i64, i64, ctypes.POINTER(sz), ctypes.POINTER(sz)]
     lib.bitlinear_pack_weights_trit24.argtypes = [vp, i64, i64, vp, sz, vp, vp, sz, vp]
@@ -602,3 +610,37 @@ def quant_act_multi(groups, stream=None):
         arr[g] = QuantGroup(_ptr(X), M, K, _ptr(Xq), _ptr(xs), _ptr(rs))
     _check("bitlinear_quant_act_multi", load_library().bitlinear_quant_act_multi(arr, len(groups),
                                                                                  _stream(stream)))
+
+
+def forward_grouped_multi(groups, nm=NM_DENSE, stream=None):
+    """forward_grouped for several quantised inputs in one call: `groups` is a
+    list of (Xq, x_scale, x_rowsum, projs, Ys, accs) with Xq an M x K int8
+    tensor (M the same for every group), projs a list of (packed, w_scale, N)
+    reading it, Ys their M x N fp32 outputs and accs None or their M x N
+    int32 accumulators."""
+    import torch
+    keep = []
+    garr = (ActGroup * max(len(groups), 1))()
+    M = None
+    for g, (Xq, xs, rs, projs, Ys, accs) in enumerate(groups):
+        _require(Xq, torch.int8, None, "Xq")
+        m, K = Xq.shape
+        if M is None:
+            M = m
+        elif m != M:
+            raise ValueError("every group of forward_grouped_multi has the same token count (%d, %d)" % (M, m))
+        _require(xs, torch.float32, (M,), "x_scale")
+        _require(rs, torch.int32, (M,), "x_rowsum")
+        arr = (Proj * max(len(projs), 1))()
+        for i, (packed, ws, N) in enumerate(projs):
+            _require(packed, torch.uint8, None, "packed")
+            _require(ws, torch.float32, (1,), "w_scale")
+            _require(Ys[i], torch.float32, (M, N), "Y")
+            if accs is not None:
+                _require(accs[i], torch.int32, (M, N), "acc")
+            arr[i] = Proj(packed.data_ptr(), ws.data_ptr(), N, Ys[i].data_ptr(),
+                          accs[i].data_ptr() if accs is not None else None)
+        keep.append(arr)
+        garr[g] = ActGroup(_ptr(Xq), _ptr(xs), _ptr(rs), K, arr, len(projs))
+    _check("bitlinear_forward_grouped_multi", load_library().bitlinear_forward_grouped_multi(
+        garr, len(groups), M or 0, _nm(nm), _stream(stream)))

@@ -721,6 +721,47 @@ bitlinear_status bitlinear_forward_fused_multi(const bitlinear_input_group *grou
     return BITLINEAR_OK;
 }
 
+bitlinear_status bitlinear_forward_grouped_multi(const bitlinear_act_group *groups, int32_t ngroups, int64_t M,
+                                                 bitlinear_nm nm, hipStream_t stream)
+{
+    bl::Pattern p;
+    CHECK(check_nm(nm, &p));
+    CHECK(check_m(M));
+    if (!groups) return fail(BITLINEAR_EINVAL, "groups must not be NULL");
+    if (ngroups < 1) return fail(BITLINEAR_EINVAL, "ngroups = %d must be >= 1", ngroups);
+    if (ngroups > bl::kMaxInputGroups)
+        return fail(BITLINEAR_EUNSUPPORTED, "ngroups = %d: at most %d input groups per call", ngroups,
+                    bl::kMaxInputGroups);
+    bl::DirectMultiArgs da = {};
+    da.ngroups = ngroups;
+    da.M = M;
+    for (int g = 0; g < ngroups; ++g) {
+        const bitlinear_act_group &a = groups[g];
+        CHECK(check_k(a.K));
+        CHECK(check_projs(a.projs, a.nproj, M, &da.args[g]));
+        if (M > 0) {
+            CHECK(check_ptr(a.Xq, 16, "groups[g].Xq"));
+            CHECK(check_ptr(a.x_scale, 4, "groups[g].x_scale"));
+            CHECK(check_ptr(a.x_rowsum, 4, "groups[g].x_rowsum"));
+        }
+        da.Xq[g] = a.Xq;
+        da.x_scale[g] = a.x_scale;
+        da.x_rowsum[g] = a.x_rowsum;
+        da.K[g] = a.K;
+    }
+    if (M == 0) { set_dispatch("none"); return BITLINEAR_OK; }
+    if (p != bl::Pattern::Dense)
+        return fail(BITLINEAR_EUNSUPPORTED, "the multi-input grouped forward takes dense weights (nm = {0, 0})");
+    const char *name = "";
+    const hipError_t e = bl::launch_skinny_direct_multi(da, stream, &name, false);
+    if (e == hipErrorNotSupported)
+        return fail(BITLINEAR_EUNSUPPORTED, "the multi-input grouped forward supports 5 <= M <= 8 and "
+                    "256 <= K <= 12288 (M = %lld)", (long long)M);
+    if (e != hipSuccess) return hip_fail("multi-input grouped forward launch", e);
+    set_dispatch(name);
+    return BITLINEAR_OK;
+}
+
 const char *bitlinear_last_error(void) { return g_error; }
 
 const char *bitlinear_last_dispatch(void) { return g_dispatch; }

@@ -66,6 +66,13 @@ constexpr int64_t kSkinnyMaxM = 64;
 
 struct FusedProjArgs;                // skinny_impl.hpp
 struct MultiGroupArgs;               // skinny_impl.hpp
+struct DirectMultiArgs;              // skinny_impl.hpp
+
+// Several quantised inputs at 5-8 tokens, dense weights, in one launch of the
+// direct-load skinny kernel (every group 256 <= K <= 12288);
+// hipErrorNotSupported otherwise.  The host fills Xq, x_scale, x_rowsum, K,
+// M, ngroups and each group's projections; the launcher fills the rest.
+hipError_t launch_skinny_direct_multi(DirectMultiArgs da, hipStream_t stream, const char **name, bool query);
 
 // One-token fused decode of several input groups, dense weights, in one
 // launch (K <= 16384 per group); hipErrorNotSupported otherwise.  The host

@@ -53,27 +53,29 @@ struct Lds {
 // Dense weights only.  1 <= M - 16 y <= MT tokens per tile (tiles of 16
 // along y when M > 16, then MT == 16); the host keeps KS <= K / 64 and
 // K / 64 <= KS * CMAX.
+// `bx`, `by`: the workgroup's column block (within this launch's share of the
+// grid) and token tile; `smem`: Lds<KS, CMAX, MT, RG>::kBytes of LDS.  Only
+// waves below KS may enter.
 template <int KS, int CMAX, int MT, int RG>
-__global__ __launch_bounds__(64 * KS) void skinny_direct_kernel(const int8_t *__restrict__ Xq,
-                                                                const float *__restrict__ x_scale,
-                                                                const int32_t *__restrict__ x_rowsum,
-                                                                FusedProjArgs args, int64_t M, int64_t K)
+__device__ __forceinline__ void skinny_direct_body(const int8_t *__restrict__ Xq, const float *__restrict__ x_scale,
+                                                   const int32_t *__restrict__ x_rowsum, const FusedProjArgs &args,
+                                                   int64_t M, int64_t K, int bx, int by, uint8_t *smem)
 {
     static_assert(CMAX % 4 == 0 && MT >= 1 && MT <= 16, "config");
     using L = Lds<KS, CMAX, MT, RG>;
     constexpr int SMAX = CMAX / 4;                                 // 256-wide steps per wave
     constexpr int XLOADS = (MT * CMAX * 4 + 63) / 64;
-    __shared__ __attribute__((aligned(16))) uint8_t s_x[KS][L::kWave];
-    __shared__ i32x4 s_part[KS > 1 ? KS - 1 : 1][RG][64];
+    auto s_x = reinterpret_cast<uint8_t (*)[L::kWave]>(smem);                       // [KS][kWave]
+    auto s_part = reinterpret_cast<i32x4 (*)[RG][64]>(smem + KS * L::kWave);        // [KS - 1][RG][64]
 
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
-    const int p = proj_of_block(args, (int)blockIdx.x);
+    const int p = proj_of_block(args, bx);
     const int64_t N = args.N[p];
     const uint8_t *packed = args.packed[p];
     const float *w_scale = args.w_scale[p];
-    const int64_t n0 = (int64_t)(blockIdx.x - args.block_start[p]) * 16 * RG;
-    const int64_t t0 = (int64_t)blockIdx.y * 16;                   // token tile
+    const int64_t n0 = (int64_t)(bx - args.block_start[p]) * 16 * RG;
+    const int64_t t0 = (int64_t)by * 16;                           // token tile
     Xq += t0 * K;
     x_scale += t0;
     x_rowsum += t0;
@@ -202,6 +204,49 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_kernel(const int8_t *__
     }
 }
 
+template <int KS, int CMAX, int MT, int RG>
+__global__ __launch_bounds__(64 * KS) void skinny_direct_kernel(const int8_t *__restrict__ Xq,
+                                                                const float *__restrict__ x_scale,
+                                                                const int32_t *__restrict__ x_rowsum,
+                                                                FusedProjArgs args, int64_t M, int64_t K)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    skinny_direct_body<KS, CMAX, MT, RG>(Xq, x_scale, x_rowsum, args, M, K, (int)blockIdx.x, (int)blockIdx.y, smem);
+}
+
+// Several inputs in one launch (workgroups of 512 threads: a configuration
+// with KS waves runs them in waves 0 .. KS - 1, the others end at once; a
+// barrier waits only for the waves that have not ended).  The argument is
+// read in place in the kernel-argument segment (indexed by the group, a copy
+// would live in scratch memory).
+#define BL_DIRECT_CASE(ID, KS, CMAX, MT, RG)                                                                    \
+    case ID:                                                                                                    \
+        if (wave < (KS))                                                                                        \
+            skinny_direct_body<KS, CMAX, MT, RG>(da.Xq[gi], da.x_scale[gi], da.x_rowsum[gi], da.args[gi], da.M, \
+                                                 da.K[gi], blk, 0, smem);                                       \
+        return;
+
+__global__ __launch_bounds__(512) void skinny_direct_multi_kernel(DirectMultiArgs)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const DirectMultiArgs &da = *(const DirectMultiArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxInputGroups; ++i)
+        if (i < da.ngroups && (int)blockIdx.x >= da.group_start[i]) gi = i;
+    const int blk = (int)blockIdx.x - da.group_start[gi];
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    switch (da.cfg[gi]) {
+        BL_DIRECT_CASE(0, 4, 8, 8, 1)
+        BL_DIRECT_CASE(1, 4, 8, 8, 2)
+        BL_DIRECT_CASE(2, 2, 20, 8, 1)
+        BL_DIRECT_CASE(3, 8, 24, 8, 1)
+    default: return;
+    }
+}
+
+#undef BL_DIRECT_CASE
+
 }  // namespace skinny_direct
 
 namespace {
@@ -227,9 +272,15 @@ hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, FusedPro
              args.nproj > 1 ? "_grouped" : "");
     *name = g_name;
     if (query) return hipSuccess;
-    hipLaunchKernelGGL((skinny_direct::skinny_direct_kernel<KS, CMAX, MT, RG>),
-                       dim3((unsigned)blocks, (unsigned)((M + 15) / 16)), dim3(64 * KS), 0, stream, Xq, xs, rs, args,
-                       M, K);
+    auto kern = skinny_direct::skinny_direct_kernel<KS, CMAX, MT, RG>;
+    constexpr size_t lds = skinny_direct::Lds<KS, CMAX, MT, RG>::kBytes;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks, (unsigned)((M + 15) / 16)), dim3(64 * KS), lds, stream, Xq, xs,
+                       rs, args, M, K);
     return hipGetLastError();
 }
 
@@ -254,6 +305,80 @@ hipError_t launch_skinny_direct(const int8_t *Xq, const float *xs, const int32_t
     if (M >= 17 && M <= kSkinnyMaxM && args.nproj >= 2 && C >= 8 && C <= 32)
         return launch<4, 8, 16, 1>(Xq, xs, rs, args, M, K, stream, name, query);
     return hipErrorNotSupported;
+}
+
+// The multi-input launch at 5-8 tokens.  Each group's configuration (KS
+// waves splitting K, CMAX chunks per wave, RG blocks of 16 weight rows per
+// wave): K <= 2048 (at most 32 chunks) KS = 4, RG = 2 from 8192 rows in all
+// (the single-input rule's), else RG = 1; 33-40 chunks KS = 2 (the
+// single-input rule's); 41-192 chunks KS = 8 (the single-input rule's from
+// 129 chunks).  Groups take the grid in order of decreasing K, as in the
+// one-token multi-input launch.
+hipError_t launch_skinny_direct_multi(DirectMultiArgs da, hipStream_t stream, const char **name, bool query)
+{
+    thread_local char g_mname[160];
+    if (da.ngroups < 1 || da.ngroups > kMaxInputGroups || da.M < 5 || da.M > 8) return hipErrorNotSupported;
+    {
+        // decreasing K, stable
+        DirectMultiArgs in = da;
+        int order[kMaxInputGroups];
+        for (int g = 0; g < da.ngroups; ++g) order[g] = g;
+        for (int i = 1; i < da.ngroups; ++i)
+            for (int j = i; j > 0 && in.K[order[j]] > in.K[order[j - 1]]; --j) {
+                const int t = order[j];
+                order[j] = order[j - 1];
+                order[j - 1] = t;
+            }
+        for (int g = 0; g < da.ngroups; ++g) {
+            const int o = order[g];
+            da.Xq[g] = in.Xq[o];
+            da.x_scale[g] = in.x_scale[o];
+            da.x_rowsum[g] = in.x_rowsum[o];
+            da.K[g] = in.K[o];
+            da.args[g] = in.args[o];
+        }
+    }
+    static const int kKS[4] = {4, 4, 2, 8}, kRG[4] = {1, 2, 1, 1};
+    static const size_t kLds[4] = {skinny_direct::Lds<4, 8, 8, 1>::kBytes, skinny_direct::Lds<4, 8, 8, 2>::kBytes,
+                                   skinny_direct::Lds<2, 20, 8, 1>::kBytes, skinny_direct::Lds<8, 24, 8, 1>::kBytes};
+    int64_t blocks = 0;
+    size_t lds = 0;
+    int len = snprintf(g_mname, sizeof g_mname, "skinny_direct_multi_dense");
+    for (int g = 0; g < da.ngroups; ++g) {
+        FusedProjArgs &a = da.args[g];
+        if (a.nproj < 1 || a.nproj > kMaxFusedProj) return hipErrorNotSupported;
+        const int64_t C = da.K[g] / 64;
+        int64_t rows = 0;
+        for (int i = 0; i < a.nproj; ++i) rows += a.N[i];
+        int cfg;
+        if (C >= 4 && C <= 32) cfg = rows >= 8192 ? 1 : 0;
+        else if (C >= 33 && C <= 40) cfg = 2;
+        else if (C >= 41 && C <= 192) cfg = 3;
+        else return hipErrorNotSupported;
+        da.cfg[g] = cfg;
+        da.group_start[g] = (int32_t)blocks;
+        for (int i = 0; i < a.nproj; ++i) {
+            a.block_start[i] = (int32_t)(blocks - da.group_start[g]);
+            blocks += (a.N[i] + 16 * kRG[cfg] - 1) / (16 * kRG[cfg]);
+        }
+        for (int i = a.nproj; i <= kMaxFusedProj; ++i) a.block_start[i] = (int32_t)(blocks - da.group_start[g]);
+        if (blocks > (1LL << 30)) return hipErrorNotSupported;
+        if (kLds[cfg] > lds) lds = kLds[cfg];
+        if (len < (int)sizeof g_mname)
+            len += snprintf(g_mname + len, sizeof g_mname - len, "%sks%d_rg%d_p%d", g ? "+" : "_", kKS[cfg], kRG[cfg],
+                            a.nproj);
+    }
+    for (int g = da.ngroups; g <= kMaxInputGroups; ++g) da.group_start[g] = (int32_t)blocks;
+    *name = g_mname;
+    if (query) return hipSuccess;
+    auto kern = skinny_direct::skinny_direct_multi_kernel;
+    if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                 (int)lds);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), lds, stream, da);
+    return hipGetLastError();
 }
 
 }  // namespace bl

@@ -77,6 +77,22 @@ struct MultiGroupArgs {
     FusedProjArgs args[kMaxInputGroups];
 };
 
+// Several quantised inputs in one launch of the direct-load skinny kernel
+// (skinny_direct.hip), M tokens each: group g reads Xq[g] (M x K[g]) with
+// the projections args[g]; its workgroups are [group_start[g],
+// group_start[g + 1]) and run configuration cfg[g] of the kernel's menu.
+struct DirectMultiArgs {
+    const int8_t *Xq[kMaxInputGroups];
+    const float *x_scale[kMaxInputGroups];
+    const int32_t *x_rowsum[kMaxInputGroups];
+    int64_t K[kMaxInputGroups];
+    int32_t cfg[kMaxInputGroups];
+    int32_t group_start[kMaxInputGroups + 1];
+    int32_t ngroups;
+    int64_t M;
+    FusedProjArgs args[kMaxInputGroups];
+};
+
 // the projection of workgroup `block`
 __device__ __forceinline__ int proj_of_block(const FusedProjArgs &args, int block)
 {

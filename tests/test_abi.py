@@ -370,6 +370,30 @@ def test_quant_multi_validation(lib):
     assert f(groups(ok, (P(), 2, 128, P(), P(), P(2))), 2, None) == -1        # misaligned x_rowsum
 
 
+def test_grouped_multi_validation(lib):
+    from ternary_weight_linear_act_amd.binding import NM, Proj, ActGroup
+    f = lib.bitlinear_forward_grouped_multi
+    arr = (Proj * 9)(*[Proj(A, A, 64, A, None) for _ in range(9)])
+
+    def groups(*gs):
+        return (ActGroup * max(len(gs), 1))(*[ActGroup(*g) for g in gs])
+    ok = (P(), P(), P(), 2048, arr, 1)
+    assert f(None, 1, 8, NM(0, 0), None) == -1                                     # groups NULL
+    assert f(groups(ok), 0, 8, NM(0, 0), None) == -1                               # ngroups 0
+    assert f(groups(*[ok] * 5), 5, 8, NM(0, 0), None) == -2                        # more than 4 groups
+    assert f(groups(ok), 1, 8, NM(3, 4), None) == -2                               # unsupported N:M
+    assert f(groups(ok), 1, 8, NM(2, 4), None) == -2                               # N:M weights
+    assert f(groups(ok), 1, 4, NM(0, 0), None) == -2                               # M below 5
+    assert f(groups(ok), 1, 9, NM(0, 0), None) == -2                               # M above 8
+    assert f(groups(ok), 1, -1, NM(0, 0), None) == -1                              # negative M
+    assert f(groups(ok, (P(4), P(), P(), 2048, arr, 1)), 2, 8, NM(0, 0), None) == -1   # misaligned Xq
+    assert f(groups(ok, (P(), P(), P(), 100, arr, 1)), 2, 8, NM(0, 0), None) == -1     # K not a multiple of 64
+    assert f(groups(ok, (P(), P(), P(), 12352, arr, 1)), 2, 8, NM(0, 0), None) == -2   # K past 12288
+    assert f(groups(ok, (P(), P(), P(), 2048, arr, 9)), 2, 8, NM(0, 0), None) == -2    # too many projections
+    assert f(groups(ok, (P(), P(), None, 2048, arr, 1)), 2, 8, NM(0, 0), None) == -1   # x_rowsum NULL
+    assert f(groups(ok), 1, 0, NM(0, 0), None) == 0                                # M = 0: no-op
+
+
 def test_trit24_sizes_and_validation(lib):
     # the trit-packed 2:4 layout: 12 bytes per 64 weights, as the oracle's
     # layout arithmetic counts them
