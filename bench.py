@@ -730,31 +730,50 @@ def bench_configs(torch, bl, workloads, dev, log, only=None):
                       "one_quant_launches": 1 + sum(1 if grouped_m[g] else len(g) for g in fused_groups),
                       "one_quant_groups": ["+".join(g) + (" grouped" if grouped_m[g] else " forward each")
                                            for g in fused_groups]})
-            if 5 <= M <= 8 and all(nm_of(n) == (0, 0) for n in projs) and not masked:
-                # and every group's forward in one launch: two launches a step
+            if 5 <= M <= 64 and all(nm_of(n) == (0, 0) for n in projs) and not masked:
+                # and the groups' forwards in one launch (at 9-64 tokens the
+                # groups within the token-tile kernel's K; the others as above)
+                mg = [g for g in fused_groups if M <= 8 or shapes[g[0]][1] <= 3072]
+                rest = [g for g in fused_groups if g not in mg]
                 fgroups = [[(Xq_m[g], xs_m[g], rs_m[g], [(pools[n][j], ws[n], shapes[n][0]) for n in g],
-                             [Y[n] for n in g], None) for g in fused_groups] for j in range(P)]
-                bl.quant_act_multi(qgroups)
-                bl.forward_grouped_multi(fgroups[0])
-                fk = bl.last_dispatch()
-                torch.cuda.synchronize()
-                for n in projs:
-                    if not torch.equal(Y[n], Yref[n]):
-                        raise SystemExit("%s: two-launch and two-call outputs differ for %s" % (name, n))
+                             [Y[n] for n in g], None) for g in mg] for j in range(P)]
 
-                def two_launch(j):
+                def multi_step(j):
                     bl.quant_act_multi(qgroups)
                     bl.forward_grouped_multi(fgroups[j])
-                ms, _ = timed_graph(torch, lambda: [two_launch(j % P) for j in range(G)], reps=2)
-                tl = ms * 1e3 / G
-                r.update({"two_launch_us": round(tl, 3), "two_launch_kernels": [qk, fk]})
+                    for g in rest:
+                        if grouped_m[g]:
+                            bl.forward_grouped(Xq_m[g], xs_m[g], rs_m[g],
+                                               [(pools[n][j], ws[n], shapes[n][0]) for n in g],
+                                               nm=nm_of(g[0]), Ys=[Y[n] for n in g])
+                        else:
+                            for n in g:
+                                bl.forward(Xq_m[g], xs_m[g], rs_m[g], pools[n][j], ws[n], shapes[n][0],
+                                           nm=nm_of(n), Y=Y[n])
+                try:
+                    bl.quant_act_multi(qgroups)
+                    bl.forward_grouped_multi(fgroups[0])
+                    fk = bl.last_dispatch()
+                except bl.BitLinearError:
+                    fk = None
+                if fk is not None and len(mg) > 1:
+                    multi_step(0)
+                    torch.cuda.synchronize()
+                    for n in projs:
+                        if not torch.equal(Y[n], Yref[n]):
+                            raise SystemExit("%s: multi-input and two-call outputs differ for %s" % (name, n))
+                    ms, _ = timed_graph(torch, lambda: [multi_step(j % P) for j in range(G)], reps=2)
+                    tl = ms * 1e3 / G
+                    r.update({"multi_input_us": round(tl, 3), "multi_input_kernels": [qk, fk],
+                              "multi_input_launches": 2 + sum(1 if grouped_m[g] else len(g) for g in rest),
+                              "multi_input_rest": ["+".join(g) for g in rest]})
         res[name] = r
         log("%-28s M=%-4d two-call %8.2f us%s%s%s" % (name, M, us, (" fused %.2f us" % r["fused_us"]) if "fused_us" in r else "",
                                                      (" shared quant %.2f us" % r["shared_quant_us"])
                                                      if "shared_quant_us" in r else "",
                                                      (" one quant %.2f us" % r["one_quant_us"])
                                                      if "one_quant_us" in r else "") +
-            ((" two launches %.2f us" % r["two_launch_us"]) if "two_launch_us" in r else ""))
+            ((" multi-input %.2f us" % r["multi_input_us"]) if "multi_input_us" in r else ""))
 
     dense = lambda n: (0, 0)
     case("single_1024/M1", "single_1024", ("linear",), 1, dense, [("linear",)])

@@ -366,10 +366,15 @@ typedef struct {
  * discussion: decode gains are diluted by launch overhead at small batches).
  * `groups` is a host array of 1 <= ngroups <= 4 entries; no output may
  * overlap another output or any input.  Supported: dense weights
- * (nm = {0, 0}), 5 <= M <= 8, every K in [256, 12288], up to 8 projections
- * per group; anything else returns BITLINEAR_EUNSUPPORTED and launches
- * nothing (call bitlinear_forward_grouped or bitlinear_forward per group
- * then).  Needs no workspace.  Errors: EINVAL for a bad group (as
+ * (nm = {0, 0}), up to 8 projections per group, and either 5 <= M <= 8 with
+ * every K in [256, 12288], or 9 <= M <= 64 with every group within the
+ * direct-load token-tile kernel's rules of bitlinear_forward_grouped
+ * (256 <= K <= 3072 and at least 6912 rows in the group at 9-64 tokens, 2560
+ * from 17 tokens, 2048 from 33; at 33-64 tokens fewer than 13824 rows, or at
+ * least 16384 with K <= 2048); anything else returns
+ * BITLINEAR_EUNSUPPORTED and launches nothing (call
+ * bitlinear_forward_grouped or bitlinear_forward per group then).  Needs no
+ * workspace.  Errors: EINVAL for a bad group (as
  * bitlinear_forward_grouped) or ngroups < 1. */
 bitlinear_status bitlinear_forward_grouped_multi(const bitlinear_act_group *groups, int32_t ngroups, int64_t M,
                                                  bitlinear_nm nm, hipStream_t stream);

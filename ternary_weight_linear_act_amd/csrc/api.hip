@@ -753,10 +753,12 @@ bitlinear_status bitlinear_forward_grouped_multi(const bitlinear_act_group *grou
     if (p != bl::Pattern::Dense)
         return fail(BITLINEAR_EUNSUPPORTED, "the multi-input grouped forward takes dense weights (nm = {0, 0})");
     const char *name = "";
-    const hipError_t e = bl::launch_skinny_direct_multi(da, stream, &name, false);
+    const hipError_t e = M <= 8 ? bl::launch_skinny_direct_multi(da, stream, &name, false)
+                                : bl::launch_skinny_direct_tiles_multi(da, stream, &name, false);
     if (e == hipErrorNotSupported)
-        return fail(BITLINEAR_EUNSUPPORTED, "the multi-input grouped forward supports 5 <= M <= 8 and "
-                    "256 <= K <= 12288 (M = %lld)", (long long)M);
+        return fail(BITLINEAR_EUNSUPPORTED, "the multi-input grouped forward supports 5 <= M <= 8 with "
+                    "256 <= K <= 12288, or 9 <= M <= 64 with every group on the token-tile kernel (M = %lld)",
+                    (long long)M);
     if (e != hipSuccess) return hip_fail("multi-input grouped forward launch", e);
     set_dispatch(name);
     return BITLINEAR_OK;

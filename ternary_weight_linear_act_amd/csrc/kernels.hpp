@@ -74,6 +74,11 @@ struct DirectMultiArgs;              // skinny_impl.hpp
 // M, ngroups and each group's projections; the launcher fills the rest.
 hipError_t launch_skinny_direct_multi(DirectMultiArgs da, hipStream_t stream, const char **name, bool query);
 
+// The same at 9-64 tokens on the direct-load kernel with several token tiles
+// per workgroup, where every group fits its single-input rule;
+// hipErrorNotSupported otherwise.
+hipError_t launch_skinny_direct_tiles_multi(DirectMultiArgs da, hipStream_t stream, const char **name, bool query);
+
 // One-token fused decode of several input groups, dense weights, in one
 // launch (K <= 16384 per group); hipErrorNotSupported otherwise.  The host
 // fills X, x_scale_out, K, ngroups and each group's projections; the

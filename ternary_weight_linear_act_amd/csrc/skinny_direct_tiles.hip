@@ -78,25 +78,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // host keeps KS <= (chunks of a K part) <= 4 * S * KS.  SPLIT (one
 // projection): each workgroup writes the raw int32 sums of its K part to
 // ws[part][m][n] (M x N per part) and split_epilogue_kernel finishes.
+// `id`: the workgroup's index within this launch's share of the grid (a
+// multiple of 8 from the grid's start, so that ids 8 apart still share an
+// XCD); `smem`: Lds<TT, RG, S>::kBytes + 512 bytes of LDS.
 template <int TT, int RG, int S, bool SPLIT>
-__global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8_t *__restrict__ Xq,
-                                                                      const float *__restrict__ x_scale,
-                                                                      const int32_t *__restrict__ x_rowsum,
-                                                                      FusedProjArgs args, int64_t M, int64_t K,
-                                                                      int32_t parts, int32_t *__restrict__ ws)
+__device__ __forceinline__ void skinny_direct_tiles_body(const int8_t *__restrict__ Xq,
+                                                         const float *__restrict__ x_scale,
+                                                         const int32_t *__restrict__ x_rowsum,
+                                                         const FusedProjArgs &args, int64_t M, int64_t K,
+                                                         int32_t parts, int32_t *__restrict__ ws, int id,
+                                                         uint8_t *smem)
 {
     using L = Lds<TT, RG, S>;
     constexpr int XLOADS = TT * 16 * S * 16 / 64;                 // 16-byte pieces per lane
-    __shared__ __attribute__((aligned(16))) uint8_t s_x[L::kBytes];
-    __shared__ int32_t s_rs[64];
-    __shared__ float s_xs[64];
+    uint8_t *s_x = smem;
+    int32_t *s_rs = reinterpret_cast<int32_t *>(smem + L::kBytes);
+    float *s_xs = reinterpret_cast<float *>(smem + L::kBytes + 256);
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, q = lane >> 4;
 
     // workgroup id -> (row block, token group, K part): ids 8 apart share an XCD
     const int ty = (int)((M + 16 * TT - 1) / (16 * TT));
     const int ny = SPLIT ? ty * parts : ty;
-    const int id = (int)blockIdx.x;
     const int yy = (id / 8) % ny;
     const int bx = (id / (8 * ny)) * 8 + id % 8;
     const int by = yy % ty;
@@ -290,6 +293,50 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8
     }
 }
 
+template <int TT, int RG, int S, bool SPLIT>
+__global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_kernel(const int8_t *__restrict__ Xq,
+                                                                      const float *__restrict__ x_scale,
+                                                                      const int32_t *__restrict__ x_rowsum,
+                                                                      FusedProjArgs args, int64_t M, int64_t K,
+                                                                      int32_t parts, int32_t *__restrict__ ws)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    skinny_direct_tiles_body<TT, RG, S, SPLIT>(Xq, x_scale, x_rowsum, args, M, K, parts, ws, (int)blockIdx.x, smem);
+}
+
+// Several quantised inputs in one launch (9-64 tokens each): group g's
+// workgroups are [group_start[g], group_start[g + 1]) (multiples of 8: each
+// group keeps the one-input kernel's XCD placement) and run configuration
+// cfg[g] (as numbered by tiles_config).  The argument is read in place in the
+// kernel-argument segment (indexed by the group, a copy would live in
+// scratch memory).
+#define BL_TILES_CASE(ID, TT, RG, S)                                                                            \
+    case ID:                                                                                                    \
+        skinny_direct_tiles_body<TT, RG, S, false>(da.Xq[gi], da.x_scale[gi], da.x_rowsum[gi], da.args[gi], da.M,  \
+                                                   da.K[gi], 1, nullptr, id, smem);                            \
+        return;
+
+__global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_multi_kernel(DirectMultiArgs)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const DirectMultiArgs &da = *(const DirectMultiArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    int gi = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxInputGroups; ++i)
+        if (i < da.ngroups && (int)blockIdx.x >= da.group_start[i]) gi = i;
+    const int id = (int)blockIdx.x - da.group_start[gi];
+    switch (da.cfg[gi]) {
+        BL_TILES_CASE(0, 1, 2, 2)
+        BL_TILES_CASE(1, 1, 2, 3)
+        BL_TILES_CASE(2, 1, 4, 2)
+        BL_TILES_CASE(3, 1, 4, 3)
+        BL_TILES_CASE(4, 2, 6, 2)
+    default: return;
+    }
+}
+
+#undef BL_TILES_CASE
+
 // Sum of the K parts' int32 partials (integer sums: exact in any order),
 // offset-code correction and dequant scale; one output per thread.
 __global__ __launch_bounds__(256) void split_epilogue_kernel(const float *__restrict__ x_scale,
@@ -314,6 +361,13 @@ namespace {
 
 thread_local char g_name[80];
 
+// Dynamic LDS past 64 KB must be allowed per kernel.
+hipError_t allow_lds(const void *kern, size_t bytes)
+{
+    if (bytes <= 64 * 1024) return hipSuccess;
+    return hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
 template <int TT, int RG, int S>
 hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, FusedProjArgs args, int64_t M, int64_t K,
                   hipStream_t stream, const char **name, bool query)
@@ -335,8 +389,11 @@ hipError_t launch(const int8_t *Xq, const float *xs, const int32_t *rs, FusedPro
     snprintf(g_name, sizeof g_name, "skinny_direct_tiles_dense_t%d_rg%d_s%d%s", TT, RG, S, args.nproj > 1 ? "_grouped" : "");
     *name = g_name;
     if (query) return hipSuccess;
-    hipLaunchKernelGGL((skinny_direct_tiles::skinny_direct_tiles_kernel<TT, RG, S, false>), dim3((unsigned)grid),
-                       dim3(64 * KS), 0, stream, Xq, xs, rs, args, M, K, 1, nullptr);
+    auto kern = skinny_direct_tiles::skinny_direct_tiles_kernel<TT, RG, S, false>;
+    const hipError_t e = allow_lds((const void *)kern, L::kBytes + 512);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KS), (size_t)(L::kBytes + 512), stream, Xq, xs, rs, args,
+                       M, K, 1, nullptr);
     return hipGetLastError();
 }
 
@@ -371,8 +428,14 @@ hipError_t launch_split(const int8_t *Xq, const float *xs, const int32_t *rs, co
     args.block_start[0] = 0;
     for (int i = 1; i <= kMaxFusedProj; ++i) args.block_start[i] = (int32_t)blocks;
     int32_t *ws = reinterpret_cast<int32_t *>(scratch.ptr);
-    hipLaunchKernelGGL((skinny_direct_tiles::skinny_direct_tiles_kernel<TT, RG, S, true>), dim3((unsigned)grid),
-                       dim3(64 * KS), 0, stream, Xq, xs, rs, args, M, K, (int32_t)parts, ws);
+    {
+        using LS = skinny_direct_tiles::Lds<TT, RG, S>;
+        auto kern = skinny_direct_tiles::skinny_direct_tiles_kernel<TT, RG, S, true>;
+        const hipError_t e0 = allow_lds((const void *)kern, LS::kBytes + 512);
+        if (e0 != hipSuccess) return e0;
+        hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * KS), (size_t)(LS::kBytes + 512), stream, Xq, xs, rs,
+                           args, M, K, (int32_t)parts, ws);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(skinny_direct_tiles::split_epilogue_kernel, dim3((unsigned)((M * N + 255) / 256)), dim3(256), 0,
@@ -390,28 +453,40 @@ hipError_t launch_k(const int8_t *Xq, const float *xs, const int32_t *rs, const 
 
 }  // namespace
 
+namespace {
+
 // The measured cases of the file comment (dense weights, 9-64 tokens, K 256 to
-// 3072); hipErrorNotSupported (nothing launched) for every other shape.
+// 3072): the configuration <TT, RG, S> as 0: <1, 2, 2>, 1: <1, 2, 3>,
+// 2: <1, 4, 2>, 3: <1, 4, 3>, 4: <2, 6, 2>; -1 for every other shape.
+int tiles_config(int64_t M, int64_t K, int64_t rows)
+{
+    const int64_t C = K / 64;
+    if (M < 9 || M > 64 || C < skinny_direct_tiles::KS || C > 48 || rows < 2048) return -1;
+    const int s3 = C <= 32 ? 0 : 1;                                // S = 2 up to 32 chunks, else 3
+    if (rows < 6912) return M >= (rows < 2560 ? 33 : 17) ? 0 + s3 : -1;
+    if (M <= 16) return 0 + s3;
+    if (M <= 32) return rows >= 13824 ? 2 + s3 : 0 + s3;
+    if (rows < 13824) return 2 + s3;
+    if (rows >= 16384 && C <= 32) return 4;
+    return -1;
+}
+
+}  // namespace
+
 hipError_t launch_skinny_direct_tiles(const int8_t *Xq, const float *xs, const int32_t *rs, const FusedProjArgs &args,
                                Pattern p, int64_t M, int64_t K, hipStream_t stream, const char **name, bool query)
 {
     if (p != Pattern::Dense || args.nproj < 1 || args.nproj > kMaxFusedProj) return hipErrorNotSupported;
     int64_t rows = 0;
     for (int i = 0; i < args.nproj; ++i) rows += args.N[i];
-    const int64_t C = K / 64;
-    if (M < 9 || M > 64 || C < skinny_direct_tiles::KS || C > 48 || rows < 2048) return hipErrorNotSupported;
-    if (rows < 6912) {
-        if (M >= (rows < 2560 ? 33 : 17)) return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
-        return hipErrorNotSupported;
+    switch (tiles_config(M, K, rows)) {
+    case 0: return launch<1, 2, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+    case 1: return launch<1, 2, 3>(Xq, xs, rs, args, M, K, stream, name, query);
+    case 2: return launch<1, 4, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+    case 3: return launch<1, 4, 3>(Xq, xs, rs, args, M, K, stream, name, query);
+    case 4: return launch<2, 6, 2>(Xq, xs, rs, args, M, K, stream, name, query);
+    default: return hipErrorNotSupported;
     }
-    if (M <= 16) return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
-    if (M <= 32) {
-        if (rows >= 13824) return launch_k<1, 4>(Xq, xs, rs, args, M, K, stream, name, query);
-        return launch_k<1, 2>(Xq, xs, rs, args, M, K, stream, name, query);
-    }
-    if (rows < 13824) return launch_k<1, 4>(Xq, xs, rs, args, M, K, stream, name, query);
-    if (rows >= 16384 && C <= 32) return launch<2, 6, 2>(Xq, xs, rs, args, M, K, stream, name, query);
-    return hipErrorNotSupported;
 }
 
 // One dense projection at 9-64 tokens with K too deep for one workgroup's
@@ -437,6 +512,53 @@ hipError_t launch_skinny_direct_tiles_split(const int8_t *Xq, const float *xs, c
     if (M <= 32)
         return launch_split<1, 2, 3>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, parts, scratch, stream, name);
     return launch_split<2, 4, 3>(Xq, xs, rs, packed, w_scale, M, N, K, Y, acc, parts, scratch, stream, name);
+}
+
+// The multi-input launch at 9-64 tokens: every group must fit the one-input
+// rule (tiles_config).
+hipError_t launch_skinny_direct_tiles_multi(DirectMultiArgs da, hipStream_t stream, const char **name, bool query)
+{
+    thread_local char g_mname[160];
+    if (da.ngroups < 1 || da.ngroups > kMaxInputGroups) return hipErrorNotSupported;
+    static const int kTT[5] = {1, 1, 1, 1, 2}, kRG[5] = {2, 2, 4, 4, 6}, kS[5] = {2, 3, 2, 3, 2};
+    static const size_t kLds[5] = {
+        skinny_direct_tiles::Lds<1, 2, 2>::kBytes + 512, skinny_direct_tiles::Lds<1, 2, 3>::kBytes + 512,
+        skinny_direct_tiles::Lds<1, 4, 2>::kBytes + 512, skinny_direct_tiles::Lds<1, 4, 3>::kBytes + 512,
+        skinny_direct_tiles::Lds<2, 6, 2>::kBytes + 512};
+    int64_t grid = 0;
+    size_t lds = 0;
+    int len = snprintf(g_mname, sizeof g_mname, "skinny_direct_tiles_multi_dense");
+    for (int g = 0; g < da.ngroups; ++g) {
+        FusedProjArgs &a = da.args[g];
+        if (a.nproj < 1 || a.nproj > kMaxFusedProj) return hipErrorNotSupported;
+        int64_t rows = 0;
+        for (int i = 0; i < a.nproj; ++i) rows += a.N[i];
+        const int cfg = tiles_config(da.M, da.K[g], rows);
+        if (cfg < 0) return hipErrorNotSupported;
+        da.cfg[g] = cfg;
+        int64_t blocks = 0;
+        for (int i = 0; i < a.nproj; ++i) {
+            a.block_start[i] = (int32_t)blocks;
+            blocks += (a.N[i] + 16 * kRG[cfg] - 1) / (16 * kRG[cfg]);
+        }
+        for (int i = a.nproj; i <= kMaxFusedProj; ++i) a.block_start[i] = (int32_t)blocks;
+        const int64_t ty = (da.M + 16 * kTT[cfg] - 1) / (16 * kTT[cfg]);
+        da.group_start[g] = (int32_t)grid;
+        grid += (blocks + 7) / 8 * 8 * ty;
+        if (grid > (1LL << 30)) return hipErrorNotSupported;
+        if (kLds[cfg] > lds) lds = kLds[cfg];
+        if (len < (int)sizeof g_mname)
+            len += snprintf(g_mname + len, sizeof g_mname - len, "%st%d_rg%d_s%d_p%d", g ? "+" : "_", kTT[cfg],
+                            kRG[cfg], kS[cfg], a.nproj);
+    }
+    for (int g = da.ngroups; g <= kMaxInputGroups; ++g) da.group_start[g] = (int32_t)grid;
+    *name = g_mname;
+    if (query) return hipSuccess;
+    auto kern = skinny_direct_tiles::skinny_direct_tiles_multi_kernel;
+    const hipError_t e = allow_lds((const void *)kern, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * skinny_direct_tiles::KS), lds, stream, da);
+    return hipGetLastError();
 }
 
 }  // namespace bl

@@ -89,8 +89,47 @@ def test_grouped_multi_shapes(case):
     check(groups, outs)
 
 
-@pytest.mark.parametrize("M,K,nm", [(4, 2048, (0, 0)), (9, 2048, (0, 0)), (8, 192, (0, 0)), (8, 12352, (0, 0)),
-                                    (8, 2048, (2, 4))])
+# 9-64 tokens, the token-tile kernel's configurations <TT, RG, S>: <1,2,2>
+# and <1,2,3> (K up to 32 chunks, then to 48), <1,4,2> and <1,4,3> (from
+# 13824 rows at 17-32 tokens, 6912-13823 rows at 33-64), <2,6,2> (from 16384
+# rows at 33-64 tokens, K <= 2048); ragged rows and token counts
+TILES_CASES = [
+    (9, [(2048, (7000,)), (2560, (6912,))]),
+    (24, [(2048, (14000,)), (3072, (3000,)), (1024, (2600,))]),
+    (40, [(2560, (7000,)), (1024, (16400,))]),
+    (17, [(2048, (3000, 100)), (3072, (6912, 7000))]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(TILES_CASES)))
+def test_grouped_multi_token_tiles(case):
+    M, spec = TILES_CASES[case]
+    groups = []
+    for gi, (K, Ns) in enumerate(spec):
+        seed = 4500 + 31 * case + 7 * gi + K
+        Ws = [workloads.small_case(seed + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+        _, X = workloads.small_case(seed + 99, M, 8, K, outlier_frac=0.01)
+        groups.append((Ws, X))
+    print("case grouped multi tiles M=%d %s" % (M, spec), flush=True)
+    outs, call, name = run(groups)
+    assert name.startswith("skinny_direct_tiles_multi_dense"), name
+    check(groups, outs)
+
+
+def test_block_3b_at_64_tokens_shallow_groups():
+    # q k v, o and gate up of the 3B block at 64 tokens in one launch (down,
+    # K = 11008, is past the token-tile kernel's K)
+    d = workloads.draw("block_3b", projs=["q", "k", "v", "o", "gate", "up"], Ms=(64,))
+    gs = [("q", "k", "v"), ("o",), ("gate", "up")]
+    groups = [([d.W[n] for n in g], d.X[(g[0], 64)]) for g in gs]
+    print("case grouped multi block_3b M=64", flush=True)
+    outs, call, name = run(groups)
+    assert name.startswith("skinny_direct_tiles_multi_dense") and name.count("+") == 2, name
+    check(groups, outs)
+
+
+@pytest.mark.parametrize("M,K,nm", [(4, 2048, (0, 0)), (8, 192, (0, 0)), (8, 12352, (0, 0)), (8, 2048, (2, 4)),
+                                    (9, 2048, (0, 0)), (64, 11008, (0, 0)), (65, 2048, (0, 0))])
 def test_grouped_multi_unsupported(M, K, nm):
     import torch
     import ternary_weight_linear_act_amd as bl
