@@ -1414,15 +1414,18 @@ def main():
             traffic = None
     # the same fraction from the committed rocprofv3 kernel trace of the
     # bench's graph form (--trace-probe), while the kernel sources match it
-    frac_trace, trace_us = None, None
+    frac_trace, trace_us, frac_trace_median, trace_median_us = None, None, None, None
     if os.path.exists(TRACE_FILE):
         try:
             t = json.load(open(TRACE_FILE))
             if t.get("source_digest") == digest:
                 trace_us = {k: v["avg_us"] for k, v in t["kernels"].items()}
+                trace_median_us = {k: v["median_us"] for k, v in t["kernels"].items()}
                 frac_trace = round(step_bytes / (trace_us[step_kernel] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                frac_trace_median = round(step_bytes / (trace_median_us[step_kernel] * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                          4)
         except (ValueError, OSError, KeyError):
-            frac_trace, trace_us = None, None
+            frac_trace, trace_us, frac_trace_median, trace_median_us = None, None, None, None
 
     # ------------------------------------------------------------------ other workloads
     configs = None if args.no_configs else bench_configs(torch, bl, workloads, dev, log)
@@ -1490,6 +1493,7 @@ def main():
                      "frac_source": "HIP events: a graph of one launch per pool entry, replayed for >= 20 ms, "
                                     "median per launch (inter-launch gaps included)",
                      "frac_trace": frac_trace, "trace_avg_us": trace_us,
+                     "frac_trace_median": frac_trace_median, "trace_median_us": trace_median_us,
                      "frac_streaming_floor": round(step_bytes / (floor_step_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                      "floor_us": floor_step_us, "floor_fraction": round(floor_step_us / fused_us, 3),
                      "kernel": dispatch, "avg_launch_us": round(fused_us, 3),
