@@ -169,3 +169,24 @@ def test_grouped_multi_graph_replay():
         for r, o in zip(ref, outs):
             for a, b in zip(r, o[4]):
                 assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_grouped_multi_eight_projections_without_accumulators():
+    import torch
+    import oracle
+    import ternary_weight_linear_act_amd as bl
+    M, K = 6, 2048
+    Ns = (16, 17, 100, 255, 256, 257, 31, 64)
+    Ws = [workloads.small_case(4300 + i, 1, N, K)[0] for i, N in enumerate(Ns)]
+    _, X = workloads.small_case(4330, M, 8, K, outlier_frac=0.01)
+    packs = [hip_pack(W, (0, 0)) for W in Ws]
+    Xq, xs, rs = bl.quant_act(to_dev(X))
+    Ys = [torch.full((M, W.shape[0]), float("nan"), dtype=torch.float32, device="cuda") for W in Ws]
+    print("case grouped multi 8 projections", flush=True)
+    bl.forward_grouped_multi([(Xq, xs, rs, [(pk, ws, W.shape[0]) for (pk, ws), W in zip(packs, Ws)], Ys, None)])
+    torch.cuda.synchronize()
+    q, xs_o, _ = oracle.quant_act(X)
+    for W, Y in zip(Ws, Ys):
+        beta, w_eff, _ = oracle.quantize_weights(W)
+        acc_o, Y_o = oracle.forward(q, xs_o, w_eff, beta)
+        check_y(Y.cpu().numpy(), Y_o, acc_o)

@@ -195,3 +195,34 @@ def test_multi_zero_row_and_graph_replay():
         for r, o in zip(ref, out):
             for a, b in zip(r, o[1]):
                 assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+def test_multi_optional_outputs_and_eight_projections():
+    # a group of 8 projections without accumulators or scale output beside a
+    # group with both; outputs against the oracle
+    import torch
+    import ternary_weight_linear_act_amd as bl
+    import oracle
+    K1, K2 = 1024, 4160
+    Ns = (16, 17, 100, 255, 256, 257, 31, 64)
+    W1 = [workloads.small_case(2300 + i, 1, N, K1)[0] for i, N in enumerate(Ns)]
+    W2 = [workloads.small_case(2320, 1, 333, K2)[0]]
+    _, X1 = workloads.small_case(2330, 1, 8, K1, outlier_frac=0.01)
+    _, X2 = workloads.small_case(2331, 1, 8, K2, outlier_frac=0.01)
+    p1 = [hip_pack(W, (0, 0)) for W in W1]
+    p2 = [hip_pack(W, (0, 0)) for W in W2]
+    Y1 = [torch.full((1, W.shape[0]), float("nan"), dtype=torch.float32, device="cuda") for W in W1]
+    Y2 = [torch.full((1, W.shape[0]), float("nan"), dtype=torch.float32, device="cuda") for W in W2]
+    A2 = [torch.full((1, W.shape[0]), -7, dtype=torch.int32, device="cuda") for W in W2]
+    xs2 = torch.full((1,), float("nan"), dtype=torch.float32, device="cuda")
+    print("case multi 8 projections, optional outputs", flush=True)
+    bl.forward_fused_multi([(to_dev(X1), [(pk, ws, W.shape[0]) for (pk, ws), W in zip(p1, W1)], Y1, None, None),
+                            (to_dev(X2), [(pk, ws, W.shape[0]) for (pk, ws), W in zip(p2, W2)], Y2, A2, xs2)])
+    torch.cuda.synchronize()
+    assert bl.last_dispatch().startswith("fused_decode_multi_dense")
+    q1, xs1_o, _ = oracle.quant_act(X1)
+    for W, Y in zip(W1, Y1):
+        beta, w_eff, _ = oracle.quantize_weights(W)
+        acc_o, Y_o = oracle.forward(q1, xs1_o, w_eff, beta)
+        check_y(Y.cpu().numpy(), Y_o, acc_o)
+    check_group(W2, X2, (0, 0), Y2, A2, xs2)
