@@ -383,7 +383,7 @@ def block_traffic_summary(fetch_dir, write_dir, probe_out, out_md, commands):
         fb = float(np.mean([fetch[j][1] for j in range(i, len(fetch), len(pos))])) * fs
         wb = float(np.mean([write[j][1] for j in range(i, len(write), len(pos))])) * ws
         rows.append((p["group"], p["role"], fsym.pop(), fb, wb, p["bytes"]))
-    md = ["# HBM traffic per dispatch, 3B block at %d tokens (grouped form)" % probe["block_traffic_probe"], "",
+    md = ["# HBM traffic per dispatch, 3B block at %d tokens (multi-input form)" % probe["block_traffic_probe"], "",
           "Commands (run from /tmp with TMPDIR=/tmp, repository at $R), then the summary:", ""] + \
          ["    " + c.strip() for c in commands.split(" ;; ")] + \
          ["    python3 $R/bench.py --block-traffic-summary %s %s %s %s '%s'" % (
@@ -395,7 +395,7 @@ def block_traffic_summary(fetch_dir, write_dir, probe_out, out_md, commands):
           "|---|---|---|---:|---:|---:|---:|"]
     for g, role, sym, fb, wb, ab in rows:
         md.append("| %s | %s | `%s` | %d | %d | %d | %.3f |" % (g, role, sym, fb, wb, ab, (fb + wb) / ab))
-    md += ["", "Algorithmic bytes: quant_act 5 M K + 8 M (fp32 in, int8 out, scale and row sum); a forward the "
+    md += ["", "Algorithmic bytes: quant_act 5 M K + 8 M per input (fp32 in, int8 out, scale and row sum); a forward the "
                "packed weights, the int8 activations, scales and row sums, beta and the fp32 output; with K split, "
                "the int32 partials in the workspace are counted where they are written and read."]
     with open(out_md, "w") as f:
@@ -1036,9 +1036,11 @@ def main():
         return
 
     if args.block_probe or args.block_traffic_probe:
-        # the 3B block at M tokens in the bench's form past 16 tokens: one
-        # quant_act per input group, then the grouped forward (or the forward
-        # per projection).  --block-probe (for rocprofv3 --kernel-trace): a
+        # the 3B block at M tokens (5-64) in its multi-input form: every
+        # input group quantised in one launch, the groups within the grouped
+        # kernels' K (all at 5-8 tokens; K <= 3072 at 9-64) in one launch of
+        # the multi-input grouped forward, the others by the forward per
+        # projection.  --block-probe (for rocprofv3 --kernel-trace): a
         # graph of P block steps over a rotating weight pool, replayed
         # TRACE_REPLAYS times.  --block-traffic-probe (for --pmc FETCH_SIZE /
         # WRITE_SIZE): 2 P eager steps, then a device copy of known size
@@ -1060,38 +1062,39 @@ def main():
         bY = {n: torch.empty((M, bshapes[n][0]), dtype=torch.float32, device=dev) for n in blk}
         need = max(bl.forward_workspace_size(M, bshapes[n][0], bshapes[n][1]) for n in blk)
         bwork = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
-        grouped, kernels = {}, {}
-        for g in bgroups:
-            bl.quant_act(bX[g], bXq[g], bxs[g], brs[g])
-            grouped[g] = False
-            if len(g) > 1:
-                try:
-                    bl.forward_grouped(bXq[g], bxs[g], brs[g], [(bpool[n][0], bws[n], bshapes[n][0]) for n in g],
-                                       Ys=[bY[n] for n in g])
-                    grouped[g] = True
-                except bl.BitLinearError:
-                    pass
-            if not grouped[g]:
-                for n in g:
-                    bl.forward(bXq[g], bxs[g], brs[g], bpool[n][0], bws[n], bshapes[n][0], Y=bY[n], workspace=bwork)
+        if not 5 <= M <= 64:
+            raise SystemExit("the block probes take 5 <= M <= 64")
+        qgroups = [(bX[g], bXq[g], bxs[g], brs[g]) for g in bgroups]
+        mgroups = [g for g in bgroups if M <= 8 or bshapes[g[0]][1] <= 3072]
+        rest = [g for g in bgroups if g not in mgroups]
+        margs = [[(bXq[g], bxs[g], brs[g], [(bpool[n][j], bws[n], bshapes[n][0]) for n in g], [bY[n] for n in g],
+                   None) for g in mgroups] for j in range(PB)]
+        kernels = {}
+        bl.quant_act_multi(qgroups)
+        kernels["quant"] = bl.last_dispatch()
+        bl.forward_grouped_multi(margs[0])
+        kernels[";".join("+".join(g) for g in mgroups)] = bl.last_dispatch()
+        for g in rest:
+            for n in g:
+                bl.forward(bXq[g], bxs[g], brs[g], bpool[n][0], bws[n], bshapes[n][0], Y=bY[n], workspace=bwork)
             kernels["+".join(g)] = bl.last_dispatch()
 
         def block_step(j):
-            for g in bgroups:
-                bl.quant_act(bX[g], bXq[g], bxs[g], brs[g])
-                if grouped[g]:
-                    bl.forward_grouped(bXq[g], bxs[g], brs[g], [(bpool[n][j], bws[n], bshapes[n][0]) for n in g],
-                                       Ys=[bY[n] for n in g])
-                else:
-                    for n in g:
-                        bl.forward(bXq[g], bxs[g], brs[g], bpool[n][j], bws[n], bshapes[n][0], Y=bY[n],
-                                   workspace=bwork)
+            bl.quant_act_multi(qgroups)
+            bl.forward_grouped_multi(margs[j])
+            for g in rest:
+                for n in g:
+                    bl.forward(bXq[g], bxs[g], brs[g], bpool[n][j], bws[n], bshapes[n][0], Y=bY[n],
+                               workspace=bwork)
         if args.block_traffic_probe:
             # each step's dispatches in order, with their algorithmic bytes
-            positions = []
-            for g in bgroups:
+            positions = [{"group": "all", "role": "quant_act_multi",
+                          "bytes": sum(quant_bytes(M, bshapes[g[0]][1]) for g in bgroups)},
+                         {"group": ";".join("+".join(g) for g in mgroups), "role": "forward_grouped_multi",
+                          "bytes": sum(sum(bshapes[n][0] * bshapes[n][1] // 4 + 4 + 4 * M * bshapes[n][0] for n in g)
+                                       + M * bshapes[g[0]][1] + 8 * M for g in mgroups)}]
+            for g in rest:
                 K = bshapes[g[0]][1]
-                positions.append({"group": "+".join(g), "role": "quant_act", "bytes": quant_bytes(M, K)})
                 name = kernels["+".join(g)]
                 if "splitk" in name:
                     n = g[0]
@@ -1101,9 +1104,6 @@ def main():
                                       "bytes": N * K // 4 + 4 + M * K + 8 * M + 4 * parts * M * N})
                     positions.append({"group": "+".join(g), "role": "forward, sum of the parts and epilogue",
                                       "bytes": 4 * parts * M * N + 8 * M + 4 + 4 * M * N})
-                elif grouped[g]:
-                    nb = sum(bshapes[n][0] * K // 4 + 4 + 4 * M * bshapes[n][0] for n in g) + M * K + 8 * M
-                    positions.append({"group": "+".join(g), "role": "forward", "bytes": nb})
                 else:
                     for n in g:
                         positions.append({"group": "+".join(g), "role": "forward (%s)" % n,
