@@ -77,10 +77,13 @@ __device__ __forceinline__ void decode_dot4_body(
     __shared__ uint32_t s_sel[P == Pattern::Dense ? 1 : 2 * nm_sel_entries(P)];   // N:M byte selectors
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // entries past the last projection hold the block count, so no test of
+    // nproj is needed: without one the table loads issue together rather
+    // than one round trip each
     int p = 0;
 #pragma unroll
     for (int i = 1; i < kMaxFusedProj; ++i)
-        if (i < args.nproj && block >= args.block_start[i]) p = i;
+        if (block >= args.block_start[i]) p = i;
     const int64_t N = args.N[p];
     const uint8_t *packed = args.packed[p];
     const int64_t row = (int64_t)(block - args.block_start[p]) * RB + wave * RPW + lane / LPR;

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(512) void decode_multi_kernel(MultiGroupArgs)
     int gi = 0;
 #pragma unroll
     for (int i = 1; i < kMaxInputGroups; ++i)
-        if (i < mg.ngroups && (int)blockIdx.x >= mg.group_start[i]) gi = i;
+        if ((int)blockIdx.x >= mg.group_start[i]) gi = i;   // entries past ngroups: the block count
     const int blk = (int)blockIdx.x - mg.group_start[gi];
     const FusedProjArgs &a = mg.args[gi];
     const float *X = mg.X[gi];

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * KS) void fused_kernel(const float *__restrict_
     int p = 0;
 #pragma unroll
     for (int i = 1; i < kMaxFusedProj; ++i)
-        if (i < args.nproj && (int)blockIdx.x >= args.block_start[i]) p = i;
+        if ((int)blockIdx.x >= args.block_start[i]) p = i;       // entries past nproj: the block count
     const int64_t N = args.N[p];
     const uint8_t *packed = args.packed[p];
     const int64_t n0 = (int64_t)(blockIdx.x - args.block_start[p]) * ROWS;

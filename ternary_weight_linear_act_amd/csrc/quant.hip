@@ -195,7 +195,7 @@ __global__ __launch_bounds__(BLOCK) void quant_act_multi_kernel(QuantGroupArgs)
     int gi = 0;
 #pragma unroll
     for (int i = 1; i < kMaxQuantGroups; ++i)
-        if (i < qa.ngroups && (int64_t)blockIdx.x >= qa.row_start[i]) gi = i;
+        if ((int64_t)blockIdx.x >= qa.row_start[i]) gi = i;   // entries past ngroups: the row count
     quant_act_reg_body<BLOCK, NV>(qa.X[gi], qa.K[gi], qa.Xq[gi], qa.x_scale[gi], qa.x_rowsum[gi],
                                   (int64_t)blockIdx.x - qa.row_start[gi]);
 }

@@ -233,7 +233,7 @@ __global__ __launch_bounds__(512) void skinny_direct_multi_kernel(DirectMultiArg
     int gi = 0;
 #pragma unroll
     for (int i = 1; i < kMaxInputGroups; ++i)
-        if (i < da.ngroups && (int)blockIdx.x >= da.group_start[i]) gi = i;
+        if ((int)blockIdx.x >= da.group_start[i]) gi = i;   // entries past ngroups: the block count
     const int blk = (int)blockIdx.x - da.group_start[gi];
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
     switch (da.cfg[gi]) {

@@ -323,7 +323,7 @@ __global__ __launch_bounds__(64 * KS) void skinny_direct_tiles_multi_kernel(Dire
     int gi = 0;
 #pragma unroll
     for (int i = 1; i < kMaxInputGroups; ++i)
-        if (i < da.ngroups && (int)blockIdx.x >= da.group_start[i]) gi = i;
+        if ((int)blockIdx.x >= da.group_start[i]) gi = i;   // entries past ngroups: the block count
     const int id = (int)blockIdx.x - da.group_start[gi];
     switch (da.cfg[gi]) {
         BL_TILES_CASE(0, 1, 2, 2)

@@ -99,7 +99,7 @@ __device__ __forceinline__ int proj_of_block(const FusedProjArgs &args, int bloc
     int p = 0;
 #pragma unroll
     for (int i = 1; i < kMaxFusedProj; ++i)
-        if (i < args.nproj && block >= args.block_start[i]) p = i;
+        if (block >= args.block_start[i]) p = i;   // entries past nproj hold the block count: loads issue together
     return p;
 }
 
