@@ -444,9 +444,10 @@ typedef struct {
  * discussion notes that decode gains are diluted by launch overhead; here the
  * groups share one launch.  `groups` is a host array; no two groups' outputs
  * may overlap one another or any input.  nm applies to every group.  Dense
- * weights with every K <= 16384 run as one launch; otherwise (N:M weights, or
- * a K past 16384) each group runs as its own bitlinear_forward_fused launch,
- * with the same results.  Errors: EINVAL for a bad group (as
+ * weights with every K <= 16384 and at most 16 projections in all run as one
+ * launch; otherwise (N:M weights, a K past 16384, more projections) each
+ * group runs as its own bitlinear_forward_fused launch, with the same
+ * results.  Errors: EINVAL for a bad group (as
  * bitlinear_forward_fused) or ngroups < 1; EUNSUPPORTED for ngroups > 4 or a
  * K past 65344. */
 bitlinear_status bitlinear_forward_fused_multi(const bitlinear_input_group *groups, int32_t ngroups,

@@ -58,14 +58,23 @@ __device__ __forceinline__ int lanes_sum(int v)
 // unconditionally (a load under a branch makes the compiler wait for it at
 // the join); the host guarantees K <= 64 * U * LPR.  W waves per workgroup,
 // W * 64 / LPR rows.
-// `block` is the workgroup's index within this launch's share of the grid
-// (blockIdx.x for a launch of one input; the multi-input kernel passes the
-// index within its group).  Only threads below 64 * W may enter.
+// One projection of a workgroup: its packed weights, scale, outputs, rows.
+struct ProjView {
+    const uint8_t *packed;
+    const float *w_scale;
+    float *Y;
+    int32_t *acc;
+    int64_t N;
+};
+
+// `v`: the workgroup's projection, `row_block`: its block of RB rows there;
+// `x_scale_out`: non-NULL for the one workgroup that writes the scale.  Only
+// threads below 64 * W may enter.
 template <Pattern P, int LPR, int U, bool FUSED, int W = 4, int TR = 0>
 __device__ __forceinline__ void decode_dot4_body(
     const float *__restrict__ X, const int8_t *__restrict__ Xq, const float *__restrict__ x_scale,
-    const int32_t *__restrict__ x_rowsum, int64_t K, const FusedProjArgs &args, float *__restrict__ x_scale_out,
-    const ActTransform &tr, int block)
+    const int32_t *__restrict__ x_rowsum, int64_t K, const ProjView &v, int64_t row_block,
+    float *__restrict__ x_scale_out, const ActTransform &tr)
 {
     static_assert(TR == 0 || FUSED, "the row transform belongs to the fused form");
     constexpr bool GATE = (TR & kTrGate) != 0, NORM = (TR & kTrNorm) != 0;
@@ -77,21 +86,14 @@ __device__ __forceinline__ void decode_dot4_body(
     __shared__ uint32_t s_sel[P == Pattern::Dense ? 1 : 2 * nm_sel_entries(P)];   // N:M byte selectors
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // entries past the last projection hold the block count, so no test of
-    // nproj is needed: without one the table loads issue together rather
-    // than one round trip each
-    int p = 0;
-#pragma unroll
-    for (int i = 1; i < kMaxFusedProj; ++i)
-        if (block >= args.block_start[i]) p = i;
-    const int64_t N = args.N[p];
-    const uint8_t *packed = args.packed[p];
-    const int64_t row = (int64_t)(block - args.block_start[p]) * RB + wave * RPW + lane / LPR;
+    const int64_t N = v.N;
+    const uint8_t *packed = v.packed;
+    const int64_t row = row_block * RB + wave * RPW + lane / LPR;
     const int j = lane % LPR;
     const int64_t C = K / 64;
-    float *Y = args.Y[p];
-    int32_t *acc_out = args.acc[p];
-    const float *w_scale = args.w_scale[p];
+    float *Y = v.Y;
+    int32_t *acc_out = v.acc;
+    const float *w_scale = v.w_scale;
     // every argument read later in SGPRs now (a pending scalar load would make
     // the compiler wait for all outstanding memory operations at its use)
     asm volatile("" ::"s"(X), "s"(Xq), "s"(x_scale), "s"(x_rowsum), "s"(packed), "s"(Y), "s"(acc_out),
@@ -214,7 +216,7 @@ __device__ __forceinline__ void decode_dot4_body(
             xg = g;
         } else {
             xsc = (g == 0.0f) ? 0.0f : g / 127.0f;
-            if (x_scale_out && block == 0 && tid == 0) x_scale_out[0] = xsc;
+            if (x_scale_out && tid == 0) x_scale_out[0] = xsc;
         }
     } else {
 #pragma unroll
@@ -283,7 +285,7 @@ __device__ __forceinline__ void decode_dot4_body(
     acc = lanes_sum<LPR>(acc);
     if constexpr (NORM) {
         xsc = act_norm_scale(xg, act_rinv(ss, K, tr.eps));
-        if (x_scale_out && block == 0 && tid == 0) x_scale_out[0] = xsc;
+        if (x_scale_out && tid == 0) x_scale_out[0] = xsc;
     }
     if (j == 0 && row < N) {
         // dense codes are t + 1: subtract the activation row sum
@@ -299,7 +301,17 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
     const int32_t *__restrict__ x_rowsum, int64_t K, FusedProjArgs args, float *__restrict__ x_scale_out,
     ActTransform tr)
 {
-    decode_dot4_body<P, LPR, U, FUSED, W, TR>(X, Xq, x_scale, x_rowsum, K, args, x_scale_out, tr, (int)blockIdx.x);
+    // entries past the last projection hold the block count, so no test of
+    // nproj is needed: without one the table loads issue together rather
+    // than one round trip each
+    const int block = (int)blockIdx.x;
+    int p = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxFusedProj; ++i)
+        if (block >= args.block_start[i]) p = i;
+    const ProjView v{args.packed[p], args.w_scale[p], args.Y[p], args.acc[p], args.N[p]};
+    decode_dot4_body<P, LPR, U, FUSED, W, TR>(X, Xq, x_scale, x_rowsum, K, v, block - args.block_start[p],
+                                              block == 0 ? x_scale_out : nullptr, tr);
 }
 
 }  // namespace dot4

@@ -81,31 +81,56 @@ Dot4Config multi_config(int64_t K, const FusedProjArgs &args, int *waves)
 
 namespace dot4 {
 
+// The kernel's argument: one record per (group, projection) pair in grid
+// order, so that a workgroup finds its record with one scan of pair_start
+// and has every pointer with one more load (the one-input kernel's depth).
+struct MultiPair {
+    const float *X;
+    float *x_scale_out;          // set on the group's first pair only
+    const uint8_t *packed;
+    const float *w_scale;
+    float *Y;
+    int32_t *acc;
+    int64_t K;
+    int64_t N;
+    int32_t cfg;
+    int32_t pad;
+};
+
+// At most 16 pairs in one launch: their first blocks fill one 64-byte line
+// of the argument, read by one scalar load (more pairs: one launch per
+// group).
+constexpr int kMultiPairs = 16;
+
+struct MultiPairArgs {
+    int32_t pair_start[kMultiPairs + 1];     // entries past the last pair: the block count
+    MultiPair pair[kMultiPairs];
+};
+
 #define BL_MULTI_CASE(ID, LPR, U, W)                                                                            \
     case ID:                                                                                                    \
         if (wave < (W))                                                                                         \
-            decode_dot4_body<Pattern::Dense, LPR, U, true, W, 0>(X, nullptr, nullptr, nullptr, K, a, xso, tr,  \
-                                                                 blk);                                          \
+            decode_dot4_body<Pattern::Dense, LPR, U, true, W, 0>(e.X, nullptr, nullptr, nullptr, e.K, v, rb, xso,   \
+                                                                 tr);                                           \
         return;
 
 // The argument is read in place in the kernel-argument segment (it is the
 // launch's only argument, at offset 0): indexed by the group, a by-value
 // copy of it would live in scratch memory.
-__global__ __launch_bounds__(512) void decode_multi_kernel(MultiGroupArgs)
+__global__ __launch_bounds__(512) void decode_multi_kernel(MultiPairArgs)
 {
-    const MultiGroupArgs &mg = *(const MultiGroupArgs *)__builtin_amdgcn_kernarg_segment_ptr();
-    int gi = 0;
+    const MultiPairArgs &ma = *(const MultiPairArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+    int q = 0;
 #pragma unroll
-    for (int i = 1; i < kMaxInputGroups; ++i)
-        if ((int)blockIdx.x >= mg.group_start[i]) gi = i;   // entries past ngroups: the block count
-    const int blk = (int)blockIdx.x - mg.group_start[gi];
-    const FusedProjArgs &a = mg.args[gi];
-    const float *X = mg.X[gi];
-    float *xso = mg.x_scale_out[gi];
-    const int64_t K = mg.K[gi];
+    for (int i = 1; i < kMultiPairs; ++i)
+        if ((int)blockIdx.x >= ma.pair_start[i]) q = i;
+    const MultiPair &e = ma.pair[q];
+    const int64_t rb = (int64_t)blockIdx.x - ma.pair_start[q];
+    const ProjView v{e.packed, e.w_scale, e.Y, e.acc, e.N};
+    float *xso = rb == 0 ? e.x_scale_out : nullptr;
     const ActTransform tr{nullptr, nullptr, 0.0f};
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // uniform: a scalar branch
-    switch (mg.cfg[gi]) {
+    switch (e.cfg) {
         BL_MULTI_CASE(0, 8, 1, 8)
         BL_MULTI_CASE(1, 8, 2, 8)
         BL_MULTI_CASE(2, 8, 3, 8)
@@ -210,9 +235,22 @@ hipError_t launch_decode_multi(MultiGroupArgs mg, hipStream_t stream, const char
                             a.nproj, waves == 4 ? "" : waves == 6 ? "_w6" : "_w8");
     }
     for (int g = mg.ngroups; g <= kMaxInputGroups; ++g) mg.group_start[g] = (int32_t)blocks;
+    int pairs = 0;
+    for (int g = 0; g < mg.ngroups; ++g) pairs += mg.args[g].nproj;
+    if (pairs > dot4::kMultiPairs) return hipErrorNotSupported;
+    dot4::MultiPairArgs ma = {};
+    int q = 0;
+    for (int g = 0; g < mg.ngroups; ++g)
+        for (int i = 0; i < mg.args[g].nproj; ++i, ++q) {
+            const FusedProjArgs &a = mg.args[g];
+            ma.pair_start[q] = mg.group_start[g] + a.block_start[i];
+            ma.pair[q] = dot4::MultiPair{mg.X[g], i == 0 ? mg.x_scale_out[g] : nullptr, a.packed[i], a.w_scale[i],
+                                         a.Y[i], a.acc[i], mg.K[g], a.N[i], mg.cfg[g], 0};
+        }
+    for (int i = q; i <= dot4::kMultiPairs; ++i) ma.pair_start[i] = (int32_t)blocks;
     *name = g_name;
     if (query) return hipSuccess;
-    hipLaunchKernelGGL(dot4::decode_multi_kernel, dim3((unsigned)blocks), dim3(512), (size_t)kmax, stream, mg);
+    hipLaunchKernelGGL(dot4::decode_multi_kernel, dim3((unsigned)blocks), dim3(512), (size_t)kmax, stream, ma);
     return hipGetLastError();
 }
 
