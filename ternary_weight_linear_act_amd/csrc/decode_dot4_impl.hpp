@@ -86,32 +86,13 @@ __device__ __forceinline__ void decode_dot4_body(
     __shared__ uint32_t s_sel[P == Pattern::Dense ? 1 : 2 * nm_sel_entries(P)];   // N:M byte selectors
 
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t N = v.N;
-    const uint8_t *packed = v.packed;
-    const int64_t row = row_block * RB + wave * RPW + lane / LPR;
-    const int j = lane % LPR;
     const int64_t C = K / 64;
-    float *Y = v.Y;
-    int32_t *acc_out = v.acc;
-    const float *w_scale = v.w_scale;
-    // every argument read later in SGPRs now (a pending scalar load would make
-    // the compiler wait for all outstanding memory operations at its use)
-    asm volatile("" ::"s"(X), "s"(Xq), "s"(x_scale), "s"(x_rowsum), "s"(packed), "s"(Y), "s"(acc_out),
-                 "s"(w_scale), "s"(x_scale_out), "s"(tr.up), "s"(tr.gamma));
-
-    // 0. the scalars the epilogue needs, issued before everything else: read
-    //    at the end, each would cost a full memory round trip there
-    const float wsc = w_scale[0];
-    float xsc = 0.0f;
-    int rs = 0;
-    if constexpr (!FUSED) {
-        xsc = x_scale[0];
-        rs = x_rowsum[0];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-
-    // 1. activations: 16-byte loads, enough for K = 64 * U * LPR (indices
-    //    past the row re-read element 0 and are never used)
+    // 1. activations first: they need only the input row (an argument of the
+    //    launch), not the projection's pointers, whose scalar loads may still
+    //    be in flight where the workgroup's lookup is deep.  16-byte loads,
+    //    enough for K = 64 * U * LPR (indices past the row re-read element 0
+    //    and are never used)
+    asm volatile("" ::"s"(X), "s"(Xq), "s"(tr.up), "s"(tr.gamma));
     constexpr int XR = FUSED ? (16 * U * LPR + kThreads - 1) / kThreads : (4 * U * LPR + kThreads - 1) / kThreads;
     const int64_t n4 = K / 4, n16 = K / 16;
     f32x4 xf[FUSED ? XR : 1];          // ext vectors: HIP's float4 / uint4 structs
@@ -125,6 +106,29 @@ __device__ __forceinline__ void decode_dot4_body(
         else xb[t] = reinterpret_cast<const u32x4 *>(Xq)[i < n16 ? i : 0];
         if constexpr (GATE) uf[t] = reinterpret_cast<const f32x4 *>(tr.up)[i < n4 ? i : 0];
         if constexpr (NORM) gf[t] = reinterpret_cast<const f32x4 *>(tr.gamma)[i < n4 ? i : 0];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int64_t N = v.N;
+    const uint8_t *packed = v.packed;
+    const int64_t row = row_block * RB + wave * RPW + lane / LPR;
+    const int j = lane % LPR;
+    float *Y = v.Y;
+    int32_t *acc_out = v.acc;
+    const float *w_scale = v.w_scale;
+    // every argument read later in SGPRs now (a pending scalar load would make
+    // the compiler wait for all outstanding memory operations at its use)
+    asm volatile("" ::"s"(x_scale), "s"(x_rowsum), "s"(packed), "s"(Y), "s"(acc_out), "s"(w_scale),
+                 "s"(x_scale_out));
+
+    // 0. the scalars the epilogue needs, issued before the weights: read at
+    //    the end, each would cost a full memory round trip there
+    const float wsc = w_scale[0];
+    float xsc = 0.0f;
+    int rs = 0;
+    if constexpr (!FUSED) {
+        xsc = x_scale[0];
+        rs = x_rowsum[0];
     }
     __builtin_amdgcn_sched_barrier(0);
 
