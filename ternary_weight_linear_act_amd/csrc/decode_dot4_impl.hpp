@@ -67,14 +67,23 @@ struct ProjView {
     int64_t N;
 };
 
-// `v`: the workgroup's projection, `row_block`: its block of RB rows there;
-// `x_scale_out`: non-NULL for the one workgroup that writes the scale.  Only
-// threads below 64 * W may enter.
-template <Pattern P, int LPR, int U, bool FUSED, int W = 4, int TR = 0>
+// What a workgroup resolves once its input-row loads are issued: its
+// projection, its block of RB rows there, and x_scale_out (non-NULL for the
+// one workgroup that writes the scale).
+struct ProjSel {
+    ProjView v;
+    int64_t row_block;
+    float *x_scale_out;
+};
+
+// `resolve()` returns the workgroup's ProjSel.  It is called after the input
+// row's loads are issued, so that their scalar loads (which return out of
+// order: any use waits for all) do not hold the row loads back.  Only threads
+// below 64 * W may enter.
+template <Pattern P, int LPR, int U, bool FUSED, int W = 4, int TR = 0, class Resolve>
 __device__ __forceinline__ void decode_dot4_body(
     const float *__restrict__ X, const int8_t *__restrict__ Xq, const float *__restrict__ x_scale,
-    const int32_t *__restrict__ x_rowsum, int64_t K, const ProjView &v, int64_t row_block,
-    float *__restrict__ x_scale_out, const ActTransform &tr)
+    const int32_t *__restrict__ x_rowsum, int64_t K, const Resolve &resolve, const ActTransform &tr)
 {
     static_assert(TR == 0 || FUSED, "the row transform belongs to the fused form");
     constexpr bool GATE = (TR & kTrGate) != 0, NORM = (TR & kTrNorm) != 0;
@@ -109,6 +118,10 @@ __device__ __forceinline__ void decode_dot4_body(
     }
     __builtin_amdgcn_sched_barrier(0);
 
+    const ProjSel sel = resolve();
+    const ProjView &v = sel.v;
+    const int64_t row_block = sel.row_block;
+    float *__restrict__ x_scale_out = sel.x_scale_out;
     const int64_t N = v.N;
     const uint8_t *packed = v.packed;
     const int64_t row = row_block * RB + wave * RPW + lane / LPR;
@@ -308,14 +321,24 @@ __global__ __launch_bounds__(64 * W) void decode_dot4_kernel(
     // entries past the last projection hold the block count, so no test of
     // nproj is needed: without one the table loads issue together rather
     // than one round trip each
+    // the input row's pointers, K and the table in the first batch of
+    // argument loads; the projection's pointers are read in resolve(), after
+    // the row loads are issued
+    asm volatile("" ::"s"(X), "s"(Xq), "s"(K), "s"(tr.up), "s"(tr.gamma));
     const int block = (int)blockIdx.x;
-    int p = 0;
+    int p = 0, first = 0;
 #pragma unroll
     for (int i = 1; i < kMaxFusedProj; ++i)
-        if (block >= args.block_start[i]) p = i;
-    const ProjView v{args.packed[p], args.w_scale[p], args.Y[p], args.acc[p], args.N[p]};
-    decode_dot4_body<P, LPR, U, FUSED, W, TR>(X, Xq, x_scale, x_rowsum, K, v, block - args.block_start[p],
-                                              block == 0 ? x_scale_out : nullptr, tr);
+        if (block >= args.block_start[i]) {
+            p = i;
+            first = args.block_start[i];
+        }
+    asm volatile("" ::"s"(p), "s"(first));
+    const auto resolve = [&]() {
+        return ProjSel{ProjView{args.packed[p], args.w_scale[p], args.Y[p], args.acc[p], args.N[p]},
+                       (int64_t)(block - first), block == 0 ? x_scale_out : nullptr};
+    };
+    decode_dot4_body<P, LPR, U, FUSED, W, TR>(X, Xq, x_scale, x_rowsum, K, resolve, tr);
 }
 
 }  // namespace dot4

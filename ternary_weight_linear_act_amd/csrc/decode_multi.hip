@@ -104,15 +104,15 @@ constexpr int kMultiPairs = 16;
 
 struct MultiPairArgs {
     int32_t pair_start[kMultiPairs + 1];     // entries past the last pair: the block count
-    int32_t pair_k[kMultiPairs];             // the pairs' K and input rows, read with pair_start:
-    const float *pair_x[kMultiPairs];        // a workgroup's input loads need no second load
+    int32_t pair_kc[kMultiPairs];            // K | configuration << 16, and the input rows, read
+    const float *pair_x[kMultiPairs];        // with pair_start: the input loads wait on no second load
     MultiPair pair[kMultiPairs];
 };
 
 #define BL_MULTI_CASE(ID, LPR, U, W)                                                                            \
     case ID:                                                                                                    \
         if (wave < (W))                                                                                         \
-            decode_dot4_body<Pattern::Dense, LPR, U, true, W, 0>(x, nullptr, nullptr, nullptr, k, v, rb, xso, tr); \
+            decode_dot4_body<Pattern::Dense, LPR, U, true, W, 0>(x, nullptr, nullptr, nullptr, k, resolve, tr); \
         return;
 
 // The argument is read in place in the kernel-argument segment (it is the
@@ -121,22 +121,27 @@ struct MultiPairArgs {
 __global__ __launch_bounds__(512) void decode_multi_kernel(MultiPairArgs)
 {
     const MultiPairArgs &ma = *(const MultiPairArgs *)__builtin_amdgcn_kernarg_segment_ptr();
-    int q = 0, k = ma.pair_k[0];
+    const int block = (int)blockIdx.x;
+    int q = 0, kc = ma.pair_kc[0];        // three values selected: more made the scan a chain of branches
     const float *x = ma.pair_x[0];
 #pragma unroll
     for (int i = 1; i < kMultiPairs; ++i)
-        if ((int)blockIdx.x >= ma.pair_start[i]) {
+        if (block >= ma.pair_start[i]) {
             q = i;
-            k = ma.pair_k[i];
+            kc = ma.pair_kc[i];
             x = ma.pair_x[i];
         }
-    const MultiPair &e = ma.pair[q];
-    const int64_t rb = (int64_t)blockIdx.x - ma.pair_start[q];
-    const ProjView v{e.packed, e.w_scale, e.Y, e.acc, e.N};
-    float *xso = rb == 0 ? e.x_scale_out : nullptr;
+    const int k = kc & 0xffff, cfg = kc >> 16;
+    // the pair's record is read in resolve(), after the input-row loads
+    const auto resolve = [&]() {
+        const MultiPair &e = ma.pair[q];
+        const int first = ma.pair_start[q];
+        return ProjSel{ProjView{e.packed, e.w_scale, e.Y, e.acc, e.N}, (int64_t)(block - first),
+                       block == first ? e.x_scale_out : nullptr};
+    };
     const ActTransform tr{nullptr, nullptr, 0.0f};
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // uniform: a scalar branch
-    switch (e.cfg) {
+    switch (cfg) {
         BL_MULTI_CASE(0, 8, 1, 8)
         BL_MULTI_CASE(1, 8, 2, 8)
         BL_MULTI_CASE(2, 8, 3, 8)
@@ -250,7 +255,7 @@ hipError_t launch_decode_multi(MultiGroupArgs mg, hipStream_t stream, const char
         for (int i = 0; i < mg.args[g].nproj; ++i, ++q) {
             const FusedProjArgs &a = mg.args[g];
             ma.pair_start[q] = mg.group_start[g] + a.block_start[i];
-            ma.pair_k[q] = (int32_t)mg.K[g];
+            ma.pair_kc[q] = (int32_t)mg.K[g] | mg.cfg[g] << 16;   // K <= 16384 here
             ma.pair_x[q] = mg.X[g];
             ma.pair[q] = dot4::MultiPair{mg.X[g], i == 0 ? mg.x_scale_out[g] : nullptr, a.packed[i], a.w_scale[i],
                                          a.Y[i], a.acc[i], mg.K[g], a.N[i], mg.cfg[g], 0};
