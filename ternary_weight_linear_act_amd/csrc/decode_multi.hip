@@ -117,19 +117,30 @@ struct MultiPairArgs {
 
 // The argument is read in place in the kernel-argument segment (it is the
 // launch's only argument, at offset 0): indexed by the group, a by-value
-// copy of it would live in scratch memory.
+// copy of it would live in scratch memory.  NP: the pairs scanned (at least
+// the launch's).  Their K and row pointers are read into registers with the
+// table and selected there (selecting the index first, then loading the
+// entry, costs a second round trip before the input loads).
+template <int NP>
 __global__ __launch_bounds__(512) void decode_multi_kernel(MultiPairArgs)
 {
     const MultiPairArgs &ma = *(const MultiPairArgs *)__builtin_amdgcn_kernarg_segment_ptr();
     const int block = (int)blockIdx.x;
-    int q = 0, kc = ma.pair_kc[0];        // three values selected: more made the scan a chain of branches
-    const float *x = ma.pair_x[0];
+    int kcs[NP];
+    const float *xs[NP];
 #pragma unroll
-    for (int i = 1; i < kMultiPairs; ++i)
+    for (int i = 0; i < NP; ++i) {
+        kcs[i] = ma.pair_kc[i];
+        xs[i] = ma.pair_x[i];
+    }
+    int q = 0, kc = kcs[0];
+    const float *x = xs[0];
+#pragma unroll
+    for (int i = 1; i < NP; ++i)
         if (block >= ma.pair_start[i]) {
             q = i;
-            kc = ma.pair_kc[i];
-            x = ma.pair_x[i];
+            kc = kcs[i];
+            x = xs[i];
         }
     const int k = kc & 0xffff, cfg = kc >> 16;
     // the pair's record is read in resolve(), after the input-row loads
@@ -263,7 +274,10 @@ hipError_t launch_decode_multi(MultiGroupArgs mg, hipStream_t stream, const char
     for (int i = q; i <= dot4::kMultiPairs; ++i) ma.pair_start[i] = (int32_t)blocks;
     *name = g_name;
     if (query) return hipSuccess;
-    hipLaunchKernelGGL(dot4::decode_multi_kernel, dim3((unsigned)blocks), dim3(512), (size_t)kmax, stream, ma);
+    // the shortest scan that covers the launch's pairs
+    void (*kern)(dot4::MultiPairArgs) = q <= 4 ? dot4::decode_multi_kernel<4>
+                                      : q <= 8 ? dot4::decode_multi_kernel<8> : dot4::decode_multi_kernel<16>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(512), (size_t)kmax, stream, ma);
     return hipGetLastError();
 }
 
