@@ -230,13 +230,26 @@ __global__ __launch_bounds__(512) void skinny_direct_multi_kernel(DirectMultiArg
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const DirectMultiArgs &da = *(const DirectMultiArgs *)__builtin_amdgcn_kernarg_segment_ptr();
-    int gi = 0;
+    // the configuration and first block selected with the group from values
+    // read with the table (loaded from the selected index instead, they cost
+    // a second scalar round trip)
+    int cfgs[kMaxInputGroups], firsts[kMaxInputGroups];
+#pragma unroll
+    for (int i = 0; i < kMaxInputGroups; ++i) {
+        cfgs[i] = da.cfg[i];
+        firsts[i] = da.group_start[i];
+    }
+    int gi = 0, cfg = cfgs[0], first = firsts[0];
 #pragma unroll
     for (int i = 1; i < kMaxInputGroups; ++i)
-        if ((int)blockIdx.x >= da.group_start[i]) gi = i;   // entries past ngroups: the block count
-    const int blk = (int)blockIdx.x - da.group_start[gi];
+        if ((int)blockIdx.x >= firsts[i]) {   // entries past ngroups: the block count
+            gi = i;
+            cfg = cfgs[i];
+            first = firsts[i];
+        }
+    const int blk = (int)blockIdx.x - first;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    switch (da.cfg[gi]) {
+    switch (cfg) {
         BL_DIRECT_CASE(0, 4, 8, 8, 1)
         BL_DIRECT_CASE(1, 4, 8, 8, 2)
         BL_DIRECT_CASE(2, 2, 20, 8, 1)
